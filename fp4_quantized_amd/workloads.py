@@ -1,0 +1,184 @@
+"""Seeded synthetic inputs shaped like the workloads of the Averis paper's experiments.
+
+This module holds no step of the method: it only draws numbers.  The same bytes feed the
+HIP path and the CPU oracle.  The data stands in for Qwen3 activations and output gradients
+during DCLM pre-training, which are not available here; it imitates the structure the pages
+describe: a coherent rank-one column mean shared by all tokens, a few channels where the mean
+dominates the largest entries, and SwiGLU-style non-odd nonlinear inputs
+("均值偏置的诅咒与祝福" explainer, paper.rainbus.top, sections 核心方法 and 实验结果;
+gist.science German summary, Technische Zusammenfassung §2).
+
+Every tensor is drawn in fp64 from numpy.random.default_rng(SeedSequence(seed)) with child
+streams in a fixed order, then rounded once to fp32 and, for bf16 tensors, from fp32 to bf16
+with round-to-nearest-even.  Arrays are returned as numpy fp32 (the exact values of the
+bf16 tensors) plus a `dtype` tag; `to_torch` produces the tensor the GPU receives.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# Qwen3-0.6B-shaped linears at l = 16384 tokens: (name, m = in features, n = out features).
+SWEEP_LAYERS = [
+    ("q", 1024, 2048),
+    ("k", 1024, 1024),
+    ("v", 1024, 1024),
+    ("o", 2048, 1024),
+    ("gate", 1024, 3072),
+    ("up", 1024, 3072),
+    ("down", 3072, 1024),
+]
+
+
+@dataclass
+class Linear:
+    """One linear layer's inputs: X [l, m], D [l, n], W [m, n] (pages' orientation Y = X W)."""
+    name: str
+    x: np.ndarray
+    w: np.ndarray
+    d: np.ndarray | None
+    dtype: str  # "f32" or "bf16": the element type handed to the GPU
+    meta: dict = field(default_factory=dict)
+
+
+def _round(a, dtype):
+    a32 = np.asarray(a, dtype=np.float64).astype(np.float32)
+    if dtype == "f32":
+        return a32
+    # fp32 -> bf16, round to nearest even, on the bit pattern (finite inputs only)
+    u = a32.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+def _mean_vector(rng, m, target_rms, n_spikes, spike=20.0):
+    g = rng.standard_normal(m)
+    mu = target_rms * g / np.sqrt(np.mean(g * g))
+    idx = rng.choice(m, size=n_spikes, replace=False) if n_spikes else np.zeros(0, int)
+    mu[idx] *= spike
+    return mu
+
+
+def _n_spikes(m):
+    return max(1, int(round(0.001 * m)))
+
+
+def _grad(rng, l, n, dtype):
+    """D = 1 mu_D^T + E, E ~ N(0, 1e-6) (std 1e-3), RMS(mu_D) = the residual RMS."""
+    e = rng.standard_normal((l, n)) * 1e-3
+    mu_d = _mean_vector(rng, n, 1e-3, 0)
+    return _round(e + mu_d[None, :], dtype)
+
+
+def tiny(seed=0):
+    """Forward-only check case: X fp32 [256, 128] = 1 mu^T + R, mu_j ~ N(0, 16), R ~ N(0, 1);
+    W fp32 [128, 128] ~ N(0, 0.02^2)."""
+    ss = np.random.SeedSequence(seed)
+    r_mu, r_r, r_w = [np.random.default_rng(s) for s in ss.spawn(3)]
+    mu = r_mu.standard_normal(128) * 4.0
+    r = r_r.standard_normal((256, 128))
+    w = r_w.standard_normal((128, 128)) * 0.02
+    return Linear("tiny", _round(mu[None, :] + r, "f32"), _round(w, "f32"), None, "f32")
+
+
+def up_proj_like(seed, l, m, n, dtype="bf16", name="up_proj"):
+    """X = bf16(1 mu^T + R): R ~ Student-t(4), mu = 3 x RMS(t4) x g / rms(g) with 0.1 % of the
+    channels scaled x20; D as in `_grad`; W ~ N(0, 0.02^2) [m, n]."""
+    ss = np.random.SeedSequence(seed)
+    r_mu, r_r, r_d, r_w = [np.random.default_rng(s) for s in ss.spawn(4)]
+    mu = _mean_vector(r_mu, m, 3.0 * np.sqrt(2.0), _n_spikes(m))
+    r = r_r.standard_t(4, size=(l, m))
+    x = _round(r + mu[None, :], dtype)
+    d = _grad(r_d, l, n, dtype)
+    w = _round(r_w.standard_normal((m, n)) * 0.02, dtype)
+    return Linear(name, x, w, d, dtype)
+
+
+def down_proj_like(seed, l, m, n, dtype="bf16", name="down_proj"):
+    """X = bf16(silu(A) * B + 1 mu^T) with A, B ~ N(0, 1); mu as in up_proj_like with rms(R)
+    measured on the draw; D and W as in up_proj_like."""
+    ss = np.random.SeedSequence(seed)
+    r_mu, r_a, r_b, r_d, r_w = [np.random.default_rng(s) for s in ss.spawn(5)]
+    a = r_a.standard_normal((l, m))
+    b = r_b.standard_normal((l, m))
+    r = a / (1.0 + np.exp(-a)) * b
+    del a, b
+    mu = _mean_vector(r_mu, m, 3.0 * float(np.sqrt(np.mean(r * r))), _n_spikes(m))
+    x = _round(r + mu[None, :], dtype)
+    d = _grad(r_d, l, n, dtype)
+    w = _round(r_w.standard_normal((m, n)) * 0.02, dtype)
+    return Linear(name, x, w, d, dtype)
+
+
+def up_proj(seed=1, l=8192):
+    """Qwen3-0.6B-shaped up_proj: l = 8192 (b = 4, s = 2048), m = 1024, n = 3072, bf16."""
+    return up_proj_like(seed, l, 1024, 3072)
+
+
+def down_proj(seed=2, l=16384):
+    """down_proj: l = 16384, m = 3072, n = 1024, bf16, SwiGLU-like input."""
+    return down_proj_like(seed, l, 3072, 1024)
+
+
+def sweep(seed=3, l=16384):
+    """The seven Qwen3-0.6B-shaped linears at l = 16384, each drawn as up_proj_like."""
+    return [up_proj_like([seed, j], l, m, n, name=nm) for j, (nm, m, n) in enumerate(SWEEP_LAYERS)]
+
+
+@dataclass
+class MoE:
+    """Expert-contiguous MoE FFN inputs.  offsets [E+1] over the routed rows; per expert e,
+    rows offsets[e]:offsets[e+1] of x_gate (token states, shared by gate and up), x_down,
+    d_gateup and d_down; w_gate/w_up [E, hidden, ffn], w_down [E, ffn, hidden]."""
+    offsets: np.ndarray
+    x: np.ndarray
+    x_down: np.ndarray
+    d_gateup: np.ndarray
+    d_down: np.ndarray
+    w_gate: np.ndarray
+    w_up: np.ndarray
+    w_down: np.ndarray
+    dtype: str = "bf16"
+
+
+def zipf_topk_counts(rng, tokens, experts, topk, s=1.1):
+    """Distinct top-k experts per token by Gumbel-top-k over p_e ~ (e + 1)^-s.
+    Returns (expert ids [tokens, topk], counts [experts])."""
+    logp = -s * np.log(np.arange(1, experts + 1, dtype=np.float64))
+    g = rng.gumbel(size=(tokens, experts))
+    ids = np.argsort(-(logp[None, :] + g), axis=1)[:, :topk]
+    counts = np.bincount(ids.ravel(), minlength=experts)
+    return ids, counts
+
+
+def moe(seed=4, tokens=8192, hidden=2048, ffn=768, experts=64, topk=8, dtype="bf16"):
+    """Top-8 Zipf(1.1) routing of 8192 tokens over 64 experts; token states [tokens, hidden]
+    drawn as up_proj_like, gathered per expert; the down-projection input and the output
+    gradients drawn per routed row as in up_proj_like."""
+    ss = np.random.SeedSequence(seed)
+    r_route, r_x, r_xd, r_dg, r_dd, r_w = [np.random.default_rng(s) for s in ss.spawn(6)]
+    ids, counts = zipf_topk_counts(r_route, tokens, experts, topk)
+    offsets = np.zeros(experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    states = up_proj_like(r_x.integers(1 << 62), tokens, hidden, 8, dtype).x
+    order = np.argsort(ids.ravel(), kind="stable")  # routed rows grouped by expert
+    x = states[order // topk]
+    L = int(offsets[-1])
+    x_down = up_proj_like(r_xd.integers(1 << 62), L, ffn, 8, dtype).x
+    d_gu = _grad(r_dg, L, ffn, dtype)
+    d_dn = _grad(r_dd, L, hidden, dtype)
+    w = r_w.standard_normal((3, experts, hidden, ffn)) * 0.02
+    w_gate = _round(w[0], dtype)
+    w_up = _round(w[1], dtype)
+    w_down = _round(np.ascontiguousarray(np.swapaxes(w[2], 1, 2)), dtype)
+    return MoE(offsets, x, x_down, d_gu, d_dn, w_gate, w_up, w_down, dtype)
+
+
+def to_torch(a, dtype, device):
+    """Hand the exact values to torch as fp32 or bf16 (no rounding: values are representable)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.to(device)
