@@ -1,0 +1,198 @@
+"""Thin ctypes binding of libaveris.so (C ABI in include/averis.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP stream; every
+step of the computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or no GPU is present, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+NVFP4 = 1
+MXFP4 = 2
+F32 = 0
+BF16 = 1
+SPLIT = 1 << 0
+HADAMARD16 = 1 << 1
+MEAN_GIVEN = 1 << 2
+ACCUMULATE = 1 << 4
+KPAD = 128
+BLOCK = {NVFP4: 16, MXFP4: 32}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaveris.so")
+
+EXPORTS = [
+    "averis_abi_version", "averis_status_string",
+    "averis_split_quant_workspace_size", "averis_split_quant",
+    "averis_linear_workspace_size", "averis_linear_fwd", "averis_linear_bwd_dx",
+    "averis_linear_bwd_dw_workspace_size", "averis_linear_bwd_dw",
+]
+
+
+class CQTensor(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("tensor_scale", ctypes.c_void_p),
+        ("outer", ctypes.c_int64),
+        ("k", ctypes.c_int64),
+        ("k_pad", ctypes.c_int64),
+        ("fmt", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libaveris.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, U32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+        Q = ctypes.POINTER(CQTensor)
+        sig = {
+            "averis_abi_version": (I32, []),
+            "averis_status_string": (ctypes.c_char_p, [I32]),
+            "averis_split_quant_workspace_size": (SZ, [I64, I64, I32, U32]),
+            "averis_split_quant": (I32, [P, I32, I64, I64, I64, I32, U32, P, Q, Q, Q, P, SZ, P]),
+            "averis_linear_workspace_size": (SZ, [I64, I64, I64, I32]),
+            "averis_linear_fwd": (I32, [Q, Q, Q, P, I32, I64, P, SZ, P]),
+            "averis_linear_bwd_dx": (I32, [Q, Q, Q, P, I32, I64, P, SZ, P]),
+            "averis_linear_bwd_dw_workspace_size": (SZ, [I64, I64, I64, I32]),
+            "averis_linear_bwd_dw": (I32, [Q, Q, Q, Q, I64, P, I64, U32, P, SZ, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+class AverisError(RuntimeError):
+    pass
+
+
+def _check(status):
+    if status != 0:
+        raise AverisError(f"averis status {status}: {lib().averis_status_string(status).decode()}")
+
+
+@dataclass
+class QTensor:
+    """Device buffers of one quantized operand [outer, k] (blocks along k)."""
+    codes: torch.Tensor         # uint8 [outer, k_pad/2]
+    scales: torch.Tensor        # uint8 [outer, k_pad/g]
+    tensor_scale: torch.Tensor | None  # fp32 [1] (NVFP4)
+    outer: int
+    k: int
+    fmt: int
+    rotated: bool
+
+    @property
+    def k_pad(self):
+        return (self.k + KPAD - 1) // KPAD * KPAD
+
+    def c(self):
+        return CQTensor(self.codes.data_ptr(), self.scales.data_ptr(),
+                        self.tensor_scale.data_ptr() if self.tensor_scale is not None else None,
+                        self.outer, self.k, self.k_pad, self.fmt, HADAMARD16 if self.rotated else 0)
+
+
+def empty_qtensor(outer, k, fmt, rotated=False, device="cuda", groups=1):
+    kp = (k + KPAD - 1) // KPAD * KPAD
+    g = BLOCK[fmt]
+    return QTensor(torch.empty((outer, kp // 2), dtype=torch.uint8, device=device),
+                   torch.empty((outer, kp // g), dtype=torch.uint8, device=device),
+                   torch.empty(groups, dtype=torch.float32, device=device) if fmt == NVFP4 else None,
+                   outer, k, fmt, rotated)
+
+
+def _ptr(q):
+    return ctypes.byref(q.c()) if q is not None else None
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def split_quant(x: torch.Tensor, fmt: int, split: bool = True, hadamard: bool = False,
+                mean: torch.Tensor | None = None, row: bool = True, col: bool = True, stream=None):
+    """Mean, residual and FP4 quantization of x [rows, cols] (bf16 or fp32, row-major).
+
+    Returns dict(mean=fp32 [cols] or None, row=QTensor [rows, cols] or None,
+    col=QTensor [cols, rows] or None, mean_q=QTensor [1, cols] or None).
+    `mean` given: used instead of the column mean (MEAN_GIVEN)."""
+    assert x.dim() == 2 and x.is_cuda
+    rows, cols = x.shape
+    assert rows == 0 or x.stride(1) == 1, "x must be row-major"
+    ldx = x.stride(0) if rows > 0 else cols
+    dev = x.device
+    flags = (SPLIT if split else 0) | (HADAMARD16 if hadamard else 0) | \
+        (MEAN_GIVEN if (split and mean is not None) else 0)
+    mu = None
+    if split:
+        mu = mean.contiguous() if mean is not None else torch.empty(cols, dtype=torch.float32, device=dev)
+    q_row = empty_qtensor(rows, cols, fmt, hadamard, dev) if row else None
+    q_col = empty_qtensor(cols, rows, fmt, hadamard, dev) if col else None
+    q_mean = empty_qtensor(1, cols, fmt, hadamard, dev) if split else None
+    L = lib()
+    ws = _workspace(L.averis_split_quant_workspace_size(rows, cols, fmt, flags), dev)
+    _check(L.averis_split_quant(x.data_ptr() if rows else None, _dtype_code(x), rows, cols, ldx, fmt,
+                                flags, mu.data_ptr() if mu is not None else None, _ptr(q_row), _ptr(q_col),
+                                _ptr(q_mean), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return dict(mean=mu, row=q_row, col=q_col, mean_q=q_mean)
+
+
+def _linear(fn, a: QTensor, mu: QTensor | None, w: QTensor, out_dtype, stream):
+    dev = a.codes.device
+    out = torch.empty((a.outer, w.outer), dtype=out_dtype, device=dev)
+    L = lib()
+    ws = _workspace(L.averis_linear_workspace_size(a.outer, w.outer, a.k_pad, a.fmt), dev)
+    _check(fn(_ptr(a), _ptr(mu), _ptr(w), out.data_ptr() if out.numel() else None, _dtype_code(out), out.stride(0),
+              ws.data_ptr(), ws.numel(), _stream(stream)))
+    return out
+
+
+def linear_fwd(xr: QTensor, mu_x: QTensor | None, w: QTensor, out_dtype=torch.float32, stream=None):
+    """Y [l, n] = 1 (Q(mu_X) Q(W)) + Q(X_R) Q(W); w is the [n, m] (K = m) weight operand."""
+    return _linear(lib().averis_linear_fwd, xr, mu_x, w, out_dtype, stream)
+
+
+def linear_bwd_dx(dr: QTensor, mu_d: QTensor | None, w: QTensor, out_dtype=torch.float32, stream=None):
+    """dX [l, m] = 1 (Q(mu_D) Q(W)^T) + Q(D_R) Q(W)^T; w is the [m, n] (K = n) weight operand."""
+    return _linear(lib().averis_linear_bwd_dx, dr, mu_d, w, out_dtype, stream)
+
+
+def linear_bwd_dw(xr_t: QTensor, dr_t: QTensor, mu_x: QTensor | None, mu_d: QTensor | None, l: int,
+                  dw: torch.Tensor | None = None, accumulate: bool = False, stream=None):
+    """dW [m, n] = Q(X_R)^T Q(D_R) + l Q(mu_X)^T Q(mu_D) (fp32), optionally accumulated into dw."""
+    dev = xr_t.codes.device
+    if dw is None:
+        dw = torch.empty((xr_t.outer, dr_t.outer), dtype=torch.float32, device=dev)
+    L = lib()
+    ws = _workspace(L.averis_linear_bwd_dw_workspace_size(xr_t.outer, dr_t.outer, l, xr_t.fmt), dev)
+    _check(L.averis_linear_bwd_dw(_ptr(xr_t), _ptr(dr_t), _ptr(mu_x), _ptr(mu_d), l,
+                                  dw.data_ptr() if dw.numel() else None, dw.stride(0),
+                                  ACCUMULATE if accumulate else 0, ws.data_ptr(), ws.numel(), _stream(stream)))
+    return dw

@@ -1,0 +1,186 @@
+// C ABI of libaveris (declared in include/averis.h): argument validation, workspace sizing,
+// and dispatch to the split/quant and GEMM launchers.  Nothing is enqueued unless every
+// argument check passes.
+#include <cstring>
+
+#include "launch.h"
+
+
+
+using namespace av;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool fmt_ok(int32_t f) { return f == AVERIS_NVFP4 || f == AVERIS_MXFP4; }
+bool dtype_ok(int32_t d) { return d == AVERIS_F32 || d == AVERIS_BF16; }
+int64_t elem_size(int32_t d) { return d == AVERIS_BF16 ? 2 : 4; }
+int64_t block_of(int32_t f) { return f == AVERIS_MXFP4 ? 32 : 16; }
+
+// A qtensor the call writes or reads must have exactly the expected shape and format.
+int32_t check_q(const averis_qtensor* q, int64_t outer, int64_t k, int32_t fmt, uint32_t rot) {
+  const bool empty = outer == 0 || k == 0;
+  if (!empty && (!q->codes || !q->scales)) return AVERIS_E_NULL;
+  if (fmt == AVERIS_NVFP4 && !q->tensor_scale) return AVERIS_E_NULL;
+  if (q->fmt != fmt) return AVERIS_E_FORMAT;
+  if (q->outer != outer || q->k != k || q->k_pad != round_up(k, kKPad)) return AVERIS_E_SHAPE;
+  if ((q->flags & ~AVERIS_HADAMARD16) != 0) return AVERIS_E_FLAGS;
+  if ((q->flags & AVERIS_HADAMARD16) != rot) return AVERIS_E_FLAGS;
+  if (!aligned16(q->codes) || !aligned16(q->scales)) return AVERIS_E_ALIGN;
+  return AVERIS_OK;
+}
+
+// Operand consumed by a GEMM: shape taken from the struct, only consistency checked.
+int32_t check_in(const averis_qtensor* q) {
+  if (!q) return AVERIS_E_NULL;
+  if (!fmt_ok(q->fmt)) return AVERIS_E_FORMAT;
+  if (q->outer < 0 || q->k < 0 || q->k_pad != round_up(q->k, kKPad)) return AVERIS_E_SHAPE;
+  return check_q(q, q->outer, q->k, q->fmt, q->flags & AVERIS_HADAMARD16);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t averis_abi_version(void) { return AVERIS_ABI_VERSION; }
+
+const char* averis_status_string(int32_t s) {
+  switch (s) {
+    case AVERIS_OK: return "ok";
+    case AVERIS_E_NULL: return "required pointer is NULL";
+    case AVERIS_E_SHAPE: return "inconsistent or unsupported sizes";
+    case AVERIS_E_ALIGN: return "pointer or leading dimension not 16-byte aligned";
+    case AVERIS_E_DTYPE: return "unknown element type";
+    case AVERIS_E_FORMAT: return "unknown FP4 format or mixed formats";
+    case AVERIS_E_FLAGS: return "unknown or contradictory flags";
+    case AVERIS_E_WORKSPACE: return "workspace missing or too small";
+    case AVERIS_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t averis_split_quant_workspace_size(int64_t rows, int64_t cols, int32_t fmt, uint32_t flags) {
+  (void)fmt; (void)flags;
+  if (rows < 0 || cols <= 0) return 0;
+  return split_quant_ws_bytes(rows, cols);
+}
+
+int32_t averis_split_quant(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ldx, int32_t fmt,
+                           uint32_t flags, float* mean, const averis_qtensor* q_row, const averis_qtensor* q_col,
+                           const averis_qtensor* q_mean, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(xdt)) return AVERIS_E_DTYPE;
+  if (!fmt_ok(fmt)) return AVERIS_E_FORMAT;
+  if (flags & ~(AVERIS_SPLIT | AVERIS_HADAMARD16 | AVERIS_MEAN_GIVEN)) return AVERIS_E_FLAGS;
+  const bool split = flags & AVERIS_SPLIT, h16 = flags & AVERIS_HADAMARD16, given = flags & AVERIS_MEAN_GIVEN;
+  if (given && !split) return AVERIS_E_FLAGS;
+  if (rows < 0 || cols <= 0 || cols % kKPad != 0 || ldx < cols) return AVERIS_E_SHAPE;
+  if (rows > ((int64_t)1 << 31) || cols > ((int64_t)1 << 24)) return AVERIS_E_SHAPE;
+  if (!q_row && !q_col) return AVERIS_E_NULL;
+  if (rows > 0 && !x) return AVERIS_E_NULL;
+  if (x && (!aligned16(x) || (ldx * elem_size(xdt)) % 16 != 0)) return AVERIS_E_ALIGN;
+  const uint32_t rot = h16 ? AVERIS_HADAMARD16 : 0u;
+  int32_t st;
+  if (q_row && (st = check_q(q_row, rows, cols, fmt, rot)) != AVERIS_OK) return st;
+  if (q_col && (st = check_q(q_col, cols, rows, fmt, rot)) != AVERIS_OK) return st;
+  if (split) {
+    if (!mean || !q_mean) return AVERIS_E_NULL;
+    if (!aligned16(mean)) return AVERIS_E_ALIGN;
+    if ((st = check_q(q_mean, 1, cols, fmt, rot)) != AVERIS_OK) return st;
+  } else if (q_mean) {
+    return AVERIS_E_FLAGS;
+  }
+  if (!ws || ws_bytes < split_quant_ws_bytes(rows, cols)) return AVERIS_E_WORKSPACE;
+  if (!aligned16(ws)) return AVERIS_E_ALIGN;
+
+  SplitQuantPlan p{x, xdt, rows, cols, ldx, fmt, split, h16, given, mean, q_row, q_col, q_mean, ws,
+                   reinterpret_cast<hipStream_t>(stream)};
+  return split_quant_launch(p) == hipSuccess ? AVERIS_OK : AVERIS_E_HIP;
+}
+
+size_t averis_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t fmt) {
+  (void)fmt;
+  if (M < 0 || N < 0 || K < 0) return 0;
+  return gemm_ws_bytes(M, N, K, 1);
+}
+
+size_t averis_linear_bwd_dw_workspace_size(int64_t m, int64_t n, int64_t l, int32_t fmt) {
+  (void)fmt;
+  if (m < 0 || n < 0 || l < 0) return 0;
+  const int64_t K = round_up(l, kKPad);
+  return gemm_ws_bytes(m, n, K, choose_splits(m, n, K));
+}
+
+static int32_t linear_common(const averis_qtensor* a, const averis_qtensor* mu, const averis_qtensor* w, void* out,
+                             int32_t odt, int64_t ldo, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st;
+  if ((st = check_in(a)) != AVERIS_OK) return st;
+  if ((st = check_in(w)) != AVERIS_OK) return st;
+  if (!dtype_ok(odt)) return AVERIS_E_DTYPE;
+  if (a->fmt != w->fmt) return AVERIS_E_FORMAT;
+  if (a->k != w->k || a->k % kKPad != 0) return AVERIS_E_SHAPE;
+  if ((a->flags ^ w->flags) & AVERIS_HADAMARD16) return AVERIS_E_FLAGS;
+  if (mu) {
+    if ((st = check_in(mu)) != AVERIS_OK) return st;
+    if (mu->fmt != a->fmt) return AVERIS_E_FORMAT;
+    if (mu->outer != 1 || mu->k != a->k) return AVERIS_E_SHAPE;
+    if ((mu->flags ^ a->flags) & AVERIS_HADAMARD16) return AVERIS_E_FLAGS;
+  }
+  if (ldo < w->outer) return AVERIS_E_SHAPE;
+  if (a->outer > 0 && w->outer > 0) {
+    if (!out) return AVERIS_E_NULL;
+    if (!aligned16(out) || (ldo * elem_size(odt)) % 16 != 0) return AVERIS_E_ALIGN;
+  }
+  if (!ws || ws_bytes < gemm_ws_bytes(a->outer, w->outer, a->k_pad, 1)) return AVERIS_E_WORKSPACE;
+  if (!aligned16(ws)) return AVERIS_E_ALIGN;
+  GemmPlan p{};
+  p.a = a; p.b = w; p.c = out; p.ldc = ldo; p.c_bf16 = odt == AVERIS_BF16;
+  p.mu = mu; p.splits = 1; p.ws = ws; p.stream = reinterpret_cast<hipStream_t>(stream);
+  return gemm_launch(p) == hipSuccess ? AVERIS_OK : AVERIS_E_HIP;
+}
+
+int32_t averis_linear_fwd(const averis_qtensor* xr, const averis_qtensor* mu_x, const averis_qtensor* w, void* y,
+                          int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  return linear_common(xr, mu_x, w, y, ydt, ldy, ws, ws_bytes, stream);
+}
+
+int32_t averis_linear_bwd_dx(const averis_qtensor* dr, const averis_qtensor* mu_d, const averis_qtensor* w, void* dx,
+                             int32_t dxdt, int64_t lddx, void* ws, size_t ws_bytes, void* stream) {
+  return linear_common(dr, mu_d, w, dx, dxdt, lddx, ws, ws_bytes, stream);
+}
+
+int32_t averis_linear_bwd_dw(const averis_qtensor* xr_t, const averis_qtensor* dr_t, const averis_qtensor* mu_x,
+                             const averis_qtensor* mu_d, int64_t l, float* dw, int64_t lddw, uint32_t flags, void* ws,
+                             size_t ws_bytes, void* stream) {
+  int32_t st;
+  if (flags & ~AVERIS_ACCUMULATE) return AVERIS_E_FLAGS;
+  if ((st = check_in(xr_t)) != AVERIS_OK) return st;
+  if ((st = check_in(dr_t)) != AVERIS_OK) return st;
+  if (xr_t->fmt != dr_t->fmt) return AVERIS_E_FORMAT;
+  if (xr_t->k != l || dr_t->k != l) return AVERIS_E_SHAPE;
+  if ((xr_t->flags ^ dr_t->flags) & AVERIS_HADAMARD16) return AVERIS_E_FLAGS;
+  if ((mu_x == nullptr) != (mu_d == nullptr)) return AVERIS_E_NULL;
+  if (mu_x) {
+    if ((st = check_in(mu_x)) != AVERIS_OK) return st;
+    if ((st = check_in(mu_d)) != AVERIS_OK) return st;
+    if (mu_x->fmt != xr_t->fmt || mu_d->fmt != xr_t->fmt) return AVERIS_E_FORMAT;
+    if (mu_x->outer != 1 || mu_d->outer != 1 || mu_x->k != xr_t->outer || mu_d->k != dr_t->outer) return AVERIS_E_SHAPE;
+    if ((mu_x->flags ^ mu_d->flags) & AVERIS_HADAMARD16) return AVERIS_E_FLAGS;
+  }
+  const int64_t m = xr_t->outer, n = dr_t->outer;
+  if (lddw < n) return AVERIS_E_SHAPE;
+  if (m > 0 && n > 0) {
+    if (!dw) return AVERIS_E_NULL;
+    if (!aligned16(dw) || (lddw * 4) % 16 != 0) return AVERIS_E_ALIGN;
+  }
+  const int splits = choose_splits(m, n, xr_t->k_pad);
+  if (!ws || ws_bytes < gemm_ws_bytes(m, n, xr_t->k_pad, splits)) return AVERIS_E_WORKSPACE;
+  if (!aligned16(ws)) return AVERIS_E_ALIGN;
+  GemmPlan p{};
+  p.a = xr_t; p.b = dr_t; p.c = dw; p.ldc = lddw; p.c_bf16 = 0;
+  p.mu_u = mu_x; p.mu_v = mu_d; p.r1 = (float)l;
+  p.accumulate = (flags & AVERIS_ACCUMULATE) ? 1 : 0;
+  p.splits = splits; p.ws = ws; p.stream = reinterpret_cast<hipStream_t>(stream);
+  return gemm_launch(p) == hipSuccess ? AVERIS_OK : AVERIS_E_HIP;
+}
+
+}  // extern "C"

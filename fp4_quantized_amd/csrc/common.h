@@ -1,0 +1,141 @@
+// Shared device helpers for libaveris (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "averis.h"
+
+namespace av {
+
+constexpr int kKPad = 128;  // storage padding multiple along K
+
+static inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- element loads ------------
+// Inputs are bf16 (bit patterns in uint16) or fp32.  VEC = elements per 16-byte load.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int VEC = 4;
+  __device__ static inline void unpack(const uint4& w, float* v) {
+    v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
+    v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
+  }
+  __device__ static inline float load1(const float* p) { return *p; }
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int VEC = 8;
+  __device__ static inline void unpack(const uint4& w, float* v) {
+    const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(a[i] << 16);
+      v[2 * i + 1] = __uint_as_float(a[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ static inline float load1(const uint16_t* p) { return __uint_as_float((uint32_t)(*p) << 16); }
+};
+
+// ---------------------------------------------------------------- number formats -----------
+// E4M3 (fn): bias 7, max 448 = 0x7E.  Round to nearest even, saturate (finite t >= 0 only).
+__device__ inline uint32_t e4m3_encode(float t) {
+  if (t >= 448.0f) return 0x7Eu;  // [448, 464) rounds to 448; above saturates
+  const uint32_t u = __float_as_uint(t);
+  const int ef = (int)(u >> 23);  // biased exponent (t >= 0)
+  if (ef < 127 - 6) {             // below 2^-6: subnormal E4M3, quantum 2^-9
+    return (uint32_t)__builtin_rintf(t * 512.0f);  // exact scaling; 8 == code 0x08 (2^-6)
+  }
+  const uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) & ~0xFFFFFu;  // RNE to 3 mantissa bits
+  return ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));             // (e - 127 + 7) << 3 | m
+}
+
+__device__ inline float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  if (e == 0) return (float)m * (1.0f / 512.0f);
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// E8M0 exponent of an MXFP4 block: floor(log2 amax) - 2 clamped to [-127, 127].  Zero and
+// fp32-subnormal amax (exponent field 0) land on the clamp.
+__device__ inline int mx_exponent(float amax) {
+  const int ef = (int)(__float_as_uint(amax) >> 23);
+  const int e = ef - 129;
+  return e < -127 ? -127 : e;
+}
+
+// Two E2M1 codes (RNE, ties to even code, saturating, sign kept) into byte SEL of `old`;
+// `a` goes to the low nibble.  Hardware conversion with unit scale.
+template <int SEL>
+__device__ inline uint32_t cvt_fp4x2(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// Eight E2M1 codes of v[0..7] (already scaled) packed into one dword, element 0 lowest.
+__device__ inline uint32_t pack8_fp4(const float* v) {
+  uint32_t w = 0;
+  w = cvt_fp4x2<0>(w, v[0], v[1]);
+  w = cvt_fp4x2<1>(w, v[2], v[3]);
+  w = cvt_fp4x2<2>(w, v[4], v[5]);
+  w = cvt_fp4x2<3>(w, v[6], v[7]);
+  return w;
+}
+__device__ inline uint32_t pack4_fp4(const float* v) {
+  uint32_t w = 0;
+  w = cvt_fp4x2<0>(w, v[0], v[1]);
+  w = cvt_fp4x2<1>(w, v[2], v[3]);
+  return w;
+}
+
+// Per-block quantization parameters.  `mul` scales elements before the E2M1 conversion;
+// `dead` zeroes the block's codes; `sbyte` is the stored scale code.
+struct BlockQ {
+  float mul;
+  uint32_t sbyte;
+  bool dead;
+};
+
+template <int FMT>
+__device__ inline BlockQ block_params(float amax, float s_dec) {
+  BlockQ q;
+  if (FMT == AVERIS_MXFP4) {
+    const int e = mx_exponent(amax);
+    q.mul = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, exact
+    q.sbyte = (uint32_t)(e + 127);
+    q.dead = !(amax > 0.0f);
+  } else {
+    // e_b = E4M3(fl(fl(a/6)/s_dec)); S = fl(val(e_b) * s_dec); mul = fl(1/S)
+    if (!(s_dec > 0.0f)) {
+      q.mul = 0.0f; q.sbyte = 0; q.dead = true;
+      return q;
+    }
+    const float t = __fdiv_rn(__fdiv_rn(amax, 6.0f), s_dec);
+    const uint32_t e = e4m3_encode(t);
+    const float S = __fmul_rn(e4m3_value(e), s_dec);
+    q.sbyte = e;
+    q.dead = (e == 0u) || !(S >= 1.17549435e-38f);
+    q.mul = q.dead ? 0.0f : __fdiv_rn(1.0f, S);
+  }
+  return q;
+}
+
+__device__ inline float nvfp4_tensor_scale(float amax) { return __fdiv_rn(amax, 2688.0f); }
+
+// ---------------------------------------------------------------- wave helpers -------------
+__device__ inline float wave_xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
+
+// Workgroup-id remap so that consecutive logical tiles run on the same XCD (workgroups are
+// dispatched round-robin over the 8 XCDs); partial cache lines written by neighbouring tiles
+// then meet in that XCD's L2.
+__device__ inline int xcd_remap(int bid, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int xcd = bid & 7, idx = bid >> 3;
+  return xcd * q + (xcd < r ? xcd : r) + idx;
+}
+
+}  // namespace av

@@ -1,0 +1,181 @@
+/*
+ * averis.h -- C ABI of libaveris.so: the Averis mean-residual split before blockwise FP4
+ * quantization, and the three quantized training GEMMs with the mean terms added back,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "The Curse and Blessing of Mean Bias in FP4-Quantized LLM Training"
+ * (arXiv 2603.10444).  Passages cited by page key:
+ *   [rainbus]    explainer "均值偏置的诅咒与祝福：FP4量化大语言模型训练" (paper.rainbus.top)
+ *   [paperlayer] source-linked summary of v2 (paperlayer.ai), sections 1-6 and appendices
+ *   [chatpaper]  v1 abstract (chatpaper.ai)
+ *
+ * For activations X [l, m] (l = b*s tokens) and output gradients D [l, n] of a linear layer
+ * with weight W [m, n] ([rainbus] 方法步骤详情):
+ *   mu_X = (1/l) 1^T X,   X_R = X - 1 mu_X          (same for D)
+ *   Y     = 1 (Q(mu_X) Q(W))   + Q(X_R) Q(W)
+ *   dX    = 1 (Q(mu_D) Q(W)^T) + Q(D_R) Q(W)^T
+ *   dW    = Q(X_R)^T Q(D_R)    + l Q(mu_X)^T Q(mu_D)   (cross terms vanish, dropped)
+ * where Q is a blockwise FP4 (E2M1) quantizer applied independently to each operand, with
+ * blocks along that operand's own GEMM reduction axis.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent), 16-byte aligned.
+ *    Host pointers are named h_*.  The caller owns every buffer; the library never
+ *    allocates, frees or keeps device memory between calls.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *    returns without waiting.  Inputs must stay valid until the stream reaches the work.
+ *    Calls on different streams are independent; calls sharing a workspace must be ordered.
+ *  - Arguments are validated before anything is enqueued: on any error a non-zero status is
+ *    returned, nothing is launched and no output is touched.  A failed launch returns
+ *    AVERIS_E_HIP.  Faults inside kernels surface at the caller's next synchronisation.
+ *  - Inputs must be finite.  Results for NaN/Inf inputs are unspecified.
+ *  - Results are deterministic: no floating-point atomics; every reduction has a fixed order.
+ */
+#ifndef AVERIS_H
+#define AVERIS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AVERIS_ABI_VERSION 1
+
+typedef enum {
+  AVERIS_OK = 0,
+  AVERIS_E_NULL = 1,      /* a required pointer is NULL */
+  AVERIS_E_SHAPE = 2,     /* sizes inconsistent or outside the documented preconditions */
+  AVERIS_E_ALIGN = 3,     /* pointer or leading dimension not 16-byte aligned */
+  AVERIS_E_DTYPE = 4,     /* unknown element type */
+  AVERIS_E_FORMAT = 5,    /* unknown FP4 format, or operands of different formats */
+  AVERIS_E_FLAGS = 6,     /* unknown or contradictory flag bits */
+  AVERIS_E_WORKSPACE = 7, /* workspace NULL or smaller than the *_workspace_size query */
+  AVERIS_E_HIP = 8        /* a HIP runtime call or kernel launch failed */
+} averis_status;
+
+/* Block formats (readings of the pages' "blockwise FP4 quantization", [rainbus] 块量化):
+ *  AVERIS_NVFP4: 16-element blocks, E4M3 block scale, plus an fp32 tensor decode scale
+ *                s_dec = amax(operand) / (6 * 448).  Per block b with max magnitude a_b:
+ *                e_b = E4M3(fl(fl(a_b / 6) / s_dec)); elements x -> E2M1(fl(x * fl(1 / fl(val(e_b) * s_dec)))).
+ *                Decode: e2m1(code) * val(e_b) * s_dec.
+ *  AVERIS_MXFP4: 32-element blocks, E8M0 scale 2^E with E = floor(log2 a_b) - 2 clamped to
+ *                [-127, 127], stored as E + 127; elements x -> E2M1(x * 2^-E).  Decode:
+ *                e2m1(code) * 2^E.  This is the format gfx950's scaled MFMA consumes natively.
+ * E2M1 rounding is to nearest, ties to the even code, saturating at 6; the sign of a value
+ * that rounds to zero is kept (code 0x8).  A block whose scale is zero (all-zero block, or
+ * NVFP4 e_b == 0 or decode scale below 2^-126) has all-zero codes. */
+typedef enum { AVERIS_NVFP4 = 1, AVERIS_MXFP4 = 2 } averis_format;
+
+typedef enum { AVERIS_F32 = 0, AVERIS_BF16 = 1 } averis_dtype;
+
+/* Flag bits. */
+#define AVERIS_SPLIT       (1u << 0) /* subtract the column mean before quantizing (Averis);
+                                        without it the quantizer is the vanilla one (and the
+                                        one used for weights) */
+#define AVERIS_HADAMARD16  (1u << 1) /* rotate every 16-block along K by H16/4 (Sylvester
+                                        order) after the subtraction ([rainbus] Hadamard变换,
+                                        技术新颖性: Averis and Hadamard compose) */
+#define AVERIS_MEAN_GIVEN  (1u << 2) /* split_quant: `mean` is an input, not computed */
+#define AVERIS_ACCUMULATE  (1u << 4) /* bwd_dw: dW += result instead of dW = result */
+
+/* A quantized operand [outer, k] with blocks along k (K-inner, row-major).
+ *   codes:        device uint8 [outer][k_pad / 2]; element 2i in bits 3:0, 2i+1 in bits 7:4.
+ *   scales:       device uint8 [outer][k_pad / g]; g = 16 (E4M3 codes) or 32 (E8M0 codes).
+ *   tensor_scale: device fp32 s_dec (NVFP4; one per group for grouped operands); NULL for MXFP4.
+ *   k_pad:        storage length along k = k rounded up to a multiple of 128; elements in
+ *                 [k, k_pad) hold code 0 and their blocks scale byte 0.
+ *   flags:        AVERIS_HADAMARD16 if the operand was rotated along k.
+ * The caller fills every field before a call that writes the operand, and the library checks
+ * outer/k/k_pad/fmt/flags against what the call expects. */
+typedef struct averis_qtensor {
+  uint8_t *codes;
+  uint8_t *scales;
+  float *tensor_scale;
+  int64_t outer;
+  int64_t k;
+  int64_t k_pad;
+  int32_t fmt;
+  uint32_t flags;
+} averis_qtensor;
+
+int32_t averis_abi_version(void);
+const char *averis_status_string(int32_t status);
+
+/* -----------------------------------------------------------------------------------------
+ * averis_split_quant -- column statistics, mean, subtraction, optional Hadamard, FP4 quant.
+ * [rainbus] 方法步骤详情 (mu_X = (1/l) 1^T X, X_R = X - 1 mu_X, Q_b applied independently to
+ * the mean and the residual); [paperlayer] §3 Method (the mean matrix is broadcast, never
+ * materialized: X_R exists only as the quantized operands written here).
+ *
+ *  x      device [rows, cols] row-major, element type xdt, leading dimension ldx (elements).
+ *         rows >= 0; cols > 0 and cols % 128 == 0; ldx >= cols, ldx * elem_size % 16 == 0.
+ *  flags  AVERIS_SPLIT, AVERIS_HADAMARD16, AVERIS_MEAN_GIVEN (requires SPLIT).
+ *  mean   device fp32 [cols].  With SPLIT: written with mu (fp32 of the fixed-order fp64 sum
+ *         divided by rows; rows == 0 gives 0), or read if MEAN_GIVEN.  Without SPLIT: unused
+ *         (may be NULL).
+ *  q_row  [outer = rows, k = cols] operand (the K = features layout used by fwd and dX), or NULL.
+ *  q_col  [outer = cols, k = rows] operand (the K = tokens layout used by dW), or NULL.  Rows
+ *         [rows, k_pad) are zero residuals.
+ *  q_mean [outer = 1, k = cols] quantized mean (own tensor scale); required with SPLIT,
+ *         must be NULL without it.
+ * With NVFP4 each written operand gets the tensor scale of its own amax (after rotation).
+ * At least one of q_row / q_col must be given.
+ * ----------------------------------------------------------------------------------------- */
+size_t averis_split_quant_workspace_size(int64_t rows, int64_t cols, int32_t fmt, uint32_t flags);
+
+int32_t averis_split_quant(const void *x, int32_t xdt, int64_t rows, int64_t cols, int64_t ldx,
+                           int32_t fmt, uint32_t flags, float *mean,
+                           const averis_qtensor *q_row, const averis_qtensor *q_col,
+                           const averis_qtensor *q_mean, void *ws, size_t ws_bytes, void *stream);
+
+/* -----------------------------------------------------------------------------------------
+ * averis_linear_fwd -- Y = 1 (Q(mu_X) Q(W)) + Q(X_R) Q(W)   ([rainbus] 方法步骤详情, forward)
+ *  xr    [outer = l, k = m]  (q_row of split_quant(X))
+ *  mu_x  [outer = 1, k = m]  (q_mean of split_quant(X)), or NULL for the vanilla GEMM
+ *  w     [outer = n, k = m]  (q_col of split_quant(W [m, n]) without SPLIT)
+ *  y     device [l, n] row-major, element type ydt, leading dimension ldy >= n.
+ * All operands share fmt and the HADAMARD16 bit.  m % 128 == 0.  The mean term is
+ * computed once per call as a GEMV and added to every row in the GEMM epilogue.
+ * ----------------------------------------------------------------------------------------- */
+size_t averis_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t fmt);
+
+int32_t averis_linear_fwd(const averis_qtensor *xr, const averis_qtensor *mu_x,
+                          const averis_qtensor *w, void *y, int32_t ydt, int64_t ldy,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* -----------------------------------------------------------------------------------------
+ * averis_linear_bwd_dx -- dX = 1 (Q(mu_D) Q(W)^T) + Q(D_R) Q(W)^T   ([rainbus] 方法步骤详情)
+ *  dr    [outer = l, k = n]  (q_row of split_quant(D))
+ *  mu_d  [outer = 1, k = n]  or NULL (vanilla)
+ *  w     [outer = m, k = n]  (q_row of split_quant(W [m, n]) without SPLIT)
+ *  dx    device [l, m], element type dxdt, leading dimension lddx >= m.
+ * ----------------------------------------------------------------------------------------- */
+int32_t averis_linear_bwd_dx(const averis_qtensor *dr, const averis_qtensor *mu_d,
+                             const averis_qtensor *w, void *dx, int32_t dxdt, int64_t lddx,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* -----------------------------------------------------------------------------------------
+ * averis_linear_bwd_dw -- dW = Q(X_R)^T Q(D_R) + l Q(mu_X)^T Q(mu_D)   ([rainbus] 方法步骤详情:
+ * the cross terms vanish because the residuals have zero column means, so only two
+ * quantized GEMMs are needed).
+ *  xr_t  [outer = m, k = l]  (q_col of split_quant(X))
+ *  dr_t  [outer = n, k = l]  (q_col of split_quant(D))
+ *  mu_x, mu_d  quantized means, both or neither (NULL, NULL = vanilla: no rank-one term).
+ *        If they carry HADAMARD16 the rotation is undone before the outer product.
+ *  l     the unpadded token count (the rank-one factor); must equal xr_t->k.
+ *  dw    device fp32 [m, n], leading dimension lddw >= n.  AVERIS_ACCUMULATE: dw += result.
+ * The token axis is split across workgroups with fp32 partials reduced in a fixed order.
+ * ----------------------------------------------------------------------------------------- */
+size_t averis_linear_bwd_dw_workspace_size(int64_t m, int64_t n, int64_t l, int32_t fmt);
+
+int32_t averis_linear_bwd_dw(const averis_qtensor *xr_t, const averis_qtensor *dr_t,
+                             const averis_qtensor *mu_x, const averis_qtensor *mu_d, int64_t l,
+                             float *dw, int64_t lddw, uint32_t flags, void *ws, size_t ws_bytes,
+                             void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AVERIS_H */

@@ -1,0 +1,150 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every function that
+include/averis.h declares, and rejects bad arguments with the documented status before
+enqueuing anything (these calls return before any HIP runtime call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import fp4_quantized_amd.averis as av
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "averis.h")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_FORMAT, E_FLAGS, E_WORKSPACE = range(8)
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced by the validation paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(averis_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 9
+    nm = subprocess.run(["nm", "-D", "--defined-only", av.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (averis_\w+)", nm))
+    assert set(names) <= exported, set(names) - exported
+    assert set(names) == set(av.EXPORTS)
+    L = av.lib()
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_abi_version_and_status_strings():
+    L = av.lib()
+    assert L.averis_abi_version() == 1
+    for s in range(9):
+        assert L.averis_status_string(s)
+    assert L.averis_status_string(0) == b"ok"
+
+
+def q(outer, k, fmt=av.NVFP4, flags=0, codes=FAKE, scales=FAKE, ts=FAKE):
+    kp = (k + 127) // 128 * 128
+    return av.CQTensor(codes, scales, ts, outer, k, kp, fmt, flags)
+
+
+def split(x=FAKE, xdt=av.BF16, rows=256, cols=128, ldx=128, fmt=av.NVFP4, flags=av.SPLIT, mean=FAKE,
+          q_row="auto", q_col="auto", q_mean="auto", ws=FAKE, ws_bytes=1 << 30):
+    L = av.lib()
+    if q_row == "auto":
+        q_row = q(rows, cols, fmt, flags & av.HADAMARD16)
+    if q_col == "auto":
+        q_col = q(cols, rows, fmt, flags & av.HADAMARD16)
+    if q_mean == "auto":
+        q_mean = q(1, cols, fmt, flags & av.HADAMARD16) if flags & av.SPLIT else None
+    ref = lambda t: ctypes.byref(t) if t is not None else None
+    return L.averis_split_quant(x, xdt, rows, cols, ldx, fmt, flags, mean, ref(q_row), ref(q_col), ref(q_mean),
+                                ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(xdt=7), E_DTYPE),
+    (dict(fmt=3), E_FORMAT),
+    (dict(flags=1 << 9), E_FLAGS),
+    (dict(flags=av.MEAN_GIVEN), E_FLAGS),
+    (dict(cols=100, ldx=100), E_SHAPE),
+    (dict(ldx=64), E_SHAPE),
+    (dict(rows=-1), E_SHAPE),
+    (dict(x=None), E_NULL),
+    (dict(x=FAKE + 4), E_ALIGN),
+    (dict(ldx=130), E_ALIGN),
+    (dict(q_row=None, q_col=None), E_NULL),
+    (dict(mean=None), E_NULL),
+    (dict(q_mean=None), E_NULL),
+    (dict(flags=0, q_mean=q(1, 128)), E_FLAGS),
+    (dict(ws=None), E_WORKSPACE),
+    (dict(ws_bytes=16), E_WORKSPACE),
+    (dict(q_row=q(255, 128)), E_SHAPE),
+    (dict(q_col=q(128, 256, av.MXFP4)), E_FORMAT),
+    (dict(q_row=q(256, 128, av.NVFP4, av.HADAMARD16)), E_FLAGS),
+    (dict(q_row=q(256, 128, ts=None)), E_NULL),
+    (dict(q_row=q(256, 128, codes=FAKE + 8)), E_ALIGN),
+])
+def test_split_quant_rejects(kw, status):
+    assert split(**kw) == status
+
+
+def test_split_quant_workspace_size():
+    L = av.lib()
+    assert L.averis_split_quant_workspace_size(8192, 1024, av.NVFP4, av.SPLIT) >= 32 * 1024 * 16
+    assert L.averis_split_quant_workspace_size(0, 1024, av.NVFP4, av.SPLIT) > 0
+    assert L.averis_split_quant_workspace_size(-1, 1024, av.NVFP4, av.SPLIT) == 0
+
+
+def lin(fn, a, mu, w, out=FAKE, odt=av.F32, ldo=None, ws=FAKE, wsb=1 << 30):
+    ref = lambda t: ctypes.byref(t) if t is not None else None
+    ldo = w.outer if ldo is None else ldo
+    return fn(ref(a), ref(mu), ref(w), out, odt, ldo, ws, wsb, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    ("mixed_fmt", E_FORMAT), ("k_mismatch", E_SHAPE), ("rot_mismatch", E_FLAGS), ("mu_shape", E_SHAPE),
+    ("bad_dtype", E_DTYPE), ("small_ld", E_SHAPE), ("null_out", E_NULL), ("no_ws", E_WORKSPACE),
+    ("k_not_128", E_SHAPE),
+])
+def test_linear_rejects(case, status):
+    L = av.lib()
+    a, mu, w = q(256, 512), q(1, 512), q(384, 512)
+    kw = {}
+    if case == "mixed_fmt":
+        w = q(384, 512, av.MXFP4)
+    elif case == "k_mismatch":
+        w = q(384, 256)
+    elif case == "rot_mismatch":
+        w = q(384, 512, flags=av.HADAMARD16)
+    elif case == "mu_shape":
+        mu = q(2, 512)
+    elif case == "bad_dtype":
+        kw["odt"] = 9
+    elif case == "small_ld":
+        kw["ldo"] = 100
+    elif case == "null_out":
+        kw["out"] = None
+    elif case == "no_ws":
+        kw["ws"] = None
+    elif case == "k_not_128":
+        a, mu, w = q(256, 96), q(1, 96), q(384, 96)
+    for fn in (L.averis_linear_fwd, L.averis_linear_bwd_dx):
+        assert lin(fn, a, mu, w, **kw) == status
+
+
+def test_bwd_dw_rejects():
+    L = av.lib()
+    ref = ctypes.byref
+    xr, dr, mx, md = q(512, 300), q(384, 300), q(1, 512), q(1, 384)
+    call = lambda xr=xr, dr=dr, mx=mx, md=md, l=300, dw=FAKE, ld=384, fl=0, ws=FAKE, wsb=1 << 30: \
+        L.averis_linear_bwd_dw(ref(xr), ref(dr), ref(mx) if mx else None, ref(md) if md else None, l, dw, ld, fl, ws,
+                               wsb, None)
+    assert call(fl=1 << 3) == E_FLAGS
+    assert call(l=299) == E_SHAPE
+    assert call(md=None) == E_NULL
+    assert call(mx=q(1, 500)) == E_SHAPE
+    assert call(ld=100) == E_SHAPE
+    assert call(dw=None) == E_NULL
+    assert call(wsb=100) == E_WORKSPACE
+    assert call(dr=q(384, 300, av.MXFP4)) == E_FORMAT
+    assert L.averis_linear_bwd_dw_workspace_size(512, 384, 300, av.NVFP4) > 0

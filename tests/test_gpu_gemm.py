@@ -1,0 +1,117 @@
+"""GPU parity of the three quantized GEMMs (forward, input gradient, weight gradient) against
+the CPU oracle's exact (fp64) products of the dequantized operands.
+
+The GPU quantizes every operand; the same bytes are handed to the oracle (whose own
+quantization of the same inputs is checked bit-exact in test_gpu_quant.py), and fp32 outputs
+must be within 1e-5 relative Frobenius error.  bf16 outputs are checked at bf16's own
+rounding (2^-8 relative per element).
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp4_quantized_amd.averis as av
+from fp4_quantized_amd import workloads
+from oracle import averis_oracle as O
+from tests.gpu_util import device, rel_fro, to_oracle
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [(av.NVFP4, "nvfp4"), (av.MXFP4, "mxfp4")]
+TOL = 1e-5
+
+
+def quantize_layer(lin, fmt, hadamard, dev, split=True):
+    dt = lin.dtype
+    x = workloads.to_torch(lin.x, dt, dev)
+    d = workloads.to_torch(lin.d, dt, dev)
+    w = workloads.to_torch(lin.w, dt, dev)
+    sx = av.split_quant(x, fmt, split=split, hadamard=hadamard)
+    sd = av.split_quant(d, fmt, split=split, hadamard=hadamard)
+    sw = av.split_quant(w, fmt, split=False, hadamard=hadamard)
+    return sx, sd, sw
+
+
+def check_layer(lin, fmt, hadamard, tag, split=True, out_dtype=torch.float32):
+    dev = device()
+    print(f"case {tag} l={lin.x.shape[0]} m={lin.x.shape[1]} n={lin.d.shape[1]} fmt={fmt} h16={hadamard} "
+          f"split={split} out={out_dtype}", flush=True)
+    l = lin.x.shape[0]
+    sx, sd, sw = quantize_layer(lin, fmt, hadamard, dev, split)
+    mx = sx["mean_q"] if split else None
+    md = sd["mean_q"] if split else None
+    y = av.linear_fwd(sx["row"], mx, sw["col"], out_dtype)
+    dx = av.linear_bwd_dx(sd["row"], md, sw["row"], out_dtype)
+    dw = av.linear_bwd_dw(sx["col"], sd["col"], mx, md, l)
+    torch.cuda.synchronize()
+    omx = to_oracle(mx) if split else None
+    omd = to_oracle(md) if split else None
+    y_ref = O.linear_fwd(to_oracle(sx["row"]), omx, to_oracle(sw["col"]))
+    dx_ref = O.linear_bwd_dx(to_oracle(sd["row"]), omd, to_oracle(sw["row"]))
+    dw_ref = O.linear_bwd_dw(to_oracle(sx["col"]), to_oracle(sd["col"]), omx, omd, l)
+    outs = [("Y", y, y_ref), ("dX", dx, dx_ref), ("dW", dw, dw_ref)]
+    for name, got, ref in outs:
+        g = got.float().cpu().numpy()
+        assert g.shape == ref.shape, (tag, name)
+        if got.dtype == torch.bfloat16:
+            bad = np.abs(g - ref) > 2.0 ** -8 * np.abs(ref) + 1e-30 + 1e-5 * np.abs(ref).max()
+            assert not bad.any(), f"{tag} {name}: {bad.sum()} bf16 outputs off"
+        else:
+            err = rel_fro(g, ref)
+            assert err <= TOL, f"{tag} {name}: relative Frobenius error {err:.3e}"
+    return y, dx, dw
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+def test_tiny_forward(fmt, fname):
+    dev = device()
+    lin = workloads.tiny(0)
+    x = workloads.to_torch(lin.x, "f32", dev)
+    w = workloads.to_torch(lin.w, "f32", dev)
+    sx = av.split_quant(x, fmt)
+    sw = av.split_quant(w, fmt, split=False)
+    y = av.linear_fwd(sx["row"], sx["mean_q"], sw["col"])
+    torch.cuda.synchronize()
+    ref = O.linear_fwd(to_oracle(sx["row"]), to_oracle(sx["mean_q"]), to_oracle(sw["col"]))
+    assert rel_fro(y.cpu().numpy(), ref) <= TOL
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+@pytest.mark.parametrize("hadamard", [False, True])
+@pytest.mark.parametrize("split", [True, False])
+def test_small_layer(fmt, fname, hadamard, split):
+    # ragged: l = 1000 tokens (not a tile multiple), m = 256, n = 384 (not a 128-tile multiple of 256)
+    lin = workloads.up_proj_like(21, 1000, 256, 384)
+    check_layer(lin, fmt, hadamard, f"small-{fname}-h{int(hadamard)}-s{int(split)}", split)
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+@pytest.mark.parametrize("l", [1, 17, 130])
+def test_few_tokens(fmt, fname, l):
+    lin = workloads.up_proj_like(22, l, 128, 256)
+    check_layer(lin, fmt, False, f"few-{fname}-{l}")
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+def test_bf16_outputs(fmt, fname):
+    lin = workloads.up_proj_like(23, 512, 256, 384)
+    check_layer(lin, fmt, False, f"bf16-{fname}", out_dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+def test_up_proj_full_size(fmt, fname):
+    # l = 8192, m = 1024, n = 3072: full outputs of Y, dX and dW against the oracle
+    check_layer(workloads.up_proj(), fmt, False, f"up_proj-{fname}")
+
+
+def test_dw_accumulate_and_determinism():
+    dev = device()
+    lin = workloads.up_proj_like(24, 3000, 256, 384)
+    sx, sd, _ = quantize_layer(lin, av.MXFP4, False, dev)
+    base = torch.randn(256, 384, device=dev)
+    dw1 = av.linear_bwd_dw(sx["col"], sd["col"], sx["mean_q"], sd["mean_q"], 3000)
+    dw2 = av.linear_bwd_dw(sx["col"], sd["col"], sx["mean_q"], sd["mean_q"], 3000)
+    acc = av.linear_bwd_dw(sx["col"], sd["col"], sx["mean_q"], sd["mean_q"], 3000, dw=base.clone(), accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dw1, dw2)
+    assert torch.allclose(acc, base + dw1, rtol=1e-6, atol=1e-6)

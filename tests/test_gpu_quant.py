@@ -1,0 +1,113 @@
+"""GPU parity of averis_split_quant against the CPU oracle.
+
+The mean must match the oracle's fp64 mean within 1e-6 (relative to |mu| + mean |x|); given
+the GPU's fp32 mean, every packed code, block scale and tensor scale must be bit-exact, in
+both layouts and for the quantized mean.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp4_quantized_amd.averis as av
+from fp4_quantized_amd import workloads
+from oracle import averis_oracle as O
+from tests.gpu_util import assert_q_equal, device, mean_ok
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [(av.NVFP4, "nvfp4"), (av.MXFP4, "mxfp4")]
+
+
+def run_case(x_np, dtype, fmt, split=True, hadamard=False, mean=None, tag=""):
+    dev = device()
+    print(f"case {tag} shape={x_np.shape} dtype={dtype} fmt={fmt} split={split} h16={hadamard}", flush=True)
+    x = workloads.to_torch(x_np, dtype, dev)
+    m_t = torch.from_numpy(mean).to(dev) if mean is not None else None
+    g = av.split_quant(x, fmt, split=split, hadamard=hadamard, mean=m_t)
+    torch.cuda.synchronize()
+    mu_gpu = g["mean"].cpu().numpy() if split else None
+    if split and mean is None:
+        assert mean_ok(mu_gpu, x_np), f"{tag}: mean outside tolerance"
+    if mean is not None:
+        np.testing.assert_array_equal(mu_gpu, mean)
+    o = O.split_quant(x_np, fmt, split=split, hadamard=hadamard, mean=mu_gpu)
+    assert_q_equal(g["row"], o["row"], f"{tag} row layout")
+    assert_q_equal(g["col"], o["col"], f"{tag} column layout")
+    if split:
+        assert_q_equal(g["mean_q"], o["mean"], f"{tag} quantized mean")
+    return g, o
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+@pytest.mark.parametrize("split", [True, False])
+@pytest.mark.parametrize("hadamard", [False, True])
+def test_tiny_fp32(fmt, fname, split, hadamard):
+    lin = workloads.tiny(0)
+    run_case(lin.x, "f32", fmt, split, hadamard, tag=f"tiny-{fname}")
+    run_case(lin.w, "f32", fmt, False, hadamard, tag=f"tiny-w-{fname}")
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+@pytest.mark.parametrize("hadamard", [False, True])
+@pytest.mark.parametrize("rows", [1000, 1, 17, 64, 129, 320])
+def test_ragged_bf16(fmt, fname, hadamard, rows):
+    # 384 columns = 1.5 column tiles of 256 bf16; rows not a multiple of the 64-row tile
+    lin = workloads.up_proj_like(11, rows, 384, 128)
+    run_case(lin.x, "bf16", fmt, True, hadamard, tag=f"ragged-{fname}-{rows}")
+    run_case(lin.d, "bf16", fmt, True, hadamard, tag=f"ragged-d-{fname}-{rows}")
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+def test_zero_rows(fmt, fname):
+    run_case(np.zeros((0, 256), np.float32), "bf16", fmt, True, False, tag=f"empty-{fname}")
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+@pytest.mark.parametrize("hadamard", [False, True])
+def test_degenerate_inputs(fmt, fname, hadamard):
+    rng = np.random.default_rng(5)
+    mu = workloads._round(rng.standard_normal(256) * 8, "bf16")
+    const = np.repeat(mu[None, :], 200, axis=0)            # residual exactly 0 everywhere
+    g, _ = run_case(const, "bf16", fmt, True, hadamard, tag=f"constant-cols-{fname}")
+    assert not g["row"].codes.any().item() and not g["col"].codes.any().item()
+    run_case(np.zeros((96, 128), np.float32), "f32", fmt, True, hadamard, tag=f"zeros-{fname}")
+    spikes = workloads._round(rng.standard_normal((300, 256)), "bf16")
+    spikes[:, 7] *= 1000.0
+    spikes[13, 100] = -3e4
+    run_case(workloads._round(spikes, "bf16"), "bf16", fmt, True, hadamard, tag=f"spikes-{fname}")
+    tiny_vals = workloads._round(rng.standard_normal((128, 128)) * 1e-30, "f32")
+    run_case(tiny_vals, "f32", fmt, True, hadamard, tag=f"tiny-magnitudes-{fname}")
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+def test_mean_given(fmt, fname):
+    lin = workloads.up_proj_like(12, 300, 256, 128)
+    mean = (lin.x.astype(np.float64).mean(axis=0) + 0.25).astype(np.float32)
+    run_case(lin.x, "bf16", fmt, True, False, mean=mean, tag=f"mean-given-{fname}")
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+def test_up_proj_full_size(fmt, fname):
+    # l = 8192 tokens, m = 1024, n = 3072: X, D and W in both layouts, full comparison
+    lin = workloads.up_proj()
+    run_case(lin.x, "bf16", fmt, True, False, tag=f"up_proj-X-{fname}")
+    run_case(lin.d, "bf16", fmt, True, False, tag=f"up_proj-D-{fname}")
+    run_case(lin.w, "bf16", fmt, False, False, tag=f"up_proj-W-{fname}")
+
+
+def test_down_proj_hadamard_nvfp4_full_size():
+    # l = 16384, m = 3072 SwiGLU-like input with the 16x16 Hadamard on the residual
+    lin = workloads.down_proj()
+    run_case(lin.x, "bf16", av.NVFP4, True, True, tag="down_proj-X-nvfp4-h16")
+
+
+def test_deterministic():
+    dev = device()
+    lin = workloads.up_proj_like(13, 2000, 512, 128)
+    x = workloads.to_torch(lin.x, "bf16", dev)
+    a = av.split_quant(x, av.NVFP4)
+    b = av.split_quant(x, av.NVFP4)
+    torch.cuda.synchronize()
+    assert torch.equal(a["mean"], b["mean"])
+    for k in ("row", "col", "mean_q"):
+        assert torch.equal(a[k].codes, b[k].codes) and torch.equal(a[k].scales, b[k].scales)
