@@ -136,13 +136,28 @@ def _workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+def split_quant_outputs(rows, cols, fmt, split=True, hadamard=False, row=True, col=True, device="cuda"):
+    """Allocate the outputs of split_quant (for callers that reuse them, e.g. under graph capture)."""
+    return dict(mean=torch.empty(cols, dtype=torch.float32, device=device) if split else None,
+                row=empty_qtensor(rows, cols, fmt, hadamard, device) if row else None,
+                col=empty_qtensor(cols, rows, fmt, hadamard, device) if col else None,
+                mean_q=empty_qtensor(1, cols, fmt, hadamard, device) if split else None)
+
+
+def split_quant_workspace(rows, cols, fmt, split=True, hadamard=False, device="cuda"):
+    flags = (SPLIT if split else 0) | (HADAMARD16 if hadamard else 0)
+    return _workspace(lib().averis_split_quant_workspace_size(rows, cols, fmt, flags), device)
+
+
 def split_quant(x: torch.Tensor, fmt: int, split: bool = True, hadamard: bool = False,
-                mean: torch.Tensor | None = None, row: bool = True, col: bool = True, stream=None):
+                mean: torch.Tensor | None = None, row: bool = True, col: bool = True, stream=None,
+                out=None, ws=None):
     """Mean, residual and FP4 quantization of x [rows, cols] (bf16 or fp32, row-major).
 
     Returns dict(mean=fp32 [cols] or None, row=QTensor [rows, cols] or None,
     col=QTensor [cols, rows] or None, mean_q=QTensor [1, cols] or None).
-    `mean` given: used instead of the column mean (MEAN_GIVEN)."""
+    `mean` given: used instead of the column mean (MEAN_GIVEN).  `out` / `ws`: preallocated
+    outputs (from split_quant_outputs) and workspace (from split_quant_workspace)."""
     assert x.dim() == 2 and x.is_cuda
     rows, cols = x.shape
     assert rows == 0 or x.stride(1) == 1, "x must be row-major"
@@ -150,48 +165,62 @@ def split_quant(x: torch.Tensor, fmt: int, split: bool = True, hadamard: bool = 
     dev = x.device
     flags = (SPLIT if split else 0) | (HADAMARD16 if hadamard else 0) | \
         (MEAN_GIVEN if (split and mean is not None) else 0)
-    mu = None
-    if split:
-        mu = mean.contiguous() if mean is not None else torch.empty(cols, dtype=torch.float32, device=dev)
-    q_row = empty_qtensor(rows, cols, fmt, hadamard, dev) if row else None
-    q_col = empty_qtensor(cols, rows, fmt, hadamard, dev) if col else None
-    q_mean = empty_qtensor(1, cols, fmt, hadamard, dev) if split else None
+    if out is None:
+        out = split_quant_outputs(rows, cols, fmt, split, hadamard, row, col, dev)
+    if split and mean is not None:
+        out = dict(out, mean=mean.contiguous())
+    mu = out["mean"]
+    if ws is None:
+        ws = split_quant_workspace(rows, cols, fmt, split, hadamard, dev)
     L = lib()
-    ws = _workspace(L.averis_split_quant_workspace_size(rows, cols, fmt, flags), dev)
     _check(L.averis_split_quant(x.data_ptr() if rows else None, _dtype_code(x), rows, cols, ldx, fmt,
-                                flags, mu.data_ptr() if mu is not None else None, _ptr(q_row), _ptr(q_col),
-                                _ptr(q_mean), ws.data_ptr(), ws.numel(), _stream(stream)))
-    return dict(mean=mu, row=q_row, col=q_col, mean_q=q_mean)
+                                flags, mu.data_ptr() if mu is not None else None, _ptr(out["row"]),
+                                _ptr(out["col"]), _ptr(out["mean_q"]), ws.data_ptr(), ws.numel(),
+                                _stream(stream)))
+    return out
 
 
-def _linear(fn, a: QTensor, mu: QTensor | None, w: QTensor, out_dtype, stream):
+def linear_workspace(a: QTensor, w: QTensor):
+    return _workspace(lib().averis_linear_workspace_size(a.outer, w.outer, a.k_pad, a.fmt), a.codes.device)
+
+
+def _linear(fn, a: QTensor, mu: QTensor | None, w: QTensor, out_dtype, stream, out, ws):
     dev = a.codes.device
-    out = torch.empty((a.outer, w.outer), dtype=out_dtype, device=dev)
-    L = lib()
-    ws = _workspace(L.averis_linear_workspace_size(a.outer, w.outer, a.k_pad, a.fmt), dev)
+    if out is None:
+        out = torch.empty((a.outer, w.outer), dtype=out_dtype, device=dev)
+    if ws is None:
+        ws = linear_workspace(a, w)
     _check(fn(_ptr(a), _ptr(mu), _ptr(w), out.data_ptr() if out.numel() else None, _dtype_code(out), out.stride(0),
               ws.data_ptr(), ws.numel(), _stream(stream)))
     return out
 
 
-def linear_fwd(xr: QTensor, mu_x: QTensor | None, w: QTensor, out_dtype=torch.float32, stream=None):
+def linear_fwd(xr: QTensor, mu_x: QTensor | None, w: QTensor, out_dtype=torch.float32, stream=None,
+               out=None, ws=None):
     """Y [l, n] = 1 (Q(mu_X) Q(W)) + Q(X_R) Q(W); w is the [n, m] (K = m) weight operand."""
-    return _linear(lib().averis_linear_fwd, xr, mu_x, w, out_dtype, stream)
+    return _linear(lib().averis_linear_fwd, xr, mu_x, w, out_dtype, stream, out, ws)
 
 
-def linear_bwd_dx(dr: QTensor, mu_d: QTensor | None, w: QTensor, out_dtype=torch.float32, stream=None):
+def linear_bwd_dx(dr: QTensor, mu_d: QTensor | None, w: QTensor, out_dtype=torch.float32, stream=None,
+                  out=None, ws=None):
     """dX [l, m] = 1 (Q(mu_D) Q(W)^T) + Q(D_R) Q(W)^T; w is the [m, n] (K = n) weight operand."""
-    return _linear(lib().averis_linear_bwd_dx, dr, mu_d, w, out_dtype, stream)
+    return _linear(lib().averis_linear_bwd_dx, dr, mu_d, w, out_dtype, stream, out, ws)
+
+
+def linear_bwd_dw_workspace(xr_t: QTensor, dr_t: QTensor, l: int):
+    return _workspace(lib().averis_linear_bwd_dw_workspace_size(xr_t.outer, dr_t.outer, l, xr_t.fmt),
+                      xr_t.codes.device)
 
 
 def linear_bwd_dw(xr_t: QTensor, dr_t: QTensor, mu_x: QTensor | None, mu_d: QTensor | None, l: int,
-                  dw: torch.Tensor | None = None, accumulate: bool = False, stream=None):
+                  dw: torch.Tensor | None = None, accumulate: bool = False, stream=None, ws=None):
     """dW [m, n] = Q(X_R)^T Q(D_R) + l Q(mu_X)^T Q(mu_D) (fp32), optionally accumulated into dw."""
     dev = xr_t.codes.device
     if dw is None:
         dw = torch.empty((xr_t.outer, dr_t.outer), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = linear_bwd_dw_workspace(xr_t, dr_t, l)
     L = lib()
-    ws = _workspace(L.averis_linear_bwd_dw_workspace_size(xr_t.outer, dr_t.outer, l, xr_t.fmt), dev)
     _check(L.averis_linear_bwd_dw(_ptr(xr_t), _ptr(dr_t), _ptr(mu_x), _ptr(mu_d), l,
                                   dw.data_ptr() if dw.numel() else None, dw.stride(0),
                                   ACCUMULATE if accumulate else 0, ws.data_ptr(), ws.numel(), _stream(stream)))
