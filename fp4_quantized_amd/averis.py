@@ -20,7 +20,7 @@ SPLIT = 1 << 0
 HADAMARD16 = 1 << 1
 MEAN_GIVEN = 1 << 2
 ACCUMULATE = 1 << 4
-KPAD = 128
+KPAD = 256
 BLOCK = {NVFP4: 16, MXFP4: 32}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaveris.so")
@@ -89,7 +89,7 @@ def _check(status):
 class QTensor:
     """Device buffers of one quantized operand [outer, k] (blocks along k)."""
     codes: torch.Tensor         # uint8 [outer, k_pad/2]
-    scales: torch.Tensor        # uint8 [outer, k_pad/g]
+    scales: torch.Tensor        # uint8, round_up(outer, 32) * k_pad/g bytes, tiled (see include/averis.h)
     tensor_scale: torch.Tensor | None  # fp32 [1] (NVFP4)
     outer: int
     k: int
@@ -109,8 +109,9 @@ class QTensor:
 def empty_qtensor(outer, k, fmt, rotated=False, device="cuda", groups=1):
     kp = (k + KPAD - 1) // KPAD * KPAD
     g = BLOCK[fmt]
+    rp = (outer + 31) // 32 * 32
     return QTensor(torch.empty((outer, kp // 2), dtype=torch.uint8, device=device),
-                   torch.empty((outer, kp // g), dtype=torch.uint8, device=device),
+                   torch.empty((rp, kp // g), dtype=torch.uint8, device=device),
                    torch.empty(groups, dtype=torch.float32, device=device) if fmt == NVFP4 else None,
                    outer, k, fmt, rotated)
 

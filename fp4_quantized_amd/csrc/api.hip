@@ -73,7 +73,7 @@ int32_t averis_split_quant(const void* x, int32_t xdt, int64_t rows, int64_t col
   if (flags & ~(AVERIS_SPLIT | AVERIS_HADAMARD16 | AVERIS_MEAN_GIVEN)) return AVERIS_E_FLAGS;
   const bool split = flags & AVERIS_SPLIT, h16 = flags & AVERIS_HADAMARD16, given = flags & AVERIS_MEAN_GIVEN;
   if (given && !split) return AVERIS_E_FLAGS;
-  if (rows < 0 || cols <= 0 || cols % kKPad != 0 || ldx < cols) return AVERIS_E_SHAPE;
+  if (rows < 0 || cols <= 0 || cols % kColMult != 0 || ldx < cols) return AVERIS_E_SHAPE;
   if (rows > ((int64_t)1 << 31) || cols > ((int64_t)1 << 24)) return AVERIS_E_SHAPE;
   if (!q_row && !q_col) return AVERIS_E_NULL;
   if (rows > 0 && !x) return AVERIS_E_NULL;
@@ -117,7 +117,7 @@ static int32_t linear_common(const averis_qtensor* a, const averis_qtensor* mu, 
   if ((st = check_in(w)) != AVERIS_OK) return st;
   if (!dtype_ok(odt)) return AVERIS_E_DTYPE;
   if (a->fmt != w->fmt) return AVERIS_E_FORMAT;
-  if (a->k != w->k || a->k % kKPad != 0) return AVERIS_E_SHAPE;
+  if (a->k != w->k) return AVERIS_E_SHAPE;
   if ((a->flags ^ w->flags) & AVERIS_HADAMARD16) return AVERIS_E_FLAGS;
   if (mu) {
     if ((st = check_in(mu)) != AVERIS_OK) return st;
@@ -125,7 +125,7 @@ static int32_t linear_common(const averis_qtensor* a, const averis_qtensor* mu, 
     if (mu->outer != 1 || mu->k != a->k) return AVERIS_E_SHAPE;
     if ((mu->flags ^ a->flags) & AVERIS_HADAMARD16) return AVERIS_E_FLAGS;
   }
-  if (ldo < w->outer) return AVERIS_E_SHAPE;
+  if (ldo < w->outer || w->outer % 8 != 0) return AVERIS_E_SHAPE;
   if (a->outer > 0 && w->outer > 0) {
     if (!out) return AVERIS_E_NULL;
     if (!aligned16(out) || (ldo * elem_size(odt)) % 16 != 0) return AVERIS_E_ALIGN;
@@ -167,7 +167,7 @@ int32_t averis_linear_bwd_dw(const averis_qtensor* xr_t, const averis_qtensor* d
     if ((mu_x->flags ^ mu_d->flags) & AVERIS_HADAMARD16) return AVERIS_E_FLAGS;
   }
   const int64_t m = xr_t->outer, n = dr_t->outer;
-  if (lddw < n) return AVERIS_E_SHAPE;
+  if (lddw < n || n % 8 != 0) return AVERIS_E_SHAPE;
   if (m > 0 && n > 0) {
     if (!dw) return AVERIS_E_NULL;
     if (!aligned16(dw) || (lddw * 4) % 16 != 0) return AVERIS_E_ALIGN;

@@ -8,10 +8,22 @@
 
 namespace av {
 
-constexpr int kKPad = 128;  // storage padding multiple along K
+constexpr int kKPad = 256;  // storage padding multiple along K (one GEMM K-step)
+constexpr int kColMult = 128;  // split_quant needs cols to be a multiple of this
 
-static inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
-static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Block scales are stored tiled for the GEMM: for each group of 32 rows and each 256-element
+// K-step the group's 32 x (256 / g) scale bytes are contiguous (row-major inside the piece), so
+// one K-step of a 128-row tile fetches 4 contiguous pieces instead of 128 scattered rows.
+// Byte offset of the scale of K-block `blk` (elements blk*g ..) of row `r`:
+__host__ __device__ inline int64_t scale_offset(int64_t r, int64_t blk, int64_t k_pad, int g) {
+  const int64_t spb = 256 / g;  // scale bytes per row per K-step
+  return ((r >> 5) * (k_pad >> 8) + blk / spb) * (32 * spb) + (r & 31) * spb + blk % spb;
+}
+// Bytes of a tiled scale array: rows padded to a multiple of 32.
+static inline int64_t scale_bytes(int64_t outer, int64_t k_pad, int g) { return round_up(outer, 32) * (k_pad / g); }
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));

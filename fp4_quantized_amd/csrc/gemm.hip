@@ -7,39 +7,55 @@
 //
 // One tile loop C[M, N] = A[M, K] B[N, K]^T over K-inner packed E2M1 operands:
 //   MXFP4: v_mfma_scale_f32_32x32x64_f8f6f4 consumes the codes and the E8M0 block scales
-//          directly (lane l holds row l % 32, K elements 32 (l / 32) .. + 31 = one MX block).
-//   NVFP4: E4M3 scales are not powers of two, which the scaled MFMA cannot apply, so each
-//          lane dequantizes its 32 codes exactly to bf16 (code x E4M3 value has <= 6
-//          significant bits) and issues four v_mfma_f32_32x32x16_bf16; the fp32 tensor scales
-//          multiply the accumulator in the epilogue.
+//          directly; a lane holds one row and 32 K elements (= one MX block) per instruction.
+//   NVFP4: E4M3 scales are not powers of two, which the scaled MFMA cannot apply (it uses only
+//          a scale's exponent), so each lane dequantizes its 32 codes exactly to bf16 (code x
+//          E4M3 value has <= 6 significant bits) and issues four v_mfma_f32_32x32x16_bf16; the
+//          fp32 tensor scales multiply the accumulator in the epilogue.
+// K order inside a K-step is permuted (the same way for A and B, so products pair up): lane
+// half h takes the step's 32-element chunks h*S .. h*S+S-1 for its S MFMAs, which makes its
+// block scales for the whole step one contiguous LDS load.
+// Pipeline: operands go straight from global memory to LDS (gfx950 global_load_lds) into a
+// ring of stages; while K-step i is multiplied, steps i+1 .. i+STAGES-1 are in flight.  One
+// barrier per K-step, no fence: each wave waits on its own vmcnt, then all meet at s_barrier.
 // Epilogue: out = alpha * acc + bias[col] + r1 * u[row] * v[col] (+ C when accumulating),
 // alpha = product of the operands' tensor decode scales (NVFP4) or 1.
+#include <cstdlib>
+
 #include "launch.h"
 
 namespace av {
 
-constexpr int kGemmThreads = 256;
-constexpr int BM = 128, BN = 128;
-constexpr int BKB = 128;           // bytes of codes per row per K-step (256 elements)
-constexpr int BKE = 2 * BKB;       // elements per K-step
-constexpr int LDS_ROW = BKB + 16;  // padded LDS row stride (bytes)
-
 struct GemmArgs {
-  const uint8_t* a_codes; const uint8_t* a_scales; int64_t lda_b; int64_t lds_a;  // row strides: bytes of codes, bytes of scales
-  const uint8_t* b_codes; const uint8_t* b_scales; int64_t ldb_b; int64_t lds_b;
+  const uint8_t* a_codes; const uint8_t* a_scales; int64_t lda_b;  // codes row stride (bytes); scales tiled
+  const uint8_t* b_codes; const uint8_t* b_scales; int64_t ldb_b;
   const float* a_ts; const float* b_ts;  // tensor decode scales (NVFP4) or nullptr
   int64_t M, N, K;                      // K = padded length (multiple of 128)
   void* c; int64_t ldc; int c_bf16;     // output (or split-K partials base when splits > 1)
   const float* bias;                    // [N] or nullptr
   const float* r1u; const float* r1v; float r1;  // rank-one term r1 * u[row] * v[col], or nullptr
+  // rank-one vectors decoded in the epilogue from unrotated quantized means (when r1u is null)
+  const uint8_t* mu_codes; const uint8_t* mu_scales; const float* mu_ts; int64_t mu_kpad;
+  const uint8_t* mv_codes; const uint8_t* mv_scales; const float* mv_ts; int64_t mv_kpad;
   int accumulate;
-  int splits; int64_t k_chunk;          // K range per split (multiple of BKE), partials at c + s * M * N
+  int splits; int64_t k_chunk;          // K range per split (multiple of the K-step), partials at c + s * M * N
   int tiles_m, tiles_n;
+  int group_m;                          // tile rows per group in the tile order (L2 locality)
 };
 
 __device__ inline uint32_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ inline float2 fp4x2_to_f32(uint32_t w, int sel) {
+  // exact decode of the two codes in byte `sel` (low nibble first), unit scale
+  switch (sel) {
+    case 0: { auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); return make_float2(r[0], r[1]); }
+    case 1: { auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); return make_float2(r[0], r[1]); }
+    case 2: { auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); return make_float2(r[0], r[1]); }
+    default: { auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); return make_float2(r[0], r[1]); }
+  }
 }
 
 // 32 E2M1 codes (16 bytes) times two block scales (elements 0-15: s0, 16-31: s1) -> 4 x 8 bf16.
@@ -51,210 +67,430 @@ __device__ inline void dequant32_bf16(const uint4& c, float s0, float s1, v8bf* 
     uint32_t h[4];
 #pragma unroll
     for (int bsel = 0; bsel < 4; ++bsel) {
-      float2 f;
-      switch (bsel) {
-        case 0: { auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 0); f = make_float2(r[0], r[1]); break; }
-        case 1: { auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 1); f = make_float2(r[0], r[1]); break; }
-        case 2: { auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 2); f = make_float2(r[0], r[1]); break; }
-        default: { auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[q], 1.0f, 3); f = make_float2(r[0], r[1]); break; }
-      }
+      const float2 f = fp4x2_to_f32(w[q], bsel);
       // exact products, so dropping the low 16 bits is an exact bf16 conversion
-      const uint32_t lo = __float_as_uint(f.x * s) >> 16, hi = __float_as_uint(f.y * s) & 0xFFFF0000u;
-      h[bsel] = lo | hi;
+      h[bsel] = (__float_as_uint(f.x * s) >> 16) | (__float_as_uint(f.y * s) & 0xFFFF0000u);
     }
     out[q] = __builtin_bit_cast(v8bf, make_uint4(h[0], h[1], h[2], h[3]));
   }
 }
 
+// Dequantized element k of a one-row operand (a quantized mean vector) with padded length
+// k_pad (fp32; exact for codes times an E8M0 scale, one rounding for NVFP4's decode scale).
 template <int FMT>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm(GemmArgs g) {
+__device__ inline float dq_one(const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t k, int64_t k_pad) {
   constexpr int G = FMT == AVERIS_MXFP4 ? 32 : 16;
-  constexpr int SB = BKE / G;  // scale bytes per row per K-step (8 or 16)
-  __shared__ __attribute__((aligned(16))) uint8_t sA[BM * LDS_ROW];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[BN * LDS_ROW];
-  __shared__ __attribute__((aligned(16))) uint8_t sSA[BM * SB];
-  __shared__ __attribute__((aligned(16))) uint8_t sSB[BN * SB];
+  const uint32_t byte = codes[k >> 1];
+  const uint32_t c = (k & 1) ? (byte >> 4) : (byte & 15u);
+  const float v = fp4x2_to_f32(c, 0).x;
+  const uint32_t s = scales[scale_offset(0, k / G, k_pad, G)];
+  if (FMT == AVERIS_MXFP4) return ldexpf(v, (int)s - 127);
+  return __fmul_rn(__fmul_rn(v, e4m3_value(s)), ts[0]);
+}
 
-  const int ntiles = g.tiles_m * g.tiles_n;
-  const int lin = xcd_remap(blockIdx.x, ntiles * g.splits);
-  const int split = lin / ntiles;
-  const int tile = lin % ntiles;
-  const int tm = tile / g.tiles_n, tn = tile % g.tiles_n;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t kb = (int64_t)split * g.k_chunk;
-  const int64_t ke = kb + g.k_chunk < g.K ? kb + g.k_chunk : g.K;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves, 64 x 64 each
+// Raw buffer resource over `bytes` bytes at `base`: loads at offsets >= bytes return zero,
+// which pads partial tiles (rows past M or N) with zero codes and zero scales.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// One wave-wide direct-to-LDS load: lane L's SIZE bytes from rsrc[voff + soff] land at lds + L * SIZE.
+template <int AUX>
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, AUX);
+}
+template <int AUX>
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, voff, soff, 0, AUX);
+}
+// Two fp32 values to packed bf16 (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+  const v2bf16 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// Wait until at most N vector-memory ops of this wave are outstanding and all its LDS ops are
+// done (gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
 
-  // global -> register staging: 16 KB of codes per operand = 4 x 16 B per thread
-  const int ld_chunk = tid & 7, ld_row = tid >> 3;  // 8 threads per 128-byte row, 32 rows per pass
-  uint4 ra[4], rb[4];
-  uint32_t rsa[SB / 8], rsb[SB / 8];  // scales: BM * SB bytes = 1 or 2 KB -> 4 or 8 bytes/thread
+// Tile order: consecutive logical tiles walk down a group of `gm` tile rows, then move one
+// tile column right.  With the XCD remap each XCD owns a contiguous run of logical tiles, so
+// it works on a compact (group rows x run / group columns) block and re-reads little of A or B
+// from beyond its L2.
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int gm, int& tm, int& tn) {
+  const int per_group = gm * tiles_n;
+  const int group = t / per_group, first_m = group * gm;
+  const int rows = tiles_m - first_m < gm ? tiles_m - first_m : gm;
+  const int r = t % per_group;
+  tm = first_m + r % rows;
+  tn = r / rows;
+}
 
-  auto gload = [&](int64_t k0) {
-    const int64_t kbyte = k0 / 2;
-    const bool kin = k0 + (int64_t)(ld_chunk + 1) * 32 <= ke;  // this 16-byte chunk (32 elems) in range
+// LDS row swizzle (16-byte slot index within a 128-byte row): conflict-free fragment reads of
+// 32 consecutive rows for 32- and 64-bank LDS.  Depends only on the row's low 4 bits.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int FMT, int WM, int WN, int TM, int TN, int STAGES, int AUX = 0>
+struct GemmCfg {
+  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  static constexpr int BKB = 128, BKE = 256;     // bytes / elements per row per K-step
+  static constexpr int G = FMT == AVERIS_MXFP4 ? 32 : 16;
+  static constexpr int SB = BKE / G;             // scale bytes per row per K-step (8 or 16)
+  static constexpr int PIECE = 32 * SB;          // tiled scale bytes of one 32-row group per K-step
+  static constexpr int NKK = BKE / 64;           // MFMA K-substeps per K-step
+  static constexpr int A_OFF = 0, B_OFF = BM * BKB, SA_OFF = (BM + BN) * BKB, SB_OFF = SA_OFF + BM * SB;
+  static constexpr int DUMMY_OFF = SB_OFF + BN * SB;            // sink for padding scale loads
+  static constexpr int STAGE = DUMMY_OFF + 256;
+  static constexpr int IA = BM / 8, IB = BN / 8;                // 1 KB code loads per step
+  static constexpr int ISA = BM * SB / 256, ISB = BN * SB / 256;  // 256-byte scale loads per step
+  // scale loads are padded to a multiple of the wave count (extra ones load zeros into the
+  // sink) so that every wave issues the same number of loads per step
+  static constexpr int ISA_P = (ISA + NW - 1) / NW * NW, ISB_P = (ISB + NW - 1) / NW * NW;
+  static_assert(IA % NW == 0 && IB % NW == 0, "code loads must split evenly over waves");
+  static constexpr int NLA = IA / NW, NLB = IB / NW, NLSA = ISA_P / NW, NLSB = ISB_P / NW;
+  static constexpr int LPS = NLA + NLB + NLSA + NLSB;          // load instructions per wave per step
+  static_assert(LPS * (STAGES - 2) < 64, "vmcnt range");
+  // epilogue staging: per wave a 32 x (TN * 32) fp32 tile, padded rows
+  static constexpr int EPI_LD = TN * 32 + 4;
+  static constexpr int EPI_WAVE = 32 * EPI_LD * 4;
+  static_assert((NW + 1) / 2 * EPI_WAVE <= STAGE, "epilogue staging must fit in two stages");
+};
+
+template <int FMT, int WM, int WN, int TM, int TN, int STAGES, int AUX = 0>
+struct GemmTile {
+  using C = GemmCfg<FMT, WM, WN, TM, TN, STAGES, AUX>;
+  __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+  int va[C::NLA], vb[C::NLB], vsa[C::NLSA], vsb[C::NLSB];  // per-lane byte offsets (loop invariant)
+  int ldsa[C::NLSA], ldsb[C::NLSB];                          // LDS destinations of the scale loads
+  int frag_off[C::NKK];   // lane's LDS byte offset of its fragment chunk for each substep
+  int scale_off;          // lane's LDS byte offset of its scale bytes within a fragment row block
+  int wave, wm, wn;
+  v16f acc[TM][TN];
+
+  __device__ __forceinline__ void setup(const GemmArgs& g, int64_t m0, int64_t n0) {
+    const int lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6; wm = wave / WN; wn = wave % WN;
+    const int fr = lane & 31, fk = lane >> 5;
+    // operands restricted to this tile's rows: offsets past the last row read as zero
+    const int64_t rows_a = g.M - m0 < C::BM ? g.M - m0 : C::BM, rows_b = g.N - n0 < C::BN ? g.N - n0 : C::BN;
+    ra = make_rsrc(g.a_codes + m0 * g.lda_b, rows_a * g.lda_b);
+    rb = make_rsrc(g.b_codes + n0 * g.ldb_b, rows_b * g.ldb_b);
+    // tiled scales: this tile's 32-row groups start at group m0 / 32; a group spans K / 256 pieces
+    const int64_t gstride = (g.K / C::BKE) * C::PIECE;
+    rsa = make_rsrc(g.a_scales + (m0 / 32) * gstride, ceil_div(rows_a, 32) * gstride);
+    rsb = make_rsrc(g.b_scales + (n0 / 32) * gstride, ceil_div(rows_b, 32) * gstride);
+    const int lr = lane >> 3, sl = lane & 7;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t ra_row = m0 + ld_row + 32 * i, rb_row = n0 + ld_row + 32 * i;
-      ra[i] = (kin && ra_row < g.M) ? *reinterpret_cast<const uint4*>(g.a_codes + ra_row * g.lda_b + kbyte + ld_chunk * 16) : make_uint4(0, 0, 0, 0);
-      rb[i] = (kin && rb_row < g.N) ? *reinterpret_cast<const uint4*>(g.b_codes + rb_row * g.ldb_b + kbyte + ld_chunk * 16) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < C::NLA; ++i) {
+      const int t = i * C::NW + wave, r = t * 8 + lr;
+      va[i] = (int)(r * g.lda_b) + ((sl ^ swz(r)) << 4);
     }
-    // scales: thread t covers row t / (256 / BM) ... one dword (4 scale bytes) per load
 #pragma unroll
-    for (int i = 0; i < SB / 8; ++i) {
-      const int idx = tid + i * kGemmThreads;     // dword index within the BM x SB tile
-      const int row = idx / (SB / 4), dw = idx % (SB / 4);
-      const int64_t kblk = k0 / G + dw * 4;        // first block of this dword
-      const bool sin = kblk * G + 4 * G <= ke;      // all 4 blocks inside the K range
-      const int64_t ar = m0 + row, br = n0 + row;
-      rsa[i] = (sin && ar < g.M) ? *reinterpret_cast<const uint32_t*>(g.a_scales + ar * g.lds_a + kblk) : 0u;
-      rsb[i] = (sin && br < g.N) ? *reinterpret_cast<const uint32_t*>(g.b_scales + br * g.lds_b + kblk) : 0u;
+    for (int i = 0; i < C::NLB; ++i) {
+      const int t = i * C::NW + wave, r = t * 8 + lr;
+      vb[i] = (int)(r * g.ldb_b) + ((sl ^ swz(r)) << 4);
     }
-  };
-  auto lstore = [&]() {
+    // scale load t (256 bytes) covers piece t * 256 / PIECE of the step, part t % (PIECE / 256)
+    constexpr int PP = C::PIECE / 256;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(sA + (ld_row + 32 * i) * LDS_ROW + ld_chunk * 16) = ra[i];
-      *reinterpret_cast<uint4*>(sB + (ld_row + 32 * i) * LDS_ROW + ld_chunk * 16) = rb[i];
+    for (int i = 0; i < C::NLSA; ++i) {
+      const int t = i * C::NW + wave;
+      vsa[i] = t < C::ISA ? (int)((t / PP) * gstride) + (t % PP) * 256 + lane * 4 : 0x7FFFFFF0;
+      ldsa[i] = t < C::ISA ? C::SA_OFF + t * 256 : C::DUMMY_OFF;
     }
 #pragma unroll
-    for (int i = 0; i < SB / 8; ++i) {
-      const int idx = tid + i * kGemmThreads;
-      reinterpret_cast<uint32_t*>(sSA)[idx] = rsa[i];
-      reinterpret_cast<uint32_t*>(sSB)[idx] = rsb[i];
+    for (int i = 0; i < C::NLSB; ++i) {
+      const int t = i * C::NW + wave;
+      vsb[i] = t < C::ISB ? (int)((t / PP) * gstride) + (t % PP) * 256 + lane * 4 : 0x7FFFFFF0;
+      ldsb[i] = t < C::ISB ? C::SB_OFF + t * 256 : C::DUMMY_OFF;
     }
-  };
+    const int sw = swz(fr);
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) frag_off[kk] = fr * C::BKB + (((fk * C::NKK + kk) ^ sw) << 4);
+    scale_off = fr * C::SB + fk * (C::SB / 2);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
+  }
 
-  v16f acc[2][2];
+  // This wave's share of the loads of the K-step starting at byte `kbyte` into stage s.
+  __device__ __forceinline__ void issue(int kbyte, int sbyte, uint8_t* s) const {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::NLA; ++i) dma16<AUX>(ra, s + C::A_OFF + (i * C::NW + wave) * 1024, va[i], kbyte);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+    for (int i = 0; i < C::NLB; ++i) dma16<AUX>(rb, s + C::B_OFF + (i * C::NW + wave) * 1024, vb[i], kbyte);
+#pragma unroll
+    for (int i = 0; i < C::NLSA; ++i) dma4<AUX>(rsa, s + ldsa[i], vsa[i], sbyte);
+#pragma unroll
+    for (int i = 0; i < C::NLSB; ++i) dma4<AUX>(rsb, s + ldsb[i], vsb[i], sbyte);
+  }
 
-  const int fr = lane & 31, fk = lane >> 5;  // fragment row, K half
-  for (int64_t k0 = kb; k0 < ke; k0 += BKE) {
-    gload(k0);
-    __syncthreads();  // previous compute done with LDS
-    lstore();
-    __syncthreads();
+  __device__ __forceinline__ void compute(const uint8_t* s) {
+    constexpr int LSB = C::SB / 2;  // scale bytes per lane half per K-step (4 or 8)
+    uint32_t sa[TM][LSB / 4], sb[TN][LSB / 4];
 #pragma unroll
-    for (int kk = 0; kk < BKE / 64; ++kk) {
-      uint4 fa[2], fb[2];
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        fa[i] = *reinterpret_cast<const uint4*>(sA + (wm * 64 + i * 32 + fr) * LDS_ROW + kk * 32 + fk * 16);
-        fb[i] = *reinterpret_cast<const uint4*>(sB + (wn * 64 + i * 32 + fr) * LDS_ROW + kk * 32 + fk * 16);
-      }
+      for (int w = 0; w < LSB / 4; ++w)
+        sa[i][w] = *reinterpret_cast<const uint32_t*>(s + C::SA_OFF + (wm * TM * 32 + i * 32) * C::SB + scale_off + 4 * w);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int w = 0; w < LSB / 4; ++w)
+        sb[j][w] = *reinterpret_cast<const uint32_t*>(s + C::SB_OFF + (wn * TN * 32 + j * 32) * C::SB + scale_off + 4 * w);
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+      uint4 fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fa[i] = *reinterpret_cast<const uint4*>(s + C::A_OFF + (wm * TM * 32 + i * 32) * C::BKB + frag_off[kk]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        fb[j] = *reinterpret_cast<const uint4*>(s + C::B_OFF + (wn * TN * 32 + j * 32) * C::BKB + frag_off[kk]);
       if (FMT == AVERIS_MXFP4) {
-        int sa[2], sb[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          sa[i] = sSA[(wm * 64 + i * 32 + fr) * SB + kk * 2 + fk];
-          sb[i] = sSB[(wn * 64 + i * 32 + fr) * SB + kk * 2 + fk];
-        }
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
+          for (int j = 0; j < TN; ++j) {
             const v8i av = {(int)fa[i].x, (int)fa[i].y, (int)fa[i].z, (int)fa[i].w, 0, 0, 0, 0};
             const v8i bv = {(int)fb[j].x, (int)fb[j].y, (int)fb[j].z, (int)fb[j].w, 0, 0, 0, 0};
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 4, 4, 0, sa[i], 0, sb[j]);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                av, bv, acc[i][j], 4, 4, 0, (int)__builtin_amdgcn_ubfe(sa[i][0], 8 * kk, 8), 0,
+                (int)__builtin_amdgcn_ubfe(sb[j][0], 8 * kk, 8));
           }
       } else {
-        v8bf da[2][4], db[2][4];
+        v8bf da[TM][4], db[TN][4];
+        const int wsel = kk / 2, sh = 16 * (kk % 2);  // two scale bytes per chunk
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const uint8_t* pa = sSA + (wm * 64 + i * 32 + fr) * SB + kk * 4 + fk * 2;
-          const uint8_t* pb = sSB + (wn * 64 + i * 32 + fr) * SB + kk * 4 + fk * 2;
-          dequant32_bf16(fa[i], e4m3_value(pa[0]), e4m3_value(pa[1]), da[i]);
-          dequant32_bf16(fb[i], e4m3_value(pb[0]), e4m3_value(pb[1]), db[i]);
+        for (int i = 0; i < TM; ++i) {
+          const uint32_t w = sa[i][wsel];
+          dequant32_bf16(fa[i], e4m3_value((w >> sh) & 255u), e4m3_value((w >> (sh + 8)) & 255u), da[i]);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < TN; ++j) {
+          const uint32_t w = sb[j][wsel];
+          dequant32_bf16(fb[j], e4m3_value((w >> sh) & 255u), e4m3_value((w >> (sh + 8)) & 255u), db[j]);
+        }
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[i][q], db[j][q], acc[i][j], 0, 0, 0);
       }
     }
   }
+};
 
-  // ---- epilogue ----
+// One pipeline step: wait until K-step `step` has landed (STAGES - 2 younger steps may stay in
+// flight), meet at the barrier (all waves are then done with the stage refilled next), refill
+// that stage with K-step step + STAGES - 1, multiply.  Every step issues the same loads (steps
+// past the end re-load step 0's bytes into a stage nobody reads) so the vmcnt arithmetic is exact.
+template <class T, int STAGES>
+__device__ __forceinline__ void pipe_step(T& t, int step, int nsteps, int kb_byte, int kb_sbyte, uint8_t* cur,
+                                          uint8_t* nxt) {
+  using C = typename T::C;
+  wait_vm<C::LPS * (STAGES - 2)>();
+  __builtin_amdgcn_s_barrier();
+  const int ns = step + STAGES - 1;
+  const bool live = ns < nsteps;
+  t.issue(live ? kb_byte + ns * C::BKB : 0, live ? kb_sbyte + ns * C::PIECE : 0, nxt);
+  if (step < nsteps) t.compute(cur);
+}
+
+template <int FMT, int WM, int WN, int TM, int TN, int STAGES, int AUX = 0>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs g) {
+  using T = GemmTile<FMT, WM, WN, TM, TN, STAGES, AUX>;
+  using C = typename T::C;
+  static_assert(STAGES == 2 || STAGES == 3 || STAGES == 4, "stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGES >= 3 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[STAGES >= 4 ? C::STAGE : 16];
+
+  const int ntiles = g.tiles_m * g.tiles_n;
+  const int lin = xcd_remap(blockIdx.x, ntiles * g.splits);
+  const int split = lin / ntiles;
+  int tm, tn;
+  tile_coords(lin % ntiles, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+  const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+  const int64_t kb = (int64_t)split * g.k_chunk;
+  const int64_t ke = kb + g.k_chunk < g.K ? kb + g.k_chunk : g.K;
+  const int nsteps = (int)((ke - kb) / C::BKE);  // K and k_chunk are multiples of the K-step
+  const int kb_byte = (int)(kb / 2), kb_sbyte = (int)(kb / C::BKE) * C::PIECE;
+
+  T t;
+  t.setup(g, m0, n0);
+  // prologue: K-steps 0 .. STAGES-2
+  t.issue(kb_byte, kb_sbyte, st0);
+  if (STAGES >= 3) t.issue(1 < nsteps ? kb_byte + C::BKB : 0, 1 < nsteps ? kb_sbyte + C::PIECE : 0, st1);
+  if (STAGES >= 4) t.issue(2 < nsteps ? kb_byte + 2 * C::BKB : 0, 2 < nsteps ? kb_sbyte + 2 * C::PIECE : 0, st2);
+  for (int it = 0; it < nsteps; it += STAGES) {
+    if (STAGES == 2) {
+      pipe_step<T, STAGES>(t, it, nsteps, kb_byte, kb_sbyte, st0, st1);
+      pipe_step<T, STAGES>(t, it + 1, nsteps, kb_byte, kb_sbyte, st1, st0);
+    } else if (STAGES == 3) {
+      pipe_step<T, STAGES>(t, it, nsteps, kb_byte, kb_sbyte, st0, st2);
+      pipe_step<T, STAGES>(t, it + 1, nsteps, kb_byte, kb_sbyte, st1, st0);
+      pipe_step<T, STAGES>(t, it + 2, nsteps, kb_byte, kb_sbyte, st2, st1);
+    } else {
+      pipe_step<T, STAGES>(t, it, nsteps, kb_byte, kb_sbyte, st0, st3);
+      pipe_step<T, STAGES>(t, it + 1, nsteps, kb_byte, kb_sbyte, st1, st0);
+      pipe_step<T, STAGES>(t, it + 2, nsteps, kb_byte, kb_sbyte, st2, st1);
+      pipe_step<T, STAGES>(t, it + 3, nsteps, kb_byte, kb_sbyte, st3, st2);
+    }
+  }
+  wait_vm<0>();                 // no load may still be writing LDS
+  __builtin_amdgcn_s_barrier();  // every wave is done reading the stages
+
+  // ---- epilogue: per 32-row slab, stage the wave's fp32 tile in LDS, then 16-byte stores ----
+  const int lane = threadIdx.x & 63, fr = lane & 31, fk = lane >> 5;
+  const int wave = t.wave, wm = t.wm, wn = t.wn;
+  float* epi = reinterpret_cast<float*>((wave < (C::NW + 1) / 2 ? st0 : st1) + (wave % ((C::NW + 1) / 2)) * C::EPI_WAVE);
   float alpha = 1.0f;
   if (FMT == AVERIS_NVFP4) alpha = __fmul_rn(g.a_ts[0], g.b_ts[0]);
   const bool partial = g.splits > 1;
+  const bool r1_direct = !partial && g.r1u == nullptr && g.mu_codes != nullptr;
+  const bool r1_vec = !partial && g.r1u != nullptr;
+  float bcol[TN], vcol[TN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < TN; ++j) {
+    const int64_t col = n0 + wn * TN * 32 + j * 32 + fr;
+    const bool cin = col < g.N;
+    bcol[j] = (!partial && g.bias && cin) ? g.bias[col] : 0.0f;
+    vcol[j] = 0.0f;
+    if (r1_vec && cin) vcol[j] = g.r1v[col];
+    if (r1_direct && cin) vcol[j] = dq_one<FMT>(g.mv_codes, g.mv_scales, g.mv_ts, col, g.mv_kpad);
+  }
+  constexpr int W = TN * 32;  // columns of the wave tile
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wn * 64 + j * 32 + fr;
-      if (col >= g.N) continue;
-      const float bcol = (!partial && g.bias) ? g.bias[col] : 0.0f;
-      const float vcol = (!partial && g.r1u) ? g.r1v[col] : 0.0f;
+  for (int i = 0; i < TM; ++i) {
+    const int64_t rbase = m0 + wm * TM * 32 + i * 32;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 64 + i * 32 + (e >> 2) * 8 + fk * 4 + (e & 3);
-        if (row >= g.M) continue;
-        float out = __fmul_rn(acc[i][j][e], alpha);
-        if (partial) {
-          reinterpret_cast<float*>(g.c)[(int64_t)split * g.M * g.N + row * g.N + col] = out;
-          continue;
+        const int rr = (e >> 2) * 8 + fk * 4 + (e & 3);
+        float out = __fmul_rn(t.acc[i][j][e], alpha);
+        if (!partial) {
+          out = __fadd_rn(out, bcol[j]);
+          if (r1_vec || r1_direct) {
+            const int64_t row = rbase + rr;
+            float urow = 0.0f;
+            if (row < g.M) urow = r1_vec ? g.r1u[row] : dq_one<FMT>(g.mu_codes, g.mu_scales, g.mu_ts, row, g.mu_kpad);
+            out = __fadd_rn(out, __fmul_rn(__fmul_rn(g.r1, urow), vcol[j]));
+          }
         }
-        if (g.bias) out = __fadd_rn(out, bcol);
-        if (g.r1u) out = __fadd_rn(out, __fmul_rn(__fmul_rn(g.r1, g.r1u[row]), vcol));
-        if (g.c_bf16) {
-          reinterpret_cast<uint16_t*>(g.c)[row * g.ldc + col] = (uint16_t)f32_to_bf16_rne(out);
-        } else {
-          float* p = reinterpret_cast<float*>(g.c) + row * g.ldc + col;
-          *p = g.accumulate ? __fadd_rn(*p, out) : out;
+        epi[rr * C::EPI_LD + j * 32 + fr] = out;
+      }
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // this wave's LDS writes done
+    // copy-out: every store instruction writes whole contiguous row segments of 16-byte chunks
+    if (g.c_bf16 && !partial) {
+      constexpr int LPR = W * 2 / 16, RPI = 64 / LPR;  // lanes per row, rows per instruction
+      const int lr = lane / LPR, ch = lane % LPR;
+      const int64_t gcol = n0 + wn * W + ch * 8;
+#pragma unroll
+      for (int p = 0; p < 32 / RPI; ++p) {
+        const int rr = p * RPI + lr;
+        const int64_t row = rbase + rr;
+        if (row < g.M && gcol < g.N) {
+          const float* src = epi + rr * C::EPI_LD + ch * 8;
+          const float4 a = *reinterpret_cast<const float4*>(src), b = *reinterpret_cast<const float4*>(src + 4);
+          uint4 o;
+          o.x = pack_bf16x2(a.x, a.y); o.y = pack_bf16x2(a.z, a.w);
+          o.z = pack_bf16x2(b.x, b.y); o.w = pack_bf16x2(b.z, b.w);
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.c) + row * g.ldc + gcol) = o;
+        }
+      }
+    } else {
+      constexpr int LPR = W * 4 / 16, RPI = 64 / LPR;
+      const int lr = lane / LPR, ch = lane % LPR;
+      const int64_t gcol = n0 + wn * W + ch * 4;
+#pragma unroll
+      for (int p = 0; p < 32 / RPI; ++p) {
+        const int rr = p * RPI + lr;
+        const int64_t row = rbase + rr;
+        if (row < g.M && gcol < g.N) {
+          float4 v = *reinterpret_cast<const float4*>(epi + rr * C::EPI_LD + ch * 4);
+          float* dst = partial ? reinterpret_cast<float*>(g.c) + (int64_t)split * g.M * g.N + row * g.N + gcol
+                               : reinterpret_cast<float*>(g.c) + row * g.ldc + gcol;
+          if (!partial && g.accumulate) {
+            const float4 o = *reinterpret_cast<const float4*>(dst);
+            v.x = __fadd_rn(o.x, v.x); v.y = __fadd_rn(o.y, v.y); v.z = __fadd_rn(o.z, v.z); v.w = __fadd_rn(o.w, v.w);
+          }
+          *reinterpret_cast<float4*>(dst) = v;
         }
       }
     }
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // reads done before the next slab
+  }
 }
 
 // Split-K reduce: C = (accumulate ? C : 0) + sum_s P[s] (fixed order) + r1 * u[row] * v[col].
-__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int splits, int64_t M, int64_t N,
-                                                       float* __restrict__ c, int64_t ldc, const float* __restrict__ u,
-                                                       const float* __restrict__ v, float r1, int accumulate) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= M * N) return;
-  const int64_t row = idx / N, col = idx % N;
-  float s = part[idx];
-  for (int p = 1; p < splits; ++p) s = __fadd_rn(s, part[(int64_t)p * M * N + idx]);
-  if (u) s = __fadd_rn(s, __fmul_rn(__fmul_rn(r1, u[row]), v[col]));
-  float* dst = c + row * ldc + col;
-  *dst = accumulate ? __fadd_rn(*dst, s) : s;
-}
-
-// Dequantized value of element k of a packed row (fp64, exact).
 template <int FMT>
-__device__ inline double dq_elem(const uint8_t* codes, const uint8_t* scales, int64_t k) {
-  const uint32_t byte = codes[k >> 1];
-  const uint32_t c = (k & 1) ? (byte >> 4) : (byte & 15u);
-  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  double v = e == 0 ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
-  if (c & 8u) v = -v;
-  if (FMT == AVERIS_MXFP4) return v * ldexp(1.0, (int)scales[k >> 5] - 127);
-  return v * (double)e4m3_value(scales[k >> 4]);
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int splits, GemmArgs g,
+                                                       float* __restrict__ c, int64_t ldc) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= g.M * g.N) return;
+  const int64_t row = idx / g.N, col = idx % g.N;
+  float s = part[idx];
+  for (int p = 1; p < splits; ++p) s = __fadd_rn(s, part[(int64_t)p * g.M * g.N + idx]);
+  if (g.r1u) {
+    s = __fadd_rn(s, __fmul_rn(__fmul_rn(g.r1, g.r1u[row]), g.r1v[col]));
+  } else if (g.mu_codes) {
+    const float u = dq_one<FMT>(g.mu_codes, g.mu_scales, g.mu_ts, row, g.mu_kpad);
+    const float v = dq_one<FMT>(g.mv_codes, g.mv_scales, g.mv_ts, col, g.mv_kpad);
+    s = __fadd_rn(s, __fmul_rn(__fmul_rn(g.r1, u), v));
+  }
+  float* dst = c + row * ldc + col;
+  *dst = g.accumulate ? __fadd_rn(*dst, s) : s;
 }
 
-// Mean-term GEMV: out[j] = alpha * sum_k DQ(mu)[k] DQ(B)[j][k], one wave per output, fp64
-// accumulation with a fixed-order lane reduction.  alpha = s_mu * s_B (NVFP4) or 1.
+// Mean-term GEMV: out[j] = alpha * sum_k DQ(mu)[k] DQ(B)[j][k], one wave per output row.
+// Each lane takes 32-element chunks; code products summed exactly in fp32 within a chunk, the
+// chunk sums scaled and accumulated in fp64; fixed-order lane reduction.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_gemv_mean(const uint8_t* __restrict__ mu_codes, const uint8_t* __restrict__ mu_scales,
                                                    const float* __restrict__ mu_ts, const uint8_t* __restrict__ b_codes,
-                                                   const uint8_t* __restrict__ b_scales, int64_t ldb_b, int64_t lds_b,
+                                                   const uint8_t* __restrict__ b_scales, int64_t ldb_b,
                                                    const float* __restrict__ b_ts, int64_t N, int64_t K, float* __restrict__ out) {
+  constexpr int G = FMT == AVERIS_MXFP4 ? 32 : 16;
   const int lane = threadIdx.x & 63;
   const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (j >= N) return;
   const uint8_t* bc = b_codes + j * ldb_b;
-  const uint8_t* bs = b_scales + j * lds_b;
   double s = 0.0;
-  for (int64_t k = lane; k < K; k += 64) s += dq_elem<FMT>(mu_codes, mu_scales, k) * dq_elem<FMT>(bc, bs, k);
+  for (int64_t ch = lane; ch * 32 < K; ch += 64) {
+    const uint4 ca = *reinterpret_cast<const uint4*>(mu_codes + ch * 16);
+    const uint4 cb = *reinterpret_cast<const uint4*>(bc + ch * 16);
+    const uint32_t wa[4] = {ca.x, ca.y, ca.z, ca.w}, wb[4] = {cb.x, cb.y, cb.z, cb.w};
+    float part[2] = {0.0f, 0.0f};  // exact: sums of products of E2M1 values
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int bsel = 0; bsel < 4; ++bsel) {
+        const float2 a = fp4x2_to_f32(wa[q], bsel), b = fp4x2_to_f32(wb[q], bsel);
+        part[q >> 1] = __fadd_rn(part[q >> 1], __fadd_rn(__fmul_rn(a.x, b.x), __fmul_rn(a.y, b.y)));
+      }
+    if (FMT == AVERIS_MXFP4) {
+      const int e = (int)mu_scales[scale_offset(0, ch, K, G)] + (int)b_scales[scale_offset(j, ch, K, G)] - 254;
+      s += ldexp((double)part[0] + (double)part[1], e);
+    } else {
+      const int64_t b0 = 2 * ch, b1 = 2 * ch + 1;
+      s += (double)part[0] * ((double)e4m3_value(mu_scales[scale_offset(0, b0, K, G)]) *
+                              (double)e4m3_value(b_scales[scale_offset(j, b0, K, G)])) +
+           (double)part[1] * ((double)e4m3_value(mu_scales[scale_offset(0, b1, K, G)]) *
+                              (double)e4m3_value(b_scales[scale_offset(j, b1, K, G)]));
+    }
+  }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
   if (lane == 0) {
@@ -264,41 +500,59 @@ __global__ __launch_bounds__(256) void k_gemv_mean(const uint8_t* __restrict__ m
   }
 }
 
-// Dequantized mean vector for the rank-one dW term, rotation undone in fp64 if `rotated`.
+// Dequantized, un-rotated mean vectors for the rank-one dW term (used only for rotated means).
 template <int FMT>
-__global__ __launch_bounds__(256) void k_mean_vec(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                                                  const float* __restrict__ ts, int64_t K, int rotated, float* __restrict__ out) {
-  const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 16-element chunk
+__global__ __launch_bounds__(256) void k_mean_vec(const uint8_t* __restrict__ c0, const uint8_t* __restrict__ s0,
+                                                  const float* __restrict__ t0, int64_t K0, int64_t P0, float* __restrict__ o0,
+                                                  const uint8_t* __restrict__ c1, const uint8_t* __restrict__ s1,
+                                                  const float* __restrict__ t1, int64_t K1, int64_t P1, float* __restrict__ o1) {
+  const int64_t n0 = (K0 + 15) / 16;
+  int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const uint8_t *codes = c0, *scales = s0;
+  const float* ts = t0;
+  int64_t K = K0, P = P0;
+  float* out = o0;
+  if (blk >= n0) { blk -= n0; codes = c1; scales = s1; ts = t1; K = K1; P = P1; out = o1; }
   if (blk * 16 >= K) return;
-  const double sd = FMT == AVERIS_NVFP4 ? (double)ts[0] : 1.0;
   double v[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = dq_elem<FMT>(codes, scales, blk * 16 + j) * sd;
-  if (rotated) {
+  for (int j = 0; j < 16; ++j) v[j] = (double)dq_one<FMT>(codes, scales, ts, blk * 16 + j, P);
 #pragma unroll
-    for (int h = 1; h < 16; h <<= 1)
+  for (int h = 1; h < 16; h <<= 1)
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if ((j & h) == 0) { const double a = v[j], b = v[j + h]; v[j] = a + b; v[j + h] = a - b; }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] *= 0.25;
-  }
+    for (int j = 0; j < 16; ++j)
+      if ((j & h) == 0) { const double a = v[j], b = v[j + h]; v[j] = a + b; v[j + h] = a - b; }
 #pragma unroll
   for (int j = 0; j < 16; ++j)
-    if (blk * 16 + j < K) out[blk * 16 + j] = (float)v[j];
+    if (blk * 16 + j < K) out[blk * 16 + j] = (float)(v[j] * 0.25);
 }
 
 // ------------------------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------------------------
-
-
 static int g_count(int fmt) { return fmt == AVERIS_MXFP4 ? 32 : 16; }
 
+// Tile configurations: waves along M x N, 32x32 MFMA tiles per wave along M x N, LDS stages.
+struct TileCfg { int bm, bn; };
+static int tuning_cfg() {
+  static int c = [] { const char* e = getenv("AVERIS_GEMM_CFG"); return e ? atoi(e) : 0; }();
+  return c;
+}
+static TileCfg tile_of(int cfg) {
+  switch (cfg) {
+    case 3: case 7: return {256, 128};
+    case 4: return {128, 256};
+    case 8: return {256, 256};
+    default: return {128, 128};
+  }
+}
+constexpr int kBKE = 256;
 int choose_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ceil_div(M, BM) * ceil_div(N, BN);
-  int64_t s = 512 / (tiles > 0 ? tiles : 1);
-  const int64_t ksteps = ceil_div(K, BKE);
+  const TileCfg tc = tile_of(tuning_cfg());
+  const int64_t tiles = ceil_div(M, tc.bm) * ceil_div(N, tc.bn);
+  if (tiles >= 192) return 1;
+  int64_t s = ceil_div(256, tiles > 0 ? tiles : 1);
+  const int64_t ksteps = ceil_div(K, kBKE);
   if (s > ksteps) s = ksteps;
   if (s > 8) s = 8;
   return s < 1 ? 1 : (int)s;
@@ -313,11 +567,25 @@ size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int splits) {
   return b;
 }
 
+template <int FMT>
+static void launch_fmt(const GemmArgs& g, unsigned grid, hipStream_t s) {
+  switch (tuning_cfg()) {
+    case 1: hipLaunchKernelGGL((k_gemm<FMT, 2, 2, 2, 2, 2>), dim3(grid), dim3(256), 0, s, g); break;
+    case 2: hipLaunchKernelGGL((k_gemm<FMT, 2, 2, 2, 2, 4>), dim3(grid), dim3(256), 0, s, g); break;
+    case 3: hipLaunchKernelGGL((k_gemm<FMT, 2, 2, 4, 2, 2>), dim3(grid), dim3(256), 0, s, g); break;
+    case 4: hipLaunchKernelGGL((k_gemm<FMT, 2, 4, 2, 2, 2>), dim3(grid), dim3(512), 0, s, g); break;
+    case 5: hipLaunchKernelGGL((k_gemm<FMT, 2, 2, 2, 2, 2, 1>), dim3(grid), dim3(256), 0, s, g); break;
+    case 6: hipLaunchKernelGGL((k_gemm<FMT, 2, 2, 2, 2, 2, 2>), dim3(grid), dim3(256), 0, s, g); break;
+    case 7: hipLaunchKernelGGL((k_gemm<FMT, 4, 2, 2, 2, 2>), dim3(grid), dim3(512), 0, s, g); break;
+    case 8: hipLaunchKernelGGL((k_gemm<FMT, 2, 4, 4, 2, 2>), dim3(grid), dim3(512), 0, s, g); break;
+    default: hipLaunchKernelGGL((k_gemm<FMT, 2, 2, 2, 2, 3>), dim3(grid), dim3(256), 0, s, g); break;
+  }
+}
+
 hipError_t gemm_launch(const GemmPlan& p) {
   const averis_qtensor& A = *p.a;
   const averis_qtensor& B = *p.b;
   const int fmt = A.fmt;
-  const int G = g_count(fmt);
   uint8_t* ws = reinterpret_cast<uint8_t*>(p.ws);
   float* bias = reinterpret_cast<float*>(ws + 256);
   float* u = bias + B.outer;
@@ -325,11 +593,19 @@ hipError_t gemm_launch(const GemmPlan& p) {
   float* partials = reinterpret_cast<float*>(ws + partials_offset(A.outer, B.outer));
 
   GemmArgs g{};
-  g.a_codes = A.codes; g.a_scales = A.scales; g.lda_b = A.k_pad / 2; g.lds_a = A.k_pad / G;
-  g.b_codes = B.codes; g.b_scales = B.scales; g.ldb_b = B.k_pad / 2; g.lds_b = B.k_pad / G;
+  g.a_codes = A.codes; g.a_scales = A.scales; g.lda_b = A.k_pad / 2;
+  g.b_codes = B.codes; g.b_scales = B.scales; g.ldb_b = B.k_pad / 2;
   g.a_ts = A.tensor_scale; g.b_ts = B.tensor_scale;
   g.M = A.outer; g.N = B.outer; g.K = A.k_pad;
-  g.tiles_m = (int)ceil_div(g.M, BM); g.tiles_n = (int)ceil_div(g.N, BN);
+  const TileCfg tc = tile_of(tuning_cfg());
+  g.tiles_m = (int)ceil_div(g.M, tc.bm); g.tiles_n = (int)ceil_div(g.N, tc.bn);
+  {
+    // group height ~ sqrt of the tiles each XCD owns, so its block of tiles is near square
+    const int per_xcd = (int)ceil_div((int64_t)g.tiles_m * g.tiles_n * p.splits, 8);
+    int gm = 1;
+    while (gm * gm * 2 <= per_xcd && gm * 2 <= g.tiles_m) gm *= 2;
+    g.group_m = gm;
+  }
   g.accumulate = p.accumulate;
   if (g.M == 0 || g.N == 0) return hipSuccess;
 
@@ -338,41 +614,49 @@ hipError_t gemm_launch(const GemmPlan& p) {
     const unsigned blocks = (unsigned)ceil_div(g.N, 4);
     if (fmt == AVERIS_MXFP4)
       hipLaunchKernelGGL(k_gemv_mean<AVERIS_MXFP4>, dim3(blocks), dim3(256), 0, p.stream, U.codes, U.scales, U.tensor_scale,
-                         B.codes, B.scales, g.ldb_b, g.lds_b, B.tensor_scale, g.N, B.k_pad, bias);
+                         B.codes, B.scales, g.ldb_b, B.tensor_scale, g.N, B.k_pad, bias);
     else
       hipLaunchKernelGGL(k_gemv_mean<AVERIS_NVFP4>, dim3(blocks), dim3(256), 0, p.stream, U.codes, U.scales, U.tensor_scale,
-                         B.codes, B.scales, g.ldb_b, g.lds_b, B.tensor_scale, g.N, B.k_pad, bias);
+                         B.codes, B.scales, g.ldb_b, B.tensor_scale, g.N, B.k_pad, bias);
     g.bias = bias;
   }
   if (p.mu_u) {
-    const averis_qtensor* vs[2] = {p.mu_u, p.mu_v};
-    float* outs[2] = {u, v};
-    for (int t = 0; t < 2; ++t) {
-      const averis_qtensor& Q = *vs[t];
-      const unsigned blocks = (unsigned)ceil_div(ceil_div(Q.k, 16), 256);
-      const int rot = (Q.flags & AVERIS_HADAMARD16) ? 1 : 0;
+    g.r1 = p.r1;
+    const averis_qtensor& Qu = *p.mu_u;
+    const averis_qtensor& Qv = *p.mu_v;
+    if (Qu.flags & AVERIS_HADAMARD16) {
+      const unsigned blocks = (unsigned)ceil_div(ceil_div(Qu.k, 16) + ceil_div(Qv.k, 16), 256);
       if (fmt == AVERIS_MXFP4)
-        hipLaunchKernelGGL(k_mean_vec<AVERIS_MXFP4>, dim3(blocks), dim3(256), 0, p.stream, Q.codes, Q.scales, Q.tensor_scale, Q.k, rot, outs[t]);
+        hipLaunchKernelGGL(k_mean_vec<AVERIS_MXFP4>, dim3(blocks), dim3(256), 0, p.stream, Qu.codes, Qu.scales,
+                           Qu.tensor_scale, Qu.k, Qu.k_pad, u, Qv.codes, Qv.scales, Qv.tensor_scale, Qv.k, Qv.k_pad, v);
       else
-        hipLaunchKernelGGL(k_mean_vec<AVERIS_NVFP4>, dim3(blocks), dim3(256), 0, p.stream, Q.codes, Q.scales, Q.tensor_scale, Q.k, rot, outs[t]);
+        hipLaunchKernelGGL(k_mean_vec<AVERIS_NVFP4>, dim3(blocks), dim3(256), 0, p.stream, Qu.codes, Qu.scales,
+                           Qu.tensor_scale, Qu.k, Qu.k_pad, u, Qv.codes, Qv.scales, Qv.tensor_scale, Qv.k, Qv.k_pad, v);
+      g.r1u = u; g.r1v = v;
+    } else {
+      g.mu_codes = Qu.codes; g.mu_scales = Qu.scales; g.mu_ts = Qu.tensor_scale; g.mu_kpad = Qu.k_pad;
+      g.mv_codes = Qv.codes; g.mv_scales = Qv.scales; g.mv_ts = Qv.tensor_scale; g.mv_kpad = Qv.k_pad;
     }
-    g.r1u = u; g.r1v = v; g.r1 = p.r1;
   }
   g.splits = p.splits;
-  const int64_t ksteps = ceil_div(g.K, BKE);
-  g.k_chunk = ceil_div(ksteps, p.splits) * BKE;
+  const int64_t ksteps = ceil_div(g.K, kBKE);
+  g.k_chunk = ceil_div(ksteps, p.splits) * kBKE;
   if (p.splits > 1) {
     g.c = partials; g.ldc = g.N; g.c_bf16 = 0;
   } else {
     g.c = p.c; g.ldc = p.ldc; g.c_bf16 = p.c_bf16;
   }
   const unsigned grid = (unsigned)(g.tiles_m * g.tiles_n * p.splits);
-  if (fmt == AVERIS_MXFP4) hipLaunchKernelGGL(k_gemm<AVERIS_MXFP4>, dim3(grid), dim3(kGemmThreads), 0, p.stream, g);
-  else hipLaunchKernelGGL(k_gemm<AVERIS_NVFP4>, dim3(grid), dim3(kGemmThreads), 0, p.stream, g);
+  if (fmt == AVERIS_MXFP4) launch_fmt<AVERIS_MXFP4>(g, grid, p.stream);
+  else launch_fmt<AVERIS_NVFP4>(g, grid, p.stream);
   if (p.splits > 1) {
     const int64_t n = g.M * g.N;
-    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, p.stream, partials, p.splits, g.M,
-                       g.N, reinterpret_cast<float*>(p.c), p.ldc, g.r1u, g.r1v, g.r1, p.accumulate);
+    if (fmt == AVERIS_MXFP4)
+      hipLaunchKernelGGL(k_splitk_reduce<AVERIS_MXFP4>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, p.stream,
+                         partials, p.splits, g, reinterpret_cast<float*>(p.c), p.ldc);
+    else
+      hipLaunchKernelGGL(k_splitk_reduce<AVERIS_NVFP4>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, p.stream,
+                         partials, p.splits, g, reinterpret_cast<float*>(p.c), p.ldc);
   }
   return hipGetLastError();
 }

@@ -191,7 +191,7 @@ __device__ inline void h16_lanes(float* v, int lane) {
 // k_quant_mean: one workgroup quantizes mu [cols] along its length.
 // ------------------------------------------------------------------------------------------
 template <int FMT, bool H16>
-__global__ __launch_bounds__(kThreads) void k_quant_mean(const float* __restrict__ mean, int64_t cols,
+__global__ __launch_bounds__(kThreads) void k_quant_mean(const float* __restrict__ mean, int64_t cols, int64_t k_pad,
                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                          float* __restrict__ tscale) {
   constexpr int G = FMT == AVERIS_MXFP4 ? 32 : 16;
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mean(const float* __restrict
       const uint32_t w = q.dead ? 0u : pack8_fp4(v + 8 * j);
       *reinterpret_cast<uint32_t*>(codes + b * (G / 2) + 4 * j) = w;
     }
-    scales[b] = (uint8_t)q.sbyte;
+    scales[scale_offset(0, b, k_pad, G)] = (uint8_t)q.sbyte;
   }
 }
 
@@ -265,6 +265,7 @@ struct QuantArgs {
   uint8_t* col_scales;
   float* col_ts;
   int64_t col_kpad;            // padded token count of the column layout
+  int64_t row_kpad;            // padded column count of the row layout (its row stride in elements)
   int tiles_r, tiles_c;
 };
 
@@ -335,10 +336,10 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs a) {
 #pragma unroll
       for (int j = 0; j < VEC; ++j) v[j] = __fmul_rn(v[j], q.mul);
       if (r < a.rows && col_ok) {
-        uint8_t* dst = a.row_codes + r * (a.cols / 2) + cc / 2;
+        uint8_t* dst = a.row_codes + r * (a.row_kpad / 2) + cc / 2;
         if (VEC == 8) *reinterpret_cast<uint32_t*>(dst) = q.dead ? 0u : pack8_fp4(v);
         else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(q.dead ? 0u : pack4_fp4(v));
-        if ((lane_c % LPB) == 0) a.row_scales[r * (a.cols / G) + cc / G] = (uint8_t)q.sbyte;
+        if ((lane_c % LPB) == 0) a.row_scales[scale_offset(r, cc / G, a.row_kpad, G)] = (uint8_t)q.sbyte;
       }
     }
   }
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs a) {
             o.y = q.dead ? 0u : pack8_fp4(v + b * G + 8);
             *reinterpret_cast<uint2*>(dst) = o;
           }
-          a.col_scales[col * (a.col_kpad / G) + k0 / G] = (uint8_t)q.sbyte;
+          a.col_scales[scale_offset(col, k0 / G, a.col_kpad, G)] = (uint8_t)q.sbyte;
         }
       }
     }
@@ -414,6 +415,26 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs a) {
       atomicMax(a.amax_out + 2, __float_as_uint(v));
     }
   }
+}
+
+// Zero bytes [start, start + len) of each of `rows` rows of stride ld (K padding of a layout).
+__global__ void k_zero_tail(uint8_t* __restrict__ base, int64_t rows, int64_t ld, int64_t start, int64_t len) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t r = i / len, b = i % len;
+  if (r < rows) base[r * ld + start + b] = 0;
+}
+
+// Zero the tiled scale bytes outside the data: blocks [k/g, k_pad/g) of rows [0, outer) and
+// every block of the group-padding rows [outer, round_up(outer, 32)).
+__global__ void k_zero_scale_pad(uint8_t* __restrict__ scales, int64_t outer, int64_t k, int64_t k_pad, int g) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nb = k_pad / g, kb = k / g, tail = nb - kb;
+  const int64_t n1 = outer * tail, n2 = (round_up(outer, 32) - outer) * nb;
+  int64_t r, b;
+  if (i < n1) { r = i / tail; b = kb + i % tail; }
+  else if (i < n1 + n2) { r = outer + (i - n1) / nb; b = (i - n1) % nb; }
+  else return;
+  scales[scale_offset(r, b, k_pad, g)] = 0;
 }
 
 __global__ void k_fill_f32(float* p, int n, float v) {
@@ -445,6 +466,7 @@ static hipError_t launch_quant_t(const SplitQuantPlan& p, uint32_t* slots) {
   a.amax_slots = slots; a.amax_out = slots;
   const int64_t col_kpad = round_up(p.rows, kKPad);
   a.col_kpad = col_kpad;
+  a.row_kpad = round_up(p.cols, kKPad);
   a.tiles_c = (int)ceil_div(p.cols, TC);
   // column layout covers the padding rows too (they are zero residuals)
   a.tiles_r = (int)ceil_div(p.q_col ? col_kpad : p.rows, kTileRows);
@@ -472,6 +494,22 @@ static hipError_t launch_quant_f(const SplitQuantPlan& p, uint32_t* slots) {
   return p.xdt == AVERIS_BF16 ? launch_quant_t<uint16_t, FMT, H16>(p, slots) : launch_quant_t<float, FMT, H16>(p, slots);
 }
 
+// Zero the padding of an operand the quantizer writes: codes [k, k_pad) of every row, and the
+// scale bytes outside the data (K tail and the rows that pad the last 32-row group).
+static void zero_padding(const averis_qtensor* q, int fmt, hipStream_t s) {
+  const int G = fmt == AVERIS_MXFP4 ? 32 : 16;
+  if (!q || q->outer == 0 || q->k_pad == 0) return;
+  if (q->k_pad > q->k) {
+    const int64_t cl = (q->k_pad - q->k) / 2;
+    hipLaunchKernelGGL(k_zero_tail, dim3((unsigned)ceil_div(q->outer * cl, 256)), dim3(256), 0, s, q->codes, q->outer,
+                       q->k_pad / 2, q->k / 2, cl);
+  }
+  const int64_t n = q->outer * (q->k_pad / G - q->k / G) + (round_up(q->outer, 32) - q->outer) * (q->k_pad / G);
+  if (n > 0)
+    hipLaunchKernelGGL(k_zero_scale_pad, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, q->scales, q->outer, q->k,
+                       q->k_pad, G);
+}
+
 hipError_t split_quant_launch(const SplitQuantPlan& p) {
   uint8_t* ws = reinterpret_cast<uint8_t*>(p.ws);
   uint32_t* slots = reinterpret_cast<uint32_t*>(ws);
@@ -496,13 +534,15 @@ hipError_t split_quant_launch(const SplitQuantPlan& p) {
   }
   if (p.split) {
     if (p.fmt == AVERIS_NVFP4) {
-      if (p.h16) hipLaunchKernelGGL((k_quant_mean<AVERIS_NVFP4, true>), dim3(1), dim3(kThreads), 0, p.stream, p.mean, p.cols, p.q_mean->codes, p.q_mean->scales, p.q_mean->tensor_scale);
-      else hipLaunchKernelGGL((k_quant_mean<AVERIS_NVFP4, false>), dim3(1), dim3(kThreads), 0, p.stream, p.mean, p.cols, p.q_mean->codes, p.q_mean->scales, p.q_mean->tensor_scale);
+      if (p.h16) hipLaunchKernelGGL((k_quant_mean<AVERIS_NVFP4, true>), dim3(1), dim3(kThreads), 0, p.stream, p.mean, p.cols, p.q_mean->k_pad, p.q_mean->codes, p.q_mean->scales, p.q_mean->tensor_scale);
+      else hipLaunchKernelGGL((k_quant_mean<AVERIS_NVFP4, false>), dim3(1), dim3(kThreads), 0, p.stream, p.mean, p.cols, p.q_mean->k_pad, p.q_mean->codes, p.q_mean->scales, p.q_mean->tensor_scale);
     } else {
-      if (p.h16) hipLaunchKernelGGL((k_quant_mean<AVERIS_MXFP4, true>), dim3(1), dim3(kThreads), 0, p.stream, p.mean, p.cols, p.q_mean->codes, p.q_mean->scales, (float*)nullptr);
-      else hipLaunchKernelGGL((k_quant_mean<AVERIS_MXFP4, false>), dim3(1), dim3(kThreads), 0, p.stream, p.mean, p.cols, p.q_mean->codes, p.q_mean->scales, (float*)nullptr);
+      if (p.h16) hipLaunchKernelGGL((k_quant_mean<AVERIS_MXFP4, true>), dim3(1), dim3(kThreads), 0, p.stream, p.mean, p.cols, p.q_mean->k_pad, p.q_mean->codes, p.q_mean->scales, (float*)nullptr);
+      else hipLaunchKernelGGL((k_quant_mean<AVERIS_MXFP4, false>), dim3(1), dim3(kThreads), 0, p.stream, p.mean, p.cols, p.q_mean->k_pad, p.q_mean->codes, p.q_mean->scales, (float*)nullptr);
     }
   }
+  zero_padding(p.q_row, p.fmt, p.stream);  // the column layout's padding rows are written by k_quant
+  zero_padding(p.q_mean, p.fmt, p.stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.fmt == AVERIS_NVFP4) return p.h16 ? launch_quant_f<AVERIS_NVFP4, true>(p, slots) : launch_quant_f<AVERIS_NVFP4, false>(p, slots);

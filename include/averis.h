@@ -82,10 +82,14 @@ typedef enum { AVERIS_F32 = 0, AVERIS_BF16 = 1 } averis_dtype;
 
 /* A quantized operand [outer, k] with blocks along k (K-inner, row-major).
  *   codes:        device uint8 [outer][k_pad / 2]; element 2i in bits 3:0, 2i+1 in bits 7:4.
- *   scales:       device uint8 [outer][k_pad / g]; g = 16 (E4M3 codes) or 32 (E8M0 codes).
+ *   scales:       device uint8, round_up(outer, 32) * (k_pad / g) bytes; g = 16 (E4M3 codes) or 32
+ *                 (E8M0 codes).  Tiled for the GEMM: the scale of K-block b (elements b*g ..) of
+ *                 row r is at byte ((r / 32) * (k_pad / 256) + b / S) * 32 * S + (r % 32) * S + b % S
+ *                 with S = 256 / g, i.e. per 32-row group and 256-element K-step the 32 x S bytes
+ *                 are contiguous.  Rows [outer, round_up(outer, 32)) hold zero scales.
  *   tensor_scale: device fp32 s_dec (NVFP4; one per group for grouped operands); NULL for MXFP4.
- *   k_pad:        storage length along k = k rounded up to a multiple of 128; elements in
- *                 [k, k_pad) hold code 0 and their blocks scale byte 0.
+ *   k_pad:        storage length along k = k rounded up to a multiple of 256; elements in
+ *                 [k, k_pad) hold code 0 and blocks past k scale byte 0.
  *   flags:        AVERIS_HADAMARD16 if the operand was rotated along k.
  * The caller fills every field before a call that writes the operand, and the library checks
  * outer/k/k_pad/fmt/flags against what the call expects. */
@@ -135,8 +139,8 @@ int32_t averis_split_quant(const void *x, int32_t xdt, int64_t rows, int64_t col
  *  xr    [outer = l, k = m]  (q_row of split_quant(X))
  *  mu_x  [outer = 1, k = m]  (q_mean of split_quant(X)), or NULL for the vanilla GEMM
  *  w     [outer = n, k = m]  (q_col of split_quant(W [m, n]) without SPLIT)
- *  y     device [l, n] row-major, element type ydt, leading dimension ldy >= n.
- * All operands share fmt and the HADAMARD16 bit.  m % 128 == 0.  The mean term is
+ *  y     device [l, n] row-major, element type ydt, leading dimension ldy >= n; n % 8 == 0.
+ * All operands share fmt and the HADAMARD16 bit.  The mean term is
  * computed once per call as a GEMV and added to every row in the GEMM epilogue.
  * ----------------------------------------------------------------------------------------- */
 size_t averis_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t fmt);
@@ -150,7 +154,7 @@ int32_t averis_linear_fwd(const averis_qtensor *xr, const averis_qtensor *mu_x,
  *  dr    [outer = l, k = n]  (q_row of split_quant(D))
  *  mu_d  [outer = 1, k = n]  or NULL (vanilla)
  *  w     [outer = m, k = n]  (q_row of split_quant(W [m, n]) without SPLIT)
- *  dx    device [l, m], element type dxdt, leading dimension lddx >= m.
+ *  dx    device [l, m], element type dxdt, leading dimension lddx >= m; m % 8 == 0.
  * ----------------------------------------------------------------------------------------- */
 int32_t averis_linear_bwd_dx(const averis_qtensor *dr, const averis_qtensor *mu_d,
                              const averis_qtensor *w, void *dx, int32_t dxdt, int64_t lddx,
@@ -165,7 +169,7 @@ int32_t averis_linear_bwd_dx(const averis_qtensor *dr, const averis_qtensor *mu_
  *  mu_x, mu_d  quantized means, both or neither (NULL, NULL = vanilla: no rank-one term).
  *        If they carry HADAMARD16 the rotation is undone before the outer product.
  *  l     the unpadded token count (the rank-one factor); must equal xr_t->k.
- *  dw    device fp32 [m, n], leading dimension lddw >= n.  AVERIS_ACCUMULATE: dw += result.
+ *  dw    device fp32 [m, n], leading dimension lddw >= n; n % 8 == 0.  AVERIS_ACCUMULATE: dw += result.
  * The token axis is split across workgroups with fp32 partials reduced in a fixed order.
  * ----------------------------------------------------------------------------------------- */
 size_t averis_linear_bwd_dw_workspace_size(int64_t m, int64_t n, int64_t l, int32_t fmt);

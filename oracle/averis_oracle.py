@@ -29,7 +29,7 @@ Readings where the pages are silent (all listed again in the design notes):
     all-zero codes.
   * each operand is quantized in blocks along its own GEMM's reduction axis, so X_R and D_R are
     each quantized twice (K = features for fwd/dX, K = tokens for dW), W twice (K = m, K = n).
-  * token-axis (K = rows) layouts are zero-padded, after subtraction, to a multiple of 128 rows.
+  * every layout is zero-padded along K, after subtraction, to a multiple of 256 elements.
   * the mean vector is quantized along its length with its own tensor scale; the optional
     16x16 Hadamard rotates every operand along its reduction axis (the mean too), and the
     weight-gradient rank-one term undoes the mean's rotation exactly.
@@ -42,7 +42,7 @@ import numpy as np
 NVFP4 = 1
 MXFP4 = 2
 BLOCK = {NVFP4: 16, MXFP4: 32}
-KPAD = 128  # storage padding multiple along K for the token-axis layouts
+KPAD = 256  # storage padding multiple along K (zero elements after the logical length)
 
 F32 = np.float32
 
@@ -316,9 +316,17 @@ def round_up(a, b):
     return (a + b - 1) // b * b
 
 
+def pad_k(r):
+    """Zero-pad the last axis of an fp32 operand to a multiple of KPAD."""
+    r = np.asarray(r, dtype=F32)
+    out = np.zeros((r.shape[0], round_up(r.shape[1], KPAD)), dtype=F32)
+    out[:, :r.shape[1]] = r
+    return out
+
+
 def split_quant(x, fmt, split=True, hadamard=False, mean=None):
-    """Returns dict(mu64, mu32, row=QTensor [rows, cols], col=QTensor [cols, rows_pad],
-    mean=QTensor [1, cols] or None).
+    """Returns dict(mu64, mu32, row=QTensor [rows, cols], col=QTensor [cols, rows],
+    mean=QTensor [1, cols] or None), each stored zero-padded along K to a multiple of KPAD.
 
     `mean` (fp32 [cols]) replaces the computed mean -- used to quantize with the exact mean
     vector another implementation produced.  split=False is the vanilla quantizer (also the
@@ -336,12 +344,9 @@ def split_quant(x, fmt, split=True, hadamard=False, mean=None):
     else:
         mu32 = None
         r = np.asarray(x, dtype=F32)
-    q_row = quantize(r, fmt, rotate=hadamard)
-    rp = round_up(rows, KPAD)
-    rt = np.zeros((cols, rp), dtype=F32)
-    rt[:, :rows] = r.T
-    q_col = quantize(rt, fmt, rotate=hadamard, k=rows)
-    q_mean = quantize(mu32[None, :], fmt, rotate=hadamard) if split else None
+    q_row = quantize(pad_k(r), fmt, rotate=hadamard, k=cols)
+    q_col = quantize(pad_k(r.T), fmt, rotate=hadamard, k=rows)
+    q_mean = quantize(pad_k(mu32[None, :]), fmt, rotate=hadamard, k=cols) if split else None
     return dict(mu64=mu64, mu32=mu32, row=q_row, col=q_col, mean=q_mean)
 
 
@@ -378,12 +383,12 @@ def dw_dense(xr_t, dr_t, mu_x, mu_d, l):
 def _mean_row(qm):
     """Dequantized mean for the weight-gradient rank-one term (rotation undone exactly)."""
     v = dequantize(qm)[0]
-    return unrotate16_f64(v) if qm.rotated else v
+    return (unrotate16_f64(v) if qm.rotated else v)[:qm.k]
 
 
 def linear_fwd(q_xr, q_mu, q_w):
     """Quantized forward GEMM: q_xr [l, m], q_mu [1, m] or None (vanilla), q_w [n, m]."""
-    mu = dequantize(q_mu)[0] if q_mu is not None else None
+    mu = dequantize(q_mu)[0, :q_mu.k] if q_mu is not None else None
     return fwd_dense(dequantize(q_xr)[:, :q_xr.k], mu, dequantize(q_w)[:, :q_w.k])
 
 
@@ -450,8 +455,8 @@ def relative_error(approx, exact):
 
 def reconstruct(sq, rows):
     """X ~ DQ(Q(X_R)) + 1 DQ(Q(mu)) from the row layout (unrotated operands only)."""
-    xr = dequantize(sq["row"])
+    xr = dequantize(sq["row"])[:, :sq["row"].k]
     if sq["mean"] is not None:
-        xr = xr + dequantize(sq["mean"])
+        xr = xr + dequantize(sq["mean"])[:, :sq["mean"].k]
     return xr[:rows]
 

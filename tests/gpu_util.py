@@ -14,10 +14,24 @@ def device():
     return torch.device("cuda:0")
 
 
+def untile_scales(tiled, outer, k_pad, g):
+    """Device scale layout (per 32-row group and 256-element K-step, 32 x 256/g contiguous
+    bytes) -> row-major [round_up(outer, 32), k_pad / g]."""
+    spb = 256 // g
+    t = np.asarray(tiled, np.uint8).reshape(-1)
+    rp = (outer + 31) // 32 * 32
+    t = t.reshape(rp // 32, k_pad // 256, 32, spb).transpose(0, 2, 1, 3)
+    return t.reshape(rp, k_pad // g)
+
+
+def row_scales(q):
+    return untile_scales(q.scales.cpu().numpy(), q.outer, q.k_pad, O.BLOCK[q.fmt])
+
+
 def to_oracle(q):
-    """Copy a device QTensor into the oracle's QTensor (same bytes)."""
+    """Copy a device QTensor into the oracle's QTensor (same bytes, scales untiled)."""
     ts = None if q.tensor_scale is None else np.float32(q.tensor_scale[0].item())
-    return O.QTensor(q.codes.cpu().numpy(), q.scales.cpu().numpy(), ts, q.fmt, q.k, q.rotated)
+    return O.QTensor(q.codes.cpu().numpy(), row_scales(q)[:q.outer], ts, q.fmt, q.k, q.rotated)
 
 
 def mean_ok(mu_gpu, x):
@@ -33,8 +47,10 @@ def mean_ok(mu_gpu, x):
 
 
 def assert_q_equal(g, o, what):
-    """Codes and scales bit-exact, NVFP4 tensor scale exact."""
-    gc, gs = g.codes.cpu().numpy(), g.scales.cpu().numpy()
+    """Codes and scales bit-exact, NVFP4 tensor scale exact; group-padding scale rows zero."""
+    gc, full = g.codes.cpu().numpy(), row_scales(g)
+    gs = full[:g.outer]
+    assert not full[g.outer:].any(), f"{what}: scale rows past outer are not zero"
     assert gc.shape == o.codes.shape and gs.shape == o.scales.shape, what
     if not np.array_equal(gs, o.scales):
         bad = np.argwhere(gs != o.scales)

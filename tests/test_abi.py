@@ -43,7 +43,7 @@ def test_abi_version_and_status_strings():
 
 
 def q(outer, k, fmt=av.NVFP4, flags=0, codes=FAKE, scales=FAKE, ts=FAKE):
-    kp = (k + 127) // 128 * 128
+    kp = (k + 255) // 256 * 256
     return av.CQTensor(codes, scales, ts, outer, k, kp, fmt, flags)
 
 
@@ -104,7 +104,7 @@ def lin(fn, a, mu, w, out=FAKE, odt=av.F32, ldo=None, ws=FAKE, wsb=1 << 30):
 @pytest.mark.parametrize("case,status", [
     ("mixed_fmt", E_FORMAT), ("k_mismatch", E_SHAPE), ("rot_mismatch", E_FLAGS), ("mu_shape", E_SHAPE),
     ("bad_dtype", E_DTYPE), ("small_ld", E_SHAPE), ("null_out", E_NULL), ("no_ws", E_WORKSPACE),
-    ("k_not_128", E_SHAPE),
+    ("bad_kpad", E_SHAPE),
 ])
 def test_linear_rejects(case, status):
     L = av.lib()
@@ -126,8 +126,8 @@ def test_linear_rejects(case, status):
         kw["out"] = None
     elif case == "no_ws":
         kw["ws"] = None
-    elif case == "k_not_128":
-        a, mu, w = q(256, 96), q(1, 96), q(384, 96)
+    elif case == "bad_kpad":
+        a = av.CQTensor(FAKE, FAKE, FAKE, 256, 512, 640, av.NVFP4, 0)
     for fn in (L.averis_linear_fwd, L.averis_linear_bwd_dx):
         assert lin(fn, a, mu, w, **kw) == status
 
