@@ -8,7 +8,7 @@ GEMM (bf16 dX) and the weight-gradient GEMM (fp32 dW) with the mean terms.  The 
 format is MXFP4 (gfx950's native scaled-MFMA format); NVFP4-style blocks are reported beside it.
 
 Timing: the step is captured once in a HIP graph; each timed replay is bracketed by HIP events
-on the launching stream, after a 512 MiB write that evicts the 256 MB Infinity Cache and the
+on the launching stream, after a 512 MiB read that evicts the 256 MB Infinity Cache and the
 L2, so inputs start in HBM.  value = GEMM flops of the step / step time.
 
 Prints one JSON line.  --gpus N > 1 is refused: everything here runs on one GPU.
@@ -72,7 +72,10 @@ def main():
     x = workloads.to_torch(lin.x, "bf16", dev)
     d = workloads.to_torch(lin.d, "bf16", dev)
     w = workloads.to_torch(lin.w, "bf16", dev)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # Cache eviction between timed replays: read (not write) 512 MiB, so the L2 and the 256 MB
+    # Infinity Cache end up holding clean lines of another buffer and the step pays no
+    # write-back of someone else's dirty data.
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     def timed(fn, steps, warmup):
@@ -86,7 +89,7 @@ def main():
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for i in range(steps):
-            flush.fill_(i & 255)
+            flush.sum()
             evs[i][0].record()
             g.replay()
             evs[i][1].record()

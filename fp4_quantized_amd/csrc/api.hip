@@ -98,16 +98,15 @@ int32_t averis_split_quant(const void* x, int32_t xdt, int64_t rows, int64_t col
 }
 
 size_t averis_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t fmt) {
-  (void)fmt;
   if (M < 0 || N < 0 || K < 0) return 0;
-  return gemm_ws_bytes(M, N, K, 1);
+  const int64_t kp = round_up(K, kKPad);
+  return gemm_ws_bytes(M, N, kp, choose_splits(fmt, M, N, kp));
 }
 
 size_t averis_linear_bwd_dw_workspace_size(int64_t m, int64_t n, int64_t l, int32_t fmt) {
-  (void)fmt;
   if (m < 0 || n < 0 || l < 0) return 0;
   const int64_t K = round_up(l, kKPad);
-  return gemm_ws_bytes(m, n, K, choose_splits(m, n, K));
+  return gemm_ws_bytes(m, n, K, choose_splits(fmt, m, n, K));
 }
 
 static int32_t linear_common(const averis_qtensor* a, const averis_qtensor* mu, const averis_qtensor* w, void* out,
@@ -130,11 +129,12 @@ static int32_t linear_common(const averis_qtensor* a, const averis_qtensor* mu, 
     if (!out) return AVERIS_E_NULL;
     if (!aligned16(out) || (ldo * elem_size(odt)) % 16 != 0) return AVERIS_E_ALIGN;
   }
-  if (!ws || ws_bytes < gemm_ws_bytes(a->outer, w->outer, a->k_pad, 1)) return AVERIS_E_WORKSPACE;
+  const int splits = choose_splits(a->fmt, a->outer, w->outer, a->k_pad);
+  if (!ws || ws_bytes < gemm_ws_bytes(a->outer, w->outer, a->k_pad, splits)) return AVERIS_E_WORKSPACE;
   if (!aligned16(ws)) return AVERIS_E_ALIGN;
   GemmPlan p{};
   p.a = a; p.b = w; p.c = out; p.ldc = ldo; p.c_bf16 = odt == AVERIS_BF16;
-  p.mu = mu; p.splits = 1; p.ws = ws; p.stream = reinterpret_cast<hipStream_t>(stream);
+  p.mu = mu; p.splits = splits; p.ws = ws; p.stream = reinterpret_cast<hipStream_t>(stream);
   return gemm_launch(p) == hipSuccess ? AVERIS_OK : AVERIS_E_HIP;
 }
 
@@ -172,7 +172,7 @@ int32_t averis_linear_bwd_dw(const averis_qtensor* xr_t, const averis_qtensor* d
     if (!dw) return AVERIS_E_NULL;
     if (!aligned16(dw) || (lddw * 4) % 16 != 0) return AVERIS_E_ALIGN;
   }
-  const int splits = choose_splits(m, n, xr_t->k_pad);
+  const int splits = choose_splits(xr_t->fmt, m, n, xr_t->k_pad);
   if (!ws || ws_bytes < gemm_ws_bytes(m, n, xr_t->k_pad, splits)) return AVERIS_E_WORKSPACE;
   if (!aligned16(ws)) return AVERIS_E_ALIGN;
   GemmPlan p{};

@@ -20,8 +20,6 @@
 // barrier per K-step, no fence: each wave waits on its own vmcnt, then all meet at s_barrier.
 // Epilogue: out = alpha * acc + bias[col] + r1 * u[row] * v[col] (+ C when accumulating),
 // alpha = product of the operands' tensor decode scales (NVFP4) or 1.
-#include <cstdlib>
-
 #include "launch.h"
 
 namespace av {
@@ -34,9 +32,6 @@ struct GemmArgs {
   void* c; int64_t ldc; int c_bf16;     // output (or split-K partials base when splits > 1)
   const float* bias;                    // [N] or nullptr
   const float* r1u; const float* r1v; float r1;  // rank-one term r1 * u[row] * v[col], or nullptr
-  // rank-one vectors decoded in the epilogue from unrotated quantized means (when r1u is null)
-  const uint8_t* mu_codes; const uint8_t* mu_scales; const float* mu_ts; int64_t mu_kpad;
-  const uint8_t* mv_codes; const uint8_t* mv_scales; const float* mv_ts; int64_t mv_kpad;
   int accumulate;
   int splits; int64_t k_chunk;          // K range per split (multiple of the K-step), partials at c + s * M * N
   int tiles_m, tiles_n;
@@ -261,9 +256,11 @@ struct GemmTile {
           for (int j = 0; j < TN; ++j) {
             const v8i av = {(int)fa[i].x, (int)fa[i].y, (int)fa[i].z, (int)fa[i].w, 0, 0, 0, 0};
             const v8i bv = {(int)fb[j].x, (int)fb[j].y, (int)fb[j].z, (int)fb[j].w, 0, 0, 0, 0};
+            // B rows feed the MFMA's first operand, so a lane ends up holding four consecutive
+            // output columns of one output row
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                av, bv, acc[i][j], 4, 4, 0, (int)__builtin_amdgcn_ubfe(sa[i][0], 8 * kk, 8), 0,
-                (int)__builtin_amdgcn_ubfe(sb[j][0], 8 * kk, 8));
+                bv, av, acc[i][j], 4, 4, 0, (int)__builtin_amdgcn_ubfe(sb[j][0], 8 * kk, 8), 0,
+                (int)__builtin_amdgcn_ubfe(sa[i][0], 8 * kk, 8));
           }
       } else {
         v8bf da[TM][4], db[TN][4];
@@ -284,7 +281,7 @@ struct GemmTile {
           for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[i][q], db[j][q], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(db[j][q], da[i][q], acc[i][j], 0, 0, 0);
       }
     }
   }
@@ -304,6 +301,89 @@ __device__ __forceinline__ void pipe_step(T& t, int step, int nsteps, int kb_byt
   const bool live = ns < nsteps;
   t.issue(live ? kb_byte + ns * C::BKB : 0, live ? kb_sbyte + ns * C::PIECE : 0, nxt);
   if (step < nsteps) t.compute(cur);
+}
+
+__device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// out = alpha * acc (+ bias[col]) (+ r1 * u[row] * v[col]) for CW consecutive columns, each
+// step rounded once in fp32.
+template <int CW>
+__device__ __forceinline__ void finish_cols(const GemmArgs& g, float* v, int64_t row, int64_t col, float alpha) {
+#pragma unroll
+  for (int e = 0; e < CW; ++e) v[e] = __fmul_rn(v[e], alpha);
+  if (g.bias) {
+#pragma unroll
+    for (int e = 0; e < CW; e += 4) {
+      const float4 b = *reinterpret_cast<const float4*>(g.bias + col + e);
+      v[e] = __fadd_rn(v[e], b.x); v[e + 1] = __fadd_rn(v[e + 1], b.y);
+      v[e + 2] = __fadd_rn(v[e + 2], b.z); v[e + 3] = __fadd_rn(v[e + 3], b.w);
+    }
+  }
+  if (g.r1u) {
+    const float ur = __fmul_rn(g.r1, g.r1u[row]);
+#pragma unroll
+    for (int e = 0; e < CW; e += 4) {
+      const float4 b = *reinterpret_cast<const float4*>(g.r1v + col + e);
+      v[e] = __fadd_rn(v[e], __fmul_rn(ur, b.x)); v[e + 1] = __fadd_rn(v[e + 1], __fmul_rn(ur, b.y));
+      v[e + 2] = __fadd_rn(v[e + 2], __fmul_rn(ur, b.z)); v[e + 3] = __fadd_rn(v[e + 3], __fmul_rn(ur, b.w));
+    }
+  }
+}
+
+// Copy one staged 32 x W fp32 slab (row stride LD floats) to C: each lane moves 16 output
+// bytes of one row per pass (8 bf16 or 4 fp32 columns), so each store instruction writes
+// whole row segments.  Split-K partials get alpha * acc only.
+template <int W, int LD>
+__device__ __forceinline__ void store_slab(const GemmArgs& g, const float* epi, int64_t rbase, int64_t cbase, float alpha,
+                                           int split, int lane) {
+  if (g.splits > 1) {
+    constexpr int LPR = W / 4, NQ = 32 * LPR;
+#pragma unroll 1
+    for (int q = lane; q < NQ; q += 64) {
+      const int rr = q / LPR, ch = q % LPR;
+      const int64_t row = rbase + rr, col = cbase + ch * 4;
+      if (row < g.M && col < g.N) {
+        float4 v = *reinterpret_cast<const float4*>(epi + rr * LD + ch * 4);
+        v.x = __fmul_rn(v.x, alpha); v.y = __fmul_rn(v.y, alpha); v.z = __fmul_rn(v.z, alpha); v.w = __fmul_rn(v.w, alpha);
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.c) + (int64_t)split * g.M * g.N + row * g.N + col) = v;
+      }
+    }
+  } else if (g.c_bf16) {
+    constexpr int LPR = W / 8, NQ = 32 * LPR;
+#pragma unroll 1
+    for (int q = lane; q < NQ; q += 64) {
+      const int rr = q / LPR, ch = q % LPR;
+      const int64_t row = rbase + rr, col = cbase + ch * 8;
+      if (row < g.M && col < g.N) {
+        float v[8];
+        *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(epi + rr * LD + ch * 8);
+        *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(epi + rr * LD + ch * 8 + 4);
+        finish_cols<8>(g, v, row, col, alpha);
+        uint4 o;
+        o.x = pack_bf16x2(v[0], v[1]); o.y = pack_bf16x2(v[2], v[3]);
+        o.z = pack_bf16x2(v[4], v[5]); o.w = pack_bf16x2(v[6], v[7]);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.c) + row * g.ldc + col) = o;
+      }
+    }
+  } else {
+    constexpr int LPR = W / 4, NQ = 32 * LPR;
+#pragma unroll 1
+    for (int q = lane; q < NQ; q += 64) {
+      const int rr = q / LPR, ch = q % LPR;
+      const int64_t row = rbase + rr, col = cbase + ch * 4;
+      if (row < g.M && col < g.N) {
+        float v[4];
+        *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(epi + rr * LD + ch * 4);
+        finish_cols<4>(g, v, row, col, alpha);
+        float* dst = reinterpret_cast<float*>(g.c) + row * g.ldc + col;
+        if (g.accumulate) {
+          const float4 o = *reinterpret_cast<const float4*>(dst);
+          v[0] = __fadd_rn(o.x, v[0]); v[1] = __fadd_rn(o.y, v[1]); v[2] = __fadd_rn(o.z, v[2]); v[3] = __fadd_rn(o.w, v[3]);
+        }
+        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
 }
 
 template <int FMT, int WM, int WN, int TM, int TN, int STAGES, int AUX = 0>
@@ -352,106 +432,59 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs g) {
   __builtin_amdgcn_s_barrier();  // every wave is done reading the stages
 
   // ---- epilogue: per 32-row slab, stage the wave's fp32 tile in LDS, then 16-byte stores ----
+  // acc[i][j][4q + r] is C[row i*32 + lane%32][col j*32 + 8q + 4(lane/32) + r] of the wave tile.
   const int lane = threadIdx.x & 63, fr = lane & 31, fk = lane >> 5;
   const int wave = t.wave, wm = t.wm, wn = t.wn;
   float* epi = reinterpret_cast<float*>((wave < (C::NW + 1) / 2 ? st0 : st1) + (wave % ((C::NW + 1) / 2)) * C::EPI_WAVE);
   float alpha = 1.0f;
   if (FMT == AVERIS_NVFP4) alpha = __fmul_rn(g.a_ts[0], g.b_ts[0]);
-  const bool partial = g.splits > 1;
-  const bool r1_direct = !partial && g.r1u == nullptr && g.mu_codes != nullptr;
-  const bool r1_vec = !partial && g.r1u != nullptr;
-  float bcol[TN], vcol[TN];
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int64_t col = n0 + wn * TN * 32 + j * 32 + fr;
-    const bool cin = col < g.N;
-    bcol[j] = (!partial && g.bias && cin) ? g.bias[col] : 0.0f;
-    vcol[j] = 0.0f;
-    if (r1_vec && cin) vcol[j] = g.r1v[col];
-    if (r1_direct && cin) vcol[j] = dq_one<FMT>(g.mv_codes, g.mv_scales, g.mv_ts, col, g.mv_kpad);
-  }
-  constexpr int W = TN * 32;  // columns of the wave tile
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t rbase = m0 + wm * TM * 32 + i * 32;
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int rr = (e >> 2) * 8 + fk * 4 + (e & 3);
-        float out = __fmul_rn(t.acc[i][j][e], alpha);
-        if (!partial) {
-          out = __fadd_rn(out, bcol[j]);
-          if (r1_vec || r1_direct) {
-            const int64_t row = rbase + rr;
-            float urow = 0.0f;
-            if (row < g.M) urow = r1_vec ? g.r1u[row] : dq_one<FMT>(g.mu_codes, g.mu_scales, g.mu_ts, row, g.mu_kpad);
-            out = __fadd_rn(out, __fmul_rn(__fmul_rn(g.r1, urow), vcol[j]));
-          }
-        }
-        epi[rr * C::EPI_LD + j * 32 + fr] = out;
-      }
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // this wave's LDS writes done
-    // copy-out: every store instruction writes whole contiguous row segments of 16-byte chunks
-    if (g.c_bf16 && !partial) {
-      constexpr int LPR = W * 2 / 16, RPI = 64 / LPR;  // lanes per row, rows per instruction
-      const int lr = lane / LPR, ch = lane % LPR;
-      const int64_t gcol = n0 + wn * W + ch * 8;
-#pragma unroll
-      for (int p = 0; p < 32 / RPI; ++p) {
-        const int rr = p * RPI + lr;
-        const int64_t row = rbase + rr;
-        if (row < g.M && gcol < g.N) {
-          const float* src = epi + rr * C::EPI_LD + ch * 8;
-          const float4 a = *reinterpret_cast<const float4*>(src), b = *reinterpret_cast<const float4*>(src + 4);
-          uint4 o;
-          o.x = pack_bf16x2(a.x, a.y); o.y = pack_bf16x2(a.z, a.w);
-          o.z = pack_bf16x2(b.x, b.y); o.w = pack_bf16x2(b.z, b.w);
-          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.c) + row * g.ldc + gcol) = o;
-        }
-      }
-    } else {
-      constexpr int LPR = W * 4 / 16, RPI = 64 / LPR;
-      const int lr = lane / LPR, ch = lane % LPR;
-      const int64_t gcol = n0 + wn * W + ch * 4;
-#pragma unroll
-      for (int p = 0; p < 32 / RPI; ++p) {
-        const int rr = p * RPI + lr;
-        const int64_t row = rbase + rr;
-        if (row < g.M && gcol < g.N) {
-          float4 v = *reinterpret_cast<const float4*>(epi + rr * C::EPI_LD + ch * 4);
-          float* dst = partial ? reinterpret_cast<float*>(g.c) + (int64_t)split * g.M * g.N + row * g.N + gcol
-                               : reinterpret_cast<float*>(g.c) + row * g.ldc + gcol;
-          if (!partial && g.accumulate) {
-            const float4 o = *reinterpret_cast<const float4*>(dst);
-            v.x = __fadd_rn(o.x, v.x); v.y = __fadd_rn(o.y, v.y); v.z = __fadd_rn(o.z, v.z); v.w = __fadd_rn(o.w, v.w);
-          }
-          *reinterpret_cast<float4*>(dst) = v;
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // reads done before the next slab
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(epi + fr * C::EPI_LD + j * 32 + q * 8 + fk * 4) =
+            make_float4(t.acc[i][j][4 * q], t.acc[i][j][4 * q + 1], t.acc[i][j][4 * q + 2], t.acc[i][j][4 * q + 3]);
+    lgkm_wait0();  // this wave's staging writes are done
+    store_slab<TN * 32, C::EPI_LD>(g, epi, m0 + wm * TM * 32 + i * 32, n0 + wn * TN * 32, alpha, split, lane);
+    lgkm_wait0();  // its reads are done before the next slab overwrites the staging area
   }
 }
 
-// Split-K reduce: C = (accumulate ? C : 0) + sum_s P[s] (fixed order) + r1 * u[row] * v[col].
+// Split-K reduce: C = (accumulate ? C : 0) + (sum_s P[s] in split order + bias[col]
+// + r1 * u[row] * v[col]), four columns per thread (N % 8 == 0); fp32 or bf16 output.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int splits, GemmArgs g,
-                                                       float* __restrict__ c, int64_t ldc) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= g.M * g.N) return;
-  const int64_t row = idx / g.N, col = idx % g.N;
-  float s = part[idx];
-  for (int p = 1; p < splits; ++p) s = __fadd_rn(s, part[(int64_t)p * g.M * g.N + idx]);
-  if (g.r1u) {
-    s = __fadd_rn(s, __fmul_rn(__fmul_rn(g.r1, g.r1u[row]), g.r1v[col]));
-  } else if (g.mu_codes) {
-    const float u = dq_one<FMT>(g.mu_codes, g.mu_scales, g.mu_ts, row, g.mu_kpad);
-    const float v = dq_one<FMT>(g.mv_codes, g.mv_scales, g.mv_ts, col, g.mv_kpad);
-    s = __fadd_rn(s, __fmul_rn(__fmul_rn(g.r1, u), v));
+                                                       void* __restrict__ c, int64_t ldc, int c_bf16) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nq = g.N / 4;
+  if (q >= g.M * nq) return;
+  const int64_t row = q / nq, col = (q % nq) * 4;
+  const int64_t idx = row * g.N + col;
+  float4 s = *reinterpret_cast<const float4*>(part + idx);
+  for (int p = 1; p < splits; ++p) {
+    const float4 t = *reinterpret_cast<const float4*>(part + (int64_t)p * g.M * g.N + idx);
+    s.x = __fadd_rn(s.x, t.x); s.y = __fadd_rn(s.y, t.y); s.z = __fadd_rn(s.z, t.z); s.w = __fadd_rn(s.w, t.w);
   }
-  float* dst = c + row * ldc + col;
-  *dst = g.accumulate ? __fadd_rn(*dst, s) : s;
+  float v[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (g.bias) v[e] = __fadd_rn(v[e], g.bias[col + e]);
+    if (g.r1u) v[e] = __fadd_rn(v[e], __fmul_rn(__fmul_rn(g.r1, g.r1u[row]), g.r1v[col + e]));
+  }
+  if (c_bf16) {
+    uint2 o;
+    o.x = pack_bf16x2(v[0], v[1]); o.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(c) + row * ldc + col) = o;
+  } else {
+    float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(c) + row * ldc + col);
+    if (g.accumulate) {
+      const float4 o = *dst;
+      v[0] = __fadd_rn(o.x, v[0]); v[1] = __fadd_rn(o.y, v[1]); v[2] = __fadd_rn(o.z, v[2]); v[3] = __fadd_rn(o.w, v[3]);
+    }
+    *dst = make_float4(v[0], v[1], v[2], v[3]);
+  }
 }
 
 // Mean-term GEMV: out[j] = alpha * sum_k DQ(mu)[k] DQ(B)[j][k], one wave per output row.
@@ -500,12 +533,14 @@ __global__ __launch_bounds__(256) void k_gemv_mean(const uint8_t* __restrict__ m
   }
 }
 
-// Dequantized, un-rotated mean vectors for the rank-one dW term (used only for rotated means).
+// Dequantized mean vectors for the rank-one dW term, un-rotated when the means were quantized
+// after the 16x16 Hadamard rotation (rot != 0).
 template <int FMT>
 __global__ __launch_bounds__(256) void k_mean_vec(const uint8_t* __restrict__ c0, const uint8_t* __restrict__ s0,
                                                   const float* __restrict__ t0, int64_t K0, int64_t P0, float* __restrict__ o0,
                                                   const uint8_t* __restrict__ c1, const uint8_t* __restrict__ s1,
-                                                  const float* __restrict__ t1, int64_t K1, int64_t P1, float* __restrict__ o1) {
+                                                  const float* __restrict__ t1, int64_t K1, int64_t P1, float* __restrict__ o1,
+                                                  int rot) {
   const int64_t n0 = (K0 + 15) / 16;
   int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const uint8_t *codes = c0, *scales = s0;
@@ -517,14 +552,17 @@ __global__ __launch_bounds__(256) void k_mean_vec(const uint8_t* __restrict__ c0
   double v[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) v[j] = (double)dq_one<FMT>(codes, scales, ts, blk * 16 + j, P);
+  if (rot) {
 #pragma unroll
-  for (int h = 1; h < 16; h <<= 1)
+    for (int h = 1; h < 16; h <<= 1)
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if ((j & h) == 0) { const double a = v[j], b = v[j + h]; v[j] = a + b; v[j + h] = a - b; }
+      for (int j = 0; j < 16; ++j)
+        if ((j & h) == 0) { const double a = v[j], b = v[j + h]; v[j] = a + b; v[j + h] = a - b; }
+  }
+  const double sc = rot ? 0.25 : 1.0;
 #pragma unroll
   for (int j = 0; j < 16; ++j)
-    if (blk * 16 + j < K) out[blk * 16 + j] = (float)(v[j] * 0.25);
+    if (blk * 16 + j < K) out[blk * 16 + j] = (float)(v[j] * sc);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -532,23 +570,35 @@ __global__ __launch_bounds__(256) void k_mean_vec(const uint8_t* __restrict__ c0
 // ------------------------------------------------------------------------------------------
 static int g_count(int fmt) { return fmt == AVERIS_MXFP4 ? 32 : 16; }
 
-// Tile configurations: waves along M x N, 32x32 MFMA tiles per wave along M x N, LDS stages.
+// Tile configurations (waves along M x N, 32x32 MFMA tiles per wave along M x N, LDS stages).
+// Larger wave tiles cut LDS fragment reads per MFMA: a wave with TM x TN tiles reads
+// (TM + TN) KB per TM * TN scaled MFMAs each 64-element substep.
 struct TileCfg { int bm, bn; };
-static int tuning_cfg() {
-  static int c = [] { const char* e = getenv("AVERIS_GEMM_CFG"); return e ? atoi(e) : 0; }();
-  return c;
-}
 static TileCfg tile_of(int cfg) {
   switch (cfg) {
-    case 3: case 7: return {256, 128};
-    case 4: return {128, 256};
-    case 8: return {256, 256};
+    case 1: return {256, 256};
+    case 2: case 5: return {256, 128};
+    case 3: return {128, 256};
+    case 4: return {256, 192};
     default: return {128, 128};
   }
 }
 constexpr int kBKE = 256;
-int choose_splits(int64_t M, int64_t N, int64_t K) {
-  const TileCfg tc = tile_of(tuning_cfg());
+
+// Configuration per format and shape.
+// Measured on MI355X with the Qwen3-0.6B-shaped linears: 128 x 128 tiles win at these sizes.
+// Short K (the forward and input-gradient GEMMs): two stages, two workgroups per CU, so one
+// workgroup's epilogue overlaps the other's main loop.  Long K (weight gradients over the
+// token dimension): three stages, one workgroup per CU, deeper prefetch.
+static bool cfg_valid(int fmt, int cfg);
+static int pick_cfg(int fmt, int64_t M, int64_t N, int64_t K) {
+  (void)M; (void)N;
+  const int c = K >= 4096 ? 0 : 6;
+  return cfg_valid(fmt, c) ? c : 0;
+}
+
+static int splits_for(int cfg, int64_t M, int64_t N, int64_t K) {
+  const TileCfg tc = tile_of(cfg);
   const int64_t tiles = ceil_div(M, tc.bm) * ceil_div(N, tc.bn);
   if (tiles >= 192) return 1;
   int64_t s = ceil_div(256, tiles > 0 ? tiles : 1);
@@ -557,9 +607,11 @@ int choose_splits(int64_t M, int64_t N, int64_t K) {
   if (s > 8) s = 8;
   return s < 1 ? 1 : (int)s;
 }
+int choose_splits(int fmt, int64_t M, int64_t N, int64_t K) { return splits_for(pick_cfg(fmt, M, N, K), M, N, K); }
 
-// workspace: [256 B][bias N][u M][v N] fp32, then split-K partials [splits][M][N] fp32
-static size_t partials_offset(int64_t M, int64_t N) { return 256 + (size_t)round_up((N + M + N) * 4, 1024); }
+// workspace: [256 B][bias N][u round_up(M, 4)][v N] fp32 (16-byte aligned vectors), then
+// split-K partials [splits][M][N] fp32
+static size_t partials_offset(int64_t M, int64_t N) { return 256 + (size_t)round_up((N + round_up(M, 4) + N) * 4, 1024); }
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int splits) {
   size_t b = partials_offset(M, N);
@@ -567,20 +619,29 @@ size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int splits) {
   return b;
 }
 
-template <int FMT>
-static void launch_fmt(const GemmArgs& g, unsigned grid, hipStream_t s) {
-  switch (tuning_cfg()) {
-    case 1: hipLaunchKernelGGL((k_gemm<FMT, 2, 2, 2, 2, 2>), dim3(grid), dim3(256), 0, s, g); break;
-    case 2: hipLaunchKernelGGL((k_gemm<FMT, 2, 2, 2, 2, 4>), dim3(grid), dim3(256), 0, s, g); break;
-    case 3: hipLaunchKernelGGL((k_gemm<FMT, 2, 2, 4, 2, 2>), dim3(grid), dim3(256), 0, s, g); break;
-    case 4: hipLaunchKernelGGL((k_gemm<FMT, 2, 4, 2, 2, 2>), dim3(grid), dim3(512), 0, s, g); break;
-    case 5: hipLaunchKernelGGL((k_gemm<FMT, 2, 2, 2, 2, 2, 1>), dim3(grid), dim3(256), 0, s, g); break;
-    case 6: hipLaunchKernelGGL((k_gemm<FMT, 2, 2, 2, 2, 2, 2>), dim3(grid), dim3(256), 0, s, g); break;
-    case 7: hipLaunchKernelGGL((k_gemm<FMT, 4, 2, 2, 2, 2>), dim3(grid), dim3(512), 0, s, g); break;
-    case 8: hipLaunchKernelGGL((k_gemm<FMT, 2, 4, 4, 2, 2>), dim3(grid), dim3(512), 0, s, g); break;
-    default: hipLaunchKernelGGL((k_gemm<FMT, 2, 2, 2, 2, 3>), dim3(grid), dim3(256), 0, s, g); break;
+// MXFP4 takes every configuration; NVFP4 (bf16 MFMAs on dequantized fragments, 16 scale bytes
+// per row and K-step) only those whose registers and LDS fit.
+static void launch_mx(int cfg, const GemmArgs& g, unsigned grid, hipStream_t s) {
+  constexpr int F = AVERIS_MXFP4;
+  switch (cfg) {
+    case 1: hipLaunchKernelGGL((k_gemm<F, 2, 2, 4, 4, 2>), dim3(grid), dim3(256), 0, s, g); break;
+    case 2: hipLaunchKernelGGL((k_gemm<F, 2, 2, 4, 2, 3>), dim3(grid), dim3(256), 0, s, g); break;
+    case 3: hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 4, 3>), dim3(grid), dim3(256), 0, s, g); break;
+    case 4: hipLaunchKernelGGL((k_gemm<F, 2, 2, 4, 3, 2>), dim3(grid), dim3(256), 0, s, g); break;
+    case 5: hipLaunchKernelGGL((k_gemm<F, 2, 2, 4, 2, 2>), dim3(grid), dim3(256), 0, s, g); break;
+    case 6: hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 2>), dim3(grid), dim3(256), 0, s, g); break;
+    default: hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 3>), dim3(grid), dim3(256), 0, s, g); break;
   }
 }
+static void launch_nv(int cfg, const GemmArgs& g, unsigned grid, hipStream_t s) {
+  constexpr int F = AVERIS_NVFP4;
+  switch (cfg) {
+    case 5: hipLaunchKernelGGL((k_gemm<F, 2, 2, 4, 2, 2>), dim3(grid), dim3(256), 0, s, g); break;
+    case 6: hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 2>), dim3(grid), dim3(256), 0, s, g); break;
+    default: hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 3>), dim3(grid), dim3(256), 0, s, g); break;
+  }
+}
+static bool cfg_valid(int fmt, int cfg) { return fmt == AVERIS_MXFP4 ? (cfg >= 0 && cfg <= 6) : (cfg == 0 || cfg == 5 || cfg == 6); }
 
 hipError_t gemm_launch(const GemmPlan& p) {
   const averis_qtensor& A = *p.a;
@@ -589,7 +650,7 @@ hipError_t gemm_launch(const GemmPlan& p) {
   uint8_t* ws = reinterpret_cast<uint8_t*>(p.ws);
   float* bias = reinterpret_cast<float*>(ws + 256);
   float* u = bias + B.outer;
-  float* v = u + A.outer;
+  float* v = u + round_up(A.outer, 4);
   float* partials = reinterpret_cast<float*>(ws + partials_offset(A.outer, B.outer));
 
   GemmArgs g{};
@@ -597,7 +658,8 @@ hipError_t gemm_launch(const GemmPlan& p) {
   g.b_codes = B.codes; g.b_scales = B.scales; g.ldb_b = B.k_pad / 2;
   g.a_ts = A.tensor_scale; g.b_ts = B.tensor_scale;
   g.M = A.outer; g.N = B.outer; g.K = A.k_pad;
-  const TileCfg tc = tile_of(tuning_cfg());
+  const int cfg = pick_cfg(fmt, g.M, g.N, g.K);
+  const TileCfg tc = tile_of(cfg);
   g.tiles_m = (int)ceil_div(g.M, tc.bm); g.tiles_n = (int)ceil_div(g.N, tc.bn);
   {
     // group height ~ sqrt of the tiles each XCD owns, so its block of tiles is near square
@@ -624,19 +686,15 @@ hipError_t gemm_launch(const GemmPlan& p) {
     g.r1 = p.r1;
     const averis_qtensor& Qu = *p.mu_u;
     const averis_qtensor& Qv = *p.mu_v;
-    if (Qu.flags & AVERIS_HADAMARD16) {
-      const unsigned blocks = (unsigned)ceil_div(ceil_div(Qu.k, 16) + ceil_div(Qv.k, 16), 256);
-      if (fmt == AVERIS_MXFP4)
-        hipLaunchKernelGGL(k_mean_vec<AVERIS_MXFP4>, dim3(blocks), dim3(256), 0, p.stream, Qu.codes, Qu.scales,
-                           Qu.tensor_scale, Qu.k, Qu.k_pad, u, Qv.codes, Qv.scales, Qv.tensor_scale, Qv.k, Qv.k_pad, v);
-      else
-        hipLaunchKernelGGL(k_mean_vec<AVERIS_NVFP4>, dim3(blocks), dim3(256), 0, p.stream, Qu.codes, Qu.scales,
-                           Qu.tensor_scale, Qu.k, Qu.k_pad, u, Qv.codes, Qv.scales, Qv.tensor_scale, Qv.k, Qv.k_pad, v);
-      g.r1u = u; g.r1v = v;
-    } else {
-      g.mu_codes = Qu.codes; g.mu_scales = Qu.scales; g.mu_ts = Qu.tensor_scale; g.mu_kpad = Qu.k_pad;
-      g.mv_codes = Qv.codes; g.mv_scales = Qv.scales; g.mv_ts = Qv.tensor_scale; g.mv_kpad = Qv.k_pad;
-    }
+    const int rot = (Qu.flags & AVERIS_HADAMARD16) ? 1 : 0;
+    const unsigned blocks = (unsigned)ceil_div(ceil_div(Qu.k, 16) + ceil_div(Qv.k, 16), 256);
+    if (fmt == AVERIS_MXFP4)
+      hipLaunchKernelGGL(k_mean_vec<AVERIS_MXFP4>, dim3(blocks), dim3(256), 0, p.stream, Qu.codes, Qu.scales,
+                         Qu.tensor_scale, Qu.k, Qu.k_pad, u, Qv.codes, Qv.scales, Qv.tensor_scale, Qv.k, Qv.k_pad, v, rot);
+    else
+      hipLaunchKernelGGL(k_mean_vec<AVERIS_NVFP4>, dim3(blocks), dim3(256), 0, p.stream, Qu.codes, Qu.scales,
+                         Qu.tensor_scale, Qu.k, Qu.k_pad, u, Qv.codes, Qv.scales, Qv.tensor_scale, Qv.k, Qv.k_pad, v, rot);
+    g.r1u = u; g.r1v = v;
   }
   g.splits = p.splits;
   const int64_t ksteps = ceil_div(g.K, kBKE);
@@ -647,16 +705,16 @@ hipError_t gemm_launch(const GemmPlan& p) {
     g.c = p.c; g.ldc = p.ldc; g.c_bf16 = p.c_bf16;
   }
   const unsigned grid = (unsigned)(g.tiles_m * g.tiles_n * p.splits);
-  if (fmt == AVERIS_MXFP4) launch_fmt<AVERIS_MXFP4>(g, grid, p.stream);
-  else launch_fmt<AVERIS_NVFP4>(g, grid, p.stream);
+  if (fmt == AVERIS_MXFP4) launch_mx(cfg, g, grid, p.stream);
+  else launch_nv(cfg, g, grid, p.stream);
   if (p.splits > 1) {
-    const int64_t n = g.M * g.N;
+    const unsigned blocks = (unsigned)ceil_div(g.M * (g.N / 4), 256);
     if (fmt == AVERIS_MXFP4)
-      hipLaunchKernelGGL(k_splitk_reduce<AVERIS_MXFP4>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, p.stream,
-                         partials, p.splits, g, reinterpret_cast<float*>(p.c), p.ldc);
+      hipLaunchKernelGGL(k_splitk_reduce<AVERIS_MXFP4>, dim3(blocks), dim3(256), 0, p.stream, partials, p.splits, g, p.c,
+                         p.ldc, p.c_bf16);
     else
-      hipLaunchKernelGGL(k_splitk_reduce<AVERIS_NVFP4>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, p.stream,
-                         partials, p.splits, g, reinterpret_cast<float*>(p.c), p.ldc);
+      hipLaunchKernelGGL(k_splitk_reduce<AVERIS_NVFP4>, dim3(blocks), dim3(256), 0, p.stream, partials, p.splits, g, p.c,
+                         p.ldc, p.c_bf16);
   }
   return hipGetLastError();
 }

@@ -26,7 +26,7 @@ struct GemmPlan {
   void* ws;
   hipStream_t stream;
 };
-int choose_splits(int64_t M, int64_t N, int64_t K);
+int choose_splits(int fmt, int64_t M, int64_t N, int64_t K);
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int splits);
 hipError_t gemm_launch(const GemmPlan& p);
 

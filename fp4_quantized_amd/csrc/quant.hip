@@ -9,135 +9,23 @@
 // in registers between the load of X and the store of its FP4 codes.
 //
 // Pass structure (X is read twice; the second read usually hits the 256 MB Infinity Cache):
-//   k_stats     per-slab column sum (fp64 over fp32 groups of 8 rows), min and max
-//   k_finalize  fixed-order reduction of the slabs -> mu (fp32), residual amax from min/max
-//               (exact: fl(x - mu) is monotone in x), integer atomic max into one slot
-//   k_quant_mean  Q_b of the mean vector (own tensor scale), optional rotation
+//   k_colstats  per-slab (128 rows) column sums: fp32 over 8 rows, fp64 beyond; NVFP4 also
+//               column min and max
+//   k_finalize  fixed-order reduction of the slabs -> mu (fp32); per-workgroup maxima of the
+//               residual (exact from min / max: fl(x - mu) is monotone in x) and of the mean
 //   k_quant     re-read a 64-row tile, subtract, rotate, block amax, scale, E2M1, and emit
 //               both layouts: K = features (row layout) from registers, K = tokens (column
-//               layout) through an LDS transpose.  With NVFP4 + Hadamard the rotated amax is
-//               not available from min/max, so k_quant first runs once in amax-only mode.
+//               layout) through an LDS transpose; row tile 0 also quantizes the mean, and each
+//               tile zeroes the padding it owns.  With NVFP4 + Hadamard the rotated amax is
+//               not available from min / max, so k_quant first runs once in amax-only mode.
+// A vanilla MXFP4 operand (no split) needs k_quant only.
 #include "launch.h"
 
 namespace av {
 
 constexpr int kThreads = 256;
-constexpr int kSlab = 256;     // rows per k_stats workgroup
-constexpr int kTileRows = 64;  // rows per k_quant tile
-
-// ------------------------------------------------------------------------------------------
-// k_stats: grid (ceil(cols / TC), nslab); TC = 32 lanes * VEC columns.  Thread t covers VEC
-// columns at (t % 32) * VEC and rows slab0 + t / 32 + 8 i.
-// ------------------------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(kThreads) void k_stats(const T* __restrict__ x, int64_t rows, int64_t cols,
-                                                    int64_t ldx, double* __restrict__ psum,
-                                                    float* __restrict__ pmin, float* __restrict__ pmax,
-                                                    uint32_t* __restrict__ amax_slots) {
-  constexpr int VEC = Elem<T>::VEC;
-  constexpr int TC = 32 * VEC;
-  __shared__ double s_sum[8][TC];
-  __shared__ float s_min[8][TC];
-  __shared__ float s_max[8][TC];
-
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 4) amax_slots[threadIdx.x] = 0u;
-
-  const int lane_c = threadIdx.x & 31, phase = threadIdx.x >> 5;
-  const int64_t c0 = (int64_t)blockIdx.x * TC + lane_c * VEC;
-  const int64_t r_begin = (int64_t)blockIdx.y * kSlab;
-  const int64_t r_end = r_begin + kSlab < rows ? r_begin + kSlab : rows;
-  const bool col_ok = c0 < cols;
-
-  double sum[VEC];
-  float mn[VEC], mx[VEC];
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) { sum[j] = 0.0; mn[j] = __builtin_huge_valf(); mx[j] = -__builtin_huge_valf(); }
-
-  if (col_ok) {
-    // groups of 8 rows per thread: fp32 partial over the group, then one fp64 add
-    for (int64_t g = r_begin + phase; g < r_end; g += 8 * 8) {
-      uint4 w[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t r = g + 8 * i;
-        w[i] = r < r_end ? *reinterpret_cast<const uint4*>(x + r * ldx + c0) : make_uint4(0, 0, 0, 0);
-      }
-      float part[VEC];
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) part[j] = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (g + 8 * i < r_end) {
-          float v[VEC];
-          Elem<T>::unpack(w[i], v);
-#pragma unroll
-          for (int j = 0; j < VEC; ++j) {
-            part[j] += v[j];
-            mn[j] = fminf(mn[j], v[j]);
-            mx[j] = fmaxf(mx[j], v[j]);
-          }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) sum[j] += (double)part[j];
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) {
-    s_sum[phase][lane_c * VEC + j] = sum[j];
-    s_min[phase][lane_c * VEC + j] = mn[j];
-    s_max[phase][lane_c * VEC + j] = mx[j];
-  }
-  __syncthreads();
-  for (int c = threadIdx.x; c < TC; c += kThreads) {
-    const int64_t col = (int64_t)blockIdx.x * TC + c;
-    if (col >= cols) continue;
-    double s = 0.0;
-    float a = __builtin_huge_valf(), b = -__builtin_huge_valf();
-#pragma unroll
-    for (int p = 0; p < 8; ++p) { s += s_sum[p][c]; a = fminf(a, s_min[p][c]); b = fmaxf(b, s_max[p][c]); }
-    const int64_t o = (int64_t)blockIdx.y * cols + col;
-    psum[o] = s; pmin[o] = a; pmax[o] = b;
-  }
-}
-
-// ------------------------------------------------------------------------------------------
-// k_finalize: one thread per column.  mode bit 0 = SPLIT, bit 1 = MEAN_GIVEN.
-// ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void k_finalize(const double* __restrict__ psum, const float* __restrict__ pmin,
-                                                       const float* __restrict__ pmax, int nslab, int64_t rows,
-                                                       int64_t cols, int mode, float* __restrict__ mean,
-                                                       uint32_t* __restrict__ amax_slot) {
-  __shared__ float s_red[kThreads / 64];
-  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  float amax = 0.0f;
-  if (c < cols && rows > 0) {
-    double s = 0.0;
-    float a = __builtin_huge_valf(), b = -__builtin_huge_valf();
-    for (int p = 0; p < nslab; ++p) {
-      const int64_t o = (int64_t)p * cols + c;
-      s += psum[o]; a = fminf(a, pmin[o]); b = fmaxf(b, pmax[o]);
-    }
-    float mu = 0.0f;
-    if (mode & 1) {
-      if (mode & 2) mu = mean[c];
-      else { mu = (float)(s / (double)rows); mean[c] = mu; }
-    }
-    amax = fmaxf(__fsub_rn(b, mu), __fsub_rn(mu, a));
-  } else if (c < cols && (mode & 1) && !(mode & 2)) {
-    mean[c] = 0.0f;
-  }
-  // workgroup max, then one integer atomic max (amax >= 0, so its bits order like uints)
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) amax = wave_xor_max(amax, m);
-  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = amax;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float v = s_red[0];
-    for (int i = 1; i < kThreads / 64; ++i) v = fmaxf(v, s_red[i]);
-    atomicMax(amax_slot, __float_as_uint(v));
-  }
-}
+constexpr int kStatRows = 128;  // rows per k_colstats workgroup: 16 per thread, loaded in one batch
+constexpr int kTileRows = 64;   // rows per k_quant tile
 
 // ------------------------------------------------------------------------------------------
 // 16-point Hadamard butterflies (Sylvester order, stages h = 1, 2, 4, 8), then x 0.25.
@@ -188,56 +76,146 @@ __device__ inline void h16_lanes(float* v, int lane) {
 }
 
 // ------------------------------------------------------------------------------------------
-// k_quant_mean: one workgroup quantizes mu [cols] along its length.
+// k_colstats: grid (ceil(cols / TC), nslab); TC = 32 lanes * VEC columns.  Thread t covers VEC
+// columns at (t % 32) * VEC and rows slab0 + t / 32 + 8 i, i < 16, all loaded before any use.
+// Column sums: fp32 over each group of 8 rows, fp64 across groups and threads (fixed order).
+// MINMAX (NVFP4 tensor scale): column min and max as well.
 // ------------------------------------------------------------------------------------------
-template <int FMT, bool H16>
-__global__ __launch_bounds__(kThreads) void k_quant_mean(const float* __restrict__ mean, int64_t cols, int64_t k_pad,
-                                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                         float* __restrict__ tscale) {
-  constexpr int G = FMT == AVERIS_MXFP4 ? 32 : 16;
-  __shared__ float s_red[kThreads / 64];
-  const int64_t nblk = cols / G;
-  float s_dec = 0.0f;
-  if (FMT == AVERIS_NVFP4) {
-    float amax = 0.0f;
-    for (int64_t b = threadIdx.x; b < nblk; b += kThreads) {
-      float v[32];
+template <typename T, bool MINMAX>
+__global__ __launch_bounds__(kThreads) void k_colstats(const T* __restrict__ x, int64_t rows, int64_t cols,
+                                                       int64_t ldx, double* __restrict__ psum,
+                                                       float* __restrict__ pmin, float* __restrict__ pmax,
+                                                       uint32_t* __restrict__ slots) {
+  constexpr int VEC = Elem<T>::VEC;
+  constexpr int TC = 32 * VEC;
+  constexpr int PER = kStatRows / 8;
+  __shared__ double s_sum[8][TC];
+  __shared__ float s_min[MINMAX ? 8 : 1][TC];
+  __shared__ float s_max[MINMAX ? 8 : 1][TC];
+
+  // the rotated-amax slots are atomically maxed only by later kernels of the same call
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 4) slots[threadIdx.x] = 0u;
+
+  const int lane_c = threadIdx.x & 31, phase = threadIdx.x >> 5;
+  const int64_t c0 = (int64_t)blockIdx.x * TC + lane_c * VEC;
+  const int64_t r0 = (int64_t)blockIdx.y * kStatRows + phase;
+  const bool col_ok = c0 < cols;
+
+  uint4 w[PER];
 #pragma unroll
-      for (int j = 0; j < G; ++j) v[j] = mean[b * G + j];
-      if (H16) h16_inreg(v);
-#pragma unroll
-      for (int j = 0; j < G; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) amax = wave_xor_max(amax, m);
-    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = amax;
-    __syncthreads();
-    amax = s_red[0];
-    for (int i = 1; i < kThreads / 64; ++i) amax = fmaxf(amax, s_red[i]);
-    s_dec = nvfp4_tensor_scale(amax);
-    if (threadIdx.x == 0) tscale[0] = s_dec;
+  for (int i = 0; i < PER; ++i) {
+    const int64_t r = r0 + 8 * i;
+    w[i] = (col_ok && r < rows) ? *reinterpret_cast<const uint4*>(x + r * ldx + c0) : make_uint4(0, 0, 0, 0);
   }
-  for (int64_t b = threadIdx.x; b < nblk; b += kThreads) {
-    float v[32];
+  double sum[VEC];
+  float mn[VEC], mx[VEC];
 #pragma unroll
-    for (int j = 0; j < G; ++j) v[j] = mean[b * G + j];
-    if (H16) {
-      h16_inreg(v);
-      if (G == 32) h16_inreg(v + 16);
+  for (int j = 0; j < VEC; ++j) { sum[j] = 0.0; mn[j] = __builtin_huge_valf(); mx[j] = -__builtin_huge_valf(); }
+#pragma unroll
+  for (int grp = 0; grp < PER / 8; ++grp) {
+    float part[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) part[j] = 0.0f;
+#pragma unroll
+    for (int i = grp * 8; i < grp * 8 + 8; ++i) {
+      float v[VEC];
+      Elem<T>::unpack(w[i], v);  // rows past the end are zeros: harmless in the sum
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) part[j] = __fadd_rn(part[j], v[j]);
+      if (MINMAX && r0 + 8 * i < rows) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) { mn[j] = fminf(mn[j], v[j]); mx[j] = fmaxf(mx[j], v[j]); }
+      }
     }
-    float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < G; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    const BlockQ q = block_params<FMT>(amax, s_dec);
-#pragma unroll
-    for (int j = 0; j < G; ++j) v[j] = __fmul_rn(v[j], q.mul);
-#pragma unroll
-    for (int j = 0; j < G / 8; ++j) {
-      const uint32_t w = q.dead ? 0u : pack8_fp4(v + 8 * j);
-      *reinterpret_cast<uint32_t*>(codes + b * (G / 2) + 4 * j) = w;
-    }
-    scales[scale_offset(0, b, k_pad, G)] = (uint8_t)q.sbyte;
+    for (int j = 0; j < VEC; ++j) sum[j] += (double)part[j];
   }
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    s_sum[phase][lane_c * VEC + j] = sum[j];
+    if (MINMAX) { s_min[phase][lane_c * VEC + j] = mn[j]; s_max[phase][lane_c * VEC + j] = mx[j]; }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < TC; c += kThreads) {
+    const int64_t col = (int64_t)blockIdx.x * TC + c;
+    if (col >= cols) continue;
+    double sacc = 0.0;
+    float a = __builtin_huge_valf(), b = -__builtin_huge_valf();
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      sacc += s_sum[p][c];
+      if (MINMAX) { a = fminf(a, s_min[p][c]); b = fmaxf(b, s_max[p][c]); }
+    }
+    const int64_t o = (int64_t)blockIdx.y * cols + col;
+    psum[o] = sacc;
+    if (MINMAX) { pmin[o] = a; pmax[o] = b; }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// k_finalize: grid ceil(cols / 64); wave q of 4 reduces slabs [q * per, (q + 1) * per) of 64
+// columns, the four partials are then added in wave order.  Writes mu (SPLIT without
+// MEAN_GIVEN) and, per workgroup, the max |residual| (MINMAX: exact from the column min / max,
+// since fl(x - mu) is monotone in x) and the max |mu| (after the 16x16 rotation when h16),
+// both as per-workgroup partials: no atomics, nothing to clear.
+// mode bit 0 = SPLIT, bit 1 = MEAN_GIVEN.
+// ------------------------------------------------------------------------------------------
+template <bool MINMAX>
+__global__ __launch_bounds__(kThreads) void k_finalize(const double* __restrict__ psum, const float* __restrict__ pmin,
+                                                       const float* __restrict__ pmax, int nslab, int64_t rows,
+                                                       int64_t cols, int mode, int h16, float* __restrict__ mean,
+                                                       float* __restrict__ ramax_part, float* __restrict__ mamax_part) {
+  __shared__ double s_sum[4][64];
+  __shared__ float s_min[4][64], s_max[4][64];
+  const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+  const bool cin = c < cols;
+  const int per = (nslab + 3) / 4;
+  const int pb = q * per, pe = pb + per < nslab ? pb + per : nslab;
+  double s = 0.0;
+  float a = __builtin_huge_valf(), b = -__builtin_huge_valf();
+  if (cin && (mode & 1) && !(mode & 2)) {
+    for (int p0 = pb; p0 < pe; p0 += 8) {
+      double t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = p0 + u < pe ? psum[(int64_t)(p0 + u) * cols + c] : 0.0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += t[u];
+    }
+  }
+  if (cin && MINMAX) {
+    for (int p0 = pb; p0 < pe; p0 += 8) {
+      float lo[8], hi[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool ok = p0 + u < pe;
+        lo[u] = ok ? pmin[(int64_t)(p0 + u) * cols + c] : __builtin_huge_valf();
+        hi[u] = ok ? pmax[(int64_t)(p0 + u) * cols + c] : -__builtin_huge_valf();
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) { a = fminf(a, lo[u]); b = fmaxf(b, hi[u]); }
+    }
+  }
+  s_sum[q][lane] = s; s_min[q][lane] = a; s_max[q][lane] = b;
+  __syncthreads();
+  if (q != 0) return;
+  const double S = ((s_sum[0][lane] + s_sum[1][lane]) + s_sum[2][lane]) + s_sum[3][lane];
+  a = fminf(fminf(s_min[0][lane], s_min[1][lane]), fminf(s_min[2][lane], s_min[3][lane]));
+  b = fmaxf(fmaxf(s_max[0][lane], s_max[1][lane]), fmaxf(s_max[2][lane], s_max[3][lane]));
+  float mu = 0.0f;
+  if (cin && (mode & 1)) {
+    if (mode & 2) mu = mean[c];
+    else { mu = rows > 0 ? (float)(S / (double)rows) : 0.0f; mean[c] = mu; }
+  }
+  float ra = 0.0f;
+  if (MINMAX && cin && rows > 0) ra = fmaxf(__fsub_rn(b, mu), __fsub_rn(mu, a));
+  // |mu| per column, rotated within 16-column blocks when the mean is quantized rotated
+  float mv[1] = {cin ? mu : 0.0f};
+  if (h16) h16_lanes<1>(mv, lane);
+  float ma = fabsf(mv[0]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) { ra = wave_xor_max(ra, m); ma = wave_xor_max(ma, m); }
+  if (lane == 0) { ramax_part[blockIdx.x] = ra; mamax_part[blockIdx.x] = ma; }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -249,6 +227,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_mean(const float* __restrict
 // Column layout: the raw tile goes to LDS; thread t then takes column t % TC and the 32-row
 // half (t / TC + j * (256 / TC)) and quantizes down the column in registers.
 //
+// The workgroups of row tile 0 also quantize the mean's blocks in their columns, and every
+// workgroup zeroes the padding it owns (row-layout K tail, scale rows up to the 32-row group,
+// the quantized mean's tail and rows 1..31), so one launch writes every output byte.
+//
 // AMAX_ONLY: compute max |rotated residual| of each layout and atomically max it into
 // amax_slots[1] (row) and amax_slots[2] (column); nothing is stored.
 // ------------------------------------------------------------------------------------------
@@ -256,8 +238,15 @@ struct QuantArgs {
   const void* x;
   int64_t rows, cols, ldx;
   const float* mean;           // nullptr: no subtraction
-  const uint32_t* amax_slots;  // NVFP4: [0] residual amax, [1] rotated row amax, [2] rotated col amax
+  const uint32_t* amax_slots;  // NVFP4 with rotation: [1] rotated row amax, [2] rotated col amax
   uint32_t* amax_out;          // AMAX_ONLY target (same buffer as amax_slots)
+  const float* ramax_part;     // NVFP4: per-workgroup max |residual| from k_finalize
+  const float* mamax_part;     // NVFP4: per-workgroup max |(rotated) mean|
+  int n_part;
+  uint8_t* mean_codes;         // quantized mean (nullptr: none)
+  uint8_t* mean_scales;
+  float* mean_ts;
+  int64_t mean_kpad;
   uint8_t* row_codes;          // nullptr: row layout not written
   uint8_t* row_scales;
   float* row_ts;
@@ -268,6 +257,75 @@ struct QuantArgs {
   int64_t row_kpad;            // padded column count of the row layout (its row stride in elements)
   int tiles_r, tiles_c;
 };
+
+
+// Mean quantization (row tile 0) and padding zeroes for k_quant's tile (tr, tc).
+template <int FMT, bool H16, int TC>
+__device__ __forceinline__ void quant_extras(const QuantArgs& a, int tr, int tc, int64_t r0, int64_t c0) {
+  constexpr int G = FMT == AVERIS_MXFP4 ? 32 : 16;
+  const int t = threadIdx.x;
+  const bool last_tc = tc == a.tiles_c - 1;
+  const int64_t cend = c0 + TC < a.cols ? c0 + TC : a.cols;
+  // ---- row layout: K tail of codes and scales, and scale rows up to the 32-row group ----
+  if (a.row_codes) {
+    const int64_t kp = a.row_kpad, rp = round_up(a.rows, 32);
+    const int64_t rend_d = r0 + kTileRows < a.rows ? r0 + kTileRows : a.rows;
+    const int64_t rend_p = r0 + kTileRows < rp ? r0 + kTileRows : rp;
+    if (last_tc && kp > a.cols) {
+      const int nq = (int)((kp - a.cols) / 32);  // 16-byte chunks of code tail per row
+      for (int64_t i = t; i < (rend_d - r0) * nq; i += kThreads) {
+        const int64_t r = r0 + i / nq;
+        *reinterpret_cast<uint4*>(a.row_codes + r * (kp / 2) + a.cols / 2 + (i % nq) * 16) = make_uint4(0, 0, 0, 0);
+      }
+      const int nt = (int)((kp - a.cols) / G);
+      for (int64_t i = t; i < (rend_p - r0) * nt; i += kThreads)
+        a.row_scales[scale_offset(r0 + i / nt, a.cols / G + i % nt, kp, G)] = 0;
+    }
+    const int64_t pr0 = r0 > a.rows ? r0 : a.rows;
+    const int nb = (int)((cend - c0) / G);
+    for (int64_t i = t; i < (rend_p - pr0) * nb; i += kThreads)
+      a.row_scales[scale_offset(pr0 + i / nb, c0 / G + i % nb, kp, G)] = 0;
+  }
+  if (!a.mean_codes || tr != 0) return;
+  // ---- quantized mean: this tile's blocks of row 0, zero rows 1..31 and the K tail ----
+  const int64_t kp = a.mean_kpad;
+  float s_dec = 0.0f;
+  if (FMT == AVERIS_NVFP4) {
+    float m = 0.0f;
+    for (int i = t & 63; i < a.n_part; i += 64) m = fmaxf(m, a.mamax_part[i]);
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) m = wave_xor_max(m, s);
+    s_dec = nvfp4_tensor_scale(m);
+    if (tc == 0 && t == 0) a.mean_ts[0] = s_dec;
+  }
+  for (int64_t c = c0 + (int64_t)t * G; c < cend; c += (int64_t)kThreads * G) {
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < G; ++j) v[j] = a.mean[c + j];
+    if (H16) {
+      h16_inreg(v);
+      if (G == 32) h16_inreg(v + 16);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < G; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    const BlockQ q = block_params<FMT>(amax, s_dec);
+#pragma unroll
+    for (int j = 0; j < G; ++j) v[j] = __fmul_rn(v[j], q.mul);
+#pragma unroll
+    for (int j = 0; j < G / 8; ++j)
+      *reinterpret_cast<uint32_t*>(a.mean_codes + c / 2 + 4 * j) = q.dead ? 0u : pack8_fp4(v + 8 * j);
+    a.mean_scales[scale_offset(0, c / G, kp, G)] = (uint8_t)q.sbyte;
+  }
+  const int nb = (int)((cend - c0) / G);
+  for (int i = t; i < 31 * nb; i += kThreads) a.mean_scales[scale_offset(1 + i / nb, c0 / G + i % nb, kp, G)] = 0;
+  if (last_tc && kp > a.cols) {
+    const int nq = (int)((kp - a.cols) / 32);
+    if (t < nq) *reinterpret_cast<uint4*>(a.mean_codes + a.cols / 2 + t * 16) = make_uint4(0, 0, 0, 0);
+    const int nt = (int)((kp - a.cols) / G);
+    for (int i = t; i < 32 * nt; i += kThreads) a.mean_scales[scale_offset(i / nt, a.cols / G + i % nt, kp, G)] = 0;
+  }
+}
 
 template <typename T, int FMT, bool H16, bool AMAX_ONLY>
 __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs a) {
@@ -288,8 +346,17 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs a) {
   // tensor decode scales (NVFP4): residual amax, or the rotated amax per layout
   float sd_row = 0.0f, sd_col = 0.0f;
   if (FMT == AVERIS_NVFP4 && !AMAX_ONLY) {
-    const float ar = __uint_as_float(a.amax_slots[H16 ? 1 : 0]);
-    const float ac = __uint_as_float(a.amax_slots[H16 ? 2 : 0]);
+    float ar, ac;
+    if (H16) {
+      ar = __uint_as_float(a.amax_slots[1]);
+      ac = __uint_as_float(a.amax_slots[2]);
+    } else {
+      float m = 0.0f;
+      for (int i = lane; i < a.n_part; i += 64) m = fmaxf(m, a.ramax_part[i]);
+#pragma unroll
+      for (int s = 32; s >= 1; s >>= 1) m = wave_xor_max(m, s);
+      ar = ac = m;
+    }
     sd_row = nvfp4_tensor_scale(ar);
     sd_col = nvfp4_tensor_scale(ac);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -297,6 +364,7 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs a) {
       if (a.col_ts) a.col_ts[0] = sd_col;
     }
   }
+  if (!AMAX_ONLY) quant_extras<FMT, H16, TC>(a, tr, tc, r0, c0);
 
   // ---- load the tile (rows >= a.rows read as 0) ----
   const int64_t cc = c0 + lane_c * VEC;
@@ -378,8 +446,8 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs a) {
         const BlockQ q = block_params<FMT>(m, sd_col);
 #pragma unroll
         for (int j = 0; j < G; ++j) v[b * G + j] = __fmul_rn(v[b * G + j], q.mul);
-        if (col < a.cols) {
-          const int64_t k0 = r0 + half * 32 + b * G;  // first token of this block
+        const int64_t k0 = r0 + half * 32 + b * G;  // first token of this block
+        if (col < a.cols && k0 < a.col_kpad) {
           uint8_t* dst = a.col_codes + col * (a.col_kpad / 2) + k0 / 2;
           if (G == 32) {
             uint4 o;
@@ -417,26 +485,6 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs a) {
   }
 }
 
-// Zero bytes [start, start + len) of each of `rows` rows of stride ld (K padding of a layout).
-__global__ void k_zero_tail(uint8_t* __restrict__ base, int64_t rows, int64_t ld, int64_t start, int64_t len) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t r = i / len, b = i % len;
-  if (r < rows) base[r * ld + start + b] = 0;
-}
-
-// Zero the tiled scale bytes outside the data: blocks [k/g, k_pad/g) of rows [0, outer) and
-// every block of the group-padding rows [outer, round_up(outer, 32)).
-__global__ void k_zero_scale_pad(uint8_t* __restrict__ scales, int64_t outer, int64_t k, int64_t k_pad, int g) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t nb = k_pad / g, kb = k / g, tail = nb - kb;
-  const int64_t n1 = outer * tail, n2 = (round_up(outer, 32) - outer) * nb;
-  int64_t r, b;
-  if (i < n1) { r = i / tail; b = kb + i % tail; }
-  else if (i < n1 + n2) { r = outer + (i - n1) / nb; b = (i - n1) % nb; }
-  else return;
-  scales[scale_offset(r, b, k_pad, g)] = 0;
-}
-
 __global__ void k_fill_f32(float* p, int n, float v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -446,34 +494,56 @@ __global__ void k_fill_f32(float* p, int n, float v) {
 // Host side
 // ------------------------------------------------------------------------------------------
 static int64_t slab_count(int64_t rows) {
-  const int64_t n = ceil_div(rows, kSlab);
+  const int64_t n = ceil_div(rows, kStatRows);
   return n > 0 ? n : 1;  // one (empty) slab when rows == 0
 }
 
-size_t split_quant_ws_bytes(int64_t rows, int64_t cols) {
-  const int64_t nslab = slab_count(rows);
-  return 256 + (size_t)nslab * cols * (8 + 4 + 4) + 256;
+// workspace: [0, 256) amax slots | [256, ..) finalize partials (2 x n_part fp32) | column
+// statistics: psum [nslab][cols] fp64, pmin and pmax [nslab][cols] fp32
+struct SqLayout {
+  uint32_t* slots; float* ramax; float* mamax; double* psum; float* pmin; float* pmax; int n_part; int64_t nslab;
+};
+static SqLayout sq_layout(void* ws, int64_t rows, int64_t cols) {
+  SqLayout L;
+  uint8_t* b = reinterpret_cast<uint8_t*>(ws);
+  L.n_part = (int)ceil_div(cols, 64);
+  L.nslab = slab_count(rows);
+  const size_t pb = (size_t)round_up(L.n_part * 4, 256);
+  L.slots = reinterpret_cast<uint32_t*>(b);
+  L.ramax = reinterpret_cast<float*>(b + 256);
+  L.mamax = reinterpret_cast<float*>(b + 256 + pb);
+  L.psum = reinterpret_cast<double*>(b + 256 + 2 * pb);
+  L.pmin = reinterpret_cast<float*>(b + 256 + 2 * pb + (size_t)L.nslab * cols * 8);
+  L.pmax = L.pmin + (size_t)L.nslab * cols;
+  return L;
 }
 
-
+size_t split_quant_ws_bytes(int64_t rows, int64_t cols) {
+  const int64_t n_part = ceil_div(cols, 64);
+  return 256 + 2 * (size_t)round_up(n_part * 4, 256) + (size_t)slab_count(rows) * cols * (8 + 4 + 4) + 256;
+}
 
 template <typename T, int FMT, bool H16>
-static hipError_t launch_quant_t(const SplitQuantPlan& p, uint32_t* slots) {
+static hipError_t launch_quant_t(const SplitQuantPlan& p, const SqLayout& L) {
   constexpr int TC = 32 * Elem<T>::VEC;
   QuantArgs a{};
   a.x = p.x; a.rows = p.rows; a.cols = p.cols; a.ldx = p.ldx;
   a.mean = p.split ? p.mean : nullptr;
-  a.amax_slots = slots; a.amax_out = slots;
+  a.amax_slots = L.slots; a.amax_out = L.slots;
+  a.ramax_part = L.ramax; a.mamax_part = L.mamax; a.n_part = L.n_part;
   const int64_t col_kpad = round_up(p.rows, kKPad);
   a.col_kpad = col_kpad;
   a.row_kpad = round_up(p.cols, kKPad);
   a.tiles_c = (int)ceil_div(p.cols, TC);
-  // column layout covers the padding rows too (they are zero residuals)
-  a.tiles_r = (int)ceil_div(p.q_col ? col_kpad : p.rows, kTileRows);
+  // column layout covers the padding rows too (they are zero residuals); at least one row tile
+  // so that the tensor scales, the quantized mean and the padding are written for rows == 0
+  const int64_t tr = ceil_div(p.q_col ? col_kpad : p.rows, kTileRows);
+  a.tiles_r = (int)(tr > 0 ? tr : 1);
   const int ntiles = a.tiles_r * a.tiles_c;
-  if (ntiles == 0) {  // empty operands: still define their tensor scales (0)
+  if (ntiles == 0) {  // no columns: still define the tensor scales (0)
     if (FMT == AVERIS_NVFP4) {
-      float* ts[2] = {p.q_row ? p.q_row->tensor_scale : nullptr, p.q_col ? p.q_col->tensor_scale : nullptr};
+      float* ts[3] = {p.q_row ? p.q_row->tensor_scale : nullptr, p.q_col ? p.q_col->tensor_scale : nullptr,
+                      p.q_mean ? p.q_mean->tensor_scale : nullptr};
       for (float* t : ts)
         if (t) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(64), 0, p.stream, t, 1, 0.0f);
     }
@@ -485,68 +555,45 @@ static hipError_t launch_quant_t(const SplitQuantPlan& p, uint32_t* slots) {
   }
   if (p.q_row) { a.row_codes = p.q_row->codes; a.row_scales = p.q_row->scales; a.row_ts = p.q_row->tensor_scale; }
   if (p.q_col) { a.col_codes = p.q_col->codes; a.col_scales = p.q_col->scales; a.col_ts = p.q_col->tensor_scale; }
+  if (p.split && p.q_mean) {
+    a.mean_codes = p.q_mean->codes; a.mean_scales = p.q_mean->scales; a.mean_ts = p.q_mean->tensor_scale;
+    a.mean_kpad = p.q_mean->k_pad;
+  }
   hipLaunchKernelGGL((k_quant<T, FMT, H16, false>), dim3(ntiles), dim3(kThreads), 0, p.stream, a);
   return hipGetLastError();
 }
 
 template <int FMT, bool H16>
-static hipError_t launch_quant_f(const SplitQuantPlan& p, uint32_t* slots) {
-  return p.xdt == AVERIS_BF16 ? launch_quant_t<uint16_t, FMT, H16>(p, slots) : launch_quant_t<float, FMT, H16>(p, slots);
+static hipError_t launch_quant_f(const SplitQuantPlan& p, const SqLayout& L) {
+  return p.xdt == AVERIS_BF16 ? launch_quant_t<uint16_t, FMT, H16>(p, L) : launch_quant_t<float, FMT, H16>(p, L);
 }
 
-// Zero the padding of an operand the quantizer writes: codes [k, k_pad) of every row, and the
-// scale bytes outside the data (K tail and the rows that pad the last 32-row group).
-static void zero_padding(const averis_qtensor* q, int fmt, hipStream_t s) {
-  const int G = fmt == AVERIS_MXFP4 ? 32 : 16;
-  if (!q || q->outer == 0 || q->k_pad == 0) return;
-  if (q->k_pad > q->k) {
-    const int64_t cl = (q->k_pad - q->k) / 2;
-    hipLaunchKernelGGL(k_zero_tail, dim3((unsigned)ceil_div(q->outer * cl, 256)), dim3(256), 0, s, q->codes, q->outer,
-                       q->k_pad / 2, q->k / 2, cl);
-  }
-  const int64_t n = q->outer * (q->k_pad / G - q->k / G) + (round_up(q->outer, 32) - q->outer) * (q->k_pad / G);
-  if (n > 0)
-    hipLaunchKernelGGL(k_zero_scale_pad, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, q->scales, q->outer, q->k,
-                       q->k_pad, G);
+template <typename T, bool MINMAX>
+static void launch_stats_t(const SplitQuantPlan& p, const SqLayout& L) {
+  constexpr int TC = 32 * Elem<T>::VEC;
+  const dim3 grid((unsigned)ceil_div(p.cols, TC), (unsigned)L.nslab);
+  hipLaunchKernelGGL((k_colstats<T, MINMAX>), grid, dim3(kThreads), 0, p.stream, reinterpret_cast<const T*>(p.x), p.rows,
+                     p.cols, p.ldx, L.psum, L.pmin, L.pmax, L.slots);
+  const int mode = (p.split ? 1 : 0) | (p.mean_given ? 2 : 0);
+  hipLaunchKernelGGL((k_finalize<MINMAX>), dim3((unsigned)L.n_part), dim3(kThreads), 0, p.stream, L.psum, L.pmin,
+                     L.pmax, (int)L.nslab, p.rows, p.cols, mode, (p.split && p.h16) ? 1 : 0, p.mean, L.ramax, L.mamax);
 }
 
 hipError_t split_quant_launch(const SplitQuantPlan& p) {
-  uint8_t* ws = reinterpret_cast<uint8_t*>(p.ws);
-  uint32_t* slots = reinterpret_cast<uint32_t*>(ws);
-  const int64_t nslab = slab_count(p.rows);
-  double* psum = reinterpret_cast<double*>(ws + 256);
-  float* pmin = reinterpret_cast<float*>(ws + 256 + (size_t)nslab * p.cols * 8);
-  float* pmax = pmin + (size_t)nslab * p.cols;
-
-  const bool need_stats = p.fmt == AVERIS_NVFP4 || (p.split && !p.mean_given);
-  if (need_stats) {
-    const int tc = p.xdt == AVERIS_BF16 ? 256 : 128;
-    const dim3 grid((unsigned)ceil_div(p.cols, tc), (unsigned)nslab);
-    if (p.xdt == AVERIS_BF16)
-      hipLaunchKernelGGL(k_stats<uint16_t>, grid, dim3(kThreads), 0, p.stream, (const uint16_t*)p.x, p.rows, p.cols,
-                         p.ldx, psum, pmin, pmax, slots);
-    else
-      hipLaunchKernelGGL(k_stats<float>, grid, dim3(kThreads), 0, p.stream, (const float*)p.x, p.rows, p.cols, p.ldx,
-                         psum, pmin, pmax, slots);
-    const int mode = (p.split ? 1 : 0) | (p.mean_given ? 2 : 0);
-    hipLaunchKernelGGL(k_finalize, dim3((unsigned)ceil_div(p.cols, kThreads)), dim3(kThreads), 0, p.stream, psum, pmin,
-                       pmax, (int)ceil_div(p.rows, kSlab), p.rows, p.cols, mode, p.mean, slots);
-  }
-  if (p.split) {
-    if (p.fmt == AVERIS_NVFP4) {
-      if (p.h16) hipLaunchKernelGGL((k_quant_mean<AVERIS_NVFP4, true>), dim3(1), dim3(kThreads), 0, p.stream, p.mean, p.cols, p.q_mean->k_pad, p.q_mean->codes, p.q_mean->scales, p.q_mean->tensor_scale);
-      else hipLaunchKernelGGL((k_quant_mean<AVERIS_NVFP4, false>), dim3(1), dim3(kThreads), 0, p.stream, p.mean, p.cols, p.q_mean->k_pad, p.q_mean->codes, p.q_mean->scales, p.q_mean->tensor_scale);
+  const SqLayout L = sq_layout(p.ws, p.rows, p.cols);
+  const bool nv = p.fmt == AVERIS_NVFP4;
+  // column statistics: the mean (SPLIT without MEAN_GIVEN) and, for NVFP4, the residual amax
+  if (p.cols > 0 && (nv || (p.split && !p.mean_given))) {
+    if (p.xdt == AVERIS_BF16) {
+      if (nv) launch_stats_t<uint16_t, true>(p, L); else launch_stats_t<uint16_t, false>(p, L);
     } else {
-      if (p.h16) hipLaunchKernelGGL((k_quant_mean<AVERIS_MXFP4, true>), dim3(1), dim3(kThreads), 0, p.stream, p.mean, p.cols, p.q_mean->k_pad, p.q_mean->codes, p.q_mean->scales, (float*)nullptr);
-      else hipLaunchKernelGGL((k_quant_mean<AVERIS_MXFP4, false>), dim3(1), dim3(kThreads), 0, p.stream, p.mean, p.cols, p.q_mean->k_pad, p.q_mean->codes, p.q_mean->scales, (float*)nullptr);
+      if (nv) launch_stats_t<float, true>(p, L); else launch_stats_t<float, false>(p, L);
     }
   }
-  zero_padding(p.q_row, p.fmt, p.stream);  // the column layout's padding rows are written by k_quant
-  zero_padding(p.q_mean, p.fmt, p.stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.fmt == AVERIS_NVFP4) return p.h16 ? launch_quant_f<AVERIS_NVFP4, true>(p, slots) : launch_quant_f<AVERIS_NVFP4, false>(p, slots);
-  return p.h16 ? launch_quant_f<AVERIS_MXFP4, true>(p, slots) : launch_quant_f<AVERIS_MXFP4, false>(p, slots);
+  if (nv) return p.h16 ? launch_quant_f<AVERIS_NVFP4, true>(p, L) : launch_quant_f<AVERIS_NVFP4, false>(p, L);
+  return p.h16 ? launch_quant_f<AVERIS_MXFP4, true>(p, L) : launch_quant_f<AVERIS_MXFP4, false>(p, L);
 }
 
 }  // namespace av
