@@ -30,6 +30,9 @@ EXPORTS = [
     "averis_split_quant_workspace_size", "averis_split_quant",
     "averis_linear_workspace_size", "averis_linear_fwd", "averis_linear_bwd_dx",
     "averis_linear_bwd_dw_workspace_size", "averis_linear_bwd_dw",
+    "averis_split_quant_grouped_workspace_size", "averis_split_quant_grouped",
+    "averis_linear_grouped_workspace_size", "averis_linear_fwd_grouped", "averis_linear_bwd_dx_grouped",
+    "averis_linear_bwd_dw_grouped_workspace_size", "averis_linear_bwd_dw_grouped",
 ]
 
 
@@ -68,6 +71,13 @@ def lib():
             "averis_linear_bwd_dx": (I32, [Q, Q, Q, P, I32, I64, P, SZ, P]),
             "averis_linear_bwd_dw_workspace_size": (SZ, [I64, I64, I64, I32]),
             "averis_linear_bwd_dw": (I32, [Q, Q, Q, Q, I64, P, I64, U32, P, SZ, P]),
+            "averis_split_quant_grouped_workspace_size": (SZ, [I64, I64, I32, I32, U32]),
+            "averis_split_quant_grouped": (I32, [P, I32, I64, I64, P, P, I32, I32, U32, P, Q, Q, Q, P, SZ, P]),
+            "averis_linear_grouped_workspace_size": (SZ, [I64, I32, I32]),
+            "averis_linear_fwd_grouped": (I32, [Q, Q, Q, P, P, I32, P, I32, I64, P, SZ, P]),
+            "averis_linear_bwd_dx_grouped": (I32, [Q, Q, Q, P, P, I32, P, I32, I64, P, SZ, P]),
+            "averis_linear_bwd_dw_grouped_workspace_size": (SZ, [I64, I64, I32, I32]),
+            "averis_linear_bwd_dw_grouped": (I32, [Q, Q, Q, Q, P, P, I32, P, I64, U32, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -95,10 +105,11 @@ class QTensor:
     k: int
     fmt: int
     rotated: bool
+    kpad: int | None = None  # storage length along k when it is not round_up(k, 256) (grouped)
 
     @property
     def k_pad(self):
-        return (self.k + KPAD - 1) // KPAD * KPAD
+        return self.kpad if self.kpad is not None else (self.k + KPAD - 1) // KPAD * KPAD
 
     def c(self):
         return CQTensor(self.codes.data_ptr(), self.scales.data_ptr(),
@@ -106,14 +117,14 @@ class QTensor:
                         self.outer, self.k, self.k_pad, self.fmt, HADAMARD16 if self.rotated else 0)
 
 
-def empty_qtensor(outer, k, fmt, rotated=False, device="cuda", groups=1):
-    kp = (k + KPAD - 1) // KPAD * KPAD
+def empty_qtensor(outer, k, fmt, rotated=False, device="cuda", groups=1, kpad=None):
+    kp = kpad if kpad is not None else (k + KPAD - 1) // KPAD * KPAD
     g = BLOCK[fmt]
     rp = (outer + 31) // 32 * 32
     return QTensor(torch.empty((outer, kp // 2), dtype=torch.uint8, device=device),
                    torch.empty((rp, kp // g), dtype=torch.uint8, device=device),
                    torch.empty(groups, dtype=torch.float32, device=device) if fmt == NVFP4 else None,
-                   outer, k, fmt, rotated)
+                   outer, k, fmt, rotated, kpad)
 
 
 def _ptr(q):
@@ -225,4 +236,121 @@ def linear_bwd_dw(xr_t: QTensor, dr_t: QTensor, mu_x: QTensor | None, mu_d: QTen
     _check(L.averis_linear_bwd_dw(_ptr(xr_t), _ptr(dr_t), _ptr(mu_x), _ptr(mu_d), l,
                                   dw.data_ptr() if dw.numel() else None, dw.stride(0),
                                   ACCUMULATE if accumulate else 0, ws.data_ptr(), ws.numel(), _stream(stream)))
+    return dw
+
+
+# ------------------------------------------------------------------------------------------
+# Grouped (MoE) variants: group e = rows [offsets[e], offsets[e+1]) of a token-major input.
+# ------------------------------------------------------------------------------------------
+def _ru(a, b):
+    return (a + b - 1) // b * b
+
+
+class Groups:
+    """Group offsets [E + 1] kept on the device (read by the kernels) and on the host (launch
+    sizing); plus the sizes of the grouped layouts."""
+
+    def __init__(self, offsets, device="cuda"):
+        offs = [int(v) for v in offsets]
+        self.offsets = offs
+        self.E = len(offs) - 1
+        self.lens = [offs[e + 1] - offs[e] for e in range(self.E)]
+        self.rows = offs[-1]
+        self.row_starts = [0]
+        self.tok_starts = [0]
+        for n in self.lens:
+            self.row_starts.append(self.row_starts[-1] + _ru(n, 32))
+            self.tok_starts.append(self.tok_starts[-1] + _ru(n, KPAD))
+        self.rows32 = self.row_starts[-1]
+        self.tok256 = self.tok_starts[-1]
+        self.h = (ctypes.c_int64 * (self.E + 1))(*offs)
+        self.d = torch.tensor(offs, dtype=torch.int64, device=device)
+
+
+def split_quant_grouped_outputs(grp: Groups, cols, fmt, split=True, hadamard=False, row=True, col=True,
+                                device="cuda"):
+    E = grp.E
+    return dict(mean=torch.empty((E, cols), dtype=torch.float32, device=device) if split else None,
+                row=empty_qtensor(grp.rows32, cols, fmt, hadamard, device, groups=E) if row else None,
+                col=empty_qtensor(cols, grp.rows, fmt, hadamard, device, groups=E, kpad=grp.tok256) if col else None,
+                mean_q=empty_qtensor(E, cols, fmt, hadamard, device, groups=E) if split else None)
+
+
+def split_quant_grouped(x: torch.Tensor, grp: Groups, fmt: int, split: bool = True, hadamard: bool = False,
+                        means: torch.Tensor | None = None, row: bool = True, col: bool = True, stream=None,
+                        out=None, ws=None):
+    """Per group, exactly split_quant on its rows; outputs in the grouped layouts of
+    include/averis.h (row layout [sum round_up(l_e, 32), cols], column layout [cols, L] with
+    per-group token padding, means [E, cols], quantized means [E, cols], one tensor scale per
+    group)."""
+    assert x.dim() == 2 and x.is_cuda and x.shape[0] == grp.rows
+    rows, cols = x.shape
+    assert rows == 0 or x.stride(1) == 1, "x must be row-major"
+    ldx = x.stride(0) if rows > 0 else cols
+    dev = x.device
+    flags = (SPLIT if split else 0) | (HADAMARD16 if hadamard else 0) | \
+        (MEAN_GIVEN if (split and means is not None) else 0)
+    if out is None:
+        out = split_quant_grouped_outputs(grp, cols, fmt, split, hadamard, row, col, dev)
+    if split and means is not None:
+        out = dict(out, mean=means.contiguous())
+    mu = out["mean"]
+    L = lib()
+    if ws is None:
+        ws = _workspace(L.averis_split_quant_grouped_workspace_size(rows, cols, grp.E, fmt, flags), dev)
+    _check(L.averis_split_quant_grouped(x.data_ptr() if rows else None, _dtype_code(x), cols, ldx,
+                                        grp.d.data_ptr(), grp.h, grp.E, fmt, flags,
+                                        mu.data_ptr() if mu is not None else None, _ptr(out["row"]),
+                                        _ptr(out["col"]), _ptr(out["mean_q"]), ws.data_ptr(), ws.numel(),
+                                        _stream(stream)))
+    return out
+
+
+def stacked_weight_view(col_q: QTensor, E: int, m: int) -> QTensor:
+    """The column layout of grouped weights (E groups of m rows, outer = n) seen as E stacked
+    [n, m] operands (outer = E * n): the same bytes, the forward GEMM's B operand."""
+    n = col_q.outer
+    kp = _ru(m, KPAD)
+    return QTensor(col_q.codes.view(-1).view(E * n, kp // 2), col_q.scales.view(-1).view(E * n, kp // BLOCK[col_q.fmt]),
+                   col_q.tensor_scale, E * n, m, col_q.fmt, col_q.rotated)
+
+
+def _linear_grouped(fn, a: QTensor, mu: QTensor | None, w: QTensor, grp: Groups, out_dtype, stream, out, ws):
+    dev = a.codes.device
+    N = w.outer // grp.E
+    if out is None:
+        out = torch.empty((grp.rows, N), dtype=out_dtype, device=dev)
+    if ws is None:
+        ws = _workspace(lib().averis_linear_grouped_workspace_size(N, grp.E, a.fmt), dev)
+    _check(fn(_ptr(a), _ptr(mu), _ptr(w), grp.d.data_ptr(), grp.h, grp.E, out.data_ptr() if out.numel() else None,
+              _dtype_code(out), out.stride(0), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return out
+
+
+def linear_fwd_grouped(xr: QTensor, mu_x: QTensor | None, w: QTensor, grp: Groups, out_dtype=torch.float32,
+                       stream=None, out=None, ws=None):
+    """Y [L, n]: per group the forward GEMM with its own mean term; w = E stacked [n, m] operands."""
+    return _linear_grouped(lib().averis_linear_fwd_grouped, xr, mu_x, w, grp, out_dtype, stream, out, ws)
+
+
+def linear_bwd_dx_grouped(dr: QTensor, mu_d: QTensor | None, w: QTensor, grp: Groups, out_dtype=torch.float32,
+                          stream=None, out=None, ws=None):
+    """dX [L, m]: per group the input-gradient GEMM; w = E stacked [m, n] operands."""
+    return _linear_grouped(lib().averis_linear_bwd_dx_grouped, dr, mu_d, w, grp, out_dtype, stream, out, ws)
+
+
+def linear_bwd_dw_grouped(xr_t: QTensor, dr_t: QTensor, mu_x: QTensor | None, mu_d: QTensor | None, grp: Groups,
+                          dw: torch.Tensor | None = None, accumulate: bool = False, stream=None, ws=None):
+    """dW [E, m, n] (fp32): per group Q(X_R)^T Q(D_R) + l_e Q(mu_X)^T Q(mu_D)."""
+    dev = xr_t.codes.device
+    m, n = xr_t.outer, dr_t.outer
+    if dw is None:
+        dw = torch.empty((grp.E, m, n), dtype=torch.float32, device=dev)
+    L = lib()
+    if ws is None:
+        ws = _workspace(L.averis_linear_bwd_dw_grouped_workspace_size(m, n, grp.E, xr_t.fmt), dev)
+    _check(L.averis_linear_bwd_dw_grouped(_ptr(xr_t), _ptr(dr_t), _ptr(mu_x), _ptr(mu_d), grp.d.data_ptr(), grp.h,
+                                          grp.E, dw.data_ptr() if dw.numel() else None, dw.stride(1),
+                                          ACCUMULATE if accumulate else 0, ws.data_ptr(), ws.numel(),
+                                          _stream(stream)))
     return dw

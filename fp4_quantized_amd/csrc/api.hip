@@ -18,16 +18,34 @@ int64_t elem_size(int32_t d) { return d == AVERIS_BF16 ? 2 : 4; }
 int64_t block_of(int32_t f) { return f == AVERIS_MXFP4 ? 32 : 16; }
 
 // A qtensor the call writes or reads must have exactly the expected shape and format.
-int32_t check_q(const averis_qtensor* q, int64_t outer, int64_t k, int32_t fmt, uint32_t rot) {
+int32_t check_qp(const averis_qtensor* q, int64_t outer, int64_t k, int64_t k_pad, int32_t fmt, uint32_t rot) {
   const bool empty = outer == 0 || k == 0;
   if (!empty && (!q->codes || !q->scales)) return AVERIS_E_NULL;
   if (fmt == AVERIS_NVFP4 && !q->tensor_scale) return AVERIS_E_NULL;
   if (q->fmt != fmt) return AVERIS_E_FORMAT;
-  if (q->outer != outer || q->k != k || q->k_pad != round_up(k, kKPad)) return AVERIS_E_SHAPE;
+  if (q->outer != outer || q->k != k || q->k_pad != k_pad) return AVERIS_E_SHAPE;
   if ((q->flags & ~AVERIS_HADAMARD16) != 0) return AVERIS_E_FLAGS;
   if ((q->flags & AVERIS_HADAMARD16) != rot) return AVERIS_E_FLAGS;
   if (!aligned16(q->codes) || !aligned16(q->scales)) return AVERIS_E_ALIGN;
   return AVERIS_OK;
+}
+int32_t check_q(const averis_qtensor* q, int64_t outer, int64_t k, int32_t fmt, uint32_t rot) {
+  return check_qp(q, outer, k, round_up(k, kKPad), fmt, rot);
+}
+
+// Group offsets: E >= 1, both copies given, host copy starts at 0 and never decreases.
+// Returns the total row count, or -1.
+int64_t check_offsets(const int64_t* d_offsets, const int64_t* h_offsets, int32_t E) {
+  if (E < 1 || E > (1 << 20) || !d_offsets || !h_offsets) return -1;
+  if (h_offsets[0] != 0) return -1;
+  for (int32_t e = 0; e < E; ++e)
+    if (h_offsets[e + 1] < h_offsets[e]) return -1;
+  return h_offsets[E];
+}
+int64_t sum_round(const int64_t* h, int32_t E, int64_t m) {
+  int64_t s = 0;
+  for (int32_t e = 0; e < E; ++e) s += round_up(h[e + 1] - h[e], m);
+  return s;
 }
 
 // Operand consumed by a GEMM: shape taken from the struct, only consistency checked.
@@ -180,6 +198,149 @@ int32_t averis_linear_bwd_dw(const averis_qtensor* xr_t, const averis_qtensor* d
   p.mu_u = mu_x; p.mu_v = mu_d; p.r1 = (float)l;
   p.accumulate = (flags & AVERIS_ACCUMULATE) ? 1 : 0;
   p.splits = splits; p.ws = ws; p.stream = reinterpret_cast<hipStream_t>(stream);
+  return gemm_launch(p) == hipSuccess ? AVERIS_OK : AVERIS_E_HIP;
+}
+
+// ------------------------------------------------------------------------------------------
+// Grouped (MoE) variants
+// ------------------------------------------------------------------------------------------
+size_t averis_split_quant_grouped_workspace_size(int64_t rows, int64_t cols, int32_t E, int32_t fmt, uint32_t flags) {
+  (void)fmt; (void)flags;
+  if (rows < 0 || cols <= 0 || E < 1) return 0;
+  return split_quant_grouped_ws_bytes(rows, cols, E);
+}
+
+int32_t averis_split_quant_grouped(const void* x, int32_t xdt, int64_t cols, int64_t ldx, const int64_t* d_offsets,
+                                   const int64_t* h_offsets, int32_t E, int32_t fmt, uint32_t flags, float* means,
+                                   const averis_qtensor* q_row, const averis_qtensor* q_col,
+                                   const averis_qtensor* q_mean, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(xdt)) return AVERIS_E_DTYPE;
+  if (!fmt_ok(fmt)) return AVERIS_E_FORMAT;
+  if (flags & ~(AVERIS_SPLIT | AVERIS_HADAMARD16 | AVERIS_MEAN_GIVEN)) return AVERIS_E_FLAGS;
+  const bool split = flags & AVERIS_SPLIT, h16 = flags & AVERIS_HADAMARD16, given = flags & AVERIS_MEAN_GIVEN;
+  if (given && !split) return AVERIS_E_FLAGS;
+  const int64_t rows = check_offsets(d_offsets, h_offsets, E);
+  if (rows < 0) return E < 1 || !d_offsets || !h_offsets ? (E < 1 ? AVERIS_E_SHAPE : AVERIS_E_NULL) : AVERIS_E_SHAPE;
+  if (cols <= 0 || cols % kColMult != 0 || ldx < cols) return AVERIS_E_SHAPE;
+  if (rows > ((int64_t)1 << 31) || cols > ((int64_t)1 << 24)) return AVERIS_E_SHAPE;
+  if (!q_row && !q_col) return AVERIS_E_NULL;
+  if (rows > 0 && !x) return AVERIS_E_NULL;
+  if (x && (!aligned16(x) || (ldx * elem_size(xdt)) % 16 != 0)) return AVERIS_E_ALIGN;
+  if (!aligned16(d_offsets)) return AVERIS_E_ALIGN;
+  const uint32_t rot = h16 ? AVERIS_HADAMARD16 : 0u;
+  int32_t st;
+  if (q_row && (st = check_q(q_row, sum_round(h_offsets, E, 32), cols, fmt, rot)) != AVERIS_OK) return st;
+  if (q_col && (st = check_qp(q_col, cols, rows, sum_round(h_offsets, E, kKPad), fmt, rot)) != AVERIS_OK) return st;
+  if (split) {
+    if (!means || !q_mean) return AVERIS_E_NULL;
+    if (!aligned16(means)) return AVERIS_E_ALIGN;
+    if ((st = check_q(q_mean, E, cols, fmt, rot)) != AVERIS_OK) return st;
+  } else if (q_mean) {
+    return AVERIS_E_FLAGS;
+  }
+  if (!ws || ws_bytes < split_quant_grouped_ws_bytes(rows, cols, E)) return AVERIS_E_WORKSPACE;
+  if (!aligned16(ws)) return AVERIS_E_ALIGN;
+
+  SplitQuantPlan p{x, xdt, rows, cols, ldx, fmt, split, h16, given, means, q_row, q_col, q_mean, ws,
+                   reinterpret_cast<hipStream_t>(stream), d_offsets, h_offsets, E};
+  return split_quant_launch(p) == hipSuccess ? AVERIS_OK : AVERIS_E_HIP;
+}
+
+size_t averis_linear_grouped_workspace_size(int64_t N, int32_t E, int32_t fmt) {
+  (void)fmt;
+  if (N < 0 || E < 1) return 0;
+  return gemm_grouped_ws_bytes(0, N, E);
+}
+
+static int32_t linear_grouped_common(const averis_qtensor* a, const averis_qtensor* mu, const averis_qtensor* w,
+                                     const int64_t* d_offsets, const int64_t* h_offsets, int32_t E, void* out,
+                                     int32_t odt, int64_t ldo, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st;
+  const int64_t rows = check_offsets(d_offsets, h_offsets, E);
+  if (rows < 0) return (!d_offsets || !h_offsets) && E >= 1 ? AVERIS_E_NULL : AVERIS_E_SHAPE;
+  if (!aligned16(d_offsets)) return AVERIS_E_ALIGN;
+  if ((st = check_in(a)) != AVERIS_OK) return st;
+  if ((st = check_in(w)) != AVERIS_OK) return st;
+  if (!dtype_ok(odt)) return AVERIS_E_DTYPE;
+  if (a->fmt != w->fmt) return AVERIS_E_FORMAT;
+  if (a->k != w->k) return AVERIS_E_SHAPE;
+  if ((a->flags ^ w->flags) & AVERIS_HADAMARD16) return AVERIS_E_FLAGS;
+  if (a->outer != sum_round(h_offsets, E, 32)) return AVERIS_E_SHAPE;
+  if (w->outer % E != 0) return AVERIS_E_SHAPE;
+  const int64_t N = w->outer / E;
+  if (N % 32 != 0) return AVERIS_E_SHAPE;  // per-group weight blocks align with the 32-row scale groups
+  if (mu) {
+    if ((st = check_in(mu)) != AVERIS_OK) return st;
+    if (mu->fmt != a->fmt) return AVERIS_E_FORMAT;
+    if (mu->outer != E || mu->k != a->k) return AVERIS_E_SHAPE;
+    if ((mu->flags ^ a->flags) & AVERIS_HADAMARD16) return AVERIS_E_FLAGS;
+  }
+  if (ldo < N) return AVERIS_E_SHAPE;
+  if (rows > 0 && N > 0) {
+    if (!out) return AVERIS_E_NULL;
+    if (!aligned16(out) || (ldo * elem_size(odt)) % 16 != 0) return AVERIS_E_ALIGN;
+  }
+  if (!ws || ws_bytes < gemm_grouped_ws_bytes(0, N, E)) return AVERIS_E_WORKSPACE;
+  if (!aligned16(ws)) return AVERIS_E_ALIGN;
+  GemmPlan p{};
+  p.a = a; p.b = w; p.c = out; p.ldc = ldo; p.c_bf16 = odt == AVERIS_BF16;
+  p.mu = mu; p.splits = 1; p.ws = ws; p.stream = reinterpret_cast<hipStream_t>(stream);
+  p.grouped = 1; p.d_offsets = d_offsets; p.h_offsets = h_offsets; p.E = E;
+  return gemm_launch(p) == hipSuccess ? AVERIS_OK : AVERIS_E_HIP;
+}
+
+int32_t averis_linear_fwd_grouped(const averis_qtensor* xr, const averis_qtensor* mu_x, const averis_qtensor* w,
+                                  const int64_t* d_offsets, const int64_t* h_offsets, int32_t E, void* y, int32_t ydt,
+                                  int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  return linear_grouped_common(xr, mu_x, w, d_offsets, h_offsets, E, y, ydt, ldy, ws, ws_bytes, stream);
+}
+
+int32_t averis_linear_bwd_dx_grouped(const averis_qtensor* dr, const averis_qtensor* mu_d, const averis_qtensor* w,
+                                     const int64_t* d_offsets, const int64_t* h_offsets, int32_t E, void* dx,
+                                     int32_t dxdt, int64_t lddx, void* ws, size_t ws_bytes, void* stream) {
+  return linear_grouped_common(dr, mu_d, w, d_offsets, h_offsets, E, dx, dxdt, lddx, ws, ws_bytes, stream);
+}
+
+size_t averis_linear_bwd_dw_grouped_workspace_size(int64_t m, int64_t n, int32_t E, int32_t fmt) {
+  (void)fmt;
+  if (m < 0 || n < 0 || E < 1) return 0;
+  return gemm_grouped_ws_bytes(m, n, E);
+}
+
+int32_t averis_linear_bwd_dw_grouped(const averis_qtensor* xr_t, const averis_qtensor* dr_t,
+                                     const averis_qtensor* mu_x, const averis_qtensor* mu_d, const int64_t* d_offsets,
+                                     const int64_t* h_offsets, int32_t E, float* dw, int64_t lddw, uint32_t flags,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  int32_t st;
+  if (flags & ~AVERIS_ACCUMULATE) return AVERIS_E_FLAGS;
+  const int64_t rows = check_offsets(d_offsets, h_offsets, E);
+  if (rows < 0) return (!d_offsets || !h_offsets) && E >= 1 ? AVERIS_E_NULL : AVERIS_E_SHAPE;
+  if (!aligned16(d_offsets)) return AVERIS_E_ALIGN;
+  if (!xr_t || !dr_t) return AVERIS_E_NULL;
+  if (!fmt_ok(xr_t->fmt)) return AVERIS_E_FORMAT;
+  const uint32_t rot = xr_t->flags & AVERIS_HADAMARD16;
+  const int64_t tpad = sum_round(h_offsets, E, kKPad);
+  if ((st = check_qp(xr_t, xr_t->outer, rows, tpad, xr_t->fmt, rot)) != AVERIS_OK) return st;
+  if ((st = check_qp(dr_t, dr_t->outer, rows, tpad, xr_t->fmt, rot)) != AVERIS_OK) return st;
+  if ((mu_x == nullptr) != (mu_d == nullptr)) return AVERIS_E_NULL;
+  const int64_t m = xr_t->outer, n = dr_t->outer;
+  if (mu_x) {
+    if ((st = check_q(mu_x, E, m, xr_t->fmt, rot)) != AVERIS_OK) return st;
+    if ((st = check_q(mu_d, E, n, xr_t->fmt, rot)) != AVERIS_OK) return st;
+  }
+  if (lddw < n || n % 8 != 0) return AVERIS_E_SHAPE;
+  if (m > 0 && n > 0) {
+    if (!dw) return AVERIS_E_NULL;
+    if (!aligned16(dw) || (lddw * 4) % 16 != 0) return AVERIS_E_ALIGN;
+  }
+  if (!ws || ws_bytes < gemm_grouped_ws_bytes(m, n, E)) return AVERIS_E_WORKSPACE;
+  if (!aligned16(ws)) return AVERIS_E_ALIGN;
+  GemmPlan p{};
+  p.a = xr_t; p.b = dr_t; p.c = dw; p.ldc = lddw; p.c_bf16 = 0;
+  p.mu_u = mu_x; p.mu_v = mu_d; p.r1 = 0.0f;  // the factor is each group's own token count
+  p.accumulate = (flags & AVERIS_ACCUMULATE) ? 1 : 0;
+  p.splits = 1; p.ws = ws; p.stream = reinterpret_cast<hipStream_t>(stream);
+  p.grouped = 2; p.d_offsets = d_offsets; p.h_offsets = h_offsets; p.E = E;
   return gemm_launch(p) == hipSuccess ? AVERIS_OK : AVERIS_E_HIP;
 }
 

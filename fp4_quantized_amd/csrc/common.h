@@ -141,6 +141,55 @@ __device__ inline float nvfp4_tensor_scale(float amax) { return __fdiv_rn(amax, 
 // ---------------------------------------------------------------- wave helpers -------------
 __device__ inline float wave_xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
 
+// ---------------------------------------------------------------- grouped operands ---------
+// Group e (an expert) covers input rows [off[e], off[e+1]).  Per group: len = l_e, and the
+// exclusive prefix sums p32 = sum round_up(l_e', 32) (its first row in a grouped row layout)
+// and p256 = sum round_up(l_e', 256) (its first token in a grouped column layout).
+struct GroupPos {
+  int e;          // group, or -1 past the last item
+  int64_t local;  // item index inside the group
+  int64_t base;   // items of the groups before it
+  int64_t off, len, p32, p256;
+};
+
+// Wave-wide scan over the groups, 64 at a time.  Group e owns cnt(l_e) consecutive items; with
+// `by_item` the group holding item t is returned, otherwise group t itself.  Every lane of the
+// wave gets the same answer.
+template <class F>
+__device__ inline GroupPos group_scan(const int64_t* __restrict__ off, int E, int64_t t, bool by_item, F cnt) {
+  const int lane = threadIdx.x & 63;
+  int64_t b_cnt = 0, b32 = 0, b256 = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    const int64_t len = e < E ? off[e + 1] - off[e] : 0;
+    const int64_t c = e < E ? cnt(len) : 0, r32 = round_up(len, 32), r256 = round_up(len, 256);
+    int64_t sc = c, s32 = r32, s256 = r256;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t x = __shfl_up(sc, d, 64), y = __shfl_up(s32, d, 64), z = __shfl_up(s256, d, 64);
+      if (lane >= d) { sc += x; s32 += y; s256 += z; }
+    }
+    const bool mine = by_item ? (e < E && b_cnt + sc > t) : (e == t);
+    const uint64_t hit = __ballot(mine);
+    if (hit) {
+      const int L = __builtin_ctzll(hit);
+      GroupPos g;
+      g.e = e0 + L;
+      g.base = b_cnt + __shfl(sc, L, 64) - __shfl(c, L, 64);
+      g.local = t - g.base;
+      g.len = __shfl(len, L, 64);
+      g.off = off[g.e];
+      g.p32 = b32 + __shfl(s32, L, 64) - __shfl(r32, L, 64);
+      g.p256 = b256 + __shfl(s256, L, 64) - __shfl(r256, L, 64);
+      return g;
+    }
+    b_cnt += __shfl(sc, 63, 64); b32 += __shfl(s32, 63, 64); b256 += __shfl(s256, 63, 64);
+  }
+  GroupPos g{};
+  g.e = -1;
+  return g;
+}
+
 // Workgroup-id remap so that consecutive logical tiles run on the same XCD (workgroups are
 // dispatched round-robin over the 8 XCDs); partial cache lines written by neighbouring tiles
 // then meet in that XCD's L2.

@@ -20,6 +20,8 @@
 // barrier per K-step, no fence: each wave waits on its own vmcnt, then all meet at s_barrier.
 // Epilogue: out = alpha * acc + bias[col] + r1 * u[row] * v[col] (+ C when accumulating),
 // alpha = product of the operands' tensor decode scales (NVFP4) or 1.
+#include <algorithm>
+
 #include "launch.h"
 
 namespace av {
@@ -36,6 +38,13 @@ struct GemmArgs {
   int splits; int64_t k_chunk;          // K range per split (multiple of the K-step), partials at c + s * M * N
   int tiles_m, tiles_n;
   int group_m;                          // tile rows per group in the tile order (L2 locality)
+  // Grouped (MoE) launches: group e covers rows [offsets[e], offsets[e+1]) of the token axis.
+  //   grouped == 1 (forward / input gradient): A = grouped row layout (group e starts at row
+  //     p32[e]), B = E stacked [N, K] operands, C rows offsets[e] + r, bias [E][N], M = l_e.
+  //   grouped == 2 (weight gradient): A, B = per-group column layouts ([M, K_e] and [N, K_e],
+  //     K_e = round_up(l_e, 256), at token offset p256[e]), C = [E][M][ldc], rank-one factor
+  //     l_e with u [E][M] and v [E][N].  Every group has tiles_m x tiles_n tiles.
+  const int64_t* offsets; int E; int grouped;
 };
 
 __device__ inline uint32_t f32_to_bf16_rne(float f) {
@@ -70,17 +79,18 @@ __device__ inline void dequant32_bf16(const uint4& c, float s0, float s1, v8bf* 
   }
 }
 
-// Dequantized element k of a one-row operand (a quantized mean vector) with padded length
-// k_pad (fp32; exact for codes times an E8M0 scale, one rounding for NVFP4's decode scale).
+// Dequantized element k of row `row` of a quantized mean operand with padded length k_pad
+// (fp32; exact for codes times an E8M0 scale, one rounding for NVFP4's decode scale).
 template <int FMT>
-__device__ inline float dq_one(const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t k, int64_t k_pad) {
+__device__ inline float dq_one(const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t row, int64_t k,
+                               int64_t k_pad) {
   constexpr int G = FMT == AVERIS_MXFP4 ? 32 : 16;
-  const uint32_t byte = codes[k >> 1];
+  const uint32_t byte = codes[row * (k_pad / 2) + (k >> 1)];
   const uint32_t c = (k & 1) ? (byte >> 4) : (byte & 15u);
   const float v = fp4x2_to_f32(c, 0).x;
-  const uint32_t s = scales[scale_offset(0, k / G, k_pad, G)];
+  const uint32_t s = scales[scale_offset(row, k / G, k_pad, G)];
   if (FMT == AVERIS_MXFP4) return ldexpf(v, (int)s - 127);
-  return __fmul_rn(__fmul_rn(v, e4m3_value(s)), ts[0]);
+  return __fmul_rn(__fmul_rn(v, e4m3_value(s)), ts[row]);
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -387,20 +397,54 @@ __device__ __forceinline__ void store_slab(const GemmArgs& g, const float* epi, 
 }
 
 template <int FMT, int WM, int WN, int TM, int TN, int STAGES, int AUX = 0>
-__global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs g) {
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs gin) {
   using T = GemmTile<FMT, WM, WN, TM, TN, STAGES, AUX>;
   using C = typename T::C;
   static_assert(STAGES == 2 || STAGES == 3 || STAGES == 4, "stages");
+  GemmArgs g = gin;  // this workgroup's view (grouped launches retarget it to one group)
   __shared__ __attribute__((aligned(1024))) uint8_t st0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGES >= 3 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t st3[STAGES >= 4 ? C::STAGE : 16];
 
-  const int ntiles = g.tiles_m * g.tiles_n;
-  const int lin = xcd_remap(blockIdx.x, ntiles * g.splits);
-  const int split = lin / ntiles;
-  int tm, tn;
-  tile_coords(lin % ntiles, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+  int ntiles = g.tiles_m * g.tiles_n;
+  const int lin = xcd_remap(blockIdx.x, (int)gridDim.x);
+  int split = 0, tm, tn;
+  if (gin.grouped == 1) {
+    const int tn_all = gin.tiles_n;
+    const GroupPos gp = group_scan(gin.offsets, gin.E, lin, true,
+                                   [tn_all](int64_t len) { return ceil_div(len, (int64_t)C::BM) * tn_all; });
+    if (gp.e < 0) return;
+    const int tms = (int)ceil_div(gp.len, (int64_t)C::BM);
+    tile_coords((int)gp.local, tms, tn_all, gin.group_m < tms ? gin.group_m : tms, tm, tn);
+    const int64_t gsa = (gin.K / C::BKE) * C::PIECE;  // tiled scale bytes per 32-row group
+    g.M = gp.len;
+    g.a_codes += gp.p32 * gin.lda_b;
+    g.a_scales += (gp.p32 / 32) * gsa;
+    g.b_codes += (int64_t)gp.e * gin.N * gin.ldb_b;
+    g.b_scales += ((int64_t)gp.e * gin.N / 32) * gsa;
+    if (FMT == AVERIS_NVFP4) { g.a_ts += gp.e; g.b_ts += gp.e; }
+    if (gin.bias) g.bias += (int64_t)gp.e * gin.N;
+    g.c = reinterpret_cast<uint8_t*>(gin.c) + gp.off * gin.ldc * (gin.c_bf16 ? 2 : 4);
+  } else if (gin.grouped == 2) {
+    const int e = lin / ntiles;
+    tile_coords(lin % ntiles, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+    const GroupPos gp = group_scan(gin.offsets, gin.E, e, false, [](int64_t) { return (int64_t)1; });
+    const int64_t ke_pad = round_up(gp.len, (int64_t)C::BKE);
+    g.K = ke_pad; g.k_chunk = ke_pad;
+    g.lda_b = ke_pad / 2; g.ldb_b = ke_pad / 2;
+    g.a_codes += gin.M * gp.p256 / 2;
+    g.a_scales += gin.M * gp.p256 / C::G;
+    g.b_codes += gin.N * gp.p256 / 2;
+    g.b_scales += gin.N * gp.p256 / C::G;
+    if (FMT == AVERIS_NVFP4) { g.a_ts += e; g.b_ts += e; }
+    g.r1 = (float)gp.len;
+    if (gin.r1u) { g.r1u += (int64_t)e * gin.M; g.r1v += (int64_t)e * gin.N; }
+    g.c = reinterpret_cast<float*>(gin.c) + (int64_t)e * gin.M * gin.ldc;
+  } else {
+    split = lin / ntiles;
+    tile_coords(lin % ntiles, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+  }
   const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
   const int64_t kb = (int64_t)split * g.k_chunk;
   const int64_t ke = kb + g.k_chunk < g.K ? kb + g.k_chunk : g.K;
@@ -488,6 +532,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 }
 
 // Mean-term GEMV: out[j] = alpha * sum_k DQ(mu)[k] DQ(B)[j][k], one wave per output row.
+// Grouped launches (gridDim.y = E): group e uses row e of mu, rows e N .. of B, out + e N.
 // Each lane takes 32-element chunks; code products summed exactly in fp32 within a chunk, the
 // chunk sums scaled and accumulated in fp64; fixed-order lane reduction.
 template <int FMT>
@@ -497,9 +542,12 @@ __global__ __launch_bounds__(256) void k_gemv_mean(const uint8_t* __restrict__ m
                                                    const float* __restrict__ b_ts, int64_t N, int64_t K, float* __restrict__ out) {
   constexpr int G = FMT == AVERIS_MXFP4 ? 32 : 16;
   const int lane = threadIdx.x & 63;
+  const int64_t e = blockIdx.y;
   const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (j >= N) return;
-  const uint8_t* bc = b_codes + j * ldb_b;
+  const int64_t jb = e * N + j;  // row of B
+  mu_codes += e * (K / 2);
+  const uint8_t* bc = b_codes + jb * ldb_b;
   double s = 0.0;
   for (int64_t ch = lane; ch * 32 < K; ch += 64) {
     const uint4 ca = *reinterpret_cast<const uint4*>(mu_codes + ch * 16);
@@ -514,55 +562,57 @@ __global__ __launch_bounds__(256) void k_gemv_mean(const uint8_t* __restrict__ m
         part[q >> 1] = __fadd_rn(part[q >> 1], __fadd_rn(__fmul_rn(a.x, b.x), __fmul_rn(a.y, b.y)));
       }
     if (FMT == AVERIS_MXFP4) {
-      const int e = (int)mu_scales[scale_offset(0, ch, K, G)] + (int)b_scales[scale_offset(j, ch, K, G)] - 254;
-      s += ldexp((double)part[0] + (double)part[1], e);
+      const int ex = (int)mu_scales[scale_offset(e, ch, K, G)] + (int)b_scales[scale_offset(jb, ch, K, G)] - 254;
+      s += ldexp((double)part[0] + (double)part[1], ex);
     } else {
       const int64_t b0 = 2 * ch, b1 = 2 * ch + 1;
-      s += (double)part[0] * ((double)e4m3_value(mu_scales[scale_offset(0, b0, K, G)]) *
-                              (double)e4m3_value(b_scales[scale_offset(j, b0, K, G)])) +
-           (double)part[1] * ((double)e4m3_value(mu_scales[scale_offset(0, b1, K, G)]) *
-                              (double)e4m3_value(b_scales[scale_offset(j, b1, K, G)]));
+      s += (double)part[0] * ((double)e4m3_value(mu_scales[scale_offset(e, b0, K, G)]) *
+                              (double)e4m3_value(b_scales[scale_offset(jb, b0, K, G)])) +
+           (double)part[1] * ((double)e4m3_value(mu_scales[scale_offset(e, b1, K, G)]) *
+                              (double)e4m3_value(b_scales[scale_offset(jb, b1, K, G)]));
     }
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
   if (lane == 0) {
     double alpha = 1.0;
-    if (FMT == AVERIS_NVFP4) alpha = (double)mu_ts[0] * (double)b_ts[0];
-    out[j] = (float)(s * alpha);
+    if (FMT == AVERIS_NVFP4) alpha = (double)mu_ts[e] * (double)b_ts[e];
+    out[e * N + j] = (float)(s * alpha);
   }
 }
 
 // Dequantized mean vectors for the rank-one dW term, un-rotated when the means were quantized
-// after the 16x16 Hadamard rotation (rot != 0).
+// after the 16x16 Hadamard rotation (rot != 0).  `rows` mean rows per operand (one per group):
+// o0 [rows][K0], o1 [rows][K1].
 template <int FMT>
 __global__ __launch_bounds__(256) void k_mean_vec(const uint8_t* __restrict__ c0, const uint8_t* __restrict__ s0,
                                                   const float* __restrict__ t0, int64_t K0, int64_t P0, float* __restrict__ o0,
                                                   const uint8_t* __restrict__ c1, const uint8_t* __restrict__ s1,
                                                   const float* __restrict__ t1, int64_t K1, int64_t P1, float* __restrict__ o1,
-                                                  int rot) {
-  const int64_t n0 = (K0 + 15) / 16;
+                                                  int64_t rows, int rot) {
+  const int64_t nb0 = (K0 + 15) / 16, nb1 = (K1 + 15) / 16;
   int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const uint8_t *codes = c0, *scales = s0;
   const float* ts = t0;
-  int64_t K = K0, P = P0;
+  int64_t K = K0, P = P0, nb = nb0;
   float* out = o0;
-  if (blk >= n0) { blk -= n0; codes = c1; scales = s1; ts = t1; K = K1; P = P1; out = o1; }
-  if (blk * 16 >= K) return;
+  if (blk >= rows * nb0) { blk -= rows * nb0; codes = c1; scales = s1; ts = t1; K = K1; P = P1; nb = nb1; out = o1; }
+  if (blk >= rows * nb) return;
+  const int64_t row = blk / nb, b = blk % nb;
   double v[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = (double)dq_one<FMT>(codes, scales, ts, blk * 16 + j, P);
+  for (int j = 0; j < 16; ++j) v[j] = b * 16 + j < P ? (double)dq_one<FMT>(codes, scales, ts, row, b * 16 + j, P) : 0.0;
   if (rot) {
 #pragma unroll
     for (int h = 1; h < 16; h <<= 1)
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        if ((j & h) == 0) { const double a = v[j], b = v[j + h]; v[j] = a + b; v[j + h] = a - b; }
+        if ((j & h) == 0) { const double a = v[j], c = v[j + h]; v[j] = a + c; v[j + h] = a - c; }
   }
   const double sc = rot ? 0.25 : 1.0;
 #pragma unroll
   for (int j = 0; j < 16; ++j)
-    if (blk * 16 + j < K) out[blk * 16 + j] = (float)(v[j] * sc);
+    if (b * 16 + j < K) out[row * K + b * 16 + j] = (float)(v[j] * sc);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -609,15 +659,19 @@ static int splits_for(int cfg, int64_t M, int64_t N, int64_t K) {
 }
 int choose_splits(int fmt, int64_t M, int64_t N, int64_t K) { return splits_for(pick_cfg(fmt, M, N, K), M, N, K); }
 
-// workspace: [256 B][bias N][u round_up(M, 4)][v N] fp32 (16-byte aligned vectors), then
-// split-K partials [splits][M][N] fp32
-static size_t partials_offset(int64_t M, int64_t N) { return 256 + (size_t)round_up((N + round_up(M, 4) + N) * 4, 1024); }
+// workspace: [256 B][bias E x N][u E x round_up(M, 4)][v E x N] fp32 (16-byte aligned vectors),
+// then split-K partials [splits][M][N] fp32 (dense launches only)
+static size_t partials_offset(int64_t M, int64_t N, int64_t E) {
+  return 256 + (size_t)round_up(E * (N + round_up(M, 4) + N) * 4, 1024);
+}
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int splits) {
-  size_t b = partials_offset(M, N);
+  (void)K;
+  size_t b = partials_offset(M, N, 1);
   if (splits > 1) b += (size_t)splits * M * N * 4;
   return b;
 }
+size_t gemm_grouped_ws_bytes(int64_t M, int64_t N, int64_t E) { return partials_offset(M, N, E); }
 
 // MXFP4 takes every configuration; NVFP4 (bf16 MFMAs on dequantized fragments, 16 scale bytes
 // per row and K-step) only those whose registers and LDS fit.
@@ -647,39 +701,57 @@ hipError_t gemm_launch(const GemmPlan& p) {
   const averis_qtensor& A = *p.a;
   const averis_qtensor& B = *p.b;
   const int fmt = A.fmt;
+  const int64_t E = p.grouped ? p.E : 1;
+  // per-group GEMM sizes: rows of A (grouped forward: the largest group), rows of B, padded K
+  int64_t M = A.outer, N = B.outer, K = A.k_pad;
+  int64_t total_tiles_m = 0;
+  if (p.grouped == 1) {
+    N = B.outer / E;
+    M = 0;
+    for (int64_t e = 0; e < E; ++e) M = std::max<int64_t>(M, p.h_offsets[e + 1] - p.h_offsets[e]);
+  } else if (p.grouped == 2) {
+    K = 0;
+    for (int64_t e = 0; e < E; ++e) K = std::max<int64_t>(K, round_up(p.h_offsets[e + 1] - p.h_offsets[e], kBKE));
+  }
+  // grouped forward / input gradient use only the bias vectors of the workspace
+  const int64_t Mws = p.grouped == 1 ? 0 : M;
   uint8_t* ws = reinterpret_cast<uint8_t*>(p.ws);
   float* bias = reinterpret_cast<float*>(ws + 256);
-  float* u = bias + B.outer;
-  float* v = u + round_up(A.outer, 4);
-  float* partials = reinterpret_cast<float*>(ws + partials_offset(A.outer, B.outer));
+  float* u = bias + E * N;
+  float* v = u + E * round_up(Mws, 4);
+  float* partials = reinterpret_cast<float*>(ws + partials_offset(Mws, N, E));
 
   GemmArgs g{};
   g.a_codes = A.codes; g.a_scales = A.scales; g.lda_b = A.k_pad / 2;
   g.b_codes = B.codes; g.b_scales = B.scales; g.ldb_b = B.k_pad / 2;
   g.a_ts = A.tensor_scale; g.b_ts = B.tensor_scale;
-  g.M = A.outer; g.N = B.outer; g.K = A.k_pad;
-  const int cfg = pick_cfg(fmt, g.M, g.N, g.K);
+  g.M = M; g.N = N; g.K = K;
+  g.offsets = p.d_offsets; g.E = (int)E; g.grouped = p.grouped;
+  const int cfg = p.grouped == 2 ? 0 : pick_cfg(fmt, M, N, K);  // grouped dW: long, varying K
   const TileCfg tc = tile_of(cfg);
-  g.tiles_m = (int)ceil_div(g.M, tc.bm); g.tiles_n = (int)ceil_div(g.N, tc.bn);
+  g.tiles_m = (int)ceil_div(M, tc.bm); g.tiles_n = (int)ceil_div(N, tc.bn);
+  if (p.grouped == 1)
+    for (int64_t e = 0; e < E; ++e) total_tiles_m += ceil_div(p.h_offsets[e + 1] - p.h_offsets[e], tc.bm);
   {
     // group height ~ sqrt of the tiles each XCD owns, so its block of tiles is near square
-    const int per_xcd = (int)ceil_div((int64_t)g.tiles_m * g.tiles_n * p.splits, 8);
+    const int64_t tiles = p.grouped == 1 ? total_tiles_m * g.tiles_n : (int64_t)g.tiles_m * g.tiles_n * p.splits * E;
+    const int per_xcd = (int)ceil_div(tiles, 8);
     int gm = 1;
     while (gm * gm * 2 <= per_xcd && gm * 2 <= g.tiles_m) gm *= 2;
     g.group_m = gm;
   }
   g.accumulate = p.accumulate;
-  if (g.M == 0 || g.N == 0) return hipSuccess;
+  if (M == 0 || N == 0 || E == 0) return hipSuccess;
 
   if (p.mu) {
     const averis_qtensor& U = *p.mu;
-    const unsigned blocks = (unsigned)ceil_div(g.N, 4);
+    const dim3 blocks((unsigned)ceil_div(N, 4), (unsigned)E);
     if (fmt == AVERIS_MXFP4)
-      hipLaunchKernelGGL(k_gemv_mean<AVERIS_MXFP4>, dim3(blocks), dim3(256), 0, p.stream, U.codes, U.scales, U.tensor_scale,
-                         B.codes, B.scales, g.ldb_b, B.tensor_scale, g.N, B.k_pad, bias);
+      hipLaunchKernelGGL(k_gemv_mean<AVERIS_MXFP4>, blocks, dim3(256), 0, p.stream, U.codes, U.scales, U.tensor_scale,
+                         B.codes, B.scales, g.ldb_b, B.tensor_scale, N, B.k_pad, bias);
     else
-      hipLaunchKernelGGL(k_gemv_mean<AVERIS_NVFP4>, dim3(blocks), dim3(256), 0, p.stream, U.codes, U.scales, U.tensor_scale,
-                         B.codes, B.scales, g.ldb_b, B.tensor_scale, g.N, B.k_pad, bias);
+      hipLaunchKernelGGL(k_gemv_mean<AVERIS_NVFP4>, blocks, dim3(256), 0, p.stream, U.codes, U.scales, U.tensor_scale,
+                         B.codes, B.scales, g.ldb_b, B.tensor_scale, N, B.k_pad, bias);
     g.bias = bias;
   }
   if (p.mu_u) {
@@ -687,33 +759,36 @@ hipError_t gemm_launch(const GemmPlan& p) {
     const averis_qtensor& Qu = *p.mu_u;
     const averis_qtensor& Qv = *p.mu_v;
     const int rot = (Qu.flags & AVERIS_HADAMARD16) ? 1 : 0;
-    const unsigned blocks = (unsigned)ceil_div(ceil_div(Qu.k, 16) + ceil_div(Qv.k, 16), 256);
+    const unsigned blocks = (unsigned)ceil_div(E * (ceil_div(Qu.k, 16) + ceil_div(Qv.k, 16)), 256);
     if (fmt == AVERIS_MXFP4)
       hipLaunchKernelGGL(k_mean_vec<AVERIS_MXFP4>, dim3(blocks), dim3(256), 0, p.stream, Qu.codes, Qu.scales,
-                         Qu.tensor_scale, Qu.k, Qu.k_pad, u, Qv.codes, Qv.scales, Qv.tensor_scale, Qv.k, Qv.k_pad, v, rot);
+                         Qu.tensor_scale, Qu.k, Qu.k_pad, u, Qv.codes, Qv.scales, Qv.tensor_scale, Qv.k, Qv.k_pad, v, E,
+                         rot);
     else
       hipLaunchKernelGGL(k_mean_vec<AVERIS_NVFP4>, dim3(blocks), dim3(256), 0, p.stream, Qu.codes, Qu.scales,
-                         Qu.tensor_scale, Qu.k, Qu.k_pad, u, Qv.codes, Qv.scales, Qv.tensor_scale, Qv.k, Qv.k_pad, v, rot);
+                         Qu.tensor_scale, Qu.k, Qu.k_pad, u, Qv.codes, Qv.scales, Qv.tensor_scale, Qv.k, Qv.k_pad, v, E,
+                         rot);
     g.r1u = u; g.r1v = v;
   }
-  g.splits = p.splits;
-  const int64_t ksteps = ceil_div(g.K, kBKE);
-  g.k_chunk = ceil_div(ksteps, p.splits) * kBKE;
-  if (p.splits > 1) {
-    g.c = partials; g.ldc = g.N; g.c_bf16 = 0;
+  g.splits = p.grouped ? 1 : p.splits;
+  const int64_t ksteps = ceil_div(K, kBKE);
+  g.k_chunk = ceil_div(ksteps, g.splits) * kBKE;
+  if (g.splits > 1) {
+    g.c = partials; g.ldc = N; g.c_bf16 = 0;
   } else {
     g.c = p.c; g.ldc = p.ldc; g.c_bf16 = p.c_bf16;
   }
-  const unsigned grid = (unsigned)(g.tiles_m * g.tiles_n * p.splits);
-  if (fmt == AVERIS_MXFP4) launch_mx(cfg, g, grid, p.stream);
-  else launch_nv(cfg, g, grid, p.stream);
-  if (p.splits > 1) {
-    const unsigned blocks = (unsigned)ceil_div(g.M * (g.N / 4), 256);
+  const int64_t grid = p.grouped == 1 ? total_tiles_m * g.tiles_n : (int64_t)g.tiles_m * g.tiles_n * g.splits * E;
+  if (grid == 0) return hipGetLastError();
+  if (fmt == AVERIS_MXFP4) launch_mx(cfg, g, (unsigned)grid, p.stream);
+  else launch_nv(cfg, g, (unsigned)grid, p.stream);
+  if (g.splits > 1) {
+    const unsigned blocks = (unsigned)ceil_div(M * (N / 4), 256);
     if (fmt == AVERIS_MXFP4)
-      hipLaunchKernelGGL(k_splitk_reduce<AVERIS_MXFP4>, dim3(blocks), dim3(256), 0, p.stream, partials, p.splits, g, p.c,
+      hipLaunchKernelGGL(k_splitk_reduce<AVERIS_MXFP4>, dim3(blocks), dim3(256), 0, p.stream, partials, g.splits, g, p.c,
                          p.ldc, p.c_bf16);
     else
-      hipLaunchKernelGGL(k_splitk_reduce<AVERIS_NVFP4>, dim3(blocks), dim3(256), 0, p.stream, partials, p.splits, g, p.c,
+      hipLaunchKernelGGL(k_splitk_reduce<AVERIS_NVFP4>, dim3(blocks), dim3(256), 0, p.stream, partials, g.splits, g, p.c,
                          p.ldc, p.c_bf16);
   }
   return hipGetLastError();

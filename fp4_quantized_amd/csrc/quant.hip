@@ -85,7 +85,8 @@ template <typename T, bool MINMAX>
 __global__ __launch_bounds__(kThreads) void k_colstats(const T* __restrict__ x, int64_t rows, int64_t cols,
                                                        int64_t ldx, double* __restrict__ psum,
                                                        float* __restrict__ pmin, float* __restrict__ pmax,
-                                                       uint32_t* __restrict__ slots) {
+                                                       uint32_t* __restrict__ slots, int n_slots,
+                                                       const int64_t* __restrict__ offsets, int E) {
   constexpr int VEC = Elem<T>::VEC;
   constexpr int TC = 32 * VEC;
   constexpr int PER = kStatRows / 8;
@@ -94,18 +95,27 @@ __global__ __launch_bounds__(kThreads) void k_colstats(const T* __restrict__ x, 
   __shared__ float s_max[MINMAX ? 8 : 1][TC];
 
   // the rotated-amax slots are atomically maxed only by later kernels of the same call
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 4) slots[threadIdx.x] = 0u;
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < n_slots; i += kThreads) slots[i] = 0u;
 
+  // rows of this slab: [rb, re); grouped launches number the slabs group after group
+  int64_t rb = (int64_t)blockIdx.y * kStatRows, re = rows;
+  if (offsets) {
+    const GroupPos gp = group_scan(offsets, E, blockIdx.y, true, [](int64_t len) { return ceil_div(len, (int64_t)kStatRows); });
+    rb = gp.e < 0 ? 0 : gp.off + gp.local * kStatRows;
+    re = gp.e < 0 ? 0 : gp.off + gp.len;
+  }
+  if (re > rb + kStatRows) re = rb + kStatRows;
   const int lane_c = threadIdx.x & 31, phase = threadIdx.x >> 5;
   const int64_t c0 = (int64_t)blockIdx.x * TC + lane_c * VEC;
-  const int64_t r0 = (int64_t)blockIdx.y * kStatRows + phase;
+  const int64_t r0 = rb + phase;
   const bool col_ok = c0 < cols;
 
   uint4 w[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int64_t r = r0 + 8 * i;
-    w[i] = (col_ok && r < rows) ? *reinterpret_cast<const uint4*>(x + r * ldx + c0) : make_uint4(0, 0, 0, 0);
+    w[i] = (col_ok && r < re) ? *reinterpret_cast<const uint4*>(x + r * ldx + c0) : make_uint4(0, 0, 0, 0);
   }
   double sum[VEC];
   float mn[VEC], mx[VEC];
@@ -122,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void k_colstats(const T* __restrict__ x, 
       Elem<T>::unpack(w[i], v);  // rows past the end are zeros: harmless in the sum
 #pragma unroll
       for (int j = 0; j < VEC; ++j) part[j] = __fadd_rn(part[j], v[j]);
-      if (MINMAX && r0 + 8 * i < rows) {
+      if (MINMAX && r0 + 8 * i < re) {
 #pragma unroll
         for (int j = 0; j < VEC; ++j) { mn[j] = fminf(mn[j], v[j]); mx[j] = fmaxf(mx[j], v[j]); }
       }
@@ -157,19 +167,30 @@ __global__ __launch_bounds__(kThreads) void k_colstats(const T* __restrict__ x, 
 // columns, the four partials are then added in wave order.  Writes mu (SPLIT without
 // MEAN_GIVEN) and, per workgroup, the max |residual| (MINMAX: exact from the column min / max,
 // since fl(x - mu) is monotone in x) and the max |mu| (after the 16x16 rotation when h16),
-// both as per-workgroup partials: no atomics, nothing to clear.
+// both as per-workgroup partials: no atomics, nothing to clear.  Grouped launches: group
+// blockIdx.y, its slabs and rows, mean row, and partials [group][workgroup].
 // mode bit 0 = SPLIT, bit 1 = MEAN_GIVEN.
 // ------------------------------------------------------------------------------------------
 template <bool MINMAX>
 __global__ __launch_bounds__(kThreads) void k_finalize(const double* __restrict__ psum, const float* __restrict__ pmin,
                                                        const float* __restrict__ pmax, int nslab, int64_t rows,
                                                        int64_t cols, int mode, int h16, float* __restrict__ mean,
-                                                       float* __restrict__ ramax_part, float* __restrict__ mamax_part) {
+                                                       float* __restrict__ ramax_part, float* __restrict__ mamax_part,
+                                                       const int64_t* __restrict__ offsets, int E) {
   __shared__ double s_sum[4][64];
   __shared__ float s_min[4][64], s_max[4][64];
   const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t c = (int64_t)blockIdx.x * 64 + lane;
   const bool cin = c < cols;
+  int64_t s0 = 0;
+  if (offsets) {
+    const GroupPos gp = group_scan(offsets, E, blockIdx.y, false, [](int64_t len) { return ceil_div(len, (int64_t)kStatRows); });
+    s0 = gp.base;
+    nslab = (int)ceil_div(gp.len, (int64_t)kStatRows);
+    rows = gp.len;
+    mean += (int64_t)blockIdx.y * cols;
+  }
+  psum += s0 * cols; pmin += s0 * cols; pmax += s0 * cols;
   const int per = (nslab + 3) / 4;
   const int pb = q * per, pe = pb + per < nslab ? pb + per : nslab;
   double s = 0.0;
@@ -215,7 +236,10 @@ __global__ __launch_bounds__(kThreads) void k_finalize(const double* __restrict_
   float ma = fabsf(mv[0]);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) { ra = wave_xor_max(ra, m); ma = wave_xor_max(ma, m); }
-  if (lane == 0) { ramax_part[blockIdx.x] = ra; mamax_part[blockIdx.x] = ma; }
+  if (lane == 0) {
+    const int64_t o = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    ramax_part[o] = ra; mamax_part[o] = ma;
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -256,6 +280,13 @@ struct QuantArgs {
   int64_t col_kpad;            // padded token count of the column layout
   int64_t row_kpad;            // padded column count of the row layout (its row stride in elements)
   int tiles_r, tiles_c;
+  int64_t rows_out;            // rows of the row layout written (rows past `rows` are zero residuals)
+  int mean_row, mean_rows;     // row of the quantized mean written here; its rows in total
+  int cover_kpad;              // row tiles cover the column layout's padded token count
+  // grouped launches: group e = input rows [offsets[e], offsets[e+1]), quantized on its own
+  // (own mean row, tensor scales and amax partials); row layout rows start at the group's
+  // 32-aligned offset, column layout tokens at its 256-aligned offset
+  const int64_t* offsets; int E;
 };
 
 
@@ -268,8 +299,8 @@ __device__ __forceinline__ void quant_extras(const QuantArgs& a, int tr, int tc,
   const int64_t cend = c0 + TC < a.cols ? c0 + TC : a.cols;
   // ---- row layout: K tail of codes and scales, and scale rows up to the 32-row group ----
   if (a.row_codes) {
-    const int64_t kp = a.row_kpad, rp = round_up(a.rows, 32);
-    const int64_t rend_d = r0 + kTileRows < a.rows ? r0 + kTileRows : a.rows;
+    const int64_t kp = a.row_kpad, rp = round_up(a.rows_out, 32);
+    const int64_t rend_d = r0 + kTileRows < a.rows_out ? r0 + kTileRows : a.rows_out;
     const int64_t rend_p = r0 + kTileRows < rp ? r0 + kTileRows : rp;
     if (last_tc && kp > a.cols) {
       const int nq = (int)((kp - a.cols) / 32);  // 16-byte chunks of code tail per row
@@ -281,14 +312,15 @@ __device__ __forceinline__ void quant_extras(const QuantArgs& a, int tr, int tc,
       for (int64_t i = t; i < (rend_p - r0) * nt; i += kThreads)
         a.row_scales[scale_offset(r0 + i / nt, a.cols / G + i % nt, kp, G)] = 0;
     }
-    const int64_t pr0 = r0 > a.rows ? r0 : a.rows;
+    const int64_t pr0 = r0 > a.rows_out ? r0 : a.rows_out;
     const int nb = (int)((cend - c0) / G);
     for (int64_t i = t; i < (rend_p - pr0) * nb; i += kThreads)
       a.row_scales[scale_offset(pr0 + i / nb, c0 / G + i % nb, kp, G)] = 0;
   }
   if (!a.mean_codes || tr != 0) return;
-  // ---- quantized mean: this tile's blocks of row 0, zero rows 1..31 and the K tail ----
-  const int64_t kp = a.mean_kpad;
+  // ---- quantized mean: this tile's blocks of its row, the row's K tail, and (first group)
+  // the zero rows up to the 32-row group ----
+  const int64_t kp = a.mean_kpad, mr = a.mean_row;
   float s_dec = 0.0f;
   if (FMT == AVERIS_NVFP4) {
     float m = 0.0f;
@@ -296,7 +328,7 @@ __device__ __forceinline__ void quant_extras(const QuantArgs& a, int tr, int tc,
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) m = wave_xor_max(m, s);
     s_dec = nvfp4_tensor_scale(m);
-    if (tc == 0 && t == 0) a.mean_ts[0] = s_dec;
+    if (tc == 0 && t == 0) a.mean_ts[mr] = s_dec;
   }
   for (int64_t c = c0 + (int64_t)t * G; c < cend; c += (int64_t)kThreads * G) {
     float v[32];
@@ -314,21 +346,34 @@ __device__ __forceinline__ void quant_extras(const QuantArgs& a, int tr, int tc,
     for (int j = 0; j < G; ++j) v[j] = __fmul_rn(v[j], q.mul);
 #pragma unroll
     for (int j = 0; j < G / 8; ++j)
-      *reinterpret_cast<uint32_t*>(a.mean_codes + c / 2 + 4 * j) = q.dead ? 0u : pack8_fp4(v + 8 * j);
-    a.mean_scales[scale_offset(0, c / G, kp, G)] = (uint8_t)q.sbyte;
+      *reinterpret_cast<uint32_t*>(a.mean_codes + mr * (kp / 2) + c / 2 + 4 * j) = q.dead ? 0u : pack8_fp4(v + 8 * j);
+    a.mean_scales[scale_offset(mr, c / G, kp, G)] = (uint8_t)q.sbyte;
   }
-  const int nb = (int)((cend - c0) / G);
-  for (int i = t; i < 31 * nb; i += kThreads) a.mean_scales[scale_offset(1 + i / nb, c0 / G + i % nb, kp, G)] = 0;
+  const int nt = (int)((kp - a.cols) / G);  // K-tail blocks per row
   if (last_tc && kp > a.cols) {
     const int nq = (int)((kp - a.cols) / 32);
-    if (t < nq) *reinterpret_cast<uint4*>(a.mean_codes + a.cols / 2 + t * 16) = make_uint4(0, 0, 0, 0);
-    const int nt = (int)((kp - a.cols) / G);
-    for (int i = t; i < 32 * nt; i += kThreads) a.mean_scales[scale_offset(i / nt, a.cols / G + i % nt, kp, G)] = 0;
+    if (t < nq) *reinterpret_cast<uint4*>(a.mean_codes + mr * (kp / 2) + a.cols / 2 + t * 16) = make_uint4(0, 0, 0, 0);
+    for (int i = t; i < nt; i += kThreads) a.mean_scales[scale_offset(mr, a.cols / G + i, kp, G)] = 0;
+  }
+  if (mr == 0) {
+    const int64_t z0 = a.mean_rows, zn = round_up(a.mean_rows, 32) - a.mean_rows;
+    const int nb = (int)((cend - c0) / G) + (last_tc ? nt : 0);
+    for (int64_t i = t; i < zn * nb; i += kThreads) {
+      const int64_t r = z0 + i / nb, bi = i % nb;
+      const int64_t blk = bi < (cend - c0) / G ? c0 / G + bi : a.cols / G + (bi - (cend - c0) / G);
+      a.mean_scales[scale_offset(r, blk, kp, G)] = 0;
+    }
   }
 }
 
+// Row tiles of a group of `len` rows.
+__device__ __host__ inline int64_t quant_row_tiles(int64_t len, int cover_kpad) {
+  const int64_t t = ceil_div(cover_kpad ? round_up(len, kKPad) : round_up(len, 32), kTileRows);
+  return t > 0 ? t : 1;
+}
+
 template <typename T, int FMT, bool H16, bool AMAX_ONLY>
-__global__ __launch_bounds__(kThreads) void k_quant(QuantArgs a) {
+__global__ __launch_bounds__(kThreads) void k_quant(QuantArgs ain) {
   constexpr int VEC = Elem<T>::VEC;
   constexpr int TC = 32 * VEC;
   constexpr int G = FMT == AVERIS_MXFP4 ? 32 : 16;
@@ -336,8 +381,40 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs a) {
   __shared__ T s_tile[kTileRows][TC];
   __shared__ float s_red[2][kThreads / 64];
 
-  const int tile = xcd_remap(blockIdx.x, a.tiles_r * a.tiles_c);
-  const int tr = tile % a.tiles_r, tc = tile / a.tiles_r;
+  QuantArgs a = ain;  // this workgroup's view (grouped launches retarget it to one group)
+  const int tile = xcd_remap(blockIdx.x, (int)gridDim.x);
+  int tr, tc;
+  if (ain.offsets) {
+    const int tcs = ain.tiles_c, cov = ain.cover_kpad;
+    const GroupPos gp = group_scan(ain.offsets, ain.E, tile, true,
+                                   [tcs, cov](int64_t len) { return quant_row_tiles(len, cov) * tcs; });
+    if (gp.e < 0) return;
+    const int64_t trs = quant_row_tiles(gp.len, cov);
+    tr = (int)(gp.local % trs); tc = (int)(gp.local / trs);
+    const int e = gp.e;
+    a.x = reinterpret_cast<const T*>(ain.x) + gp.off * ain.ldx;
+    a.rows = gp.len;
+    a.rows_out = round_up(gp.len, 32);
+    if (a.mean) a.mean += (int64_t)e * ain.cols;
+    a.ramax_part += (int64_t)e * ain.n_part;
+    a.mamax_part += (int64_t)e * ain.n_part;
+    a.amax_slots += 2 * e;
+    a.amax_out += 2 * e;
+    a.mean_row = e;
+    if (a.row_codes) {
+      a.row_codes += gp.p32 * (ain.row_kpad / 2);
+      a.row_scales += scale_offset(gp.p32, 0, ain.row_kpad, G);
+    }
+    if (a.row_ts) a.row_ts += e;
+    if (a.col_codes) {
+      a.col_codes += ain.cols * gp.p256 / 2;
+      a.col_scales += ain.cols * gp.p256 / G;
+    }
+    if (a.col_ts) a.col_ts += e;
+    a.col_kpad = round_up(gp.len, kKPad);
+  } else {
+    tr = tile % ain.tiles_r; tc = tile / ain.tiles_r;
+  }
   const int64_t r0 = (int64_t)tr * kTileRows, c0 = (int64_t)tc * TC;
   const int lane_c = threadIdx.x & 31, phase = threadIdx.x >> 5;
   const int lane = threadIdx.x & 63;
@@ -359,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs a) {
     }
     sd_row = nvfp4_tensor_scale(ar);
     sd_col = nvfp4_tensor_scale(ac);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (tr == 0 && tc == 0 && threadIdx.x == 0) {
       if (a.row_ts) a.row_ts[0] = sd_row;
       if (a.col_ts) a.col_ts[0] = sd_col;
     }
@@ -388,8 +465,9 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs a) {
       const int64_t r = r0 + phase + 8 * i;
       float v[VEC];
       Elem<T>::unpack(w[i], v);
+      const bool live = r < a.rows;  // rows past the data are zero residuals
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) v[j] = __fsub_rn(v[j], mu[j]);
+      for (int j = 0; j < VEC; ++j) v[j] = live ? __fsub_rn(v[j], mu[j]) : 0.0f;
       if (H16) h16_lanes<VEC>(v, lane);
       float m = 0.0f;
 #pragma unroll
@@ -403,7 +481,7 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs a) {
       const BlockQ q = block_params<FMT>(m, sd_row);
 #pragma unroll
       for (int j = 0; j < VEC; ++j) v[j] = __fmul_rn(v[j], q.mul);
-      if (r < a.rows && col_ok) {
+      if (r < a.rows_out && col_ok) {
         uint8_t* dst = a.row_codes + r * (a.row_kpad / 2) + cc / 2;
         if (VEC == 8) *reinterpret_cast<uint32_t*>(dst) = q.dead ? 0u : pack8_fp4(v);
         else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(q.dead ? 0u : pack4_fp4(v));
@@ -498,34 +576,43 @@ static int64_t slab_count(int64_t rows) {
   return n > 0 ? n : 1;  // one (empty) slab when rows == 0
 }
 
-// workspace: [0, 256) amax slots | [256, ..) finalize partials (2 x n_part fp32) | column
-// statistics: psum [nslab][cols] fp64, pmin and pmax [nslab][cols] fp32
+// workspace: [0, hdr) amax slots (3 + 2 E uint32) | finalize partials (2 x E x n_part fp32) |
+// column statistics: psum [nslab][cols] fp64, pmin and pmax [nslab][cols] fp32
 struct SqLayout {
-  uint32_t* slots; float* ramax; float* mamax; double* psum; float* pmin; float* pmax; int n_part; int64_t nslab;
+  uint32_t* slots; int n_slots; float* ramax; float* mamax; double* psum; float* pmin; float* pmax;
+  int n_part; int64_t nslab;
 };
-static SqLayout sq_layout(void* ws, int64_t rows, int64_t cols) {
+static size_t sq_header(int64_t E) { return (size_t)round_up((3 + 2 * E) * 4, 256); }
+static SqLayout sq_layout(void* ws, int64_t nslab, int64_t cols, int64_t E) {
   SqLayout L;
   uint8_t* b = reinterpret_cast<uint8_t*>(ws);
   L.n_part = (int)ceil_div(cols, 64);
-  L.nslab = slab_count(rows);
-  const size_t pb = (size_t)round_up(L.n_part * 4, 256);
+  L.nslab = nslab;
+  const size_t h = sq_header(E), pb = (size_t)round_up(E * L.n_part * 4, 256);
   L.slots = reinterpret_cast<uint32_t*>(b);
-  L.ramax = reinterpret_cast<float*>(b + 256);
-  L.mamax = reinterpret_cast<float*>(b + 256 + pb);
-  L.psum = reinterpret_cast<double*>(b + 256 + 2 * pb);
-  L.pmin = reinterpret_cast<float*>(b + 256 + 2 * pb + (size_t)L.nslab * cols * 8);
+  L.n_slots = (int)(3 + 2 * E);
+  L.ramax = reinterpret_cast<float*>(b + h);
+  L.mamax = reinterpret_cast<float*>(b + h + pb);
+  L.psum = reinterpret_cast<double*>(b + h + 2 * pb);
+  L.pmin = reinterpret_cast<float*>(b + h + 2 * pb + (size_t)L.nslab * cols * 8);
   L.pmax = L.pmin + (size_t)L.nslab * cols;
   return L;
 }
-
-size_t split_quant_ws_bytes(int64_t rows, int64_t cols) {
+static size_t sq_bytes(int64_t nslab, int64_t cols, int64_t E) {
   const int64_t n_part = ceil_div(cols, 64);
-  return 256 + 2 * (size_t)round_up(n_part * 4, 256) + (size_t)slab_count(rows) * cols * (8 + 4 + 4) + 256;
+  return sq_header(E) + 2 * (size_t)round_up(E * n_part * 4, 256) + (size_t)nslab * cols * (8 + 4 + 4) + 256;
+}
+
+size_t split_quant_ws_bytes(int64_t rows, int64_t cols) { return sq_bytes(slab_count(rows), cols, 1); }
+// grouped: at most ceil(rows / 128) + E slabs
+size_t split_quant_grouped_ws_bytes(int64_t rows, int64_t cols, int64_t E) {
+  return sq_bytes(ceil_div(rows, kStatRows) + E + 1, cols, E);
 }
 
 template <typename T, int FMT, bool H16>
 static hipError_t launch_quant_t(const SplitQuantPlan& p, const SqLayout& L) {
   constexpr int TC = 32 * Elem<T>::VEC;
+  const bool grouped = p.E > 0;
   QuantArgs a{};
   a.x = p.x; a.rows = p.rows; a.cols = p.cols; a.ldx = p.ldx;
   a.mean = p.split ? p.mean : nullptr;
@@ -535,13 +622,24 @@ static hipError_t launch_quant_t(const SplitQuantPlan& p, const SqLayout& L) {
   a.col_kpad = col_kpad;
   a.row_kpad = round_up(p.cols, kKPad);
   a.tiles_c = (int)ceil_div(p.cols, TC);
-  // column layout covers the padding rows too (they are zero residuals); at least one row tile
-  // so that the tensor scales, the quantized mean and the padding are written for rows == 0
-  const int64_t tr = ceil_div(p.q_col ? col_kpad : p.rows, kTileRows);
-  a.tiles_r = (int)(tr > 0 ? tr : 1);
-  const int ntiles = a.tiles_r * a.tiles_c;
-  if (ntiles == 0) {  // no columns: still define the tensor scales (0)
-    if (FMT == AVERIS_NVFP4) {
+  a.rows_out = p.rows;
+  a.mean_row = 0; a.mean_rows = grouped ? (int)p.E : 1;
+  a.cover_kpad = p.q_col ? 1 : 0;
+  int64_t ntiles;
+  if (grouped) {
+    a.offsets = p.d_offsets; a.E = (int)p.E;
+    int64_t tr = 0;
+    for (int64_t e = 0; e < p.E; ++e) tr += quant_row_tiles(p.h_offsets[e + 1] - p.h_offsets[e], a.cover_kpad);
+    a.tiles_r = (int)tr;
+    ntiles = tr * a.tiles_c;
+  } else {
+    // column layout covers the padding rows too (they are zero residuals); at least one row tile
+    // so that the tensor scales, the quantized mean and the padding are written for rows == 0
+    a.tiles_r = (int)quant_row_tiles(p.rows, a.cover_kpad);
+    ntiles = (int64_t)a.tiles_r * a.tiles_c;
+  }
+  if (ntiles == 0) {  // no columns or no groups: still define the tensor scales (0)
+    if (FMT == AVERIS_NVFP4 && !grouped) {
       float* ts[3] = {p.q_row ? p.q_row->tensor_scale : nullptr, p.q_col ? p.q_col->tensor_scale : nullptr,
                       p.q_mean ? p.q_mean->tensor_scale : nullptr};
       for (float* t : ts)
@@ -551,7 +649,7 @@ static hipError_t launch_quant_t(const SplitQuantPlan& p, const SqLayout& L) {
   }
   if (FMT == AVERIS_NVFP4 && H16) {
     QuantArgs m = a;
-    hipLaunchKernelGGL((k_quant<T, FMT, H16, true>), dim3(ntiles), dim3(kThreads), 0, p.stream, m);
+    hipLaunchKernelGGL((k_quant<T, FMT, H16, true>), dim3((unsigned)ntiles), dim3(kThreads), 0, p.stream, m);
   }
   if (p.q_row) { a.row_codes = p.q_row->codes; a.row_scales = p.q_row->scales; a.row_ts = p.q_row->tensor_scale; }
   if (p.q_col) { a.col_codes = p.q_col->codes; a.col_scales = p.q_col->scales; a.col_ts = p.q_col->tensor_scale; }
@@ -559,7 +657,7 @@ static hipError_t launch_quant_t(const SplitQuantPlan& p, const SqLayout& L) {
     a.mean_codes = p.q_mean->codes; a.mean_scales = p.q_mean->scales; a.mean_ts = p.q_mean->tensor_scale;
     a.mean_kpad = p.q_mean->k_pad;
   }
-  hipLaunchKernelGGL((k_quant<T, FMT, H16, false>), dim3(ntiles), dim3(kThreads), 0, p.stream, a);
+  hipLaunchKernelGGL((k_quant<T, FMT, H16, false>), dim3((unsigned)ntiles), dim3(kThreads), 0, p.stream, a);
   return hipGetLastError();
 }
 
@@ -571,16 +669,27 @@ static hipError_t launch_quant_f(const SplitQuantPlan& p, const SqLayout& L) {
 template <typename T, bool MINMAX>
 static void launch_stats_t(const SplitQuantPlan& p, const SqLayout& L) {
   constexpr int TC = 32 * Elem<T>::VEC;
+  const bool grouped = p.E > 0;
+  const int64_t groups = grouped ? p.E : 1;
   const dim3 grid((unsigned)ceil_div(p.cols, TC), (unsigned)L.nslab);
   hipLaunchKernelGGL((k_colstats<T, MINMAX>), grid, dim3(kThreads), 0, p.stream, reinterpret_cast<const T*>(p.x), p.rows,
-                     p.cols, p.ldx, L.psum, L.pmin, L.pmax, L.slots);
+                     p.cols, p.ldx, L.psum, L.pmin, L.pmax, L.slots, L.n_slots, grouped ? p.d_offsets : nullptr,
+                     (int)groups);
   const int mode = (p.split ? 1 : 0) | (p.mean_given ? 2 : 0);
-  hipLaunchKernelGGL((k_finalize<MINMAX>), dim3((unsigned)L.n_part), dim3(kThreads), 0, p.stream, L.psum, L.pmin,
-                     L.pmax, (int)L.nslab, p.rows, p.cols, mode, (p.split && p.h16) ? 1 : 0, p.mean, L.ramax, L.mamax);
+  hipLaunchKernelGGL((k_finalize<MINMAX>), dim3((unsigned)L.n_part, (unsigned)groups), dim3(kThreads), 0, p.stream,
+                     L.psum, L.pmin, L.pmax, (int)L.nslab, p.rows, p.cols, mode, (p.split && p.h16) ? 1 : 0, p.mean,
+                     L.ramax, L.mamax, grouped ? p.d_offsets : nullptr, (int)groups);
 }
 
 hipError_t split_quant_launch(const SplitQuantPlan& p) {
-  const SqLayout L = sq_layout(p.ws, p.rows, p.cols);
+  const bool grouped = p.E > 0;
+  int64_t nslab = slab_count(p.rows);
+  if (grouped) {
+    nslab = 0;
+    for (int64_t e = 0; e < p.E; ++e) nslab += ceil_div(p.h_offsets[e + 1] - p.h_offsets[e], kStatRows);
+    if (nslab == 0) nslab = 1;
+  }
+  const SqLayout L = sq_layout(p.ws, nslab, p.cols, grouped ? p.E : 1);
   const bool nv = p.fmt == AVERIS_NVFP4;
   // column statistics: the mean (SPLIT without MEAN_GIVEN) and, for NVFP4, the residual amax
   if (p.cols > 0 && (nv || (p.split && !p.mean_given))) {

@@ -179,6 +179,73 @@ int32_t averis_linear_bwd_dw(const averis_qtensor *xr_t, const averis_qtensor *d
                              float *dw, int64_t lddw, uint32_t flags, void *ws, size_t ws_bytes,
                              void *stream);
 
+/* =========================================================================================
+ * Grouped (MoE) variants.  [rainbus] 实验结果 and 结构化数据: the 7B-A1.5B mixture-of-experts
+ * model is trained with Averis; the split is applied per expert on the expert's own token
+ * slice, so every group gets its own mean, residual and (NVFP4) tensor scales, and the dW
+ * rank-one factor is the group's own token count.
+ *
+ * Groups: E >= 1 groups of consecutive token rows, group e = rows [offsets[e], offsets[e+1]),
+ * offsets[0] = 0, non-decreasing, L = offsets[E] rows in total (empty groups allowed).
+ *   d_offsets  device int64 [E + 1], read by the kernels (16-byte aligned);
+ *   h_offsets  host int64 [E + 1] with the same values, used to size the launch and to validate.
+ * Grouped operand layouts (l_e = offsets[e+1] - offsets[e]):
+ *   row layout (K = features): outer = sum_e round_up(l_e, 32), k = cols; group e's rows start
+ *     at sum_{e'<e} round_up(l_e', 32), so scale groups never straddle groups; rows past l_e
+ *     inside a group hold zero codes and scales.
+ *   column layout (K = tokens): outer = cols, k = L, k_pad = sum_e round_up(l_e, 256); group e is
+ *     a [cols, round_up(l_e, 256)] operand starting at token t_e = sum_{e'<e} round_up(l_e', 256):
+ *     codes at byte cols * t_e / 2, tiled scales at byte cols * t_e / g.
+ *   quantized means: outer = E, k = cols (row e = group e).
+ *   tensor_scale (NVFP4): one fp32 per group.
+ * Stacked weights W_e [m, n] (input [E * m, n], groups of m rows, m % 32 == 0) quantized with
+ * SPLIT off give exactly the two weight operands: the row layout is E stacked [m, n] operands
+ * (input-gradient B) and the column layout is E stacked [n, m] operands (forward B).
+ * ========================================================================================= */
+size_t averis_split_quant_grouped_workspace_size(int64_t rows, int64_t cols, int32_t E, int32_t fmt,
+                                                 uint32_t flags);
+
+/* Per group exactly averis_split_quant on its rows.  means: device fp32 [E][cols].  q_row,
+ * q_col, q_mean as described above (q_mean required with SPLIT). */
+int32_t averis_split_quant_grouped(const void *x, int32_t xdt, int64_t cols, int64_t ldx,
+                                   const int64_t *d_offsets, const int64_t *h_offsets, int32_t E,
+                                   int32_t fmt, uint32_t flags, float *means,
+                                   const averis_qtensor *q_row, const averis_qtensor *q_col,
+                                   const averis_qtensor *q_mean, void *ws, size_t ws_bytes,
+                                   void *stream);
+
+/* Workspace of the grouped forward / input-gradient GEMMs with N output columns per group. */
+size_t averis_linear_grouped_workspace_size(int64_t N, int32_t E, int32_t fmt);
+
+/* Per group e: Y[offsets[e] + r] = 1 (Q(mu_X,e) Q(W_e)) + Q(X_R,e) Q(W_e), one launch for all
+ * groups.  xr: grouped row layout [sum round_up(l_e, 32), m]; mu_x: [E, m] or NULL; w: E stacked
+ * [n, m] operands (outer = E * n, n % 32 == 0; the column layout of the stacked weights).
+ * y: device [L, n], element type ydt, leading dimension ldy >= n. */
+int32_t averis_linear_fwd_grouped(const averis_qtensor *xr, const averis_qtensor *mu_x,
+                                  const averis_qtensor *w, const int64_t *d_offsets,
+                                  const int64_t *h_offsets, int32_t E, void *y, int32_t ydt,
+                                  int64_t ldy, void *ws, size_t ws_bytes, void *stream);
+
+/* Per group e: dX[offsets[e] + r] = 1 (Q(mu_D,e) Q(W_e)^T) + Q(D_R,e) Q(W_e)^T.  dr: grouped row
+ * layout [sum round_up(l_e, 32), n]; mu_d [E, n] or NULL; w: E stacked [m, n] operands
+ * (outer = E * m, m % 32 == 0; the row layout of the stacked weights); dx: [L, m]. */
+int32_t averis_linear_bwd_dx_grouped(const averis_qtensor *dr, const averis_qtensor *mu_d,
+                                     const averis_qtensor *w, const int64_t *d_offsets,
+                                     const int64_t *h_offsets, int32_t E, void *dx, int32_t dxdt,
+                                     int64_t lddx, void *ws, size_t ws_bytes, void *stream);
+
+size_t averis_linear_bwd_dw_grouped_workspace_size(int64_t m, int64_t n, int32_t E, int32_t fmt);
+
+/* Per group e: dW_e = Q(X_R,e)^T Q(D_R,e) + l_e Q(mu_X,e)^T Q(mu_D,e).  xr_t, dr_t: grouped
+ * column layouts (outer m and n); mu_x [E, m], mu_d [E, n], both or neither; dw: device fp32
+ * [E][m][lddw] (group stride m * lddw).  An empty group's dW is zero (or unchanged with
+ * AVERIS_ACCUMULATE). */
+int32_t averis_linear_bwd_dw_grouped(const averis_qtensor *xr_t, const averis_qtensor *dr_t,
+                                     const averis_qtensor *mu_x, const averis_qtensor *mu_d,
+                                     const int64_t *d_offsets, const int64_t *h_offsets, int32_t E,
+                                     float *dw, int64_t lddw, uint32_t flags, void *ws,
+                                     size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -430,6 +430,16 @@ def linear_fwd_grouped(sq_x, q_ws, offsets, n):
     return np.concatenate(ys, axis=0) if ys else np.zeros((0, n))
 
 
+def linear_bwd_dx_grouped(sq_d, q_ws, offsets, m):
+    """Stack of per-expert input gradients, [total_tokens, m]; q_ws[e] is expert e's K = n weight."""
+    ds = []
+    for e, s in enumerate(sq_d):
+        if s is None:
+            continue
+        ds.append(linear_bwd_dx(s["row"], s["mean"], q_ws[e]))
+    return np.concatenate(ds, axis=0) if ds else np.zeros((0, m))
+
+
 def linear_bwd_dw_grouped(sq_x, sq_d, offsets, m, n):
     """Per-expert dW [E, m, n]; an empty expert's dW is zero."""
     E = len(offsets) - 1

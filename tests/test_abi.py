@@ -148,3 +148,67 @@ def test_bwd_dw_rejects():
     assert call(wsb=100) == E_WORKSPACE
     assert call(dr=q(384, 300, av.MXFP4)) == E_FORMAT
     assert L.averis_linear_bwd_dw_workspace_size(512, 384, 300, av.NVFP4) > 0
+
+
+def offs(*v):
+    return (ctypes.c_int64 * len(v))(*v)
+
+
+def test_split_quant_grouped_rejects():
+    L = av.lib()
+    ref = ctypes.byref
+    h = offs(0, 37, 37, 100)  # E = 3, row layout 64 + 0 + 64 rows, tokens 256 + 0 + 256
+    E, cols = 3, 128
+
+    def call(x=FAKE, h=h, E=E, d=FAKE, q_row="auto", q_col="auto", q_mean="auto", flags=av.SPLIT, means=FAKE,
+             ws=FAKE, wsb=1 << 30):
+        if q_row == "auto":
+            q_row = q(128, cols)
+        if q_col == "auto":
+            q_col = av.CQTensor(FAKE, FAKE, FAKE, cols, 100, 512, av.NVFP4, 0)
+        if q_mean == "auto":
+            q_mean = q(E, cols)
+        r = lambda t: ref(t) if t is not None else None
+        return L.averis_split_quant_grouped(x, av.BF16, cols, cols, d, h, E, av.NVFP4, flags, means, r(q_row),
+                                            r(q_col), r(q_mean), ws, wsb, None)
+
+    assert call(E=0) == E_SHAPE
+    assert call(d=None) == E_NULL
+    assert call(h=offs(1, 37, 37, 100)) == E_SHAPE          # offsets must start at 0
+    assert call(h=offs(0, 37, 30, 100)) == E_SHAPE          # and never decrease
+    assert call(q_row=q(100, cols)) == E_SHAPE              # rows are padded per group to 32
+    assert call(q_col=q(cols, 100)) == E_SHAPE              # tokens are padded per group to 256
+    assert call(q_mean=q(1, cols)) == E_SHAPE               # one mean row per group
+    assert call(means=None) == E_NULL
+    assert call(wsb=16) == E_WORKSPACE
+    assert L.averis_split_quant_grouped_workspace_size(100, cols, E, av.NVFP4, av.SPLIT) > 0
+    assert L.averis_split_quant_grouped_workspace_size(100, cols, 0, av.NVFP4, av.SPLIT) == 0
+
+
+def test_linear_grouped_rejects():
+    L = av.lib()
+    ref = ctypes.byref
+    h = offs(0, 37, 37, 100)
+    E, m, n = 3, 256, 128
+    a, mu, w = q(128, m), q(E, m), q(E * n, m)
+
+    def call(a=a, mu=mu, w=w, h=h, d=FAKE, out=FAKE, ldo=n, wsb=1 << 30):
+        r = lambda t: ref(t) if t is not None else None
+        return L.averis_linear_fwd_grouped(r(a), r(mu), r(w), d, h, E, out, av.F32, ldo, FAKE, wsb, None)
+
+    assert call(a=q(100, m)) == E_SHAPE        # grouped row layout has 32-row padded groups
+    assert call(w=q(E * n + 32, m)) == E_SHAPE  # weights stack E equal groups
+    assert call(w=q(E * 80, m)) == E_SHAPE      # each group a multiple of 32 rows
+    assert call(mu=q(1, m)) == E_SHAPE
+    assert call(d=None) == E_NULL
+    assert call(out=None) == E_NULL
+    assert call(ldo=64) == E_SHAPE
+    assert call(wsb=16) == E_WORKSPACE
+    xt = av.CQTensor(FAKE, FAKE, FAKE, m, 100, 512, av.NVFP4, 0)
+    dt = av.CQTensor(FAKE, FAKE, FAKE, n, 100, 512, av.NVFP4, 0)
+    dw = lambda xt=xt, dt=dt, mx=q(E, m), md=q(E, n), fl=0: L.averis_linear_bwd_dw_grouped(
+        ref(xt), ref(dt), ref(mx) if mx else None, ref(md) if md else None, FAKE, h, E, FAKE, n, fl, FAKE, 1 << 30, None)
+    assert dw(fl=1 << 3) == E_FLAGS
+    assert dw(dt=av.CQTensor(FAKE, FAKE, FAKE, n, 100, 256, av.NVFP4, 0)) == E_SHAPE
+    assert dw(md=None) == E_NULL
+    assert dw(mx=q(1, m)) == E_SHAPE

@@ -390,3 +390,31 @@ def test_grouped_equals_per_expert_calls():
     np.testing.assert_array_equal(g[3]["row"].codes, s["row"].codes)
     np.testing.assert_array_equal(g[3]["col"].codes, s["col"].codes)
     np.testing.assert_array_equal(g[3]["mu32"], x[17:100].astype(np.float64).mean(axis=0).astype(np.float32))
+
+
+def test_grouped_linear_stacks_per_expert_results():
+    # the grouped GEMMs are the per-expert GEMMs stacked in expert order; an empty expert adds
+    # no rows and gets dW = 0; each expert's rank-one factor is its own token count
+    rng = np.random.default_rng(43)
+    offs = np.array([0, 40, 40, 90])
+    m, n = 64, 32
+    x = (rng.standard_normal((90, m)) + 2).astype(np.float32)
+    d = (rng.standard_normal((90, n)) * 1e-3 + 1e-3).astype(np.float32)
+    ws = [(rng.standard_normal((m, n)) * 0.02).astype(np.float32) for _ in range(3)]
+    sx = O.split_quant_grouped(x, offs, O.NVFP4)
+    sd = O.split_quant_grouped(d, offs, O.NVFP4)
+    qw = [O.split_quant(w, O.NVFP4, split=False) for w in ws]
+    y = O.linear_fwd_grouped(sx, [q["col"] for q in qw], offs, n)
+    dx = O.linear_bwd_dx_grouped(sd, [q["row"] for q in qw], offs, m)
+    dw = O.linear_bwd_dw_grouped(sx, sd, offs, m, n)
+    assert y.shape == (90, n) and dx.shape == (90, m) and dw.shape == (3, m, n)
+    np.testing.assert_array_equal(y[40:], O.linear_fwd(sx[2]["row"], sx[2]["mean"], qw[2]["col"]))
+    np.testing.assert_array_equal(dx[:40], O.linear_bwd_dx(sd[0]["row"], sd[0]["mean"], qw[0]["row"]))
+    assert not dw[1].any()
+    ref = O.linear_bwd_dw(sx[2]["col"], sd[2]["col"], sx[2]["mean"], sd[2]["mean"], 50)
+    np.testing.assert_array_equal(dw[2], ref)
+    # the rank-one term uses l_e = 50, not the total 90: removing it leaves X_R^T D_R alone
+    no_mean = O.linear_bwd_dw(sx[2]["col"], sd[2]["col"], None, None, 50)
+    u = O.dequantize(sx[2]["mean"])[0, :m]
+    v = O.dequantize(sd[2]["mean"])[0, :n]
+    np.testing.assert_allclose(dw[2] - no_mean, 50.0 * np.outer(u, v), rtol=1e-12, atol=1e-18)
