@@ -152,6 +152,14 @@ struct GroupPos {
   int64_t off, len, p32, p256;
 };
 
+// Values equal in every lane, moved to scalar registers so that the compiler knows it (buffer
+// descriptors built from them stay uniform).
+__device__ inline int uniform32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Wave-wide scan over the groups, 64 at a time.  Group e owns cnt(l_e) consecutive items; with
 // `by_item` the group holding item t is returned, otherwise group t itself.  Every lane of the
 // wave gets the same answer.
@@ -174,13 +182,13 @@ __device__ inline GroupPos group_scan(const int64_t* __restrict__ off, int E, in
     if (hit) {
       const int L = __builtin_ctzll(hit);
       GroupPos g;
-      g.e = e0 + L;
-      g.base = b_cnt + __shfl(sc, L, 64) - __shfl(c, L, 64);
-      g.local = t - g.base;
-      g.len = __shfl(len, L, 64);
-      g.off = off[g.e];
-      g.p32 = b32 + __shfl(s32, L, 64) - __shfl(r32, L, 64);
-      g.p256 = b256 + __shfl(s256, L, 64) - __shfl(r256, L, 64);
+      g.e = uniform32(e0 + L);
+      g.base = uniform64(b_cnt + __shfl(sc, L, 64) - __shfl(c, L, 64));
+      g.local = uniform64(t) - g.base;
+      g.len = uniform64(__shfl(len, L, 64));
+      g.off = uniform64(off[g.e]);
+      g.p32 = uniform64(b32 + __shfl(s32, L, 64) - __shfl(r32, L, 64));
+      g.p256 = uniform64(b256 + __shfl(s256, L, 64) - __shfl(r256, L, 64));
       return g;
     }
     b_cnt += __shfl(sc, 63, 64); b32 += __shfl(s32, 63, 64); b256 += __shfl(s256, 63, 64);
