@@ -97,6 +97,20 @@ __device__ inline uint32_t pack8_fp4(const float* v) {
   w = cvt_fp4x2<3>(w, v[6], v[7]);
   return w;
 }
+// Eight E2M1 codes of v[j] / scale.  With an MXFP4 block scale 2^e the conversion's division is
+// exact, fl(v / 2^e) == fl(v * 2^-e), so it replaces the separate multiply.
+__device__ inline uint32_t pack8_fp4_div(const float* v, float scale) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], scale, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], scale, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], scale, 3);
+  return w;
+}
+// 2^e of an MXFP4 scale code e + 127 as fp32 (2^-127 is subnormal).
+__device__ inline float mx_scale_value(uint32_t sbyte) {
+  return sbyte ? __uint_as_float(sbyte << 23) : __uint_as_float(0x00400000u);
+}
 __device__ inline uint32_t pack4_fp4(const float* v) {
   uint32_t w = 0;
   w = cvt_fp4x2<0>(w, v[0], v[1]);
@@ -140,6 +154,36 @@ __device__ inline float nvfp4_tensor_scale(float amax) { return __fdiv_rn(amax, 
 
 // ---------------------------------------------------------------- wave helpers -------------
 __device__ inline float wave_xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
+
+// Workgroup barrier that orders LDS accesses only: the wave waits for its own LDS operations,
+// not for its global stores to be acknowledged (__syncthreads() waits for those too).  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// ---------------------------------------------------------------- direct-to-LDS loads -----
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Raw buffer resource over `bytes` bytes at `base` (bytes < 2^32): loads at offsets >= bytes
+// return zero, which pads partial tiles with zeros and keeps them inside the allocation.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// One wave-wide direct-to-LDS load: lane L's SIZE bytes from rsrc[voff + soff] land at lds + L * SIZE.
+template <int AUX>
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, AUX);
+}
+template <int AUX>
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, voff, soff, 0, AUX);
+}
+// Wait until at most N vector-memory ops of this wave are outstanding and all its LDS ops are
+// done (gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
 
 // ---------------------------------------------------------------- grouped operands ---------
 // Group e (an expert) covers input rows [off[e], off[e+1]).  Per group: len = l_e, and the
@@ -196,6 +240,19 @@ __device__ inline GroupPos group_scan(const int64_t* __restrict__ off, int E, in
   GroupPos g{};
   g.e = -1;
   return g;
+}
+
+// Persistent launches: the logical tiles [0, n) are cut into 8 contiguous runs, one per XCD
+// (workgroups are dispatched round-robin over the 8 XCDs, so workgroup b runs on XCD b % 8);
+// workgroup k of XCD x takes tiles start_x + k, start_x + k + G_x, ... where G_x is the number of
+// workgroups on XCD x.  Neighbouring tiles are then in flight at the same time on one XCD.
+__device__ inline void xcd_tiles(int b, int grid, int n, int& first, int& stride, int& end) {
+  const int x = b & 7, k = b >> 3;
+  const int q = n >> 3, r = n & 7;
+  const int start = x * q + (x < r ? x : r), cnt = q + (x < r ? 1 : 0);
+  first = start + k;
+  stride = (grid >> 3) + ((grid & 7) > x ? 1 : 0);
+  end = start + cnt;
 }
 
 // Workgroup-id remap so that consecutive logical tiles run on the same XCD (workgroups are

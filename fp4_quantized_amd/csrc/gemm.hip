@@ -93,34 +93,11 @@ __device__ inline float dq_one(const uint8_t* codes, const uint8_t* scales, cons
   return __fmul_rn(__fmul_rn(v, e4m3_value(s)), ts[row]);
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Raw buffer resource over `bytes` bytes at `base`: loads at offsets >= bytes return zero,
-// which pads partial tiles (rows past M or N) with zero codes and zero scales.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-// One wave-wide direct-to-LDS load: lane L's SIZE bytes from rsrc[voff + soff] land at lds + L * SIZE.
-template <int AUX>
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, AUX);
-}
-template <int AUX>
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, voff, soff, 0, AUX);
-}
 // Two fp32 values to packed bf16 (round to nearest even), low half first.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
   const v2bf16 v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
-}
-// Wait until at most N vector-memory ops of this wave are outstanding and all its LDS ops are
-// done (gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
 }
 
 // Tile order: consecutive logical tiles walk down a group of `gm` tile rows, then move one

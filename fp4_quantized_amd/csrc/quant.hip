@@ -13,11 +13,12 @@
 //               column min and max
 //   k_finalize  fixed-order reduction of the slabs -> mu (fp32); per-workgroup maxima of the
 //               residual (exact from min / max: fl(x - mu) is monotone in x) and of the mean
-//   k_quant     re-read a 64-row tile, subtract, rotate, block amax, scale, E2M1, and emit
-//               both layouts: K = features (row layout) from registers, K = tokens (column
-//               layout) through an LDS transpose; row tile 0 also quantizes the mean, and each
-//               tile zeroes the padding it owns.  With NVFP4 + Hadamard the rotated amax is
-//               not available from min / max, so k_quant first runs once in amax-only mode.
+//   k_quant     re-read a 32-row tile into LDS, subtract, rotate, block amax, scale, E2M1,
+//               and emit both layouts: K = features (row layout) one 64-byte unit per thread,
+//               K = tokens (column layout) one column per thread; row tile 0 also quantizes
+//               the mean, and each tile zeroes the padding it owns.  With NVFP4 + Hadamard
+//               the rotated amax is not available from min / max, so k_quant first runs once
+//               in amax-only mode.
 // A vanilla MXFP4 operand (no split) needs k_quant only.
 #include "launch.h"
 
@@ -25,7 +26,6 @@ namespace av {
 
 constexpr int kThreads = 256;
 constexpr int kStatRows = 128;  // rows per k_colstats workgroup: 16 per thread, loaded in one batch
-constexpr int kTileRows = 64;   // rows per k_quant tile
 
 // ------------------------------------------------------------------------------------------
 // 16-point Hadamard butterflies (Sylvester order, stages h = 1, 2, 4, 8), then x 0.25.
@@ -243,21 +243,36 @@ __global__ __launch_bounds__(kThreads) void k_finalize(const double* __restrict_
 }
 
 // ------------------------------------------------------------------------------------------
-// k_quant: one workgroup per 64-row x TC-column tile (TC = 32 * VEC: 256 bf16 or 128 fp32
-// columns).  Grid is 1-D over tiles_r x tiles_c, XCD-remapped with the row tile fastest.
+// k_quant: one workgroup per 32-row x TC-column tile (TC = 32 * VEC: 256 bf16 or 128 fp32
+// columns), row tile fastest in the tile numbering.  The tile is loaded with coalesced 16-byte
+// loads and staged in LDS in the plane layout below, the column means in a swizzled order; both
+// layouts then read from LDS:
+//   row layout     thread t quantizes one 64-byte unit of row t / 8 (two units for fp32 MXFP4,
+//                  whose 32-element block spans two): whole blocks, no lane exchange;
+//   column layout  thread t quantizes column t over the tile's 32 rows.
+// MXFP4 divides by the power-of-two block scale inside the E2M1 conversion (exact); tiles whose
+// rows all hold data skip the per-element row masks.
 //
-// Row layout: thread t holds VEC consecutive columns (t % 32) * VEC of rows t / 32 + 8 i; a
-// block of G columns spans G / VEC lanes and its amax is a lane-shuffle max.
-// Column layout: the raw tile goes to LDS; thread t then takes column t % TC and the 32-row
-// half (t / TC + j * (256 / TC)) and quantizes down the column in registers.
-//
-// The workgroups of row tile 0 also quantize the mean's blocks in their columns, and every
-// workgroup zeroes the padding it owns (row-layout K tail, scale rows up to the 32-row group,
-// the quantized mean's tail and rows 1..31), so one launch writes every output byte.
+// The tiles of row tile 0 also quantize the mean's blocks in their columns, and every tile
+// zeroes the padding it owns (row-layout K tail, scale rows up to the 32-row group, the
+// quantized mean's tail and rows 1..31), so one launch writes every output byte.  Grouped
+// launches number the tiles group after group; a tile belongs to one group.
 //
 // AMAX_ONLY: compute max |rotated residual| of each layout and atomically max it into
 // amax_slots[1] (row) and amax_slots[2] (column); nothing is stored.
 // ------------------------------------------------------------------------------------------
+constexpr int kQRows = 32;                  // rows per tile
+// LDS layout of a tile: a tile row (512 bytes) is 8 units of 64 bytes, a unit 4 chunks of 16
+// bytes.  Chunk j of unit u of row r sits in plane j at slot r * 8 + u; planes are kQPlane
+// slots apart.  A thread reading its whole unit (row layout) and 64 lanes reading one element
+// each of 64 consecutive columns (column layout) then hit distinct LDS banks.
+constexpr int kQPlane = kQRows * 8 + 2;     // slots per plane (2 slots of padding)
+constexpr int kQBufBytes = 4 * kQPlane * 16;
+// Column means of a tile: unit u's float chunk i (4 floats) at 16-byte slot i * 8 + u, so that
+// the 8 units' chunks read together are contiguous.
+template <int EPU>
+__device__ __forceinline__ int mean_slot(int c) { return ((c % EPU) >> 2) * 8 + c / EPU; }
+
 struct QuantArgs {
   const void* x;
   int64_t rows, cols, ldx;
@@ -289,9 +304,8 @@ struct QuantArgs {
   const int64_t* offsets; int E;
 };
 
-
-// Mean quantization (row tile 0) and padding zeroes for k_quant's tile (tr, tc).
-template <int FMT, bool H16, int TC>
+// Mean quantization (row tile 0) and padding zeroes for tile (tr, tc) of ROWS rows.
+template <int FMT, bool H16, int TC, int ROWS>
 __device__ __forceinline__ void quant_extras(const QuantArgs& a, int tr, int tc, int64_t r0, int64_t c0) {
   constexpr int G = FMT == AVERIS_MXFP4 ? 32 : 16;
   const int t = threadIdx.x;
@@ -300,8 +314,8 @@ __device__ __forceinline__ void quant_extras(const QuantArgs& a, int tr, int tc,
   // ---- row layout: K tail of codes and scales, and scale rows up to the 32-row group ----
   if (a.row_codes) {
     const int64_t kp = a.row_kpad, rp = round_up(a.rows_out, 32);
-    const int64_t rend_d = r0 + kTileRows < a.rows_out ? r0 + kTileRows : a.rows_out;
-    const int64_t rend_p = r0 + kTileRows < rp ? r0 + kTileRows : rp;
+    const int64_t rend_d = r0 + ROWS < a.rows_out ? r0 + ROWS : a.rows_out;
+    const int64_t rend_p = r0 + ROWS < rp ? r0 + ROWS : rp;
     if (last_tc && kp > a.cols) {
       const int nq = (int)((kp - a.cols) / 32);  // 16-byte chunks of code tail per row
       for (int64_t i = t; i < (rend_d - r0) * nq; i += kThreads) {
@@ -367,19 +381,193 @@ __device__ __forceinline__ void quant_extras(const QuantArgs& a, int tr, int tc,
 }
 
 // Row tiles of a group of `len` rows.
+template <int ROWS>
 __device__ __host__ inline int64_t quant_row_tiles(int64_t len, int cover_kpad) {
-  const int64_t t = ceil_div(cover_kpad ? round_up(len, kKPad) : round_up(len, 32), kTileRows);
+  const int64_t t = ceil_div(cover_kpad ? round_up(len, kKPad) : round_up(len, 32), ROWS);
   return t > 0 ? t : 1;
 }
 
-template <typename T, int FMT, bool H16, bool AMAX_ONLY>
-__global__ __launch_bounds__(kThreads) void k_quant(QuantArgs ain) {
-  constexpr int VEC = Elem<T>::VEC;
-  constexpr int TC = 32 * VEC;
+// NVFP4 tensor decode scales of one launch (or group): from the rotated amax slots (H16), else
+// from k_finalize's per-workgroup maxima of |residual|.  Every lane of the wave gets them.
+template <bool H16>
+__device__ __forceinline__ void nvfp4_scales(const QuantArgs& a, float& sd_row, float& sd_col) {
+  float ar, ac;
+  if (H16) {
+    ar = __uint_as_float(a.amax_slots[1]);
+    ac = __uint_as_float(a.amax_slots[2]);
+  } else {
+    float m = 0.0f;
+    for (int i = threadIdx.x & 63; i < a.n_part; i += 64) m = fmaxf(m, a.ramax_part[i]);
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) m = wave_xor_max(m, s);
+    ar = ac = m;
+  }
+  sd_row = nvfp4_tensor_scale(ar);
+  sd_col = nvfp4_tensor_scale(ac);
+}
+
+// Per-wave maxima of the AMAX_ONLY pass -> one atomic max per slot and workgroup.  Every wave
+// of the workgroup calls it (it holds a barrier); waves >= `nw` contribute nothing.
+__device__ __forceinline__ void amax_commit(const QuantArgs& a, float ra, float ca, float (*s_red)[8], int nw) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    ra = wave_xor_max(ra, m);
+    ca = wave_xor_max(ca, m);
+  }
+  if (lane == 0 && wave < nw) { s_red[0][wave] = ra; s_red[1][wave] = ca; }
+  lds_barrier();
+  if (threadIdx.x == 0) {
+    float u = s_red[0][0], v = s_red[1][0];
+    for (int i = 1; i < nw; ++i) { u = fmaxf(u, s_red[0][i]); v = fmaxf(v, s_red[1][i]); }
+    atomicMax(a.amax_out + 1, __float_as_uint(u));
+    atomicMax(a.amax_out + 2, __float_as_uint(v));
+  }
+}
+
+// E2M1 codes of n (8 or 16) values of one block into dst words, after its scale decision.
+template <int FMT>
+__device__ __forceinline__ void block_codes(float* v, int n, const BlockQ& q, uint32_t* dst) {
+  if (FMT == AVERIS_MXFP4) {
+    const float sc = mx_scale_value(q.sbyte);
+    for (int k = 0; k < n / 8; ++k) dst[k] = q.dead ? 0u : pack8_fp4_div(v + 8 * k, sc);
+  } else {
+    for (int j = 0; j < n; ++j) v[j] = __fmul_rn(v[j], q.mul);
+    for (int k = 0; k < n / 8; ++k) dst[k] = q.dead ? 0u : pack8_fp4(v + 8 * k);
+  }
+}
+
+// Row layout of a tile: thread t quantizes one 64-byte unit (two for fp32 MXFP4, whose
+// 32-element block spans two units) of row t * UPT / 8: whole blocks, so no lane exchange.
+// FULL: every row of the tile holds data.
+template <typename T, int FMT, bool H16, bool AMAX_ONLY, bool FULL>
+__device__ __forceinline__ void tile_rows(const QuantArgs& a, int64_t r0, int64_t c0, const uint8_t* tile,
+                                            const float* means, float sd_row, float& amax_acc) {
+  constexpr int SZ = (int)sizeof(T);
   constexpr int G = FMT == AVERIS_MXFP4 ? 32 : 16;
-  constexpr int LPB = G / VEC;  // lanes per row-layout block
-  __shared__ T s_tile[kTileRows][TC];
-  __shared__ float s_red[2][kThreads / 64];
+  constexpr int UPT = G * SZ > 64 ? G * SZ / 64 : 1;  // units per thread
+  constexpr int EPU = 64 / SZ;                         // elements per unit
+  constexpr int EPT = UPT * EPU;                       // elements per thread
+  constexpr int NT = kQRows * 8 / UPT;                 // threads with work
+  const int t = threadIdx.x;
+  if (t >= NT) return;
+  const int r = (t * UPT) >> 3, u0 = (t * UPT) & 7;
+  const int64_t row = r0 + r, cbase = c0 + u0 * EPU;
+  uint32_t d[EPT * SZ / 4];
+#pragma unroll
+  for (int q = 0; q < UPT; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 c = *reinterpret_cast<const uint4*>(tile + (j * kQPlane + r * 8 + u0 + q) * 16);
+      d[q * 16 + j * 4] = c.x; d[q * 16 + j * 4 + 1] = c.y; d[q * 16 + j * 4 + 2] = c.z; d[q * 16 + j * 4 + 3] = c.w;
+    }
+  float v[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT * SZ / 16; ++i) {
+    const int e0 = i * (16 / SZ);  // first element of chunk i of the thread
+    const float4 m4 = *reinterpret_cast<const float4*>(means + 4 * mean_slot<EPU>(u0 * EPU + e0));
+    float x[4 * (SZ == 2 ? 2 : 1)];
+    Elem<T>::unpack(make_uint4(d[4 * i], d[4 * i + 1], d[4 * i + 2], d[4 * i + 3]), x);
+    if (SZ == 2) {
+      const float4 m5 = *reinterpret_cast<const float4*>(means + 4 * mean_slot<EPU>(u0 * EPU + e0 + 4));
+      const float mm[8] = {m4.x, m4.y, m4.z, m4.w, m5.x, m5.y, m5.z, m5.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[8 * i + e] = __fsub_rn(x[e], mm[e]);
+    } else {
+      const float mm[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * i + e] = __fsub_rn(x[e], mm[e]);
+    }
+  }
+  if (!FULL && row >= a.rows) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) v[e] = 0.0f;  // rows past the data are zero residuals
+  }
+  if (H16) {
+#pragma unroll
+    for (int h = 0; h < EPT / 16; ++h) h16_inreg(v + 16 * h);
+  }
+  const bool col_ok = cbase < a.cols;
+  uint32_t codes[EPT / 8];
+  uint32_t sb = 0;
+#pragma unroll
+  for (int b = 0; b < EPT / G; ++b) {
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < G; ++j) m = fmaxf(m, fabsf(v[b * G + j]));
+    if (AMAX_ONLY) {
+      if ((FULL || row < a.rows) && col_ok) amax_acc = fmaxf(amax_acc, m);
+      continue;
+    }
+    const BlockQ q = block_params<FMT>(m, sd_row);
+    block_codes<FMT>(v + b * G, G, q, codes + b * (G / 8));
+    sb |= q.sbyte << (8 * b);
+  }
+  if (AMAX_ONLY) return;
+  if (row < a.rows_out && col_ok) {
+    uint8_t* dst = a.row_codes + row * (a.row_kpad / 2) + cbase / 2;
+    if (EPT == 32) *reinterpret_cast<uint4*>(dst) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+    else *reinterpret_cast<uint2*>(dst) = make_uint2(codes[0], codes[1]);
+    uint8_t* sd = a.row_scales + scale_offset(row, cbase / G, a.row_kpad, G);
+    if (EPT / G == 2) *reinterpret_cast<uint16_t*>(sd) = (uint16_t)sb;
+    else *sd = (uint8_t)sb;
+  }
+}
+
+// Column layout of a tile: thread t quantizes column t over the tile's 32 rows.
+template <typename T, int FMT, bool H16, bool AMAX_ONLY, bool FULL>
+__device__ __forceinline__ void tile_cols(const QuantArgs& a, int64_t r0, int64_t c0, const uint8_t* tile,
+                                            const float* means, float sd_col, float& amax_acc) {
+  constexpr int SZ = (int)sizeof(T);
+  constexpr int TC = 32 * Elem<T>::VEC;
+  constexpr int G = FMT == AVERIS_MXFP4 ? 32 : 16;
+  constexpr int EPU = 64 / SZ, EPC = 16 / SZ;  // elements per unit, per chunk
+  const int c = threadIdx.x;
+  if (c >= TC) return;
+  const int64_t col = c0 + c;
+  const uint8_t* p = tile + ((c % EPU) / EPC * kQPlane + c / EPU) * 16 + (c % EPC) * SZ;  // + 128 bytes a row
+  const float m_c = means[4 * mean_slot<EPU>(c) + (c & 3)];
+  float v[32];
+#pragma unroll
+  for (int rr = 0; rr < 32; ++rr) {
+    const float xv = Elem<T>::load1(reinterpret_cast<const T*>(p + rr * 128));
+    v[rr] = (FULL || r0 + rr < a.rows) ? __fsub_rn(xv, m_c) : 0.0f;
+  }
+  if (H16) { h16_inreg(v); h16_inreg(v + 16); }
+  uint32_t codes[4];
+  uint32_t sb = 0;
+#pragma unroll
+  for (int b = 0; b < 32 / G; ++b) {
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < G; ++j) m = fmaxf(m, fabsf(v[b * G + j]));
+    if (AMAX_ONLY) {
+      if (col < a.cols) amax_acc = fmaxf(amax_acc, m);
+      continue;
+    }
+    const BlockQ q = block_params<FMT>(m, sd_col);
+    block_codes<FMT>(v + b * G, G, q, codes + b * (G / 8));
+    sb |= q.sbyte << (8 * b);
+  }
+  if (AMAX_ONLY) return;
+  if (col < a.cols && r0 < a.col_kpad) {
+    *reinterpret_cast<uint4*>(a.col_codes + col * (a.col_kpad / 2) + r0 / 2) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+    uint8_t* sd = a.col_scales + scale_offset(col, r0 / G, a.col_kpad, G);
+    if (G == 16) *reinterpret_cast<uint16_t*>(sd) = (uint16_t)sb;
+    else *sd = (uint8_t)sb;
+  }
+}
+
+template <typename T, int FMT, bool H16, bool AMAX_ONLY>
+__global__ __launch_bounds__(kThreads, 4) void k_quant(QuantArgs ain) {
+  constexpr int SZ = (int)sizeof(T);
+  constexpr int TC = 32 * Elem<T>::VEC;
+  constexpr int EPU = 64 / SZ, EPC = 16 / SZ;  // elements per unit, per chunk
+  constexpr int G = FMT == AVERIS_MXFP4 ? 32 : 16;
+  static_assert(TC * SZ == 512, "tile rows are 512 bytes");
+  __shared__ __align__(16) uint8_t s_tile[kQBufBytes];
+  __shared__ __align__(16) float s_mean[256];
+  __shared__ float s_red[2][8];
 
   QuantArgs a = ain;  // this workgroup's view (grouped launches retarget it to one group)
   const int tile = xcd_remap(blockIdx.x, (int)gridDim.x);
@@ -387,9 +575,9 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs ain) {
   if (ain.offsets) {
     const int tcs = ain.tiles_c, cov = ain.cover_kpad;
     const GroupPos gp = group_scan(ain.offsets, ain.E, tile, true,
-                                   [tcs, cov](int64_t len) { return quant_row_tiles(len, cov) * tcs; });
+                                   [tcs, cov](int64_t len) { return quant_row_tiles<kQRows>(len, cov) * tcs; });
     if (gp.e < 0) return;
-    const int64_t trs = quant_row_tiles(gp.len, cov);
+    const int64_t trs = quant_row_tiles<kQRows>(gp.len, cov);
     tr = (int)(gp.local % trs); tc = (int)(gp.local / trs);
     const int e = gp.e;
     a.x = reinterpret_cast<const T*>(ain.x) + gp.off * ain.ldx;
@@ -415,152 +603,49 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs ain) {
   } else {
     tr = tile % ain.tiles_r; tc = tile / ain.tiles_r;
   }
-  const int64_t r0 = (int64_t)tr * kTileRows, c0 = (int64_t)tc * TC;
-  const int lane_c = threadIdx.x & 31, phase = threadIdx.x >> 5;
-  const int lane = threadIdx.x & 63;
+  const int64_t r0 = (int64_t)tr * kQRows, c0 = (int64_t)tc * TC;
+  const int t = threadIdx.x;
   const T* x = reinterpret_cast<const T*>(a.x);
 
-  // tensor decode scales (NVFP4): residual amax, or the rotated amax per layout
+  // ---- loads first (rows >= a.rows and columns >= a.cols read as 0), staged in LDS before any
+  // store is issued, so no later step waits for this workgroup's stores.  Load k of thread t
+  // is 16-byte chunk q = 256 k + t of the tile (row q / 32, chunk q % 32 of the row). ----
+  uint4 w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int q = k * kThreads + t;
+    const int64_t row = r0 + (q >> 5), col = c0 + (int64_t)(q & 31) * EPC;
+    w[k] = (row < a.rows && col < a.cols) ? *reinterpret_cast<const uint4*>(x + row * a.ldx + col) : make_uint4(0, 0, 0, 0);
+  }
+  float4 m4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (t < TC / 4 && a.mean && c0 + 4 * t < a.cols) m4 = *reinterpret_cast<const float4*>(a.mean + c0 + 4 * t);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int q = k * kThreads + t, ch = q & 31;
+    *reinterpret_cast<uint4*>(s_tile + ((ch & 3) * kQPlane + (q >> 5) * 8 + (ch >> 2)) * 16) = w[k];
+  }
+  if (t < TC / 4) *reinterpret_cast<float4*>(s_mean + 4 * mean_slot<EPU>(4 * t)) = m4;
+
   float sd_row = 0.0f, sd_col = 0.0f;
   if (FMT == AVERIS_NVFP4 && !AMAX_ONLY) {
-    float ar, ac;
-    if (H16) {
-      ar = __uint_as_float(a.amax_slots[1]);
-      ac = __uint_as_float(a.amax_slots[2]);
-    } else {
-      float m = 0.0f;
-      for (int i = lane; i < a.n_part; i += 64) m = fmaxf(m, a.ramax_part[i]);
-#pragma unroll
-      for (int s = 32; s >= 1; s >>= 1) m = wave_xor_max(m, s);
-      ar = ac = m;
-    }
-    sd_row = nvfp4_tensor_scale(ar);
-    sd_col = nvfp4_tensor_scale(ac);
-    if (tr == 0 && tc == 0 && threadIdx.x == 0) {
+    nvfp4_scales<H16>(a, sd_row, sd_col);
+    if (tr == 0 && tc == 0 && t == 0) {
       if (a.row_ts) a.row_ts[0] = sd_row;
       if (a.col_ts) a.col_ts[0] = sd_col;
     }
   }
-  if (!AMAX_ONLY) quant_extras<FMT, H16, TC>(a, tr, tc, r0, c0);
+  if (!AMAX_ONLY) quant_extras<FMT, H16, TC, kQRows>(a, tr, tc, r0, c0);
+  lds_barrier();
 
-  // ---- load the tile (rows >= a.rows read as 0) ----
-  const int64_t cc = c0 + lane_c * VEC;
-  const bool col_ok = cc < a.cols;
-  uint4 w[kTileRows / 8];
-#pragma unroll
-  for (int i = 0; i < kTileRows / 8; ++i) {
-    const int64_t r = r0 + phase + 8 * i;
-    w[i] = (col_ok && r < a.rows) ? *reinterpret_cast<const uint4*>(x + r * a.ldx + cc) : make_uint4(0, 0, 0, 0);
+  float amax_row = 0.0f, amax_col = 0.0f;
+  if (r0 + kQRows <= a.rows) {
+    if (a.row_codes || AMAX_ONLY) tile_rows<T, FMT, H16, AMAX_ONLY, true>(a, r0, c0, s_tile, s_mean, sd_row, amax_row);
+    if (a.col_codes || AMAX_ONLY) tile_cols<T, FMT, H16, AMAX_ONLY, true>(a, r0, c0, s_tile, s_mean, sd_col, amax_col);
+  } else {
+    if (a.row_codes || AMAX_ONLY) tile_rows<T, FMT, H16, AMAX_ONLY, false>(a, r0, c0, s_tile, s_mean, sd_row, amax_row);
+    if (a.col_codes || AMAX_ONLY) tile_cols<T, FMT, H16, AMAX_ONLY, false>(a, r0, c0, s_tile, s_mean, sd_col, amax_col);
   }
-  float mu[VEC];
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) mu[j] = (a.mean && col_ok) ? a.mean[cc + j] : 0.0f;
-
-  float amax_row_acc = 0.0f, amax_col_acc = 0.0f;
-
-  // ---- row layout (K = cols) ----
-  if (a.row_codes || AMAX_ONLY) {
-#pragma unroll
-    for (int i = 0; i < kTileRows / 8; ++i) {
-      const int64_t r = r0 + phase + 8 * i;
-      float v[VEC];
-      Elem<T>::unpack(w[i], v);
-      const bool live = r < a.rows;  // rows past the data are zero residuals
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) v[j] = live ? __fsub_rn(v[j], mu[j]) : 0.0f;
-      if (H16) h16_lanes<VEC>(v, lane);
-      float m = 0.0f;
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) m = fmaxf(m, fabsf(v[j]));
-#pragma unroll
-      for (int s = 1; s < LPB; s <<= 1) m = wave_xor_max(m, s);
-      if (AMAX_ONLY) {
-        if (r < a.rows && col_ok) amax_row_acc = fmaxf(amax_row_acc, m);
-        continue;
-      }
-      const BlockQ q = block_params<FMT>(m, sd_row);
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) v[j] = __fmul_rn(v[j], q.mul);
-      if (r < a.rows_out && col_ok) {
-        uint8_t* dst = a.row_codes + r * (a.row_kpad / 2) + cc / 2;
-        if (VEC == 8) *reinterpret_cast<uint32_t*>(dst) = q.dead ? 0u : pack8_fp4(v);
-        else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(q.dead ? 0u : pack4_fp4(v));
-        if ((lane_c % LPB) == 0) a.row_scales[scale_offset(r, cc / G, a.row_kpad, G)] = (uint8_t)q.sbyte;
-      }
-    }
-  }
-
-  // ---- column layout (K = rows) through LDS ----
-  if (a.col_codes || AMAX_ONLY) {
-#pragma unroll
-    for (int i = 0; i < kTileRows / 8; ++i)
-      *reinterpret_cast<uint4*>(&s_tile[phase + 8 * i][lane_c * VEC]) = w[i];
-    __syncthreads();
-    constexpr int HALVES = kTileRows / 32;       // 32-row groups per tile
-    constexpr int ITEMS = TC * HALVES / kThreads; // items per thread
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int item = threadIdx.x + it * kThreads;
-      const int c = item % TC, half = item / TC;
-      const int64_t col = c0 + c;
-      const float m_c = (a.mean && col < a.cols) ? a.mean[col] : 0.0f;
-      float v[32];
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const int rr = half * 32 + j;
-        const float xv = Elem<T>::load1(&s_tile[rr][c]);
-        v[j] = (r0 + rr < a.rows) ? __fsub_rn(xv, m_c) : 0.0f;
-      }
-      if (H16) { h16_inreg(v); h16_inreg(v + 16); }
-#pragma unroll
-      for (int b = 0; b < 32 / G; ++b) {
-        float m = 0.0f;
-#pragma unroll
-        for (int j = 0; j < G; ++j) m = fmaxf(m, fabsf(v[b * G + j]));
-        if (AMAX_ONLY) {
-          if (col < a.cols) amax_col_acc = fmaxf(amax_col_acc, m);
-          continue;
-        }
-        const BlockQ q = block_params<FMT>(m, sd_col);
-#pragma unroll
-        for (int j = 0; j < G; ++j) v[b * G + j] = __fmul_rn(v[b * G + j], q.mul);
-        const int64_t k0 = r0 + half * 32 + b * G;  // first token of this block
-        if (col < a.cols && k0 < a.col_kpad) {
-          uint8_t* dst = a.col_codes + col * (a.col_kpad / 2) + k0 / 2;
-          if (G == 32) {
-            uint4 o;
-            o.x = q.dead ? 0u : pack8_fp4(v + b * G);
-            o.y = q.dead ? 0u : pack8_fp4(v + b * G + 8);
-            o.z = q.dead ? 0u : pack8_fp4(v + b * G + 16);
-            o.w = q.dead ? 0u : pack8_fp4(v + b * G + 24);
-            *reinterpret_cast<uint4*>(dst) = o;
-          } else {
-            uint2 o;
-            o.x = q.dead ? 0u : pack8_fp4(v + b * G);
-            o.y = q.dead ? 0u : pack8_fp4(v + b * G + 8);
-            *reinterpret_cast<uint2*>(dst) = o;
-          }
-          a.col_scales[scale_offset(col, k0 / G, a.col_kpad, G)] = (uint8_t)q.sbyte;
-        }
-      }
-    }
-  }
-
-  if (AMAX_ONLY) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      amax_row_acc = wave_xor_max(amax_row_acc, m);
-      amax_col_acc = wave_xor_max(amax_col_acc, m);
-    }
-    if (lane == 0) { s_red[0][threadIdx.x >> 6] = amax_row_acc; s_red[1][threadIdx.x >> 6] = amax_col_acc; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float u = s_red[0][0], v = s_red[1][0];
-      for (int i = 1; i < kThreads / 64; ++i) { u = fmaxf(u, s_red[0][i]); v = fmaxf(v, s_red[1][i]); }
-      atomicMax(a.amax_out + 1, __float_as_uint(u));
-      atomicMax(a.amax_out + 2, __float_as_uint(v));
-    }
-  }
+  if (AMAX_ONLY) amax_commit(a, amax_row, amax_col, s_red, kThreads / 64);
 }
 
 __global__ void k_fill_f32(float* p, int n, float v) {
@@ -629,13 +714,13 @@ static hipError_t launch_quant_t(const SplitQuantPlan& p, const SqLayout& L) {
   if (grouped) {
     a.offsets = p.d_offsets; a.E = (int)p.E;
     int64_t tr = 0;
-    for (int64_t e = 0; e < p.E; ++e) tr += quant_row_tiles(p.h_offsets[e + 1] - p.h_offsets[e], a.cover_kpad);
+    for (int64_t e = 0; e < p.E; ++e) tr += quant_row_tiles<kQRows>(p.h_offsets[e + 1] - p.h_offsets[e], a.cover_kpad);
     a.tiles_r = (int)tr;
     ntiles = tr * a.tiles_c;
   } else {
     // column layout covers the padding rows too (they are zero residuals); at least one row tile
     // so that the tensor scales, the quantized mean and the padding are written for rows == 0
-    a.tiles_r = (int)quant_row_tiles(p.rows, a.cover_kpad);
+    a.tiles_r = (int)quant_row_tiles<kQRows>(p.rows, a.cover_kpad);
     ntiles = (int64_t)a.tiles_r * a.tiles_c;
   }
   if (ntiles == 0) {  // no columns or no groups: still define the tensor scales (0)

@@ -111,3 +111,32 @@ def test_deterministic():
     assert torch.equal(a["mean"], b["mean"])
     for k in ("row", "col", "mean_q"):
         assert torch.equal(a[k].codes, b[k].codes) and torch.equal(a[k].scales, b[k].scales)
+
+
+@pytest.mark.parametrize("fmt,fname,hadamard", [(av.MXFP4, "mxfp4", False), (av.NVFP4, "nvfp4", False),
+                                                (av.NVFP4, "nvfp4", True)])
+def test_many_tiles_per_workgroup(fmt, fname, hadamard):
+    # 16001 rows x 1152 columns (4.5 column tiles of 256 bf16): about 2500 tiles of 32 rows, more
+    # than four per workgroup of the persistent launch, so the LDS ring wraps; ragged last rows
+    lin = workloads.up_proj_like(31, 16001, 1152, 128)
+    run_case(lin.x, "bf16", fmt, True, hadamard, tag=f"many-{fname}-{hadamard}")
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_strided_rows(fmt, fname, dtype):
+    # x is a column slice of a wider matrix: row stride 640 elements, 384 columns used
+    dev = device()
+    lin = workloads.up_proj_like(32, 777, 640, 128)
+    wide = workloads.to_torch(lin.x, dtype, dev)
+    x = wide[:, :384]
+    print(f"case strided-{fname}-{dtype} shape={tuple(x.shape)} ldx={x.stride(0)}", flush=True)
+    g = av.split_quant(x, fmt, split=True)
+    torch.cuda.synchronize()
+    x_np = lin.x[:, :384]
+    mu = g["mean"].cpu().numpy()
+    assert mean_ok(mu, x_np.astype(np.float64)), "mean"
+    o = O.split_quant(np.ascontiguousarray(x_np), fmt, split=True, mean=mu)
+    assert_q_equal(g["row"], o["row"], "row layout")
+    assert_q_equal(g["col"], o["col"], "column layout")
+    assert_q_equal(g["mean_q"], o["mean"], "quantized mean")
