@@ -292,82 +292,103 @@ __device__ __forceinline__ void pipe_step(T& t, int step, int nsteps, int kb_byt
 
 __device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14)); }
 
-// out = alpha * acc (+ bias[col]) (+ r1 * u[row] * v[col]) for CW consecutive columns, each
-// step rounded once in fp32.
-template <int CW>
-__device__ __forceinline__ void finish_cols(const GemmArgs& g, float* v, int64_t row, int64_t col, float alpha) {
+// Epilogue of one wave, straight from the accumulators: acc[i][j][4q + r] holds
+// C[row i*32 + lane%32][col j*32 + 8q + 4h + r], h = lane / 32.
+//   fp32 output (and split-K partials): a lane's 4 consecutive columns are one 16-byte store.
+//   bf16 output: v_permlane32_swap exchanges quad q+1 of the low half with quad q of the high
+//   half, after which lane (fr, h) holds the 8 consecutive columns j*32 + 16p + 8h of its row
+//   (p = q / 2): one 16-byte store of 8 bf16.
+// Per-column terms (bias, v) and per-row terms (u) are loaded once per tile, in one batch,
+// before the first store.
+//   out = alpha * acc (+ bias[col]) (+ r1 * u[row] * v[col]) (+ C when accumulating), each step
+//   rounded once in fp32; split-K partials get alpha * acc only.
+template <int FMT, int TM, int TN>
+__device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&acc)[TM][TN], int64_t rbase,
+                                              int64_t cbase, int split, int lane) {
+  const int fr = lane & 31, h = lane >> 5;
+  const bool bf = g.c_bf16 && g.splits == 1;
+  const bool terms = g.splits == 1;
+  const bool hb = terms && g.bias, hr = terms && g.r1u;
+  // this lane's columns: bf16 -> j*32 + 16p + 8h + (0..7); fp32 -> j*32 + 8q + 4h + (0..3)
+  float bias[TN][16], vv[TN][16], uu[TM];
 #pragma unroll
-  for (int e = 0; e < CW; ++e) v[e] = __fmul_rn(v[e], alpha);
-  if (g.bias) {
+  for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int e = 0; e < CW; e += 4) {
-      const float4 b = *reinterpret_cast<const float4*>(g.bias + col + e);
-      v[e] = __fadd_rn(v[e], b.x); v[e + 1] = __fadd_rn(v[e + 1], b.y);
-      v[e + 2] = __fadd_rn(v[e + 2], b.z); v[e + 3] = __fadd_rn(v[e + 3], b.w);
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const int off = bf ? j * 32 + 16 * (c4 >> 1) + 8 * h + 4 * (c4 & 1) : j * 32 + 8 * c4 + 4 * h;
+      const int64_t col = cbase + off;
+      const bool ok = col < g.N;
+      const float4 b = (hb && ok) ? *reinterpret_cast<const float4*>(g.bias + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 r = (hr && ok) ? *reinterpret_cast<const float4*>(g.r1v + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+      bias[j][4 * c4] = b.x; bias[j][4 * c4 + 1] = b.y; bias[j][4 * c4 + 2] = b.z; bias[j][4 * c4 + 3] = b.w;
+      vv[j][4 * c4] = r.x; vv[j][4 * c4 + 1] = r.y; vv[j][4 * c4 + 2] = r.z; vv[j][4 * c4 + 3] = r.w;
     }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t row = rbase + i * 32 + fr;
+    uu[i] = (hr && row < g.M) ? __fmul_rn(g.r1, g.r1u[row]) : 0.0f;
   }
-  if (g.r1u) {
-    const float ur = __fmul_rn(g.r1, g.r1u[row]);
+  float alpha = 1.0f;
+  if (FMT == AVERIS_NVFP4) alpha = __fmul_rn(g.a_ts[0], g.b_ts[0]);
 #pragma unroll
-    for (int e = 0; e < CW; e += 4) {
-      const float4 b = *reinterpret_cast<const float4*>(g.r1v + col + e);
-      v[e] = __fadd_rn(v[e], __fmul_rn(ur, b.x)); v[e + 1] = __fadd_rn(v[e + 1], __fmul_rn(ur, b.y));
-      v[e + 2] = __fadd_rn(v[e + 2], __fmul_rn(ur, b.z)); v[e + 3] = __fadd_rn(v[e + 3], __fmul_rn(ur, b.w));
-    }
-  }
-}
-
-// Copy one staged 32 x W fp32 slab (row stride LD floats) to C: each lane moves 16 output
-// bytes of one row per pass (8 bf16 or 4 fp32 columns), so each store instruction writes
-// whole row segments.  Split-K partials get alpha * acc only.
-template <int W, int LD>
-__device__ __forceinline__ void store_slab(const GemmArgs& g, const float* epi, int64_t rbase, int64_t cbase, float alpha,
-                                           int split, int lane) {
-  if (g.splits > 1) {
-    constexpr int LPR = W / 4, NQ = 32 * LPR;
-#pragma unroll 1
-    for (int q = lane; q < NQ; q += 64) {
-      const int rr = q / LPR, ch = q % LPR;
-      const int64_t row = rbase + rr, col = cbase + ch * 4;
-      if (row < g.M && col < g.N) {
-        float4 v = *reinterpret_cast<const float4*>(epi + rr * LD + ch * 4);
-        v.x = __fmul_rn(v.x, alpha); v.y = __fmul_rn(v.y, alpha); v.z = __fmul_rn(v.z, alpha); v.w = __fmul_rn(v.w, alpha);
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(g.c) + (int64_t)split * g.M * g.N + row * g.N + col) = v;
+  for (int i = 0; i < TM; ++i) {
+    const int64_t row = rbase + i * 32 + fr;
+    const bool row_ok = row < g.M;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      float x[16];
+      if (bf) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][j][8 * p + r]),
+                                                             __float_as_uint(acc[i][j][8 * p + 4 + r]), false, false);
+            x[8 * p + r] = __uint_as_float(sw[0]);
+            x[8 * p + 4 + r] = __uint_as_float(sw[1]);
+          }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = acc[i][j][e];
       }
-    }
-  } else if (g.c_bf16) {
-    constexpr int LPR = W / 8, NQ = 32 * LPR;
-#pragma unroll 1
-    for (int q = lane; q < NQ; q += 64) {
-      const int rr = q / LPR, ch = q % LPR;
-      const int64_t row = rbase + rr, col = cbase + ch * 8;
-      if (row < g.M && col < g.N) {
-        float v[8];
-        *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(epi + rr * LD + ch * 8);
-        *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(epi + rr * LD + ch * 8 + 4);
-        finish_cols<8>(g, v, row, col, alpha);
-        uint4 o;
-        o.x = pack_bf16x2(v[0], v[1]); o.y = pack_bf16x2(v[2], v[3]);
-        o.z = pack_bf16x2(v[4], v[5]); o.w = pack_bf16x2(v[6], v[7]);
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.c) + row * g.ldc + col) = o;
+      if (FMT == AVERIS_NVFP4) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = __fmul_rn(x[e], alpha);
       }
-    }
-  } else {
-    constexpr int LPR = W / 4, NQ = 32 * LPR;
-#pragma unroll 1
-    for (int q = lane; q < NQ; q += 64) {
-      const int rr = q / LPR, ch = q % LPR;
-      const int64_t row = rbase + rr, col = cbase + ch * 4;
-      if (row < g.M && col < g.N) {
-        float v[4];
-        *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(epi + rr * LD + ch * 4);
-        finish_cols<4>(g, v, row, col, alpha);
-        float* dst = reinterpret_cast<float*>(g.c) + row * g.ldc + col;
-        if (g.accumulate) {
-          const float4 o = *reinterpret_cast<const float4*>(dst);
-          v[0] = __fadd_rn(o.x, v[0]); v[1] = __fadd_rn(o.y, v[1]); v[2] = __fadd_rn(o.z, v[2]); v[3] = __fadd_rn(o.w, v[3]);
+      if (hb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = __fadd_rn(x[e], bias[j][e]);
+      }
+      if (hr) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = __fadd_rn(x[e], __fmul_rn(uu[i], vv[j][e]));
+      }
+      if (!row_ok) continue;
+      if (bf) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int64_t col = cbase + j * 32 + 16 * p + 8 * h;
+          if (col < g.N) {
+            uint4 o;
+            o.x = pack_bf16x2(x[8 * p], x[8 * p + 1]); o.y = pack_bf16x2(x[8 * p + 2], x[8 * p + 3]);
+            o.z = pack_bf16x2(x[8 * p + 4], x[8 * p + 5]); o.w = pack_bf16x2(x[8 * p + 6], x[8 * p + 7]);
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.c) + row * g.ldc + col) = o;
+          }
         }
-        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = cbase + j * 32 + 8 * q + 4 * h;
+          if (col >= g.N) continue;
+          float* dst = g.splits > 1 ? reinterpret_cast<float*>(g.c) + (int64_t)split * g.M * g.N + row * g.N + col
+                                    : reinterpret_cast<float*>(g.c) + row * g.ldc + col;
+          float4 o = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+          if (g.splits == 1 && g.accumulate) {
+            const float4 c = *reinterpret_cast<const float4*>(dst);
+            o.x = __fadd_rn(c.x, o.x); o.y = __fadd_rn(c.y, o.y); o.z = __fadd_rn(c.z, o.z); o.w = __fadd_rn(c.w, o.w);
+          }
+          *reinterpret_cast<float4*>(dst) = o;
+        }
       }
     }
   }
@@ -452,25 +473,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs gin) {
   wait_vm<0>();                 // no load may still be writing LDS
   __builtin_amdgcn_s_barrier();  // every wave is done reading the stages
 
-  // ---- epilogue: per 32-row slab, stage the wave's fp32 tile in LDS, then 16-byte stores ----
-  // acc[i][j][4q + r] is C[row i*32 + lane%32][col j*32 + 8q + 4(lane/32) + r] of the wave tile.
-  const int lane = threadIdx.x & 63, fr = lane & 31, fk = lane >> 5;
-  const int wave = t.wave, wm = t.wm, wn = t.wn;
-  float* epi = reinterpret_cast<float*>((wave < (C::NW + 1) / 2 ? st0 : st1) + (wave % ((C::NW + 1) / 2)) * C::EPI_WAVE);
-  float alpha = 1.0f;
-  if (FMT == AVERIS_NVFP4) alpha = __fmul_rn(g.a_ts[0], g.b_ts[0]);
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4*>(epi + fr * C::EPI_LD + j * 32 + q * 8 + fk * 4) =
-            make_float4(t.acc[i][j][4 * q], t.acc[i][j][4 * q + 1], t.acc[i][j][4 * q + 2], t.acc[i][j][4 * q + 3]);
-    lgkm_wait0();  // this wave's staging writes are done
-    store_slab<TN * 32, C::EPI_LD>(g, epi, m0 + wm * TM * 32 + i * 32, n0 + wn * TN * 32, alpha, split, lane);
-    lgkm_wait0();  // its reads are done before the next slab overwrites the staging area
-  }
+  // ---- epilogue ----
+  epilogue_regs<FMT, TM, TN>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, split, threadIdx.x & 63);
 }
 
 // Split-K reduce: C = (accumulate ? C : 0) + (sum_s P[s] in split order + bias[col]
