@@ -117,6 +117,29 @@ def main():
         r["overhead_pct"] = 100.0 * (r["averis_step_ms"] - r["vanilla_step_ms"]) / r["vanilla_step_ms"]
         results[name] = r
 
+    # Layer sweep (the overhead target's workload): the seven Qwen3-0.6B-shaped linears at
+    # l = 16384, one step = all seven linears' quantize + fwd/dX/dW, Averis vs vanilla.
+    sweep = {}
+    layers = workloads.sweep_device(3, 16384, dev)
+    sweep_flops = sum(6.0 * x_.shape[0] * x_.shape[1] * d_.shape[1] for _, x_, d_, _ in layers)
+    for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
+        r = {}
+        for split in (True, False):
+            sts = [LinearStep(x_, d_, w_, fmt, split=split) for _, x_, d_, w_ in layers]
+
+            def run_all():
+                for s_ in sts:
+                    s_.run()
+            tag = "averis" if split else "vanilla"
+            r[f"{tag}_step_ms"] = round(timed(run_all, max(3, args.steps // 4), max(1, args.warmup // 2)), 4)
+            del sts
+        r["overhead_pct"] = round(100.0 * (r["averis_step_ms"] - r["vanilla_step_ms"]) / r["vanilla_step_ms"], 2)
+        r["step_tflops"] = round(sweep_flops / (r["averis_step_ms"] * 1e-3) / 1e12, 1)
+        print(f"# sweep {name}: averis {r['averis_step_ms']*1e3:.0f} us, vanilla {r['vanilla_step_ms']*1e3:.0f} us, "
+              f"overhead {r['overhead_pct']:.1f} %", file=sys.stderr, flush=True)
+        sweep[name] = r
+    del layers
+
     # Dominant kernel: the MXFP4 GEMM tile kernel.  The vanilla forward and input-gradient GEMMs
     # are exactly one k_gemm launch each (2 l m n flops per launch).  A graph of REPS back-to-back
     # (forward, input-gradient) pairs is replayed after a cache-evicting read; HIP events on the
@@ -169,6 +192,9 @@ def main():
         "overhead_pct_vs_vanilla": round(mx["overhead_pct"], 2),
         "vanilla_ms_per_step": round(mx["vanilla_step_ms"], 5),
         "nvfp4": {k: round(v, 5) for k, v in results["nvfp4"].items()},
+        "layer_sweep": dict(workload="Qwen3-0.6B-shaped layer sweep: q, k, v, o, gate, up, down linears at "
+                                     "l=16384, fwd+dX+dW each, bf16 in", l=16384, linears=7,
+                            gflop=round(sweep_flops / 1e9, 1), **sweep),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

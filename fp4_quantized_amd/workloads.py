@@ -126,6 +126,38 @@ def sweep(seed=3, l=16384):
     return [up_proj_like([seed, j], l, m, n, name=nm) for j, (nm, m, n) in enumerate(SWEEP_LAYERS)]
 
 
+def sweep_device(seed=3, l=16384, device="cuda"):
+    """The seven sweep linears drawn directly on the device, for timing: the up_proj_like recipe
+    (X = bf16(1 mu^T + R), R ~ Student-t(4) as Z / sqrt(V / 4) with V ~ chi2(4); D = bf16(1 mu_D^T
+    + N(0, 1e-6)); W ~ N(0, 0.02^2)) from torch's generator seeded with `seed`.  The values are
+    not those of `sweep` (a different generator); parity tests use the numpy draws.
+    Returns [(name, x, d, w)] of bf16 tensors, x [l, m], d [l, n], w [m, n]."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = []
+    for name, m, n in SWEEP_LAYERS:
+        def normal(*shape):
+            return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
+
+        def mean_vec(k, rms, spikes):
+            g = normal(k)
+            mu = rms * g / torch.sqrt(torch.mean(g * g))
+            if spikes:
+                idx = torch.randperm(k, generator=gen, device=device)[:spikes]
+                mu[idx] *= 20.0
+            return mu
+
+        mu = mean_vec(m, 3.0 * 2.0 ** 0.5, _n_spikes(m))
+        v = sum(normal(l, m) ** 2 for _ in range(4))
+        x = (normal(l, m) / torch.sqrt(v / 4.0) + mu[None, :]).to(torch.bfloat16)
+        del v
+        d = (normal(l, n) * 1e-3 + mean_vec(n, 1e-3, 0)[None, :]).to(torch.bfloat16)
+        w = (normal(m, n) * 0.02).to(torch.bfloat16)
+        out.append((name, x, d, w))
+    return out
+
+
 @dataclass
 class MoE:
     """Expert-contiguous MoE FFN inputs.  offsets [E+1] over the routed rows; per expert e,
