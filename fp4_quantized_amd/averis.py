@@ -145,7 +145,9 @@ def _dtype_code(t):
 
 
 def _workspace(nbytes, device):
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    # zero-filled once: split_quant's workspace carries counters that must start at zero (each
+    # call leaves them at zero again)
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 def split_quant_outputs(rows, cols, fmt, split=True, hadamard=False, row=True, col=True, device="cuda"):

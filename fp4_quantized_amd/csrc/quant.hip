@@ -9,9 +9,9 @@
 // in registers between the load of X and the store of its FP4 codes.
 //
 // Pass structure (X is read twice; the second read usually hits the 256 MB Infinity Cache):
-//   k_colstats  per-slab (128 rows) column sums: fp32 over 8 rows, fp64 beyond; NVFP4 also
-//               column min and max
-//   k_finalize  fixed-order reduction of the slabs -> mu (fp32); per-workgroup maxima of the
+//   k_colstats  per (512-row slab, 64-column strip) column sums: fp32 over 8 rows, fp64 beyond;
+//               NVFP4 also column min and max.  The last workgroup of each strip reduces the
+//               strip's slabs in fixed order -> mu (fp32), and the strip's maxima of the
 //               residual (exact from min / max: fl(x - mu) is monotone in x) and of the mean
 //   k_quant     re-read a 32-row tile into LDS, subtract, rotate, block amax, scale, E2M1,
 //               and emit both layouts: K = features (row layout) one 64-byte unit per thread,
@@ -25,7 +25,6 @@
 namespace av {
 
 constexpr int kThreads = 256;
-constexpr int kStatRows = 128;  // rows per k_colstats workgroup: 16 per thread, loaded in one batch
 
 // ------------------------------------------------------------------------------------------
 // 16-point Hadamard butterflies (Sylvester order, stages h = 1, 2, 4, 8), then x 0.25.
@@ -76,169 +75,215 @@ __device__ inline void h16_lanes(float* v, int lane) {
 }
 
 // ------------------------------------------------------------------------------------------
-// k_colstats: grid (ceil(cols / TC), nslab); TC = 32 lanes * VEC columns.  Thread t covers VEC
-// columns at (t % 32) * VEC and rows slab0 + t / 32 + 8 i, i < 16, all loaded before any use.
-// Column sums: fp32 over each group of 8 rows, fp64 across groups and threads (fixed order).
-// MINMAX (NVFP4 tensor scale): column min and max as well.
+// k_colstats: column statistics and, in the last workgroup of each column strip, the mean.
+// Grid (n_strips, nslab): workgroup (s, b) covers columns [64 s, 64 s + 64) of the rows of
+// slab b (kCsRows rows; grouped launches number the slabs group after group, at least one per
+// group so empty groups still get their mean of 0).  Thread t holds VEC columns (t % LPR) * VEC
+// of rows t / LPR + RPB k, loaded in batches of 16 before use.  Column sums: fp32 over each
+// group of 8 rows, fp64 across groups and threads (fixed order); MINMAX (NVFP4): column min
+// and max too.  The partials go to the workspace; the workgroup then counts its arrival on its
+// strip's counter (device-scope fence + atomic).  The last one to arrive finalizes the strip:
+// fixed-order fp64 reduction of the strip's slabs -> mu (fp32; SPLIT without MEAN_GIVEN), the
+// strip's max |residual| (MINMAX: exact from the column min / max, since fl(x - mu) is
+// monotone in x) and max |(rotated) mean| as per-strip partials, and resets the counter to 0.
+// The counters must be zero before the first call on a workspace and are zero after every call.
+// mode bit 0 = SPLIT, bit 1 = MEAN_GIVEN.
 // ------------------------------------------------------------------------------------------
+// 64-column strips with 512-row slabs measured fastest on the sweep shapes (256-column strips
+// read longer row segments but leave the finalizing workgroup 4x the slabs to reduce).
+constexpr int kCsRows = 512;            // rows per column-statistics workgroup
+constexpr int kCsCols = 64;             // columns per column-statistics workgroup (one strip)
+constexpr int kCsWaves = kCsCols / 64;  // finalize: one wave per 64 columns of the strip
+
+struct ColArgs {
+  const void* x; int64_t rows, cols, ldx;
+  double* psum; float* pmin; float* pmax;  // [nslab][cols]
+  uint32_t* slots; int n_slots;            // amax slots, zeroed here for later kernels
+  uint32_t* counters;                      // [groups][n_strips]
+  float* mean;                             // [groups][cols]
+  float* ramax_part; float* mamax_part;    // [groups][n_strips]
+  int n_strips, mode, h16;
+  const int64_t* offsets; int E;
+};
+
+__device__ __host__ inline int64_t cs_slabs(int64_t len) {
+  const int64_t n = ceil_div(len, kCsRows);
+  return n > 0 ? n : 1;
+}
+
 template <typename T, bool MINMAX>
-__global__ __launch_bounds__(kThreads) void k_colstats(const T* __restrict__ x, int64_t rows, int64_t cols,
-                                                       int64_t ldx, double* __restrict__ psum,
-                                                       float* __restrict__ pmin, float* __restrict__ pmax,
-                                                       uint32_t* __restrict__ slots, int n_slots,
-                                                       const int64_t* __restrict__ offsets, int E) {
+__global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
   constexpr int VEC = Elem<T>::VEC;
-  constexpr int TC = 32 * VEC;
-  constexpr int PER = kStatRows / 8;
-  __shared__ double s_sum[8][TC];
-  __shared__ float s_min[MINMAX ? 8 : 1][TC];
-  __shared__ float s_max[MINMAX ? 8 : 1][TC];
+  constexpr int LPR = kCsCols / VEC;   // lanes per row
+  constexpr int RPB = kThreads / LPR;  // rows per pass of the workgroup
+  constexpr int PER = kCsRows / RPB;   // rows per thread (16 bf16, 32 fp32)
+  constexpr int BATCH = 16;            // loads in flight per thread
+  static_assert(PER % BATCH == 0 && BATCH % 8 == 0, "row batches");
+  __shared__ double s_sum[RPB][kCsCols];
+  __shared__ float s_min[MINMAX ? RPB : 1][kCsCols];
+  __shared__ float s_max[MINMAX ? RPB : 1][kCsCols];
+  __shared__ double f_sum[4][kCsCols];
+  __shared__ float f_min[4][kCsCols], f_max[4][kCsCols];
+  __shared__ int s_last;
 
-  // the rotated-amax slots are atomically maxed only by later kernels of the same call
+  const int t = threadIdx.x;
   if (blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = threadIdx.x; i < n_slots; i += kThreads) slots[i] = 0u;
+    for (int i = t; i < a.n_slots; i += kThreads) a.slots[i] = 0u;  // maxed by later kernels
 
-  // rows of this slab: [rb, re); grouped launches number the slabs group after group
-  int64_t rb = (int64_t)blockIdx.y * kStatRows, re = rows;
-  if (offsets) {
-    const GroupPos gp = group_scan(offsets, E, blockIdx.y, true, [](int64_t len) { return ceil_div(len, (int64_t)kStatRows); });
-    rb = gp.e < 0 ? 0 : gp.off + gp.local * kStatRows;
-    re = gp.e < 0 ? 0 : gp.off + gp.len;
+  // this workgroup's rows [rb, re) and its group's slabs [s0, s0 + nsl)
+  int64_t rb = (int64_t)blockIdx.y * kCsRows, re = a.rows, s0 = 0, glen = a.rows;
+  int e = 0, nsl = (int)cs_slabs(a.rows);
+  if (a.offsets) {
+    const GroupPos gp = group_scan(a.offsets, a.E, blockIdx.y, true, [](int64_t len) { return cs_slabs(len); });
+    if (gp.e < 0) return;
+    e = gp.e;
+    rb = gp.off + gp.local * kCsRows;
+    re = gp.off + gp.len;
+    s0 = gp.base;
+    nsl = (int)cs_slabs(gp.len);
+    glen = gp.len;
   }
-  if (re > rb + kStatRows) re = rb + kStatRows;
-  const int lane_c = threadIdx.x & 31, phase = threadIdx.x >> 5;
-  const int64_t c0 = (int64_t)blockIdx.x * TC + lane_c * VEC;
-  const int64_t r0 = rb + phase;
-  const bool col_ok = c0 < cols;
+  if (re > rb + kCsRows) re = rb + kCsRows;
+  const int strip = blockIdx.x;
+  const int64_t c0 = (int64_t)strip * kCsCols;
+  const int lc = t % LPR, rr = t / LPR;
+  const int64_t col = c0 + lc * VEC;
+  const bool col_ok = col < a.cols;
+  const T* x = reinterpret_cast<const T*>(a.x);
 
-  uint4 w[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int64_t r = r0 + 8 * i;
-    w[i] = (col_ok && r < re) ? *reinterpret_cast<const uint4*>(x + r * ldx + c0) : make_uint4(0, 0, 0, 0);
-  }
   double sum[VEC];
   float mn[VEC], mx[VEC];
 #pragma unroll
   for (int j = 0; j < VEC; ++j) { sum[j] = 0.0; mn[j] = __builtin_huge_valf(); mx[j] = -__builtin_huge_valf(); }
 #pragma unroll
-  for (int grp = 0; grp < PER / 8; ++grp) {
-    float part[VEC];
+  for (int b0 = 0; b0 < PER; b0 += BATCH) {
+    uint4 w[BATCH];
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) part[j] = 0.0f;
-#pragma unroll
-    for (int i = grp * 8; i < grp * 8 + 8; ++i) {
-      float v[VEC];
-      Elem<T>::unpack(w[i], v);  // rows past the end are zeros: harmless in the sum
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) part[j] = __fadd_rn(part[j], v[j]);
-      if (MINMAX && r0 + 8 * i < re) {
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) { mn[j] = fminf(mn[j], v[j]); mx[j] = fmaxf(mx[j], v[j]); }
-      }
+    for (int i = 0; i < BATCH; ++i) {
+      const int64_t r = rb + rr + (int64_t)RPB * (b0 + i);
+      w[i] = (col_ok && r < re) ? *reinterpret_cast<const uint4*>(x + r * a.ldx + col) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) sum[j] += (double)part[j];
+    for (int g8 = 0; g8 < BATCH; g8 += 8) {
+      float part[VEC];
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) part[j] = 0.0f;
+#pragma unroll
+      for (int i = g8; i < g8 + 8; ++i) {
+        float v[VEC];
+        Elem<T>::unpack(w[i], v);  // rows past the end are zeros: harmless in the sum
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) part[j] = __fadd_rn(part[j], v[j]);
+        if (MINMAX && rb + rr + (int64_t)RPB * (b0 + i) < re) {
+#pragma unroll
+          for (int j = 0; j < VEC; ++j) { mn[j] = fminf(mn[j], v[j]); mx[j] = fmaxf(mx[j], v[j]); }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) sum[j] += (double)part[j];
+    }
   }
 #pragma unroll
   for (int j = 0; j < VEC; ++j) {
-    s_sum[phase][lane_c * VEC + j] = sum[j];
-    if (MINMAX) { s_min[phase][lane_c * VEC + j] = mn[j]; s_max[phase][lane_c * VEC + j] = mx[j]; }
+    s_sum[rr][lc * VEC + j] = sum[j];
+    if (MINMAX) { s_min[rr][lc * VEC + j] = mn[j]; s_max[rr][lc * VEC + j] = mx[j]; }
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < TC; c += kThreads) {
-    const int64_t col = (int64_t)blockIdx.x * TC + c;
-    if (col >= cols) continue;
+  if (t < kCsCols && c0 + t < a.cols) {
     double sacc = 0.0;
-    float a = __builtin_huge_valf(), b = -__builtin_huge_valf();
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      sacc += s_sum[p][c];
-      if (MINMAX) { a = fminf(a, s_min[p][c]); b = fmaxf(b, s_max[p][c]); }
+    float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+    for (int q = 0; q < RPB; ++q) {
+      sacc += s_sum[q][t];
+      if (MINMAX) { lo = fminf(lo, s_min[q][t]); hi = fmaxf(hi, s_max[q][t]); }
     }
-    const int64_t o = (int64_t)blockIdx.y * cols + col;
-    psum[o] = sacc;
-    if (MINMAX) { pmin[o] = a; pmax[o] = b; }
+    // device-coherent stores (they reach the point of coherence of all XCDs; no L2 flush)
+    const int64_t o = (int64_t)blockIdx.y * a.cols + c0 + t;
+    __hip_atomic_store(a.psum + o, sacc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (MINMAX) {
+      __hip_atomic_store(a.pmin + o, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.pmax + o, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
-}
 
-// ------------------------------------------------------------------------------------------
-// k_finalize: grid ceil(cols / 64); wave q of 4 reduces slabs [q * per, (q + 1) * per) of 64
-// columns, the four partials are then added in wave order.  Writes mu (SPLIT without
-// MEAN_GIVEN) and, per workgroup, the max |residual| (MINMAX: exact from the column min / max,
-// since fl(x - mu) is monotone in x) and the max |mu| (after the 16x16 rotation when h16),
-// both as per-workgroup partials: no atomics, nothing to clear.  Grouped launches: group
-// blockIdx.y, its slabs and rows, mean row, and partials [group][workgroup].
-// mode bit 0 = SPLIT, bit 1 = MEAN_GIVEN.
-// ------------------------------------------------------------------------------------------
-template <bool MINMAX>
-__global__ __launch_bounds__(kThreads) void k_finalize(const double* __restrict__ psum, const float* __restrict__ pmin,
-                                                       const float* __restrict__ pmax, int nslab, int64_t rows,
-                                                       int64_t cols, int mode, int h16, float* __restrict__ mean,
-                                                       float* __restrict__ ramax_part, float* __restrict__ mamax_part,
-                                                       const int64_t* __restrict__ offsets, int E) {
-  __shared__ double s_sum[4][64];
-  __shared__ float s_min[4][64], s_max[4][64];
-  const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
-  const bool cin = c < cols;
-  int64_t s0 = 0;
-  if (offsets) {
-    const GroupPos gp = group_scan(offsets, E, blockIdx.y, false, [](int64_t len) { return ceil_div(len, (int64_t)kStatRows); });
-    s0 = gp.base;
-    nslab = (int)ceil_div(gp.len, (int64_t)kStatRows);
-    rows = gp.len;
-    mean += (int64_t)blockIdx.y * cols;
-  }
-  psum += s0 * cols; pmin += s0 * cols; pmax += s0 * cols;
-  const int per = (nslab + 3) / 4;
-  const int pb = q * per, pe = pb + per < nslab ? pb + per : nslab;
-  double s = 0.0;
-  float a = __builtin_huge_valf(), b = -__builtin_huge_valf();
-  if (cin && (mode & 1) && !(mode & 2)) {
+  // ---- arrival on the strip's counter; the last workgroup finalizes the strip ----
+  // the partial stores (wave 0) must be complete before thread 0 counts the arrival
+  asm volatile("" ::: "memory");
+  wait_vm<0>();
+  asm volatile("" ::: "memory");
+  __syncthreads();
+  uint32_t* counter = a.counters + (int64_t)e * a.n_strips + strip;
+  if (t == 0)
+    s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nsl - 1);
+  __syncthreads();
+  if (!s_last) return;
+
+  // kCsWaves == 1: the four waves split the slabs; otherwise wave q takes columns 64 q ..
+  constexpr int SPLITS = kCsWaves == 1 ? 4 : 1;
+  const int q = t >> 6, lane = t & 63;
+  const int cw = kCsWaves == 1 ? 0 : q;  // this wave's 64-column group of the strip
+  const int64_t c = c0 + 64 * cw + lane;
+  const bool cin = c < a.cols;
+  double* psum = a.psum + s0 * a.cols;
+  float* pmin = a.pmin + s0 * a.cols;
+  float* pmax = a.pmax + s0 * a.cols;
+  const int per = (nsl + SPLITS - 1) / SPLITS;
+  const int pb = SPLITS == 1 ? 0 : q * per, pe = SPLITS == 1 ? nsl : (pb + per < nsl ? pb + per : nsl);
+  double sacc = 0.0;
+  float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+  // device-coherent loads: the other workgroups' partials, whatever XCD wrote them
+  // (eight slabs per batch of loads, summed in slab order)
+  if (cin && (a.mode & 1) && !(a.mode & 2))
     for (int p0 = pb; p0 < pe; p0 += 8) {
-      double t[8];
+      double v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) t[u] = p0 + u < pe ? psum[(int64_t)(p0 + u) * cols + c] : 0.0;
+      for (int u = 0; u < 8; ++u)
+        v[u] = p0 + u < pe ? __hip_atomic_load(psum + (int64_t)(p0 + u) * a.cols + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += t[u];
+      for (int u = 0; u < 8; ++u) sacc += v[u];
     }
-  }
-  if (cin && MINMAX) {
+  if (cin && MINMAX)
     for (int p0 = pb; p0 < pe; p0 += 8) {
-      float lo[8], hi[8];
+      float l8[8], h8[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const bool ok = p0 + u < pe;
-        lo[u] = ok ? pmin[(int64_t)(p0 + u) * cols + c] : __builtin_huge_valf();
-        hi[u] = ok ? pmax[(int64_t)(p0 + u) * cols + c] : -__builtin_huge_valf();
+        const int64_t o = (int64_t)(p0 + u) * a.cols + c;
+        l8[u] = ok ? __hip_atomic_load(pmin + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : __builtin_huge_valf();
+        h8[u] = ok ? __hip_atomic_load(pmax + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -__builtin_huge_valf();
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) { a = fminf(a, lo[u]); b = fmaxf(b, hi[u]); }
+      for (int u = 0; u < 8; ++u) { lo = fminf(lo, l8[u]); hi = fmaxf(hi, h8[u]); }
     }
+  if (SPLITS == 4) {
+    f_sum[q][lane] = sacc; f_min[q][lane] = lo; f_max[q][lane] = hi;
   }
-  s_sum[q][lane] = s; s_min[q][lane] = a; s_max[q][lane] = b;
   __syncthreads();
-  if (q != 0) return;
-  const double S = ((s_sum[0][lane] + s_sum[1][lane]) + s_sum[2][lane]) + s_sum[3][lane];
-  a = fminf(fminf(s_min[0][lane], s_min[1][lane]), fminf(s_min[2][lane], s_min[3][lane]));
-  b = fmaxf(fmaxf(s_max[0][lane], s_max[1][lane]), fmaxf(s_max[2][lane], s_max[3][lane]));
-  float mu = 0.0f;
-  if (cin && (mode & 1)) {
-    if (mode & 2) mu = mean[c];
-    else { mu = rows > 0 ? (float)(S / (double)rows) : 0.0f; mean[c] = mu; }
-  }
-  float ra = 0.0f;
-  if (MINMAX && cin && rows > 0) ra = fmaxf(__fsub_rn(b, mu), __fsub_rn(mu, a));
-  // |mu| per column, rotated within 16-column blocks when the mean is quantized rotated
-  float mv[1] = {cin ? mu : 0.0f};
-  if (h16) h16_lanes<1>(mv, lane);
-  float ma = fabsf(mv[0]);
+  if (SPLITS == 1 || q == 0) {
+    const double S = SPLITS == 1 ? sacc : ((f_sum[0][lane] + f_sum[1][lane]) + f_sum[2][lane]) + f_sum[3][lane];
+    if (SPLITS == 4) {
+      lo = fminf(fminf(f_min[0][lane], f_min[1][lane]), fminf(f_min[2][lane], f_min[3][lane]));
+      hi = fmaxf(fmaxf(f_max[0][lane], f_max[1][lane]), fmaxf(f_max[2][lane], f_max[3][lane]));
+    }
+    float* mean = a.mean ? a.mean + (int64_t)e * a.cols : nullptr;
+    float mu = 0.0f;
+    if (cin && (a.mode & 1)) {
+      if (a.mode & 2) mu = mean[c];
+      else { mu = glen > 0 ? (float)(S / (double)glen) : 0.0f; mean[c] = mu; }
+    }
+    float ra = 0.0f;
+    if (MINMAX && cin && glen > 0) ra = fmaxf(__fsub_rn(hi, mu), __fsub_rn(mu, lo));
+    // |mu| per column, rotated within 16-column blocks when the mean is quantized rotated
+    float mv[1] = {cin ? mu : 0.0f};
+    if (a.h16) h16_lanes<1>(mv, lane);
+    float ma = fabsf(mv[0]);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) { ra = wave_xor_max(ra, m); ma = wave_xor_max(ma, m); }
-  if (lane == 0) {
-    const int64_t o = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-    ramax_part[o] = ra; mamax_part[o] = ma;
+    for (int m = 32; m >= 1; m >>= 1) { ra = wave_xor_max(ra, m); ma = wave_xor_max(ma, m); }
+    if (lane == 0) {
+      const int64_t o = ((int64_t)e * a.n_strips + strip) * kCsWaves + cw;  // per 64 columns
+      a.ramax_part[o] = ra; a.mamax_part[o] = ma;
+      if (cw == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
+    }
   }
 }
 
@@ -279,7 +324,7 @@ struct QuantArgs {
   const float* mean;           // nullptr: no subtraction
   const uint32_t* amax_slots;  // NVFP4 with rotation: [1] rotated row amax, [2] rotated col amax
   uint32_t* amax_out;          // AMAX_ONLY target (same buffer as amax_slots)
-  const float* ramax_part;     // NVFP4: per-workgroup max |residual| from k_finalize
+  const float* ramax_part;     // NVFP4: per-strip max |residual| from k_colstats
   const float* mamax_part;     // NVFP4: per-workgroup max |(rotated) mean|
   int n_part;
   uint8_t* mean_codes;         // quantized mean (nullptr: none)
@@ -388,7 +433,7 @@ __device__ __host__ inline int64_t quant_row_tiles(int64_t len, int cover_kpad) 
 }
 
 // NVFP4 tensor decode scales of one launch (or group): from the rotated amax slots (H16), else
-// from k_finalize's per-workgroup maxima of |residual|.  Every lane of the wave gets them.
+// from k_colstats' per-strip maxima of |residual|.  Every lane of the wave gets them.
 template <bool H16>
 __device__ __forceinline__ void nvfp4_scales(const QuantArgs& a, float& sd_row, float& sd_col) {
   float ar, ac;
@@ -656,26 +701,25 @@ __global__ void k_fill_f32(float* p, int n, float v) {
 // ------------------------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------------------------
-static int64_t slab_count(int64_t rows) {
-  const int64_t n = ceil_div(rows, kStatRows);
-  return n > 0 ? n : 1;  // one (empty) slab when rows == 0
-}
-
-// workspace: [0, hdr) amax slots (3 + 2 E uint32) | finalize partials (2 x E x n_part fp32) |
-// column statistics: psum [nslab][cols] fp64, pmin and pmax [nslab][cols] fp32
+// workspace: [0, hdr) amax slots (3 + 2 E uint32), then strip counters (E x n_part uint32,
+// zero between calls) | per-strip partial maxima (2 x E x n_part fp32) | column statistics:
+// psum [nslab][cols] fp64, pmin and pmax [nslab][cols] fp32
 struct SqLayout {
-  uint32_t* slots; int n_slots; float* ramax; float* mamax; double* psum; float* pmin; float* pmax;
-  int n_part; int64_t nslab;
+  uint32_t* slots; int n_slots; uint32_t* counters; float* ramax; float* mamax; double* psum; float* pmin;
+  float* pmax; int n_part; int64_t nslab;
 };
-static size_t sq_header(int64_t E) { return (size_t)round_up((3 + 2 * E) * 4, 256); }
+static int64_t n_strips(int64_t cols) { return ceil_div(cols, kCsCols); }
+static int64_t n_parts(int64_t cols) { return n_strips(cols) * kCsWaves; }  // per-64-column partial maxima
+static size_t sq_header(int64_t cols, int64_t E) { return (size_t)round_up((3 + 2 * E + E * n_strips(cols)) * 4, 256); }
 static SqLayout sq_layout(void* ws, int64_t nslab, int64_t cols, int64_t E) {
   SqLayout L;
   uint8_t* b = reinterpret_cast<uint8_t*>(ws);
-  L.n_part = (int)ceil_div(cols, 64);
+  L.n_part = (int)n_parts(cols);
   L.nslab = nslab;
-  const size_t h = sq_header(E), pb = (size_t)round_up(E * L.n_part * 4, 256);
+  const size_t h = sq_header(cols, E), pb = (size_t)round_up(E * L.n_part * 4, 256);
   L.slots = reinterpret_cast<uint32_t*>(b);
   L.n_slots = (int)(3 + 2 * E);
+  L.counters = L.slots + L.n_slots;
   L.ramax = reinterpret_cast<float*>(b + h);
   L.mamax = reinterpret_cast<float*>(b + h + pb);
   L.psum = reinterpret_cast<double*>(b + h + 2 * pb);
@@ -684,14 +728,14 @@ static SqLayout sq_layout(void* ws, int64_t nslab, int64_t cols, int64_t E) {
   return L;
 }
 static size_t sq_bytes(int64_t nslab, int64_t cols, int64_t E) {
-  const int64_t n_part = ceil_div(cols, 64);
-  return sq_header(E) + 2 * (size_t)round_up(E * n_part * 4, 256) + (size_t)nslab * cols * (8 + 4 + 4) + 256;
+  return sq_header(cols, E) + 2 * (size_t)round_up(E * n_parts(cols) * 4, 256) + (size_t)nslab * cols * (8 + 4 + 4) +
+         256;
 }
 
-size_t split_quant_ws_bytes(int64_t rows, int64_t cols) { return sq_bytes(slab_count(rows), cols, 1); }
-// grouped: at most ceil(rows / 128) + E slabs
+size_t split_quant_ws_bytes(int64_t rows, int64_t cols) { return sq_bytes(cs_slabs(rows), cols, 1); }
+// grouped: at most ceil(rows / kCsRows) + E slabs
 size_t split_quant_grouped_ws_bytes(int64_t rows, int64_t cols, int64_t E) {
-  return sq_bytes(ceil_div(rows, kStatRows) + E + 1, cols, E);
+  return sq_bytes(ceil_div(rows, kCsRows) + E + 1, cols, E);
 }
 
 template <typename T, int FMT, bool H16>
@@ -753,26 +797,27 @@ static hipError_t launch_quant_f(const SplitQuantPlan& p, const SqLayout& L) {
 
 template <typename T, bool MINMAX>
 static void launch_stats_t(const SplitQuantPlan& p, const SqLayout& L) {
-  constexpr int TC = 32 * Elem<T>::VEC;
   const bool grouped = p.E > 0;
-  const int64_t groups = grouped ? p.E : 1;
-  const dim3 grid((unsigned)ceil_div(p.cols, TC), (unsigned)L.nslab);
-  hipLaunchKernelGGL((k_colstats<T, MINMAX>), grid, dim3(kThreads), 0, p.stream, reinterpret_cast<const T*>(p.x), p.rows,
-                     p.cols, p.ldx, L.psum, L.pmin, L.pmax, L.slots, L.n_slots, grouped ? p.d_offsets : nullptr,
-                     (int)groups);
-  const int mode = (p.split ? 1 : 0) | (p.mean_given ? 2 : 0);
-  hipLaunchKernelGGL((k_finalize<MINMAX>), dim3((unsigned)L.n_part, (unsigned)groups), dim3(kThreads), 0, p.stream,
-                     L.psum, L.pmin, L.pmax, (int)L.nslab, p.rows, p.cols, mode, (p.split && p.h16) ? 1 : 0, p.mean,
-                     L.ramax, L.mamax, grouped ? p.d_offsets : nullptr, (int)groups);
+  ColArgs a{};
+  a.x = p.x; a.rows = p.rows; a.cols = p.cols; a.ldx = p.ldx;
+  a.psum = L.psum; a.pmin = L.pmin; a.pmax = L.pmax;
+  a.slots = L.slots; a.n_slots = L.n_slots; a.counters = L.counters;
+  a.mean = p.mean; a.ramax_part = L.ramax; a.mamax_part = L.mamax;
+  a.n_strips = (int)n_strips(p.cols);
+  a.mode = (p.split ? 1 : 0) | (p.mean_given ? 2 : 0);
+  a.h16 = (p.split && p.h16) ? 1 : 0;
+  a.offsets = grouped ? p.d_offsets : nullptr;
+  a.E = grouped ? (int)p.E : 1;
+  const dim3 grid((unsigned)n_strips(p.cols), (unsigned)L.nslab);
+  hipLaunchKernelGGL((k_colstats<T, MINMAX>), grid, dim3(kThreads), 0, p.stream, a);
 }
 
 hipError_t split_quant_launch(const SplitQuantPlan& p) {
   const bool grouped = p.E > 0;
-  int64_t nslab = slab_count(p.rows);
+  int64_t nslab = cs_slabs(p.rows);
   if (grouped) {
     nslab = 0;
-    for (int64_t e = 0; e < p.E; ++e) nslab += ceil_div(p.h_offsets[e + 1] - p.h_offsets[e], kStatRows);
-    if (nslab == 0) nslab = 1;
+    for (int64_t e = 0; e < p.E; ++e) nslab += cs_slabs(p.h_offsets[e + 1] - p.h_offsets[e]);
   }
   const SqLayout L = sq_layout(p.ws, nslab, p.cols, grouped ? p.E : 1);
   const bool nv = p.fmt == AVERIS_NVFP4;

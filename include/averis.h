@@ -25,6 +25,11 @@
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
  *    returns without waiting.  Inputs must stay valid until the stream reaches the work.
  *    Calls on different streams are independent; calls sharing a workspace must be ordered.
+ *  - Workspaces (ws, ws_bytes >= the matching *_workspace_size query) are device scratch.  A
+ *    split_quant workspace must be zero-filled before its first use: it holds per-column-strip
+ *    arrival counters, and every call leaves them at zero again, so it can be reused as is by
+ *    calls with the same cols (and E).  Zero it again before using it for other cols or E.
+ *    The other workspaces need no initial contents.
  *  - Arguments are validated before anything is enqueued: on any error a non-zero status is
  *    returned, nothing is launched and no output is touched.  A failed launch returns
  *    AVERIS_E_HIP.  Faults inside kernels surface at the caller's next synchronisation.

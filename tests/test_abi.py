@@ -89,8 +89,10 @@ def test_split_quant_rejects(kw, status):
 
 
 def test_split_quant_workspace_size():
+    # column statistics of 512-row slabs: psum fp64 + min, max fp32 per slab and column, plus
+    # one arrival counter and two partial maxima per 64-column strip
     L = av.lib()
-    assert L.averis_split_quant_workspace_size(8192, 1024, av.NVFP4, av.SPLIT) >= 32 * 1024 * 16
+    assert L.averis_split_quant_workspace_size(8192, 1024, av.NVFP4, av.SPLIT) >= 16 * 1024 * 16 + 16 * 12
     assert L.averis_split_quant_workspace_size(0, 1024, av.NVFP4, av.SPLIT) > 0
     assert L.averis_split_quant_workspace_size(-1, 1024, av.NVFP4, av.SPLIT) == 0
 
