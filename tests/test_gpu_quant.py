@@ -140,3 +140,26 @@ def test_strided_rows(fmt, fname, dtype):
     assert_q_equal(g["row"], o["row"], "row layout")
     assert_q_equal(g["col"], o["col"], "column layout")
     assert_q_equal(g["mean_q"], o["mean"], "quantized mean")
+
+
+def test_workspace_reused_across_calls():
+    # the split's workspace carries per-strip arrival counters that each call must leave at
+    # zero: three calls on one workspace (different data, both formats) must each match the
+    # oracle, and the counters must read zero afterwards
+    dev = device()
+    rows, cols = 1500, 384
+    ws = av.split_quant_workspace(rows, cols, av.NVFP4, split=True, device=dev)
+    for k, fmt in enumerate((av.MXFP4, av.NVFP4, av.MXFP4)):
+        lin = workloads.up_proj_like(40 + k, rows, cols, 128)
+        print(f"case reuse-{k} fmt={fmt}", flush=True)
+        g = av.split_quant(workloads.to_torch(lin.x, "bf16", dev), fmt, split=True, ws=ws)
+        torch.cuda.synchronize()
+        mu = g["mean"].cpu().numpy()
+        assert mean_ok(mu, lin.x), f"call {k}: mean"
+        o = O.split_quant(lin.x, fmt, split=True, mean=mu)
+        assert_q_equal(g["row"], o["row"], f"call {k} row layout")
+        assert_q_equal(g["col"], o["col"], f"call {k} column layout")
+        assert_q_equal(g["mean_q"], o["mean"], f"call {k} quantized mean")
+    # header: amax slots (3 + 2 uint32) then one counter per 64-column strip
+    counters = ws[20:20 + 4 * (cols // 64)].cpu().numpy().view(np.uint32)
+    assert not counters.any(), f"strip counters left at {counters}"
