@@ -160,8 +160,8 @@ def main():
     achieved = 2.0 * l * m * n / launch_s / 1e12
     roofline = {"bound": "mfma", "kernel": "k_gemm<MXFP4> (forward and input-gradient GEMMs)",
                 "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_FP4_TFLOPS, 4), "traffic": None,
-                "launch_us": round(launch_s * 1e6, 2)}
+                "frac": round(achieved / PEAK_FP4_TFLOPS, 4), "traffic": gemm_traffic(),
+                "traffic_unit": "bytes per launch (HBM, counter runs)", "launch_us": round(launch_s * 1e6, 2)}
     del st
 
     cpu = None
@@ -199,6 +199,27 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def gemm_traffic():
+    """HBM bytes per k_gemm launch from the committed counter summary, or None once the GEMM
+    source has changed since those counters were taken."""
+    import hashlib
+    import re
+    prof = os.path.join(ROOT, "profiles", "k_gemm_mxfp4_up_proj_traffic.md")
+    try:
+        text = open(prof).read()
+    except OSError:
+        return None
+    m_t = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
+    m_h = re.search(r"^gemm_source_sha1: ([0-9a-f]+)$", text, re.M)
+    if not (m_t and m_h):
+        return None
+    h = hashlib.sha1()
+    for f in ("gemm.hip", "common.h"):
+        with open(os.path.join(ROOT, "fp4_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return int(m_t.group(1)) if h.hexdigest()[:len(m_h.group(1))] == m_h.group(1) else None
 
 
 def cpu_baseline(lin, rows):
