@@ -206,7 +206,7 @@ def gemm_traffic():
     source has changed since those counters were taken."""
     import hashlib
     import re
-    prof = os.path.join(ROOT, "profiles", "k_gemm_mxfp4_up_proj_traffic.md")
+    prof = os.path.join(ROOT, "profiles", "k_gemm_mxfp4_up_proj_traffic.txt")
     try:
         text = open(prof).read()
     except OSError:

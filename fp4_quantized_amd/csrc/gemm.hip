@@ -26,6 +26,10 @@
 
 namespace av {
 
+// A quantized mean read in place: element k of row `row` of a [rows, k_pad] FP4 operand (codes,
+// tiled scales, NVFP4 per-row tensor scales), quantized after the 16x16 rotation when rot != 0.
+struct MeanVec { const uint8_t* codes; const uint8_t* scales; const float* ts; int64_t k_pad; int rot; };
+
 struct GemmArgs {
   const uint8_t* a_codes; const uint8_t* a_scales; int64_t lda_b;  // codes row stride (bytes); scales tiled
   const uint8_t* b_codes; const uint8_t* b_scales; int64_t ldb_b;
@@ -33,7 +37,8 @@ struct GemmArgs {
   int64_t M, N, K;                      // K = padded length (multiple of 128)
   void* c; int64_t ldc; int c_bf16;     // output (or split-K partials base when splits > 1)
   const float* bias;                    // [N] or nullptr
-  const float* r1u; const float* r1v; float r1;  // rank-one term r1 * u[row] * v[col], or nullptr
+  // rank-one term r1 * u[row] * v[col] (has_r1): u, v = dequantized means ru, rv (row r1_row)
+  MeanVec ru, rv; int has_r1; float r1; int64_t r1_row;
   int accumulate;
   int splits; int64_t k_chunk;          // K range per split (multiple of the K-step), partials at c + s * M * N
   int tiles_m, tiles_n;
@@ -45,6 +50,7 @@ struct GemmArgs {
   //     K_e = round_up(l_e, 256), at token offset p256[e]), C = [E][M][ldc], rank-one factor
   //     l_e with u [E][M] and v [E][N].  Every group has tiles_m x tiles_n tiles.
   const int64_t* offsets; int E; int grouped;
+  int n_work;                           // logical tiles of the launch (a workgroup may take several)
 };
 
 __device__ inline uint32_t f32_to_bf16_rne(float f) {
@@ -93,6 +99,24 @@ __device__ inline float dq_one(const uint8_t* codes, const uint8_t* scales, cons
   return __fmul_rn(__fmul_rn(v, e4m3_value(s)), ts[row]);
 }
 
+// Element k of a dequantized mean vector, the rotation undone when the mean was quantized
+// rotated: 0.25 * sum_j H16[p][j] DQ(q[16 b + j]), k = 16 b + p, H16[p][j] = (-1)^popcount(p & j)
+// (Sylvester order).  The 16 terms are fp32 values within a factor 12 of each other, so their
+// fp64 sum is exact in any order and the result is one rounding of the exact value.
+template <int FMT>
+__device__ inline float mean_value(const MeanVec& mv, int64_t row, int64_t k) {
+  if (!mv.rot) return dq_one<FMT>(mv.codes, mv.scales, mv.ts, row, k, mv.k_pad);
+  const int64_t b = k >> 4;
+  const int p = (int)(k & 15);
+  double s = 0.0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const double v = (double)dq_one<FMT>(mv.codes, mv.scales, mv.ts, row, b * 16 + j, mv.k_pad);
+    s += (__popc(p & j) & 1) ? -v : v;
+  }
+  return (float)(s * 0.25);
+}
+
 // Two fp32 values to packed bf16 (round to nearest even), low half first.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
@@ -138,10 +162,6 @@ struct GemmCfg {
   static constexpr int NLA = IA / NW, NLB = IB / NW, NLSA = ISA_P / NW, NLSB = ISB_P / NW;
   static constexpr int LPS = NLA + NLB + NLSA + NLSB;          // load instructions per wave per step
   static_assert(LPS * (STAGES - 2) < 64, "vmcnt range");
-  // epilogue staging: per wave a 32 x (TN * 32) fp32 tile, padded rows
-  static constexpr int EPI_LD = TN * 32 + 4;
-  static constexpr int EPI_WAVE = 32 * EPI_LD * 4;
-  static_assert((NW + 1) / 2 * EPI_WAVE <= STAGE, "epilogue staging must fit in two stages");
 };
 
 template <int FMT, int WM, int WN, int TM, int TN, int STAGES, int AUX = 0>
@@ -299,16 +319,17 @@ __device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt((15) |
 //   half, after which lane (fr, h) holds the 8 consecutive columns j*32 + 16p + 8h of its row
 //   (p = q / 2): one 16-byte store of 8 bf16.
 // Per-column terms (bias, v) and per-row terms (u) are loaded once per tile, in one batch,
-// before the first store.
+// before the first store; u (times r1) and v come from the tile's LDS copy (su: this wave's rows,
+// sv: its columns).
 //   out = alpha * acc (+ bias[col]) (+ r1 * u[row] * v[col]) (+ C when accumulating), each step
 //   rounded once in fp32; split-K partials get alpha * acc only.
 template <int FMT, int TM, int TN>
 __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&acc)[TM][TN], int64_t rbase,
-                                              int64_t cbase, int split, int lane) {
+                                              int64_t cbase, int split, int lane, const float* su, const float* sv) {
   const int fr = lane & 31, h = lane >> 5;
   const bool bf = g.c_bf16 && g.splits == 1;
   const bool terms = g.splits == 1;
-  const bool hb = terms && g.bias, hr = terms && g.r1u;
+  const bool hb = terms && g.bias, hr = terms && g.has_r1;
   // this lane's columns: bf16 -> j*32 + 16p + 8h + (0..7); fp32 -> j*32 + 8q + 4h + (0..3)
   float bias[TN][16], vv[TN][16], uu[TM];
 #pragma unroll
@@ -319,14 +340,14 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
       const int64_t col = cbase + off;
       const bool ok = col < g.N;
       const float4 b = (hb && ok) ? *reinterpret_cast<const float4*>(g.bias + col) : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 r = (hr && ok) ? *reinterpret_cast<const float4*>(g.r1v + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 r = hr ? *reinterpret_cast<const float4*>(sv + off) : make_float4(0.f, 0.f, 0.f, 0.f);
       bias[j][4 * c4] = b.x; bias[j][4 * c4 + 1] = b.y; bias[j][4 * c4 + 2] = b.z; bias[j][4 * c4 + 3] = b.w;
       vv[j][4 * c4] = r.x; vv[j][4 * c4 + 1] = r.y; vv[j][4 * c4 + 2] = r.z; vv[j][4 * c4 + 3] = r.w;
     }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int64_t row = rbase + i * 32 + fr;
-    uu[i] = (hr && row < g.M) ? __fmul_rn(g.r1, g.r1u[row]) : 0.0f;
+    uu[i] = (hr && row < g.M) ? su[i * 32 + fr] : 0.0f;
   }
   float alpha = 1.0f;
   if (FMT == AVERIS_NVFP4) alpha = __fmul_rn(g.a_ts[0], g.b_ts[0]);
@@ -394,91 +415,122 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
   }
 }
 
+// Two-stage 2 x 2 wave tiles run two workgroups per CU (two waves per SIMD): the register budget
+// is held to that occupancy.
 template <int FMT, int WM, int WN, int TM, int TN, int STAGES, int AUX = 0>
-__global__ __launch_bounds__(64 * WM * WN) void k_gemm(GemmArgs gin) {
+__global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1) void k_gemm(GemmArgs gin) {
   using T = GemmTile<FMT, WM, WN, TM, TN, STAGES, AUX>;
   using C = typename T::C;
   static_assert(STAGES == 2 || STAGES == 3 || STAGES == 4, "stages");
-  GemmArgs g = gin;  // this workgroup's view (grouped launches retarget it to one group)
   __shared__ __attribute__((aligned(1024))) uint8_t st0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGES >= 3 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t st3[STAGES >= 4 ? C::STAGE : 16];
+  __shared__ float s_uv[C::BM + C::BN];  // rank-one term: r1 * u over the tile's rows, then v over its columns
+  static_assert(C::BM + C::BN == C::NT, "one rank-one element per thread");
 
-  int ntiles = g.tiles_m * g.tiles_n;
-  const int lin = xcd_remap(blockIdx.x, (int)gridDim.x);
-  int split = 0, tm, tn;
-  if (gin.grouped == 1) {
-    const int tn_all = gin.tiles_n;
-    const GroupPos gp = group_scan(gin.offsets, gin.E, lin, true,
-                                   [tn_all](int64_t len) { return ceil_div(len, (int64_t)C::BM) * tn_all; });
-    if (gp.e < 0) return;
-    const int tms = (int)ceil_div(gp.len, (int64_t)C::BM);
-    tile_coords((int)gp.local, tms, tn_all, gin.group_m < tms ? gin.group_m : tms, tm, tn);
-    const int64_t gsa = (gin.K / C::BKE) * C::PIECE;  // tiled scale bytes per 32-row group
-    g.M = gp.len;
-    g.a_codes += gp.p32 * gin.lda_b;
-    g.a_scales += (gp.p32 / 32) * gsa;
-    g.b_codes += (int64_t)gp.e * gin.N * gin.ldb_b;
-    g.b_scales += ((int64_t)gp.e * gin.N / 32) * gsa;
-    if (FMT == AVERIS_NVFP4) { g.a_ts += gp.e; g.b_ts += gp.e; }
-    if (gin.bias) g.bias += (int64_t)gp.e * gin.N;
-    g.c = reinterpret_cast<uint8_t*>(gin.c) + gp.off * gin.ldc * (gin.c_bf16 ? 2 : 4);
-  } else if (gin.grouped == 2) {
-    const int e = lin / ntiles;
-    tile_coords(lin % ntiles, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
-    const GroupPos gp = group_scan(gin.offsets, gin.E, e, false, [](int64_t) { return (int64_t)1; });
-    const int64_t ke_pad = round_up(gp.len, (int64_t)C::BKE);
-    g.K = ke_pad; g.k_chunk = ke_pad;
-    g.lda_b = ke_pad / 2; g.ldb_b = ke_pad / 2;
-    g.a_codes += gin.M * gp.p256 / 2;
-    g.a_scales += gin.M * gp.p256 / C::G;
-    g.b_codes += gin.N * gp.p256 / 2;
-    g.b_scales += gin.N * gp.p256 / C::G;
-    if (FMT == AVERIS_NVFP4) { g.a_ts += e; g.b_ts += e; }
-    g.r1 = (float)gp.len;
-    if (gin.r1u) { g.r1u += (int64_t)e * gin.M; g.r1v += (int64_t)e * gin.N; }
-    g.c = reinterpret_cast<float*>(gin.c) + (int64_t)e * gin.M * gin.ldc;
-  } else {
-    split = lin / ntiles;
-    tile_coords(lin % ntiles, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
-  }
-  const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
-  const int64_t kb = (int64_t)split * g.k_chunk;
-  const int64_t ke = kb + g.k_chunk < g.K ? kb + g.k_chunk : g.K;
-  const int nsteps = (int)((ke - kb) / C::BKE);  // K and k_chunk are multiples of the K-step
-  const int kb_byte = (int)(kb / 2), kb_sbyte = (int)(kb / C::BKE) * C::PIECE;
-
-  T t;
-  t.setup(g, m0, n0);
-  // prologue: K-steps 0 .. STAGES-2
-  t.issue(kb_byte, kb_sbyte, st0);
-  if (STAGES >= 3) t.issue(1 < nsteps ? kb_byte + C::BKB : 0, 1 < nsteps ? kb_sbyte + C::PIECE : 0, st1);
-  if (STAGES >= 4) t.issue(2 < nsteps ? kb_byte + 2 * C::BKB : 0, 2 < nsteps ? kb_sbyte + 2 * C::PIECE : 0, st2);
-  for (int it = 0; it < nsteps; it += STAGES) {
-    if (STAGES == 2) {
-      pipe_step<T, STAGES>(t, it, nsteps, kb_byte, kb_sbyte, st0, st1);
-      pipe_step<T, STAGES>(t, it + 1, nsteps, kb_byte, kb_sbyte, st1, st0);
-    } else if (STAGES == 3) {
-      pipe_step<T, STAGES>(t, it, nsteps, kb_byte, kb_sbyte, st0, st2);
-      pipe_step<T, STAGES>(t, it + 1, nsteps, kb_byte, kb_sbyte, st1, st0);
-      pipe_step<T, STAGES>(t, it + 2, nsteps, kb_byte, kb_sbyte, st2, st1);
+  // This workgroup's logical tiles: a strided run within its XCD's contiguous share of the
+  // launch (one tile when the grid covers every tile).  Each tile runs prologue, K loop and
+  // epilogue in turn; the epilogue does not touch LDS, and every wave has finished reading the
+  // stages before it starts, so the next tile's prologue may refill them at once.
+  int first, stride, end;
+  xcd_tiles((int)blockIdx.x, (int)gridDim.x, gin.n_work, first, stride, end);
+  for (int lin = first; lin < end; lin += stride) {
+    GemmArgs g = gin;  // this tile's view (grouped launches retarget it to one group)
+    int ntiles = g.tiles_m * g.tiles_n;
+    int split = 0, tm, tn;
+    if (gin.grouped == 1) {
+      const int tn_all = gin.tiles_n;
+      const GroupPos gp = group_scan(gin.offsets, gin.E, lin, true,
+                                     [tn_all](int64_t len) { return ceil_div(len, (int64_t)C::BM) * tn_all; });
+      if (gp.e < 0) continue;
+      const int tms = (int)ceil_div(gp.len, (int64_t)C::BM);
+      tile_coords((int)gp.local, tms, tn_all, gin.group_m < tms ? gin.group_m : tms, tm, tn);
+      const int64_t gsa = (gin.K / C::BKE) * C::PIECE;  // tiled scale bytes per 32-row group
+      g.M = gp.len;
+      g.a_codes += gp.p32 * gin.lda_b;
+      g.a_scales += (gp.p32 / 32) * gsa;
+      g.b_codes += (int64_t)gp.e * gin.N * gin.ldb_b;
+      g.b_scales += ((int64_t)gp.e * gin.N / 32) * gsa;
+      if (FMT == AVERIS_NVFP4) { g.a_ts += gp.e; g.b_ts += gp.e; }
+      if (gin.bias) g.bias += (int64_t)gp.e * gin.N;
+      g.c = reinterpret_cast<uint8_t*>(gin.c) + gp.off * gin.ldc * (gin.c_bf16 ? 2 : 4);
+    } else if (gin.grouped == 2) {
+      const int e = lin / ntiles;
+      tile_coords(lin % ntiles, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+      const GroupPos gp = group_scan(gin.offsets, gin.E, e, false, [](int64_t) { return (int64_t)1; });
+      const int64_t ke_pad = round_up(gp.len, (int64_t)C::BKE);
+      g.K = ke_pad; g.k_chunk = ke_pad;
+      g.lda_b = ke_pad / 2; g.ldb_b = ke_pad / 2;
+      g.a_codes += gin.M * gp.p256 / 2;
+      g.a_scales += gin.M * gp.p256 / C::G;
+      g.b_codes += gin.N * gp.p256 / 2;
+      g.b_scales += gin.N * gp.p256 / C::G;
+      if (FMT == AVERIS_NVFP4) { g.a_ts += e; g.b_ts += e; }
+      g.r1 = (float)gp.len;
+      g.r1_row = e;
+      g.c = reinterpret_cast<float*>(gin.c) + (int64_t)e * gin.M * gin.ldc;
     } else {
-      pipe_step<T, STAGES>(t, it, nsteps, kb_byte, kb_sbyte, st0, st3);
-      pipe_step<T, STAGES>(t, it + 1, nsteps, kb_byte, kb_sbyte, st1, st0);
-      pipe_step<T, STAGES>(t, it + 2, nsteps, kb_byte, kb_sbyte, st2, st1);
-      pipe_step<T, STAGES>(t, it + 3, nsteps, kb_byte, kb_sbyte, st3, st2);
+      split = lin / ntiles;
+      tile_coords(lin % ntiles, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
     }
-  }
-  wait_vm<0>();                 // no load may still be writing LDS
-  __builtin_amdgcn_s_barrier();  // every wave is done reading the stages
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    const int64_t kb = (int64_t)split * g.k_chunk;
+    const int64_t ke = kb + g.k_chunk < g.K ? kb + g.k_chunk : g.K;
+    const int nsteps = (int)((ke - kb) / C::BKE);  // K and k_chunk are multiples of the K-step
+    const int kb_byte = (int)(kb / 2), kb_sbyte = (int)(kb / C::BKE) * C::PIECE;
 
-  // ---- epilogue ----
-  epilogue_regs<FMT, TM, TN>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, split, threadIdx.x & 63);
+    T t;
+    t.setup(g, m0, n0);
+    // prologue: K-steps 0 .. STAGES-2
+    t.issue(kb_byte, kb_sbyte, st0);
+    if (STAGES >= 3) t.issue(1 < nsteps ? kb_byte + C::BKB : 0, 1 < nsteps ? kb_sbyte + C::PIECE : 0, st1);
+    if (STAGES >= 4) t.issue(2 < nsteps ? kb_byte + 2 * C::BKB : 0, 2 < nsteps ? kb_sbyte + 2 * C::PIECE : 0, st2);
+    // this thread's rank-one element (loads overlap the prologue; used in the epilogue)
+    const bool hr = g.splits == 1 && g.has_r1;
+    float uv = 0.0f;
+    if (hr) {
+      const int i = threadIdx.x;
+      if (i < C::BM) {
+        const int64_t row = m0 + i;
+        if (row < g.M) uv = __fmul_rn(g.r1, mean_value<FMT>(g.ru, g.r1_row, row));
+      } else {
+        const int64_t col = n0 + (i - C::BM);
+        if (col < g.N) uv = mean_value<FMT>(g.rv, g.r1_row, col);
+      }
+    }
+    for (int it = 0; it < nsteps; it += STAGES) {
+      if (STAGES == 2) {
+        pipe_step<T, STAGES>(t, it, nsteps, kb_byte, kb_sbyte, st0, st1);
+        pipe_step<T, STAGES>(t, it + 1, nsteps, kb_byte, kb_sbyte, st1, st0);
+      } else if (STAGES == 3) {
+        pipe_step<T, STAGES>(t, it, nsteps, kb_byte, kb_sbyte, st0, st2);
+        pipe_step<T, STAGES>(t, it + 1, nsteps, kb_byte, kb_sbyte, st1, st0);
+        pipe_step<T, STAGES>(t, it + 2, nsteps, kb_byte, kb_sbyte, st2, st1);
+      } else {
+        pipe_step<T, STAGES>(t, it, nsteps, kb_byte, kb_sbyte, st0, st3);
+        pipe_step<T, STAGES>(t, it + 1, nsteps, kb_byte, kb_sbyte, st1, st0);
+        pipe_step<T, STAGES>(t, it + 2, nsteps, kb_byte, kb_sbyte, st2, st1);
+        pipe_step<T, STAGES>(t, it + 3, nsteps, kb_byte, kb_sbyte, st3, st2);
+      }
+    }
+    wait_vm<0>();                 // no load may still be writing LDS
+    __builtin_amdgcn_s_barrier();  // every wave is done reading the stages
+
+    // ---- epilogue ----
+    // every wave is past this tile's last barrier, so none still reads the previous tile's s_uv
+    if (hr) {
+      s_uv[threadIdx.x] = uv;
+      lds_barrier();
+    }
+    epilogue_regs<FMT, TM, TN>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, split, threadIdx.x & 63,
+                               s_uv + t.wm * TM * 32, s_uv + C::BM + t.wn * TN * 32);
+  }
 }
 
 // Split-K reduce: C = (accumulate ? C : 0) + (sum_s P[s] in split order + bias[col]
-// + r1 * u[row] * v[col]), four columns per thread (N % 8 == 0); fp32 or bf16 output.
+// + r1 * u[row] * v[col]), four columns per thread (N % 8 == 0); fp32 or bf16 output; u and v
+// dequantized from the quantized means in place.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int splits, GemmArgs g,
                                                        void* __restrict__ c, int64_t ldc, int c_bf16) {
@@ -493,10 +545,11 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
     s.x = __fadd_rn(s.x, t.x); s.y = __fadd_rn(s.y, t.y); s.z = __fadd_rn(s.z, t.z); s.w = __fadd_rn(s.w, t.w);
   }
   float v[4] = {s.x, s.y, s.z, s.w};
+  const float ru = g.has_r1 ? __fmul_rn(g.r1, mean_value<FMT>(g.ru, g.r1_row, row)) : 0.0f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if (g.bias) v[e] = __fadd_rn(v[e], g.bias[col + e]);
-    if (g.r1u) v[e] = __fadd_rn(v[e], __fmul_rn(__fmul_rn(g.r1, g.r1u[row]), g.r1v[col + e]));
+    if (g.has_r1) v[e] = __fadd_rn(v[e], __fmul_rn(ru, mean_value<FMT>(g.rv, g.r1_row, col + e)));
   }
   if (c_bf16) {
     uint2 o;
@@ -562,71 +615,23 @@ __global__ __launch_bounds__(256) void k_gemv_mean(const uint8_t* __restrict__ m
   }
 }
 
-// Dequantized mean vectors for the rank-one dW term, un-rotated when the means were quantized
-// after the 16x16 Hadamard rotation (rot != 0).  `rows` mean rows per operand (one per group):
-// o0 [rows][K0], o1 [rows][K1].
-template <int FMT>
-__global__ __launch_bounds__(256) void k_mean_vec(const uint8_t* __restrict__ c0, const uint8_t* __restrict__ s0,
-                                                  const float* __restrict__ t0, int64_t K0, int64_t P0, float* __restrict__ o0,
-                                                  const uint8_t* __restrict__ c1, const uint8_t* __restrict__ s1,
-                                                  const float* __restrict__ t1, int64_t K1, int64_t P1, float* __restrict__ o1,
-                                                  int64_t rows, int rot) {
-  const int64_t nb0 = (K0 + 15) / 16, nb1 = (K1 + 15) / 16;
-  int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const uint8_t *codes = c0, *scales = s0;
-  const float* ts = t0;
-  int64_t K = K0, P = P0, nb = nb0;
-  float* out = o0;
-  if (blk >= rows * nb0) { blk -= rows * nb0; codes = c1; scales = s1; ts = t1; K = K1; P = P1; nb = nb1; out = o1; }
-  if (blk >= rows * nb) return;
-  const int64_t row = blk / nb, b = blk % nb;
-  double v[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = b * 16 + j < P ? (double)dq_one<FMT>(codes, scales, ts, row, b * 16 + j, P) : 0.0;
-  if (rot) {
-#pragma unroll
-    for (int h = 1; h < 16; h <<= 1)
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if ((j & h) == 0) { const double a = v[j], c = v[j + h]; v[j] = a + c; v[j + h] = a - c; }
-  }
-  const double sc = rot ? 0.25 : 1.0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-    if (b * 16 + j < K) out[row * K + b * 16 + j] = (float)(v[j] * sc);
-}
-
 // ------------------------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------------------------
 static int g_count(int fmt) { return fmt == AVERIS_MXFP4 ? 32 : 16; }
 
-// Tile configurations (waves along M x N, 32x32 MFMA tiles per wave along M x N, LDS stages).
-// Larger wave tiles cut LDS fragment reads per MFMA: a wave with TM x TN tiles reads
-// (TM + TN) KB per TM * TN scaled MFMAs each 64-element substep.
+// Two tile configurations, both 128 x 128 tiles of 2 x 2 waves with 2 x 2 MFMA tiles each
+// (measured on MI355X against 256 x 128, 128 x 256, 256 x 192 and 256 x 256 tiles at the
+// Qwen3-0.6B-shaped linears; 128 x 128 was fastest at every shape):
+//   KCFG_SHORT  two LDS stages, two workgroups per CU (70 KB LDS, <= 256 VGPRs each), for
+//               short K (forward and input-gradient GEMMs over the feature dimension);
+//   KCFG_LONG   three stages, one workgroup per CU, deeper prefetch, for long K (weight
+//               gradients over the token dimension).
+constexpr int KCFG_LONG = 0, KCFG_SHORT = 1;
 struct TileCfg { int bm, bn; };
-static TileCfg tile_of(int cfg) {
-  switch (cfg) {
-    case 1: return {256, 256};
-    case 2: case 5: return {256, 128};
-    case 3: return {128, 256};
-    case 4: return {256, 192};
-    default: return {128, 128};
-  }
-}
+static TileCfg tile_of(int) { return {128, 128}; }
 constexpr int kBKE = 256;
-
-// Configuration per format and shape.
-// Measured on MI355X with the Qwen3-0.6B-shaped linears: 128 x 128 tiles win at these sizes.
-// Short K (the forward and input-gradient GEMMs): two stages, two workgroups per CU, so one
-// workgroup's epilogue overlaps the other's main loop.  Long K (weight gradients over the
-// token dimension): three stages, one workgroup per CU, deeper prefetch.
-static bool cfg_valid(int fmt, int cfg);
-static int pick_cfg(int fmt, int64_t M, int64_t N, int64_t K) {
-  (void)M; (void)N;
-  const int c = K >= 4096 ? 0 : 6;
-  return cfg_valid(fmt, c) ? c : 0;
-}
+static int pick_cfg(int64_t K) { return K >= 4096 ? KCFG_LONG : KCFG_SHORT; }
 
 static int splits_for(int cfg, int64_t M, int64_t N, int64_t K) {
   const TileCfg tc = tile_of(cfg);
@@ -638,45 +643,44 @@ static int splits_for(int cfg, int64_t M, int64_t N, int64_t K) {
   if (s > 8) s = 8;
   return s < 1 ? 1 : (int)s;
 }
-int choose_splits(int fmt, int64_t M, int64_t N, int64_t K) { return splits_for(pick_cfg(fmt, M, N, K), M, N, K); }
-
-// workspace: [256 B][bias E x N][u E x round_up(M, 4)][v E x N] fp32 (16-byte aligned vectors),
-// then split-K partials [splits][M][N] fp32 (dense launches only)
-static size_t partials_offset(int64_t M, int64_t N, int64_t E) {
-  return 256 + (size_t)round_up(E * (N + round_up(M, 4) + N) * 4, 1024);
+int choose_splits(int fmt, int64_t M, int64_t N, int64_t K) {
+  (void)fmt;
+  return splits_for(pick_cfg(K), M, N, K);
 }
+
+// workspace: [256 B][mean-term bias E x N fp32], then split-K partials [splits][M][N] fp32
+// (dense launches only)
+static size_t partials_offset(int64_t N, int64_t E) { return 256 + (size_t)round_up(E * N * 4, 1024); }
 
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int splits) {
   (void)K;
-  size_t b = partials_offset(M, N, 1);
+  size_t b = partials_offset(N, 1);
   if (splits > 1) b += (size_t)splits * M * N * 4;
   return b;
 }
-size_t gemm_grouped_ws_bytes(int64_t M, int64_t N, int64_t E) { return partials_offset(M, N, E); }
+size_t gemm_grouped_ws_bytes(int64_t M, int64_t N, int64_t E) {
+  (void)M;
+  return partials_offset(N, E);
+}
 
-// MXFP4 takes every configuration; NVFP4 (bf16 MFMAs on dequantized fragments, 16 scale bytes
-// per row and K-step) only those whose registers and LDS fit.
-static void launch_mx(int cfg, const GemmArgs& g, unsigned grid, hipStream_t s) {
-  constexpr int F = AVERIS_MXFP4;
-  switch (cfg) {
-    case 1: hipLaunchKernelGGL((k_gemm<F, 2, 2, 4, 4, 2>), dim3(grid), dim3(256), 0, s, g); break;
-    case 2: hipLaunchKernelGGL((k_gemm<F, 2, 2, 4, 2, 3>), dim3(grid), dim3(256), 0, s, g); break;
-    case 3: hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 4, 3>), dim3(grid), dim3(256), 0, s, g); break;
-    case 4: hipLaunchKernelGGL((k_gemm<F, 2, 2, 4, 3, 2>), dim3(grid), dim3(256), 0, s, g); break;
-    case 5: hipLaunchKernelGGL((k_gemm<F, 2, 2, 4, 2, 2>), dim3(grid), dim3(256), 0, s, g); break;
-    case 6: hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 2>), dim3(grid), dim3(256), 0, s, g); break;
-    default: hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 3>), dim3(grid), dim3(256), 0, s, g); break;
-  }
+template <int F>
+static void launch_cfg(int cfg, const GemmArgs& g, unsigned grid, hipStream_t s) {
+  if (cfg == KCFG_SHORT) hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 2>), dim3(grid), dim3(256), 0, s, g);
+  else hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 3>), dim3(grid), dim3(256), 0, s, g);
 }
-static void launch_nv(int cfg, const GemmArgs& g, unsigned grid, hipStream_t s) {
-  constexpr int F = AVERIS_NVFP4;
-  switch (cfg) {
-    case 5: hipLaunchKernelGGL((k_gemm<F, 2, 2, 4, 2, 2>), dim3(grid), dim3(256), 0, s, g); break;
-    case 6: hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 2>), dim3(grid), dim3(256), 0, s, g); break;
-    default: hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 3>), dim3(grid), dim3(256), 0, s, g); break;
-  }
+// Workgroups resident per CU: two for the two-stage configuration, one for the three-stage one
+// (105 KB of LDS).
+static int resident_per_cu(int cfg) { return cfg == KCFG_SHORT ? 2 : 1; }
+static int cu_count() {
+  static int cached[64] = {};  // per device id
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cached[dev] = n;
+  return n;
 }
-static bool cfg_valid(int fmt, int cfg) { return fmt == AVERIS_MXFP4 ? (cfg >= 0 && cfg <= 6) : (cfg == 0 || cfg == 5 || cfg == 6); }
 
 hipError_t gemm_launch(const GemmPlan& p) {
   const averis_qtensor& A = *p.a;
@@ -694,13 +698,9 @@ hipError_t gemm_launch(const GemmPlan& p) {
     K = 0;
     for (int64_t e = 0; e < E; ++e) K = std::max<int64_t>(K, round_up(p.h_offsets[e + 1] - p.h_offsets[e], kBKE));
   }
-  // grouped forward / input gradient use only the bias vectors of the workspace
-  const int64_t Mws = p.grouped == 1 ? 0 : M;
   uint8_t* ws = reinterpret_cast<uint8_t*>(p.ws);
   float* bias = reinterpret_cast<float*>(ws + 256);
-  float* u = bias + E * N;
-  float* v = u + E * round_up(Mws, 4);
-  float* partials = reinterpret_cast<float*>(ws + partials_offset(Mws, N, E));
+  float* partials = reinterpret_cast<float*>(ws + partials_offset(N, E));
 
   GemmArgs g{};
   g.a_codes = A.codes; g.a_scales = A.scales; g.lda_b = A.k_pad / 2;
@@ -708,7 +708,7 @@ hipError_t gemm_launch(const GemmPlan& p) {
   g.a_ts = A.tensor_scale; g.b_ts = B.tensor_scale;
   g.M = M; g.N = N; g.K = K;
   g.offsets = p.d_offsets; g.E = (int)E; g.grouped = p.grouped;
-  const int cfg = p.grouped == 2 ? 0 : pick_cfg(fmt, M, N, K);  // grouped dW: long, varying K
+  const int cfg = p.grouped == 2 ? KCFG_LONG : pick_cfg(K);  // grouped dW: long, varying K
   const TileCfg tc = tile_of(cfg);
   g.tiles_m = (int)ceil_div(M, tc.bm); g.tiles_n = (int)ceil_div(N, tc.bn);
   if (p.grouped == 1)
@@ -736,20 +736,14 @@ hipError_t gemm_launch(const GemmPlan& p) {
     g.bias = bias;
   }
   if (p.mu_u) {
-    g.r1 = p.r1;
+    // rank-one term: the kernels dequantize the means in place (undoing the rotation if any)
     const averis_qtensor& Qu = *p.mu_u;
     const averis_qtensor& Qv = *p.mu_v;
-    const int rot = (Qu.flags & AVERIS_HADAMARD16) ? 1 : 0;
-    const unsigned blocks = (unsigned)ceil_div(E * (ceil_div(Qu.k, 16) + ceil_div(Qv.k, 16)), 256);
-    if (fmt == AVERIS_MXFP4)
-      hipLaunchKernelGGL(k_mean_vec<AVERIS_MXFP4>, dim3(blocks), dim3(256), 0, p.stream, Qu.codes, Qu.scales,
-                         Qu.tensor_scale, Qu.k, Qu.k_pad, u, Qv.codes, Qv.scales, Qv.tensor_scale, Qv.k, Qv.k_pad, v, E,
-                         rot);
-    else
-      hipLaunchKernelGGL(k_mean_vec<AVERIS_NVFP4>, dim3(blocks), dim3(256), 0, p.stream, Qu.codes, Qu.scales,
-                         Qu.tensor_scale, Qu.k, Qu.k_pad, u, Qv.codes, Qv.scales, Qv.tensor_scale, Qv.k, Qv.k_pad, v, E,
-                         rot);
-    g.r1u = u; g.r1v = v;
+    g.has_r1 = 1;
+    g.r1 = p.r1;
+    g.r1_row = 0;
+    g.ru = MeanVec{Qu.codes, Qu.scales, Qu.tensor_scale, Qu.k_pad, (Qu.flags & AVERIS_HADAMARD16) ? 1 : 0};
+    g.rv = MeanVec{Qv.codes, Qv.scales, Qv.tensor_scale, Qv.k_pad, (Qv.flags & AVERIS_HADAMARD16) ? 1 : 0};
   }
   g.splits = p.grouped ? 1 : p.splits;
   const int64_t ksteps = ceil_div(K, kBKE);
@@ -759,10 +753,13 @@ hipError_t gemm_launch(const GemmPlan& p) {
   } else {
     g.c = p.c; g.ldc = p.ldc; g.c_bf16 = p.c_bf16;
   }
-  const int64_t grid = p.grouped == 1 ? total_tiles_m * g.tiles_n : (int64_t)g.tiles_m * g.tiles_n * g.splits * E;
-  if (grid == 0) return hipGetLastError();
-  if (fmt == AVERIS_MXFP4) launch_mx(cfg, g, (unsigned)grid, p.stream);
-  else launch_nv(cfg, g, (unsigned)grid, p.stream);
+  const int64_t work = p.grouped == 1 ? total_tiles_m * g.tiles_n : (int64_t)g.tiles_m * g.tiles_n * g.splits * E;
+  if (work == 0) return hipGetLastError();
+  // one resident round of workgroups, each looping over its tiles
+  g.n_work = (int)work;
+  const int64_t grid = std::min<int64_t>(work, (int64_t)resident_per_cu(cfg) * cu_count());
+  if (fmt == AVERIS_MXFP4) launch_cfg<AVERIS_MXFP4>(cfg, g, (unsigned)grid, p.stream);
+  else launch_cfg<AVERIS_NVFP4>(cfg, g, (unsigned)grid, p.stream);
   if (g.splits > 1) {
     const unsigned blocks = (unsigned)ceil_div(M * (N / 4), 256);
     if (fmt == AVERIS_MXFP4)

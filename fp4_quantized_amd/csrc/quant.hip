@@ -94,12 +94,15 @@ __device__ inline void h16_lanes(float* v, int lane) {
 constexpr int kCsRows = 512;            // rows per column-statistics workgroup
 constexpr int kCsCols = 64;             // columns per column-statistics workgroup (one strip)
 constexpr int kCsWaves = kCsCols / 64;  // finalize: one wave per 64 columns of the strip
+// Each strip's arrival counter has a 128-byte line of its own: the 32 slabs of a strip arrive
+// within a microsecond, and counters sharing a line would serialize every strip's atomics.
+constexpr int kCounterStride = 32;  // uint32 per counter line
 
 struct ColArgs {
   const void* x; int64_t rows, cols, ldx;
   double* psum; float* pmin; float* pmax;  // [nslab][cols]
   uint32_t* slots; int n_slots;            // amax slots, zeroed here for later kernels
-  uint32_t* counters;                      // [groups][n_strips]
+  uint32_t* counters;                      // [groups][n_strips], kCounterStride apart
   float* mean;                             // [groups][cols]
   float* ramax_part; float* mamax_part;    // [groups][n_strips]
   int n_strips, mode, h16;
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
   wait_vm<0>();
   asm volatile("" ::: "memory");
   __syncthreads();
-  uint32_t* counter = a.counters + (int64_t)e * a.n_strips + strip;
+  uint32_t* counter = a.counters + ((int64_t)e * a.n_strips + strip) * kCounterStride;
   if (t == 0)
     s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nsl - 1);
   __syncthreads();
@@ -551,7 +554,7 @@ __device__ __forceinline__ void tile_rows(const QuantArgs& a, int64_t r0, int64_
   if (AMAX_ONLY) return;
   if (row < a.rows_out && col_ok) {
     uint8_t* dst = a.row_codes + row * (a.row_kpad / 2) + cbase / 2;
-    if (EPT == 32) *reinterpret_cast<uint4*>(dst) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+    if constexpr (EPT == 32) *reinterpret_cast<uint4*>(dst) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
     else *reinterpret_cast<uint2*>(dst) = make_uint2(codes[0], codes[1]);
     uint8_t* sd = a.row_scales + scale_offset(row, cbase / G, a.row_kpad, G);
     if (EPT / G == 2) *reinterpret_cast<uint16_t*>(sd) = (uint16_t)sb;
@@ -701,16 +704,20 @@ __global__ void k_fill_f32(float* p, int n, float v) {
 // ------------------------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------------------------
-// workspace: [0, hdr) amax slots (3 + 2 E uint32), then strip counters (E x n_part uint32,
-// zero between calls) | per-strip partial maxima (2 x E x n_part fp32) | column statistics:
-// psum [nslab][cols] fp64, pmin and pmax [nslab][cols] fp32
+// workspace: [0, hdr) amax slots (3 + 2 E uint32, 256-byte aligned end), then strip counters
+// (E x n_strips, one 128-byte line each, zero between calls) | per-strip partial maxima
+// (2 x E x n_part fp32) | column statistics: psum [nslab][cols] fp64, pmin and pmax [nslab][cols]
+// fp32
 struct SqLayout {
   uint32_t* slots; int n_slots; uint32_t* counters; float* ramax; float* mamax; double* psum; float* pmin;
   float* pmax; int n_part; int64_t nslab;
 };
 static int64_t n_strips(int64_t cols) { return ceil_div(cols, kCsCols); }
 static int64_t n_parts(int64_t cols) { return n_strips(cols) * kCsWaves; }  // per-64-column partial maxima
-static size_t sq_header(int64_t cols, int64_t E) { return (size_t)round_up((3 + 2 * E + E * n_strips(cols)) * 4, 256); }
+static size_t sq_slots_bytes(int64_t E) { return (size_t)round_up((3 + 2 * E) * 4, 256); }
+static size_t sq_header(int64_t cols, int64_t E) {
+  return sq_slots_bytes(E) + (size_t)round_up(E * n_strips(cols) * kCounterStride * 4, 256);
+}
 static SqLayout sq_layout(void* ws, int64_t nslab, int64_t cols, int64_t E) {
   SqLayout L;
   uint8_t* b = reinterpret_cast<uint8_t*>(ws);
@@ -719,7 +726,7 @@ static SqLayout sq_layout(void* ws, int64_t nslab, int64_t cols, int64_t E) {
   const size_t h = sq_header(cols, E), pb = (size_t)round_up(E * L.n_part * 4, 256);
   L.slots = reinterpret_cast<uint32_t*>(b);
   L.n_slots = (int)(3 + 2 * E);
-  L.counters = L.slots + L.n_slots;
+  L.counters = reinterpret_cast<uint32_t*>(b + sq_slots_bytes(E));
   L.ramax = reinterpret_cast<float*>(b + h);
   L.mamax = reinterpret_cast<float*>(b + h + pb);
   L.psum = reinterpret_cast<double*>(b + h + 2 * pb);

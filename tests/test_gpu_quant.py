@@ -160,6 +160,7 @@ def test_workspace_reused_across_calls():
         assert_q_equal(g["row"], o["row"], f"call {k} row layout")
         assert_q_equal(g["col"], o["col"], f"call {k} column layout")
         assert_q_equal(g["mean_q"], o["mean"], f"call {k} quantized mean")
-    # header: amax slots (3 + 2 uint32) then one counter per 64-column strip
-    counters = ws[20:20 + 4 * (cols // 64)].cpu().numpy().view(np.uint32)
-    assert not counters.any(), f"strip counters left at {counters}"
+    # header: amax slots (3 + 2 uint32, padded to 256 bytes), then one 128-byte line per
+    # 64-column strip holding that strip's counter (the rest of the line stays zero)
+    counters = ws[256:256 + 128 * (cols // 64)].cpu().numpy().view(np.uint32)
+    assert not counters.any(), f"strip counters left at {counters.reshape(-1, 32)[:, 0]}"
