@@ -37,6 +37,9 @@ struct GemmArgs {
   int64_t M, N, K;                      // K = padded length (multiple of 128)
   void* c; int64_t ldc; int c_bf16;     // output (or split-K partials base when splits > 1)
   const float* bias;                    // [N] or nullptr
+  // broadcast mean term computed inside the tile loop (kernels with MU): row mu_row of the
+  // quantized mean [rows, K] (codes, tiled scales, NVFP4 tensor scales) times B
+  const uint8_t* mu_codes; const uint8_t* mu_scales; const float* mu_ts; int64_t mu_row;
   // rank-one term r1 * u[row] * v[col] (has_r1): u, v = dequantized means ru, rv (row r1_row)
   MeanVec ru, rv; int has_r1; float r1; int64_t r1_row;
   int accumulate;
@@ -164,16 +167,23 @@ struct GemmCfg {
   static_assert(LPS * (STAGES - 2) < 64, "vmcnt range");
 };
 
-template <int FMT, int WM, int WN, int TM, int TN, int STAGES, int AUX = 0>
+// The mean term (MU): longest K whose quantized mean row fits the tile's LDS copy.
+constexpr int kMuMaxK = 8192;
+constexpr int kMuCodes = kMuMaxK / 2, kMuBytes = kMuCodes + 1024;  // codes, then 4 x 256 scale bytes
+
+template <int FMT, int WM, int WN, int TM, int TN, int STAGES, int AUX = 0, bool MU = false>
 struct GemmTile {
   using C = GemmCfg<FMT, WM, WN, TM, TN, STAGES, AUX>;
+  static_assert(!MU || TN == WM, "the mean term splits a wave's column blocks over the wave rows");
   __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
   int va[C::NLA], vb[C::NLB], vsa[C::NLSA], vsb[C::NLSB];  // per-lane byte offsets (loop invariant)
   int ldsa[C::NLSA], ldsb[C::NLSB];                          // LDS destinations of the scale loads
   int frag_off[C::NKK];   // lane's LDS byte offset of its fragment chunk for each substep
   int scale_off;          // lane's LDS byte offset of its scale bytes within a fragment row block
   int wave, wm, wn;
+  int mu_off, mu_soff;    // lane half's byte offsets within a K-step of the mean's codes / scales
   v16f acc[TM][TN];
+  v16f acc_mu;            // MU: 32 x 32 block (every row the mean) x this wave's column block wm
 
   __device__ __forceinline__ void setup(const GemmArgs& g, int64_t m0, int64_t n0) {
     const int lane = threadIdx.x & 63;
@@ -216,10 +226,26 @@ struct GemmTile {
 #pragma unroll
     for (int kk = 0; kk < C::NKK; ++kk) frag_off[kk] = fr * C::BKB + (((fk * C::NKK + kk) ^ sw) << 4);
     scale_off = fr * C::SB + fk * (C::SB / 2);
+    mu_off = fk * C::NKK * 16;
+    mu_soff = fk * (C::SB / 2);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
+    acc_mu = v16f{};
+  }
+
+  // MU: DMA of the mean row (codes, then per K-step scale bytes) into smu.  Issued before the
+  // prologue, so the first pipeline wait covers it (vector memory ops complete in order).
+  __device__ __forceinline__ void issue_mean(const GemmArgs& g, uint8_t* smu) const {
+    const int lane = threadIdx.x & 63, i = wave * 64 + lane;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.mu_codes + g.mu_row * (g.K / 2), g.K / 2);
+    dma16<AUX>(rc, smu + wave * 1024, i * 16, 0);
+    const int64_t pieces = g.K / C::BKE;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.mu_scales + (g.mu_row >> 5) * pieces * C::PIECE, pieces * C::PIECE);
+    constexpr int LPP = C::SB / 4;  // lanes per K-step piece (4 bytes each)
+    const int voff = (i / LPP) * C::PIECE + (int)(g.mu_row & 31) * C::SB + (i % LPP) * 4;
+    dma4<AUX>(rs, smu + kMuCodes + wave * 256, voff, 0);
   }
 
   // This wave's share of the loads of the K-step starting at byte `kbyte` into stage s.
@@ -234,8 +260,15 @@ struct GemmTile {
     for (int i = 0; i < C::NLSB; ++i) dma4<AUX>(rsb, s + ldsb[i], vsb[i], sbyte);
   }
 
-  __device__ __forceinline__ void compute(const uint8_t* s) {
+  // One K-step from stage s; with MU also the mean's K-step `kstep` from smu.
+  __device__ __forceinline__ void compute(const uint8_t* s, const uint8_t* smu, int kstep) {
     constexpr int LSB = C::SB / 2;  // scale bytes per lane half per K-step (4 or 8)
+    uint32_t msc[LSB / 4];          // MU: the mean's scale bytes of this lane half's chunks
+    if constexpr (MU) {
+#pragma unroll
+      for (int w = 0; w < LSB / 4; ++w)
+        msc[w] = *reinterpret_cast<const uint32_t*>(smu + kMuCodes + kstep * C::SB + mu_soff + 4 * w);
+    }
     uint32_t sa[TM][LSB / 4], sb[TN][LSB / 4];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -269,6 +302,18 @@ struct GemmTile {
                 bv, av, acc[i][j], 4, 4, 0, (int)__builtin_amdgcn_ubfe(sb[j][0], 8 * kk, 8), 0,
                 (int)__builtin_amdgcn_ubfe(sa[i][0], 8 * kk, 8));
           }
+        if constexpr (MU) {
+          // every row of the A block is the mean (one broadcast LDS read per lane half);
+          // column block wm of this wave's columns
+          const uint4 fm = *reinterpret_cast<const uint4*>(smu + kstep * C::BKB + mu_off + kk * 16);
+          const uint4 fbm = wm ? fb[TN - 1] : fb[0];
+          const uint32_t sbm = wm ? sb[TN - 1][0] : sb[0][0];
+          const v8i mv = {(int)fm.x, (int)fm.y, (int)fm.z, (int)fm.w, 0, 0, 0, 0};
+          const v8i bv = {(int)fbm.x, (int)fbm.y, (int)fbm.z, (int)fbm.w, 0, 0, 0, 0};
+          acc_mu = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              bv, mv, acc_mu, 4, 4, 0, (int)__builtin_amdgcn_ubfe(sbm, 8 * kk, 8), 0,
+              (int)__builtin_amdgcn_ubfe(msc[0], 8 * kk, 8));
+        }
       } else {
         v8bf da[TM][4], db[TN][4];
         const int wsel = kk / 2, sh = 16 * (kk % 2);  // two scale bytes per chunk
@@ -289,6 +334,15 @@ struct GemmTile {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(db[j][q], da[i][q], acc[i][j], 0, 0, 0);
+        if constexpr (MU) {
+          const uint4 fm = *reinterpret_cast<const uint4*>(smu + kstep * C::BKB + mu_off + kk * 16);
+          v8bf dm[4];
+          const uint32_t w = msc[wsel];
+          dequant32_bf16(fm, e4m3_value((w >> sh) & 255u), e4m3_value((w >> (sh + 8)) & 255u), dm);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc_mu = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wm ? db[TN - 1][q] : db[0][q], dm[q], acc_mu, 0, 0, 0);
+        }
       }
     }
   }
@@ -300,14 +354,14 @@ struct GemmTile {
 // past the end re-load step 0's bytes into a stage nobody reads) so the vmcnt arithmetic is exact.
 template <class T, int STAGES>
 __device__ __forceinline__ void pipe_step(T& t, int step, int nsteps, int kb_byte, int kb_sbyte, uint8_t* cur,
-                                          uint8_t* nxt) {
+                                          uint8_t* nxt, const uint8_t* smu, int k0) {
   using C = typename T::C;
   wait_vm<C::LPS * (STAGES - 2)>();
   __builtin_amdgcn_s_barrier();
   const int ns = step + STAGES - 1;
   const bool live = ns < nsteps;
   t.issue(live ? kb_byte + ns * C::BKB : 0, live ? kb_sbyte + ns * C::PIECE : 0, nxt);
-  if (step < nsteps) t.compute(cur);
+  if (step < nsteps) t.compute(cur, smu, k0 + step);
 }
 
 __device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14)); }
@@ -323,13 +377,18 @@ __device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt((15) |
 // sv: its columns).
 //   out = alpha * acc (+ bias[col]) (+ r1 * u[row] * v[col]) (+ C when accumulating), each step
 //   rounded once in fp32; split-K partials get alpha * acc only.
-template <int FMT, int TM, int TN>
+template <int FMT, int TM, int TN, bool MU>
 __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&acc)[TM][TN], int64_t rbase,
-                                              int64_t cbase, int split, int lane, const float* su, const float* sv) {
+                                              int64_t cbase, int split, int lane, const float* su, const float* sv,
+                                              const float* sbias) {
   const int fr = lane & 31, h = lane >> 5;
   const bool bf = g.c_bf16 && g.splits == 1;
   const bool terms = g.splits == 1;
-  const bool hb = terms && g.bias, hr = terms && g.has_r1;
+  // mean term: from the tile's MFMAs (MU; split-K partials carry their share) or a precomputed
+  // bias vector (dense launches without MU)
+  const bool hb = MU || (terms && g.bias), hr = terms && g.has_r1;
+  float alpha_mu = 1.0f;
+  if (FMT == AVERIS_NVFP4 && MU) alpha_mu = __fmul_rn(g.mu_ts[g.mu_row], g.b_ts[0]);
   // this lane's columns: bf16 -> j*32 + 16p + 8h + (0..7); fp32 -> j*32 + 8q + 4h + (0..3)
   float bias[TN][16], vv[TN][16], uu[TM];
 #pragma unroll
@@ -339,7 +398,16 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
       const int off = bf ? j * 32 + 16 * (c4 >> 1) + 8 * h + 4 * (c4 & 1) : j * 32 + 8 * c4 + 4 * h;
       const int64_t col = cbase + off;
       const bool ok = col < g.N;
-      const float4 b = (hb && ok) ? *reinterpret_cast<const float4*>(g.bias + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (MU) {
+        b = *reinterpret_cast<const float4*>(sbias + off);
+        if (FMT == AVERIS_NVFP4) {
+          b.x = __fmul_rn(alpha_mu, b.x); b.y = __fmul_rn(alpha_mu, b.y);
+          b.z = __fmul_rn(alpha_mu, b.z); b.w = __fmul_rn(alpha_mu, b.w);
+        }
+      } else if (hb && ok) {
+        b = *reinterpret_cast<const float4*>(g.bias + col);
+      }
       const float4 r = hr ? *reinterpret_cast<const float4*>(sv + off) : make_float4(0.f, 0.f, 0.f, 0.f);
       bias[j][4 * c4] = b.x; bias[j][4 * c4 + 1] = b.y; bias[j][4 * c4 + 2] = b.z; bias[j][4 * c4 + 3] = b.w;
       vv[j][4 * c4] = r.x; vv[j][4 * c4 + 1] = r.y; vv[j][4 * c4 + 2] = r.z; vv[j][4 * c4 + 3] = r.w;
@@ -417,9 +485,11 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
 
 // Two-stage 2 x 2 wave tiles run two workgroups per CU (two waves per SIMD): the register budget
 // is held to that occupancy.
-template <int FMT, int WM, int WN, int TM, int TN, int STAGES, int AUX = 0>
+// MU: the launch carries a broadcast mean term, computed by one extra MFMA per wave and substep
+// on the tile's B fragments (every row of that A block is the quantized mean).
+template <int FMT, int WM, int WN, int TM, int TN, int STAGES, int AUX = 0, bool MU = false>
 __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1) void k_gemm(GemmArgs gin) {
-  using T = GemmTile<FMT, WM, WN, TM, TN, STAGES, AUX>;
+  using T = GemmTile<FMT, WM, WN, TM, TN, STAGES, AUX, MU>;
   using C = typename T::C;
   static_assert(STAGES == 2 || STAGES == 3 || STAGES == 4, "stages");
   __shared__ __attribute__((aligned(1024))) uint8_t st0[C::STAGE];
@@ -427,6 +497,8 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
   __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGES >= 3 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t st3[STAGES >= 4 ? C::STAGE : 16];
   __shared__ float s_uv[C::BM + C::BN];  // rank-one term: r1 * u over the tile's rows, then v over its columns
+  __shared__ __attribute__((aligned(16))) uint8_t s_mu[MU ? kMuBytes : 16];  // the mean row (MU)
+  __shared__ float s_bias[MU ? WN * TN * 32 : 1];  // the tile's mean term, per column
   static_assert(C::BM + C::BN == C::NT, "one rank-one element per thread");
 
   // This workgroup's logical tiles: a strided run within its XCD's contiguous share of the
@@ -454,6 +526,7 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
       g.b_scales += ((int64_t)gp.e * gin.N / 32) * gsa;
       if (FMT == AVERIS_NVFP4) { g.a_ts += gp.e; g.b_ts += gp.e; }
       if (gin.bias) g.bias += (int64_t)gp.e * gin.N;
+      g.mu_row = gp.e;
       g.c = reinterpret_cast<uint8_t*>(gin.c) + gp.off * gin.ldc * (gin.c_bf16 ? 2 : 4);
     } else if (gin.grouped == 2) {
       const int e = lin / ntiles;
@@ -480,8 +553,11 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
     const int nsteps = (int)((ke - kb) / C::BKE);  // K and k_chunk are multiples of the K-step
     const int kb_byte = (int)(kb / 2), kb_sbyte = (int)(kb / C::BKE) * C::PIECE;
 
+    const int k0 = (int)(kb / C::BKE);  // absolute index of the first K-step
+
     T t;
     t.setup(g, m0, n0);
+    if constexpr (MU) t.issue_mean(g, s_mu);
     // prologue: K-steps 0 .. STAGES-2
     t.issue(kb_byte, kb_sbyte, st0);
     if (STAGES >= 3) t.issue(1 < nsteps ? kb_byte + C::BKB : 0, 1 < nsteps ? kb_sbyte + C::PIECE : 0, st1);
@@ -501,30 +577,39 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
     }
     for (int it = 0; it < nsteps; it += STAGES) {
       if (STAGES == 2) {
-        pipe_step<T, STAGES>(t, it, nsteps, kb_byte, kb_sbyte, st0, st1);
-        pipe_step<T, STAGES>(t, it + 1, nsteps, kb_byte, kb_sbyte, st1, st0);
+        pipe_step<T, STAGES>(t, it, nsteps, kb_byte, kb_sbyte, st0, st1, s_mu, k0);
+        pipe_step<T, STAGES>(t, it + 1, nsteps, kb_byte, kb_sbyte, st1, st0, s_mu, k0);
       } else if (STAGES == 3) {
-        pipe_step<T, STAGES>(t, it, nsteps, kb_byte, kb_sbyte, st0, st2);
-        pipe_step<T, STAGES>(t, it + 1, nsteps, kb_byte, kb_sbyte, st1, st0);
-        pipe_step<T, STAGES>(t, it + 2, nsteps, kb_byte, kb_sbyte, st2, st1);
+        pipe_step<T, STAGES>(t, it, nsteps, kb_byte, kb_sbyte, st0, st2, s_mu, k0);
+        pipe_step<T, STAGES>(t, it + 1, nsteps, kb_byte, kb_sbyte, st1, st0, s_mu, k0);
+        pipe_step<T, STAGES>(t, it + 2, nsteps, kb_byte, kb_sbyte, st2, st1, s_mu, k0);
       } else {
-        pipe_step<T, STAGES>(t, it, nsteps, kb_byte, kb_sbyte, st0, st3);
-        pipe_step<T, STAGES>(t, it + 1, nsteps, kb_byte, kb_sbyte, st1, st0);
-        pipe_step<T, STAGES>(t, it + 2, nsteps, kb_byte, kb_sbyte, st2, st1);
-        pipe_step<T, STAGES>(t, it + 3, nsteps, kb_byte, kb_sbyte, st3, st2);
+        pipe_step<T, STAGES>(t, it, nsteps, kb_byte, kb_sbyte, st0, st3, s_mu, k0);
+        pipe_step<T, STAGES>(t, it + 1, nsteps, kb_byte, kb_sbyte, st1, st0, s_mu, k0);
+        pipe_step<T, STAGES>(t, it + 2, nsteps, kb_byte, kb_sbyte, st2, st1, s_mu, k0);
+        pipe_step<T, STAGES>(t, it + 3, nsteps, kb_byte, kb_sbyte, st3, st2, s_mu, k0);
       }
     }
     wait_vm<0>();                 // no load may still be writing LDS
     __builtin_amdgcn_s_barrier();  // every wave is done reading the stages
 
     // ---- epilogue ----
-    // every wave is past this tile's last barrier, so none still reads the previous tile's s_uv
-    if (hr) {
-      s_uv[threadIdx.x] = uv;
-      lds_barrier();
+    // every wave is past this tile's last barrier, so none still reads the previous tile's
+    // s_uv / s_bias.  MU: row 0 of a wave's mean block (lanes 0 and 32) holds the mean term of
+    // its column block wm; waves (0, wn) and (1, wn) cover the two blocks of columns wn.
+    if constexpr (MU) {
+      if ((threadIdx.x & 31) == 0) {
+        float* sb = s_bias + (t.wn * TN + t.wm) * 32 + 4 * ((threadIdx.x >> 5) & 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sb[8 * q + r] = t.acc_mu[4 * q + r];
+      }
     }
-    epilogue_regs<FMT, TM, TN>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, split, threadIdx.x & 63,
-                               s_uv + t.wm * TM * 32, s_uv + C::BM + t.wn * TN * 32);
+    if (hr) s_uv[threadIdx.x] = uv;
+    if (MU || hr) lds_barrier();
+    epilogue_regs<FMT, TM, TN, MU>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, split, threadIdx.x & 63,
+                                   s_uv + t.wm * TM * 32, s_uv + C::BM + t.wn * TN * 32, s_bias + t.wn * TN * 32);
   }
 }
 
@@ -664,7 +749,14 @@ size_t gemm_grouped_ws_bytes(int64_t M, int64_t N, int64_t E) {
 }
 
 template <int F>
-static void launch_cfg(int cfg, const GemmArgs& g, unsigned grid, hipStream_t s) {
+static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipStream_t s) {
+  if constexpr (F == AVERIS_MXFP4) {
+    if (mu) {
+      if (cfg == KCFG_SHORT) hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 2, 0, true>), dim3(grid), dim3(256), 0, s, g);
+      else hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 3, 0, true>), dim3(grid), dim3(256), 0, s, g);
+      return;
+    }
+  }
   if (cfg == KCFG_SHORT) hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 2>), dim3(grid), dim3(256), 0, s, g);
   else hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 3>), dim3(grid), dim3(256), 0, s, g);
 }
@@ -724,7 +816,14 @@ hipError_t gemm_launch(const GemmPlan& p) {
   g.accumulate = p.accumulate;
   if (M == 0 || N == 0 || E == 0) return hipSuccess;
 
-  if (p.mu) {
+  // mean term: MXFP4 computes it inside the GEMM (one scaled MFMA more per four) while the mean
+  // row fits the tile's LDS copy.  Otherwise, and for NVFP4 (whose bf16 MFMAs on dequantized
+  // fragments would need four more per sixteen, measured 12 % slower), a GEMV writes the
+  // workspace's bias vector, added in the epilogue.
+  const bool mu_in = p.mu && fmt == AVERIS_MXFP4 && K <= kMuMaxK;
+  if (mu_in) {
+    g.mu_codes = p.mu->codes; g.mu_scales = p.mu->scales; g.mu_ts = p.mu->tensor_scale; g.mu_row = 0;
+  } else if (p.mu) {
     const averis_qtensor& U = *p.mu;
     const dim3 blocks((unsigned)ceil_div(N, 4), (unsigned)E);
     if (fmt == AVERIS_MXFP4)
@@ -758,8 +857,8 @@ hipError_t gemm_launch(const GemmPlan& p) {
   // one resident round of workgroups, each looping over its tiles
   g.n_work = (int)work;
   const int64_t grid = std::min<int64_t>(work, (int64_t)resident_per_cu(cfg) * cu_count());
-  if (fmt == AVERIS_MXFP4) launch_cfg<AVERIS_MXFP4>(cfg, g, (unsigned)grid, p.stream);
-  else launch_cfg<AVERIS_NVFP4>(cfg, g, (unsigned)grid, p.stream);
+  if (fmt == AVERIS_MXFP4) launch_cfg<AVERIS_MXFP4>(cfg, mu_in, g, (unsigned)grid, p.stream);
+  else launch_cfg<AVERIS_NVFP4>(cfg, mu_in, g, (unsigned)grid, p.stream);
   if (g.splits > 1) {
     const unsigned blocks = (unsigned)ceil_div(M * (N / 4), 256);
     if (fmt == AVERIS_MXFP4)
