@@ -127,6 +127,10 @@ size_t averis_linear_bwd_dw_workspace_size(int64_t m, int64_t n, int64_t l, int3
   return gemm_ws_bytes(m, n, K, choose_splits(fmt, m, n, K));
 }
 
+// Leading dimensions of GEMM outputs are below 2^23 elements: a wave's 64 output rows then span
+// under 2^31 bytes, the reach of a buffer store's 32-bit offset.
+constexpr int64_t kMaxLd = int64_t(1) << 23;
+
 static int32_t linear_common(const averis_qtensor* a, const averis_qtensor* mu, const averis_qtensor* w, void* out,
                              int32_t odt, int64_t ldo, void* ws, size_t ws_bytes, void* stream) {
   int32_t st;
@@ -142,7 +146,7 @@ static int32_t linear_common(const averis_qtensor* a, const averis_qtensor* mu, 
     if (mu->outer != 1 || mu->k != a->k) return AVERIS_E_SHAPE;
     if ((mu->flags ^ a->flags) & AVERIS_HADAMARD16) return AVERIS_E_FLAGS;
   }
-  if (ldo < w->outer || w->outer % 8 != 0) return AVERIS_E_SHAPE;
+  if (ldo < w->outer || ldo >= kMaxLd || w->outer % 8 != 0) return AVERIS_E_SHAPE;
   if (a->outer > 0 && w->outer > 0) {
     if (!out) return AVERIS_E_NULL;
     if (!aligned16(out) || (ldo * elem_size(odt)) % 16 != 0) return AVERIS_E_ALIGN;
@@ -185,7 +189,7 @@ int32_t averis_linear_bwd_dw(const averis_qtensor* xr_t, const averis_qtensor* d
     if ((mu_x->flags ^ mu_d->flags) & AVERIS_HADAMARD16) return AVERIS_E_FLAGS;
   }
   const int64_t m = xr_t->outer, n = dr_t->outer;
-  if (lddw < n || n % 8 != 0) return AVERIS_E_SHAPE;
+  if (lddw < n || lddw >= kMaxLd || n % 8 != 0) return AVERIS_E_SHAPE;
   if (m > 0 && n > 0) {
     if (!dw) return AVERIS_E_NULL;
     if (!aligned16(dw) || (lddw * 4) % 16 != 0) return AVERIS_E_ALIGN;
@@ -275,7 +279,7 @@ static int32_t linear_grouped_common(const averis_qtensor* a, const averis_qtens
     if (mu->outer != E || mu->k != a->k) return AVERIS_E_SHAPE;
     if ((mu->flags ^ a->flags) & AVERIS_HADAMARD16) return AVERIS_E_FLAGS;
   }
-  if (ldo < N) return AVERIS_E_SHAPE;
+  if (ldo < N || ldo >= kMaxLd) return AVERIS_E_SHAPE;
   if (rows > 0 && N > 0) {
     if (!out) return AVERIS_E_NULL;
     if (!aligned16(out) || (ldo * elem_size(odt)) % 16 != 0) return AVERIS_E_ALIGN;
@@ -328,7 +332,7 @@ int32_t averis_linear_bwd_dw_grouped(const averis_qtensor* xr_t, const averis_qt
     if ((st = check_q(mu_x, E, m, xr_t->fmt, rot)) != AVERIS_OK) return st;
     if ((st = check_q(mu_d, E, n, xr_t->fmt, rot)) != AVERIS_OK) return st;
   }
-  if (lddw < n || n % 8 != 0) return AVERIS_E_SHAPE;
+  if (lddw < n || lddw >= kMaxLd || n % 8 != 0) return AVERIS_E_SHAPE;
   if (m > 0 && n > 0) {
     if (!dw) return AVERIS_E_NULL;
     if (!aligned16(dw) || (lddw * 4) % 16 != 0) return AVERIS_E_ALIGN;

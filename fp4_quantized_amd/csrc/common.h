@@ -28,6 +28,7 @@ static inline int64_t scale_bytes(int64_t outer, int64_t k_pad, int g) { return 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------- element loads ------------

@@ -109,13 +109,20 @@ __device__ inline float dq_one(const uint8_t* codes, const uint8_t* scales, cons
 template <int FMT>
 __device__ inline float mean_value(const MeanVec& mv, int64_t row, int64_t k) {
   if (!mv.rot) return dq_one<FMT>(mv.codes, mv.scales, mv.ts, row, k, mv.k_pad);
+  constexpr int G = FMT == AVERIS_MXFP4 ? 32 : 16;
   const int64_t b = k >> 4;
   const int p = (int)(k & 15);
+  // the block's 16 codes (8 bytes) and the one scale they share, each one load
+  const uint2 cw = *reinterpret_cast<const uint2*>(mv.codes + row * (mv.k_pad / 2) + b * 8);
+  const uint32_t sc = mv.scales[scale_offset(row, b * 16 / G, mv.k_pad, G)];
+  const float ts = FMT == AVERIS_NVFP4 ? mv.ts[row] : 1.0f;
   double s = 0.0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const double v = (double)dq_one<FMT>(mv.codes, mv.scales, mv.ts, row, b * 16 + j, mv.k_pad);
-    s += (__popc(p & j) & 1) ? -v : v;
+    const uint32_t c = ((j < 8 ? cw.x : cw.y) >> (4 * (j & 7))) & 15u;
+    const float e = fp4x2_to_f32(c, 0).x;  // the same per-element decode as dq_one
+    const float v = FMT == AVERIS_MXFP4 ? ldexpf(e, (int)sc - 127) : __fmul_rn(__fmul_rn(e, e4m3_value(sc)), ts);
+    s += (__popc(p & j) & 1) ? -(double)v : (double)v;
   }
   return (float)(s * 0.25);
 }
@@ -185,7 +192,8 @@ struct GemmTile {
   v16f acc[TM][TN];
   v16f acc_mu;            // MU: 32 x 32 block (every row the mean) x this wave's column block wm
 
-  __device__ __forceinline__ void setup(const GemmArgs& g, int64_t m0, int64_t n0) {
+  // Operand views of tile (m0, n0); the accumulators are left alone (clear() resets them).
+  __device__ __forceinline__ void bind(const GemmArgs& g, int64_t m0, int64_t n0) {
     const int lane = threadIdx.x & 63;
     wave = threadIdx.x >> 6; wm = wave / WN; wn = wave % WN;
     const int fr = lane & 31, fk = lane >> 5;
@@ -228,6 +236,8 @@ struct GemmTile {
     scale_off = fr * C::SB + fk * (C::SB / 2);
     mu_off = fk * C::NKK * 16;
     mu_soff = fk * (C::SB / 2);
+  }
+  __device__ __forceinline__ void clear() {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -419,10 +429,21 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
   }
   float alpha = 1.0f;
   if (FMT == AVERIS_NVFP4) alpha = __fmul_rn(g.a_ts[0], g.b_ts[0]);
+  // Output stores (accumulation aside) go through a buffer over this wave's rows: rows past M
+  // lie beyond its range and columns past N get an out-of-range offset, which the hardware
+  // drops (no branches around the stores).
+  const bool acc_in = g.splits == 1 && g.accumulate;
+  const int esz = bf ? 2 : 4;
+  const int64_t ldo = g.splits > 1 ? g.N : g.ldc;
+  uint8_t* obase = g.splits > 1 ? reinterpret_cast<uint8_t*>(g.c) + (((int64_t)split * g.M + rbase) * g.N) * 4
+                                : reinterpret_cast<uint8_t*>(g.c) + rbase * g.ldc * esz;
+  const int64_t nrows = g.M - rbase < TM * 32 ? g.M - rbase : TM * 32;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(obase, nrows > 0 ? (nrows - 1) * ldo * esz + g.N * esz : 0);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int64_t row = rbase + i * 32 + fr;
     const bool row_ok = row < g.M;
+    const int roff = (i * 32 + fr) * (int)(ldo * esz);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       float x[16];
@@ -452,31 +473,32 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
 #pragma unroll
         for (int e = 0; e < 16; ++e) x[e] = __fadd_rn(x[e], __fmul_rn(uu[i], vv[j][e]));
       }
-      if (!row_ok) continue;
       if (bf) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           const int64_t col = cbase + j * 32 + 16 * p + 8 * h;
-          if (col < g.N) {
-            uint4 o;
-            o.x = pack_bf16x2(x[8 * p], x[8 * p + 1]); o.y = pack_bf16x2(x[8 * p + 2], x[8 * p + 3]);
-            o.z = pack_bf16x2(x[8 * p + 4], x[8 * p + 5]); o.w = pack_bf16x2(x[8 * p + 6], x[8 * p + 7]);
-            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(g.c) + row * g.ldc + col) = o;
-          }
+          const v4u o = {pack_bf16x2(x[8 * p], x[8 * p + 1]), pack_bf16x2(x[8 * p + 2], x[8 * p + 3]),
+                         pack_bf16x2(x[8 * p + 4], x[8 * p + 5]), pack_bf16x2(x[8 * p + 6], x[8 * p + 7])};
+          __builtin_amdgcn_raw_buffer_store_b128(o, ro, col < g.N ? roff + (int)col * 2 : 0x7FFFFFF0, 0, 0);
         }
-      } else {
+      } else if (!acc_in) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = cbase + j * 32 + 8 * q + 4 * h;
+          const v4u o = {__float_as_uint(x[4 * q]), __float_as_uint(x[4 * q + 1]), __float_as_uint(x[4 * q + 2]),
+                         __float_as_uint(x[4 * q + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(o, ro, col < g.N ? roff + (int)col * 4 : 0x7FFFFFF0, 0, 0);
+        }
+      } else {  // accumulate into fp32 C
+        if (!row_ok) continue;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t col = cbase + j * 32 + 8 * q + 4 * h;
           if (col >= g.N) continue;
-          float* dst = g.splits > 1 ? reinterpret_cast<float*>(g.c) + (int64_t)split * g.M * g.N + row * g.N + col
-                                    : reinterpret_cast<float*>(g.c) + row * g.ldc + col;
-          float4 o = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
-          if (g.splits == 1 && g.accumulate) {
-            const float4 c = *reinterpret_cast<const float4*>(dst);
-            o.x = __fadd_rn(c.x, o.x); o.y = __fadd_rn(c.y, o.y); o.z = __fadd_rn(c.z, o.z); o.w = __fadd_rn(c.w, o.w);
-          }
-          *reinterpret_cast<float4*>(dst) = o;
+          float* dst = reinterpret_cast<float*>(g.c) + row * g.ldc + col;
+          const float4 c = *reinterpret_cast<const float4*>(dst);
+          *reinterpret_cast<float4*>(dst) = make_float4(__fadd_rn(c.x, x[4 * q]), __fadd_rn(c.y, x[4 * q + 1]),
+                                                        __fadd_rn(c.z, x[4 * q + 2]), __fadd_rn(c.w, x[4 * q + 3]));
         }
       }
     }
@@ -487,6 +509,14 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
 // is held to that occupancy.
 // MU: the launch carries a broadcast mean term, computed by one extra MFMA per wave and substep
 // on the tile's B fragments (every row of that A block is the quantized mean).
+//
+// A workgroup takes a strided run of logical tiles within its XCD's contiguous share of the
+// launch (one tile when the grid covers every tile).  Each tile runs prologue, K loop and
+// epilogue in turn: the epilogue reads no stage memory and every wave has finished with the
+// stages before it starts, so the next tile's prologue may refill them at once.  (The next
+// tile's first loads cannot be issued ahead of the epilogue's stores: loads and stores share
+// one vector-memory counter and may complete out of order, so no wait could single out the
+// loads.)
 template <int FMT, int WM, int WN, int TM, int TN, int STAGES, int AUX = 0, bool MU = false>
 __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1) void k_gemm(GemmArgs gin) {
   using T = GemmTile<FMT, WM, WN, TM, TN, STAGES, AUX, MU>;
@@ -501,12 +531,11 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
   __shared__ float s_bias[MU ? WN * TN * 32 : 1];  // the tile's mean term, per column
   static_assert(C::BM + C::BN == C::NT, "one rank-one element per thread");
 
-  // This workgroup's logical tiles: a strided run within its XCD's contiguous share of the
-  // launch (one tile when the grid covers every tile).  Each tile runs prologue, K loop and
-  // epilogue in turn; the epilogue does not touch LDS, and every wave has finished reading the
-  // stages before it starts, so the next tile's prologue may refill them at once.
   int first, stride, end;
   xcd_tiles((int)blockIdx.x, (int)gridDim.x, gin.n_work, first, stride, end);
+  T t;
+  t.clear();
+  bool mu_loaded = false;
   for (int lin = first; lin < end; lin += stride) {
     GemmArgs g = gin;  // this tile's view (grouped launches retarget it to one group)
     int ntiles = g.tiles_m * g.tiles_n;
@@ -552,12 +581,14 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
     const int64_t ke = kb + g.k_chunk < g.K ? kb + g.k_chunk : g.K;
     const int nsteps = (int)((ke - kb) / C::BKE);  // K and k_chunk are multiples of the K-step
     const int kb_byte = (int)(kb / 2), kb_sbyte = (int)(kb / C::BKE) * C::PIECE;
-
     const int k0 = (int)(kb / C::BKE);  // absolute index of the first K-step
 
-    T t;
-    t.setup(g, m0, n0);
-    if constexpr (MU) t.issue_mean(g, s_mu);
+    t.bind(g, m0, n0);
+    // the mean row: once for a dense launch, per tile for a grouped one (its group's row)
+    if constexpr (MU) {
+      if (!mu_loaded || gin.grouped) t.issue_mean(g, s_mu);
+      mu_loaded = true;
+    }
     // prologue: K-steps 0 .. STAGES-2
     t.issue(kb_byte, kb_sbyte, st0);
     if (STAGES >= 3) t.issue(1 < nsteps ? kb_byte + C::BKB : 0, 1 < nsteps ? kb_sbyte + C::PIECE : 0, st1);
@@ -594,9 +625,9 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
     __builtin_amdgcn_s_barrier();  // every wave is done reading the stages
 
     // ---- epilogue ----
-    // every wave is past this tile's last barrier, so none still reads the previous tile's
-    // s_uv / s_bias.  MU: row 0 of a wave's mean block (lanes 0 and 32) holds the mean term of
-    // its column block wm; waves (0, wn) and (1, wn) cover the two blocks of columns wn.
+    // no wave still reads the previous tile's s_uv / s_bias.  MU: row 0 of a wave's mean block
+    // (lanes 0 and 32) holds the mean term of its column block wm; waves (0, wn) and (1, wn)
+    // cover the two blocks of columns wn.
     if constexpr (MU) {
       if ((threadIdx.x & 31) == 0) {
         float* sb = s_bias + (t.wn * TN + t.wm) * 32 + 4 * ((threadIdx.x >> 5) & 1);
@@ -610,6 +641,7 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
     if (MU || hr) lds_barrier();
     epilogue_regs<FMT, TM, TN, MU>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, split, threadIdx.x & 63,
                                    s_uv + t.wm * TM * 32, s_uv + C::BM + t.wn * TN * 32, s_bias + t.wn * TN * 32);
+    t.clear();
   }
 }
 

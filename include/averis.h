@@ -144,7 +144,7 @@ int32_t averis_split_quant(const void *x, int32_t xdt, int64_t rows, int64_t col
  *  xr    [outer = l, k = m]  (q_row of split_quant(X))
  *  mu_x  [outer = 1, k = m]  (q_mean of split_quant(X)), or NULL for the vanilla GEMM
  *  w     [outer = n, k = m]  (q_col of split_quant(W [m, n]) without SPLIT)
- *  y     device [l, n] row-major, element type ydt, leading dimension ldy >= n; n % 8 == 0.
+ *  y     device [l, n] row-major, element type ydt, leading dimension n <= ldy < 2^23; n % 8 == 0.
  * All operands share fmt and the HADAMARD16 bit.  The mean term is
  * computed once per call as a GEMV and added to every row in the GEMM epilogue.
  * ----------------------------------------------------------------------------------------- */
@@ -159,7 +159,7 @@ int32_t averis_linear_fwd(const averis_qtensor *xr, const averis_qtensor *mu_x,
  *  dr    [outer = l, k = n]  (q_row of split_quant(D))
  *  mu_d  [outer = 1, k = n]  or NULL (vanilla)
  *  w     [outer = m, k = n]  (q_row of split_quant(W [m, n]) without SPLIT)
- *  dx    device [l, m], element type dxdt, leading dimension lddx >= m; m % 8 == 0.
+ *  dx    device [l, m], element type dxdt, leading dimension m <= lddx < 2^23; m % 8 == 0.
  * ----------------------------------------------------------------------------------------- */
 int32_t averis_linear_bwd_dx(const averis_qtensor *dr, const averis_qtensor *mu_d,
                              const averis_qtensor *w, void *dx, int32_t dxdt, int64_t lddx,
@@ -174,7 +174,7 @@ int32_t averis_linear_bwd_dx(const averis_qtensor *dr, const averis_qtensor *mu_
  *  mu_x, mu_d  quantized means, both or neither (NULL, NULL = vanilla: no rank-one term).
  *        If they carry HADAMARD16 the rotation is undone before the outer product.
  *  l     the unpadded token count (the rank-one factor); must equal xr_t->k.
- *  dw    device fp32 [m, n], leading dimension lddw >= n; n % 8 == 0.  AVERIS_ACCUMULATE: dw += result.
+ *  dw    device fp32 [m, n], leading dimension n <= lddw < 2^23; n % 8 == 0.  AVERIS_ACCUMULATE: dw += result.
  * The token axis is split across workgroups with fp32 partials reduced in a fixed order.
  * ----------------------------------------------------------------------------------------- */
 size_t averis_linear_bwd_dw_workspace_size(int64_t m, int64_t n, int64_t l, int32_t fmt);
@@ -225,7 +225,7 @@ size_t averis_linear_grouped_workspace_size(int64_t N, int32_t E, int32_t fmt);
 /* Per group e: Y[offsets[e] + r] = 1 (Q(mu_X,e) Q(W_e)) + Q(X_R,e) Q(W_e), one launch for all
  * groups.  xr: grouped row layout [sum round_up(l_e, 32), m]; mu_x: [E, m] or NULL; w: E stacked
  * [n, m] operands (outer = E * n, n % 32 == 0; the column layout of the stacked weights).
- * y: device [L, n], element type ydt, leading dimension ldy >= n. */
+ * y: device [L, n], element type ydt, leading dimension n <= ldy < 2^23. */
 int32_t averis_linear_fwd_grouped(const averis_qtensor *xr, const averis_qtensor *mu_x,
                                   const averis_qtensor *w, const int64_t *d_offsets,
                                   const int64_t *h_offsets, int32_t E, void *y, int32_t ydt,

@@ -105,8 +105,8 @@ def lin(fn, a, mu, w, out=FAKE, odt=av.F32, ldo=None, ws=FAKE, wsb=1 << 30):
 
 @pytest.mark.parametrize("case,status", [
     ("mixed_fmt", E_FORMAT), ("k_mismatch", E_SHAPE), ("rot_mismatch", E_FLAGS), ("mu_shape", E_SHAPE),
-    ("bad_dtype", E_DTYPE), ("small_ld", E_SHAPE), ("null_out", E_NULL), ("no_ws", E_WORKSPACE),
-    ("bad_kpad", E_SHAPE),
+    ("bad_dtype", E_DTYPE), ("small_ld", E_SHAPE), ("huge_ld", E_SHAPE), ("null_out", E_NULL),
+    ("no_ws", E_WORKSPACE), ("bad_kpad", E_SHAPE),
 ])
 def test_linear_rejects(case, status):
     L = av.lib()
@@ -124,6 +124,8 @@ def test_linear_rejects(case, status):
         kw["odt"] = 9
     elif case == "small_ld":
         kw["ldo"] = 100
+    elif case == "huge_ld":
+        kw["ldo"] = 1 << 23  # output offsets of a wave's 64 rows must stay below 2^31 bytes
     elif case == "null_out":
         kw["out"] = None
     elif case == "no_ws":
@@ -146,6 +148,7 @@ def test_bwd_dw_rejects():
     assert call(md=None) == E_NULL
     assert call(mx=q(1, 500)) == E_SHAPE
     assert call(ld=100) == E_SHAPE
+    assert call(ld=1 << 23) == E_SHAPE
     assert call(dw=None) == E_NULL
     assert call(wsb=100) == E_WORKSPACE
     assert call(dr=q(384, 300, av.MXFP4)) == E_FORMAT
