@@ -529,7 +529,7 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
   __shared__ float s_uv[C::BM + C::BN];  // rank-one term: r1 * u over the tile's rows, then v over its columns
   __shared__ __attribute__((aligned(16))) uint8_t s_mu[MU ? kMuBytes : 16];  // the mean row (MU)
   __shared__ float s_bias[MU ? WN * TN * 32 : 1];  // the tile's mean term, per column
-  static_assert(C::BM + C::BN == C::NT, "one rank-one element per thread");
+  static_assert(C::BM + C::BN <= C::NT, "one rank-one element per thread");
 
   int first, stride, end;
   xcd_tiles((int)blockIdx.x, (int)gridDim.x, gin.n_work, first, stride, end);
@@ -596,7 +596,7 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
     // this thread's rank-one element (loads overlap the prologue; used in the epilogue)
     const bool hr = g.splits == 1 && g.has_r1;
     float uv = 0.0f;
-    if (hr) {
+    if (hr && (int)threadIdx.x < C::BM + C::BN) {
       const int i = threadIdx.x;
       if (i < C::BM) {
         const int64_t row = m0 + i;
@@ -637,7 +637,7 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
           for (int r = 0; r < 4; ++r) sb[8 * q + r] = t.acc_mu[4 * q + r];
       }
     }
-    if (hr) s_uv[threadIdx.x] = uv;
+    if (hr && (int)threadIdx.x < C::BM + C::BN) s_uv[threadIdx.x] = uv;
     if (MU || hr) lds_barrier();
     epilogue_regs<FMT, TM, TN, MU>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, split, threadIdx.x & 63,
                                    s_uv + t.wm * TM * 32, s_uv + C::BM + t.wn * TN * 32, s_bias + t.wn * TN * 32);
@@ -738,8 +738,9 @@ __global__ __launch_bounds__(256) void k_gemv_mean(const uint8_t* __restrict__ m
 static int g_count(int fmt) { return fmt == AVERIS_MXFP4 ? 32 : 16; }
 
 // Two tile configurations, both 128 x 128 tiles of 2 x 2 waves with 2 x 2 MFMA tiles each
-// (measured on MI355X against 256 x 128, 128 x 256, 256 x 192 and 256 x 256 tiles at the
-// Qwen3-0.6B-shaped linears; 128 x 128 was fastest at every shape):
+// (measured on MI355X against 256 x 128 (4 and 8 waves), 128 x 256, 256 x 192 and 256 x 256
+// tiles, and against 128-element K-steps with 3 and 4 stages, at the Qwen3-0.6B-shaped
+// linears; this one was fastest at every shape):
 //   KCFG_SHORT  two LDS stages, two workgroups per CU (70 KB LDS, <= 256 VGPRs each), for
 //               short K (forward and input-gradient GEMMs over the feature dimension);
 //   KCFG_LONG   three stages, one workgroup per CU, deeper prefetch, for long K (weight
@@ -784,8 +785,8 @@ template <int F>
 static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipStream_t s) {
   if constexpr (F == AVERIS_MXFP4) {
     if (mu) {
-      if (cfg == KCFG_SHORT) hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 2, 0, true>), dim3(grid), dim3(256), 0, s, g);
-      else hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 3, 0, true>), dim3(grid), dim3(256), 0, s, g);
+      if (cfg == KCFG_LONG) hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 3, 0, true>), dim3(grid), dim3(256), 0, s, g);
+      else hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 2, 0, true>), dim3(grid), dim3(256), 0, s, g);
       return;
     }
   }
@@ -832,6 +833,8 @@ hipError_t gemm_launch(const GemmPlan& p) {
   g.a_ts = A.tensor_scale; g.b_ts = B.tensor_scale;
   g.M = M; g.N = N; g.K = K;
   g.offsets = p.d_offsets; g.E = (int)E; g.grouped = p.grouped;
+  // mean term inside the GEMM: MXFP4 while the mean row fits the tile's LDS copy (see below)
+  const bool mu_in = p.mu && fmt == AVERIS_MXFP4 && K <= kMuMaxK;
   const int cfg = p.grouped == 2 ? KCFG_LONG : pick_cfg(K);  // grouped dW: long, varying K
   const TileCfg tc = tile_of(cfg);
   g.tiles_m = (int)ceil_div(M, tc.bm); g.tiles_n = (int)ceil_div(N, tc.bn);
@@ -852,7 +855,6 @@ hipError_t gemm_launch(const GemmPlan& p) {
   // row fits the tile's LDS copy.  Otherwise, and for NVFP4 (whose bf16 MFMAs on dequantized
   // fragments would need four more per sixteen, measured 12 % slower), a GEMV writes the
   // workspace's bias vector, added in the epilogue.
-  const bool mu_in = p.mu && fmt == AVERIS_MXFP4 && K <= kMuMaxK;
   if (mu_in) {
     g.mu_codes = p.mu->codes; g.mu_scales = p.mu->scales; g.mu_ts = p.mu->tensor_scale; g.mu_row = 0;
   } else if (p.mu) {
