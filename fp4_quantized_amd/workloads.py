@@ -130,7 +130,8 @@ def sweep_device(seed=3, l=16384, device="cuda"):
     """The seven sweep linears drawn directly on the device, for timing: the up_proj_like recipe
     (X = bf16(1 mu^T + R), R ~ Student-t(4) as Z / sqrt(V / 4) with V ~ chi2(4); D = bf16(1 mu_D^T
     + N(0, 1e-6)); W ~ N(0, 0.02^2)) from torch's generator seeded with `seed`.  The values are
-    not those of `sweep` (a different generator); parity tests use the numpy draws.
+    not those of `sweep` (a different generator); the full-size sweep parity test copies these
+    draws to the oracle.
     Returns [(name, x, d, w)] of bf16 tensors, x [l, m], d [l, n], w [m, n]."""
     import torch
     gen = torch.Generator(device=device)
