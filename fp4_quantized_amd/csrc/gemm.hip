@@ -9,9 +9,10 @@
 //   MXFP4: v_mfma_scale_f32_32x32x64_f8f6f4 consumes the codes and the E8M0 block scales
 //          directly; a lane holds one row and 32 K elements (= one MX block) per instruction.
 //   NVFP4: E4M3 scales are not powers of two, which the scaled MFMA cannot apply (it uses only
-//          a scale's exponent), so each lane dequantizes its 32 codes exactly to bf16 (code x
-//          E4M3 value has <= 6 significant bits) and issues four v_mfma_f32_32x32x16_bf16; the
-//          fp32 tensor scales multiply the accumulator in the epilogue.
+//          a scale's exponent), so each lane dequantizes its 32 codes exactly to f16 (code x
+//          E4M3 value has <= 6 significant bits; one conversion and one packed multiply per two
+//          codes) and issues four v_mfma_f32_32x32x16_f16; the fp32 tensor scales multiply the
+//          accumulator in the epilogue.
 // K order inside a K-step is permuted (the same way for A and B, so products pair up): lane
 // half h takes the step's 32-element chunks h*S .. h*S+S-1 for its S MFMAs, which makes its
 // block scales for the whole step one contiguous LDS load.
@@ -71,20 +72,37 @@ __device__ inline float2 fp4x2_to_f32(uint32_t w, int sel) {
   }
 }
 
-// 32 E2M1 codes (16 bytes) times two block scales (elements 0-15: s0, 16-31: s1) -> 4 x 8 bf16.
-__device__ inline void dequant32_bf16(const uint4& c, float s0, float s1, v8bf* out) {
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// The gfx950 conversions below apply only the power-of-two part of their scale operand, so they
+// run with scale 1.0 and stay exact: E2M1 codes and E4M3 scales are all f16 values.
+__device__ inline v2h fp4x2_to_f16(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  }
+}
+// The two E4M3 scale bytes in the low (hi = 0) or high 16 bits of w, as f16.
+__device__ inline v2h e4m3x2_to_f16(uint32_t w, int hi) {
+  return hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+            : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+}
+
+// 32 E2M1 codes (16 bytes) times two block scales (elements 0-15: sc.x, 16-31: sc.y) -> 4 x 8
+// f16.  A code has at most 2 significant bits and an E4M3 value at most 4, so each product (one
+// packed f16 multiply per two codes) is exact: magnitudes lie in [2^-10, 2688], all normal f16.
+__device__ inline void dequant32_f16(const uint4& c, v2h sc, v8h* out) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float s = q < 2 ? s0 : s1;
-    uint32_t h[4];
+    const v2h s = q < 2 ? v2h{sc.x, sc.x} : v2h{sc.y, sc.y};
+    v2h h[4];
 #pragma unroll
-    for (int bsel = 0; bsel < 4; ++bsel) {
-      const float2 f = fp4x2_to_f32(w[q], bsel);
-      // exact products, so dropping the low 16 bits is an exact bf16 conversion
-      h[bsel] = (__float_as_uint(f.x * s) >> 16) | (__float_as_uint(f.y * s) & 0xFFFF0000u);
-    }
-    out[q] = __builtin_bit_cast(v8bf, make_uint4(h[0], h[1], h[2], h[3]));
+    for (int bsel = 0; bsel < 4; ++bsel) h[bsel] = fp4x2_to_f16(w[q], bsel) * s;
+    out[q] = v8h{h[0].x, h[0].y, h[1].x, h[1].y, h[2].x, h[2].y, h[3].x, h[3].y};
   }
 }
 
@@ -325,33 +343,26 @@ struct GemmTile {
               (int)__builtin_amdgcn_ubfe(msc[0], 8 * kk, 8));
         }
       } else {
-        v8bf da[TM][4], db[TN][4];
-        const int wsel = kk / 2, sh = 16 * (kk % 2);  // two scale bytes per chunk
+        v8h da[TM][4], db[TN][4];
+        const int wsel = kk / 2, hi = kk % 2;  // two scale bytes per chunk
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const uint32_t w = sa[i][wsel];
-          dequant32_bf16(fa[i], e4m3_value((w >> sh) & 255u), e4m3_value((w >> (sh + 8)) & 255u), da[i]);
-        }
+        for (int i = 0; i < TM; ++i) dequant32_f16(fa[i], e4m3x2_to_f16(sa[i][wsel], hi), da[i]);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const uint32_t w = sb[j][wsel];
-          dequant32_bf16(fb[j], e4m3_value((w >> sh) & 255u), e4m3_value((w >> (sh + 8)) & 255u), db[j]);
-        }
+        for (int j = 0; j < TN; ++j) dequant32_f16(fb[j], e4m3x2_to_f16(sb[j][wsel], hi), db[j]);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(db[j][q], da[i][q], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(db[j][q], da[i][q], acc[i][j], 0, 0, 0);
         if constexpr (MU) {
           const uint4 fm = *reinterpret_cast<const uint4*>(smu + kstep * C::BKB + mu_off + kk * 16);
-          v8bf dm[4];
-          const uint32_t w = msc[wsel];
-          dequant32_bf16(fm, e4m3_value((w >> sh) & 255u), e4m3_value((w >> (sh + 8)) & 255u), dm);
+          v8h dm[4];
+          dequant32_f16(fm, e4m3x2_to_f16(msc[wsel], hi), dm);
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            acc_mu = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wm ? db[TN - 1][q] : db[0][q], dm[q], acc_mu, 0, 0, 0);
+            acc_mu = __builtin_amdgcn_mfma_f32_32x32x16_f16(wm ? db[TN - 1][q] : db[0][q], dm[q], acc_mu, 0, 0, 0);
         }
       }
     }
@@ -852,7 +863,7 @@ hipError_t gemm_launch(const GemmPlan& p) {
   if (M == 0 || N == 0 || E == 0) return hipSuccess;
 
   // mean term: MXFP4 computes it inside the GEMM (one scaled MFMA more per four) while the mean
-  // row fits the tile's LDS copy.  Otherwise, and for NVFP4 (whose bf16 MFMAs on dequantized
+  // row fits the tile's LDS copy.  Otherwise, and for NVFP4 (whose f16 MFMAs on dequantized
   // fragments would need four more per sixteen, measured 12 % slower), a GEMV writes the
   // workspace's bias vector, added in the epilogue.
   if (mu_in) {
