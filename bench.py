@@ -158,10 +158,18 @@ def main():
 
     launch_s = timed(gemm_pairs, args.steps, args.warmup) * 1e-3 / (2 * REPS)
     achieved = 2.0 * l * m * n / launch_s / 1e12
+    # the binding roofline of each launch: max(MFMA time, HBM time of its algorithmic bytes:
+    # both packed operands read once, the bf16 output written once), averaged over the pair
+    op = 0.5 + 1.0 / 32
+    t_mfma = 2.0 * l * m * n / (PEAK_FP4_TFLOPS * 1e12)
+    t_hbm = [((l * m + n * m) * op + 2 * l * n) / (PEAK_HBM_GBPS * 1e9),   # Y [l, n]
+             ((l * n + m * n) * op + 2 * l * m) / (PEAK_HBM_GBPS * 1e9)]   # dX [l, m]
+    t_bind = sum(max(t_mfma, t) for t in t_hbm) / 2
     roofline = {"bound": "mfma", "kernel": "k_gemm<MXFP4> (forward and input-gradient GEMMs)",
                 "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_FP4_TFLOPS, 4), "traffic": gemm_traffic(),
-                "traffic_unit": "bytes per launch (HBM, counter runs)", "launch_us": round(launch_s * 1e6, 2)}
+                "traffic_unit": "bytes per launch (HBM, counter runs)", "launch_us": round(launch_s * 1e6, 2),
+                "binding_roofline_us": round(t_bind * 1e6, 2), "frac_of_binding": round(t_bind / launch_s, 4)}
     del st
 
     cpu = None
