@@ -165,7 +165,7 @@ def main():
     t_hbm = [((l * m + n * m) * op + 2 * l * n) / (PEAK_HBM_GBPS * 1e9),   # Y [l, n]
              ((l * n + m * n) * op + 2 * l * m) / (PEAK_HBM_GBPS * 1e9)]   # dX [l, m]
     t_bind = sum(max(t_mfma, t) for t in t_hbm) / 2
-    roofline = {"bound": "mfma", "kernel": "k_gemm<MXFP4> (forward and input-gradient GEMMs)",
+    roofline = {"bound": "mfma", "kernel": "k_gemm_ws<MXFP4> (forward and input-gradient GEMMs)",
                 "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_FP4_TFLOPS, 4), "traffic": gemm_traffic(),
                 "traffic_unit": "bytes per launch (HBM, counter runs)", "launch_us": round(launch_s * 1e6, 2),

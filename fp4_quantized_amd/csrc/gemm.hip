@@ -211,9 +211,12 @@ struct GemmTile {
   v16f acc_mu;            // MU: 32 x 32 block (every row the mean) x this wave's column block wm
 
   // Operand views of tile (m0, n0); the accumulators are left alone (clear() resets them).
-  __device__ __forceinline__ void bind(const GemmArgs& g, int64_t m0, int64_t n0) {
+  // as_wave >= 0: the views of wave as_wave's share of the loads (a loader wave issuing them).
+  __device__ __forceinline__ void bind(const GemmArgs& g, int64_t m0, int64_t n0, int as_wave = -1) {
     const int lane = threadIdx.x & 63;
-    wave = threadIdx.x >> 6; wm = wave / WN; wn = wave % WN;
+    // wave-uniform, and known to be: the epilogue's buffer resources then stay scalar
+    wave = as_wave >= 0 ? as_wave : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    wm = wave / WN; wn = wave % WN;
     const int fr = lane & 31, fk = lane >> 5;
     // operands restricted to this tile's rows: offsets past the last row read as zero
     const int64_t rows_a = g.M - m0 < C::BM ? g.M - m0 : C::BM, rows_b = g.N - n0 < C::BN ? g.N - n0 : C::BN;
@@ -398,7 +401,9 @@ __device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt((15) |
 // sv: its columns).
 //   out = alpha * acc (+ bias[col]) (+ r1 * u[row] * v[col]) (+ C when accumulating), each step
 //   rounded once in fp32; split-K partials get alpha * acc only.
-template <int FMT, int TM, int TN, bool MU>
+// ALL = false: the launch has no bias vector, rank-one term or accumulation (the epilogue then
+// issues no global loads).
+template <int FMT, int TM, int TN, bool MU, bool ALL = true>
 __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&acc)[TM][TN], int64_t rbase,
                                               int64_t cbase, int split, int lane, const float* su, const float* sv,
                                               const float* sbias) {
@@ -407,7 +412,7 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
   const bool terms = g.splits == 1;
   // mean term: from the tile's MFMAs (MU; split-K partials carry their share) or a precomputed
   // bias vector (dense launches without MU)
-  const bool hb = MU || (terms && g.bias), hr = terms && g.has_r1;
+  const bool hb = MU || (ALL && terms && g.bias), hr = ALL && terms && g.has_r1;
   float alpha_mu = 1.0f;
   if (FMT == AVERIS_NVFP4 && MU) alpha_mu = __fmul_rn(g.mu_ts[g.mu_row], g.b_ts[0]);
   // this lane's columns: bf16 -> j*32 + 16p + 8h + (0..7); fp32 -> j*32 + 8q + 4h + (0..3)
@@ -443,7 +448,7 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
   // Output stores (accumulation aside) go through a buffer over this wave's rows: rows past M
   // lie beyond its range and columns past N get an out-of-range offset, which the hardware
   // drops (no branches around the stores).
-  const bool acc_in = g.splits == 1 && g.accumulate;
+  const bool acc_in = ALL && g.splits == 1 && g.accumulate;
   const int esz = bf ? 2 : 4;
   const int64_t ldo = g.splits > 1 ? g.N : g.ldc;
   uint8_t* obase = g.splits > 1 ? reinterpret_cast<uint8_t*>(g.c) + (((int64_t)split * g.M + rbase) * g.N) * 4
@@ -656,6 +661,112 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
   }
 }
 
+// Warp-specialized form of the 128 x 128 tile for dense single-split launches whose epilogue
+// issues no global loads (no bias vector, rank-one term or accumulation): waves 0-3 multiply and
+// store, waves 4 .. 4+L-1 issue every operand load (loader l takes the shares of waves l, l+L, ..).
+// A workgroup's K-steps form one stream across its tiles (all tiles have nsteps = K / 256 steps);
+// global step q lives in ring stage q % S.  The loaders keep S - 1 steps in flight, crossing tile
+// boundaries, and since their waits count only their own loads (no stores, no other waves'
+// operations) a counted vmcnt singles out the oldest step: loads complete in order.
+// Barrier sequence, the same for every wave: one barrier per K-step (a loader first waits until
+// its loads of that step have landed; after the barrier stage (q - 1) % S is free, its last reader
+// being step q - 1, and it refills it with step q + S - 1), plus one epilogue barrier per tile with
+// the mean term.  Steps past the stream's end re-load the last tile's first step into the stage
+// just freed, which nobody reads again, so every wait covers the same number of loads.
+template <int FMT, bool MU, int S, int L>
+__global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
+  constexpr int WM = 2, WN = 2, TM = 2, TN = 2;
+  using T = GemmTile<FMT, WM, WN, TM, TN, 2, 0, MU>;
+  using C = typename T::C;
+  constexpr int SSZ = (C::STAGE + 1023) / 1024 * 1024;
+  constexpr int SH = C::NW / L;                  // shares per loader wave
+  constexpr int LPW = C::LPS * SH;               // loads per loader wave per K-step
+  static_assert(C::NW % L == 0 && LPW * (S - 2) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[S * SSZ];
+  __shared__ __attribute__((aligned(16))) uint8_t s_mu[MU ? kMuBytes : 16];
+  __shared__ float s_bias[MU ? WN * TN * 32 : 1];
+
+  int first, stride, end;
+  xcd_tiles((int)blockIdx.x, (int)gridDim.x, g.n_work, first, stride, end);
+  if (first >= end) return;
+  const int nsteps = (int)(g.K / C::BKE);       // >= 1, the same for every tile
+  const int ntw = (end - first + stride - 1) / stride;  // this workgroup's tiles
+  const int total = ntw * nsteps;               // its K-steps
+  auto origin = [&](int ti, int64_t& m0, int64_t& n0) {
+    int tm, tn;
+    tile_coords(first + ti * stride, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+    m0 = (int64_t)tm * C::BM;
+    n0 = (int64_t)tn * C::BN;
+  };
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+
+  if (wave >= C::NW) {
+    // ---- loader wave l ----
+    const int l = wave - C::NW;
+    T lt[SH];
+    int bound = 0;  // tile whose views lt holds
+    int64_t m0, n0;
+    origin(0, m0, n0);
+#pragma unroll
+    for (int i = 0; i < SH; ++i) lt[i].bind(g, m0, n0, l + i * L);
+    if constexpr (MU) {
+#pragma unroll
+      for (int i = 0; i < SH; ++i) lt[i].issue_mean(g, s_mu);
+    }
+    auto issue = [&](int q) {  // global step q into stage q % S
+      int st = 0;
+      if (q < total) {
+        const int ti = q / nsteps;
+        st = q - ti * nsteps;
+        if (ti != bound) {
+          bound = ti;
+          origin(ti, m0, n0);
+#pragma unroll
+          for (int i = 0; i < SH; ++i) lt[i].bind(g, m0, n0, l + i * L);
+        }
+      }
+      uint8_t* stg = ring + (q % S) * SSZ;
+#pragma unroll
+      for (int i = 0; i < SH; ++i) lt[i].issue(st * C::BKB, st * C::PIECE, stg);
+    };
+    for (int q = 0; q < S - 1; ++q) issue(q);
+    for (int q = 0; q < total; ++q) {
+      wait_vm<LPW * (S - 2)>();
+      __builtin_amdgcn_s_barrier();
+      issue(q + S - 1);
+      if (MU && q % nsteps == nsteps - 1) __builtin_amdgcn_s_barrier();  // the epilogue barrier
+    }
+    wait_vm<0>();  // the trailing re-loads land before the workgroup ends
+    return;
+  }
+
+  // ---- multiplying waves ----
+  T t;
+  t.bind(g, 0, 0);  // lane constants (this wave loads nothing)
+  int q = 0;
+  for (int ti = 0; ti < ntw; ++ti) {
+    int64_t m0, n0;
+    origin(ti, m0, n0);
+    t.clear();
+    for (int st = 0; st < nsteps; ++st, ++q) {
+      __builtin_amdgcn_s_barrier();
+      t.compute(ring + (q % S) * SSZ, s_mu, st);
+    }
+    if constexpr (MU) {
+      if ((threadIdx.x & 31) == 0) {
+        float* sb = s_bias + (t.wn * TN + t.wm) * 32 + 4 * ((threadIdx.x >> 5) & 1);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sb[8 * qq + r] = t.acc_mu[4 * qq + r];
+      }
+      lds_barrier();
+    }
+    epilogue_regs<FMT, TM, TN, MU, false>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, 0,
+                                          threadIdx.x & 63, nullptr, nullptr, s_bias + t.wn * TN * 32);
+  }
+}
+
 // Split-K reduce: C = (accumulate ? C : 0) + (sum_s P[s] in split order + bias[col]
 // + r1 * u[row] * v[col]), four columns per thread (N % 8 == 0); fp32 or bf16 output; u and v
 // dequantized from the quantized means in place.
@@ -748,19 +859,25 @@ __global__ __launch_bounds__(256) void k_gemv_mean(const uint8_t* __restrict__ m
 // ------------------------------------------------------------------------------------------
 static int g_count(int fmt) { return fmt == AVERIS_MXFP4 ? 32 : 16; }
 
-// Two tile configurations, both 128 x 128 tiles of 2 x 2 waves with 2 x 2 MFMA tiles each
+// Three configurations of 128 x 128 tiles, 2 x 2 multiplying waves with 2 x 2 MFMA tiles each
 // (measured on MI355X against 256 x 128 (4 and 8 waves), 128 x 256, 256 x 192 and 256 x 256
-// tiles, and against 128-element K-steps with 3 and 4 stages, at the Qwen3-0.6B-shaped
-// linears; this one was fastest at every shape):
-//   KCFG_SHORT  two LDS stages, two workgroups per CU (70 KB LDS, <= 256 VGPRs each), for
-//               short K (forward and input-gradient GEMMs over the feature dimension);
+// tiles, and against 128-element K-steps with 3 and 4 stages, at the Qwen3-0.6B-shaped linears):
+//   KCFG_WS     warp-specialized (k_gemm_ws): two loader waves keep three K-steps of a 4-stage
+//               ring in flight across tiles, one workgroup per CU; short-K MXFP4 dense launches
+//               (forward and input-gradient GEMMs over the feature dimension), 8-16 % faster
+//               than KCFG_SHORT there;
+//   KCFG_SHORT  two LDS stages, two workgroups per CU (70 KB LDS, <= 256 VGPRs each): the other
+//               short-K launches (NVFP4, grouped, split-K, accumulate, rank-one term);
 //   KCFG_LONG   three stages, one workgroup per CU, deeper prefetch, for long K (weight
 //               gradients over the token dimension).
-constexpr int KCFG_LONG = 0, KCFG_SHORT = 1;
+constexpr int KCFG_LONG = 0, KCFG_SHORT = 1, KCFG_WS = 2;
+constexpr int kWsStages = 4, kWsLoaders = 2;  // warp-specialized kernel: ring depth, loader waves
 struct TileCfg { int bm, bn; };
 static TileCfg tile_of(int) { return {128, 128}; }
 constexpr int kBKE = 256;
-static int pick_cfg(int64_t K) { return K >= 4096 ? KCFG_LONG : KCFG_SHORT; }
+// Short K: the warp-specialized kernel (MXFP4 dense launches; the rest fall back to the two-stage
+// kernel below).  Long K: three stages, one workgroup per CU.
+static int pick_cfg(int64_t K) { return K >= 4096 ? KCFG_LONG : KCFG_WS; }
 
 static int splits_for(int cfg, int64_t M, int64_t N, int64_t K) {
   const TileCfg tc = tile_of(cfg);
@@ -795,6 +912,14 @@ size_t gemm_grouped_ws_bytes(int64_t M, int64_t N, int64_t E) {
 template <int F>
 static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipStream_t s) {
   if constexpr (F == AVERIS_MXFP4) {
+    if (cfg == KCFG_WS) {
+      constexpr int S = kWsStages, L = kWsLoaders;
+      if (mu) hipLaunchKernelGGL((k_gemm_ws<F, true, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+      else hipLaunchKernelGGL((k_gemm_ws<F, false, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+      return;
+    }
+  }
+  if constexpr (F == AVERIS_MXFP4) {
     if (mu) {
       if (cfg == KCFG_LONG) hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 3, 0, true>), dim3(grid), dim3(256), 0, s, g);
       else hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 2, 0, true>), dim3(grid), dim3(256), 0, s, g);
@@ -805,7 +930,7 @@ static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipSt
   else hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 3>), dim3(grid), dim3(256), 0, s, g);
 }
 // Workgroups resident per CU: two for the two-stage configuration, one for the three-stage one
-// (105 KB of LDS).
+// (105 KB of LDS) and for the warp-specialized one (a 4 x 35 KB ring).
 static int resident_per_cu(int cfg) { return cfg == KCFG_SHORT ? 2 : 1; }
 static int cu_count() {
   static int cached[64] = {};  // per device id
@@ -846,7 +971,12 @@ hipError_t gemm_launch(const GemmPlan& p) {
   g.offsets = p.d_offsets; g.E = (int)E; g.grouped = p.grouped;
   // mean term inside the GEMM: MXFP4 while the mean row fits the tile's LDS copy (see below)
   const bool mu_in = p.mu && fmt == AVERIS_MXFP4 && K <= kMuMaxK;
-  const int cfg = p.grouped == 2 ? KCFG_LONG : pick_cfg(K);  // grouped dW: long, varying K
+  int cfg = p.grouped == 2 ? KCFG_LONG : pick_cfg(K);  // grouped dW: long, varying K
+  // the warp-specialized kernel: MXFP4 dense single-split launches with K > 0 whose epilogue
+  // issues no global loads (every tile then has the same nonzero number of K-steps)
+  if (cfg == KCFG_WS && (fmt != AVERIS_MXFP4 || p.grouped || p.accumulate || p.mu_u || (p.mu && !mu_in) ||
+                         p.splits > 1 || K == 0))
+    cfg = KCFG_SHORT;
   const TileCfg tc = tile_of(cfg);
   g.tiles_m = (int)ceil_div(M, tc.bm); g.tiles_n = (int)ceil_div(N, tc.bn);
   if (p.grouped == 1)
