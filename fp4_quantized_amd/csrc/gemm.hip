@@ -19,6 +19,8 @@
 // Pipeline: operands go straight from global memory to LDS (gfx950 global_load_lds) into a
 // ring of stages; while K-step i is multiplied, steps i+1 .. i+STAGES-1 are in flight.  One
 // barrier per K-step, no fence: each wave waits on its own vmcnt, then all meet at s_barrier.
+// MXFP4 dense launches use a warp-specialized form (k_gemm_ws): loader waves keep a 4-stage ring
+// filled across tile boundaries while the multiplying waves only multiply and store.
 // Epilogue: out = alpha * acc + bias[col] + r1 * u[row] * v[col] (+ C when accumulating),
 // alpha = product of the operands' tensor decode scales (NVFP4) or 1.
 #include <algorithm>
@@ -673,7 +675,9 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
 // being step q - 1, and it refills it with step q + S - 1), plus one epilogue barrier per tile with
 // the mean term.  Steps past the stream's end re-load the last tile's first step into the stage
 // just freed, which nobody reads again, so every wait covers the same number of loads.
-template <int FMT, bool MU, int S, int L>
+// R1: the launch has the weight gradient's rank-one term: the multiplying waves dequantize u and v
+// for each tile before its K-steps (their only global loads) and add r1 u v^T in the epilogue.
+template <int FMT, bool MU, bool R1, int S, int L>
 __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
   constexpr int WM = 2, WN = 2, TM = 2, TN = 2;
   using T = GemmTile<FMT, WM, WN, TM, TN, 2, 0, MU>;
@@ -685,16 +689,21 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S * SSZ];
   __shared__ __attribute__((aligned(16))) uint8_t s_mu[MU ? kMuBytes : 16];
   __shared__ float s_bias[MU ? WN * TN * 32 : 1];
+  __shared__ float s_uv[R1 ? C::BM + C::BN : 1];  // r1 * u over the tile's rows, then v over its columns
+  constexpr bool ebar = MU || R1;                 // the epilogue barrier
 
   int first, stride, end;
   xcd_tiles((int)blockIdx.x, (int)gridDim.x, g.n_work, first, stride, end);
   if (first >= end) return;
-  const int nsteps = (int)(g.K / C::BKE);       // >= 1, the same for every tile
-  const int ntw = (end - first + stride - 1) / stride;  // this workgroup's tiles
+  const int nsteps = (int)(g.k_chunk / C::BKE);  // >= 1, the same for every (tile, split)
+  const int ntw = (end - first + stride - 1) / stride;  // this workgroup's (tile, split) units
   const int total = ntw * nsteps;               // its K-steps
-  auto origin = [&](int ti, int64_t& m0, int64_t& n0) {
+  const int ntiles = g.tiles_m * g.tiles_n;
+  auto origin = [&](int ti, int64_t& m0, int64_t& n0, int& split) {
+    const int lin = first + ti * stride;
     int tm, tn;
-    tile_coords(first + ti * stride, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
+    split = lin / ntiles;
+    tile_coords(lin % ntiles, g.tiles_m, g.tiles_n, g.group_m, tm, tn);
     m0 = (int64_t)tm * C::BM;
     n0 = (int64_t)tn * C::BN;
   };
@@ -704,9 +713,10 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
     // ---- loader wave l ----
     const int l = wave - C::NW;
     T lt[SH];
-    int bound = 0;  // tile whose views lt holds
+    int bound = 0;  // unit whose views lt holds
     int64_t m0, n0;
-    origin(0, m0, n0);
+    int split;
+    origin(0, m0, n0, split);
 #pragma unroll
     for (int i = 0; i < SH; ++i) lt[i].bind(g, m0, n0, l + i * L);
     if constexpr (MU) {
@@ -720,21 +730,22 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
         st = q - ti * nsteps;
         if (ti != bound) {
           bound = ti;
-          origin(ti, m0, n0);
+          origin(ti, m0, n0, split);
 #pragma unroll
           for (int i = 0; i < SH; ++i) lt[i].bind(g, m0, n0, l + i * L);
         }
       }
       uint8_t* stg = ring + (q % S) * SSZ;
+      const int kstep = (int)((int64_t)split * g.k_chunk / C::BKE) + st;  // absolute K-step
 #pragma unroll
-      for (int i = 0; i < SH; ++i) lt[i].issue(st * C::BKB, st * C::PIECE, stg);
+      for (int i = 0; i < SH; ++i) lt[i].issue(kstep * C::BKB, kstep * C::PIECE, stg);
     };
     for (int q = 0; q < S - 1; ++q) issue(q);
     for (int q = 0; q < total; ++q) {
       wait_vm<LPW * (S - 2)>();
       __builtin_amdgcn_s_barrier();
       issue(q + S - 1);
-      if (MU && q % nsteps == nsteps - 1) __builtin_amdgcn_s_barrier();  // the epilogue barrier
+      if (ebar && q % nsteps == nsteps - 1) __builtin_amdgcn_s_barrier();  // the epilogue barrier
     }
     wait_vm<0>();  // the trailing re-loads land before the workgroup ends
     return;
@@ -746,11 +757,22 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
   int q = 0;
   for (int ti = 0; ti < ntw; ++ti) {
     int64_t m0, n0;
-    origin(ti, m0, n0);
+    int split;
+    origin(ti, m0, n0, split);
+    const int k0 = (int)((int64_t)split * g.k_chunk / C::BKE);
     t.clear();
+    float uv = 0.0f;
+    if constexpr (R1) {
+      const int i = threadIdx.x;  // 256 multiplying threads = BM + BN
+      if (i < C::BM) {
+        if (m0 + i < g.M) uv = __fmul_rn(g.r1, mean_value<FMT>(g.ru, g.r1_row, m0 + i));
+      } else if (n0 + (i - C::BM) < g.N) {
+        uv = mean_value<FMT>(g.rv, g.r1_row, n0 + (i - C::BM));
+      }
+    }
     for (int st = 0; st < nsteps; ++st, ++q) {
       __builtin_amdgcn_s_barrier();
-      t.compute(ring + (q % S) * SSZ, s_mu, st);
+      t.compute(ring + (q % S) * SSZ, s_mu, k0 + st);
     }
     if constexpr (MU) {
       if ((threadIdx.x & 31) == 0) {
@@ -760,10 +782,12 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) sb[8 * qq + r] = t.acc_mu[4 * qq + r];
       }
-      lds_barrier();
     }
-    epilogue_regs<FMT, TM, TN, MU, false>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, 0,
-                                          threadIdx.x & 63, nullptr, nullptr, s_bias + t.wn * TN * 32);
+    if constexpr (R1) s_uv[threadIdx.x] = uv;
+    if constexpr (ebar) lds_barrier();
+    epilogue_regs<FMT, TM, TN, MU, R1>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, split, threadIdx.x & 63,
+                                       s_uv + t.wm * TM * 32, s_uv + C::BM + t.wn * TN * 32,
+                                       s_bias + t.wn * TN * 32);
   }
 }
 
@@ -859,24 +883,30 @@ __global__ __launch_bounds__(256) void k_gemv_mean(const uint8_t* __restrict__ m
 // ------------------------------------------------------------------------------------------
 static int g_count(int fmt) { return fmt == AVERIS_MXFP4 ? 32 : 16; }
 
-// Three configurations of 128 x 128 tiles, 2 x 2 multiplying waves with 2 x 2 MFMA tiles each
-// (measured on MI355X against 256 x 128 (4 and 8 waves), 128 x 256, 256 x 192 and 256 x 256
-// tiles, and against 128-element K-steps with 3 and 4 stages, at the Qwen3-0.6B-shaped linears):
+// Configurations: 128 x 128 tiles of 2 x 2 multiplying waves with 2 x 2 MFMA tiles each, except
+// KCFG_LONG96 (measured on MI355X against 256 x 128 (4 and 8 waves), 128 x 256, 256 x 192 and
+// 256 x 256 tiles, and against 128-element K-steps with 3 and 4 stages, at the Qwen3-0.6B-shaped
+// linears):
 //   KCFG_WS     warp-specialized (k_gemm_ws): two loader waves keep three K-steps of a 4-stage
-//               ring in flight across tiles, one workgroup per CU; short-K MXFP4 dense launches
-//               (forward and input-gradient GEMMs over the feature dimension), 8-16 % faster
-//               than KCFG_SHORT there;
+//               ring in flight across tiles, one workgroup per CU; every MXFP4 dense launch
+//               without accumulation whose K-steps split evenly (forward and input-gradient
+//               GEMMs: 8-16 % faster than KCFG_SHORT; weight gradients: 23-27 % faster than
+//               KCFG_LONG);
 //   KCFG_SHORT  two LDS stages, two workgroups per CU (70 KB LDS, <= 256 VGPRs each): the other
-//               short-K launches (NVFP4, grouped, split-K, accumulate, rank-one term);
-//   KCFG_LONG   three stages, one workgroup per CU, deeper prefetch, for long K (weight
-//               gradients over the token dimension).
-constexpr int KCFG_LONG = 0, KCFG_SHORT = 1, KCFG_WS = 2;
+//               short-K launches (NVFP4, grouped, accumulate, GEMV mean term);
+//   KCFG_LONG   three stages, one workgroup per CU, deeper prefetch, for the other long-K
+//               launches (NVFP4 and grouped weight gradients);
+//   KCFG_LONG96 the long-K kernel on 128 x 96 tiles (4 x 1 waves of 32 x 96), for dense
+//               single-split long-K launches whose 128 x 128 tiles would leave CUs idle in
+//               their last round (the NVFP4 1024 x 3072 weight gradient: 192 tiles -> 256).
+constexpr int KCFG_LONG = 0, KCFG_SHORT = 1, KCFG_WS = 2, KCFG_LONG96 = 3;
 constexpr int kWsStages = 4, kWsLoaders = 2;  // warp-specialized kernel: ring depth, loader waves
+constexpr bool kWsLongK = true;               // warp-specialized kernel for long K too
 struct TileCfg { int bm, bn; };
-static TileCfg tile_of(int) { return {128, 128}; }
+static TileCfg tile_of(int cfg) { return cfg == KCFG_LONG96 ? TileCfg{128, 96} : TileCfg{128, 128}; }
 constexpr int kBKE = 256;
 // Short K: the warp-specialized kernel (MXFP4 dense launches; the rest fall back to the two-stage
-// kernel below).  Long K: three stages, one workgroup per CU.
+// kernel).  Long K: three stages, one workgroup per CU (MXFP4 dense launches: warp-specialized).
 static int pick_cfg(int64_t K) { return K >= 4096 ? KCFG_LONG : KCFG_WS; }
 
 static int splits_for(int cfg, int64_t M, int64_t N, int64_t K) {
@@ -914,8 +944,10 @@ static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipSt
   if constexpr (F == AVERIS_MXFP4) {
     if (cfg == KCFG_WS) {
       constexpr int S = kWsStages, L = kWsLoaders;
-      if (mu) hipLaunchKernelGGL((k_gemm_ws<F, true, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
-      else hipLaunchKernelGGL((k_gemm_ws<F, false, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+      if (mu) hipLaunchKernelGGL((k_gemm_ws<F, true, false, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+      else if (g.has_r1 && g.splits == 1)
+        hipLaunchKernelGGL((k_gemm_ws<F, false, true, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+      else hipLaunchKernelGGL((k_gemm_ws<F, false, false, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
       return;
     }
   }
@@ -927,6 +959,7 @@ static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipSt
     }
   }
   if (cfg == KCFG_SHORT) hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 2>), dim3(grid), dim3(256), 0, s, g);
+  else if (cfg == KCFG_LONG96) hipLaunchKernelGGL((k_gemm<F, 4, 1, 1, 3, 3>), dim3(grid), dim3(256), 0, s, g);
   else hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 3>), dim3(grid), dim3(256), 0, s, g);
 }
 // Workgroups resident per CU: two for the two-stage configuration, one for the three-stage one
@@ -972,11 +1005,20 @@ hipError_t gemm_launch(const GemmPlan& p) {
   // mean term inside the GEMM: MXFP4 while the mean row fits the tile's LDS copy (see below)
   const bool mu_in = p.mu && fmt == AVERIS_MXFP4 && K <= kMuMaxK;
   int cfg = p.grouped == 2 ? KCFG_LONG : pick_cfg(K);  // grouped dW: long, varying K
-  // the warp-specialized kernel: MXFP4 dense single-split launches with K > 0 whose epilogue
-  // issues no global loads (every tile then has the same nonzero number of K-steps)
-  if (cfg == KCFG_WS && (fmt != AVERIS_MXFP4 || p.grouped || p.accumulate || p.mu_u || (p.mu && !mu_in) ||
-                         p.splits > 1 || K == 0))
-    cfg = KCFG_SHORT;
+  // the warp-specialized kernel: MXFP4 dense launches with K > 0 split into equal K chunks (every
+  // (tile, split) unit then has the same nonzero number of K-steps), no accumulation and no bias
+  // vector
+  const bool ws_ok = fmt == AVERIS_MXFP4 && !p.grouped && !p.accumulate && (!p.mu || mu_in) && K > 0 &&
+                     ceil_div(K, (int64_t)kBKE) % p.splits == 0;
+  if (cfg == KCFG_WS && !ws_ok) cfg = KCFG_SHORT;
+  if (kWsLongK && cfg == KCFG_LONG && ws_ok) cfg = KCFG_WS;
+  if (cfg == KCFG_LONG && !p.grouped && !p.mu && p.splits == 1 && N % 96 == 0) {
+    // fuller last round of the one-per-CU grid with 128 x 96 tiles?
+    const int64_t cus = cu_count();
+    auto fill = [cus](int64_t t) { return (double)t / (double)(cus * ceil_div(t, cus)); };
+    const int64_t t128 = ceil_div(M, (int64_t)128) * ceil_div(N, (int64_t)128), t96 = ceil_div(M, (int64_t)128) * (N / 96);
+    if (fill(t96) > fill(t128) + 0.05) cfg = KCFG_LONG96;
+  }
   const TileCfg tc = tile_of(cfg);
   g.tiles_m = (int)ceil_div(M, tc.bm); g.tiles_n = (int)ceil_div(N, tc.bn);
   if (p.grouped == 1)

@@ -104,6 +104,15 @@ def test_up_proj_full_size(fmt, fname):
     check_layer(workloads.up_proj(), fmt, False, f"up_proj-{fname}")
 
 
+@pytest.mark.parametrize("fmt,fname", FMTS)
+def test_long_k_ragged_128x96_tiles(fmt, fname):
+    # the weight gradient of m = 1024 by n = 3072 over l = 4100 tokens (K padded to 17 K-steps,
+    # ragged): on 256 CUs its 8 x 24 tiles of 128 x 128 leave a quarter of the CUs idle, so it
+    # runs on 8 x 32 tiles of 128 x 96; rank-one term with rotated means
+    lin = workloads.up_proj_like(25, 4100, 1024, 3072)
+    check_layer(lin, fmt, True, f"long-k-{fname}")
+
+
 def test_dw_accumulate_and_determinism():
     dev = device()
     lin = workloads.up_proj_like(24, 3000, 256, 384)
