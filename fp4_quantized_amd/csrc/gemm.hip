@@ -372,6 +372,55 @@ struct GemmTile {
       }
     }
   }
+  // MXFP4 K-step with every fragment of the step read from LDS before the first MFMA: a wave that
+  // is alone on its SIMD (the warp-specialized kernel) then waits for LDS once per step instead of
+  // once per 64-element substep.
+  __device__ __forceinline__ void compute_mx_preload(const uint8_t* s, const uint8_t* smu, int kstep) {
+    static_assert(FMT == AVERIS_MXFP4, "MXFP4 only");
+    uint32_t msc = 0;
+    if constexpr (MU) msc = *reinterpret_cast<const uint32_t*>(smu + kMuCodes + kstep * C::SB + mu_soff);
+    uint32_t sa[TM], sb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      sa[i] = *reinterpret_cast<const uint32_t*>(s + C::SA_OFF + (wm * TM * 32 + i * 32) * C::SB + scale_off);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      sb[j] = *reinterpret_cast<const uint32_t*>(s + C::SB_OFF + (wn * TN * 32 + j * 32) * C::SB + scale_off);
+    uint4 fa[C::NKK][TM], fb[C::NKK][TN], fm[C::NKK];
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fa[kk][i] = *reinterpret_cast<const uint4*>(s + C::A_OFF + (wm * TM * 32 + i * 32) * C::BKB + frag_off[kk]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        fb[kk][j] = *reinterpret_cast<const uint4*>(s + C::B_OFF + (wn * TN * 32 + j * 32) * C::BKB + frag_off[kk]);
+      if constexpr (MU) fm[kk] = *reinterpret_cast<const uint4*>(smu + kstep * C::BKB + mu_off + kk * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the MFMAs (the scheduler would sink them)
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const v8i av = {(int)fa[kk][i].x, (int)fa[kk][i].y, (int)fa[kk][i].z, (int)fa[kk][i].w, 0, 0, 0, 0};
+          const v8i bv = {(int)fb[kk][j].x, (int)fb[kk][j].y, (int)fb[kk][j].z, (int)fb[kk][j].w, 0, 0, 0, 0};
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              bv, av, acc[i][j], 4, 4, 0, (int)__builtin_amdgcn_ubfe(sb[j], 8 * kk, 8), 0,
+              (int)__builtin_amdgcn_ubfe(sa[i], 8 * kk, 8));
+        }
+      if constexpr (MU) {
+        const uint4 fbm = wm ? fb[kk][TN - 1] : fb[kk][0];
+        const uint32_t sbm = wm ? sb[TN - 1] : sb[0];
+        const v8i mv = {(int)fm[kk].x, (int)fm[kk].y, (int)fm[kk].z, (int)fm[kk].w, 0, 0, 0, 0};
+        const v8i bv = {(int)fbm.x, (int)fbm.y, (int)fbm.z, (int)fbm.w, 0, 0, 0, 0};
+        acc_mu = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            bv, mv, acc_mu, 4, 4, 0, (int)__builtin_amdgcn_ubfe(sbm, 8 * kk, 8), 0,
+            (int)__builtin_amdgcn_ubfe(msc, 8 * kk, 8));
+      }
+    }
+  }
 };
 
 // One pipeline step: wait until K-step `step` has landed (STAGES - 2 younger steps may stay in
@@ -772,7 +821,7 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
     }
     for (int st = 0; st < nsteps; ++st, ++q) {
       __builtin_amdgcn_s_barrier();
-      t.compute(ring + (q % S) * SSZ, s_mu, k0 + st);
+      t.compute_mx_preload(ring + (q % S) * SSZ, s_mu, k0 + st);
     }
     if constexpr (MU) {
       if ((threadIdx.x & 31) == 0) {
