@@ -140,6 +140,29 @@ def main():
         sweep[name] = r
     del layers
 
+    # Averis vs 16x16-Hadamard preprocessing at the operator level (the explainer's comparison of
+    # the two activation transforms): X [l, m] bf16 quantized for the forward GEMM (row layout),
+    # vanilla, with the mean-residual split, and with the Hadamard instead; the preprocessing cost
+    # of each is its time minus vanilla's.  l = 65536 tokens (the pages' 512 x 2048 scaled down by
+    # 16: every operand stays below 2^31 bytes), m = 4096 and 8192.
+    prep = {}
+    for m_ in (4096, 8192):
+        xa = workloads.activations_device(7, 65536, m_, dev)
+        for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
+            r = {}
+            for tag, split, h16 in (("vanilla", False, False), ("averis", True, False), ("hadamard", False, True)):
+                out = av.split_quant_outputs(65536, m_, fmt, split, h16, row=True, col=False, device=dev)
+                ws = av.split_quant_workspace(65536, m_, fmt, split, h16, dev)
+                r[f"{tag}_ms"] = round(timed(lambda: av.split_quant(xa, fmt, split, h16, row=True, col=False,
+                                                                     out=out, ws=ws), args.steps, args.warmup), 4)
+                del out, ws
+            van = r["vanilla_ms"]
+            r["hadamard_over_averis_prep"] = round((r["hadamard_ms"] - van) / max(r["averis_ms"] - van, 1e-9), 2)
+            prep[f"{name}_m{m_}"] = r
+            print(f"# prep {name} l=65536 m={m_}: vanilla {van*1e3:.0f} us, averis {r['averis_ms']*1e3:.0f} us, "
+                  f"hadamard {r['hadamard_ms']*1e3:.0f} us", file=sys.stderr, flush=True)
+        del xa
+
     # Dominant kernel: the MXFP4 GEMM tile kernel.  The vanilla forward and input-gradient GEMMs
     # are exactly one k_gemm launch each (2 l m n flops per launch).  A graph of REPS back-to-back
     # (forward, input-gradient) pairs is replayed after a cache-evicting read; HIP events on the
@@ -203,6 +226,8 @@ def main():
         "layer_sweep": dict(workload="Qwen3-0.6B-shaped layer sweep: q, k, v, o, gate, up, down linears at "
                                      "l=16384, fwd+dX+dW each, bf16 in", l=16384, linears=7,
                             gflop=round(sweep_flops / 1e9, 1), **sweep),
+        "preprocessing": dict(workload="X [65536, m] bf16, row layout only; Averis split vs 16x16 Hadamard "
+                                        "vs vanilla FP4 quantization", **prep),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -327,6 +327,7 @@ struct QuantArgs {
   const float* mean;           // nullptr: no subtraction
   const uint32_t* amax_slots;  // NVFP4 with rotation: [1] rotated row amax, [2] rotated col amax
   uint32_t* amax_out;          // AMAX_ONLY target (same buffer as amax_slots)
+  int want_row_amax, want_col_amax;  // AMAX_ONLY: the layouts the quantizing pass will write
   const float* ramax_part;     // NVFP4: per-strip max |residual| from k_colstats
   const float* mamax_part;     // NVFP4: per-workgroup max |(rotated) mean|
   int n_part;
@@ -454,8 +455,11 @@ __device__ __forceinline__ void nvfp4_scales(const QuantArgs& a, float& sd_row, 
   sd_col = nvfp4_tensor_scale(ac);
 }
 
-// Per-wave maxima of the AMAX_ONLY pass -> one atomic max per slot and workgroup.  Every wave
-// of the workgroup calls it (it holds a barrier); waves >= `nw` contribute nothing.
+// Per-wave maxima of the AMAX_ONLY pass -> at most one atomic max per slot and workgroup.  Every
+// wave of the workgroup calls it (it holds a barrier); waves >= `nw` contribute nothing.  The
+// atomic is skipped when the slot already holds at least this workgroup's maximum (the slot only
+// grows, and non-negative floats order like their bits): tens of thousands of workgroups
+// otherwise serialize on the two addresses (measured: a 6.6x slower pass at 65536 x 4096).
 __device__ __forceinline__ void amax_commit(const QuantArgs& a, float ra, float ca, float (*s_red)[8], int nw) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
@@ -468,8 +472,10 @@ __device__ __forceinline__ void amax_commit(const QuantArgs& a, float ra, float 
   if (threadIdx.x == 0) {
     float u = s_red[0][0], v = s_red[1][0];
     for (int i = 1; i < nw; ++i) { u = fmaxf(u, s_red[0][i]); v = fmaxf(v, s_red[1][i]); }
-    atomicMax(a.amax_out + 1, __float_as_uint(u));
-    atomicMax(a.amax_out + 2, __float_as_uint(v));
+    if (__float_as_uint(u) > __hip_atomic_load(a.amax_out + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(a.amax_out + 1, __float_as_uint(u));
+    if (__float_as_uint(v) > __hip_atomic_load(a.amax_out + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(a.amax_out + 2, __float_as_uint(v));
   }
 }
 
@@ -687,11 +693,15 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant(QuantArgs ain) {
 
   float amax_row = 0.0f, amax_col = 0.0f;
   if (r0 + kQRows <= a.rows) {
-    if (a.row_codes || AMAX_ONLY) tile_rows<T, FMT, H16, AMAX_ONLY, true>(a, r0, c0, s_tile, s_mean, sd_row, amax_row);
-    if (a.col_codes || AMAX_ONLY) tile_cols<T, FMT, H16, AMAX_ONLY, true>(a, r0, c0, s_tile, s_mean, sd_col, amax_col);
+    if (AMAX_ONLY ? a.want_row_amax : a.row_codes != nullptr)
+      tile_rows<T, FMT, H16, AMAX_ONLY, true>(a, r0, c0, s_tile, s_mean, sd_row, amax_row);
+    if (AMAX_ONLY ? a.want_col_amax : a.col_codes != nullptr)
+      tile_cols<T, FMT, H16, AMAX_ONLY, true>(a, r0, c0, s_tile, s_mean, sd_col, amax_col);
   } else {
-    if (a.row_codes || AMAX_ONLY) tile_rows<T, FMT, H16, AMAX_ONLY, false>(a, r0, c0, s_tile, s_mean, sd_row, amax_row);
-    if (a.col_codes || AMAX_ONLY) tile_cols<T, FMT, H16, AMAX_ONLY, false>(a, r0, c0, s_tile, s_mean, sd_col, amax_col);
+    if (AMAX_ONLY ? a.want_row_amax : a.row_codes != nullptr)
+      tile_rows<T, FMT, H16, AMAX_ONLY, false>(a, r0, c0, s_tile, s_mean, sd_row, amax_row);
+    if (AMAX_ONLY ? a.want_col_amax : a.col_codes != nullptr)
+      tile_cols<T, FMT, H16, AMAX_ONLY, false>(a, r0, c0, s_tile, s_mean, sd_col, amax_col);
   }
   if (AMAX_ONLY) amax_commit(a, amax_row, amax_col, s_red, kThreads / 64);
 }
@@ -785,6 +795,8 @@ static hipError_t launch_quant_t(const SplitQuantPlan& p, const SqLayout& L) {
   }
   if (FMT == AVERIS_NVFP4 && H16) {
     QuantArgs m = a;
+    m.want_row_amax = p.q_row != nullptr;
+    m.want_col_amax = p.q_col != nullptr;
     hipLaunchKernelGGL((k_quant<T, FMT, H16, true>), dim3((unsigned)ntiles), dim3(kThreads), 0, p.stream, m);
   }
   if (p.q_row) { a.row_codes = p.q_row->codes; a.row_scales = p.q_row->scales; a.row_ts = p.q_row->tensor_scale; }

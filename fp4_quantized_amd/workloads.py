@@ -159,6 +159,25 @@ def sweep_device(seed=3, l=16384, device="cuda"):
     return out
 
 
+def activations_device(seed, l, m, device="cuda"):
+    """One activation matrix X [l, m] bf16 drawn on the device with the up_proj_like recipe
+    (X = bf16(1 mu^T + R), R ~ Student-t(4), spike channels x20), for timing only."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+
+    def normal(*shape):
+        return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
+
+    g = normal(m)
+    mu = 3.0 * 2.0 ** 0.5 * g / torch.sqrt(torch.mean(g * g))
+    idx = torch.randperm(m, generator=gen, device=device)[:_n_spikes(m)]
+    mu[idx] *= 20.0
+    v = sum(normal(l, m) ** 2 for _ in range(4))
+    x = (normal(l, m) / torch.sqrt(v / 4.0) + mu[None, :]).to(torch.bfloat16)
+    return x
+
+
 @dataclass
 class MoE:
     """Expert-contiguous MoE FFN inputs.  offsets [E+1] over the routed rows; per expert e,

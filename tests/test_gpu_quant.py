@@ -164,3 +164,22 @@ def test_workspace_reused_across_calls():
     # 64-column strip holding that strip's counter (the rest of the line stays zero)
     counters = ws[256:256 + 128 * (cols // 64)].cpu().numpy().view(np.uint32)
     assert not counters.any(), f"strip counters left at {counters.reshape(-1, 32)[:, 0]}"
+
+
+@pytest.mark.parametrize("layout", ["row", "col"])
+@pytest.mark.parametrize("split", [True, False])
+def test_single_layout_nvfp4_hadamard(layout, split):
+    # NVFP4 + Hadamard takes its rotated amax in a separate pass, which covers only the layouts
+    # requested: each one alone must still equal the oracle's
+    dev = device()
+    lin = workloads.up_proj_like(41, 300, 256, 128)
+    print(f"case single-layout {layout} split={split}", flush=True)
+    x = workloads.to_torch(lin.x, "bf16", dev)
+    g = av.split_quant(x, av.NVFP4, split=split, hadamard=True, row=layout == "row", col=layout == "col")
+    torch.cuda.synchronize()
+    assert g["row" if layout == "col" else "col"] is None
+    mu_gpu = g["mean"].cpu().numpy() if split else None
+    o = O.split_quant(lin.x, av.NVFP4, split=split, hadamard=True, mean=mu_gpu)
+    assert_q_equal(g[layout], o[layout], f"single {layout} layout")
+    if split:
+        assert_q_equal(g["mean_q"], o["mean"], "quantized mean")
