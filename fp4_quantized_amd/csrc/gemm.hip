@@ -712,20 +712,22 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
   }
 }
 
-// Warp-specialized form of the 128 x 128 tile for dense single-split launches whose epilogue
-// issues no global loads (no bias vector, rank-one term or accumulation): waves 0-3 multiply and
-// store, waves 4 .. 4+L-1 issue every operand load (loader l takes the shares of waves l, l+L, ..).
-// A workgroup's K-steps form one stream across its tiles (all tiles have nsteps = K / 256 steps);
-// global step q lives in ring stage q % S.  The loaders keep S - 1 steps in flight, crossing tile
-// boundaries, and since their waits count only their own loads (no stores, no other waves'
-// operations) a counted vmcnt singles out the oldest step: loads complete in order.
+// Warp-specialized form of the 128 x 128 tile for MXFP4 dense launches without a bias vector or
+// accumulation whose K-steps split evenly: waves 0-3 multiply and store, waves 4 .. 4+L-1 issue
+// every operand load (loader l takes the shares of waves l, l+L, ..).  A workgroup's K-steps form
+// one stream across its (tile, split) units, each of nsteps = k_chunk / 256 steps; global step q
+// lives in ring stage q % S.  The loaders keep S - 1 steps in flight, crossing unit boundaries,
+// and since their waits count only their own loads (no stores, no other waves' operations) a
+// counted vmcnt singles out the oldest step: loads complete in order.
 // Barrier sequence, the same for every wave: one barrier per K-step (a loader first waits until
 // its loads of that step have landed; after the barrier stage (q - 1) % S is free, its last reader
-// being step q - 1, and it refills it with step q + S - 1), plus one epilogue barrier per tile with
-// the mean term.  Steps past the stream's end re-load the last tile's first step into the stage
-// just freed, which nobody reads again, so every wait covers the same number of loads.
-// R1: the launch has the weight gradient's rank-one term: the multiplying waves dequantize u and v
-// for each tile before its K-steps (their only global loads) and add r1 u v^T in the epilogue.
+// being step q - 1, and it refills it with step q + S - 1), plus one epilogue barrier per unit
+// with the mean or the rank-one term.  Steps past the stream's end re-load the last unit's first
+// step into the stage just freed, which nobody reads again, so every wait covers the same number
+// of loads.
+// MU: the mean term of the forward and input-gradient GEMMs (one more MFMA per four).  R1 (one
+// split only): the weight gradient's rank-one term; the multiplying waves dequantize u and v for
+// each tile before its K-steps (their only global loads) and add r1 u v^T in the epilogue.
 template <int FMT, bool MU, bool R1, int S, int L>
 __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
   constexpr int WM = 2, WN = 2, TM = 2, TN = 2;
