@@ -728,15 +728,18 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
 // MU: the mean term of the forward and input-gradient GEMMs (one more MFMA per four).  R1 (one
 // split only): the weight gradient's rank-one term; the multiplying waves dequantize u and v for
 // each tile before its K-steps (their only global loads) and add r1 u v^T in the epilogue.
-template <int FMT, bool MU, bool R1, int S, int L>
+// TMW: MFMA tiles per wave along M (2: 128 x 128 workgroup tiles; 4: 256 x 128, each wave 128 x
+// 64, which reads 6 fragments from LDS per 8 MFMAs instead of 4 per 4).
+template <int FMT, bool MU, bool R1, int S, int L, int TMW = 2>
 __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
-  constexpr int WM = 2, WN = 2, TM = 2, TN = 2;
+  constexpr int WM = 2, WN = 2, TM = TMW, TN = 2;
   using T = GemmTile<FMT, WM, WN, TM, TN, 2, 0, MU>;
   using C = typename T::C;
-  constexpr int SSZ = (C::STAGE + 1023) / 1024 * 1024;
+  constexpr int SSZ = TM == 2 ? (C::STAGE + 1023) / 1024 * 1024 : (C::STAGE + 255) / 256 * 256;  // 3 x 51 KB fit
   constexpr int SH = C::NW / L;                  // shares per loader wave
   constexpr int LPW = C::LPS * SH;               // loads per loader wave per K-step
   static_assert(C::NW % L == 0 && LPW * (S - 2) < 64, "vmcnt range");
+  static_assert(!R1 || C::BM + C::BN == 256, "one rank-one factor per multiplying thread");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S * SSZ];
   __shared__ __attribute__((aligned(16))) uint8_t s_mu[MU ? kMuBytes : 16];
   __shared__ float s_bias[MU ? WN * TN * 32 : 1];
@@ -823,7 +826,8 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
     }
     for (int st = 0; st < nsteps; ++st, ++q) {
       __builtin_amdgcn_s_barrier();
-      t.compute_mx_preload(ring + (q % S) * SSZ, s_mu, k0 + st);
+      if constexpr (TM == 2) t.compute_mx_preload(ring + (q % S) * SSZ, s_mu, k0 + st);
+      else t.compute(ring + (q % S) * SSZ, s_mu, k0 + st);
     }
     if constexpr (MU) {
       if ((threadIdx.x & 31) == 0) {
@@ -950,11 +954,14 @@ static int g_count(int fmt) { return fmt == AVERIS_MXFP4 ? 32 : 16; }
 //   KCFG_LONG96 the long-K kernel on 128 x 96 tiles (4 x 1 waves of 32 x 96), for dense
 //               single-split long-K launches whose 128 x 128 tiles would leave CUs idle in
 //               their last round (the NVFP4 1024 x 3072 weight gradient: 192 tiles -> 256).
-constexpr int KCFG_LONG = 0, KCFG_SHORT = 1, KCFG_WS = 2, KCFG_LONG96 = 3;
+constexpr int KCFG_LONG = 0, KCFG_SHORT = 1, KCFG_WS = 2, KCFG_LONG96 = 3, KCFG_WSW = 4;
 constexpr int kWsStages = 4, kWsLoaders = 2;  // warp-specialized kernel: ring depth, loader waves
 constexpr bool kWsLongK = true;               // warp-specialized kernel for long K too
+constexpr bool kWsWide = true;                // 256 x 128 warp-specialized tiles for short K
 struct TileCfg { int bm, bn; };
-static TileCfg tile_of(int cfg) { return cfg == KCFG_LONG96 ? TileCfg{128, 96} : TileCfg{128, 128}; }
+static TileCfg tile_of(int cfg) {
+  return cfg == KCFG_LONG96 ? TileCfg{128, 96} : cfg == KCFG_WSW ? TileCfg{256, 128} : TileCfg{128, 128};
+}
 constexpr int kBKE = 256;
 // Short K: the warp-specialized kernel (MXFP4 dense launches; the rest fall back to the two-stage
 // kernel).  Long K: three stages, one workgroup per CU (MXFP4 dense launches: warp-specialized).
@@ -993,6 +1000,12 @@ size_t gemm_grouped_ws_bytes(int64_t M, int64_t N, int64_t E) {
 template <int F>
 static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipStream_t s) {
   if constexpr (F == AVERIS_MXFP4) {
+    if (cfg == KCFG_WSW) {  // 256 x 128 tiles: a 3-stage ring of 51 KB stages
+      constexpr int L = kWsLoaders;
+      if (mu) hipLaunchKernelGGL((k_gemm_ws<F, true, false, 3, L, 4>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+      else hipLaunchKernelGGL((k_gemm_ws<F, false, false, 3, L, 4>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+      return;
+    }
     if (cfg == KCFG_WS) {
       constexpr int S = kWsStages, L = kWsLoaders;
       if (mu) hipLaunchKernelGGL((k_gemm_ws<F, true, false, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
@@ -1063,6 +1076,9 @@ hipError_t gemm_launch(const GemmPlan& p) {
                      ceil_div(K, (int64_t)kBKE) % p.splits == 0;
   if (cfg == KCFG_WS && !ws_ok) cfg = KCFG_SHORT;
   if (kWsLongK && cfg == KCFG_LONG && ws_ok) cfg = KCFG_WS;
+  if (kWsWide && cfg == KCFG_WS && K < 4096 && !p.mu_u &&
+      ceil_div(M, (int64_t)256) * ceil_div(N, (int64_t)128) * p.splits >= cu_count())
+    cfg = KCFG_WSW;
   if (cfg == KCFG_LONG && !p.grouped && !p.mu && p.splits == 1 && N % 96 == 0) {
     // fuller last round of the one-per-CU grid with 128 x 96 tiles?
     const int64_t cus = cu_count();
