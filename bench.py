@@ -237,7 +237,6 @@ def main():
 def gemm_traffic():
     """HBM bytes per k_gemm launch from the committed counter summary, or None once the GEMM
     source has changed since those counters were taken."""
-    import hashlib
     import re
     prof = os.path.join(ROOT, "profiles", "k_gemm_mxfp4_up_proj_traffic.txt")
     try:
@@ -248,11 +247,8 @@ def gemm_traffic():
     m_h = re.search(r"^gemm_source_sha1: ([0-9a-f]+)$", text, re.M)
     if not (m_t and m_h):
         return None
-    h = hashlib.sha1()
-    for f in ("gemm.hip", "common.h"):
-        with open(os.path.join(ROOT, "fp4_quantized_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return int(m_t.group(1)) if h.hexdigest()[:len(m_h.group(1))] == m_h.group(1) else None
+    from fp4_quantized_amd.build import gemm_source_digest
+    return int(m_t.group(1)) if gemm_source_digest()[:len(m_h.group(1))] == m_h.group(1) else None
 
 
 def cpu_baseline(lin, rows):

@@ -52,3 +52,18 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+
+
+def gemm_source_digest():
+    """SHA-1 (hex) of the GEMM sources (gemm.hip, common.h) with // comments and blank lines
+    removed: it changes when the compiled code can, not when a comment does.  bench.py pairs it
+    with the committed HBM-traffic counters of the GEMM."""
+    import hashlib
+    h = hashlib.sha1()
+    for f in ("gemm.hip", "common.h"):
+        with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", f)) as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
+    return h.hexdigest()

@@ -947,6 +947,9 @@ static int g_count(int fmt) { return fmt == AVERIS_MXFP4 ? 32 : 16; }
 //               without accumulation whose K-steps split evenly (forward and input-gradient
 //               GEMMs: 8-16 % faster than KCFG_SHORT; weight gradients: 23-27 % faster than
 //               KCFG_LONG);
+//   KCFG_WSW    the warp-specialized kernel on 256 x 128 tiles (waves of 128 x 64: 0.75x the LDS
+//               bytes per flop, the bound of the 128 x 128 form), a 3-stage ring; short-K launches
+//               without the rank-one term that still give every CU a tile: 7-14 % faster;
 //   KCFG_SHORT  two LDS stages, two workgroups per CU (70 KB LDS, <= 256 VGPRs each): the other
 //               short-K launches (NVFP4, grouped, accumulate, GEMV mean term);
 //   KCFG_LONG   three stages, one workgroup per CU, deeper prefetch, for the other long-K
