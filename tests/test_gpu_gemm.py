@@ -105,6 +105,13 @@ def test_up_proj_full_size(fmt, fname):
 
 
 @pytest.mark.parametrize("fmt,fname", FMTS)
+def test_ragged_tokens_256x128_tiles(fmt, fname):
+    # l = 8300 tokens: MXFP4's forward and input-gradient GEMMs run on 256 x 128 tiles (33 x 24 and
+    # 33 x 8 of them) with a ragged last row of tiles; full outputs against the oracle
+    check_layer(workloads.up_proj_like(26, 8300, 1024, 3072), fmt, False, f"ragged-256-{fname}")
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
 def test_long_k_ragged_128x96_tiles(fmt, fname):
     # the weight gradient of m = 1024 by n = 3072 over l = 4100 tokens (K padded to 17 K-steps,
     # ragged): on 256 CUs its 8 x 24 tiles of 128 x 128 leave a quarter of the CUs idle, so it
