@@ -140,6 +140,28 @@ def main():
         sweep[name] = r
     del layers
 
+    # MoE grouped layer (every kernel one grouped launch over the experts): 8192 tokens routed
+    # top-8 over 64 experts with Zipf(1.1) skew (65,536 routed rows), hidden 2048, expert FFN 768;
+    # one step = the gate, up and down linears' split+quant, fwd, dX and dW.
+    from fp4_quantized_amd.step import MoEStep
+    moe_in = workloads.moe_device(4, device=dev)
+    moe = {}
+    for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
+        r = {}
+        for split in (True, False):
+            ms = MoEStep(*moe_in[:7], moe_in[7], fmt, split=split)
+            tag = "averis" if split else "vanilla"
+            r[f"{tag}_step_ms"] = round(timed(ms.run, max(3, args.steps // 4), max(1, args.warmup // 2)), 4)
+            flops = ms.flops
+            del ms
+        r["overhead_pct"] = round(100.0 * (r["averis_step_ms"] - r["vanilla_step_ms"]) / r["vanilla_step_ms"], 2)
+        r["step_tflops"] = round(flops / (r["averis_step_ms"] * 1e-3) / 1e12, 1)
+        print(f"# moe {name}: averis {r['averis_step_ms']*1e3:.0f} us, vanilla {r['vanilla_step_ms']*1e3:.0f} us, "
+              f"{r['step_tflops']} TFLOP/s", file=sys.stderr, flush=True)
+        moe[name] = r
+    moe_rows = int(moe_in[7][-1])
+    del moe_in
+
     # Averis vs 16x16-Hadamard preprocessing at the operator level (the explainer's comparison of
     # the two activation transforms): X [l, m] bf16 quantized for the forward GEMM (row layout),
     # vanilla, with the mean-residual split, and with the Hadamard instead; the preprocessing cost
@@ -226,6 +248,9 @@ def main():
         "layer_sweep": dict(workload="Qwen3-0.6B-shaped layer sweep: q, k, v, o, gate, up, down linears at "
                                      "l=16384, fwd+dX+dW each, bf16 in", l=16384, linears=7,
                             gflop=round(sweep_flops / 1e9, 1), **sweep),
+        "moe": dict(workload="MoE FFN layer: 8192 tokens top-8 of 64 experts (Zipf 1.1), hidden 2048, expert FFN "
+                             "768, gate/up/down fwd+dX+dW, grouped launches", routed_rows=moe_rows,
+                    gflop=round(3 * 6 * moe_rows * 2048 * 768 / 1e9, 1), **moe),
         "preprocessing": dict(workload="X [65536, m] bf16, row layout only; Averis split vs 16x16 Hadamard "
                                         "vs vanilla FP4 quantization", **prep),
         "roofline": roofline,

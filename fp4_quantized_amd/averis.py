@@ -308,6 +308,20 @@ def split_quant_grouped(x: torch.Tensor, grp: Groups, fmt: int, split: bool = Tr
     return out
 
 
+def split_quant_grouped_workspace(rows, cols, E, fmt, split=True, hadamard=False, device="cuda"):
+    flags = (SPLIT if split else 0) | (HADAMARD16 if hadamard else 0)
+    return _workspace(lib().averis_split_quant_grouped_workspace_size(rows, cols, E, fmt, flags), device)
+
+
+def linear_grouped_workspace(N, E, fmt, device="cuda"):
+    """Workspace of a grouped forward or input-gradient GEMM with N output columns per group."""
+    return _workspace(lib().averis_linear_grouped_workspace_size(N, E, fmt), device)
+
+
+def linear_bwd_dw_grouped_workspace(m, n, E, fmt, device="cuda"):
+    return _workspace(lib().averis_linear_bwd_dw_grouped_workspace_size(m, n, E, fmt), device)
+
+
 def stacked_weight_view(col_q: QTensor, E: int, m: int) -> QTensor:
     """The column layout of grouped weights (E groups of m rows, outer = n) seen as E stacked
     [n, m] operands (outer = E * n): the same bytes, the forward GEMM's B operand."""

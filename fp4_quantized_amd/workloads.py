@@ -227,6 +227,37 @@ def moe(seed=4, tokens=8192, hidden=2048, ffn=768, experts=64, topk=8, dtype="bf
     return MoE(offsets, x, x_down, d_gu, d_dn, w_gate, w_up, w_down, dtype)
 
 
+def moe_device(seed=4, tokens=8192, hidden=2048, ffn=768, experts=64, topk=8, device="cuda"):
+    """The MoE workload drawn on the device, for timing: Zipf(1.1) top-8 routing of the tokens
+    (host, as in `moe`), token states drawn like `activations_device` and gathered per expert,
+    the down projection's input likewise, output gradients N(0, 1e-6) plus their own mean,
+    weights N(0, 0.02^2) stacked per expert.  Returns (x [L, hidden], x_down [L, ffn],
+    d_gu [L, ffn], d_dn [L, hidden], w_gate [E * hidden, ffn], w_up [E * hidden, ffn],
+    w_down [E * ffn, hidden], offsets [E + 1] host int64), bf16 tensors."""
+    import torch
+    ids, counts = zipf_topk_counts(np.random.default_rng(seed), tokens, experts, topk)
+    offsets = np.zeros(experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    order = np.argsort(ids.ravel(), kind="stable")
+    L = int(offsets[-1])
+    states = activations_device(seed * 10 + 1, tokens, hidden, device)
+    x = states[torch.from_numpy(order // topk).to(device)].contiguous()
+    del states
+    x_down = activations_device(seed * 10 + 2, L, ffn, device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 10 + 3)
+
+    def grad(cols):
+        g = torch.randn(cols, generator=gen, device=device)
+        mu = 1e-3 * g / torch.sqrt(torch.mean(g * g))
+        return (torch.randn(L, cols, generator=gen, device=device) * 1e-3 + mu[None, :]).to(torch.bfloat16)
+
+    d_gu, d_dn = grad(ffn), grad(hidden)
+    w = [(torch.randn(experts * r, c, generator=gen, device=device) * 0.02).to(torch.bfloat16)
+         for r, c in ((hidden, ffn), (hidden, ffn), (ffn, hidden))]
+    return x, x_down, d_gu, d_dn, w[0], w[1], w[2], offsets
+
+
 def to_torch(a, dtype, device):
     """Hand the exact values to torch as fp32 or bf16 (no rounding: values are representable)."""
     import torch

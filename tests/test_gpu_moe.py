@@ -168,3 +168,29 @@ def test_moe_full_size_sampled_experts(fmt, fname):
     order = np.argsort(counts)
     pick = sorted({int(order[-1]), int(order[len(order) // 2]), int(order[0])})
     moe_case(fmt, [int(c) for c in counts], 2048, 768, 26, experts=pick, tag=f"moe-{fname}")
+
+
+def test_moe_step_matches_grouped_calls():
+    # the bench's MoE step (preallocated outputs and workspaces, one grouped launch per kernel)
+    # gives exactly what the grouped entry points give when called one by one
+    from fp4_quantized_amd.step import MoEStep
+    dev = device()
+    print("case moe-step", flush=True)
+    x, x_down, d_gu, d_dn, w_gate, w_up, w_down, offs = workloads.moe_device(5, tokens=512, hidden=256, ffn=128,
+                                                                               experts=8, device=dev)
+    st = MoEStep(x, x_down, d_gu, d_dn, w_gate, w_up, w_down, offs, av.MXFP4)
+    st.run()
+    torch.cuda.synchronize()
+    grp = av.Groups(offs, dev)
+    wgrp = av.Groups(np.arange(9) * 256, dev)
+    gx = av.split_quant_grouped(x, grp, av.MXFP4)
+    gd = av.split_quant_grouped(d_gu, grp, av.MXFP4)
+    gw = av.split_quant_grouped(w_up, wgrp, av.MXFP4, split=False)
+    y = av.linear_fwd_grouped(gx["row"], gx["mean_q"], av.stacked_weight_view(gw["col"], 8, 256), grp, torch.bfloat16)
+    dx = av.linear_bwd_dx_grouped(gd["row"], gd["mean_q"], gw["row"], grp, torch.bfloat16)
+    dw = av.linear_bwd_dw_grouped(gx["col"], gd["col"], gx["mean_q"], gd["mean_q"], grp)
+    torch.cuda.synchronize()
+    _, args_y, kw_y = st.gemms[3]
+    _, _, kw_dx = st.gemms[4]
+    _, _, kw_dw = st.gemms[5]
+    assert torch.equal(kw_y["out"], y) and torch.equal(kw_dx["out"], dx) and torch.equal(kw_dw["dw"], dw)
