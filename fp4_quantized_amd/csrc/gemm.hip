@@ -846,6 +846,142 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
   }
 }
 
+// Warp-specialized form of the grouped weight gradient (MXFP4, 128 x 128 tiles): unit lin is
+// tile lin % (tiles_m tiles_n) of group e = lin / (tiles_m tiles_n), whose K is the group's token
+// count padded to 256, so units differ in their number of K-steps (none for an empty group).
+// Waves as in k_gemm_ws; the loaders walk a cursor over the flattened (unit, K-step) sequence and
+// keep S - 1 steps in flight across units.  Barriers, the same for every wave: one per K-step and,
+// with the rank-one term (R1: has_r1), one per unit before its epilogue.  Steps past the stream's
+// end re-load the last step issued into the stage just freed, which nobody reads.
+template <class C>
+__device__ __forceinline__ int dw_unit(const GemmArgs& gin, int lin, GemmArgs& g, int64_t& m0, int64_t& n0) {
+  g = gin;
+  const int ntiles = gin.tiles_m * gin.tiles_n;
+  const int e = lin / ntiles;
+  int tm, tn;
+  tile_coords(lin % ntiles, gin.tiles_m, gin.tiles_n, gin.group_m, tm, tn);
+  const GroupPos gp = group_scan(gin.offsets, gin.E, e, false, [](int64_t) { return (int64_t)1; });
+  const int64_t ke_pad = round_up(gp.len, (int64_t)C::BKE);
+  g.K = ke_pad; g.k_chunk = ke_pad;
+  g.lda_b = ke_pad / 2; g.ldb_b = ke_pad / 2;
+  g.a_codes += gin.M * gp.p256 / 2;
+  g.a_scales += gin.M * gp.p256 / C::G;
+  g.b_codes += gin.N * gp.p256 / 2;
+  g.b_scales += gin.N * gp.p256 / C::G;
+  g.r1 = (float)gp.len;
+  g.r1_row = e;
+  g.c = reinterpret_cast<float*>(gin.c) + (int64_t)e * gin.M * gin.ldc;
+  m0 = (int64_t)tm * C::BM;
+  n0 = (int64_t)tn * C::BN;
+  return (int)(ke_pad / C::BKE);
+}
+
+template <int FMT, bool R1, int S, int L>
+__global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws_dw(GemmArgs g) {
+  constexpr int WM = 2, WN = 2, TM = 2, TN = 2;
+  using T = GemmTile<FMT, WM, WN, TM, TN, 2, 0, false>;
+  using C = typename T::C;
+  constexpr int SSZ = (C::STAGE + 1023) / 1024 * 1024;
+  constexpr int SH = C::NW / L;     // shares per loader wave
+  constexpr int LPW = C::LPS * SH;  // loads per loader wave per K-step
+  static_assert(C::NW % L == 0 && LPW * (S - 2) < 64, "vmcnt range");
+  static_assert(!R1 || C::BM + C::BN == 256, "one rank-one factor per multiplying thread");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[S * SSZ];
+  __shared__ float s_uv[R1 ? C::BM + C::BN : 1];  // r1 * u over the tile's rows, then v over its columns
+
+  int first, stride, end;
+  xcd_tiles((int)blockIdx.x, (int)gridDim.x, g.n_work, first, stride, end);
+  if (first >= end) return;
+  const int ntw = (end - first + stride - 1) / stride;  // this workgroup's units
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+
+  if (wave >= C::NW) {
+    // ---- loader wave l: the cursor is unit cu, its K-step cs of cns; lt holds the views of the
+    // last unit with K-steps (the lambdas are forced inline: a call would keep what they capture
+    // in scratch memory) ----
+    const int l = wave - C::NW;
+    T lt[SH];
+    int cu = 0, cs = 0, cns = 0, last = 0;
+    bool have = false;  // some unit of this workgroup has K-steps
+    auto open_unit = [&](int u) __attribute__((always_inline)) {
+      GemmArgs v;
+      int64_t m0, n0;
+      cns = dw_unit<C>(g, first + u * stride, v, m0, n0);
+      if (cns > 0) {
+#pragma unroll
+        for (int i = 0; i < SH; ++i) lt[i].bind(v, m0, n0, l + i * L);
+        have = true;
+      }
+    };
+    auto skip_empty = [&]() __attribute__((always_inline)) {
+      while (cu < ntw && cs >= cns) {
+        ++cu;
+        cs = 0;
+        if (cu < ntw) open_unit(cu);
+      }
+    };
+    auto issue_next = [&](int q) __attribute__((always_inline)) {  // into stage q % S
+      if (!have) return;  // nothing to load, and no K-step barriers either
+      int kstep = last;
+      if (cu < ntw) {
+        kstep = cs++;
+        last = kstep;
+      }
+      uint8_t* stg = ring + (q % S) * SSZ;
+#pragma unroll
+      for (int i = 0; i < SH; ++i) lt[i].issue(kstep * C::BKB, kstep * C::PIECE, stg);
+      skip_empty();
+    };
+    open_unit(0);
+    skip_empty();
+    for (int q = 0; q < S - 1; ++q) issue_next(q);
+    int q = 0;
+    for (int u = 0; u < ntw; ++u) {
+      GemmArgs gu;
+      int64_t m0, n0;
+      const int ns = dw_unit<C>(g, first + u * stride, gu, m0, n0);
+      for (int st = 0; st < ns; ++st, ++q) {
+        wait_vm<LPW * (S - 2)>();
+        __builtin_amdgcn_s_barrier();
+        issue_next(q + S - 1);
+      }
+      if (R1) __builtin_amdgcn_s_barrier();  // the epilogue barrier
+    }
+    wait_vm<0>();  // the trailing re-loads land before the workgroup ends
+    return;
+  }
+
+  // ---- multiplying waves ----
+  T t;
+  t.bind(g, 0, 0);  // lane constants (this wave loads nothing)
+  int q = 0;
+  for (int u = 0; u < ntw; ++u) {
+    GemmArgs gu;
+    int64_t m0, n0;
+    const int ns = dw_unit<C>(g, first + u * stride, gu, m0, n0);
+    t.clear();
+    float uv = 0.0f;
+    if constexpr (R1) {
+      const int i = threadIdx.x;  // 256 multiplying threads = BM + BN
+      if (i < C::BM) {
+        if (m0 + i < gu.M) uv = __fmul_rn(gu.r1, mean_value<FMT>(gu.ru, gu.r1_row, m0 + i));
+      } else if (n0 + (i - C::BM) < gu.N) {
+        uv = mean_value<FMT>(gu.rv, gu.r1_row, n0 + (i - C::BM));
+      }
+    }
+    for (int st = 0; st < ns; ++st, ++q) {
+      __builtin_amdgcn_s_barrier();
+      t.compute_mx_preload(ring + (q % S) * SSZ, ring, st);
+    }
+    if constexpr (R1) {
+      s_uv[threadIdx.x] = uv;
+      lds_barrier();
+    }
+    epilogue_regs<FMT, TM, TN, false, R1>(gu, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, 0, threadIdx.x & 63,
+                                          s_uv + t.wm * TM * 32, s_uv + C::BM + t.wn * TN * 32, s_uv);
+  }
+}
+
 // Split-K reduce: C = (accumulate ? C : 0) + (sum_s P[s] in split order + bias[col]
 // + r1 * u[row] * v[col]), four columns per thread (N % 8 == 0); fp32 or bf16 output; u and v
 // dequantized from the quantized means in place.
@@ -957,7 +1093,7 @@ static int g_count(int fmt) { return fmt == AVERIS_MXFP4 ? 32 : 16; }
 //   KCFG_LONG96 the long-K kernel on 128 x 96 tiles (4 x 1 waves of 32 x 96), for dense
 //               single-split long-K launches whose 128 x 128 tiles would leave CUs idle in
 //               their last round (the NVFP4 1024 x 3072 weight gradient: 192 tiles -> 256).
-constexpr int KCFG_LONG = 0, KCFG_SHORT = 1, KCFG_WS = 2, KCFG_LONG96 = 3, KCFG_WSW = 4;
+constexpr int KCFG_LONG = 0, KCFG_SHORT = 1, KCFG_WS = 2, KCFG_LONG96 = 3, KCFG_WSW = 4, KCFG_WSDW = 5;
 constexpr int kWsStages = 4, kWsLoaders = 2;  // warp-specialized kernel: ring depth, loader waves
 constexpr bool kWsLongK = true;               // warp-specialized kernel for long K too
 constexpr bool kWsWide = true;                // 256 x 128 warp-specialized tiles for short K
@@ -1003,6 +1139,12 @@ size_t gemm_grouped_ws_bytes(int64_t M, int64_t N, int64_t E) {
 template <int F>
 static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipStream_t s) {
   if constexpr (F == AVERIS_MXFP4) {
+    if (cfg == KCFG_WSDW) {  // grouped weight gradient
+      constexpr int S = kWsStages, L = kWsLoaders;
+      if (g.has_r1) hipLaunchKernelGGL((k_gemm_ws_dw<F, true, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+      else hipLaunchKernelGGL((k_gemm_ws_dw<F, false, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+      return;
+    }
     if (cfg == KCFG_WSW) {  // 256 x 128 tiles: a 3-stage ring of 51 KB stages
       constexpr int L = kWsLoaders;
       if (mu) hipLaunchKernelGGL((k_gemm_ws<F, true, false, 3, L, 4>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
@@ -1078,6 +1220,8 @@ hipError_t gemm_launch(const GemmPlan& p) {
   const bool ws_ok = fmt == AVERIS_MXFP4 && !p.grouped && !p.accumulate && (!p.mu || mu_in) && K > 0 &&
                      ceil_div(K, (int64_t)kBKE) % p.splits == 0;
   if (cfg == KCFG_WS && !ws_ok) cfg = KCFG_SHORT;
+  // grouped weight gradient, MXFP4: the warp-specialized form with per-group K
+  if (p.grouped == 2 && fmt == AVERIS_MXFP4 && !p.accumulate && !p.mu && K > 0) cfg = KCFG_WSDW;
   if (kWsLongK && cfg == KCFG_LONG && ws_ok) cfg = KCFG_WS;
   if (kWsWide && cfg == KCFG_WS && K < 4096 && !p.mu_u &&
       ceil_div(M, (int64_t)256) * ceil_div(N, (int64_t)128) * p.splits >= cu_count())
