@@ -151,11 +151,21 @@ def test_golden_mxfp4_blocks(case):
     np.testing.assert_array_equal(O.unpack_nibbles(codes)[0], c["codes"], err_msg=c["name"])
 
 
-@pytest.mark.parametrize("case", range(2))
+@pytest.mark.parametrize("case", range(3))
 def test_golden_nvfp4_blocks(case):
     c = _golden()["nvfp4"][case]
     v = np.array(c["values"], dtype=np.float32)[None, :]
     q = O.quantize(v, O.NVFP4)
+    assert q.s_dec == np.float32(c["s_dec"]), c["name"]
+    np.testing.assert_array_equal(q.scales[0], c["scales"], err_msg=c["name"])
+    np.testing.assert_array_equal(O.unpack_nibbles(q.codes)[0], c["codes"], err_msg=c["name"])
+
+
+def test_golden_nvfp4_hadamard_block():
+    # reading: the NVFP4 tensor scale of a rotated operand comes from its rotated amax
+    c = _golden()["nvfp4_hadamard"][0]
+    v = np.array(c["values"], dtype=np.float32)[None, :]
+    q = O.quantize(v, O.NVFP4, rotate=True)
     assert q.s_dec == np.float32(c["s_dec"]), c["name"]
     np.testing.assert_array_equal(q.scales[0], c["scales"], err_msg=c["name"])
     np.testing.assert_array_equal(O.unpack_nibbles(q.codes)[0], c["codes"], err_msg=c["name"])
@@ -250,6 +260,27 @@ def test_split_quant_vs_unquantized_is_close():
         sw = O.split_quant(w, fmt, split=False)
         y = O.linear_fwd(sx["row"], sx["mean"], sw["col"])
         assert O.relative_error(y, x @ w) < 0.15
+
+
+def test_hadamard_split_quant_fwd_dx_close_to_unquantized():
+    # With the split and the rotation both on, every operand of the forward and input-gradient
+    # GEMMs (residual, mean and weight) is rotated along K, so the products stay within FP4
+    # noise of X W and D W^T.  The mean dominates these inputs: a mean quantized without the
+    # rotation would meet a rotated weight and miss by far more than the noise.
+    rng = np.random.default_rng(8)
+    l, m, n = 256, 128, 64
+    x = rng.standard_normal((l, m)) + rng.standard_normal(m) * 6
+    d = rng.standard_normal((l, n)) * 1e-3 + rng.standard_normal(n) * 4e-3
+    w = rng.standard_normal((m, n)) * 0.02
+    for fmt in (O.NVFP4, O.MXFP4):
+        sx = O.split_quant(x, fmt, hadamard=True)
+        sd = O.split_quant(d, fmt, hadamard=True)
+        sw = O.split_quant(w, fmt, split=False, hadamard=True)
+        y = O.linear_fwd(sx["row"], sx["mean"], sw["col"])
+        dx = O.linear_bwd_dx(sd["row"], sd["mean"], sw["row"])
+        # FP4 noise of the three operands: 0.13-0.19 here; an unrotated mean gives about 1.4
+        assert O.relative_error(y, x @ w) < 0.3
+        assert O.relative_error(dx, d @ w.T) < 0.3
 
 
 # ----------------------------------------------------------------------- quantizer -----

@@ -65,3 +65,48 @@ def test_swapped_nibbles_are_caught(monkeypatch):
                         lambda c: ((np.asarray(c, np.uint8)[..., 1::2] & 15) |
                                    ((np.asarray(c, np.uint8)[..., 0::2] & 15) << 4)))
     _fails(P.test_pack_nibble_order)
+
+
+def test_nvfp4_amax_before_rotation_is_caught(monkeypatch):
+    orig = O.quantize
+
+    def bad(r, fmt, rotate=False, k=None):
+        if fmt != O.NVFP4 or not rotate:
+            return orig(r, fmt, rotate, k)
+        r = np.asarray(r, np.float32)
+        s_dec = O.nvfp4_tensor_scale(np.max(np.abs(r)) if r.size else 0.0)  # unrotated amax
+        codes, scales = O.quantize_nvfp4(O.hadamard16_f32(r), s_dec)
+        return O.QTensor(codes, scales, s_dec, fmt, r.shape[1] if k is None else k, True)
+    monkeypatch.setattr(O, "quantize", bad)
+    _fails(P.test_golden_nvfp4_hadamard_block)
+
+
+def test_subnormal_decode_scale_not_zeroed_is_caught(monkeypatch):
+    def bad(r, s_dec):  # the NVFP4 block quantizer without the "decode scale below 2^-126" rule
+        r = np.asarray(r, dtype=np.float32)
+        outer, K = r.shape
+        blk = r.reshape(outer, K // 16, 16)
+        amax = np.max(np.abs(blk), axis=2)
+        s_dec = np.float32(s_dec)
+        with np.errstate(all="ignore"):
+            e = O.e4m3_encode(((amax / np.float32(6.0)).astype(np.float32) / s_dec).astype(np.float32))
+            S = (O.e4m3_value(e).astype(np.float32) * s_dec).astype(np.float32)
+            codes = O.e2m1_encode((blk * (np.float32(1.0) / S)[:, :, None]).astype(np.float32))
+        codes[e == 0] = 0
+        return O.pack_nibbles(codes.reshape(outer, K)), e
+    monkeypatch.setattr(O, "quantize_nvfp4", bad)
+    _fails(P.test_golden_nvfp4_blocks, 2)
+
+
+def test_unrotated_mean_under_hadamard_is_caught(monkeypatch):
+    orig = O.split_quant
+
+    def bad(x, fmt, split=True, hadamard=False, mean=None):
+        out = orig(x, fmt, split, hadamard, mean)
+        if split and hadamard:  # the mean quantized without the rotation, labelled rotated
+            q = O.quantize(O.pad_k(out["mu32"][None, :]), fmt, rotate=False, k=out["mu32"].shape[0])
+            q.rotated = True
+            out["mean"] = q
+        return out
+    monkeypatch.setattr(O, "split_quant", bad)
+    _fails(P.test_hadamard_split_quant_fwd_dx_close_to_unquantized)
