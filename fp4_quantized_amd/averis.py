@@ -26,7 +26,7 @@ BLOCK = {NVFP4: 16, MXFP4: 32}
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaveris.so")
 
 EXPORTS = [
-    "averis_abi_version", "averis_status_string",
+    "averis_abi_version", "averis_status_string", "averis_source_digest",
     "averis_split_quant_workspace_size", "averis_split_quant",
     "averis_linear_workspace_size", "averis_linear_fwd", "averis_linear_bwd_dx",
     "averis_linear_bwd_dw_workspace_size", "averis_linear_bwd_dw",
@@ -52,18 +52,33 @@ class CQTensor(ctypes.Structure):
 _lib = None
 
 
+def is_current() -> bool:
+    """True when libaveris.so exists and was built from the sources next to it."""
+    from .build import source_digest
+    if not os.path.exists(LIB_PATH):
+        return False
+    L = ctypes.CDLL(LIB_PATH)
+    f = L.averis_source_digest
+    f.restype = ctypes.c_char_p
+    return f().decode() == source_digest()
+
+
 def lib():
-    """Load libaveris.so once; raise if it has not been built."""
+    """Load libaveris.so once; raise if it has not been built, or was built from other sources."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        if not is_current():
+            raise RuntimeError(f"{LIB_PATH} was built from other sources than the ones beside it: "
+                               "rebuild it with __graft_entry__.build()")
         L = ctypes.CDLL(LIB_PATH)
         P, I64, I32, U32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
         Q = ctypes.POINTER(CQTensor)
         sig = {
             "averis_abi_version": (I32, []),
             "averis_status_string": (ctypes.c_char_p, [I32]),
+            "averis_source_digest": (ctypes.c_char_p, []),
             "averis_split_quant_workspace_size": (SZ, [I64, I64, I32, U32]),
             "averis_split_quant": (I32, [P, I32, I64, I64, I64, I32, U32, P, Q, Q, Q, P, SZ, P]),
             "averis_linear_workspace_size": (SZ, [I64, I64, I64, I32]),

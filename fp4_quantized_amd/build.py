@@ -16,6 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libaveris.so")
 SOURCES = ["quant.hip", "gemm.hip", "api.hip"]
+HEADERS = ["common.h", "launch.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -33,11 +34,26 @@ def _run(cmd):
     return out
 
 
+def source_digest() -> str:
+    """SHA-1 (hex) of every file the library is built from (sources, headers, the public header
+    and this build script's flags).  It is compiled into the library, so a loader can tell a
+    library built from other sources."""
+    import hashlib
+    h = hashlib.sha1()
+    h.update(" ".join(FLAGS[:-4]).encode())
+    for f in [os.path.join(CSRC, s) for s in SOURCES + HEADERS] + [os.path.join(ROOT, "include", "averis.h")]:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source to an object, link libaveris.so; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
     objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES]
-    cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    digest = [f'-DAVERIS_SOURCE_DIGEST="{source_digest()}"']
+    cmds = [[HIPCC, *FLAGS, *(digest if s == "api.hip" else []), "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         outs = list(ex.map(_run, cmds))
     tmp = LIB + ".tmp"

@@ -5,8 +5,6 @@
 
 #include "launch.h"
 
-
-
 using namespace av;
 
 namespace {
@@ -61,6 +59,11 @@ int32_t check_in(const averis_qtensor* q) {
 extern "C" {
 
 int32_t averis_abi_version(void) { return AVERIS_ABI_VERSION; }
+
+#ifndef AVERIS_SOURCE_DIGEST
+#define AVERIS_SOURCE_DIGEST "unknown"
+#endif
+const char* averis_source_digest(void) { return AVERIS_SOURCE_DIGEST; }
 
 const char* averis_status_string(int32_t s) {
   switch (s) {
@@ -308,7 +311,7 @@ int32_t averis_linear_bwd_dx_grouped(const averis_qtensor* dr, const averis_qten
 size_t averis_linear_bwd_dw_grouped_workspace_size(int64_t m, int64_t n, int32_t E, int32_t fmt) {
   (void)fmt;
   if (m < 0 || n < 0 || E < 1) return 0;
-  return gemm_grouped_ws_bytes(m, n, E);
+  return gemm_grouped_dw_ws_bytes(m, n, E);
 }
 
 int32_t averis_linear_bwd_dw_grouped(const averis_qtensor* xr_t, const averis_qtensor* dr_t,
@@ -337,7 +340,7 @@ int32_t averis_linear_bwd_dw_grouped(const averis_qtensor* xr_t, const averis_qt
     if (!dw) return AVERIS_E_NULL;
     if (!aligned16(dw) || (lddw * 4) % 16 != 0) return AVERIS_E_ALIGN;
   }
-  if (!ws || ws_bytes < gemm_grouped_ws_bytes(m, n, E)) return AVERIS_E_WORKSPACE;
+  if (!ws || ws_bytes < gemm_grouped_dw_ws_bytes(m, n, E)) return AVERIS_E_WORKSPACE;
   if (!aligned16(ws)) return AVERIS_E_ALIGN;
   GemmPlan p{};
   p.a = xr_t; p.b = dr_t; p.c = dw; p.ldc = lddw; p.c_bf16 = 0;

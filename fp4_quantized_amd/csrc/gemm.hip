@@ -850,50 +850,103 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
 // tile lin % (tiles_m tiles_n) of group e = lin / (tiles_m tiles_n), whose K is the group's token
 // count padded to 256, so units differ in their number of K-steps (none for an empty group).
 // Waves as in k_gemm_ws; the loaders walk a cursor over the flattened (unit, K-step) sequence and
-// keep S - 1 steps in flight across units.  Barriers, the same for every wave: one per K-step and,
-// with the rank-one term (R1: has_r1), one per unit before its epilogue.  Steps past the stream's
-// end re-load the last step issued into the stage just freed, which nobody reads.
+// keep S - 1 steps in flight across units.  One barrier per K-step, the same for every wave, and
+// no other: a unit's epilogue overlaps the loaders' next K-steps, and its stores drain while the
+// multiplying waves go on to the next unit (they issue no global loads that would wait for them).
+//   * Each group's token count and first 256-token block sit in an LDS table built once per
+//     workgroup, so a unit switch reads no global memory (a loader's vector load there would have
+//     to wait for every operand load in flight).
+//   * R1: the rank-one factors l_e u and v come from fp32 tables written by k_rank_one_vectors;
+//     with every K-step the loaders also copy the unit's 128 + 128 factors into the stage, and the
+//     multiplying waves read them from the stage of the unit's last K-step during its epilogue
+//     (the loaders refill that stage only after the next K-step's barrier).  Empty units store
+//     zeros (their rank-one factor l_e is 0).
+// Steps past the stream's end re-load the last step issued into the stage just freed, which
+// nobody reads.
+constexpr int kDwMaxGroups = 1024;  // groups of the LDS table (more: the three-stage kernel)
+constexpr int kUvStage = 2048;      // R1: the unit's u (first KB, 128 floats used) and v slices
+
+struct DwUnit { int e, ns; int64_t m0, n0; };
+
 template <class C>
-__device__ __forceinline__ int dw_unit(const GemmArgs& gin, int lin, GemmArgs& g, int64_t& m0, int64_t& n0) {
+__device__ __forceinline__ DwUnit dw_unit(const GemmArgs& gin, int lin, const int* s_len, const int* s_t256,
+                                          GemmArgs& g) {
   g = gin;
   const int ntiles = gin.tiles_m * gin.tiles_n;
-  const int e = lin / ntiles;
+  DwUnit u;
+  u.e = lin / ntiles;
   int tm, tn;
   tile_coords(lin % ntiles, gin.tiles_m, gin.tiles_n, gin.group_m, tm, tn);
-  const GroupPos gp = group_scan(gin.offsets, gin.E, e, false, [](int64_t) { return (int64_t)1; });
-  const int64_t ke_pad = round_up(gp.len, (int64_t)C::BKE);
+  const int64_t len = uniform32(s_len[u.e]), t0 = (int64_t)uniform32(s_t256[u.e]) * C::BKE;
+  const int64_t ke_pad = round_up(len, (int64_t)C::BKE);
   g.K = ke_pad; g.k_chunk = ke_pad;
   g.lda_b = ke_pad / 2; g.ldb_b = ke_pad / 2;
-  g.a_codes += gin.M * gp.p256 / 2;
-  g.a_scales += gin.M * gp.p256 / C::G;
-  g.b_codes += gin.N * gp.p256 / 2;
-  g.b_scales += gin.N * gp.p256 / C::G;
-  g.r1 = (float)gp.len;
-  g.r1_row = e;
-  g.c = reinterpret_cast<float*>(gin.c) + (int64_t)e * gin.M * gin.ldc;
-  m0 = (int64_t)tm * C::BM;
-  n0 = (int64_t)tn * C::BN;
-  return (int)(ke_pad / C::BKE);
+  g.a_codes += gin.M * t0 / 2;
+  g.a_scales += gin.M * t0 / C::G;
+  g.b_codes += gin.N * t0 / 2;
+  g.b_scales += gin.N * t0 / C::G;
+  g.c = reinterpret_cast<float*>(gin.c) + (int64_t)u.e * gin.M * gin.ldc;
+  g.has_r1 = gin.has_r1 && len > 0;
+  u.m0 = (int64_t)tm * C::BM;
+  u.n0 = (int64_t)tn * C::BN;
+  u.ns = (int)(ke_pad / C::BKE);
+  return u;
+}
+
+// Rank-one factors of the grouped weight gradient, one fp32 table row per group: u_tab[e][i] =
+// l_e * u_e[i] (i < M) and v_tab[e][j] = v_e[j] (j < N), the dequantized means (rotation undone).
+template <int FMT>
+__global__ __launch_bounds__(256) void k_rank_one_vectors(GemmArgs g, float* __restrict__ u_tab,
+                                                          float* __restrict__ v_tab, int64_t mpad, int64_t npad) {
+  const int e = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const float len = (float)(g.offsets[e + 1] - g.offsets[e]);
+  if (i < g.M) u_tab[e * mpad + i] = __fmul_rn(len, mean_value<FMT>(g.ru, e, i));
+  else if (i < g.M + g.N) v_tab[e * npad + (i - g.M)] = mean_value<FMT>(g.rv, e, i - g.M);
 }
 
 template <int FMT, bool R1, int S, int L>
-__global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws_dw(GemmArgs g) {
+__global__ __launch_bounds__(64 * (4 + L), 1) void k_gemm_ws_dw(GemmArgs g, const float* __restrict__ u_tab,
+                                                                const float* __restrict__ v_tab, int64_t mpad,
+                                                                int64_t npad) {
   constexpr int WM = 2, WN = 2, TM = 2, TN = 2;
   using T = GemmTile<FMT, WM, WN, TM, TN, 2, 0, false>;
   using C = typename T::C;
-  constexpr int SSZ = (C::STAGE + 1023) / 1024 * 1024;
-  constexpr int SH = C::NW / L;     // shares per loader wave
-  constexpr int LPW = C::LPS * SH;  // loads per loader wave per K-step
+  constexpr int UV_OFF = (C::STAGE + 255) / 256 * 256;
+  constexpr int SSZ = (UV_OFF + (R1 ? kUvStage : 0) + 1023) / 1024 * 1024;
+  constexpr int SH = C::NW / L;                     // shares per loader wave
+  constexpr int LPW = C::LPS * SH + (R1 ? 1 : 0);  // loads per loader wave per K-step
   static_assert(C::NW % L == 0 && LPW * (S - 2) < 64, "vmcnt range");
-  static_assert(!R1 || C::BM + C::BN == 256, "one rank-one factor per multiplying thread");
+  static_assert(!R1 || (L == 2 && C::BM == 128 && C::BN == 128), "one rank-one slice per loader");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S * SSZ];
-  __shared__ float s_uv[R1 ? C::BM + C::BN : 1];  // r1 * u over the tile's rows, then v over its columns
+  __shared__ int s_len[kDwMaxGroups], s_t256[kDwMaxGroups];
 
   int first, stride, end;
   xcd_tiles((int)blockIdx.x, (int)gridDim.x, g.n_work, first, stride, end);
   if (first >= end) return;
   const int ntw = (end - first + stride - 1) / stride;  // this workgroup's units
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+
+  // group table: length and first 256-token block of every group (wave 0, one pass of
+  // 64-group prefix scans), before any operand load is in flight
+  if (wave == 0) {
+    int64_t base = 0;
+    for (int e0 = 0; e0 < g.E; e0 += 64) {
+      const int e = e0 + lane;
+      const int64_t len = e < g.E ? g.offsets[e + 1] - g.offsets[e] : 0;
+      const int64_t c = ceil_div(len, (int64_t)C::BKE);
+      int64_t sc = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int64_t x = __shfl_up(sc, d, 64);
+        if (lane >= d) sc += x;
+      }
+      if (e < g.E) { s_len[e] = (int)len; s_t256[e] = (int)(base + sc - c); }
+      base += __shfl(sc, 63, 64);
+    }
+  }
+  __syncthreads();
 
   if (wave >= C::NW) {
     // ---- loader wave l: the cursor is unit cu, its K-step cs of cns; lt holds the views of the
@@ -901,15 +954,21 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws_dw(GemmArgs g) {
     // in scratch memory) ----
     const int l = wave - C::NW;
     T lt[SH];
+    __amdgpu_buffer_rsrc_t ruv = make_rsrc(u_tab, 0);  // R1: this loader's rank-one slice
     int cu = 0, cs = 0, cns = 0, last = 0;
     bool have = false;  // some unit of this workgroup has K-steps
     auto open_unit = [&](int u) __attribute__((always_inline)) {
       GemmArgs v;
-      int64_t m0, n0;
-      cns = dw_unit<C>(g, first + u * stride, v, m0, n0);
+      const DwUnit du = dw_unit<C>(g, first + u * stride, s_len, s_t256, v);
+      cns = du.ns;
       if (cns > 0) {
 #pragma unroll
-        for (int i = 0; i < SH; ++i) lt[i].bind(v, m0, n0, l + i * L);
+        for (int i = 0; i < SH; ++i) lt[i].bind(v, du.m0, du.n0, l + i * L);
+        if constexpr (R1) {
+          const int64_t o0 = l == 0 ? du.m0 : du.n0, lim = l == 0 ? g.M : g.N;
+          const float* base = (l == 0 ? u_tab + du.e * mpad : v_tab + du.e * npad) + o0;
+          ruv = make_rsrc(base, (lim - o0) * 4);
+        }
         have = true;
       }
     };
@@ -930,6 +989,8 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws_dw(GemmArgs g) {
       uint8_t* stg = ring + (q % S) * SSZ;
 #pragma unroll
       for (int i = 0; i < SH; ++i) lt[i].issue(kstep * C::BKB, kstep * C::PIECE, stg);
+      // 32 lanes x 16 bytes = the 128 factors; the other lanes read past the range (zeros)
+      if constexpr (R1) dma16<0>(ruv, stg + UV_OFF + l * 1024, lane < 32 ? lane * 16 : 0x7FFFFFF0, 0);
       skip_empty();
     };
     open_unit(0);
@@ -938,14 +999,12 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws_dw(GemmArgs g) {
     int q = 0;
     for (int u = 0; u < ntw; ++u) {
       GemmArgs gu;
-      int64_t m0, n0;
-      const int ns = dw_unit<C>(g, first + u * stride, gu, m0, n0);
+      const int ns = dw_unit<C>(g, first + u * stride, s_len, s_t256, gu).ns;
       for (int st = 0; st < ns; ++st, ++q) {
         wait_vm<LPW * (S - 2)>();
         __builtin_amdgcn_s_barrier();
         issue_next(q + S - 1);
       }
-      if (R1) __builtin_amdgcn_s_barrier();  // the epilogue barrier
     }
     wait_vm<0>();  // the trailing re-loads land before the workgroup ends
     return;
@@ -957,28 +1016,16 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws_dw(GemmArgs g) {
   int q = 0;
   for (int u = 0; u < ntw; ++u) {
     GemmArgs gu;
-    int64_t m0, n0;
-    const int ns = dw_unit<C>(g, first + u * stride, gu, m0, n0);
+    const DwUnit du = dw_unit<C>(g, first + u * stride, s_len, s_t256, gu);
     t.clear();
-    float uv = 0.0f;
-    if constexpr (R1) {
-      const int i = threadIdx.x;  // 256 multiplying threads = BM + BN
-      if (i < C::BM) {
-        if (m0 + i < gu.M) uv = __fmul_rn(gu.r1, mean_value<FMT>(gu.ru, gu.r1_row, m0 + i));
-      } else if (n0 + (i - C::BM) < gu.N) {
-        uv = mean_value<FMT>(gu.rv, gu.r1_row, n0 + (i - C::BM));
-      }
-    }
-    for (int st = 0; st < ns; ++st, ++q) {
+    for (int st = 0; st < du.ns; ++st, ++q) {
       __builtin_amdgcn_s_barrier();
       t.compute_mx_preload(ring + (q % S) * SSZ, ring, st);
     }
-    if constexpr (R1) {
-      s_uv[threadIdx.x] = uv;
-      lds_barrier();
-    }
-    epilogue_regs<FMT, TM, TN, false, R1>(gu, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, 0, threadIdx.x & 63,
-                                          s_uv + t.wm * TM * 32, s_uv + C::BM + t.wn * TN * 32, s_uv);
+    // R1 with K-steps: the factors sit in the stage of the unit's last K-step
+    const float* uv = reinterpret_cast<const float*>(ring + ((q + S - 1) % S) * SSZ + UV_OFF);
+    epilogue_regs<FMT, TM, TN, false, R1>(gu, t.acc, du.m0 + t.wm * TM * 32, du.n0 + t.wn * TN * 32, 0, lane,
+                                          uv + t.wm * TM * 32, uv + 256 + t.wn * TN * 32, uv);
   }
 }
 
@@ -1135,14 +1182,28 @@ size_t gemm_grouped_ws_bytes(int64_t M, int64_t N, int64_t E) {
   (void)M;
   return partials_offset(N, E);
 }
+// grouped weight gradient: [256 B][u_tab E x round_up(M, 128) fp32][v_tab E x round_up(N, 128) fp32]
+size_t gemm_grouped_dw_ws_bytes(int64_t M, int64_t N, int64_t E) {
+  return 256 + (size_t)E * (round_up(M, 128) + round_up(N, 128)) * 4;
+}
 
 template <int F>
-static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipStream_t s) {
+static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipStream_t s, void* ws) {
   if constexpr (F == AVERIS_MXFP4) {
     if (cfg == KCFG_WSDW) {  // grouped weight gradient
       constexpr int S = kWsStages, L = kWsLoaders;
-      if (g.has_r1) hipLaunchKernelGGL((k_gemm_ws_dw<F, true, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
-      else hipLaunchKernelGGL((k_gemm_ws_dw<F, false, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+      const int64_t mpad = round_up(g.M, 128), npad = round_up(g.N, 128);
+      float* u_tab = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + 256);
+      float* v_tab = u_tab + g.E * mpad;
+      if (g.has_r1) {
+        hipLaunchKernelGGL(k_rank_one_vectors<F>, dim3((unsigned)ceil_div(g.M + g.N, 256), (unsigned)g.E), dim3(256), 0,
+                           s, g, u_tab, v_tab, mpad, npad);
+        hipLaunchKernelGGL((k_gemm_ws_dw<F, true, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab, mpad,
+                           npad);
+      } else {
+        hipLaunchKernelGGL((k_gemm_ws_dw<F, false, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab, mpad,
+                           npad);
+      }
       return;
     }
     if (cfg == KCFG_WSW) {  // 256 x 128 tiles: a 3-stage ring of 51 KB stages
@@ -1221,7 +1282,9 @@ hipError_t gemm_launch(const GemmPlan& p) {
                      ceil_div(K, (int64_t)kBKE) % p.splits == 0;
   if (cfg == KCFG_WS && !ws_ok) cfg = KCFG_SHORT;
   // grouped weight gradient, MXFP4: the warp-specialized form with per-group K
-  if (p.grouped == 2 && fmt == AVERIS_MXFP4 && !p.accumulate && !p.mu && K > 0) cfg = KCFG_WSDW;
+  if (p.grouped == 2 && fmt == AVERIS_MXFP4 && !p.accumulate && !p.mu && K > 0 && K < (int64_t(1) << 30) &&
+      E <= kDwMaxGroups)
+    cfg = KCFG_WSDW;  // (group lengths in the LDS table are int)
   if (kWsLongK && cfg == KCFG_LONG && ws_ok) cfg = KCFG_WS;
   if (kWsWide && cfg == KCFG_WS && K < 4096 && !p.mu_u &&
       ceil_div(M, (int64_t)256) * ceil_div(N, (int64_t)128) * p.splits >= cu_count())
@@ -1288,8 +1351,8 @@ hipError_t gemm_launch(const GemmPlan& p) {
   // one resident round of workgroups, each looping over its tiles
   g.n_work = (int)work;
   const int64_t grid = std::min<int64_t>(work, (int64_t)resident_per_cu(cfg) * cu_count());
-  if (fmt == AVERIS_MXFP4) launch_cfg<AVERIS_MXFP4>(cfg, mu_in, g, (unsigned)grid, p.stream);
-  else launch_cfg<AVERIS_NVFP4>(cfg, mu_in, g, (unsigned)grid, p.stream);
+  if (fmt == AVERIS_MXFP4) launch_cfg<AVERIS_MXFP4>(cfg, mu_in, g, (unsigned)grid, p.stream, p.ws);
+  else launch_cfg<AVERIS_NVFP4>(cfg, mu_in, g, (unsigned)grid, p.stream, p.ws);
   if (g.splits > 1) {
     const unsigned blocks = (unsigned)ceil_div(M * (N / 4), 256);
     if (fmt == AVERIS_MXFP4)

@@ -37,6 +37,7 @@ struct GemmPlan {
 int choose_splits(int fmt, int64_t M, int64_t N, int64_t K);
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int splits);
 size_t gemm_grouped_ws_bytes(int64_t M, int64_t N, int64_t E);
+size_t gemm_grouped_dw_ws_bytes(int64_t M, int64_t N, int64_t E);
 hipError_t gemm_launch(const GemmPlan& p);
 
 }  // namespace av

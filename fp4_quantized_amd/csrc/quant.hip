@@ -82,7 +82,8 @@ __device__ inline void h16_lanes(float* v, int lane) {
 // of rows t / LPR + RPB k, loaded in batches of 16 before use.  Column sums: fp32 over each
 // group of 8 rows, fp64 across groups and threads (fixed order); MINMAX (NVFP4): column min
 // and max too.  The partials go to the workspace; the workgroup then counts its arrival on its
-// strip's counter (device-scope fence + atomic).  The last one to arrive finalizes the strip:
+// strip's counter (agent-scope release; the last arriver acquires).  The last one to arrive
+// finalizes the strip:
 // fixed-order fp64 reduction of the strip's slabs -> mu (fp32; SPLIT without MEAN_GIVEN), the
 // strip's max |residual| (MINMAX: exact from the column min / max, since fl(x - mu) is
 // monotone in x) and max |(rotated) mean| as per-strip partials, and resets the counter to 0.
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
       sacc += s_sum[q][t];
       if (MINMAX) { lo = fminf(lo, s_min[q][t]); hi = fmaxf(hi, s_max[q][t]); }
     }
-    // device-coherent stores (they reach the point of coherence of all XCDs; no L2 flush)
+    // agent-scope stores: published to the finalizing workgroup by the release below
     const int64_t o = (int64_t)blockIdx.y * a.cols + c0 + t;
     __hip_atomic_store(a.psum + o, sacc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (MINMAX) {
@@ -209,16 +210,16 @@ __global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
   }
 
   // ---- arrival on the strip's counter; the last workgroup finalizes the strip ----
-  // the partial stores (wave 0) must be complete before thread 0 counts the arrival
-  asm volatile("" ::: "memory");
-  wait_vm<0>();
-  asm volatile("" ::: "memory");
+  // The partial stores happen before the arrival (workgroup barrier, then the counting thread's
+  // agent-scope release); the last arriver's acquire, and the acquire fence every thread of it
+  // issues after the barrier, make all other workgroups' partials visible to its loads.
   __syncthreads();
   uint32_t* counter = a.counters + ((int64_t)e * a.n_strips + strip) * kCounterStride;
   if (t == 0)
-    s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nsl - 1);
+    s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nsl - 1);
   __syncthreads();
   if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
   // kCsWaves == 1: the four waves split the slabs; otherwise wave q takes columns 64 q ..
   constexpr int SPLITS = kCsWaves == 1 ? 4 : 1;
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
   const int pb = SPLITS == 1 ? 0 : q * per, pe = SPLITS == 1 ? nsl : (pb + per < nsl ? pb + per : nsl);
   double sacc = 0.0;
   float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
-  // device-coherent loads: the other workgroups' partials, whatever XCD wrote them
+  // agent-scope loads of the other workgroups' partials, whatever XCD wrote them
   // (eight slabs per batch of loads, summed in slab order)
   if (cin && (a.mode & 1) && !(a.mode & 2))
     for (int p0 = pb; p0 < pe; p0 += 8) {

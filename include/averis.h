@@ -111,6 +111,10 @@ typedef struct averis_qtensor {
 
 int32_t averis_abi_version(void);
 const char *averis_status_string(int32_t status);
+/* SHA-1 (40 hex digits) of the sources the library was built from, fixed at build time, or
+ * "unknown".  A loader compares it with its copy of the sources to refuse a stale library.
+ * The returned string is static; the caller must not free it. */
+const char *averis_source_digest(void);
 
 /* -----------------------------------------------------------------------------------------
  * averis_split_quant -- column statistics, mean, subtraction, optional Hadamard, FP4 quant.

@@ -103,8 +103,9 @@ def test_grouped_weights_vanilla(fmt, fname):
     grouped_quant_case(w, [m] * E, fmt, split=False, tag=f"weights-{fname}")
 
 
-def moe_case(fmt, lens, m, n, seed, hadamard=False, experts=None, tag=""):
-    """Grouped forward, input gradient and weight gradient of one MoE linear, expert by expert."""
+def moe_case(fmt, lens, m, n, seed, hadamard=False, experts=None, tag="", split=True):
+    """Grouped forward, input gradient and weight gradient of one MoE linear, expert by expert
+    (split=False: the vanilla GEMMs, no mean terms)."""
     dev = device()
     rng = np.random.default_rng(seed)
     E = len(lens)
@@ -113,18 +114,19 @@ def moe_case(fmt, lens, m, n, seed, hadamard=False, experts=None, tag=""):
     d = workloads._grad(rng, L, n, "bf16")
     w = workloads._round(rng.standard_normal((E * m, n)) * 0.02, "bf16")
     offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
-    print(f"moe case {tag} E={E} L={L} m={m} n={n} fmt={fmt} h16={hadamard}", flush=True)
+    print(f"moe case {tag} E={E} L={L} m={m} n={n} fmt={fmt} h16={hadamard} split={split}", flush=True)
     grp = av.Groups(offs, dev)
     wgrp = av.Groups(np.arange(E + 1) * m, dev)
-    gx = av.split_quant_grouped(workloads.to_torch(x, "bf16", dev), grp, fmt, hadamard=hadamard)
-    gd = av.split_quant_grouped(workloads.to_torch(d, "bf16", dev), grp, fmt, hadamard=hadamard)
+    gx = av.split_quant_grouped(workloads.to_torch(x, "bf16", dev), grp, fmt, split=split, hadamard=hadamard)
+    gd = av.split_quant_grouped(workloads.to_torch(d, "bf16", dev), grp, fmt, split=split, hadamard=hadamard)
     gw = av.split_quant_grouped(workloads.to_torch(w, "bf16", dev), wgrp, fmt, split=False, hadamard=hadamard)
     w_fwd = av.stacked_weight_view(gw["col"], E, m)
     y = av.linear_fwd_grouped(gx["row"], gx["mean_q"], w_fwd, grp)
     dx = av.linear_bwd_dx_grouped(gd["row"], gd["mean_q"], gw["row"], grp)
     dw = av.linear_bwd_dw_grouped(gx["col"], gd["col"], gx["mean_q"], gd["mean_q"], grp)
     torch.cuda.synchronize()
-    mx, md = gx["mean"].cpu().numpy(), gd["mean"].cpu().numpy()
+    mx = gx["mean"].cpu().numpy() if split else [None] * E
+    md = gd["mean"].cpu().numpy() if split else [None] * E
     y, dx, dw = y.cpu().numpy(), dx.cpu().numpy(), dw.cpu().numpy()
     for e in (range(E) if experts is None else experts):
         a, b = int(offs[e]), int(offs[e + 1])
@@ -132,8 +134,8 @@ def moe_case(fmt, lens, m, n, seed, hadamard=False, experts=None, tag=""):
         if b == a:
             assert not dw[e].any(), f"{what}: empty expert dW"
             continue
-        ox = O.split_quant(x[a:b], fmt, hadamard=hadamard, mean=mx[e])
-        od = O.split_quant(d[a:b], fmt, hadamard=hadamard, mean=md[e])
+        ox = O.split_quant(x[a:b], fmt, split=split, hadamard=hadamard, mean=mx[e])
+        od = O.split_quant(d[a:b], fmt, split=split, hadamard=hadamard, mean=md[e])
         ow = O.split_quant(w[e * m:(e + 1) * m], fmt, split=False, hadamard=hadamard)
         ref_y = O.linear_fwd(ox["row"], ox["mean"], ow["col"])
         ref_dx = O.linear_bwd_dx(od["row"], od["mean"], ow["row"])
@@ -147,6 +149,22 @@ def moe_case(fmt, lens, m, n, seed, hadamard=False, experts=None, tag=""):
 @pytest.mark.parametrize("hadamard", [False, True])
 def test_grouped_linear_small(fmt, fname, hadamard):
     moe_case(fmt, [0, 37, 300, 1, 129, 0, 64], 256, 128, 23, hadamard, tag=f"small-{fname}")
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+def test_grouped_linear_small_vanilla(fmt, fname):
+    moe_case(fmt, [0, 37, 300, 1, 129, 0, 64], 256, 128, 27, tag=f"small-vanilla-{fname}", split=False)
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+@pytest.mark.parametrize("split", [True, False])
+def test_grouped_linear_empty_experts_between_full_ones(fmt, fname, split):
+    # 48 experts of 8 weight-gradient tiles each (384 units for 256 workgroups): a workgroup's
+    # units then belong to different experts, and empty experts (a third of them) sit between
+    # non-empty ones in its walk; every expert is checked
+    rng = np.random.default_rng(28)
+    lens = [0 if e % 3 == 1 else int(rng.integers(1, 400)) for e in range(48)]
+    moe_case(fmt, lens, 512, 256, 29, tag=f"gaps-{fname}-{'averis' if split else 'vanilla'}", split=split)
 
 
 @pytest.mark.parametrize("fmt,fname", FMTS)
