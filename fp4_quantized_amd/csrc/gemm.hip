@@ -24,6 +24,8 @@
 // Epilogue: out = alpha * acc + bias[col] + r1 * u[row] * v[col] (+ C when accumulating),
 // alpha = product of the operands' tensor decode scales (NVFP4) or 1.
 #include <algorithm>
+#include <utility>
+#include <vector>
 
 #include "launch.h"
 
@@ -861,22 +863,41 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
 //     multiplying waves read them from the stage of the unit's last K-step during its epilogue
 //     (the loaders refill that stage only after the next K-step's barrier).  Empty units store
 //     zeros (their rank-one factor l_e is 0).
+//   * Schedule: groups differ widely in K (a skewed routing gives one expert 30 K-steps per
+//     tile and another 1), so units are dealt by work, not by count.  The host ranks the groups
+//     by K-steps, longest first (kernel argument `order`); unit rank k is tile k % T of group
+//     order[k / T] (T tiles per group).  Round r hands ranks r G .. r G + G - 1 to the G
+//     workgroups, in reverse order on odd rounds (a snake deal), so every workgroup gets a
+//     near-equal sum of K-steps.  Workgroups are numbered XCD by XCD (dispatch puts workgroup b
+//     on XCD b % 8), so one XCD takes consecutive ranks: neighbouring tiles of one group, whose
+//     operands then meet in that XCD's L2.
 // Steps past the stream's end re-load the last step issued into the stage just freed, which
 // nobody reads.
 constexpr int kDwMaxGroups = 1024;  // groups of the LDS table (more: the three-stage kernel)
 constexpr int kUvStage = 2048;      // R1: the unit's u (first KB, 128 floats used) and v slices
 
+struct DwOrder { uint16_t e[kDwMaxGroups]; };  // groups, most K-steps first
+
 struct DwUnit { int e, ns; int64_t m0, n0; };
 
+// Logical index of workgroup b when the G workgroups are numbered XCD by XCD.
+__device__ __forceinline__ int xcd_local(int b, int G) {
+  const int x = b & 7, k = b >> 3, q = G >> 3, r = G & 7;
+  return x * q + (x < r ? x : r) + k;
+}
+
+// Rank of the u-th unit of logical workgroup lw in the snake deal over G workgroups.
+__device__ __forceinline__ int dw_rank(int u, int lw, int G) { return u * G + ((u & 1) ? G - 1 - lw : lw); }
+
 template <class C>
-__device__ __forceinline__ DwUnit dw_unit(const GemmArgs& gin, int lin, const int* s_len, const int* s_t256,
-                                          GemmArgs& g) {
+__device__ __forceinline__ DwUnit dw_unit(const GemmArgs& gin, int rank, const DwOrder& ord, const int* s_len,
+                                          const int* s_t256, GemmArgs& g) {
   g = gin;
   const int ntiles = gin.tiles_m * gin.tiles_n;
   DwUnit u;
-  u.e = lin / ntiles;
+  u.e = ord.e[uniform32(rank / ntiles)];
   int tm, tn;
-  tile_coords(lin % ntiles, gin.tiles_m, gin.tiles_n, gin.group_m, tm, tn);
+  tile_coords(rank % ntiles, gin.tiles_m, gin.tiles_n, gin.group_m, tm, tn);
   const int64_t len = uniform32(s_len[u.e]), t0 = (int64_t)uniform32(s_t256[u.e]) * C::BKE;
   const int64_t ke_pad = round_up(len, (int64_t)C::BKE);
   g.K = ke_pad; g.k_chunk = ke_pad;
@@ -908,7 +929,7 @@ __global__ __launch_bounds__(256) void k_rank_one_vectors(GemmArgs g, float* __r
 template <int FMT, bool R1, int S, int L>
 __global__ __launch_bounds__(64 * (4 + L), 1) void k_gemm_ws_dw(GemmArgs g, const float* __restrict__ u_tab,
                                                                 const float* __restrict__ v_tab, int64_t mpad,
-                                                                int64_t npad) {
+                                                                int64_t npad, DwOrder ord) {
   constexpr int WM = 2, WN = 2, TM = 2, TN = 2;
   using T = GemmTile<FMT, WM, WN, TM, TN, 2, 0, false>;
   using C = typename T::C;
@@ -921,10 +942,10 @@ __global__ __launch_bounds__(64 * (4 + L), 1) void k_gemm_ws_dw(GemmArgs g, cons
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S * SSZ];
   __shared__ int s_len[kDwMaxGroups], s_t256[kDwMaxGroups];
 
-  int first, stride, end;
-  xcd_tiles((int)blockIdx.x, (int)gridDim.x, g.n_work, first, stride, end);
-  if (first >= end) return;
-  const int ntw = (end - first + stride - 1) / stride;  // this workgroup's units
+  const int G = (int)gridDim.x, lw = xcd_local((int)blockIdx.x, G);
+  int ntw = 0;  // this workgroup's units
+  while (dw_rank(ntw, lw, G) < g.n_work) ++ntw;
+  if (ntw == 0) return;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
 
@@ -959,7 +980,7 @@ __global__ __launch_bounds__(64 * (4 + L), 1) void k_gemm_ws_dw(GemmArgs g, cons
     bool have = false;  // some unit of this workgroup has K-steps
     auto open_unit = [&](int u) __attribute__((always_inline)) {
       GemmArgs v;
-      const DwUnit du = dw_unit<C>(g, first + u * stride, s_len, s_t256, v);
+      const DwUnit du = dw_unit<C>(g, dw_rank(u, lw, G), ord, s_len, s_t256, v);
       cns = du.ns;
       if (cns > 0) {
 #pragma unroll
@@ -999,7 +1020,7 @@ __global__ __launch_bounds__(64 * (4 + L), 1) void k_gemm_ws_dw(GemmArgs g, cons
     int q = 0;
     for (int u = 0; u < ntw; ++u) {
       GemmArgs gu;
-      const int ns = dw_unit<C>(g, first + u * stride, s_len, s_t256, gu).ns;
+      const int ns = dw_unit<C>(g, dw_rank(u, lw, G), ord, s_len, s_t256, gu).ns;
       for (int st = 0; st < ns; ++st, ++q) {
         wait_vm<LPW * (S - 2)>();
         __builtin_amdgcn_s_barrier();
@@ -1016,7 +1037,7 @@ __global__ __launch_bounds__(64 * (4 + L), 1) void k_gemm_ws_dw(GemmArgs g, cons
   int q = 0;
   for (int u = 0; u < ntw; ++u) {
     GemmArgs gu;
-    const DwUnit du = dw_unit<C>(g, first + u * stride, s_len, s_t256, gu);
+    const DwUnit du = dw_unit<C>(g, dw_rank(u, lw, G), ord, s_len, s_t256, gu);
     t.clear();
     for (int st = 0; st < du.ns; ++st, ++q) {
       __builtin_amdgcn_s_barrier();
@@ -1188,21 +1209,28 @@ size_t gemm_grouped_dw_ws_bytes(int64_t M, int64_t N, int64_t E) {
 }
 
 template <int F>
-static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipStream_t s, void* ws) {
+static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipStream_t s, void* ws,
+                       const int64_t* h_offsets) {
   if constexpr (F == AVERIS_MXFP4) {
     if (cfg == KCFG_WSDW) {  // grouped weight gradient
       constexpr int S = kWsStages, L = kWsLoaders;
       const int64_t mpad = round_up(g.M, 128), npad = round_up(g.N, 128);
       float* u_tab = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + 256);
       float* v_tab = u_tab + g.E * mpad;
+      // groups ranked by K-steps, most first (stable: ties keep group order)
+      DwOrder ord;
+      std::vector<std::pair<int64_t, int>> ks((size_t)g.E);
+      for (int e = 0; e < g.E; ++e) ks[e] = {-ceil_div(h_offsets[e + 1] - h_offsets[e], (int64_t)kBKE), e};
+      std::stable_sort(ks.begin(), ks.end());
+      for (int e = 0; e < g.E; ++e) ord.e[e] = (uint16_t)ks[e].second;
       if (g.has_r1) {
         hipLaunchKernelGGL(k_rank_one_vectors<F>, dim3((unsigned)ceil_div(g.M + g.N, 256), (unsigned)g.E), dim3(256), 0,
                            s, g, u_tab, v_tab, mpad, npad);
         hipLaunchKernelGGL((k_gemm_ws_dw<F, true, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab, mpad,
-                           npad);
+                           npad, ord);
       } else {
         hipLaunchKernelGGL((k_gemm_ws_dw<F, false, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab, mpad,
-                           npad);
+                           npad, ord);
       }
       return;
     }
@@ -1351,8 +1379,8 @@ hipError_t gemm_launch(const GemmPlan& p) {
   // one resident round of workgroups, each looping over its tiles
   g.n_work = (int)work;
   const int64_t grid = std::min<int64_t>(work, (int64_t)resident_per_cu(cfg) * cu_count());
-  if (fmt == AVERIS_MXFP4) launch_cfg<AVERIS_MXFP4>(cfg, mu_in, g, (unsigned)grid, p.stream, p.ws);
-  else launch_cfg<AVERIS_NVFP4>(cfg, mu_in, g, (unsigned)grid, p.stream, p.ws);
+  if (fmt == AVERIS_MXFP4) launch_cfg<AVERIS_MXFP4>(cfg, mu_in, g, (unsigned)grid, p.stream, p.ws, p.h_offsets);
+  else launch_cfg<AVERIS_NVFP4>(cfg, mu_in, g, (unsigned)grid, p.stream, p.ws, p.h_offsets);
   if (g.splits > 1) {
     const unsigned blocks = (unsigned)ceil_div(M * (N / 4), 256);
     if (fmt == AVERIS_MXFP4)
