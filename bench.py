@@ -1,21 +1,32 @@
 #!/usr/bin/env python3
 """Throughput of the Averis hot path on one MI355X.
 
-A step is one pass of the whole path for the Qwen3-0.6B-shaped up_proj linear layer
-(l = 8192 tokens = 4 x 2048, m = 1024 -> n = 3072, bf16 inputs): split + FP4-quantize X and D
-(both layouts and the mean), quantize W, then the forward GEMM (bf16 Y), the input-gradient
-GEMM (bf16 dX) and the weight-gradient GEMM (fp32 dW) with the mean terms.  The headline
-format is MXFP4 (gfx950's native scaled-MFMA format); NVFP4-style blocks are reported beside it.
+Headline step: one training step of the seven linears of a Qwen3-0.6B-shaped transformer
+layer at l = 16384 tokens (q 1024->2048, k and v 1024->1024, o 2048->1024, gate and up
+1024->3072, down 3072->1024; bf16 inputs): split + FP4-quantize every distinct input (q, k
+and v share theirs, gate and up share theirs) and every output gradient, quantize every
+weight, then each linear's forward (bf16 Y), input-gradient (bf16 dX) and weight-gradient
+(fp32 dW) GEMM with the mean terms.  Format MXFP4 (gfx950's native scaled-MFMA format);
+NVFP4-style blocks and the vanilla (no split) step are timed beside it.
+value = GEMM flops of the step / the step's median cold time.
 
-Timing: the step is captured once in a HIP graph; each timed replay is bracketed by HIP events
-on the launching stream, after a 512 MiB read that evicts the 256 MB Infinity Cache and the
-L2, so inputs start in HBM.  value = GEMM flops of the step / step time.
+Timing: each measured call sequence is captured once in a HIP graph.  Cold replays follow a
+512 MiB read that evicts the L2s and the 256 MB Infinity Cache (inputs start in HBM); warm
+replays run back to back.  HIP events on the launching stream bracket every replay; median and
+minimum are reported.
+
+Other stages (parity configurations and the pages' comparisons): the same layer with
+independent inputs per linear, the up_proj layer (l = 8192), the down_proj layer in its four
+variants ({NVFP4, MXFP4} x {Hadamard off, on}, each also vanilla), the MoE layer, and Averis vs
+16x16-Hadamard preprocessing at the explainer's activation shapes (512 x 2048 tokens, 4096 and
+8192 channels).
 
 Prints one JSON line.  --gpus N > 1 is refused: everything here runs on one GPU.
 """
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -27,25 +38,59 @@ METRIC = "split+FP4-quant HBM GB/s; FP4 GEMM fwd+bwd TFLOP/s; Averis overhead % 
 PEAK_HBM_GBPS = 8000.0
 PEAK_FP4_TFLOPS = 10100.0
 PEAK_BF16_TFLOPS = 2500.0
+L_LAYER = 16384
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50, help="timed replays per measurement (cold and warm each)")
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=8192, help="token rows of the oracle's timed sample")
+    p.add_argument("--stages", default="all",
+                   help="comma list of stages to run: layer,independent,up_proj,down_proj,moe,prep,roofline")
     return p.parse_args()
 
 
-def quant_bytes(l, m, n, g, in_bytes=2):
-    """Algorithmic bytes of split+quant for X [l, m], D [l, n] and W [m, n]: each input read
-    once, two packed layouts written (codes 1/2 B + scales 1/g B per element), mean vectors."""
-    per = 2 * (0.5 + 1.0 / g)
-    elems = l * m + l * n + m * n
-    means = (m + n) * (4 + 0.5 + 1.0 / g)
-    return elems * (in_bytes + per) + means
+def log(msg):
+    print(f"# {msg}", file=sys.stderr, flush=True)
+
+
+def gpu_clocks():
+    """Current GPU clocks as reported by amd-smi (or rocm-smi), or None."""
+    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+        except (OSError, subprocess.TimeoutExpired):
+            continue
+        if r.returncode != 0 or not r.stdout.strip():
+            continue
+        try:
+            data = json.loads(r.stdout)
+        except ValueError:
+            return {"tool": cmd[0], "text": r.stdout.strip()[:400]}
+        return {"tool": cmd[0], "clocks": _clock_summary(data)}
+    return None
+
+
+def _clock_summary(data):
+    """The graphics and memory clocks (current, MHz) from an amd-smi / rocm-smi JSON dump."""
+    out = {}
+
+    def walk(o, path):
+        if isinstance(o, dict):
+            for k, v in o.items():
+                walk(v, path + [str(k)])
+        elif isinstance(o, list):
+            for i, v in enumerate(o):
+                walk(v, path + [str(i)])
+        else:
+            key = "/".join(path).lower()
+            if any(t in key for t in ("gfx", "sclk", "mclk", "mem")) and any(
+                    t in key for t in ("clk", "clock", "freq")) and len(out) < 16:
+                out["/".join(path[-3:])] = o
+    walk(data, [])
+    return out
 
 
 def main():
@@ -60,210 +105,297 @@ def main():
 
     import fp4_quantized_amd.averis as av
     from fp4_quantized_amd import workloads
-    from fp4_quantized_amd.step import LinearStep
+    from fp4_quantized_amd.step import LayerStep, LinearStep, MoEStep
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     av.lib()
+    stages = set(args.stages.split(",")) if args.stages != "all" else \
+        {"layer", "independent", "up_proj", "down_proj", "moe", "prep", "roofline"}
     dev = torch.device("cuda:0")
-    t0 = time.time()
-    lin = workloads.up_proj()
-    l, m = lin.x.shape
-    n = lin.d.shape[1]
-    x = workloads.to_torch(lin.x, "bf16", dev)
-    d = workloads.to_torch(lin.d, "bf16", dev)
-    w = workloads.to_torch(lin.w, "bf16", dev)
-    # Cache eviction between timed replays: read (not write) 512 MiB, so the L2 and the 256 MB
-    # Infinity Cache end up holding clean lines of another buffer and the step pays no
-    # write-back of someone else's dirty data.
+    # Cache eviction before cold replays: read (not write) 512 MiB, so the L2s and the 256 MB
+    # Infinity Cache end up holding clean lines of another buffer.
     flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-    print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    steps, warmup = args.steps, args.warmup
 
-    def timed(fn, steps, warmup):
+    def timed(fn, n=None, w=None):
+        """Median / min of cold and warm replays of fn captured in a graph (ms)."""
+        n = n or steps
+        w = warmup if w is None else w
         fn()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()
-        for _ in range(warmup):
+        for _ in range(w):
             g.replay()
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for i in range(steps):
+        cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in cold:
             flush.sum()
-            evs[i][0].record()
+            a.record()
             g.replay()
-            evs[i][1].record()
+            b.record()
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs]))  # ms
+        warm = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in warm:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        c = [a.elapsed_time(b) for a, b in cold]
+        wm = [a.elapsed_time(b) for a, b in warm]
+        del g
+        return {"cold_med": float(np.median(c)), "cold_min": float(np.min(c)),
+                "warm_med": float(np.median(wm)), "warm_min": float(np.min(wm))}
 
-    results = {}
-    for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
-        g = av.BLOCK[fmt]
-        r = {}
-        for split in (True, False):
-            st = LinearStep(x, d, w, fmt, split=split)
-            tag = "averis" if split else "vanilla"
-            r[f"{tag}_step_ms"] = timed(st.run, args.steps, args.warmup)
-            r[f"{tag}_quant_ms"] = timed(st.quantize, args.steps, args.warmup)
-            r[f"{tag}_gemm_ms"] = timed(st.gemms, args.steps, args.warmup)
-            print(f"# {name} {tag}: step {r[f'{tag}_step_ms']*1e3:.1f} us, quant {r[f'{tag}_quant_ms']*1e3:.1f} us, "
-                  f"gemm {r[f'{tag}_gemm_ms']*1e3:.1f} us", file=sys.stderr, flush=True)
-            del st
-        flops = 6.0 * l * m * n
-        qb = quant_bytes(l, m, n, g)
-        r["step_tflops"] = flops / (r["averis_step_ms"] * 1e-3) / 1e12
-        r["quant_GBps"] = qb / (r["averis_quant_ms"] * 1e-3) / 1e9
-        r["gemm_tflops"] = flops / (r["averis_gemm_ms"] * 1e-3) / 1e12
-        r["overhead_pct"] = 100.0 * (r["averis_step_ms"] - r["vanilla_step_ms"]) / r["vanilla_step_ms"]
-        results[name] = r
+    def r4(d):
+        return {k: round(v, 5) for k, v in d.items()}
 
-    # Layer sweep (the overhead target's workload): the seven Qwen3-0.6B-shaped linears at
-    # l = 16384, one step = all seven linears' quantize + fwd/dX/dW, Averis vs vanilla.
-    sweep = {}
-    layers = workloads.sweep_device(3, 16384, dev)
-    sweep_flops = sum(6.0 * x_.shape[0] * x_.shape[1] * d_.shape[1] for _, x_, d_, _ in layers)
-    for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
-        r = {}
-        for split in (True, False):
-            sts = [LinearStep(x_, d_, w_, fmt, split=split) for _, x_, d_, w_ in layers]
+    env = {"clocks_before": gpu_clocks(), "host_cores_affinity": len(os.sched_getaffinity(0)),
+           "device": torch.cuda.get_device_name(0)}
+    # measured copy bandwidth: a second denominator for the memory-bound kernels
+    src = torch.ones(256 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src))
+    env["copy_GBps"] = round(2 * src.numel() * 4 / (t_copy["cold_med"] * 1e-3) / 1e9, 1)
+    del src, dst
+    log(f"copy {env['copy_GBps']} GB/s")
 
-            def run_all():
-                for s_ in sts:
-                    s_.run()
-            tag = "averis" if split else "vanilla"
-            r[f"{tag}_step_ms"] = round(timed(run_all, max(3, args.steps // 4), max(1, args.warmup // 2)), 4)
-            del sts
-        r["overhead_pct"] = round(100.0 * (r["averis_step_ms"] - r["vanilla_step_ms"]) / r["vanilla_step_ms"], 2)
-        r["step_tflops"] = round(sweep_flops / (r["averis_step_ms"] * 1e-3) / 1e12, 1)
-        print(f"# sweep {name}: averis {r['averis_step_ms']*1e3:.0f} us, vanilla {r['vanilla_step_ms']*1e3:.0f} us, "
-              f"overhead {r['overhead_pct']:.1f} %", file=sys.stderr, flush=True)
-        sweep[name] = r
-    del layers
+    line_extra = {}
+    out = {}
 
-    # MoE grouped layer (every kernel one grouped launch over the experts): 8192 tokens routed
-    # top-8 over 64 experts with Zipf(1.1) skew (65,536 routed rows), hidden 2048, expert FFN 768;
-    # one step = the gate, up and down linears' split+quant, fwd, dX and dW.
-    from fp4_quantized_amd.step import MoEStep
-    moe_in = workloads.moe_device(4, device=dev)
-    moe = {}
-    for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
-        r = {}
-        for split in (True, False):
-            ms = MoEStep(*moe_in[:7], moe_in[7], fmt, split=split)
-            tag = "averis" if split else "vanilla"
-            r[f"{tag}_step_ms"] = round(timed(ms.run, max(3, args.steps // 4), max(1, args.warmup // 2)), 4)
-            flops = ms.flops
-            del ms
-        r["overhead_pct"] = round(100.0 * (r["averis_step_ms"] - r["vanilla_step_ms"]) / r["vanilla_step_ms"], 2)
-        r["step_tflops"] = round(flops / (r["averis_step_ms"] * 1e-3) / 1e12, 1)
-        print(f"# moe {name}: averis {r['averis_step_ms']*1e3:.0f} us, vanilla {r['vanilla_step_ms']*1e3:.0f} us, "
-              f"{r['step_tflops']} TFLOP/s", file=sys.stderr, flush=True)
-        moe[name] = r
-    moe_rows = int(moe_in[7][-1])
-    del moe_in
-
-    # Averis vs 16x16-Hadamard preprocessing at the operator level (the explainer's comparison of
-    # the two activation transforms): X [l, m] bf16 quantized for the forward GEMM (row layout),
-    # vanilla, with the mean-residual split, and with the Hadamard instead; the preprocessing cost
-    # of each is its time minus vanilla's.  l = 65536 tokens (the pages' 512 x 2048 scaled down by
-    # 16: every operand stays below 2^31 bytes), m = 4096 and 8192.
-    prep = {}
-    for m_ in (4096, 8192):
-        xa = workloads.activations_device(7, 65536, m_, dev)
+    # ---------------- headline: the layer step (shared inputs) ----------------
+    headline = None
+    if "layer" in stages or "roofline" in stages:
+        t0 = time.time()
+        layers = workloads.layer_device(3, L_LAYER, dev, shared=True)
+        log(f"layer inputs ready in {time.time() - t0:.1f}s")
+        res = {}
         for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
             r = {}
-            for tag, split, h16 in (("vanilla", False, False), ("averis", True, False), ("hadamard", False, True)):
-                out = av.split_quant_outputs(65536, m_, fmt, split, h16, row=True, col=False, device=dev)
-                ws = av.split_quant_workspace(65536, m_, fmt, split, h16, dev)
-                r[f"{tag}_ms"] = round(timed(lambda: av.split_quant(xa, fmt, split, h16, row=True, col=False,
-                                                                     out=out, ws=ws), args.steps, args.warmup), 4)
-                del out, ws
-            van = r["vanilla_ms"]
-            r["hadamard_over_averis_prep"] = round((r["hadamard_ms"] - van) / max(r["averis_ms"] - van, 1e-9), 2)
-            prep[f"{name}_m{m_}"] = r
-            print(f"# prep {name} l=65536 m={m_}: vanilla {van*1e3:.0f} us, averis {r['averis_ms']*1e3:.0f} us, "
-                  f"hadamard {r['hadamard_ms']*1e3:.0f} us", file=sys.stderr, flush=True)
-        del xa
+            for split in (True, False):
+                st = LayerStep(layers, fmt, split=split)
+                tag = "averis" if split else "vanilla"
+                r[tag] = r4(timed(st.run))
+                if fmt == av.MXFP4 or split:
+                    r[f"{tag}_quant"] = r4(timed(st.quantize))
+                    r[f"{tag}_gemm"] = r4(timed(st.gemms))
+                flops = st.flops
+                if split:
+                    qbytes = st.quant_bytes()
+                if fmt == av.MXFP4 and split:
+                    res["split_quant_bytes_mxfp4"] = int(qbytes)
+                if fmt == av.MXFP4 and split and "roofline" in stages:
+                    headline = st  # kept for the roofline launch below
+                else:
+                    del st
+                log(f"layer {name} {tag}: step {r[tag]['cold_med']*1e3:.1f} us cold, {r[tag]['warm_med']*1e3:.1f} warm")
+            r["step_tflops"] = round(flops / (r["averis"]["cold_med"] * 1e-3) / 1e12, 1)
+            r["overhead_pct"] = round(100.0 * (r["averis"]["cold_med"] - r["vanilla"]["cold_med"])
+                                      / r["vanilla"]["cold_med"], 2)
+            r["overhead_pct_warm"] = round(100.0 * (r["averis"]["warm_med"] - r["vanilla"]["warm_med"])
+                                           / r["vanilla"]["warm_med"], 2)
+            r["split_quant_GBps"] = round(qbytes / (r["averis_quant"]["cold_med"] * 1e-3) / 1e9, 1)
+            r["gemm_tflops"] = round(flops / (r["averis_gemm"]["cold_med"] * 1e-3) / 1e12, 1)
+            res[name] = r
+        res["gflop"] = round(flops / 1e9, 1)
+        out["layer"] = res
+        del layers
 
-    # Dominant kernel: the MXFP4 GEMM tile kernel.  The vanilla forward and input-gradient GEMMs
-    # are exactly one k_gemm launch each (2 l m n flops per launch).  A graph of REPS back-to-back
-    # (forward, input-gradient) pairs is replayed after a cache-evicting read; HIP events on the
-    # launching stream bracket each replay, so the per-launch time carries no event or launch
-    # gaps (inside a graph our kernels run back to back) and can be compared with the kernel
-    # trace of the same launches.  The first pair of a replay reads its operands from HBM, the
-    # rest find them in the caches.
-    REPS = 10
-    st = LinearStep(x, d, w, av.MXFP4, split=False)
-    st.quantize()
+    # ---------------- roofline: the step's longest kernel ----------------
+    roofline = None
+    if headline is not None:
+        c = next(c for c in headline.lin if c["name"] == "gate")  # gate / up forward, down dX: same shape
+        l, m, n = c["l"], c["m"], c["n"]
+        t = timed(lambda: av.linear_fwd(c["sx"]["row"], c["sx"]["mean_q"], c["sw"]["col"], out=c["y"], ws=c["ws_fwd"]))
+        launch_s = t["cold_med"] * 1e-3
+        op = 0.5 + 1.0 / 32
+        flops = 2.0 * l * m * n
+        nbytes = (l * m + n * m + m) * op + 2.0 * l * n
+        t_mfma, t_hbm = flops / (PEAK_FP4_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBPS * 1e9)
+        hbm_bound = t_hbm > t_mfma
+        roofline = {
+            "bound": "hbm" if hbm_bound else "mfma",
+            "kernel": "k_gemm_ws<MXFP4, mean term> forward GEMM, 16384 x 3072 x 1024, bf16 Y (gate and up "
+                      "forward, down input gradient: the step's longest launches)",
+            "achieved": round(nbytes / launch_s / 1e9, 1) if hbm_bound else round(flops / launch_s / 1e12, 1),
+            "peak": PEAK_HBM_GBPS if hbm_bound else PEAK_FP4_TFLOPS,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s",
+            "frac": round((t_hbm if hbm_bound else t_mfma) / launch_s, 4),
+            "traffic": gemm_traffic(),
+            "algorithmic_bytes": int(nbytes), "flops": flops,
+            "launch_us": {k: round(v * 1e3, 2) for k, v in t.items()},
+            "mfma_frac": round(t_mfma / launch_s, 4), "hbm_frac": round(t_hbm / launch_s, 4),
+            "frac_vs_measured_copy": round(nbytes / launch_s / 1e9 / env["copy_GBps"], 4),
+        }
+        log(f"roofline launch {t['cold_med']*1e3:.1f} us: {flops / launch_s / 1e12:.0f} TFLOP/s, "
+            f"{nbytes / launch_s / 1e9:.0f} GB/s")
+        del headline
 
-    def gemm_pairs():
-        for _ in range(REPS):
-            av.linear_fwd(st.sx["row"], None, st.sw["col"], out=st.y, ws=st.ws_fwd)
-            av.linear_bwd_dx(st.sd["row"], None, st.sw["row"], out=st.dx, ws=st.ws_dx)
+    # ---------------- the layer with independent inputs per linear ----------------
+    if "independent" in stages:
+        layers = workloads.layer_device(3, L_LAYER, dev, shared=False)
+        res = {}
+        for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
+            r = {}
+            for split in (True, False):
+                st = LayerStep(layers, fmt, split=split)
+                r["averis" if split else "vanilla"] = r4(timed(st.run, max(5, steps // 2)))
+                flops = st.flops
+                del st
+            r["overhead_pct"] = round(100.0 * (r["averis"]["cold_med"] - r["vanilla"]["cold_med"])
+                                      / r["vanilla"]["cold_med"], 2)
+            r["step_tflops"] = round(flops / (r["averis"]["cold_med"] * 1e-3) / 1e12, 1)
+            res[name] = r
+            log(f"layer (independent inputs) {name}: overhead {r['overhead_pct']} %")
+        out["layer_independent_inputs"] = res
+        del layers
 
-    launch_s = timed(gemm_pairs, args.steps, args.warmup) * 1e-3 / (2 * REPS)
-    achieved = 2.0 * l * m * n / launch_s / 1e12
-    # the binding roofline of each launch: max(MFMA time, HBM time of its algorithmic bytes:
-    # both packed operands read once, the bf16 output written once), averaged over the pair
-    op = 0.5 + 1.0 / 32
-    t_mfma = 2.0 * l * m * n / (PEAK_FP4_TFLOPS * 1e12)
-    t_hbm = [((l * m + n * m) * op + 2 * l * n) / (PEAK_HBM_GBPS * 1e9),   # Y [l, n]
-             ((l * n + m * n) * op + 2 * l * m) / (PEAK_HBM_GBPS * 1e9)]   # dX [l, m]
-    t_bind = sum(max(t_mfma, t) for t in t_hbm) / 2
-    roofline = {"bound": "mfma", "kernel": "k_gemm_ws<MXFP4> (forward and input-gradient GEMMs)",
-                "achieved": round(achieved, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_FP4_TFLOPS, 4), "traffic": gemm_traffic(),
-                "traffic_unit": "bytes per launch (HBM, counter runs)", "launch_us": round(launch_s * 1e6, 2),
-                "binding_roofline_us": round(t_bind * 1e6, 2), "frac_of_binding": round(t_bind / launch_s, 4)}
-    del st
+    # ---------------- up_proj (l = 8192) ----------------
+    if "up_proj" in stages:
+        lin = workloads.up_proj()
+        x, d, w = (workloads.to_torch(a, "bf16", dev) for a in (lin.x, lin.d, lin.w))
+        l, m = lin.x.shape
+        n = lin.d.shape[1]
+        res = {}
+        for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
+            r = {}
+            for split in (True, False):
+                st = LinearStep(x, d, w, fmt, split=split)
+                tag = "averis" if split else "vanilla"
+                r[tag] = r4(timed(st.run))
+                r[f"{tag}_quant"] = r4(timed(st.quantize))
+                r[f"{tag}_gemm"] = r4(timed(st.gemms))
+                del st
+            g = av.BLOCK[fmt]
+            qb = (l * m + l * n + m * n) * (2 + 2 * (0.5 + 1.0 / g)) + (m + n) * (4 + 0.5 + 1.0 / g)
+            r["step_tflops"] = round(6.0 * l * m * n / (r["averis"]["cold_med"] * 1e-3) / 1e12, 1)
+            r["split_quant_GBps"] = round(qb / (r["averis_quant"]["cold_med"] * 1e-3) / 1e9, 1)
+            r["gemm_tflops"] = round(6.0 * l * m * n / (r["averis_gemm"]["cold_med"] * 1e-3) / 1e12, 1)
+            r["overhead_pct"] = round(100.0 * (r["averis"]["cold_med"] - r["vanilla"]["cold_med"])
+                                      / r["vanilla"]["cold_med"], 2)
+            res[name] = r
+            log(f"up_proj {name}: step {r['averis']['cold_med']*1e3:.1f} us, split+quant {r['split_quant_GBps']} GB/s")
+        out["up_proj"] = res
+        del x, d, w, lin
+
+    # ---------------- down_proj (l = 16384) in its four variants ----------------
+    if "down_proj" in stages:
+        x, d, w = workloads.down_proj_device(2, L_LAYER, 3072, 1024, dev)
+        res = {}
+        for fmt, name in ((av.NVFP4, "nvfp4"), (av.MXFP4, "mxfp4")):
+            r = {}
+            for split, h16, tag in ((False, False, "vanilla"), (True, False, "averis"), (False, True, "hadamard"),
+                                    (True, True, "averis_hadamard")):
+                st = LinearStep(x, d, w, fmt, split=split, hadamard=h16)
+                r[tag] = r4(timed(st.run, max(5, steps // 2)))
+                del st
+            v = r["vanilla"]["cold_med"]
+            for tag in ("averis", "hadamard", "averis_hadamard"):
+                r[f"{tag}_overhead_pct"] = round(100.0 * (r[tag]["cold_med"] - v) / v, 2)
+            r["step_tflops"] = round(6.0 * L_LAYER * 3072 * 1024 / (r["averis"]["cold_med"] * 1e-3) / 1e12, 1)
+            res[name] = r
+            log(f"down_proj {name}: averis +{r['averis_overhead_pct']} %, hadamard +{r['hadamard_overhead_pct']} %")
+        out["down_proj"] = res
+        del x, d, w
+
+    # ---------------- MoE layer ----------------
+    if "moe" in stages:
+        moe_in = workloads.moe_device(4, device=dev)
+        res = {}
+        for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
+            r = {}
+            for split in (True, False):
+                ms = MoEStep(*moe_in[:8], moe_in[8], fmt, split=split)
+                r["averis" if split else "vanilla"] = r4(timed(ms.run, max(5, steps // 2)))
+                flops = ms.flops
+                del ms
+            r["overhead_pct"] = round(100.0 * (r["averis"]["cold_med"] - r["vanilla"]["cold_med"])
+                                      / r["vanilla"]["cold_med"], 2)
+            r["step_tflops"] = round(flops / (r["averis"]["cold_med"] * 1e-3) / 1e12, 1)
+            res[name] = r
+            log(f"moe {name}: averis {r['averis']['cold_med']*1e3:.0f} us, vanilla {r['vanilla']['cold_med']*1e3:.0f} us")
+        res["routed_rows"] = int(moe_in[8][-1])
+        res["gflop"] = round(flops / 1e9, 1)
+        out["moe"] = res
+        del moe_in
+
+    # ---------------- Averis vs 16x16 Hadamard preprocessing, the pages' shapes ----------------
+    if "prep" in stages:
+        res = {}
+        lp = 512 * 2048
+        for m_ in (4096, 8192):
+            xa = workloads.activations_device_chunked(7, lp, m_, dev)
+            for fmt, name in ((av.NVFP4, "nvfp4"), (av.MXFP4, "mxfp4")):
+                r = {}
+                for tag, split, h16 in (("vanilla", False, False), ("averis", True, False), ("hadamard", False, True)):
+                    o = av.split_quant_outputs(lp, m_, fmt, split, h16, row=True, col=False, device=dev)
+                    ws = av.split_quant_workspace(lp, m_, fmt, split, h16, dev)
+                    r[tag] = r4(timed(lambda: av.split_quant(xa, fmt, split, h16, row=True, col=False, out=o, ws=ws),
+                                      max(5, steps // 4), 2))
+                    del o, ws
+                van = r["vanilla"]["cold_med"]
+                r["averis_prep_ms"] = round(r["averis"]["cold_med"] - van, 4)
+                r["hadamard_prep_ms"] = round(r["hadamard"]["cold_med"] - van, 4)
+                r["hadamard_over_averis"] = round(r["hadamard_prep_ms"] / max(r["averis_prep_ms"], 1e-9), 2)
+                res[f"{name}_m{m_}"] = r
+                log(f"prep {name} l={lp} m={m_}: vanilla {van:.3f} ms, averis {r['averis']['cold_med']:.3f} ms, "
+                    f"hadamard {r['hadamard']['cold_med']:.3f} ms")
+            del xa
+        res["pages_blackwell_ms"] = {"averis_m4096": 2.0494, "averis_m8192": 3.9927, "hadamard_m4096": 9.1614,
+                                     "hadamard_m8192": 18.8421}
+        out["preprocessing"] = res
+
+    env["clocks_after"] = gpu_clocks()
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(lin, args.cpu_rows)
+        cpu = cpu_baseline()
 
-    mx = results["mxfp4"]
+    lay = out.get("layer", {})
+    mx = lay.get("mxfp4", {})
     line = {
         "metric": METRIC,
-        "value": round(mx["step_tflops"], 2),
+        "value": mx.get("step_tflops"),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(mx["averis_step_ms"], 5),
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(mx["averis"]["cold_med"], 5) if mx else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "mxfp4",
         "data": "synthetic",
-        "config": {"workload": "Qwen3-0.6B-shaped up_proj fwd+dX+dW: l=8192 (4x2048), m=1024, n=3072, "
-                               "bf16 in, bf16 Y/dX, fp32 dW, MXFP4 Averis split",
-                   "l": l, "m": m, "n": n, "format": "mxfp4"},
-        "split_quant": {"GBps": round(mx["quant_GBps"], 1), "frac_hbm": round(mx["quant_GBps"] / PEAK_HBM_GBPS, 4),
-                        "us": round(mx["averis_quant_ms"] * 1e3, 2)},
-        "gemm": {"TFLOPs": round(mx["gemm_tflops"], 1), "frac_fp4_peak": round(mx["gemm_tflops"] / PEAK_FP4_TFLOPS, 4),
-                 "us": round(mx["averis_gemm_ms"] * 1e3, 2)},
-        "overhead_pct_vs_vanilla": round(mx["overhead_pct"], 2),
-        "vanilla_ms_per_step": round(mx["vanilla_step_ms"], 5),
-        "nvfp4": {k: round(v, 5) for k, v in results["nvfp4"].items()},
-        "layer_sweep": dict(workload="Qwen3-0.6B-shaped layer sweep: q, k, v, o, gate, up, down linears at "
-                                     "l=16384, fwd+dX+dW each, bf16 in", l=16384, linears=7,
-                            gflop=round(sweep_flops / 1e9, 1), **sweep),
-        "moe": dict(workload="MoE FFN layer: 8192 tokens top-8 of 64 experts (Zipf 1.1), hidden 2048, expert FFN "
-                             "768, gate/up/down fwd+dX+dW, grouped launches", routed_rows=moe_rows,
-                    gflop=round(3 * 6 * moe_rows * 2048 * 768 / 1e9, 1), **moe),
-        "preprocessing": dict(workload="X [65536, m] bf16, row layout only; Averis split vs 16x16 Hadamard "
-                                        "vs vanilla FP4 quantization", **prep),
+        "config": {"workload": "Qwen3-0.6B-shaped transformer layer, 7 linears (q 1024->2048, k/v 1024->1024, "
+                               "o 2048->1024, gate/up 1024->3072, down 3072->1024) at l=16384 tokens, fwd+dX+dW "
+                               "each, bf16 in, bf16 Y/dX, fp32 dW, MXFP4 with the Averis split; q/k/v and gate/up "
+                               "share their split input",
+                   "l": L_LAYER, "format": "mxfp4", "timing": "median of cold (cache-evicted) graph replays"},
+        "split_quant": {"GBps": mx.get("split_quant_GBps"),
+                        "frac_hbm": round(mx["split_quant_GBps"] / PEAK_HBM_GBPS, 4) if mx else None,
+                        "frac_measured_copy": round(mx["split_quant_GBps"] / env["copy_GBps"], 4) if mx else None},
+        "gemm": {"TFLOPs": mx.get("gemm_tflops"),
+                 "frac_fp4_peak": round(mx["gemm_tflops"] / PEAK_FP4_TFLOPS, 4) if mx else None},
+        "overhead_pct_vs_vanilla": mx.get("overhead_pct"),
+        "overhead_pct_vs_vanilla_nvfp4": lay.get("nvfp4", {}).get("overhead_pct"),
+        "pages_overhead_pct_context": {"qwen3_0.6b": 2.01, "qwen3_7b_a1.5b": 2.20,
+                                       "note": "end-to-end training step on Blackwell, NVFP4; not this op-level "
+                                               "measurement"},
+        **out,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "env": env,
+        **line_extra,
     }
     print(json.dumps(line), flush=True)
 
 
 def gemm_traffic():
-    """HBM bytes per k_gemm launch from the committed counter summary, or None once the GEMM
-    source has changed since those counters were taken."""
+    """HBM bytes per launch of the roofline kernel from the committed counter summary, or None
+    once the GEMM source has changed since those counters were taken."""
     import re
-    prof = os.path.join(ROOT, "profiles", "k_gemm_mxfp4_up_proj_traffic.txt")
+    prof = os.path.join(ROOT, "profiles", "k_gemm_ws_mxfp4_mean_16384x3072x1024_traffic.txt")
     try:
         text = open(prof).read()
     except OSError:
@@ -276,33 +408,32 @@ def gemm_traffic():
     return int(m_t.group(1)) if gemm_source_digest()[:len(m_h.group(1))] == m_h.group(1) else None
 
 
-def cpu_baseline(lin, rows):
-    """The CPU oracle on a token sample of the same step: X and D rows [0, rows) with all of W.
-    W's quantization is a per-step cost; the rest scales with tokens, so the full-step time is
-    extrapolated as t_W + (l / rows) * t_rows."""
+def cpu_baseline():
+    """The CPU oracle on a bounded sample of the headline layer: the gate linear (1024 -> 3072)
+    at all 16384 tokens, MXFP4 with the split (split+quant of X, D and W, then the three GEMMs),
+    one of the layer's seven linears.  Throughput = that linear's GEMM flops / its time."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
+    from fp4_quantized_amd import workloads
     from oracle import averis_oracle as O
+    lin = workloads.up_proj_like([3, 4], L_LAYER, 1024, 3072, name="gate")
     l, m = lin.x.shape
     n = lin.d.shape[1]
-    xs, ds = lin.x[:rows], lin.d[:rows]
     t0 = time.perf_counter()
     sw = O.split_quant(lin.w, O.MXFP4, split=False)
-    t_w = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    sx = O.split_quant(xs, O.MXFP4)
-    sd = O.split_quant(ds, O.MXFP4)
+    sx = O.split_quant(lin.x, O.MXFP4)
+    sd = O.split_quant(lin.d, O.MXFP4)
     O.linear_fwd(sx["row"], sx["mean"], sw["col"])
     O.linear_bwd_dx(sd["row"], sd["mean"], sw["row"])
-    O.linear_bwd_dw(sx["col"], sd["col"], sx["mean"], sd["mean"], rows)
-    t_r = time.perf_counter() - t0
-    t_full = t_w + (l / rows) * t_r
+    O.linear_bwd_dw(sx["col"], sd["col"], sx["mean"], sd["mean"], l)
+    t = time.perf_counter() - t0
     blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(6.0 * l * m * n / t_full / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas),
-            "kind": "oracle",
-            "sample": f"MXFP4 step on X/D token rows 0..{rows - 1} of {l} with all of W "
-                      f"({t_w + t_r:.1f} s measured); full step extrapolated linearly in tokens: {t_full:.1f} s"}
+    return {"value": round(6.0 * l * m * n / t / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas),
+            "kind": "oracle", "host_cores_affinity": len(os.sched_getaffinity(0)),
+            "sample": f"the gate linear (1024 -> 3072) of the layer at all {l} tokens, MXFP4 split+quant of "
+                      f"X, D, W and fwd/dX/dW, one of the layer's seven linears: {t:.1f} s; numpy, fp64 GEMMs "
+                      f"on {blas} BLAS threads"}
 
 
 if __name__ == "__main__":

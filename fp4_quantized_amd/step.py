@@ -58,16 +58,81 @@ class LinearStep:
         self.gemms(stream)
 
 
+class LayerStep:
+    """One layer's quantized training step over several linears whose inputs may be shared:
+    every distinct input tensor X is split and quantized once (q, k and v read one X; gate and
+    up read one X), every output gradient D and weight W once per linear, then each linear's
+    forward, input-gradient and weight-gradient GEMMs.  linears: [(name, x, d, w)]."""
+
+    def __init__(self, linears, fmt, split=True, hadamard=False, out_dtype=torch.bfloat16):
+        self.fmt, self.split, self.hadamard = fmt, split, hadamard
+        self.quants = []  # (tensor, split, outputs, workspace) in launch order
+        qx = {}
+        self.lin = []
+        for name, x, d, w in linears:
+            l, m = x.shape
+            n = d.shape[1]
+            dev = x.device
+            if id(x) not in qx:
+                out = av.split_quant_outputs(l, m, fmt, split, hadamard, device=dev)
+                self.quants.append((x, split, out, av.split_quant_workspace(l, m, fmt, split, hadamard, dev)))
+                qx[id(x)] = out
+            sx = qx[id(x)]
+            sd = av.split_quant_outputs(l, n, fmt, split, hadamard, device=dev)
+            self.quants.append((d, split, sd, av.split_quant_workspace(l, n, fmt, split, hadamard, dev)))
+            sw = av.split_quant_outputs(m, n, fmt, False, hadamard, device=dev)
+            self.quants.append((w, False, sw, av.split_quant_workspace(m, n, fmt, False, hadamard, dev)))
+            y = torch.empty((l, n), dtype=out_dtype, device=dev)
+            dx = torch.empty((l, m), dtype=out_dtype, device=dev)
+            dw = torch.empty((m, n), dtype=torch.float32, device=dev)
+            self.lin.append(dict(name=name, l=l, m=m, n=n, sx=sx, sd=sd, sw=sw, y=y, dx=dx, dw=dw,
+                                 ws_fwd=av.linear_workspace(sx["row"], sw["col"]),
+                                 ws_dx=av.linear_workspace(sd["row"], sw["row"]),
+                                 ws_dw=av.linear_bwd_dw_workspace(sx["col"], sd["col"], l)))
+
+    @property
+    def flops(self):
+        """GEMM flops of every linear's fwd + dX + dW (the mean terms are not counted)."""
+        return sum(6 * c["l"] * c["m"] * c["n"] for c in self.lin)
+
+    def quant_bytes(self, in_bytes=2):
+        """Algorithmic bytes of the split+quant launches: each input read once, both packed
+        layouts written (codes and block scales), the mean vector and its quantized copy."""
+        g = av.BLOCK[self.fmt]
+        tot = 0.0
+        for t, sp, _, _ in self.quants:
+            r, c = t.shape
+            tot += r * c * (in_bytes + 2 * (0.5 + 1.0 / g)) + (c * (4 + 0.5 + 1.0 / g) if sp else 0.0)
+        return tot
+
+    def quantize(self, stream=None):
+        for t, sp, out, ws in self.quants:
+            av.split_quant(t, self.fmt, sp, self.hadamard, stream=stream, out=out, ws=ws)
+
+    def gemms(self, stream=None):
+        for c in self.lin:
+            mx = c["sx"]["mean_q"] if self.split else None
+            md = c["sd"]["mean_q"] if self.split else None
+            av.linear_fwd(c["sx"]["row"], mx, c["sw"]["col"], stream=stream, out=c["y"], ws=c["ws_fwd"])
+            av.linear_bwd_dx(c["sd"]["row"], md, c["sw"]["row"], stream=stream, out=c["dx"], ws=c["ws_dx"])
+            av.linear_bwd_dw(c["sx"]["col"], c["sd"]["col"], mx, md, c["l"], dw=c["dw"], stream=stream,
+                             ws=c["ws_dw"])
+
+    def run(self, stream=None):
+        self.quantize(stream)
+        self.gemms(stream)
+
+
 class MoEStep:
     """One MoE feed-forward layer's quantized training step over expert-contiguous routed rows,
     every kernel a grouped launch over all experts: gate and up (hidden -> ffn, sharing X's
     split) and down (ffn -> hidden), each forward, input gradient and weight gradient.
 
-    x [L, h] routed token states, x_down [L, f] the down projection's input, d_gu [L, f] the
-    output gradient used for both gate and up, d_dn [L, h]; w_gate and w_up [E * h, f] (E stacked
+    x [L, h] routed token states, x_down [L, f] the down projection's input, d_gate and d_up
+    [L, f] the output gradients of gate and up, d_dn [L, h]; w_gate and w_up [E * h, f] (E stacked
     [h, f]), w_down [E * f, h]; offsets [E + 1] over the L rows (host array)."""
 
-    def __init__(self, x, x_down, d_gu, d_dn, w_gate, w_up, w_down, offsets, fmt, split=True,
+    def __init__(self, x, x_down, d_gate, d_up, d_dn, w_gate, w_up, w_down, offsets, fmt, split=True,
                  out_dtype=torch.bfloat16):
         import numpy as np
         dev = x.device
@@ -82,7 +147,8 @@ class MoEStep:
         self.quants = []
         self.q = {}
         for name, t, grp, sp in (("x", x, self.grp, split), ("xd", x_down, self.grp, split),
-                                 ("dgu", d_gu, self.grp, split), ("ddn", d_dn, self.grp, split),
+                                 ("dg", d_gate, self.grp, split), ("du", d_up, self.grp, split),
+                                 ("ddn", d_dn, self.grp, split),
                                  ("wg", w_gate, wgrp_h, False), ("wu", w_up, wgrp_h, False),
                                  ("wd", w_down, wgrp_f, False)):
             out = av.split_quant_grouped_outputs(grp, t.shape[1], fmt, sp, device=dev)
@@ -92,7 +158,7 @@ class MoEStep:
         q = self.q
         mu = (lambda n: q[n]["mean_q"]) if split else (lambda n: None)
         self.gemms = []
-        for wq, xin, din, k_in, n_out in (("wg", "x", "dgu", h, f), ("wu", "x", "dgu", h, f), ("wd", "xd", "ddn", f, h)):
+        for wq, xin, din, k_in, n_out in (("wg", "x", "dg", h, f), ("wu", "x", "du", h, f), ("wd", "xd", "ddn", f, h)):
             y = torch.empty((L, n_out), dtype=out_dtype, device=dev)
             dx = torch.empty((L, k_in), dtype=out_dtype, device=dev)
             dw = torch.empty((E, k_in, n_out), dtype=torch.float32, device=dev)

@@ -159,6 +159,26 @@ def sweep_device(seed=3, l=16384, device="cuda"):
     return out
 
 
+def layer_device(seed=3, l=16384, device="cuda", shared=True):
+    """The seven linears of one Qwen3-0.6B-shaped transformer layer at l tokens, drawn on the
+    device with the recipe of `sweep_device`.  shared=True: q, k and v read the same input
+    X [l, 1024] and gate and up the same X [l, 1024], as in the layer (the attention and MLP
+    inputs after their norms); o and down have inputs of their own.  Every linear has its own
+    output gradient and weight.  Returns [(name, x, d, w)]; shared inputs are one tensor."""
+    layers = sweep_device(seed, l, device)
+    if not shared:
+        return layers
+    x_attn, x_mlp = layers[0][1], layers[4][1]
+    out = []
+    for name, x, d, w in layers:
+        if name in ("k", "v"):
+            x = x_attn
+        elif name == "up":
+            x = x_mlp
+        out.append((name, x, d, w))
+    return out
+
+
 def activations_device(seed, l, m, device="cuda"):
     """One activation matrix X [l, m] bf16 drawn on the device with the up_proj_like recipe
     (X = bf16(1 mu^T + R), R ~ Student-t(4), spike channels x20), for timing only."""
@@ -176,6 +196,55 @@ def activations_device(seed, l, m, device="cuda"):
     v = sum(normal(l, m) ** 2 for _ in range(4))
     x = (normal(l, m) / torch.sqrt(v / 4.0) + mu[None, :]).to(torch.bfloat16)
     return x
+
+
+def activations_device_chunked(seed, l, m, device="cuda", chunk=65536):
+    """activations_device for large l: the same recipe drawn in blocks of `chunk` rows (one
+    mean vector for all rows), so the fp32 temporaries stay at a few blocks' size."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+
+    def normal(*shape):
+        return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
+
+    g = normal(m)
+    mu = 3.0 * 2.0 ** 0.5 * g / torch.sqrt(torch.mean(g * g))
+    idx = torch.randperm(m, generator=gen, device=device)[:_n_spikes(m)]
+    mu[idx] *= 20.0
+    x = torch.empty((l, m), dtype=torch.bfloat16, device=device)
+    for r0 in range(0, l, chunk):
+        r1 = min(l, r0 + chunk)
+        v = sum(normal(r1 - r0, m) ** 2 for _ in range(4))
+        x[r0:r1] = (normal(r1 - r0, m) / torch.sqrt(v / 4.0) + mu[None, :]).to(torch.bfloat16)
+        del v
+    return x
+
+
+def down_proj_device(seed, l, m, n, device="cuda"):
+    """The down_proj_like recipe drawn on the device, for timing: X = bf16(silu(A) * B + 1 mu^T)
+    with A, B ~ N(0, 1), mu as in up_proj_like with rms(R) measured on the draw; D = bf16(1 mu_D^T
+    + N(0, 1e-6)); W ~ N(0, 0.02^2) [m, n].  Returns bf16 (x [l, m], d [l, n], w [m, n])."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+
+    def normal(*shape):
+        return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
+
+    a = normal(l, m)
+    r = torch.nn.functional.silu(a) * normal(l, m)
+    del a
+    g = normal(m)
+    mu = 3.0 * torch.sqrt(torch.mean(r * r)) * g / torch.sqrt(torch.mean(g * g))
+    idx = torch.randperm(m, generator=gen, device=device)[:_n_spikes(m)]
+    mu[idx] *= 20.0
+    x = (r + mu[None, :]).to(torch.bfloat16)
+    del r
+    gd = normal(n)
+    d = (normal(l, n) * 1e-3 + (1e-3 * gd / torch.sqrt(torch.mean(gd * gd)))[None, :]).to(torch.bfloat16)
+    w = (normal(m, n) * 0.02).to(torch.bfloat16)
+    return x, d, w
 
 
 @dataclass
@@ -232,8 +301,9 @@ def moe_device(seed=4, tokens=8192, hidden=2048, ffn=768, experts=64, topk=8, de
     (host, as in `moe`), token states drawn like `activations_device` and gathered per expert,
     the down projection's input likewise, output gradients N(0, 1e-6) plus their own mean,
     weights N(0, 0.02^2) stacked per expert.  Returns (x [L, hidden], x_down [L, ffn],
-    d_gu [L, ffn], d_dn [L, hidden], w_gate [E * hidden, ffn], w_up [E * hidden, ffn],
-    w_down [E * ffn, hidden], offsets [E + 1] host int64), bf16 tensors."""
+    d_gate [L, ffn], d_up [L, ffn], d_dn [L, hidden], w_gate [E * hidden, ffn],
+    w_up [E * hidden, ffn], w_down [E * ffn, hidden], offsets [E + 1] host int64), bf16
+    tensors; the gate and up projections have output gradients of their own."""
     import torch
     ids, counts = zipf_topk_counts(np.random.default_rng(seed), tokens, experts, topk)
     offsets = np.zeros(experts + 1, dtype=np.int64)
@@ -252,10 +322,10 @@ def moe_device(seed=4, tokens=8192, hidden=2048, ffn=768, experts=64, topk=8, de
         mu = 1e-3 * g / torch.sqrt(torch.mean(g * g))
         return (torch.randn(L, cols, generator=gen, device=device) * 1e-3 + mu[None, :]).to(torch.bfloat16)
 
-    d_gu, d_dn = grad(ffn), grad(hidden)
+    d_gate, d_up, d_dn = grad(ffn), grad(ffn), grad(hidden)
     w = [(torch.randn(experts * r, c, generator=gen, device=device) * 0.02).to(torch.bfloat16)
          for r, c in ((hidden, ffn), (hidden, ffn), (ffn, hidden))]
-    return x, x_down, d_gu, d_dn, w[0], w[1], w[2], offsets
+    return x, x_down, d_gate, d_up, d_dn, w[0], w[1], w[2], offsets
 
 
 def to_torch(a, dtype, device):

@@ -194,15 +194,15 @@ def test_moe_step_matches_grouped_calls():
     from fp4_quantized_amd.step import MoEStep
     dev = device()
     print("case moe-step", flush=True)
-    x, x_down, d_gu, d_dn, w_gate, w_up, w_down, offs = workloads.moe_device(5, tokens=512, hidden=256, ffn=128,
-                                                                               experts=8, device=dev)
-    st = MoEStep(x, x_down, d_gu, d_dn, w_gate, w_up, w_down, offs, av.MXFP4)
+    x, x_down, d_gate, d_up, d_dn, w_gate, w_up, w_down, offs = workloads.moe_device(
+        5, tokens=512, hidden=256, ffn=128, experts=8, device=dev)
+    st = MoEStep(x, x_down, d_gate, d_up, d_dn, w_gate, w_up, w_down, offs, av.MXFP4)
     st.run()
     torch.cuda.synchronize()
     grp = av.Groups(offs, dev)
     wgrp = av.Groups(np.arange(9) * 256, dev)
     gx = av.split_quant_grouped(x, grp, av.MXFP4)
-    gd = av.split_quant_grouped(d_gu, grp, av.MXFP4)
+    gd = av.split_quant_grouped(d_up, grp, av.MXFP4)
     gw = av.split_quant_grouped(w_up, wgrp, av.MXFP4, split=False)
     y = av.linear_fwd_grouped(gx["row"], gx["mean_q"], av.stacked_weight_view(gw["col"], 8, 256), grp, torch.bfloat16)
     dx = av.linear_bwd_dx_grouped(gd["row"], gd["mean_q"], gw["row"], grp, torch.bfloat16)

@@ -4,10 +4,11 @@ Run under `rocprofv3 --pmc FETCH_SIZE` and again under `--pmc WRITE_SIZE` (or ot
 `--kernel-trace` for the same launches' durations).  In order: a plain 64 MiB device copy (known
 bytes: it calibrates the counters, whose request-size accounting need not match this GPU's line
 size), then, each after a 512 MiB read that evicts the caches so that operands come from HBM:
-  default  the up_proj MXFP4 forward and input-gradient GEMMs (vanilla operands, the roofline
-           kernel of bench.py);
-  quant    the up_proj MXFP4 split+quant of X and D (mean split) and W, then the vanilla
-           quantization of X and D (l = 8192, m = 1024, n = 3072, bf16 inputs).
+  gemm   (default) the forward GEMM with the mean term of the layer's gate linear (MXFP4,
+         16384 x 3072 x 1024, bf16 Y): the longest launch of bench.py's layer step and its
+         roofline kernel; then the same GEMM without the mean term;
+  quant  the split+quant of the gate linear's input X [16384, 1024] and output gradient
+         D [16384, 3072] (MXFP4, mean split), then their vanilla quantization.
 """
 import os
 import sys
@@ -22,37 +23,30 @@ def main(mode="gemm"):
 
     import fp4_quantized_amd.averis as av
     from fp4_quantized_amd import workloads
-    from fp4_quantized_amd.step import LinearStep
+    from fp4_quantized_amd.step import LayerStep
 
     dev = torch.device("cuda:0")
     flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     a = torch.ones(16 << 20, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
-    lin = workloads.up_proj()
-    x, d, w = (workloads.to_torch(t, "bf16", dev) for t in (lin.x, lin.d, lin.w))
-    st = LinearStep(x, d, w, av.MXFP4, split=False)
+    gate = [c for c in workloads.layer_device(3, 16384, dev, shared=True) if c[0] == "gate"]
+    st = LayerStep(gate, av.MXFP4, split=True)
     st.quantize()
-    if mode == "quant":
-        sa = LinearStep(x, d, w, av.MXFP4, split=True)
-        sa.quantize()
-        torch.cuda.synchronize()
-        flush.sum()
-        b.copy_(a)
-        for s_, t, ou, ws_, split in ((sa, x, sa.sx, sa.ws_x, True), (sa, d, sa.sd, sa.ws_d, True),
-                                      (sa, w, sa.sw, sa.ws_w, False), (st, x, st.sx, st.ws_x, False),
-                                      (st, d, st.sd, st.ws_d, False)):
-            flush.sum()
-            av.split_quant(t, av.MXFP4, split, out=ou, ws=ws_)
-        torch.cuda.synchronize()
-        print("traffic probe done", flush=True)
-        return
+    c = st.lin[0]
     torch.cuda.synchronize()
     flush.sum()
     b.copy_(a)                      # calibration: 64 MiB read, 64 MiB written
-    flush.sum()
-    av.linear_fwd(st.sx["row"], None, st.sw["col"], out=st.y, ws=st.ws_fwd)
-    flush.sum()
-    av.linear_bwd_dx(st.sd["row"], None, st.sw["row"], out=st.dx, ws=st.ws_dx)
+    if mode == "quant":
+        sv = LayerStep(gate, av.MXFP4, split=False)
+        torch.cuda.synchronize()
+        for t, sp, out, ws in st.quants[:2] + sv.quants[:2]:
+            flush.sum()
+            av.split_quant(t, av.MXFP4, sp, out=out, ws=ws)
+    else:
+        flush.sum()
+        av.linear_fwd(c["sx"]["row"], c["sx"]["mean_q"], c["sw"]["col"], out=c["y"], ws=c["ws_fwd"])
+        flush.sum()
+        av.linear_fwd(c["sx"]["row"], None, c["sw"]["col"], out=c["y"], ws=c["ws_fwd"])
     torch.cuda.synchronize()
     print("traffic probe done", flush=True)
 
