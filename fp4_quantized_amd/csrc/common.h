@@ -9,7 +9,9 @@
 namespace av {
 
 constexpr int kKPad = 256;  // storage padding multiple along K (one GEMM K-step)
-constexpr int kColMult = 128;  // split_quant needs cols to be a multiple of this
+// split_quant needs cols to be a multiple of this: a row-layout thread quantizes one 32-element
+// (64-byte bf16) unit, all or nothing, and the code tails are zeroed in 16-byte (32-code) pieces
+constexpr int kColMult = 32;
 
 __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

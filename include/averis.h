@@ -123,7 +123,8 @@ const char *averis_source_digest(void);
  * materialized: X_R exists only as the quantized operands written here).
  *
  *  x      device [rows, cols] row-major, element type xdt, leading dimension ldx (elements).
- *         rows >= 0; cols > 0 and cols % 128 == 0; ldx >= cols, ldx * elem_size % 16 == 0.
+ *         rows >= 0; cols > 0 and cols % 32 == 0 (for NVFP4 too: the row layout is quantized in
+ *         32-element units); ldx >= cols, ldx * elem_size % 16 == 0.
  *  flags  AVERIS_SPLIT, AVERIS_HADAMARD16, AVERIS_MEAN_GIVEN (requires SPLIT).
  *  mean   device fp32 [cols].  With SPLIT: written with mu (fp32 of the fixed-order fp64 sum
  *         divided by rows; rows == 0 gives 0), or read if MEAN_GIVEN.  Without SPLIT: unused

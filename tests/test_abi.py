@@ -67,6 +67,7 @@ def split(x=FAKE, xdt=av.BF16, rows=256, cols=128, ldx=128, fmt=av.NVFP4, flags=
     (dict(flags=1 << 9), E_FLAGS),
     (dict(flags=av.MEAN_GIVEN), E_FLAGS),
     (dict(cols=100, ldx=100), E_SHAPE),
+    (dict(cols=48, ldx=48), E_SHAPE),
     (dict(ldx=64), E_SHAPE),
     (dict(rows=-1), E_SHAPE),
     (dict(x=None), E_NULL),

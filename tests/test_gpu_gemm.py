@@ -131,3 +131,43 @@ def test_dw_accumulate_and_determinism():
     torch.cuda.synchronize()
     assert torch.equal(dw1, dw2)
     assert torch.allclose(acc, base + dw1, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+def test_long_k_mean_term_gemv(fmt, fname):
+    # K = 8320 features: past the longest mean row the GEMM keeps in LDS (8192), so the MXFP4
+    # forward takes its mean term from the GEMV launch, as NVFP4 always does
+    lin = workloads.up_proj_like(61, 96, 8320, 128)
+    check_layer(lin, fmt, False, f"long-k-gemv-{fname}")
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+@pytest.mark.parametrize("hadamard", [False, True])
+def test_column_counts_multiple_of_32(fmt, fname, hadamard):
+    # m = 160 and n = 96 features: K of the forward and input-gradient GEMMs ends mid K-step and
+    # the row layouts' last 256-element piece is mostly padding
+    lin = workloads.up_proj_like(64, 300, 160, 96)
+    check_layer(lin, fmt, hadamard, f"cols-160-96-{fname}")
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+def test_split_k_bf16_outputs(fmt, fname):
+    # 256 x 256 outputs with K = 4096: few tiles, so the forward and input-gradient GEMMs split K
+    # and the fixed-order reduce writes the bf16 outputs (and adds the MXFP4 split shares of the
+    # mean term, the NVFP4 GEMV row)
+    lin = workloads.up_proj_like(62, 256, 4096, 256)
+    l, m = lin.x.shape
+    n = lin.d.shape[1]
+    assert lib_splits(fmt, l, n, m) > 1 and lib_splits(fmt, l, m, n) == 1
+    check_layer(lin, fmt, False, f"split-k-bf16-{fname}", out_dtype=torch.bfloat16)
+    lin2 = workloads.up_proj_like(63, 256, 256, 4096)
+    assert lib_splits(fmt, 256, 256, 4096) > 1
+    check_layer(lin2, fmt, False, f"split-k-bf16-dx-{fname}", out_dtype=torch.bfloat16)
+
+
+def lib_splits(fmt, M, N, K):
+    """Split-K count the library picks for an M x N x K GEMM, read from its workspace size (the
+    fixed header plus, when K is split, one fp32 M x N partial per split)."""
+    base = av.lib().averis_linear_workspace_size(M, N, 256, fmt)  # K = 256: one K-step, never split
+    ws = av.lib().averis_linear_workspace_size(M, N, K, fmt)
+    return (ws - base) // (4 * M * N) if ws > base else 1

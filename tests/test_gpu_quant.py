@@ -58,6 +58,16 @@ def test_ragged_bf16(fmt, fname, hadamard, rows):
 
 
 @pytest.mark.parametrize("fmt,fname", FMTS)
+@pytest.mark.parametrize("hadamard", [False, True])
+@pytest.mark.parametrize("cols", [32, 96, 160, 288])
+def test_column_counts_multiple_of_32(fmt, fname, hadamard, cols):
+    # columns past the last 256-column tile and past the last 64-column statistics strip
+    lin = workloads.up_proj_like(14, 333, cols, 128)
+    run_case(lin.x, "bf16", fmt, True, hadamard, tag=f"cols-{cols}-{fname}")
+    run_case(lin.x, "f32", fmt, True, hadamard, tag=f"cols-{cols}-f32-{fname}")
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
 def test_zero_rows(fmt, fname):
     run_case(np.zeros((0, 256), np.float32), "bf16", fmt, True, False, tag=f"empty-{fname}")
 
@@ -183,3 +193,55 @@ def test_single_layout_nvfp4_hadamard(layout, split):
     assert_q_equal(g[layout], o[layout], f"single {layout} layout")
     if split:
         assert_q_equal(g["mean_q"], o["mean"], "quantized mean")
+
+
+def _golden():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "blocks.json")) as f:
+        return json.load(f)
+
+
+def _golden_rows(values, rows=32, cols=128):
+    """fp32 [rows, cols]: row 0 starts with the golden values, everything else is zero."""
+    x = np.zeros((rows, cols), np.float32)
+    x[0, :len(values)] = np.asarray(values, np.float32)
+    return x
+
+
+def test_golden_mxfp4_subnormal_scale_block():
+    # hand-worked block with amax 2^-126: E = -128 clamps to -127 (scale byte 0, a subnormal
+    # 2^-127 decode scale) and the elements scale by 2^127 (tests/golden/blocks.json, MXFP4
+    # case 5): the GPU's row layout must hold exactly those codes and that scale byte
+    c = _golden()["mxfp4"][4]
+    g, _ = run_case(_golden_rows(c["values"]), "f32", av.MXFP4, False, False, tag="golden-mx-subnormal")
+    codes = O.unpack_nibbles(g["row"].codes[0].cpu().numpy())[:32]
+    np.testing.assert_array_equal(codes, c["codes"], err_msg=c["name"])
+    from tests.gpu_util import row_scales
+    assert int(row_scales(g["row"])[0, 0]) == c["scale"], c["name"]
+
+
+@pytest.mark.parametrize("case", [0, 1, 2])
+def test_golden_nvfp4_blocks_on_gpu(case):
+    # the hand-worked NVFP4 rows (tests/golden/blocks.json) as row 0 of an otherwise zero operand,
+    # so the tensor amax is the row's: case 2's tensor decode scale is an fp32 subnormal and its
+    # second block's decode scale falls below 2^-126 (that block's codes are zero)
+    c = _golden()["nvfp4"][case]
+    g, _ = run_case(_golden_rows(c["values"]), "f32", av.NVFP4, False, False, tag=f"golden-nv-{case}")
+    nv = len(c["values"])
+    codes = O.unpack_nibbles(g["row"].codes[0].cpu().numpy())[:nv]
+    np.testing.assert_array_equal(codes, c["codes"], err_msg=c["name"])
+    from tests.gpu_util import row_scales
+    np.testing.assert_array_equal(row_scales(g["row"])[0, :nv // 16], c["scales"], err_msg=c["name"])
+    assert np.float32(g["row"].tensor_scale[0].item()) == np.float32(c["s_dec"]), c["name"]
+
+
+def test_golden_nvfp4_hadamard_block_on_gpu():
+    # NVFP4 with the 16x16 rotation: the tensor scale comes from the rotated operand's amax
+    c = _golden()["nvfp4_hadamard"][0]
+    g, _ = run_case(_golden_rows(c["values"]), "f32", av.NVFP4, False, True, tag="golden-nv-h16")
+    codes = O.unpack_nibbles(g["row"].codes[0].cpu().numpy())[:32]
+    np.testing.assert_array_equal(codes, c["codes"], err_msg=c["name"])
+    from tests.gpu_util import row_scales
+    np.testing.assert_array_equal(row_scales(g["row"])[0, :2], c["scales"], err_msg=c["name"])
+    assert np.float32(g["row"].tensor_scale[0].item()) == np.float32(c["s_dec"]), c["name"]
