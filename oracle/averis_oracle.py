@@ -125,6 +125,63 @@ def mx_scale_exponent(amax):
 
 
 # --------------------------------------------------------------------------------------------
+# Stochastic rounding of E2M1 (an option: the pages round to nearest).  Random bits come from
+# Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and Shaw, "Parallel random
+# numbers: as easy as 1, 2, 3" (SC 2011): ten rounds of two 32 x 32 -> 64-bit multiplies on a
+# 4-word counter under a 2-word key, the key bumped by the Weyl constants between rounds.
+# --------------------------------------------------------------------------------------------
+
+PHILOX_M = (0xD2511F53, 0xCD9E8D57)
+PHILOX_W = (0x9E3779B9, 0xBB67AE85)
+_MASK32 = np.uint64(0xFFFFFFFF)
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 of counters ctr (uint32 array [..., 4]) under key (k0, k1): uint32 [..., 4]."""
+    ctr = np.asarray(ctr, dtype=np.uint64)
+    c0, c1, c2, c3 = (ctr[..., i] for i in range(4))
+    k0, k1 = np.uint64(key[0]), np.uint64(key[1])
+    m0, m1 = np.uint64(PHILOX_M[0]), np.uint64(PHILOX_M[1])
+    for rnd in range(10):
+        if rnd:
+            k0 = (k0 + np.uint64(PHILOX_W[0])) & _MASK32
+            k1 = (k1 + np.uint64(PHILOX_W[1])) & _MASK32
+        p0, p1 = c0 * m0, c2 * m1  # exact: 32 x 32 bits fit in 64
+        c0, c1, c2, c3 = (p1 >> np.uint64(32)) ^ c1 ^ k0, p1 & _MASK32, (p0 >> np.uint64(32)) ^ c3 ^ k1, p0 & _MASK32
+    return np.stack([c0, c1, c2, c3], axis=-1).astype(np.uint32)
+
+
+def sr_bits(outer, kpad, layout, seed):
+    """16 random bits per element of an [outer, kpad] operand: element (i, k) takes half k % 2
+    (low half first) of word (k % 8) // 2 of Philox4x32-10 at counter (k // 8, i, layout, 0)
+    under key (seed mod 2^32, seed // 2^32).  layout: 0 row layout, 1 column layout, 2 mean."""
+    blocks = kpad // 8
+    ctr = np.zeros((outer, blocks, 4), np.uint64)
+    ctr[..., 0] = np.arange(blocks, dtype=np.uint64)[None, :]
+    ctr[..., 1] = np.arange(outer, dtype=np.uint64)[:, None]
+    ctr[..., 2] = layout
+    w = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))  # [outer, blocks, 4]
+    halves = np.stack([w & 0xFFFF, w >> 16], axis=-1)                       # [outer, blocks, 4, 2]
+    return halves.reshape(outer, kpad).astype(np.uint32)
+
+
+def e2m1_encode_sr(v, u16):
+    """E2M1 with stochastic rounding: the magnitude a = |v| lies between neighbouring grid values
+    lo <= a < hi of {0, .5, 1, 1.5, 2, 3, 4, 6} and rounds to hi when u16 / 2^16 < (a - lo) /
+    (hi - lo), else to lo; a >= 6 gives 6.  (a - lo) is exact in fp32 (lo <= a < 2 lo, or lo = 0)
+    and hi - lo is a power of two, so the probability is exact.  The sign bit is v's."""
+    v = np.asarray(v, dtype=F32)
+    a = np.abs(v)
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=F32)
+    lo_i = np.clip(np.searchsorted(grid, a, side="right") - 1, 0, 6)
+    lo, hi = grid[lo_i], grid[lo_i + 1]
+    p = ((a - lo).astype(F32) / (hi - lo)).astype(F32)
+    up = np.asarray(u16, np.float64) / 65536.0 < p
+    c = np.where(a >= F32(6.0), 7, lo_i + up).astype(np.uint8)
+    return c | (np.signbit(v).astype(np.uint8) << 3)
+
+
+# --------------------------------------------------------------------------------------------
 # Split.  [rainbus] 方法步骤详情: mu_X = (1/l) 1^T X over the l = b*s token rows and
 # X_R = X - 1 mu_X; [paperlayer] §3 Method: the mean matrix is broadcast, never materialized.
 # --------------------------------------------------------------------------------------------
@@ -232,13 +289,14 @@ def nvfp4_tensor_scale(amax):
     return F32(F32(amax) / F32(2688.0))
 
 
-def quantize_nvfp4(r, s_dec):
+def quantize_nvfp4(r, s_dec, u16=None):
     """NVFP4-style Q_b along the last axis of fp32 r [outer, K], K % 16 == 0.
 
     Per 16-block b with a_b = max |r|:
       e_b = E4M3(fl(fl(a_b / 6) / s_dec)); S_b = fl(val(e_b) * s_dec); R_b = fl(1 / S_b);
       codes = E2M1(fl(r * R_b)).
-    Blocks with s_dec == 0, e_b == 0 or S_b below 2^-126 get all-zero codes.
+    Blocks with s_dec == 0, e_b == 0 or S_b below 2^-126 get all-zero codes.  u16 (uint [outer, K]):
+    stochastic rounding with these random bits instead of round to nearest.
     """
     r = np.asarray(r, dtype=F32)
     outer, K = r.shape
@@ -254,17 +312,17 @@ def quantize_nvfp4(r, s_dec):
         S = (e4m3_value(e).astype(F32) * s_dec).astype(F32)
         R = (F32(1.0) / S).astype(F32)
         v = (blk * R[:, :, None]).astype(F32)
-        codes = e2m1_encode(v)
+        codes = e2m1_encode(v) if u16 is None else e2m1_encode_sr(v, u16.reshape(outer, K // 16, 16))
     dead = (e == 0) | (S < F32(2.0 ** -126))
     codes[dead] = 0
     return pack_nibbles(codes.reshape(outer, K)), e
 
 
-def quantize_mxfp4(r):
+def quantize_mxfp4(r, u16=None):
     """MXFP4 Q_b along the last axis of fp32 r [outer, K], K % 32 == 0.
 
     Per 32-block: E = mx_scale_exponent(a_b); codes = E2M1(r * 2^-E) (exact scaling);
-    scale byte = E + 127.  All-zero blocks get all-zero codes.
+    scale byte = E + 127.  All-zero blocks get all-zero codes.  u16: stochastic rounding bits.
     """
     r = np.asarray(r, dtype=F32)
     outer, K = r.shape
@@ -273,14 +331,14 @@ def quantize_mxfp4(r):
     E = mx_scale_exponent(amax)
     R = np.ldexp(np.ones(E.shape, F32), -E).astype(F32)
     v = (blk * R[:, :, None]).astype(F32)
-    codes = e2m1_encode(v)
+    codes = e2m1_encode(v) if u16 is None else e2m1_encode_sr(v, u16.reshape(outer, K // 32, 32))
     codes[amax == 0] = 0
     return pack_nibbles(codes.reshape(outer, K)), (E + 127).astype(np.uint8)
 
 
-def quantize(r, fmt, rotate=False, k=None):
+def quantize(r, fmt, rotate=False, k=None, u16=None):
     """Q_b of the fp32 operand r [outer, K] along K; optional H16 first.  NVFP4 takes its
-    tensor scale from this operand's own amax (after rotation)."""
+    tensor scale from this operand's own amax (after rotation).  u16: stochastic rounding."""
     r = np.asarray(r, dtype=F32)
     if rotate:
         r = hadamard16_f32(r)
@@ -288,10 +346,10 @@ def quantize(r, fmt, rotate=False, k=None):
     if fmt == NVFP4:
         amax = F32(np.max(np.abs(r))) if r.size else F32(0)
         s_dec = nvfp4_tensor_scale(amax)
-        codes, scales = quantize_nvfp4(r, s_dec)
+        codes, scales = quantize_nvfp4(r, s_dec, u16)
         return QTensor(codes, scales, s_dec, fmt, k, rotate)
     if fmt == MXFP4:
-        codes, scales = quantize_mxfp4(r)
+        codes, scales = quantize_mxfp4(r, u16)
         return QTensor(codes, scales, None, fmt, k, rotate)
     raise ValueError(fmt)
 
@@ -324,13 +382,15 @@ def pad_k(r):
     return out
 
 
-def split_quant(x, fmt, split=True, hadamard=False, mean=None):
+def split_quant(x, fmt, split=True, hadamard=False, mean=None, sr_seed=None):
     """Returns dict(mu64, mu32, row=QTensor [rows, cols], col=QTensor [cols, rows],
     mean=QTensor [1, cols] or None), each stored zero-padded along K to a multiple of KPAD.
 
     `mean` (fp32 [cols]) replaces the computed mean -- used to quantize with the exact mean
     vector another implementation produced.  split=False is the vanilla quantizer (also the
-    one for weights): no mean, no mean operand.
+    one for weights): no mean, no mean operand.  sr_seed (uint64): E2M1 with stochastic
+    rounding, random bits sr_bits(.., layout 0 / 1 / 2, seed) for the row / column / mean
+    operand.
     """
     x = np.asarray(x)
     rows, cols = x.shape
@@ -344,9 +404,11 @@ def split_quant(x, fmt, split=True, hadamard=False, mean=None):
     else:
         mu32 = None
         r = np.asarray(x, dtype=F32)
-    q_row = quantize(pad_k(r), fmt, rotate=hadamard, k=cols)
-    q_col = quantize(pad_k(r.T), fmt, rotate=hadamard, k=rows)
-    q_mean = quantize(pad_k(mu32[None, :]), fmt, rotate=hadamard, k=cols) if split else None
+    rp, cp = round_up(rows, KPAD), round_up(cols, KPAD)
+    bits = (lambda o, kp, lay: None) if sr_seed is None else (lambda o, kp, lay: sr_bits(o, kp, lay, sr_seed))
+    q_row = quantize(pad_k(r), fmt, rotate=hadamard, k=cols, u16=bits(rows, cp, 0))
+    q_col = quantize(pad_k(r.T), fmt, rotate=hadamard, k=rows, u16=bits(cols, rp, 1))
+    q_mean = quantize(pad_k(mu32[None, :]), fmt, rotate=hadamard, k=cols, u16=bits(1, cp, 2)) if split else None
     return dict(mu64=mu64, mu32=mu32, row=q_row, col=q_col, mean=q_mean)
 
 

@@ -449,3 +449,75 @@ def test_grouped_linear_stacks_per_expert_results():
     u = O.dequantize(sx[2]["mean"])[0, :m]
     v = O.dequantize(sd[2]["mean"])[0, :n]
     np.testing.assert_allclose(dw[2] - no_mean, 50.0 * np.outer(u, v), rtol=1e-12, atol=1e-18)
+
+
+# ------------------------------------------------------------- stochastic rounding -----
+
+def test_philox4x32_10_known_answers():
+    # the known-answer vectors published with the Random123 library for philox4x32 with 10
+    # rounds (counter, key -> output)
+    kat = [((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+           ((0xFFFFFFFF,) * 4, (0xFFFFFFFF,) * 2, (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+           ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+            (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1))]
+    for ctr, key, want in kat:
+        got = O.philox4x32_10(np.array([ctr], dtype=np.uint64), key)[0]
+        assert [int(v) for v in got] == list(want)
+
+
+def _grid_floor_ceil(a):
+    """Largest grid magnitude <= a and smallest >= a (capped at 6), by exhaustive search."""
+    g = GRID[None, :]
+    fl = np.where(g <= a[:, None], g, -1.0).max(axis=1)
+    ce = np.where(g >= a[:, None], g, 99.0).min(axis=1)
+    return fl, np.minimum(ce, 6.0)
+
+
+def test_sr_extreme_draws_are_directed_roundings():
+    # every positive bf16 value below 8: the draw u = 0 rounds every magnitude up to the next
+    # grid value (ties: values on the grid stay), the draw u = 2^16 - 1 rounds down unless the
+    # value is within 2^-16 of a step below the next grid value
+    u = np.arange(1 << 16, dtype=np.uint32) << 16
+    v = u.view(np.float32)
+    v = v[np.isfinite(v) & (v > 0) & (v < 8)]
+    fl, ce = _grid_floor_ceil(v.astype(np.float64))
+    up = O.e2m1_value(O.e2m1_encode_sr(v, np.zeros(v.shape, np.uint32)))
+    np.testing.assert_array_equal(up, np.where(v >= 6, 6.0, ce))
+    down = O.e2m1_value(O.e2m1_encode_sr(v, np.full(v.shape, 0xFFFF, np.uint32)))
+    step = np.where(ce > fl, ce - fl, 1.0)
+    near_top = (v.astype(np.float64) - fl) / step > 65535 / 65536
+    np.testing.assert_array_equal(down, np.where(v >= 6, 6.0, np.where(near_top, ce, fl)))
+    np.testing.assert_array_equal(O.e2m1_encode_sr(-v, np.zeros(v.shape, np.uint32)) >> 3, 1)
+
+
+def test_sr_is_unbiased_over_every_draw():
+    # averaged over all 2^16 draws the rounded magnitude equals the input to within
+    # step * 2^-16 (exactly when the position between the neighbours has <= 16 fraction bits)
+    rng = np.random.default_rng(51)
+    v = np.concatenate([rng.uniform(0, 6, 200), [0.0, 0.5, 0.3, 2.75, 5.999, 4.0]]).astype(np.float32)
+    draws = np.arange(1 << 16, dtype=np.uint32)
+    for x in v:
+        mean = O.e2m1_value(O.e2m1_encode_sr(np.full(draws.shape, x, np.float32), draws)).mean()
+        fl, ce = _grid_floor_ceil(np.array([float(x)]))
+        assert abs(mean - float(x)) <= (ce[0] - fl[0]) * 2.0 ** -16 + 1e-12, x
+
+
+def test_sr_split_quant_is_seeded_and_one_step_from_nearest():
+    # same seed -> same codes; another seed -> other codes; every stochastically rounded value is
+    # one of the two grid neighbours of the scaled input (scales are those of round to nearest)
+    x, _, _ = _rand_layer(52, l=96, m=64, n=32)
+    for fmt in (O.NVFP4, O.MXFP4):
+        a = O.split_quant(x, fmt, sr_seed=7)
+        b = O.split_quant(x, fmt, sr_seed=7)
+        c = O.split_quant(x, fmt, sr_seed=8)
+        r = O.split_quant(x, fmt)
+        for lay in ("row", "col", "mean"):
+            np.testing.assert_array_equal(a[lay].codes, b[lay].codes)
+            np.testing.assert_array_equal(a[lay].scales, r[lay].scales)
+        assert not np.array_equal(a["row"].codes, c["row"].codes)
+        dq_sr, dq_rn = O.dequantize(a["row"]), O.dequantize(r["row"])
+        g = O.BLOCK[fmt]
+        scale = np.repeat(O.dequantize(O.QTensor(np.full_like(r["row"].codes, 0x22), r["row"].scales,
+                                                 r["row"].s_dec, fmt, r["row"].k, False))[:, ::g], g, axis=1)
+        steps = np.abs(dq_sr - dq_rn) / np.where(scale > 0, scale, 1.0)  # in units of the block scale
+        assert steps.max() <= 2.0 + 1e-9  # neighbours differ by at most one grid step (<= 2 units)

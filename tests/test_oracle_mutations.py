@@ -50,7 +50,7 @@ def test_ties_away_from_even_is_caught(monkeypatch):
 
 def test_missing_divide_by_six_in_nvfp4_scale_is_caught(monkeypatch):
     orig = O.quantize_nvfp4
-    monkeypatch.setattr(O, "quantize_nvfp4", lambda r, s: orig(r, np.float32(s) * np.float32(6)))
+    monkeypatch.setattr(O, "quantize_nvfp4", lambda r, s, u16=None: orig(r, np.float32(s) * np.float32(6), u16))
     _fails(P.test_golden_nvfp4_blocks, 0)
 
 
@@ -82,7 +82,7 @@ def test_nvfp4_amax_before_rotation_is_caught(monkeypatch):
 
 
 def test_subnormal_decode_scale_not_zeroed_is_caught(monkeypatch):
-    def bad(r, s_dec):  # the NVFP4 block quantizer without the "decode scale below 2^-126" rule
+    def bad(r, s_dec, u16=None):  # the NVFP4 block quantizer without the "decode scale below 2^-126" rule
         r = np.asarray(r, dtype=np.float32)
         outer, K = r.shape
         blk = r.reshape(outer, K // 16, 16)
@@ -110,3 +110,26 @@ def test_unrotated_mean_under_hadamard_is_caught(monkeypatch):
         return out
     monkeypatch.setattr(O, "split_quant", bad)
     _fails(P.test_hadamard_split_quant_fwd_dx_close_to_unquantized)
+
+
+def test_philox_key_bumped_before_the_first_round_is_caught(monkeypatch):
+    orig = O.philox4x32_10
+
+    def bad(ctr, key):  # one bump too many: the first round already uses the bumped key
+        return orig(ctr, ((key[0] + O.PHILOX_W[0]) & 0xFFFFFFFF, (key[1] + O.PHILOX_W[1]) & 0xFFFFFFFF))
+    monkeypatch.setattr(O, "philox4x32_10", bad)
+    _fails(P.test_philox4x32_10_known_answers)
+
+
+def test_sr_rounding_up_on_equal_draw_is_caught(monkeypatch):
+    def bad(v, u16):  # "<=" in place of "<": values on the grid round up on the draw 0
+        v = np.asarray(v, np.float32)
+        a = np.abs(v)
+        grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float32)
+        lo_i = np.clip(np.searchsorted(grid, a, side="right") - 1, 0, 6)
+        p = ((a - grid[lo_i]) / (grid[lo_i + 1] - grid[lo_i])).astype(np.float32)
+        up = np.asarray(u16, np.float64) / 65536.0 <= p
+        c = np.where(a >= 6, 7, lo_i + up).astype(np.uint8)
+        return c | (np.signbit(v).astype(np.uint8) << 3)
+    monkeypatch.setattr(O, "e2m1_encode_sr", bad)
+    _fails(P.test_sr_extreme_draws_are_directed_roundings)
