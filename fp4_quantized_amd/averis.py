@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaveris.s
 
 EXPORTS = [
     "averis_abi_version", "averis_status_string", "averis_source_digest",
-    "averis_split_quant_workspace_size", "averis_split_quant",
+    "averis_split_quant_workspace_size", "averis_split_quant", "averis_split_quant_sr",
     "averis_linear_workspace_size", "averis_linear_fwd", "averis_linear_bwd_dx",
     "averis_linear_bwd_dw_workspace_size", "averis_linear_bwd_dw",
     "averis_split_quant_grouped_workspace_size", "averis_split_quant_grouped",
@@ -81,6 +81,7 @@ def lib():
             "averis_source_digest": (ctypes.c_char_p, []),
             "averis_split_quant_workspace_size": (SZ, [I64, I64, I32, U32]),
             "averis_split_quant": (I32, [P, I32, I64, I64, I64, I32, U32, P, Q, Q, Q, P, SZ, P]),
+            "averis_split_quant_sr": (I32, [P, I32, I64, I64, I64, I32, U32, ctypes.c_uint64, P, Q, Q, Q, P, SZ, P]),
             "averis_linear_workspace_size": (SZ, [I64, I64, I64, I32]),
             "averis_linear_fwd": (I32, [Q, Q, Q, P, I32, I64, P, SZ, P]),
             "averis_linear_bwd_dx": (I32, [Q, Q, Q, P, I32, I64, P, SZ, P]),
@@ -180,13 +181,14 @@ def split_quant_workspace(rows, cols, fmt, split=True, hadamard=False, device="c
 
 def split_quant(x: torch.Tensor, fmt: int, split: bool = True, hadamard: bool = False,
                 mean: torch.Tensor | None = None, row: bool = True, col: bool = True, stream=None,
-                out=None, ws=None):
+                out=None, ws=None, sr_seed: int | None = None):
     """Mean, residual and FP4 quantization of x [rows, cols] (bf16 or fp32, row-major).
 
     Returns dict(mean=fp32 [cols] or None, row=QTensor [rows, cols] or None,
     col=QTensor [cols, rows] or None, mean_q=QTensor [1, cols] or None).
     `mean` given: used instead of the column mean (MEAN_GIVEN).  `out` / `ws`: preallocated
-    outputs (from split_quant_outputs) and workspace (from split_quant_workspace)."""
+    outputs (from split_quant_outputs) and workspace (from split_quant_workspace).  `sr_seed`:
+    stochastic rounding of the E2M1 codes with this 64-bit seed (averis_split_quant_sr)."""
     assert x.dim() == 2 and x.is_cuda
     rows, cols = x.shape
     assert rows == 0 or x.stride(1) == 1, "x must be row-major"
@@ -202,10 +204,14 @@ def split_quant(x: torch.Tensor, fmt: int, split: bool = True, hadamard: bool = 
     if ws is None:
         ws = split_quant_workspace(rows, cols, fmt, split, hadamard, dev)
     L = lib()
-    _check(L.averis_split_quant(x.data_ptr() if rows else None, _dtype_code(x), rows, cols, ldx, fmt,
-                                flags, mu.data_ptr() if mu is not None else None, _ptr(out["row"]),
-                                _ptr(out["col"]), _ptr(out["mean_q"]), ws.data_ptr(), ws.numel(),
-                                _stream(stream)))
+    xp, dt, mp = x.data_ptr() if rows else None, _dtype_code(x), mu.data_ptr() if mu is not None else None
+    if sr_seed is None:
+        _check(L.averis_split_quant(xp, dt, rows, cols, ldx, fmt, flags, mp, _ptr(out["row"]), _ptr(out["col"]),
+                                    _ptr(out["mean_q"]), ws.data_ptr(), ws.numel(), _stream(stream)))
+    else:
+        _check(L.averis_split_quant_sr(xp, dt, rows, cols, ldx, fmt, flags, int(sr_seed), mp, _ptr(out["row"]),
+                                       _ptr(out["col"]), _ptr(out["mean_q"]), ws.data_ptr(), ws.numel(),
+                                       _stream(stream)))
     return out
 
 

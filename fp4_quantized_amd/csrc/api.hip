@@ -86,9 +86,10 @@ size_t averis_split_quant_workspace_size(int64_t rows, int64_t cols, int32_t fmt
   return split_quant_ws_bytes(rows, cols);
 }
 
-int32_t averis_split_quant(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ldx, int32_t fmt,
-                           uint32_t flags, float* mean, const averis_qtensor* q_row, const averis_qtensor* q_col,
-                           const averis_qtensor* q_mean, void* ws, size_t ws_bytes, void* stream) {
+static int32_t split_quant_common(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ldx, int32_t fmt,
+                                  uint32_t flags, float* mean, const averis_qtensor* q_row,
+                                  const averis_qtensor* q_col, const averis_qtensor* q_mean, void* ws,
+                                  size_t ws_bytes, void* stream, bool sr, uint64_t seed) {
   if (!dtype_ok(xdt)) return AVERIS_E_DTYPE;
   if (!fmt_ok(fmt)) return AVERIS_E_FORMAT;
   if (flags & ~(AVERIS_SPLIT | AVERIS_HADAMARD16 | AVERIS_MEAN_GIVEN)) return AVERIS_E_FLAGS;
@@ -115,7 +116,24 @@ int32_t averis_split_quant(const void* x, int32_t xdt, int64_t rows, int64_t col
 
   SplitQuantPlan p{x, xdt, rows, cols, ldx, fmt, split, h16, given, mean, q_row, q_col, q_mean, ws,
                    reinterpret_cast<hipStream_t>(stream)};
+  p.sr = sr;
+  p.seed = seed;
   return split_quant_launch(p) == hipSuccess ? AVERIS_OK : AVERIS_E_HIP;
+}
+
+int32_t averis_split_quant(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ldx, int32_t fmt,
+                           uint32_t flags, float* mean, const averis_qtensor* q_row, const averis_qtensor* q_col,
+                           const averis_qtensor* q_mean, void* ws, size_t ws_bytes, void* stream) {
+  return split_quant_common(x, xdt, rows, cols, ldx, fmt, flags, mean, q_row, q_col, q_mean, ws, ws_bytes, stream,
+                            false, 0);
+}
+
+int32_t averis_split_quant_sr(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ldx, int32_t fmt,
+                              uint32_t flags, uint64_t seed, float* mean, const averis_qtensor* q_row,
+                              const averis_qtensor* q_col, const averis_qtensor* q_mean, void* ws, size_t ws_bytes,
+                              void* stream) {
+  return split_quant_common(x, xdt, rows, cols, ldx, fmt, flags, mean, q_row, q_col, q_mean, ws, ws_bytes, stream,
+                            true, seed);
 }
 
 size_t averis_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t fmt) {

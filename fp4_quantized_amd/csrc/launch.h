@@ -15,6 +15,8 @@ struct SplitQuantPlan {
   // grouped (MoE) operands: E > 0 groups of input rows [offsets[e], offsets[e+1]); device
   // offsets for the kernels, a host copy for grid sizing
   const int64_t* d_offsets; const int64_t* h_offsets; int64_t E;
+  // stochastic rounding of the E2M1 codes with this Philox key (dense launches only)
+  bool sr; uint64_t seed;
 };
 size_t split_quant_ws_bytes(int64_t rows, int64_t cols);
 size_t split_quant_grouped_ws_bytes(int64_t rows, int64_t cols, int64_t E);

@@ -353,14 +353,72 @@ struct QuantArgs {
   int64_t rows_out;            // rows of the row layout written (rows past `rows` are zero residuals)
   int mean_row, mean_rows;     // row of the quantized mean written here; its rows in total
   int cover_kpad;              // row tiles cover the column layout's padded token count
+  uint32_t sr_k0, sr_k1;        // stochastic rounding: the Philox key (the caller's seed)
   // grouped launches: group e = input rows [offsets[e], offsets[e+1]), quantized on its own
   // (own mean row, tensor scales and amax partials); row layout rows start at the group's
   // 32-aligned offset, column layout tokens at its 256-aligned offset
   const int64_t* offsets; int E;
 };
 
+// ------------------------------------------------------------------------------------------
+// Stochastic rounding (averis_split_quant_sr).  Random bits: Philox4x32-10 (Salmon, Moraes,
+// Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011) under the caller's 64-bit
+// seed; element k of outer index i of a layout (0 row, 1 column, 2 mean) takes the 16-bit half
+// k % 2 (low first) of word (k % 8) / 2 at counter (k / 8, i, layout, 0).  The magnitude of the
+// scaled value lies between grid neighbours lo <= a < hi and rounds to hi when u16 / 2^16 is
+// below (a - lo) / (hi - lo), which is exact in fp32 (Sterbenz, and a power-of-two step).
+// ------------------------------------------------------------------------------------------
+__device__ inline uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+  }
+  return c;
+}
+
+// The 16-bit draws of n (multiple of 8) consecutive elements from k0 on (k0 % 8 == 0).
+__device__ __forceinline__ void sr_draws(const QuantArgs& a, int64_t outer, int64_t k0, int layout, int n,
+                                         uint32_t* u) {
+  for (int q = 0; q < n / 8; ++q) {
+    const uint4 w = philox4x32_10(make_uint4((uint32_t)((k0 >> 3) + q), (uint32_t)outer, (uint32_t)layout, 0u),
+                                  a.sr_k0, a.sr_k1);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) u[8 * q + j] = (ws[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+  }
+}
+
+__device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t u16) {
+  const float a = fabsf(v);
+  uint32_t c = 7u;
+  if (a < 6.0f) {
+    float lo, inv_step;
+    if (a < 2.0f) { c = (uint32_t)(a * 2.0f); lo = (float)c * 0.5f; inv_step = 2.0f; }
+    else if (a < 3.0f) { c = 4u; lo = 2.0f; inv_step = 1.0f; }
+    else if (a < 4.0f) { c = 5u; lo = 3.0f; inv_step = 1.0f; }
+    else { c = 6u; lo = 4.0f; inv_step = 0.5f; }
+    const float p = __fmul_rn(__fsub_rn(a, lo), inv_step);
+    if ((float)u16 * (1.0f / 65536.0f) < p) ++c;
+  }
+  return c | ((__float_as_uint(v) >> 31) << 3);
+}
+
+// E2M1 codes of n values of one block with stochastic rounding, after its scale decision.
+template <int FMT>
+__device__ __forceinline__ void block_codes_sr(float* v, int n, const BlockQ& q, const uint32_t* u, uint32_t* dst) {
+  for (int k = 0; k < n / 8; ++k) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w |= e2m1_sr(__fmul_rn(v[8 * k + j], q.mul), u[8 * k + j]) << (4 * j);
+    dst[k] = q.dead ? 0u : w;
+  }
+}
+
 // Mean quantization (row tile 0) and padding zeroes for tile (tr, tc) of ROWS rows.
-template <int FMT, bool H16, int TC, int ROWS>
+template <int FMT, bool H16, int TC, int ROWS, bool SR = false>
 __device__ __forceinline__ void quant_extras(const QuantArgs& a, int tr, int tc, int64_t r0, int64_t c0) {
   constexpr int G = FMT == AVERIS_MXFP4 ? 32 : 16;
   const int t = threadIdx.x;
@@ -411,11 +469,19 @@ __device__ __forceinline__ void quant_extras(const QuantArgs& a, int tr, int tc,
 #pragma unroll
     for (int j = 0; j < G; ++j) amax = fmaxf(amax, fabsf(v[j]));
     const BlockQ q = block_params<FMT>(amax, s_dec);
+    if constexpr (SR) {
+      uint32_t u[G], w[G / 8];
+      sr_draws(a, 0, c, 2, G, u);
+      block_codes_sr<FMT>(v, G, q, u, w);
 #pragma unroll
-    for (int j = 0; j < G; ++j) v[j] = __fmul_rn(v[j], q.mul);
+      for (int j = 0; j < G / 8; ++j) *reinterpret_cast<uint32_t*>(a.mean_codes + mr * (kp / 2) + c / 2 + 4 * j) = w[j];
+    } else {
 #pragma unroll
-    for (int j = 0; j < G / 8; ++j)
-      *reinterpret_cast<uint32_t*>(a.mean_codes + mr * (kp / 2) + c / 2 + 4 * j) = q.dead ? 0u : pack8_fp4(v + 8 * j);
+      for (int j = 0; j < G; ++j) v[j] = __fmul_rn(v[j], q.mul);
+#pragma unroll
+      for (int j = 0; j < G / 8; ++j)
+        *reinterpret_cast<uint32_t*>(a.mean_codes + mr * (kp / 2) + c / 2 + 4 * j) = q.dead ? 0u : pack8_fp4(v + 8 * j);
+    }
     a.mean_scales[scale_offset(mr, c / G, kp, G)] = (uint8_t)q.sbyte;
   }
   const int nt = (int)((kp - a.cols) / G);  // K-tail blocks per row
@@ -500,7 +566,7 @@ __device__ __forceinline__ void block_codes(float* v, int n, const BlockQ& q, ui
 // Row layout of a tile: thread t quantizes one 64-byte unit (two for fp32 MXFP4, whose
 // 32-element block spans two units) of row t * UPT / 8: whole blocks, so no lane exchange.
 // FULL: every row of the tile holds data.
-template <typename T, int FMT, bool H16, bool AMAX_ONLY, bool FULL>
+template <typename T, int FMT, bool H16, bool AMAX_ONLY, bool FULL, bool SR = false>
 __device__ __forceinline__ void tile_rows(const QuantArgs& a, int64_t r0, int64_t c0, const uint8_t* tile,
                                             const float* means, float sd_row, float& amax_acc) {
   constexpr int SZ = (int)sizeof(T);
@@ -550,6 +616,8 @@ __device__ __forceinline__ void tile_rows(const QuantArgs& a, int64_t r0, int64_
   const bool col_ok = cbase < a.cols;
   uint32_t codes[EPT / 8];
   uint32_t sb = 0;
+  uint32_t u[SR ? EPT : 1];
+  if constexpr (SR) sr_draws(a, row, cbase, 0, EPT, u);
 #pragma unroll
   for (int b = 0; b < EPT / G; ++b) {
     float m = 0.0f;
@@ -560,7 +628,8 @@ __device__ __forceinline__ void tile_rows(const QuantArgs& a, int64_t r0, int64_
       continue;
     }
     const BlockQ q = block_params<FMT>(m, sd_row);
-    block_codes<FMT>(v + b * G, G, q, codes + b * (G / 8));
+    if constexpr (SR) block_codes_sr<FMT>(v + b * G, G, q, u + b * G, codes + b * (G / 8));
+    else block_codes<FMT>(v + b * G, G, q, codes + b * (G / 8));
     sb |= q.sbyte << (8 * b);
   }
   if (AMAX_ONLY) return;
@@ -575,7 +644,7 @@ __device__ __forceinline__ void tile_rows(const QuantArgs& a, int64_t r0, int64_
 }
 
 // Column layout of a tile: thread t quantizes column t over the tile's 32 rows.
-template <typename T, int FMT, bool H16, bool AMAX_ONLY, bool FULL>
+template <typename T, int FMT, bool H16, bool AMAX_ONLY, bool FULL, bool SR = false>
 __device__ __forceinline__ void tile_cols(const QuantArgs& a, int64_t r0, int64_t c0, const uint8_t* tile,
                                             const float* means, float sd_col, float& amax_acc) {
   constexpr int SZ = (int)sizeof(T);
@@ -596,6 +665,8 @@ __device__ __forceinline__ void tile_cols(const QuantArgs& a, int64_t r0, int64_
   if (H16) { h16_inreg(v); h16_inreg(v + 16); }
   uint32_t codes[4];
   uint32_t sb = 0;
+  uint32_t u[SR ? 32 : 1];
+  if constexpr (SR) sr_draws(a, col, r0, 1, 32, u);
 #pragma unroll
   for (int b = 0; b < 32 / G; ++b) {
     float m = 0.0f;
@@ -606,7 +677,8 @@ __device__ __forceinline__ void tile_cols(const QuantArgs& a, int64_t r0, int64_
       continue;
     }
     const BlockQ q = block_params<FMT>(m, sd_col);
-    block_codes<FMT>(v + b * G, G, q, codes + b * (G / 8));
+    if constexpr (SR) block_codes_sr<FMT>(v + b * G, G, q, u + b * G, codes + b * (G / 8));
+    else block_codes<FMT>(v + b * G, G, q, codes + b * (G / 8));
     sb |= q.sbyte << (8 * b);
   }
   if (AMAX_ONLY) return;
@@ -618,7 +690,7 @@ __device__ __forceinline__ void tile_cols(const QuantArgs& a, int64_t r0, int64_
   }
 }
 
-template <typename T, int FMT, bool H16, bool AMAX_ONLY>
+template <typename T, int FMT, bool H16, bool AMAX_ONLY, bool SR = false>
 __global__ __launch_bounds__(kThreads, 4) void k_quant(QuantArgs ain) {
   constexpr int SZ = (int)sizeof(T);
   constexpr int TC = 32 * Elem<T>::VEC;
@@ -694,20 +766,20 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant(QuantArgs ain) {
       if (a.col_ts) a.col_ts[0] = sd_col;
     }
   }
-  if (!AMAX_ONLY) quant_extras<FMT, H16, TC, kQRows>(a, tr, tc, r0, c0);
+  if (!AMAX_ONLY) quant_extras<FMT, H16, TC, kQRows, SR>(a, tr, tc, r0, c0);
   lds_barrier();
 
   float amax_row = 0.0f, amax_col = 0.0f;
   if (r0 + kQRows <= a.rows) {
     if (AMAX_ONLY ? a.want_row_amax : a.row_codes != nullptr)
-      tile_rows<T, FMT, H16, AMAX_ONLY, true>(a, r0, c0, s_tile, s_mean, sd_row, amax_row);
+      tile_rows<T, FMT, H16, AMAX_ONLY, true, SR>(a, r0, c0, s_tile, s_mean, sd_row, amax_row);
     if (AMAX_ONLY ? a.want_col_amax : a.col_codes != nullptr)
-      tile_cols<T, FMT, H16, AMAX_ONLY, true>(a, r0, c0, s_tile, s_mean, sd_col, amax_col);
+      tile_cols<T, FMT, H16, AMAX_ONLY, true, SR>(a, r0, c0, s_tile, s_mean, sd_col, amax_col);
   } else {
     if (AMAX_ONLY ? a.want_row_amax : a.row_codes != nullptr)
-      tile_rows<T, FMT, H16, AMAX_ONLY, false>(a, r0, c0, s_tile, s_mean, sd_row, amax_row);
+      tile_rows<T, FMT, H16, AMAX_ONLY, false, SR>(a, r0, c0, s_tile, s_mean, sd_row, amax_row);
     if (AMAX_ONLY ? a.want_col_amax : a.col_codes != nullptr)
-      tile_cols<T, FMT, H16, AMAX_ONLY, false>(a, r0, c0, s_tile, s_mean, sd_col, amax_col);
+      tile_cols<T, FMT, H16, AMAX_ONLY, false, SR>(a, r0, c0, s_tile, s_mean, sd_col, amax_col);
   }
   if (AMAX_ONLY) amax_commit(a, amax_row, amax_col, s_red, kThreads / 64);
 }
@@ -811,7 +883,13 @@ static hipError_t launch_quant_t(const SplitQuantPlan& p, const SqLayout& L) {
     a.mean_codes = p.q_mean->codes; a.mean_scales = p.q_mean->scales; a.mean_ts = p.q_mean->tensor_scale;
     a.mean_kpad = p.q_mean->k_pad;
   }
-  hipLaunchKernelGGL((k_quant<T, FMT, H16, false>), dim3((unsigned)ntiles), dim3(kThreads), 0, p.stream, a);
+  if (p.sr) {
+    a.sr_k0 = (uint32_t)p.seed;
+    a.sr_k1 = (uint32_t)(p.seed >> 32);
+    hipLaunchKernelGGL((k_quant<T, FMT, H16, false, true>), dim3((unsigned)ntiles), dim3(kThreads), 0, p.stream, a);
+  } else {
+    hipLaunchKernelGGL((k_quant<T, FMT, H16, false>), dim3((unsigned)ntiles), dim3(kThreads), 0, p.stream, a);
+  }
   return hipGetLastError();
 }
 

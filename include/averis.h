@@ -145,6 +145,26 @@ int32_t averis_split_quant(const void *x, int32_t xdt, int64_t rows, int64_t col
                            const averis_qtensor *q_mean, void *ws, size_t ws_bytes, void *stream);
 
 /* -----------------------------------------------------------------------------------------
+ * averis_split_quant_sr -- averis_split_quant with stochastic rounding of every E2M1 code it
+ * writes (residual layouts and quantized mean), for callers that round gradient operands
+ * stochastically.  The pages round to nearest and do not use this; it is an option.
+ *  seed   64-bit key of the counter-based Philox4x32-10 generator (Salmon et al., "Parallel
+ *         random numbers: as easy as 1, 2, 3", SC 2011): key = (seed mod 2^32, seed / 2^32).
+ *         Element k (along K) of outer index i of a layout (0 = q_row, 1 = q_col, 2 = q_mean)
+ *         draws the 16-bit half k % 2 (low half first) of output word (k % 8) / 2 at counter
+ *         (k / 8, i, layout, 0).  The same seed gives the same codes.
+ * Rounding: the scaled magnitude a (the value times the block's reciprocal scale, as for round
+ * to nearest) lies between neighbouring E2M1 magnitudes lo <= a < hi and becomes hi when
+ * draw / 2^16 < (a - lo) / (hi - lo), else lo; a >= 6 gives 6; the sign is kept.  Block scales
+ * and tensor scales are those of round to nearest.  Other arguments, preconditions and errors
+ * as averis_split_quant.
+ * ----------------------------------------------------------------------------------------- */
+int32_t averis_split_quant_sr(const void *x, int32_t xdt, int64_t rows, int64_t cols, int64_t ldx,
+                              int32_t fmt, uint32_t flags, uint64_t seed, float *mean,
+                              const averis_qtensor *q_row, const averis_qtensor *q_col,
+                              const averis_qtensor *q_mean, void *ws, size_t ws_bytes, void *stream);
+
+/* -----------------------------------------------------------------------------------------
  * averis_linear_fwd -- Y = 1 (Q(mu_X) Q(W)) + Q(X_R) Q(W)   ([rainbus] 方法步骤详情, forward)
  *  xr    [outer = l, k = m]  (q_row of split_quant(X))
  *  mu_x  [outer = 1, k = m]  (q_mean of split_quant(X)), or NULL for the vanilla GEMM
