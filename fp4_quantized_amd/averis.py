@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaveris.s
 EXPORTS = [
     "averis_abi_version", "averis_status_string", "averis_source_digest",
     "averis_split_quant_workspace_size", "averis_split_quant", "averis_split_quant_sr",
+    "averis_split_quant_noalloc_max_bytes", "averis_split_quant_noalloc",
     "averis_linear_workspace_size", "averis_linear_fwd", "averis_linear_bwd_dx",
     "averis_linear_bwd_dw_workspace_size", "averis_linear_bwd_dw",
     "averis_split_quant_grouped_workspace_size", "averis_split_quant_grouped",
@@ -82,6 +83,8 @@ def lib():
             "averis_split_quant_workspace_size": (SZ, [I64, I64, I32, U32]),
             "averis_split_quant": (I32, [P, I32, I64, I64, I64, I32, U32, P, Q, Q, Q, P, SZ, P]),
             "averis_split_quant_sr": (I32, [P, I32, I64, I64, I64, I32, U32, ctypes.c_uint64, P, Q, Q, Q, P, SZ, P]),
+            "averis_split_quant_noalloc_max_bytes": (SZ, []),
+            "averis_split_quant_noalloc": (I32, [P, I32, I64, I64, I64, I32, U32, P, Q, Q, Q, P]),
             "averis_linear_workspace_size": (SZ, [I64, I64, I64, I32]),
             "averis_linear_fwd": (I32, [Q, Q, Q, P, I32, I64, P, SZ, P]),
             "averis_linear_bwd_dx": (I32, [Q, Q, Q, P, I32, I64, P, SZ, P]),
@@ -212,6 +215,24 @@ def split_quant(x: torch.Tensor, fmt: int, split: bool = True, hadamard: bool = 
         _check(L.averis_split_quant_sr(xp, dt, rows, cols, ldx, fmt, flags, int(sr_seed), mp, _ptr(out["row"]),
                                        _ptr(out["col"]), _ptr(out["mean_q"]), ws.data_ptr(), ws.numel(),
                                        _stream(stream)))
+    return out
+
+
+def split_quant_noalloc(x: torch.Tensor, fmt: int, split: bool = True, hadamard: bool = False, out=None,
+                        stream=None):
+    """split_quant on the library's own device scratch array (no workspace argument): for callers
+    that cannot allocate; `out` from split_quant_outputs."""
+    assert x.dim() == 2 and x.is_cuda
+    rows, cols = x.shape
+    assert rows == 0 or x.stride(1) == 1, "x must be row-major"
+    ldx = x.stride(0) if rows > 0 else cols
+    flags = (SPLIT if split else 0) | (HADAMARD16 if hadamard else 0)
+    if out is None:
+        out = split_quant_outputs(rows, cols, fmt, split, hadamard, device=x.device)
+    mu = out["mean"]
+    _check(lib().averis_split_quant_noalloc(x.data_ptr() if rows else None, _dtype_code(x), rows, cols, ldx, fmt,
+                                            flags, mu.data_ptr() if mu is not None else None, _ptr(out["row"]),
+                                            _ptr(out["col"]), _ptr(out["mean_q"]), _stream(stream)))
     return out
 
 

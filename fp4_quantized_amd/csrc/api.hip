@@ -2,6 +2,7 @@
 // and dispatch to the split/quant and GEMM launchers.  Nothing is enqueued unless every
 // argument check passes.
 #include <cstring>
+#include <mutex>
 
 #include "launch.h"
 
@@ -134,6 +135,56 @@ int32_t averis_split_quant_sr(const void* x, int32_t xdt, int64_t rows, int64_t 
                               void* stream) {
   return split_quant_common(x, xdt, rows, cols, ldx, fmt, flags, mean, q_row, q_col, q_mean, ws, ws_bytes, stream,
                             true, seed);
+}
+
+// ------------------------------------------------------------------------------------------
+// The allocation-free split + quantization: its workspace is this file's device array, one copy
+// per GPU, resolved to a device address once per device (the array's name in host code is only
+// a stand-in for the symbol).  The first call on a device also clears the array with a fill
+// kernel on the caller's stream; every later call finds the strip counters at zero again, as
+// every split+quant leaves them.
+// ------------------------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ void k_zero_words(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of this GPU's scratch array, cleared on first use; nullptr on a HIP error.
+void* scratch_for_current_device(hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    hipLaunchKernelGGL(k_zero_words, dim3(256), dim3(256), 0, stream, reinterpret_cast<uint32_t*>(ptr),
+                       kScratchBytes / 4);
+    if (hipGetLastError() != hipSuccess) return nullptr;
+    g_scratch[dev] = ptr;
+  }
+  return g_scratch[dev];
+}
+}  // namespace
+
+size_t averis_split_quant_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int32_t averis_split_quant_noalloc(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ldx, int32_t fmt,
+                                   uint32_t flags, float* mean, const averis_qtensor* q_row,
+                                   const averis_qtensor* q_col, const averis_qtensor* q_mean, void* stream) {
+  if (rows < 0 || cols <= 0) return AVERIS_E_SHAPE;
+  if (split_quant_ws_bytes(rows, cols) > kScratchBytes) return AVERIS_E_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = scratch_for_current_device(s);
+  if (!ws) return AVERIS_E_HIP;
+  return split_quant_common(x, xdt, rows, cols, ldx, fmt, flags, mean, q_row, q_col, q_mean, ws, kScratchBytes,
+                            stream, false, 0);
 }
 
 size_t averis_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t fmt) {

@@ -165,6 +165,25 @@ int32_t averis_split_quant_sr(const void *x, int32_t xdt, int64_t rows, int64_t 
                               const averis_qtensor *q_mean, void *ws, size_t ws_bytes, void *stream);
 
 /* -----------------------------------------------------------------------------------------
+ * averis_split_quant_noalloc -- averis_split_quant without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It calls no allocating routine: its workspace is a
+ * library-owned device array of averis_split_quant_noalloc_max_bytes() bytes (8 MiB), one per
+ * GPU, held until the process ends.  Arguments, results and errors as averis_split_quant;
+ * AVERIS_E_WORKSPACE when averis_split_quant_workspace_size(rows, cols, ..) exceeds that size
+ * (about rows * cols <= 2^28, e.g. 65536 x 4096), AVERIS_E_HIP if the array's device address
+ * cannot be obtained.  The first call on a GPU clears the array (a kernel on `stream`).  All
+ * calls on one GPU share the array: calls that overlap in time on one GPU (other streams or
+ * host threads without ordering) race and give undefined results.
+ * ----------------------------------------------------------------------------------------- */
+size_t averis_split_quant_noalloc_max_bytes(void);
+
+int32_t averis_split_quant_noalloc(const void *x, int32_t xdt, int64_t rows, int64_t cols,
+                                   int64_t ldx, int32_t fmt, uint32_t flags, float *mean,
+                                   const averis_qtensor *q_row, const averis_qtensor *q_col,
+                                   const averis_qtensor *q_mean, void *stream);
+
+/* -----------------------------------------------------------------------------------------
  * averis_linear_fwd -- Y = 1 (Q(mu_X) Q(W)) + Q(X_R) Q(W)   ([rainbus] 方法步骤详情, forward)
  *  xr    [outer = l, k = m]  (q_row of split_quant(X))
  *  mu_x  [outer = 1, k = m]  (q_mean of split_quant(X)), or NULL for the vanilla GEMM
