@@ -19,6 +19,9 @@ BF16 = 1
 SPLIT = 1 << 0
 HADAMARD16 = 1 << 1
 MEAN_GIVEN = 1 << 2
+CHECK_FINITE = 1 << 3
+STATUS_NONFINITE = 1 << 0
+STATUS_UNDERFLOW = 1 << 1
 ACCUMULATE = 1 << 4
 KPAD = 256
 BLOCK = {NVFP4: 16, MXFP4: 32}
@@ -184,21 +187,23 @@ def split_quant_workspace(rows, cols, fmt, split=True, hadamard=False, device="c
 
 def split_quant(x: torch.Tensor, fmt: int, split: bool = True, hadamard: bool = False,
                 mean: torch.Tensor | None = None, row: bool = True, col: bool = True, stream=None,
-                out=None, ws=None, sr_seed: int | None = None):
+                out=None, ws=None, sr_seed: int | None = None, check_finite: bool = False):
     """Mean, residual and FP4 quantization of x [rows, cols] (bf16 or fp32, row-major).
 
     Returns dict(mean=fp32 [cols] or None, row=QTensor [rows, cols] or None,
     col=QTensor [cols, rows] or None, mean_q=QTensor [1, cols] or None).
     `mean` given: used instead of the column mean (MEAN_GIVEN).  `out` / `ws`: preallocated
     outputs (from split_quant_outputs) and workspace (from split_quant_workspace).  `sr_seed`:
-    stochastic rounding of the E2M1 codes with this 64-bit seed (averis_split_quant_sr)."""
+    stochastic rounding of the E2M1 codes with this 64-bit seed (averis_split_quant_sr).
+    `check_finite`: the result also holds "status", a device uint32 [1] view of the workspace's
+    status word (AVERIS_STATUS_* bits; read it after the stream reaches the call)."""
     assert x.dim() == 2 and x.is_cuda
     rows, cols = x.shape
     assert rows == 0 or x.stride(1) == 1, "x must be row-major"
     ldx = x.stride(0) if rows > 0 else cols
     dev = x.device
     flags = (SPLIT if split else 0) | (HADAMARD16 if hadamard else 0) | \
-        (MEAN_GIVEN if (split and mean is not None) else 0)
+        (MEAN_GIVEN if (split and mean is not None) else 0) | (CHECK_FINITE if check_finite else 0)
     if out is None:
         out = split_quant_outputs(rows, cols, fmt, split, hadamard, row, col, dev)
     if split and mean is not None:
@@ -215,6 +220,8 @@ def split_quant(x: torch.Tensor, fmt: int, split: bool = True, hadamard: bool = 
         _check(L.averis_split_quant_sr(xp, dt, rows, cols, ldx, fmt, flags, int(sr_seed), mp, _ptr(out["row"]),
                                        _ptr(out["col"]), _ptr(out["mean_q"]), ws.data_ptr(), ws.numel(),
                                        _stream(stream)))
+    if check_finite:
+        out = dict(out, status=ws[:4].view(torch.int32))
     return out
 
 

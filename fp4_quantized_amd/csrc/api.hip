@@ -93,7 +93,7 @@ static int32_t split_quant_common(const void* x, int32_t xdt, int64_t rows, int6
                                   size_t ws_bytes, void* stream, bool sr, uint64_t seed) {
   if (!dtype_ok(xdt)) return AVERIS_E_DTYPE;
   if (!fmt_ok(fmt)) return AVERIS_E_FORMAT;
-  if (flags & ~(AVERIS_SPLIT | AVERIS_HADAMARD16 | AVERIS_MEAN_GIVEN)) return AVERIS_E_FLAGS;
+  if (flags & ~(AVERIS_SPLIT | AVERIS_HADAMARD16 | AVERIS_MEAN_GIVEN | AVERIS_CHECK_FINITE)) return AVERIS_E_FLAGS;
   const bool split = flags & AVERIS_SPLIT, h16 = flags & AVERIS_HADAMARD16, given = flags & AVERIS_MEAN_GIVEN;
   if (given && !split) return AVERIS_E_FLAGS;
   if (rows < 0 || cols <= 0 || cols % kColMult != 0 || ldx < cols) return AVERIS_E_SHAPE;
@@ -119,6 +119,7 @@ static int32_t split_quant_common(const void* x, int32_t xdt, int64_t rows, int6
                    reinterpret_cast<hipStream_t>(stream)};
   p.sr = sr;
   p.seed = seed;
+  p.check = (flags & AVERIS_CHECK_FINITE) != 0;
   return split_quant_launch(p) == hipSuccess ? AVERIS_OK : AVERIS_E_HIP;
 }
 
@@ -179,6 +180,7 @@ int32_t averis_split_quant_noalloc(const void* x, int32_t xdt, int64_t rows, int
                                    uint32_t flags, float* mean, const averis_qtensor* q_row,
                                    const averis_qtensor* q_col, const averis_qtensor* q_mean, void* stream) {
   if (rows < 0 || cols <= 0) return AVERIS_E_SHAPE;
+  if (flags & AVERIS_CHECK_FINITE) return AVERIS_E_FLAGS;  // its status word would sit in the hidden array
   if (split_quant_ws_bytes(rows, cols) > kScratchBytes) return AVERIS_E_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   void* ws = scratch_for_current_device(s);
@@ -292,7 +294,7 @@ int32_t averis_split_quant_grouped(const void* x, int32_t xdt, int64_t cols, int
                                    const averis_qtensor* q_mean, void* ws, size_t ws_bytes, void* stream) {
   if (!dtype_ok(xdt)) return AVERIS_E_DTYPE;
   if (!fmt_ok(fmt)) return AVERIS_E_FORMAT;
-  if (flags & ~(AVERIS_SPLIT | AVERIS_HADAMARD16 | AVERIS_MEAN_GIVEN)) return AVERIS_E_FLAGS;
+  if (flags & ~(AVERIS_SPLIT | AVERIS_HADAMARD16 | AVERIS_MEAN_GIVEN | AVERIS_CHECK_FINITE)) return AVERIS_E_FLAGS;
   const bool split = flags & AVERIS_SPLIT, h16 = flags & AVERIS_HADAMARD16, given = flags & AVERIS_MEAN_GIVEN;
   if (given && !split) return AVERIS_E_FLAGS;
   const int64_t rows = check_offsets(d_offsets, h_offsets, E);
@@ -319,6 +321,7 @@ int32_t averis_split_quant_grouped(const void* x, int32_t xdt, int64_t cols, int
 
   SplitQuantPlan p{x, xdt, rows, cols, ldx, fmt, split, h16, given, means, q_row, q_col, q_mean, ws,
                    reinterpret_cast<hipStream_t>(stream), d_offsets, h_offsets, E};
+  p.check = (flags & AVERIS_CHECK_FINITE) != 0;
   return split_quant_launch(p) == hipSuccess ? AVERIS_OK : AVERIS_E_HIP;
 }
 

@@ -17,6 +17,7 @@ struct SplitQuantPlan {
   const int64_t* d_offsets; const int64_t* h_offsets; int64_t E;
   // stochastic rounding of the E2M1 codes with this Philox key (dense launches only)
   bool sr; uint64_t seed;
+  bool check;  // CHECK_FINITE: status bits into workspace word 0
 };
 size_t split_quant_ws_bytes(int64_t rows, int64_t cols);
 size_t split_quant_grouped_ws_bytes(int64_t rows, int64_t cols, int64_t E);

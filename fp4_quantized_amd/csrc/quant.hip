@@ -354,6 +354,7 @@ struct QuantArgs {
   int mean_row, mean_rows;     // row of the quantized mean written here; its rows in total
   int cover_kpad;              // row tiles cover the column layout's padded token count
   uint32_t sr_k0, sr_k1;        // stochastic rounding: the Philox key (the caller's seed)
+  uint32_t* status;             // CHECK_FINITE: status bits ORed here (workspace word 0), or null
   // grouped launches: group e = input rows [offsets[e], offsets[e+1]), quantized on its own
   // (own mean row, tensor scales and amax partials); row layout rows start at the group's
   // 32-aligned offset, column layout tokens at its 256-aligned offset
@@ -417,6 +418,23 @@ __device__ __forceinline__ void block_codes_sr(float* v, int n, const BlockQ& q,
   }
 }
 
+// CHECK_FINITE: OR `bits` of any lane of the wave into the status word (one atomic per wave
+// that found something).  Status bits: 1 = non-finite input, 2 = a nonzero block zeroed or
+// clamped because its scale underflowed.
+__device__ __forceinline__ void status_or(const QuantArgs& a, uint32_t bits) {
+  const uint64_t any1 = __ballot((bits & 1u) != 0), any2 = __ballot((bits & 2u) != 0);
+  if ((any1 | any2) && (threadIdx.x & 63) == __builtin_ctzll(any1 | any2))
+    atomicOr(a.status, (any1 ? 1u : 0u) | (any2 ? 2u : 0u));
+}
+
+// A block's scale lost its range: NVFP4 zeroes a nonzero block (E4M3 underflow or a decode
+// scale below 2^-126); MXFP4 clamps the exponent of a block whose amax is below 2^-125.
+template <int FMT>
+__device__ __forceinline__ bool scale_underflow(float amax, const BlockQ& q) {
+  if (!(amax > 0.0f)) return false;
+  return FMT == AVERIS_MXFP4 ? amax < 2.35098870e-38f : q.dead;
+}
+
 // Mean quantization (row tile 0) and padding zeroes for tile (tr, tc) of ROWS rows.
 template <int FMT, bool H16, int TC, int ROWS, bool SR = false>
 __device__ __forceinline__ void quant_extras(const QuantArgs& a, int tr, int tc, int64_t r0, int64_t c0) {
@@ -469,6 +487,7 @@ __device__ __forceinline__ void quant_extras(const QuantArgs& a, int tr, int tc,
 #pragma unroll
     for (int j = 0; j < G; ++j) amax = fmaxf(amax, fabsf(v[j]));
     const BlockQ q = block_params<FMT>(amax, s_dec);
+    if (a.status && scale_underflow<FMT>(amax, q)) atomicOr(a.status, 2u);
     if constexpr (SR) {
       uint32_t u[G], w[G / 8];
       sr_draws(a, 0, c, 2, G, u);
@@ -615,7 +634,7 @@ __device__ __forceinline__ void tile_rows(const QuantArgs& a, int64_t r0, int64_
   }
   const bool col_ok = cbase < a.cols;
   uint32_t codes[EPT / 8];
-  uint32_t sb = 0;
+  uint32_t sb = 0, flags = 0;
   uint32_t u[SR ? EPT : 1];
   if constexpr (SR) sr_draws(a, row, cbase, 0, EPT, u);
 #pragma unroll
@@ -628,11 +647,13 @@ __device__ __forceinline__ void tile_rows(const QuantArgs& a, int64_t r0, int64_
       continue;
     }
     const BlockQ q = block_params<FMT>(m, sd_row);
+    if (a.status && (FULL || row < a.rows) && col_ok && scale_underflow<FMT>(m, q)) flags |= 2u;
     if constexpr (SR) block_codes_sr<FMT>(v + b * G, G, q, u + b * G, codes + b * (G / 8));
     else block_codes<FMT>(v + b * G, G, q, codes + b * (G / 8));
     sb |= q.sbyte << (8 * b);
   }
   if (AMAX_ONLY) return;
+  if (a.status) status_or(a, flags);
   if (row < a.rows_out && col_ok) {
     uint8_t* dst = a.row_codes + row * (a.row_kpad / 2) + cbase / 2;
     if constexpr (EPT == 32) *reinterpret_cast<uint4*>(dst) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
@@ -664,7 +685,7 @@ __device__ __forceinline__ void tile_cols(const QuantArgs& a, int64_t r0, int64_
   }
   if (H16) { h16_inreg(v); h16_inreg(v + 16); }
   uint32_t codes[4];
-  uint32_t sb = 0;
+  uint32_t sb = 0, flags = 0;
   uint32_t u[SR ? 32 : 1];
   if constexpr (SR) sr_draws(a, col, r0, 1, 32, u);
 #pragma unroll
@@ -677,11 +698,13 @@ __device__ __forceinline__ void tile_cols(const QuantArgs& a, int64_t r0, int64_
       continue;
     }
     const BlockQ q = block_params<FMT>(m, sd_col);
+    if (a.status && col < a.cols && scale_underflow<FMT>(m, q)) flags |= 2u;
     if constexpr (SR) block_codes_sr<FMT>(v + b * G, G, q, u + b * G, codes + b * (G / 8));
     else block_codes<FMT>(v + b * G, G, q, codes + b * (G / 8));
     sb |= q.sbyte << (8 * b);
   }
   if (AMAX_ONLY) return;
+  if (a.status) status_or(a, flags);
   if (col < a.cols && r0 < a.col_kpad) {
     *reinterpret_cast<uint4*>(a.col_codes + col * (a.col_kpad / 2) + r0 / 2) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
     uint8_t* sd = a.col_scales + scale_offset(col, r0 / G, a.col_kpad, G);
@@ -748,6 +771,19 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant(QuantArgs ain) {
     const int q = k * kThreads + t;
     const int64_t row = r0 + (q >> 5), col = c0 + (int64_t)(q & 31) * EPC;
     w[k] = (row < a.rows && col < a.cols) ? *reinterpret_cast<const uint4*>(x + row * a.ldx + col) : make_uint4(0, 0, 0, 0);
+  }
+  if (!AMAX_ONLY && a.status) {  // CHECK_FINITE: an all-ones exponent field is a NaN or an infinity
+    uint32_t bad = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t ws[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (SZ == 2) bad |= ((ws[i] & 0x7F80u) == 0x7F80u) | ((ws[i] & 0x7F800000u) == 0x7F800000u);
+        else bad |= (ws[i] & 0x7F800000u) == 0x7F800000u;
+      }
+    }
+    status_or(a, bad ? 1u : 0u);
   }
   float4 m4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if (t < TC / 4 && a.mean && c0 + 4 * t < a.cols) m4 = *reinterpret_cast<const float4*>(a.mean + c0 + 4 * t);
@@ -841,6 +877,7 @@ static hipError_t launch_quant_t(const SplitQuantPlan& p, const SqLayout& L) {
   a.x = p.x; a.rows = p.rows; a.cols = p.cols; a.ldx = p.ldx;
   a.mean = p.split ? p.mean : nullptr;
   a.amax_slots = L.slots; a.amax_out = L.slots;
+  a.status = p.check ? L.slots : nullptr;  // word 0 (the amax slots start at word 1)
   a.ramax_part = L.ramax; a.mamax_part = L.mamax; a.n_part = L.n_part;
   const int64_t col_kpad = round_up(p.rows, kKPad);
   a.col_kpad = col_kpad;
@@ -931,6 +968,10 @@ hipError_t split_quant_launch(const SplitQuantPlan& p) {
     } else {
       if (nv) launch_stats_t<float, true>(p, L); else launch_stats_t<float, false>(p, L);
     }
+  }
+  else if (p.check) {
+    // the status word is cleared by k_colstats (with the amax slots); without it, here
+    hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(64), 0, p.stream, reinterpret_cast<float*>(L.slots), 1, 0.0f);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -33,7 +33,8 @@
  *  - Arguments are validated before anything is enqueued: on any error a non-zero status is
  *    returned, nothing is launched and no output is touched.  A failed launch returns
  *    AVERIS_E_HIP.  Faults inside kernels surface at the caller's next synchronisation.
- *  - Inputs must be finite.  Results for NaN/Inf inputs are unspecified.
+ *  - Inputs must be finite.  Results for NaN/Inf inputs are unspecified; AVERIS_CHECK_FINITE
+ *    makes split_quant report them (and scale underflow) in a device status word.
  *  - Results are deterministic: no floating-point atomics; every reduction has a fixed order.
  */
 #ifndef AVERIS_H
@@ -83,6 +84,15 @@ typedef enum { AVERIS_F32 = 0, AVERIS_BF16 = 1 } averis_dtype;
                                         order) after the subtraction ([rainbus] Hadamard变换,
                                         技术新颖性: Averis and Hadamard compose) */
 #define AVERIS_MEAN_GIVEN  (1u << 2) /* split_quant: `mean` is an input, not computed */
+#define AVERIS_CHECK_FINITE (1u << 3) /* split_quant (dense and grouped): the call writes status
+                                        bits into the first 4 bytes (uint32) of its workspace,
+                                        readable once the stream reaches the work: 0 = nothing
+                                        found, else an OR of AVERIS_STATUS_* */
+#define AVERIS_STATUS_NONFINITE  (1u << 0) /* an input element is NaN or +-Inf */
+#define AVERIS_STATUS_UNDERFLOW  (1u << 1) /* a nonzero block lost its range to scale underflow:
+                                             NVFP4 block zeroed (E4M3 scale 0 or decode scale
+                                             below 2^-126), MXFP4 block amax below 2^-125 (its
+                                             exponent clamped at -127) */
 #define AVERIS_ACCUMULATE  (1u << 4) /* bwd_dw: dW += result instead of dW = result */
 
 /* A quantized operand [outer, k] with blocks along k (K-inner, row-major).
@@ -125,7 +135,8 @@ const char *averis_source_digest(void);
  *  x      device [rows, cols] row-major, element type xdt, leading dimension ldx (elements).
  *         rows >= 0; cols > 0 and cols % 32 == 0 (for NVFP4 too: the row layout is quantized in
  *         32-element units); ldx >= cols, ldx * elem_size % 16 == 0.
- *  flags  AVERIS_SPLIT, AVERIS_HADAMARD16, AVERIS_MEAN_GIVEN (requires SPLIT).
+ *  flags  AVERIS_SPLIT, AVERIS_HADAMARD16, AVERIS_MEAN_GIVEN (requires SPLIT),
+ *         AVERIS_CHECK_FINITE (status bits in workspace word 0).
  *  mean   device fp32 [cols].  With SPLIT: written with mu (fp32 of the fixed-order fp64 sum
  *         divided by rows; rows == 0 gives 0), or read if MEAN_GIVEN.  Without SPLIT: unused
  *         (may be NULL).
@@ -170,6 +181,7 @@ int32_t averis_split_quant_sr(const void *x, int32_t xdt, int64_t rows, int64_t 
  * harnesses that forbid hipMalloc).  It calls no allocating routine: its workspace is a
  * library-owned device array of averis_split_quant_noalloc_max_bytes() bytes (8 MiB), one per
  * GPU, held until the process ends.  Arguments, results and errors as averis_split_quant;
+ * AVERIS_E_FLAGS for AVERIS_CHECK_FINITE (the status word would be in the hidden array);
  * AVERIS_E_WORKSPACE when averis_split_quant_workspace_size(rows, cols, ..) exceeds that size
  * (about rows * cols <= 2^28, e.g. 65536 x 4096), AVERIS_E_HIP if the array's device address
  * cannot be obtained.  The first call on a GPU clears the array (a kernel on `stream`).  All

@@ -218,3 +218,15 @@ def test_linear_grouped_rejects():
     assert dw(dt=av.CQTensor(FAKE, FAKE, FAKE, n, 100, 256, av.NVFP4, 0)) == E_SHAPE
     assert dw(md=None) == E_NULL
     assert dw(mx=q(1, m)) == E_SHAPE
+
+
+def test_check_finite_flag_rules():
+    L = av.lib()
+    # unknown flag bits are still refused; the allocation-free variant refuses CHECK_FINITE (its
+    # status word would sit in the library's hidden array), before touching any device
+    assert split(flags=av.SPLIT | (1 << 6)) == E_FLAGS
+    q = lambda o, k: av.CQTensor(FAKE, FAKE, FAKE, o, k, (k + 255) // 256 * 256, av.NVFP4, 0)
+    r = ctypes.byref
+    st = L.averis_split_quant_noalloc(FAKE, av.BF16, 256, 128, 128, av.NVFP4, av.SPLIT | av.CHECK_FINITE, FAKE,
+                                      r(q(256, 128)), r(q(128, 256)), r(q(1, 128)), None)
+    assert st == E_FLAGS

@@ -245,3 +245,71 @@ def test_golden_nvfp4_hadamard_block_on_gpu():
     from tests.gpu_util import row_scales
     np.testing.assert_array_equal(row_scales(g["row"])[0, :2], c["scales"], err_msg=c["name"])
     assert np.float32(g["row"].tensor_scale[0].item()) == np.float32(c["s_dec"]), c["name"]
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("split", [True, False])
+def test_check_finite_status(fmt, fname, dtype, split):
+    # AVERIS_CHECK_FINITE: status 0 and unchanged outputs for finite inputs; the non-finite bit for
+    # a NaN or an infinity anywhere; the status word cleared by every call (one workspace reused)
+    dev = device()
+    lin = workloads.up_proj_like(91, 300, 384, 8)
+    x_np = workloads._round(lin.x, dtype)
+    ws = av.split_quant_workspace(300, 384, fmt, split, device=dev)
+    x = workloads.to_torch(x_np, dtype, dev)
+    print(f"case check-finite {fname} {dtype} split={split}", flush=True)
+    for bad, where in ((np.nan, (0, 0)), (np.inf, (299, 383)), (-np.inf, (150, 200)), (None, None)):
+        xb = x.clone()
+        if bad is not None:
+            xb[where] = bad
+        g = av.split_quant(xb, fmt, split, ws=ws, check_finite=True)
+        torch.cuda.synchronize()
+        st = int(g["status"].item())
+        if bad is None:
+            assert st == 0, f"status {st} for finite input"
+            ref = av.split_quant(x, fmt, split)
+            torch.cuda.synchronize()
+            for k in ("row", "col"):
+                assert torch.equal(g[k].codes, ref[k].codes) and torch.equal(g[k].scales, ref[k].scales)
+        else:
+            assert st & av.STATUS_NONFINITE, f"status {st} for {bad} at {where}"
+
+
+@pytest.mark.parametrize("fmt,fname", FMTS)
+def test_check_finite_reports_scale_underflow(fmt, fname):
+    # a block whose scale underflows: the NVFP4 golden row whose second block is zeroed, and an
+    # MXFP4 block of amax 2^-126 (exponent clamped at -127); a normal operand reports nothing
+    dev = device()
+    c = _golden()["nvfp4"][2] if fmt == av.NVFP4 else _golden()["mxfp4"][4]
+    x = workloads.to_torch(_golden_rows(c["values"]), "f32", dev)
+    g = av.split_quant(x, fmt, split=False, check_finite=True)
+    torch.cuda.synchronize()
+    assert int(g["status"].item()) == av.STATUS_UNDERFLOW
+    lin = workloads.up_proj_like(92, 256, 256, 8)
+    g = av.split_quant(workloads.to_torch(lin.x, "bf16", dev), fmt, split=True, check_finite=True)
+    torch.cuda.synchronize()
+    assert int(g["status"].item()) == 0
+
+
+def test_check_finite_grouped():
+    dev = device()
+    lens = [0, 37, 300, 1]
+    x_np = workloads.up_proj_like(93, sum(lens), 256, 8).x
+    grp = av.Groups(np.concatenate([[0], np.cumsum(lens)]), dev)
+    x = workloads.to_torch(x_np, "bf16", dev)
+    ws = av.split_quant_grouped_workspace(sum(lens), 256, len(lens), av.MXFP4, device=dev)
+    L = av.lib()
+    for bad in (None, np.nan):
+        xb = x.clone()
+        if bad is not None:
+            xb[40, 17] = bad
+        out = av.split_quant_grouped_outputs(grp, 256, av.MXFP4, device=dev)
+        st = L.averis_split_quant_grouped(xb.data_ptr(), av.BF16, 256, 256, grp.d.data_ptr(), grp.h, grp.E, av.MXFP4,
+                                          av.SPLIT | av.CHECK_FINITE, out["mean"].data_ptr(), av._ptr(out["row"]),
+                                          av._ptr(out["col"]), av._ptr(out["mean_q"]), ws.data_ptr(), ws.numel(),
+                                          av._stream())
+        assert st == 0
+        torch.cuda.synchronize()
+        word = int(ws[:4].view(torch.int32).item())
+        assert word == (0 if bad is None else av.STATUS_NONFINITE), word
