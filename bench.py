@@ -16,7 +16,9 @@ replays run back to back.  HIP events on the launching stream bracket every repl
 minimum are reported.
 
 Other stages (parity configurations and the pages' comparisons): the same layer with
-independent inputs per linear, the up_proj layer (l = 8192), the down_proj layer in its four
+independent inputs per linear, a GEMM output split next (the gate forward GEMM, then the split
+of Y, with the statistics pass over Y or with the GEMM taking the column statistics in its
+epilogue), the up_proj layer (l = 8192), the down_proj layer in its four
 variants ({NVFP4, MXFP4} x {Hadamard off, on}, each also vanilla), the MoE layer, and Averis vs
 16x16-Hadamard preprocessing at the explainer's activation shapes (512 x 2048 tokens, 4096 and
 8192 channels).
@@ -48,7 +50,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stages", default="all",
-                   help="comma list of stages to run: layer,independent,up_proj,down_proj,moe,prep,roofline")
+                   help="comma list of stages to run: layer,independent,chain,up_proj,down_proj,moe,prep,roofline")
     return p.parse_args()
 
 
@@ -110,7 +112,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     av.lib()
     stages = set(args.stages.split(",")) if args.stages != "all" else \
-        {"layer", "independent", "up_proj", "down_proj", "moe", "prep", "roofline"}
+        {"layer", "independent", "chain", "up_proj", "down_proj", "moe", "prep", "roofline"}
     dev = torch.device("cuda:0")
     # Cache eviction before cold replays: read (not write) 512 MiB, so the L2s and the 256 MB
     # Infinity Cache end up holding clean lines of another buffer.
@@ -231,6 +233,48 @@ def main():
         log(f"roofline launch {t['cold_med']*1e3:.1f} us: {flops / launch_s / 1e12:.0f} TFLOP/s, "
             f"{nbytes / launch_s / 1e9:.0f} GB/s")
         del headline
+
+    # ---------------- producer-fused column statistics: a GEMM output split next ----------------
+    if "chain" in stages:
+        # the gate projection's forward GEMM (16384 x 1024 -> 3072, bf16 Y) followed by the split
+        # of Y, as when a GEMM output is the next linear's input: the split's statistics pass over
+        # Y against the GEMM taking them in its epilogue (and the split starting from them)
+        _, x, _, w = next(c for c in workloads.layer_device(3, L_LAYER, dev, shared=True) if c[0] == "gate")
+        l, n = x.shape[0], w.shape[1]
+        res = {}
+        for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
+            sx, sw = av.split_quant(x, fmt), av.split_quant(w, fmt, split=False)
+            y = torch.empty(l, n, dtype=torch.bfloat16, device=dev)
+            wsl = av.linear_workspace(sx["row"], sw["col"])
+            cs = av.ColStats(l, n, minmax=fmt == av.NVFP4)
+            o_a = av.split_quant_outputs(l, n, fmt, True, device=dev)
+            o_v = av.split_quant_outputs(l, n, fmt, False, device=dev)
+            wsq = av.split_quant_workspace(l, n, fmt, True, device=dev)
+
+            def gemm():
+                av.linear_fwd(sx["row"], sx["mean_q"], sw["col"], out=y, ws=wsl)
+
+            def gemm_stats():
+                av.linear_fwd_stats(sx["row"], sx["mean_q"], sw["col"], cs, out=y, ws=wsl)
+
+            r = {
+                "gemm": r4(timed(gemm)),
+                "gemm_stats": r4(timed(gemm_stats)),
+                "vanilla": r4(timed(lambda: (gemm(), av.split_quant(y, fmt, split=False, out=o_v, ws=wsq)))),
+                "averis": r4(timed(lambda: (gemm(), av.split_quant(y, fmt, out=o_a, ws=wsq)))),
+                "averis_stats": r4(timed(lambda: (gemm_stats(), av.split_quant_stats(y, cs, fmt, out=o_a, ws=wsq)))),
+            }
+            v = r["vanilla"]["cold_med"]
+            r["averis_overhead_pct"] = round(100.0 * (r["averis"]["cold_med"] - v) / v, 2)
+            r["averis_stats_overhead_pct"] = round(100.0 * (r["averis_stats"]["cold_med"] - v) / v, 2)
+            r["epilogue_stats_us"] = round((r["gemm_stats"]["cold_med"] - r["gemm"]["cold_med"]) * 1e3, 2)
+            r["part_rows"] = int(cs.part_rows)
+            res[name] = r
+            log(f"chain {name}: averis +{r['averis_overhead_pct']} %, with producer statistics "
+                f"+{r['averis_stats_overhead_pct']} % over vanilla")
+            del sx, sw, y, wsl, cs, o_a, o_v, wsq
+        out["chain_gemm_then_split"] = res
+        del x, w
 
     # ---------------- the layer with independent inputs per linear ----------------
     if "independent" in stages:

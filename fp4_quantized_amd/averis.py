@@ -33,6 +33,7 @@ EXPORTS = [
     "averis_split_quant_workspace_size", "averis_split_quant", "averis_split_quant_sr",
     "averis_split_quant_noalloc_max_bytes", "averis_split_quant_noalloc",
     "averis_linear_workspace_size", "averis_linear_fwd", "averis_linear_bwd_dx",
+    "averis_colstats_capacity", "averis_linear_fwd_stats", "averis_linear_bwd_dx_stats", "averis_split_quant_stats",
     "averis_linear_bwd_dw_workspace_size", "averis_linear_bwd_dw",
     "averis_split_quant_grouped_workspace_size", "averis_split_quant_grouped",
     "averis_linear_grouped_workspace_size", "averis_linear_fwd_grouped", "averis_linear_bwd_dx_grouped",
@@ -50,6 +51,19 @@ class CQTensor(ctypes.Structure):
         ("k_pad", ctypes.c_int64),
         ("fmt", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+    ]
+
+
+class CColStats(ctypes.Structure):
+    _fields_ = [
+        ("sum", ctypes.c_void_p),
+        ("min", ctypes.c_void_p),
+        ("max", ctypes.c_void_p),
+        ("capacity", ctypes.c_int64),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("parts", ctypes.c_int64),
+        ("part_rows", ctypes.c_int64),
     ]
 
 
@@ -79,6 +93,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P, I64, I32, U32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
         Q = ctypes.POINTER(CQTensor)
+        CS = ctypes.POINTER(CColStats)
         sig = {
             "averis_abi_version": (I32, []),
             "averis_status_string": (ctypes.c_char_p, [I32]),
@@ -91,6 +106,10 @@ def lib():
             "averis_linear_workspace_size": (SZ, [I64, I64, I64, I32]),
             "averis_linear_fwd": (I32, [Q, Q, Q, P, I32, I64, P, SZ, P]),
             "averis_linear_bwd_dx": (I32, [Q, Q, Q, P, I32, I64, P, SZ, P]),
+            "averis_colstats_capacity": (I64, [I64, I64]),
+            "averis_linear_fwd_stats": (I32, [Q, Q, Q, P, I32, I64, CS, P, SZ, P]),
+            "averis_linear_bwd_dx_stats": (I32, [Q, Q, Q, P, I32, I64, CS, P, SZ, P]),
+            "averis_split_quant_stats": (I32, [P, I32, I64, I64, I64, I32, U32, CS, P, Q, Q, Q, P, SZ, P]),
             "averis_linear_bwd_dw_workspace_size": (SZ, [I64, I64, I64, I32]),
             "averis_linear_bwd_dw": (I32, [Q, Q, Q, Q, I64, P, I64, U32, P, SZ, P]),
             "averis_split_quant_grouped_workspace_size": (SZ, [I64, I64, I32, I32, U32]),
@@ -268,6 +287,80 @@ def linear_bwd_dx(dr: QTensor, mu_d: QTensor | None, w: QTensor, out_dtype=torch
                   out=None, ws=None):
     """dX [l, m] = 1 (Q(mu_D) Q(W)^T) + Q(D_R) Q(W)^T; w is the [m, n] (K = n) weight operand."""
     return _linear(lib().averis_linear_bwd_dx, dr, mu_d, w, out_dtype, stream, out, ws)
+
+
+class ColStats:
+    """Caller-owned column partials of a GEMM output (averis_colstats): fp32 sums, and minima /
+    maxima when `minmax`, sized for any producer of a [rows, cols] output.  The producer fills in
+    rows, cols, parts and part_rows."""
+
+    def __init__(self, rows, cols, minmax=False, device="cuda"):
+        cap = int(lib().averis_colstats_capacity(rows, cols))
+        mk = lambda: torch.empty(max(cap, 1), dtype=torch.float32, device=device)  # noqa: E731
+        self.sum = mk()
+        self.min = mk() if minmax else None
+        self.max = mk() if minmax else None
+        self.cs = CColStats(self.sum.data_ptr(), self.min.data_ptr() if minmax else None,
+                            self.max.data_ptr() if minmax else None, cap, 0, 0, 0, 0)
+
+    @property
+    def parts(self):
+        return self.cs.parts
+
+    @property
+    def part_rows(self):
+        return self.cs.part_rows
+
+    def view(self, which="sum"):
+        """The written partials [parts, cols] of `which` ('sum', 'min' or 'max')."""
+        t = getattr(self, which)
+        return t[: self.cs.parts * self.cs.cols].view(self.cs.parts, self.cs.cols)
+
+
+def _linear_stats(fn, a: QTensor, mu: QTensor | None, w: QTensor, stats: ColStats, out_dtype, stream, out, ws):
+    dev = a.codes.device
+    if out is None:
+        out = torch.empty((a.outer, w.outer), dtype=out_dtype, device=dev)
+    if ws is None:
+        ws = linear_workspace(a, w)
+    _check(fn(_ptr(a), _ptr(mu), _ptr(w), out.data_ptr() if out.numel() else None, _dtype_code(out), out.stride(0),
+              ctypes.byref(stats.cs), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return out
+
+
+def linear_fwd_stats(xr: QTensor, mu_x: QTensor | None, w: QTensor, stats: ColStats, out_dtype=torch.bfloat16,
+                     stream=None, out=None, ws=None):
+    """linear_fwd that also writes the column statistics of Y (as stored) into `stats`."""
+    return _linear_stats(lib().averis_linear_fwd_stats, xr, mu_x, w, stats, out_dtype, stream, out, ws)
+
+
+def linear_bwd_dx_stats(dr: QTensor, mu_d: QTensor | None, w: QTensor, stats: ColStats, out_dtype=torch.bfloat16,
+                        stream=None, out=None, ws=None):
+    """linear_bwd_dx that also writes the column statistics of dX (as stored) into `stats`."""
+    return _linear_stats(lib().averis_linear_bwd_dx_stats, dr, mu_d, w, stats, out_dtype, stream, out, ws)
+
+
+def split_quant_stats(x: torch.Tensor, stats: ColStats, fmt: int, hadamard: bool = False, row: bool = True,
+                      col: bool = True, stream=None, out=None, ws=None, check_finite: bool = False):
+    """split_quant (SPLIT) of x from the column statistics its producer wrote into `stats`;
+    returns the same dict as split_quant."""
+    assert x.dim() == 2 and x.is_cuda
+    rows, cols = x.shape
+    assert rows == 0 or x.stride(1) == 1, "x must be row-major"
+    ldx = x.stride(0) if rows > 0 else cols
+    dev = x.device
+    flags = SPLIT | (HADAMARD16 if hadamard else 0) | (CHECK_FINITE if check_finite else 0)
+    if out is None:
+        out = split_quant_outputs(rows, cols, fmt, True, hadamard, row, col, dev)
+    if ws is None:
+        ws = split_quant_workspace(rows, cols, fmt, True, hadamard, dev)
+    _check(lib().averis_split_quant_stats(x.data_ptr() if rows else None, _dtype_code(x), rows, cols, ldx, fmt, flags,
+                                          ctypes.byref(stats.cs), out["mean"].data_ptr(), _ptr(out["row"]),
+                                          _ptr(out["col"]), _ptr(out["mean_q"]), ws.data_ptr(), ws.numel(),
+                                          _stream(stream)))
+    if check_finite:
+        out = dict(out, status=ws[:4].view(torch.int32))
+    return out
 
 
 def linear_bwd_dw_workspace(xr_t: QTensor, dr_t: QTensor, l: int):

@@ -90,7 +90,8 @@ size_t averis_split_quant_workspace_size(int64_t rows, int64_t cols, int32_t fmt
 static int32_t split_quant_common(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ldx, int32_t fmt,
                                   uint32_t flags, float* mean, const averis_qtensor* q_row,
                                   const averis_qtensor* q_col, const averis_qtensor* q_mean, void* ws,
-                                  size_t ws_bytes, void* stream, bool sr, uint64_t seed) {
+                                  size_t ws_bytes, void* stream, bool sr, uint64_t seed,
+                                  const averis_colstats* stats = nullptr) {
   if (!dtype_ok(xdt)) return AVERIS_E_DTYPE;
   if (!fmt_ok(fmt)) return AVERIS_E_FORMAT;
   if (flags & ~(AVERIS_SPLIT | AVERIS_HADAMARD16 | AVERIS_MEAN_GIVEN | AVERIS_CHECK_FINITE)) return AVERIS_E_FLAGS;
@@ -112,6 +113,14 @@ static int32_t split_quant_common(const void* x, int32_t xdt, int64_t rows, int6
   } else if (q_mean) {
     return AVERIS_E_FLAGS;
   }
+  if (stats) {
+    if (!split || given) return AVERIS_E_FLAGS;
+    if (!stats->sum || (stats->min == nullptr) != (stats->max == nullptr)) return AVERIS_E_NULL;
+    if (fmt == AVERIS_NVFP4 && !h16 && !stats->min) return AVERIS_E_NULL;
+    if (stats->rows != rows || stats->cols != cols || stats->part_rows <= 0 ||
+        stats->parts != ceil_div(rows, stats->part_rows) || stats->parts * cols > stats->capacity)
+      return AVERIS_E_SHAPE;
+  }
   if (!ws || ws_bytes < split_quant_ws_bytes(rows, cols)) return AVERIS_E_WORKSPACE;
   if (!aligned16(ws)) return AVERIS_E_ALIGN;
 
@@ -120,6 +129,10 @@ static int32_t split_quant_common(const void* x, int32_t xdt, int64_t rows, int6
   p.sr = sr;
   p.seed = seed;
   p.check = (flags & AVERIS_CHECK_FINITE) != 0;
+  if (stats) {
+    p.st_sum = stats->sum; p.st_parts = stats->parts;
+    if (fmt == AVERIS_NVFP4 && !h16) { p.st_min = stats->min; p.st_max = stats->max; }
+  }
   return split_quant_launch(p) == hipSuccess ? AVERIS_OK : AVERIS_E_HIP;
 }
 
@@ -128,6 +141,15 @@ int32_t averis_split_quant(const void* x, int32_t xdt, int64_t rows, int64_t col
                            const averis_qtensor* q_mean, void* ws, size_t ws_bytes, void* stream) {
   return split_quant_common(x, xdt, rows, cols, ldx, fmt, flags, mean, q_row, q_col, q_mean, ws, ws_bytes, stream,
                             false, 0);
+}
+
+int32_t averis_split_quant_stats(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ldx, int32_t fmt,
+                                 uint32_t flags, const averis_colstats* stats, float* mean, const averis_qtensor* q_row,
+                                 const averis_qtensor* q_col, const averis_qtensor* q_mean, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  if (!stats) return AVERIS_E_NULL;
+  return split_quant_common(x, xdt, rows, cols, ldx, fmt, flags, mean, q_row, q_col, q_mean, ws, ws_bytes, stream,
+                            false, 0, stats);
 }
 
 int32_t averis_split_quant_sr(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ldx, int32_t fmt,
@@ -205,8 +227,12 @@ size_t averis_linear_bwd_dw_workspace_size(int64_t m, int64_t n, int64_t l, int3
 // under 2^31 bytes, the reach of a buffer store's 32-bit offset.
 constexpr int64_t kMaxLd = int64_t(1) << 23;
 
+// Column-statistics partials are at least 64 rows each (the smallest epilogue row block).
+constexpr int64_t kStatsMinPartRows = 64;
+
 static int32_t linear_common(const averis_qtensor* a, const averis_qtensor* mu, const averis_qtensor* w, void* out,
-                             int32_t odt, int64_t ldo, void* ws, size_t ws_bytes, void* stream) {
+                             int32_t odt, int64_t ldo, void* ws, size_t ws_bytes, void* stream,
+                             averis_colstats* stats = nullptr, bool want_stats = false) {
   int32_t st;
   if ((st = check_in(a)) != AVERIS_OK) return st;
   if ((st = check_in(w)) != AVERIS_OK) return st;
@@ -231,7 +257,36 @@ static int32_t linear_common(const averis_qtensor* a, const averis_qtensor* mu, 
   GemmPlan p{};
   p.a = a; p.b = w; p.c = out; p.ldc = ldo; p.c_bf16 = odt == AVERIS_BF16;
   p.mu = mu; p.splits = splits; p.ws = ws; p.stream = reinterpret_cast<hipStream_t>(stream);
-  return gemm_launch(p) == hipSuccess ? AVERIS_OK : AVERIS_E_HIP;
+  GemmPlan::Stats cs{};
+  if (want_stats) {
+    if (!stats || !stats->sum || (stats->min == nullptr) != (stats->max == nullptr)) return AVERIS_E_NULL;
+    if (stats->capacity < averis_colstats_capacity(a->outer, w->outer)) return AVERIS_E_SHAPE;
+    cs = GemmPlan::Stats{stats->sum, stats->min, stats->max, 0};
+    p.stats = &cs;
+  }
+  if (gemm_launch(p) != hipSuccess) return AVERIS_E_HIP;
+  if (want_stats) {
+    stats->rows = a->outer; stats->cols = w->outer; stats->part_rows = cs.part_rows;
+    stats->parts = ceil_div(a->outer, cs.part_rows);
+  }
+  return AVERIS_OK;
+}
+
+int64_t averis_colstats_capacity(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return 0;
+  return ceil_div(rows, kStatsMinPartRows) * cols;
+}
+
+int32_t averis_linear_fwd_stats(const averis_qtensor* xr, const averis_qtensor* mu_x, const averis_qtensor* w, void* y,
+                                int32_t ydt, int64_t ldy, averis_colstats* stats, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return linear_common(xr, mu_x, w, y, ydt, ldy, ws, ws_bytes, stream, stats, true);
+}
+
+int32_t averis_linear_bwd_dx_stats(const averis_qtensor* dr, const averis_qtensor* mu_d, const averis_qtensor* w,
+                                   void* dx, int32_t dxdt, int64_t lddx, averis_colstats* stats, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  return linear_common(dr, mu_d, w, dx, dxdt, lddx, ws, ws_bytes, stream, stats, true);
 }
 
 int32_t averis_linear_fwd(const averis_qtensor* xr, const averis_qtensor* mu_x, const averis_qtensor* w, void* y,

@@ -59,6 +59,9 @@ struct GemmArgs {
   //     l_e with u [E][M] and v [E][N].  Every group has tiles_m x tiles_n tiles.
   const int64_t* offsets; int E; int grouped;
   int n_work;                           // logical tiles of the launch (a workgroup may take several)
+  // STATS kernels: per-column sums of the stored output over each wave's rows, [part][N] with
+  // part = row / (32 TM)
+  float* st_sum;
 };
 
 __device__ inline uint32_t f32_to_bf16_rne(float f) {
@@ -456,7 +459,48 @@ __device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt((15) |
 //   rounded once in fp32; split-K partials get alpha * acc only.
 // ALL = false: the launch has no bias vector, rank-one term or accumulation (the epilogue then
 // issues no global loads).
-template <int FMT, int TM, int TN, bool MU, bool ALL = true>
+// Value of lane t ^ M within each 16-lane row (DPP moves: quad permutations for M = 1, 2; row
+// half-mirror then quad reversal for 4; row rotation by 8 for 8).
+template <int M>
+__device__ __forceinline__ float row_xor(float v) {
+  const int x = __float_as_int(v);
+  if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+  else if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+  else if constexpr (M == 4)
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false), 0x1B, 0xF, 0xF, false));
+  else return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false));
+}
+
+template <int W, class OP>
+__device__ __forceinline__ void rs_step(float (&v)[16], bool upper, OP op) {
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    float a = v[k], b = v[k + W];
+    asm("" : "+v"(a), "+v"(b));  // keep the lane choice a register select, not an indexed load
+    const float keep = upper ? b : a, send = upper ? a : b;
+    v[k] = op(keep, row_xor<W>(send));
+  }
+}
+
+// Reduce-scatter of 16 per-lane values over the 32 lanes of each lane half, in a fixed order:
+// afterwards lane t of the half holds OP over the half's 32 lanes of value t % 16 (15 DPP
+// exchanges within 16-lane rows and one row swap, instead of the 80 exchanges of a butterfly
+// on every value).  Both lanes of a pair combine in the same order.
+template <class OP>
+__device__ __forceinline__ float half_reduce_scatter16(float (&v)[16], int lane, OP op) {
+  rs_step<8>(v, (lane & 8) != 0, op);
+  rs_step<4>(v, (lane & 4) != 0, op);
+  rs_step<2>(v, (lane & 2) != 0, op);
+  rs_step<1>(v, (lane & 1) != 0, op);
+  // rows 2r and 2r + 1 (lanes t and t ^ 16): both get op(row 2r, row 2r + 1)
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[0]), __float_as_uint(v[0]), false, false);
+  return op(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// STATS: column sums of the stored output over each wave's rows (fp32 partials [part][N],
+// part = row / (32 TM)).
+template <int FMT, int TM, int TN, bool MU, bool ALL = true, bool STATS = false>
 __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&acc)[TM][TN], int64_t rbase,
                                               int64_t cbase, int split, int lane, const float* su, const float* sv,
                                               const float* sbias) {
@@ -508,6 +552,10 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
                                 : reinterpret_cast<uint8_t*>(g.c) + rbase * g.ldc * esz;
   const int64_t nrows = g.M - rbase < TM * 32 ? g.M - rbase : TM * 32;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(obase, nrows > 0 ? (nrows - 1) * ldo * esz + g.N * esz : 0);
+  // STATS: column sums of the stored values over this wave's rows in fp32: each lane's TM rows
+  // in order, then across the lanes of each half in the fixed reduce-scatter order, after which
+  // lane t of a half holds value t % 16 of each column block.
+  float csum[STATS ? TN : 1][16];
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int64_t row = rbase + i * 32 + fr;
@@ -549,6 +597,11 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
           const v4u o = {pack_bf16x2(x[8 * p], x[8 * p + 1]), pack_bf16x2(x[8 * p + 2], x[8 * p + 3]),
                          pack_bf16x2(x[8 * p + 4], x[8 * p + 5]), pack_bf16x2(x[8 * p + 6], x[8 * p + 7])};
           __builtin_amdgcn_raw_buffer_store_b128(o, ro, col < g.N ? roff + (int)col * 2 : 0x7FFFFFF0, 0, 0);
+          if constexpr (STATS) {  // the values as stored
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+              x[8 * p + r] = __uint_as_float(r & 1 ? (o[r >> 1] & 0xFFFF0000u) : (o[r >> 1] << 16));
+          }
         }
       } else if (!acc_in) {
 #pragma unroll
@@ -558,7 +611,7 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
                          __float_as_uint(x[4 * q + 3])};
           __builtin_amdgcn_raw_buffer_store_b128(o, ro, col < g.N ? roff + (int)col * 4 : 0x7FFFFFF0, 0, 0);
         }
-      } else {  // accumulate into fp32 C
+      } else {  // accumulate into fp32 C (no STATS)
         if (!row_ok) continue;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -569,6 +622,28 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
           *reinterpret_cast<float4*>(dst) = make_float4(__fadd_rn(c.x, x[4 * q]), __fadd_rn(c.y, x[4 * q + 1]),
                                                         __fadd_rn(c.z, x[4 * q + 2]), __fadd_rn(c.w, x[4 * q + 3]));
         }
+      }
+      if constexpr (STATS) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float v = row_ok ? x[e] : 0.0f;
+          csum[j][e] = i == 0 ? v : __fadd_rn(csum[j][e], v);
+        }
+      }
+    }
+  }
+  if constexpr (STATS) {
+    // lane t < 16 of each half writes the totals of value t of each column block: column
+    // j*32 + 16p + 8h + r (bf16, t = 8p + r) or j*32 + 8q + 4h + r (fp32, t = 4q + r)
+    if (rbase < g.M) {
+      const int t = lane & 15;
+      const int64_t part = rbase / (TM * 32);
+      const int64_t coff = bf ? 16 * (t >> 3) + 8 * h + (t & 7) : 8 * (t >> 2) + 4 * h + (t & 3);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t col = cbase + j * 32 + coff;
+        const float sj = half_reduce_scatter16(csum[j], lane, [](float a, float b) { return __fadd_rn(a, b); });
+        if ((lane & 31) < 16 && col < g.N) g.st_sum[part * g.N + col] = sj;
       }
     }
   }
@@ -586,7 +661,7 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
 // tile's first loads cannot be issued ahead of the epilogue's stores: loads and stores share
 // one vector-memory counter and may complete out of order, so no wait could single out the
 // loads.)
-template <int FMT, int WM, int WN, int TM, int TN, int STAGES, int AUX = 0, bool MU = false>
+template <int FMT, int WM, int WN, int TM, int TN, int STAGES, int AUX = 0, bool MU = false, bool STATS = false>
 __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1) void k_gemm(GemmArgs gin) {
   using T = GemmTile<FMT, WM, WN, TM, TN, STAGES, AUX, MU>;
   using C = typename T::C;
@@ -708,7 +783,7 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
     }
     if (hr && (int)threadIdx.x < C::BM + C::BN) s_uv[threadIdx.x] = uv;
     if (MU || hr) lds_barrier();
-    epilogue_regs<FMT, TM, TN, MU>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, split, threadIdx.x & 63,
+    epilogue_regs<FMT, TM, TN, MU, true, STATS>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, split, threadIdx.x & 63,
                                    s_uv + t.wm * TM * 32, s_uv + C::BM + t.wn * TN * 32, s_bias + t.wn * TN * 32);
     t.clear();
   }
@@ -732,7 +807,7 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
 // each tile before its K-steps (their only global loads) and add r1 u v^T in the epilogue.
 // TMW: MFMA tiles per wave along M (2: 128 x 128 workgroup tiles; 4: 256 x 128, each wave 128 x
 // 64, which reads 6 fragments from LDS per 8 MFMAs instead of 4 per 4).
-template <int FMT, bool MU, bool R1, int S, int L, int TMW = 2>
+template <int FMT, bool MU, bool R1, int S, int L, int TMW = 2, bool STATS = false>
 __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
   constexpr int WM = 2, WN = 2, TM = TMW, TN = 2;
   using T = GemmTile<FMT, WM, WN, TM, TN, 2, 0, MU>;
@@ -842,7 +917,7 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
     }
     if constexpr (R1) s_uv[threadIdx.x] = uv;
     if constexpr (ebar) lds_barrier();
-    epilogue_regs<FMT, TM, TN, MU, R1>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, split, threadIdx.x & 63,
+    epilogue_regs<FMT, TM, TN, MU, R1, STATS>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, split, threadIdx.x & 63,
                                        s_uv + t.wm * TM * 32, s_uv + C::BM + t.wn * TN * 32,
                                        s_bias + t.wn * TN * 32);
   }
@@ -1208,9 +1283,11 @@ size_t gemm_grouped_dw_ws_bytes(int64_t M, int64_t N, int64_t E) {
   return 256 + (size_t)E * (round_up(M, 128) + round_up(N, 128)) * 4;
 }
 
+// stats: the STATS form of the kernels that take the output's column sums in the epilogue
+// (MXFP4 warp-specialized, NVFP4 two-stage)
 template <int F>
 static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipStream_t s, void* ws,
-                       const int64_t* h_offsets) {
+                       const int64_t* h_offsets, bool stats = false) {
   if constexpr (F == AVERIS_MXFP4) {
     if (cfg == KCFG_WSDW) {  // grouped weight gradient
       constexpr int S = kWsStages, L = kWsLoaders;
@@ -1236,12 +1313,22 @@ static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipSt
     }
     if (cfg == KCFG_WSW) {  // 256 x 128 tiles: a 3-stage ring of 51 KB stages
       constexpr int L = kWsLoaders;
+      if (stats) {
+        if (mu) hipLaunchKernelGGL((k_gemm_ws<F, true, false, 3, L, 4, true>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+        else hipLaunchKernelGGL((k_gemm_ws<F, false, false, 3, L, 4, true>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+        return;
+      }
       if (mu) hipLaunchKernelGGL((k_gemm_ws<F, true, false, 3, L, 4>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
       else hipLaunchKernelGGL((k_gemm_ws<F, false, false, 3, L, 4>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
       return;
     }
     if (cfg == KCFG_WS) {
       constexpr int S = kWsStages, L = kWsLoaders;
+      if (stats) {
+        if (mu) hipLaunchKernelGGL((k_gemm_ws<F, true, false, S, L, 2, true>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+        else hipLaunchKernelGGL((k_gemm_ws<F, false, false, S, L, 2, true>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+        return;
+      }
       if (mu) hipLaunchKernelGGL((k_gemm_ws<F, true, false, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
       else if (g.has_r1 && g.splits == 1)
         hipLaunchKernelGGL((k_gemm_ws<F, false, true, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
@@ -1253,6 +1340,12 @@ static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipSt
     if (mu) {
       if (cfg == KCFG_LONG) hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 3, 0, true>), dim3(grid), dim3(256), 0, s, g);
       else hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 2, 0, true>), dim3(grid), dim3(256), 0, s, g);
+      return;
+    }
+  }
+  if constexpr (F == AVERIS_NVFP4) {
+    if (stats && cfg == KCFG_SHORT) {
+      hipLaunchKernelGGL((k_gemm<F, 2, 2, 2, 2, 2, 0, false, true>), dim3(grid), dim3(256), 0, s, g);
       return;
     }
   }
@@ -1337,6 +1430,18 @@ hipError_t gemm_launch(const GemmPlan& p) {
     g.group_m = gm;
   }
   g.accumulate = p.accumulate;
+  g.splits = p.grouped ? 1 : p.splits;
+  // column statistics of the output: sums in the epilogue of the warp-specialized MXFP4 kernels
+  // and of the two-stage NVFP4 kernel on single-split dense launches; otherwise (and whenever
+  // minima and maxima are wanted: three reductions in the epilogue spill the two-stage kernel)
+  // a pass over the stored output after the GEMM
+  const bool st_fused = p.stats && !p.stats->min && !p.grouped && g.splits == 1 && !p.accumulate &&
+                        ((fmt == AVERIS_MXFP4 && (cfg == KCFG_WS || cfg == KCFG_WSW)) ||
+                         (fmt == AVERIS_NVFP4 && cfg == KCFG_SHORT));
+  if (p.stats) {
+    p.stats->part_rows = st_fused ? (cfg == KCFG_WSW ? 128 : 64) : colparts_rows();
+    if (st_fused) g.st_sum = p.stats->sum;
+  }
   if (M == 0 || N == 0 || E == 0) return hipSuccess;
 
   // mean term: MXFP4 computes it inside the GEMM (one scaled MFMA more per four) while the mean
@@ -1366,7 +1471,6 @@ hipError_t gemm_launch(const GemmPlan& p) {
     g.ru = MeanVec{Qu.codes, Qu.scales, Qu.tensor_scale, Qu.k_pad, (Qu.flags & AVERIS_HADAMARD16) ? 1 : 0};
     g.rv = MeanVec{Qv.codes, Qv.scales, Qv.tensor_scale, Qv.k_pad, (Qv.flags & AVERIS_HADAMARD16) ? 1 : 0};
   }
-  g.splits = p.grouped ? 1 : p.splits;
   const int64_t ksteps = ceil_div(K, kBKE);
   g.k_chunk = ceil_div(ksteps, g.splits) * kBKE;
   if (g.splits > 1) {
@@ -1379,8 +1483,8 @@ hipError_t gemm_launch(const GemmPlan& p) {
   // one resident round of workgroups, each looping over its tiles
   g.n_work = (int)work;
   const int64_t grid = std::min<int64_t>(work, (int64_t)resident_per_cu(cfg) * cu_count());
-  if (fmt == AVERIS_MXFP4) launch_cfg<AVERIS_MXFP4>(cfg, mu_in, g, (unsigned)grid, p.stream, p.ws, p.h_offsets);
-  else launch_cfg<AVERIS_NVFP4>(cfg, mu_in, g, (unsigned)grid, p.stream, p.ws, p.h_offsets);
+  if (fmt == AVERIS_MXFP4) launch_cfg<AVERIS_MXFP4>(cfg, mu_in, g, (unsigned)grid, p.stream, p.ws, p.h_offsets, st_fused);
+  else launch_cfg<AVERIS_NVFP4>(cfg, mu_in, g, (unsigned)grid, p.stream, p.ws, p.h_offsets, st_fused);
   if (g.splits > 1) {
     const unsigned blocks = (unsigned)ceil_div(M * (N / 4), 256);
     if (fmt == AVERIS_MXFP4)
@@ -1390,6 +1494,9 @@ hipError_t gemm_launch(const GemmPlan& p) {
       hipLaunchKernelGGL(k_splitk_reduce<AVERIS_NVFP4>, dim3(blocks), dim3(256), 0, p.stream, partials, g.splits, g, p.c,
                          p.ldc, p.c_bf16);
   }
+  if (p.stats && !st_fused)
+    colparts_launch(p.c, p.c_bf16 ? AVERIS_BF16 : AVERIS_F32, M, N, p.ldc, p.stats->sum, p.stats->min, p.stats->max,
+                    p.stream);
   return hipGetLastError();
 }
 

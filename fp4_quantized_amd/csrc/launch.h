@@ -18,7 +18,16 @@ struct SplitQuantPlan {
   // stochastic rounding of the E2M1 codes with this Philox key (dense launches only)
   bool sr; uint64_t seed;
   bool check;  // CHECK_FINITE: status bits into workspace word 0
+  // column partials from X's producer (dense SPLIT): st_parts rows of [cols] fp32 sums, and
+  // minima / maxima or null; replace the statistics pass over X
+  const float* st_sum = nullptr; const float* st_min = nullptr; const float* st_max = nullptr;
+  int64_t st_parts = 0;
 };
+// Column partials of an output that its GEMM could not take in the epilogue: rows of
+// colparts_rows() rows each, fp32 sums (and minima / maxima when mn is set), [part][N].
+int64_t colparts_rows();
+void colparts_launch(const void* c, int cdt, int64_t M, int64_t N, int64_t ldc, float* sum, float* mn, float* mx,
+                     hipStream_t s);
 size_t split_quant_ws_bytes(int64_t rows, int64_t cols);
 size_t split_quant_grouped_ws_bytes(int64_t rows, int64_t cols, int64_t E);
 hipError_t split_quant_launch(const SplitQuantPlan& p);
@@ -36,6 +45,9 @@ struct GemmPlan {
   const int64_t* d_offsets; const int64_t* h_offsets; int64_t E;
   void* ws;
   hipStream_t stream;
+  // column statistics of the stored output (dense launches): fp32 partials [part][N] of rows
+  // [part * part_rows, ...), sums, and minima / maxima when min is set; part_rows is written
+  struct Stats { float* sum; float* min; float* max; int64_t part_rows; }* stats = nullptr;
 };
 int choose_splits(int fmt, int64_t M, int64_t N, int64_t K);
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int splits);

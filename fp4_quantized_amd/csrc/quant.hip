@@ -108,6 +108,10 @@ struct ColArgs {
   float* ramax_part; float* mamax_part;    // [groups][n_strips]
   int n_strips, mode, h16;
   const int64_t* offsets; int E;
+  // PARTS launches: fp32 partials [slab][cols] of each slab's column sum (min, max), no finalize
+  float* o_sum; float* o_min; float* o_max;
+  // k_colstats_given: fp32 partials [g_parts][cols] of the column sums (min, max) of the rows
+  const float* g_sum; const float* g_min; const float* g_max; int64_t g_parts;
 };
 
 __device__ __host__ inline int64_t cs_slabs(int64_t len) {
@@ -115,7 +119,37 @@ __device__ __host__ inline int64_t cs_slabs(int64_t len) {
   return n > 0 ? n : 1;
 }
 
-template <typename T, bool MINMAX>
+// Finalization of one 64-column group of a strip, shared by both statistics kernels: the mean of
+// column c from its sum S over glen rows (SPLIT without MEAN_GIVEN; MEAN_GIVEN reads it), and
+// the wave's maxima of |residual| (MINMAX: exact from the column min / max, since fl(x - mu) is
+// monotone in x) and of |(rotated) mean|, one partial each.  Called by all 64 lanes of a wave.
+template <bool MINMAX>
+__device__ __forceinline__ void strip_finalize(const ColArgs& a, int e, int strip, int cw, int lane, int64_t c,
+                                               bool cin, int64_t glen, double S, float lo, float hi) {
+  float* mean = a.mean ? a.mean + (int64_t)e * a.cols : nullptr;
+  float mu = 0.0f;
+  if (cin && (a.mode & 1)) {
+    if (a.mode & 2) mu = mean[c];
+    else { mu = glen > 0 ? (float)(S / (double)glen) : 0.0f; mean[c] = mu; }
+  }
+  float ra = 0.0f;
+  if (MINMAX && cin && glen > 0) ra = fmaxf(__fsub_rn(hi, mu), __fsub_rn(mu, lo));
+  // |mu| per column, rotated within 16-column blocks when the mean is quantized rotated
+  float mv[1] = {cin ? mu : 0.0f};
+  if (a.h16) h16_lanes<1>(mv, lane);
+  float ma = fabsf(mv[0]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) { ra = wave_xor_max(ra, m); ma = wave_xor_max(ma, m); }
+  if (lane == 0) {
+    const int64_t o = ((int64_t)e * a.n_strips + strip) * kCsWaves + cw;  // per 64 columns
+    a.ramax_part[o] = ra; a.mamax_part[o] = ma;
+  }
+}
+
+// PARTS: write the slab's column partials (fp32) to o_sum / o_min / o_max and stop (no
+// counters, no slots, no finalize): the column statistics of an output whose producer could not
+// take them in its epilogue.
+template <typename T, bool MINMAX, bool PARTS = false>
 __global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
   constexpr int VEC = Elem<T>::VEC;
   constexpr int LPR = kCsCols / VEC;   // lanes per row
@@ -131,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
   __shared__ int s_last;
 
   const int t = threadIdx.x;
-  if (blockIdx.x == 0 && blockIdx.y == 0)
+  if (!PARTS && blockIdx.x == 0 && blockIdx.y == 0)
     for (int i = t; i < a.n_slots; i += kThreads) a.slots[i] = 0u;  // maxed by later kernels
 
   // this workgroup's rows [rb, re) and its group's slabs [s0, s0 + nsl)
@@ -200,6 +234,12 @@ __global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
       sacc += s_sum[q][t];
       if (MINMAX) { lo = fminf(lo, s_min[q][t]); hi = fmaxf(hi, s_max[q][t]); }
     }
+    if constexpr (PARTS) {
+      const int64_t o = (int64_t)blockIdx.y * a.cols + c0 + t;
+      a.o_sum[o] = (float)sacc;
+      if (MINMAX) { a.o_min[o] = lo; a.o_max[o] = hi; }
+      return;
+    }
     // agent-scope atomic stores: complete only at the coherence point all XCDs read from
     const int64_t o = (int64_t)blockIdx.y * a.cols + c0 + t;
     __hip_atomic_store(a.psum + o, sacc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -219,6 +259,7 @@ __global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
   // on the update, acquire in the finalizer) compiles to a full L2 write-back and invalidate per
   // workgroup and measured 2.1x slower for this pass on the layer shapes, so the ordering is
   // the hardware's completion order of these coherent accesses.
+  if constexpr (PARTS) return;
   __syncthreads();
   uint32_t* counter = a.counters + ((int64_t)e * a.n_strips + strip) * kCounterStride;
   if (t == 0)
@@ -274,26 +315,66 @@ __global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
       lo = fminf(fminf(f_min[0][lane], f_min[1][lane]), fminf(f_min[2][lane], f_min[3][lane]));
       hi = fmaxf(fmaxf(f_max[0][lane], f_max[1][lane]), fmaxf(f_max[2][lane], f_max[3][lane]));
     }
-    float* mean = a.mean ? a.mean + (int64_t)e * a.cols : nullptr;
-    float mu = 0.0f;
-    if (cin && (a.mode & 1)) {
-      if (a.mode & 2) mu = mean[c];
-      else { mu = glen > 0 ? (float)(S / (double)glen) : 0.0f; mean[c] = mu; }
-    }
-    float ra = 0.0f;
-    if (MINMAX && cin && glen > 0) ra = fmaxf(__fsub_rn(hi, mu), __fsub_rn(mu, lo));
-    // |mu| per column, rotated within 16-column blocks when the mean is quantized rotated
-    float mv[1] = {cin ? mu : 0.0f};
-    if (a.h16) h16_lanes<1>(mv, lane);
-    float ma = fabsf(mv[0]);
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) { ra = wave_xor_max(ra, m); ma = wave_xor_max(ma, m); }
-    if (lane == 0) {
-      const int64_t o = ((int64_t)e * a.n_strips + strip) * kCsWaves + cw;  // per 64 columns
-      a.ramax_part[o] = ra; a.mamax_part[o] = ma;
-      if (cw == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
-    }
+    strip_finalize<MINMAX>(a, e, strip, cw, lane, c, cin, glen, S, lo, hi);
+    if (lane == 0 && cw == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
   }
+}
+
+// ------------------------------------------------------------------------------------------
+// k_colstats_given: the mean and the strip maxima from column partials that the producer of X
+// computed (a GEMM epilogue, or k_colstats in PARTS mode): g_parts rows of fp32 sums (and, for
+// MINMAX, minima and maxima) per column.  One workgroup of kGivenWaves waves per 64-column
+// strip; wave q takes the q-th run of consecutive parts (fp64 sums in part order, its loads in
+// flight together), the runs are combined in wave order, then finalized as in k_colstats.
+// Block 0 also zeroes the amax slots.  Dense SPLIT only.
+// ------------------------------------------------------------------------------------------
+constexpr int kGivenWaves = 16;
+
+template <bool MINMAX>
+__global__ __launch_bounds__(64 * kGivenWaves) void k_colstats_given(ColArgs a) {
+  static_assert(kCsWaves == 1, "one wave per strip");
+  constexpr int BATCH = 16;
+  __shared__ double f_sum[kGivenWaves][kCsCols];
+  __shared__ float f_min[MINMAX ? kGivenWaves : 1][kCsCols], f_max[MINMAX ? kGivenWaves : 1][kCsCols];
+  const int t = threadIdx.x, q = t >> 6, lane = t & 63;
+  if (blockIdx.x == 0)
+    for (int i = t; i < a.n_slots; i += 64 * kGivenWaves) a.slots[i] = 0u;
+  const int strip = blockIdx.x;
+  const int64_t c = (int64_t)strip * kCsCols + lane;
+  const bool cin = c < a.cols;
+  const int64_t per = (a.g_parts + kGivenWaves - 1) / kGivenWaves;
+  const int64_t pb = q * per, pe = pb + per < a.g_parts ? pb + per : a.g_parts;
+  double sacc = 0.0;
+  float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+  if (cin)
+    for (int64_t p0 = pb; p0 < pe; p0 += BATCH) {
+      float v[BATCH], l8[MINMAX ? BATCH : 1], h8[MINMAX ? BATCH : 1];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const bool ok = p0 + u < pe;
+        const int64_t o = (p0 + u) * a.cols + c;
+        v[u] = ok ? a.g_sum[o] : 0.0f;
+        if constexpr (MINMAX) {
+          l8[u] = ok ? a.g_min[o] : __builtin_huge_valf();
+          h8[u] = ok ? a.g_max[o] : -__builtin_huge_valf();
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        sacc += (double)v[u];
+        if constexpr (MINMAX) { lo = fminf(lo, l8[u]); hi = fmaxf(hi, h8[u]); }
+      }
+    }
+  f_sum[q][lane] = sacc;
+  if constexpr (MINMAX) { f_min[q][lane] = lo; f_max[q][lane] = hi; }
+  __syncthreads();
+  if (q != 0) return;
+  double S = 0.0;
+  for (int i = 0; i < kGivenWaves; ++i) {
+    S += f_sum[i][lane];
+    if constexpr (MINMAX) { lo = fminf(lo, f_min[i][lane]); hi = fmaxf(hi, f_max[i][lane]); }
+  }
+  strip_finalize<MINMAX>(a, 0, strip, 0, lane, c, cin, a.rows, S, lo, hi);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -952,6 +1033,47 @@ static void launch_stats_t(const SplitQuantPlan& p, const SqLayout& L) {
   hipLaunchKernelGGL((k_colstats<T, MINMAX>), grid, dim3(kThreads), 0, p.stream, a);
 }
 
+template <bool MINMAX>
+static void launch_stats_given(const SplitQuantPlan& p, const SqLayout& L) {
+  ColArgs a{};
+  a.rows = p.rows; a.cols = p.cols;
+  a.slots = L.slots; a.n_slots = L.n_slots;
+  a.mean = p.mean; a.ramax_part = L.ramax; a.mamax_part = L.mamax;
+  a.n_strips = (int)n_strips(p.cols);
+  a.mode = 1;
+  a.h16 = p.h16 ? 1 : 0;
+  a.E = 1;
+  a.g_sum = p.st_sum; a.g_min = p.st_min; a.g_max = p.st_max; a.g_parts = p.st_parts;
+  hipLaunchKernelGGL((k_colstats_given<MINMAX>), dim3((unsigned)n_strips(p.cols)), dim3(64 * kGivenWaves), 0, p.stream,
+                     a);
+}
+
+template <typename T, bool MINMAX>
+static void launch_colparts_t(const void* c, int64_t M, int64_t N, int64_t ldc, float* sum, float* mn, float* mx,
+                              hipStream_t s) {
+  ColArgs a{};
+  a.x = c; a.rows = M; a.cols = N; a.ldx = ldc;
+  a.n_strips = (int)n_strips(N);
+  a.E = 1;
+  a.o_sum = sum; a.o_min = mn; a.o_max = mx;
+  hipLaunchKernelGGL((k_colstats<T, MINMAX, true>), dim3((unsigned)n_strips(N), (unsigned)ceil_div(M, kCsRows)),
+                     dim3(kThreads), 0, s, a);
+}
+
+int64_t colparts_rows() { return kCsRows; }
+
+void colparts_launch(const void* c, int cdt, int64_t M, int64_t N, int64_t ldc, float* sum, float* mn, float* mx,
+                     hipStream_t s) {
+  if (M <= 0 || N <= 0) return;
+  if (cdt == AVERIS_BF16) {
+    if (mn) launch_colparts_t<uint16_t, true>(c, M, N, ldc, sum, mn, mx, s);
+    else launch_colparts_t<uint16_t, false>(c, M, N, ldc, sum, mn, mx, s);
+  } else {
+    if (mn) launch_colparts_t<float, true>(c, M, N, ldc, sum, mn, mx, s);
+    else launch_colparts_t<float, false>(c, M, N, ldc, sum, mn, mx, s);
+  }
+}
+
 hipError_t split_quant_launch(const SplitQuantPlan& p) {
   const bool grouped = p.E > 0;
   int64_t nslab = cs_slabs(p.rows);
@@ -961,8 +1083,11 @@ hipError_t split_quant_launch(const SplitQuantPlan& p) {
   }
   const SqLayout L = sq_layout(p.ws, nslab, p.cols, grouped ? p.E : 1);
   const bool nv = p.fmt == AVERIS_NVFP4;
-  // column statistics: the mean (SPLIT without MEAN_GIVEN) and, for NVFP4, the residual amax
-  if (p.cols > 0 && (nv || (p.split && !p.mean_given))) {
+  // column statistics: the mean (SPLIT without MEAN_GIVEN) and, for NVFP4, the residual amax;
+  // from the producer's column partials when it computed them
+  if (p.st_sum) {
+    if (p.st_min) launch_stats_given<true>(p, L); else launch_stats_given<false>(p, L);
+  } else if (p.cols > 0 && (nv || (p.split && !p.mean_given))) {
     if (p.xdt == AVERIS_BF16) {
       if (nv) launch_stats_t<uint16_t, true>(p, L); else launch_stats_t<uint16_t, false>(p, L);
     } else {

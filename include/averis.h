@@ -201,8 +201,10 @@ int32_t averis_split_quant_noalloc(const void *x, int32_t xdt, int64_t rows, int
  *  mu_x  [outer = 1, k = m]  (q_mean of split_quant(X)), or NULL for the vanilla GEMM
  *  w     [outer = n, k = m]  (q_col of split_quant(W [m, n]) without SPLIT)
  *  y     device [l, n] row-major, element type ydt, leading dimension n <= ldy < 2^23; n % 8 == 0.
- * All operands share fmt and the HADAMARD16 bit.  The mean term is
- * computed once per call as a GEMV and added to every row in the GEMM epilogue.
+ * All operands share fmt and the HADAMARD16 bit.  The mean term Q(mu_X) Q(W) is one row added
+ * to every output row: MXFP4 launches compute it inside the GEMM from the quantized mean
+ * (one scaled MFMA per four on the tile's weight fragments) while k_pad <= 16384; NVFP4 and
+ * longer K compute it once per call as a GEMV and add it in the epilogue.
  * ----------------------------------------------------------------------------------------- */
 size_t averis_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t fmt);
 
@@ -220,6 +222,67 @@ int32_t averis_linear_fwd(const averis_qtensor *xr, const averis_qtensor *mu_x,
 int32_t averis_linear_bwd_dx(const averis_qtensor *dr, const averis_qtensor *mu_d,
                              const averis_qtensor *w, void *dx, int32_t dxdt, int64_t lddx,
                              void *ws, size_t ws_bytes, void *stream);
+
+/* -----------------------------------------------------------------------------------------
+ * Producer-fused column statistics.  The split ([rainbus] 方法步骤详情: mu = (1/l) 1^T X over
+ * all l token rows, before any element of X_R can be quantized) costs a pass over X for its
+ * column statistics; [paperlayer] §3 Method describes the split as cheap elementwise work.
+ * A GEMM that writes X (the forward GEMM whose output is the next linear's input, the
+ * input-gradient GEMM whose output is the next D) can take the statistics of what it stores,
+ * and split_quant then starts from them instead of reading X for them.
+ *
+ * averis_colstats: column partials of an output [rows, cols] over consecutive row blocks.
+ *   sum       device fp32 [capacity]: sum[p * cols + c] = fp32 sum of column c over rows
+ *             [p * part_rows, min((p + 1) * part_rows, rows)), of the values as stored
+ *             (after rounding to the output type)
+ *   min, max  device fp32 [capacity]: column minima and maxima of the same rows, or both NULL.
+ *             Needed when the statistics feed an NVFP4 split without HADAMARD16, whose residual
+ *             tensor scale comes from them.
+ *   capacity  floats each given array holds; averis_colstats_capacity(rows, cols) suffices for
+ *             every producer.
+ *   rows, cols, parts, part_rows: written by the producer (parts = ceil(rows / part_rows)).
+ * The arrays are caller-owned; a producer writes parts * cols floats of each.
+ * ----------------------------------------------------------------------------------------- */
+typedef struct averis_colstats {
+  float *sum;
+  float *min;
+  float *max;
+  int64_t capacity;
+  int64_t rows, cols, parts, part_rows;
+} averis_colstats;
+
+int64_t averis_colstats_capacity(int64_t rows, int64_t cols);
+
+/* averis_linear_fwd / averis_linear_bwd_dx that also write the column statistics of the output
+ * into *stats (written by the same stream-ordered work).  Sums without minima and maxima are
+ * taken in the GEMM epilogue by the single-split launches of the MXFP4 warp-specialized kernel
+ * and of the NVFP4 two-stage kernel (64- or 128-row parts); other launches, and requests with
+ * minima and maxima, take them in a pass over the stored output after the GEMM (512-row
+ * parts).  Errors as the plain calls, and AVERIS_E_NULL (stats
+ * or stats->sum NULL, or one of min / max NULL without the other), AVERIS_E_SHAPE (capacity
+ * below averis_colstats_capacity of the output). */
+int32_t averis_linear_fwd_stats(const averis_qtensor *xr, const averis_qtensor *mu_x,
+                                const averis_qtensor *w, void *y, int32_t ydt, int64_t ldy,
+                                averis_colstats *stats, void *ws, size_t ws_bytes, void *stream);
+
+int32_t averis_linear_bwd_dx_stats(const averis_qtensor *dr, const averis_qtensor *mu_d,
+                                   const averis_qtensor *w, void *dx, int32_t dxdt, int64_t lddx,
+                                   averis_colstats *stats, void *ws, size_t ws_bytes, void *stream);
+
+/* averis_split_quant of x with SPLIT from the column statistics `stats` that x's producer wrote
+ * (stats->rows == rows, stats->cols == cols): the mean is the fp64 sum of the partial sums in
+ * part order divided by rows (as fp32, written to `mean`), and x is read once, by the
+ * quantization.  flags: AVERIS_SPLIT required; AVERIS_HADAMARD16 and AVERIS_CHECK_FINITE as in
+ * averis_split_quant; AVERIS_MEAN_GIVEN not allowed (AVERIS_E_FLAGS).  NVFP4 without
+ * HADAMARD16 needs stats->min and stats->max (AVERIS_E_NULL).  Given the mean it writes, every
+ * output equals averis_split_quant's with AVERIS_MEAN_GIVEN and that mean (the minima and
+ * maxima are exact).  Other arguments, workspace and errors as averis_split_quant; dense only. */
+int32_t averis_split_quant_stats(const void *x, int32_t xdt, int64_t rows, int64_t cols,
+                                 int64_t ldx, int32_t fmt, uint32_t flags,
+                                 const averis_colstats *stats, float *mean,
+                                 const averis_qtensor *q_row, const averis_qtensor *q_col,
+                                 const averis_qtensor *q_mean, void *ws, size_t ws_bytes,
+                                 void *stream);
 
 /* -----------------------------------------------------------------------------------------
  * averis_linear_bwd_dw -- dW = Q(X_R)^T Q(D_R) + l Q(mu_X)^T Q(mu_D)   ([rainbus] 方法步骤详情:

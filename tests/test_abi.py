@@ -230,3 +230,76 @@ def test_check_finite_flag_rules():
     st = L.averis_split_quant_noalloc(FAKE, av.BF16, 256, 128, 128, av.NVFP4, av.SPLIT | av.CHECK_FINITE, FAKE,
                                       r(q(256, 128)), r(q(128, 256)), r(q(1, 128)), None)
     assert st == E_FLAGS
+
+
+def colstats(rows=256, cols=128, parts=4, part_rows=64, minmax=True, capacity=None):
+    cap = parts * cols if capacity is None else capacity
+    return av.CColStats(FAKE, FAKE if minmax else None, FAKE if minmax else None, cap, rows, cols, parts, part_rows)
+
+
+def split_stats(st, rows=256, cols=128, fmt=av.NVFP4, flags=av.SPLIT, mean=FAKE):
+    L = av.lib()
+    h = flags & av.HADAMARD16
+    return L.averis_split_quant_stats(FAKE, av.BF16, rows, cols, cols, fmt, flags,
+                                      ctypes.byref(st) if st is not None else None, mean,
+                                      ctypes.byref(q(rows, cols, fmt, h)), ctypes.byref(q(cols, rows, fmt, h)),
+                                      ctypes.byref(q(1, cols, fmt, h)), FAKE, 1 << 30, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    ("no_stats", E_NULL), ("no_split", E_FLAGS), ("mean_given", E_FLAGS), ("no_sum", E_NULL),
+    ("half_minmax", E_NULL), ("nvfp4_needs_minmax", E_NULL), ("rows", E_SHAPE), ("cols", E_SHAPE),
+    ("parts", E_SHAPE), ("capacity", E_SHAPE), ("part_rows", E_SHAPE),
+])
+def test_split_quant_stats_rejects(case, status):
+    st, kw = colstats(), {}
+    if case == "no_stats":
+        st = None
+    elif case == "no_split":
+        kw["flags"] = 0
+    elif case == "mean_given":
+        kw["flags"] = av.SPLIT | av.MEAN_GIVEN
+    elif case == "no_sum":
+        st.sum = None
+    elif case == "half_minmax":
+        st.max = None
+    elif case == "nvfp4_needs_minmax":
+        st = colstats(minmax=False)
+    elif case == "rows":
+        st.rows = 255
+    elif case == "cols":
+        st.cols = 96
+    elif case == "parts":
+        st.parts = 3
+    elif case == "capacity":
+        st.capacity = 3 * 128
+    elif case == "part_rows":
+        st = colstats(part_rows=0, parts=0)
+    assert split_stats(st, **kw) == status
+
+
+def test_split_quant_stats_minmax_rules():
+    # minima and maxima are required only for NVFP4 without the Hadamard: with sums alone, MXFP4
+    # and NVFP4 with the Hadamard pass that check and are refused on the mismatched row count
+    assert split_stats(colstats(minmax=False), fmt=av.NVFP4, flags=av.SPLIT) == E_NULL
+    assert split_stats(colstats(minmax=False, rows=255), fmt=av.MXFP4) == E_SHAPE
+    assert split_stats(colstats(minmax=False, rows=255), fmt=av.NVFP4, flags=av.SPLIT | av.HADAMARD16) == E_SHAPE
+
+
+def test_linear_stats_rejects():
+    L = av.lib()
+    a, mu, w = q(256, 512), q(1, 512), q(384, 512)
+    r = ctypes.byref
+    assert L.averis_colstats_capacity(256, 384) == 4 * 384
+    assert L.averis_colstats_capacity(257, 384) == 5 * 384
+    assert L.averis_colstats_capacity(-1, 384) == 0
+    for fn in (L.averis_linear_fwd_stats, L.averis_linear_bwd_dx_stats):
+        assert fn(r(a), r(mu), r(w), FAKE, av.BF16, 384, None, FAKE, 1 << 30, None) == E_NULL
+        small = colstats(rows=256, cols=384, parts=3)
+        assert fn(r(a), r(mu), r(w), FAKE, av.BF16, 384, r(small), FAKE, 1 << 30, None) == E_SHAPE
+        half = colstats(rows=256, cols=384)
+        half.min = None
+        assert fn(r(a), r(mu), r(w), FAKE, av.BF16, 384, r(half), FAKE, 1 << 30, None) == E_NULL
+        # the plain checks come first
+        assert fn(r(a), r(mu), r(q(384, 256)), FAKE, av.BF16, 384, r(colstats(cols=384)), FAKE, 1 << 30,
+                  None) == E_SHAPE
