@@ -13,7 +13,9 @@ value = GEMM flops of the step / the step's median cold time.
 Timing: each measured call sequence is captured once in a HIP graph.  Cold replays follow a
 512 MiB read that evicts the L2s and the 256 MB Infinity Cache (inputs start in HBM); warm
 replays run back to back.  HIP events on the launching stream bracket every replay; median and
-minimum are reported.
+minimum are reported.  The roofline kernel's launch duration is the mean per launch of a graph
+of ten back-to-back launches replayed between events (a replay of a one-launch graph holds
+about 10 us of launch latency inside the events, a fifth of this kernel's time).
 
 Other stages (parity configurations and the pages' comparisons): the same layer with
 independent inputs per linear, a GEMM output split next (the gate forward GEMM, then the split
@@ -150,6 +152,41 @@ def main():
         return {"cold_med": float(np.median(c)), "cold_min": float(np.min(c)),
                 "warm_med": float(np.median(wm)), "warm_min": float(np.min(wm))}
 
+    def timed_launch(fn, n=None, reps=10):
+        """One kernel's launch duration (ms): a graph of `reps` back-to-back launches replayed n
+        times between events on the launching stream, per launch (mean and median over the
+        replays); and, for reference, single eager launches after the cache-evicting read (cold),
+        whose events also hold a few microseconds of event and launch latency."""
+        n = n or steps
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        back = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in back:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        cold = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            flush.sum()
+            a.record()
+            fn()
+            b.record()
+            cold.append((a, b))
+        torch.cuda.synchronize()
+        bk = [a.elapsed_time(b) / reps for a, b in back]
+        c = [a.elapsed_time(b) for a, b in cold]
+        del g
+        return {"mean": float(np.mean(bk)), "med": float(np.median(bk)), "min": float(np.min(bk)),
+                "cold_eager_med": float(np.median(c)), "cold_eager_min": float(np.min(c))}
+
     def r4(d):
         return {k: round(v, 5) for k, v in d.items()}
 
@@ -214,8 +251,9 @@ def main():
     if headline is not None:
         c = next(c for c in headline.lin if c["name"] == "gate")  # gate / up forward, down dX: same shape
         l, m, n = c["l"], c["m"], c["n"]
-        t = timed(lambda: av.linear_fwd(c["sx"]["row"], c["sx"]["mean_q"], c["sw"]["col"], out=c["y"], ws=c["ws_fwd"]))
-        launch_s = t["cold_med"] * 1e-3
+        t = timed_launch(lambda: av.linear_fwd(c["sx"]["row"], c["sx"]["mean_q"], c["sw"]["col"], out=c["y"],
+                                               ws=c["ws_fwd"]))
+        launch_s = t["mean"] * 1e-3
         op = 0.5 + 1.0 / 32
         flops = 2.0 * l * m * n
         nbytes = (l * m + n * m + m) * op + 2.0 * l * n
@@ -235,7 +273,7 @@ def main():
             "mfma_frac": round(t_mfma / launch_s, 4), "hbm_frac": round(t_hbm / launch_s, 4),
             "frac_vs_measured_copy": round(nbytes / launch_s / 1e9 / env["copy_GBps"], 4),
         }
-        log(f"roofline launch {t['cold_med']*1e3:.1f} us: {flops / launch_s / 1e12:.0f} TFLOP/s, "
+        log(f"roofline launch {t['mean']*1e3:.1f} us: {flops / launch_s / 1e12:.0f} TFLOP/s, "
             f"{nbytes / launch_s / 1e9:.0f} GB/s")
         del headline
 
