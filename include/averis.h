@@ -202,9 +202,10 @@ int32_t averis_split_quant_noalloc(const void *x, int32_t xdt, int64_t rows, int
  *  w     [outer = n, k = m]  (q_col of split_quant(W [m, n]) without SPLIT)
  *  y     device [l, n] row-major, element type ydt, leading dimension n <= ldy < 2^23; n % 8 == 0.
  * All operands share fmt and the HADAMARD16 bit.  The mean term Q(mu_X) Q(W) is one row added
- * to every output row: MXFP4 launches compute it inside the GEMM from the quantized mean
- * (one scaled MFMA per four on the tile's weight fragments) while k_pad <= 16384; NVFP4 and
- * longer K compute it once per call as a GEMV and add it in the epilogue.
+ * to every output row: MXFP4 launches compute it inside the GEMM from the quantized mean (one
+ * more scaled MFMA per wave and K-substep, on the weight fragments the tile already holds)
+ * while k_pad <= 8192; NVFP4 and longer K compute it once per call as a GEMV and add it in the
+ * epilogue.
  * ----------------------------------------------------------------------------------------- */
 size_t averis_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t fmt);
 
