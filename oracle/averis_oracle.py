@@ -516,6 +516,43 @@ def linear_bwd_dw_grouped(sq_x, sq_d, offsets, m, n):
 
 
 # --------------------------------------------------------------------------------------------
+# Producers of a transformer block's linear inputs, whose column statistics the split can take
+# instead of reading X again.  The pages name the model (Qwen3: RMSNorm, SwiGLU) but not these
+# operations' arithmetic; the definitions are the published ones, in fp32 with one rounding per
+# operation as the kernels do them, the output rounded to bf16.  Only the sum of squares is
+# taken in fp64 here (the kernels sum in fp32), and exp is the correctly rounded one.
+# --------------------------------------------------------------------------------------------
+
+def round_bf16(v):
+    """fp32 -> bf16 (round to nearest even, finite values), returned as fp32."""
+    u = np.asarray(v, np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+def rmsnorm(x, w, eps, out_bf16=True):
+    """RMSNorm (Zhang and Sennrich, 2019): y = x * (1 / sqrt(mean_c(x^2) + eps)) * w per row.
+    fp32 steps: ms = fl(fl(s) * fl(1 / cols)), rs = fl(1 / fl(sqrt(fl(ms + eps)))),
+    y = fl(fl(x * rs) * w), with s the fp64 sum of squares rounded to fp32."""
+    x = np.asarray(x, np.float32)
+    cols = x.shape[1]
+    s = np.float32((x.astype(np.float64) ** 2).sum(axis=1)) if x.size else np.zeros(x.shape[0], np.float32)
+    ms = np.float32(s) * np.float32(np.float32(1.0) / np.float32(cols))
+    rs = np.float32(1.0) / np.sqrt(np.float32(ms + np.float32(eps)), dtype=np.float32)
+    y = (x * rs[:, None]) * np.asarray(w, np.float32)[None, :]
+    return round_bf16(y) if out_bf16 else y.astype(np.float32)
+
+
+def swiglu(g, u, out_bf16=True):
+    """SwiGLU gate (Shazeer, 2020): y = silu(g) * u, silu(g) = g / (1 + exp(-g)); fp32 steps,
+    exp correctly rounded to fp32."""
+    g = np.asarray(g, np.float32)
+    e = np.float32(np.exp(-g.astype(np.float64)))
+    y = (g / (np.float32(1.0) + e)) * np.asarray(u, np.float32)
+    return round_bf16(y) if out_bf16 else y.astype(np.float32)
+
+
+# --------------------------------------------------------------------------------------------
 # Error statistic used for the pages' directional claim ([paperlayer] D Output-Gradient Mean
 # Centering: centering lowers the relative NVFP4 quantization error).
 # --------------------------------------------------------------------------------------------

@@ -521,3 +521,40 @@ def test_sr_split_quant_is_seeded_and_one_step_from_nearest():
                                                  r["row"].s_dec, fmt, r["row"].k, False))[:, ::g], g, axis=1)
         steps = np.abs(dq_sr - dq_rn) / np.where(scale > 0, scale, 1.0)  # in units of the block scale
         assert steps.max() <= 2.0 + 1e-9  # neighbours differ by at most one grid step (<= 2 units)
+
+
+# ---------------- producers of the linear inputs (RMSNorm, SwiGLU) ----------------
+
+def test_rmsnorm_closed_form():
+    # row [3, 4]: mean of squares 12.5, so y = [3, 4] / sqrt(12.5); a zero row stays zero with eps
+    x = np.array([[3.0, 4.0], [0.0, 0.0]], np.float32)
+    y = O.rmsnorm(x[:1], np.ones(2, np.float32), 0.0, out_bf16=False)
+    np.testing.assert_allclose(y[0], np.array([3.0, 4.0]) / np.sqrt(12.5), rtol=3e-7)
+    y = O.rmsnorm(x, np.array([2.0, -1.0], np.float32), 1e-6, out_bf16=False)
+    np.testing.assert_allclose(y[0], np.array([6.0, -4.0]) / np.sqrt(12.5 + 1e-6), rtol=3e-7)
+    assert not y[1].any()
+
+
+def test_rmsnorm_matches_torch_and_is_scale_invariant():
+    rng = np.random.default_rng(40)
+    x = rng.standard_normal((64, 96)).astype(np.float32) * 3
+    w = rng.standard_normal(96).astype(np.float32)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x).double(), (96,), torch.from_numpy(w).double(), eps=1e-5)
+    y = O.rmsnorm(x, w, 1e-5, out_bf16=False)
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-6, atol=1e-6)
+    # scaling a row by a power of two scales its root mean square by the same power (eps = 0)
+    assert np.array_equal(O.rmsnorm(x * np.float32(4), w, 0.0), O.rmsnorm(x, w, 0.0))
+    # bf16 output: the fp32 result rounded to nearest even
+    yb = O.rmsnorm(x, w, 1e-5)
+    assert np.array_equal(yb, torch.from_numpy(y).to(torch.bfloat16).float().numpy())
+
+
+def test_swiglu_matches_torch_and_special_values():
+    rng = np.random.default_rng(41)
+    g = (rng.standard_normal((32, 64)) * 4).astype(np.float32)
+    u = rng.standard_normal((32, 64)).astype(np.float32)
+    ref = torch.nn.functional.silu(torch.from_numpy(g).double()) * torch.from_numpy(u).double()
+    np.testing.assert_allclose(O.swiglu(g, u, out_bf16=False), ref.numpy(), rtol=1e-6, atol=1e-7)
+    s = O.swiglu(np.array([[0.0, 40.0, -40.0, 1.0]], np.float32), np.ones((1, 4), np.float32), out_bf16=False)
+    assert s[0, 0] == 0.0 and s[0, 1] == 40.0 and abs(s[0, 2]) < 1e-15
+    np.testing.assert_allclose(s[0, 3], 1.0 / (1.0 + np.exp(-1.0)), rtol=1e-7)

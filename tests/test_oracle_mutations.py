@@ -133,3 +133,23 @@ def test_sr_rounding_up_on_equal_draw_is_caught(monkeypatch):
         return c | (np.signbit(v).astype(np.uint8) << 3)
     monkeypatch.setattr(O, "e2m1_encode_sr", bad)
     _fails(P.test_sr_extreme_draws_are_directed_roundings)
+
+
+def test_rmsnorm_mean_over_wrong_count_is_caught(monkeypatch):
+    orig = O.rmsnorm
+
+    def bad(x, w, eps, out_bf16=True):  # the mean of squares over cols + 1
+        x = np.asarray(x, np.float32)
+        xz = np.concatenate([x, np.zeros((x.shape[0], 1), np.float32)], 1)
+        return orig(xz, np.append(np.asarray(w, np.float32), np.float32(1.0)), eps, out_bf16)[:, :-1]
+    monkeypatch.setattr(O, "rmsnorm", bad)
+    _fails(P.test_rmsnorm_closed_form)
+
+
+def test_swiglu_sigmoid_without_gate_factor_is_caught(monkeypatch):
+    def bad(g, u, out_bf16=True):
+        g = np.asarray(g, np.float32)
+        y = (np.float32(1.0) / (np.float32(1.0) + np.float32(np.exp(-g.astype(np.float64))))) * np.asarray(u, np.float32)
+        return O.round_bf16(y) if out_bf16 else y
+    monkeypatch.setattr(O, "swiglu", bad)
+    _fails(P.test_swiglu_matches_torch_and_special_values)
