@@ -20,7 +20,9 @@ about 10 us of launch latency inside the events, a fifth of this kernel's time).
 Other stages (parity configurations and the pages' comparisons): the same layer with
 independent inputs per linear, a GEMM output split next (the gate forward GEMM, then the split
 of Y, with the statistics pass over Y or with the GEMM taking the column statistics in its
-epilogue), the up_proj layer (l = 8192), the down_proj layer in its four
+epilogue), the MLP block's forward (RMSNorm, split, gate and up GEMMs, SwiGLU, split, down GEMM)
+with and without RMSNorm and SwiGLU writing the splits' column statistics, the up_proj layer
+(l = 8192), the down_proj layer in its four
 variants ({NVFP4, MXFP4} x {Hadamard off, on}, each also vanilla), the MoE layer, and Averis vs
 16x16-Hadamard preprocessing at the explainer's activation shapes (512 x 2048 tokens, 4096 and
 8192 channels).
@@ -52,7 +54,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stages", default="all",
-                   help="comma list of stages to run: layer,independent,chain,up_proj,down_proj,moe,prep,roofline")
+                   help="comma list of stages to run: layer,independent,chain,mlp,up_proj,down_proj,moe,prep,roofline")
     return p.parse_args()
 
 
@@ -114,7 +116,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     av.lib()
     stages = set(args.stages.split(",")) if args.stages != "all" else \
-        {"layer", "independent", "chain", "up_proj", "down_proj", "moe", "prep", "roofline"}
+        {"layer", "independent", "chain", "mlp", "up_proj", "down_proj", "moe", "prep", "roofline"}
     dev = torch.device("cuda:0")
     # Cache eviction before cold replays: read (not write) 512 MiB, so the L2s and the 256 MB
     # Infinity Cache end up holding clean lines of another buffer.
@@ -318,6 +320,64 @@ def main():
             del sx, sw, y, wsl, cs, o_a, o_v, wsq
         out["chain_gemm_then_split"] = res
         del x, w
+
+    # ---------------- the MLP block's forward with its producers ----------------
+    if "mlp" in stages:
+        # RMSNorm of the residual stream [16384, 1024] -> split -> gate and up forward GEMMs
+        # (1024 -> 3072) -> SwiGLU -> split -> down forward GEMM (3072 -> 1024); weights quantized
+        # beforehand (once per optimizer step).  Vanilla FP4, Averis with the splits' own
+        # statistics passes, and Averis with RMSNorm and SwiGLU writing the column statistics
+        # that the splits start from.
+        lay = workloads.layer_device(3, L_LAYER, dev, shared=True)
+        h = next(c for c in lay if c[0] == "gate")[1]
+        wg, wu, wd = (next(c for c in lay if c[0] == nm)[3] for nm in ("gate", "up", "down"))
+        del lay
+        hid, ffn = wg.shape
+        gam = torch.ones(hid, dtype=torch.float32, device=dev)
+        xn = torch.empty(L_LAYER, hid, dtype=torch.bfloat16, device=dev)
+        yg, yu, xd = (torch.empty(L_LAYER, ffn, dtype=torch.bfloat16, device=dev) for _ in range(3))
+        yd = torch.empty(L_LAYER, hid, dtype=torch.bfloat16, device=dev)
+        res = {}
+        for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
+            sg, su, sd_ = (av.split_quant(w, fmt, split=False)["col"] for w in (wg, wu, wd))
+            mm = fmt == av.NVFP4
+            cs_n, cs_d = av.ColStats(L_LAYER, hid, minmax=mm), av.ColStats(L_LAYER, ffn, minmax=mm)
+            o = {sp: (av.split_quant_outputs(L_LAYER, hid, fmt, sp, device=dev),
+                      av.split_quant_outputs(L_LAYER, ffn, fmt, sp, device=dev)) for sp in (True, False)}
+            wsn, wsd = av.split_quant_workspace(L_LAYER, hid, fmt, device=dev), \
+                av.split_quant_workspace(L_LAYER, ffn, fmt, device=dev)
+            wg_ws = av.linear_workspace(o[True][0]["row"], sg)
+            wd_ws = av.linear_workspace(o[True][1]["row"], sd_)
+
+            def block(mode):
+                split = mode != "vanilla"
+                on, od = o[split]
+                prod = mode == "averis_producer"
+                av.rmsnorm(h, gam, 1e-6, stats=cs_n if prod else None, out=xn)
+                if prod:
+                    av.split_quant_stats(xn, cs_n, fmt, out=on, ws=wsn)
+                else:
+                    av.split_quant(xn, fmt, split, out=on, ws=wsn)
+                mu = on["mean_q"] if split else None
+                av.linear_fwd(on["row"], mu, sg, out=yg, ws=wg_ws)
+                av.linear_fwd(on["row"], mu, su, out=yu, ws=wg_ws)
+                av.swiglu(yg, yu, stats=cs_d if prod else None, out=xd)
+                if prod:
+                    av.split_quant_stats(xd, cs_d, fmt, out=od, ws=wsd)
+                else:
+                    av.split_quant(xd, fmt, split, out=od, ws=wsd)
+                av.linear_fwd(od["row"], od["mean_q"] if split else None, sd_, out=yd, ws=wd_ws)
+
+            r = {m: r4(timed(lambda m=m: block(m))) for m in ("vanilla", "averis", "averis_producer")}
+            v = r["vanilla"]["cold_med"]
+            r["averis_overhead_pct"] = round(100.0 * (r["averis"]["cold_med"] - v) / v, 2)
+            r["averis_producer_overhead_pct"] = round(100.0 * (r["averis_producer"]["cold_med"] - v) / v, 2)
+            res[name] = r
+            log(f"mlp forward {name}: averis +{r['averis_overhead_pct']} %, with producer statistics "
+                f"+{r['averis_producer_overhead_pct']} % over vanilla ({v*1e3:.1f} us)")
+            del sg, su, sd_, cs_n, cs_d, o, wsn, wsd, wg_ws, wd_ws
+        out["mlp_forward_with_producers"] = res
+        del h, wg, wu, wd, xn, yg, yu, xd, yd
 
     # ---------------- the layer with independent inputs per linear ----------------
     if "independent" in stages:

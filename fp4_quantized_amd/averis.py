@@ -34,6 +34,7 @@ EXPORTS = [
     "averis_split_quant_noalloc_max_bytes", "averis_split_quant_noalloc",
     "averis_linear_workspace_size", "averis_linear_fwd", "averis_linear_bwd_dx",
     "averis_colstats_capacity", "averis_linear_fwd_stats", "averis_linear_bwd_dx_stats", "averis_split_quant_stats",
+    "averis_rmsnorm_stats", "averis_swiglu_stats",
     "averis_linear_bwd_dw_workspace_size", "averis_linear_bwd_dw",
     "averis_split_quant_grouped_workspace_size", "averis_split_quant_grouped",
     "averis_linear_grouped_workspace_size", "averis_linear_fwd_grouped", "averis_linear_bwd_dx_grouped",
@@ -110,6 +111,8 @@ def lib():
             "averis_linear_fwd_stats": (I32, [Q, Q, Q, P, I32, I64, CS, P, SZ, P]),
             "averis_linear_bwd_dx_stats": (I32, [Q, Q, Q, P, I32, I64, CS, P, SZ, P]),
             "averis_split_quant_stats": (I32, [P, I32, I64, I64, I64, I32, U32, CS, P, Q, Q, Q, P, SZ, P]),
+            "averis_rmsnorm_stats": (I32, [P, I32, I64, I64, I64, P, ctypes.c_float, P, I64, CS, P]),
+            "averis_swiglu_stats": (I32, [P, P, I32, I64, I64, I64, P, I64, CS, P]),
             "averis_linear_bwd_dw_workspace_size": (SZ, [I64, I64, I64, I32]),
             "averis_linear_bwd_dw": (I32, [Q, Q, Q, Q, I64, P, I64, U32, P, SZ, P]),
             "averis_split_quant_grouped_workspace_size": (SZ, [I64, I64, I32, I32, U32]),
@@ -338,6 +341,36 @@ def linear_bwd_dx_stats(dr: QTensor, mu_d: QTensor | None, w: QTensor, stats: Co
                         stream=None, out=None, ws=None):
     """linear_bwd_dx that also writes the column statistics of dX (as stored) into `stats`."""
     return _linear_stats(lib().averis_linear_bwd_dx_stats, dr, mu_d, w, stats, out_dtype, stream, out, ws)
+
+
+def rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, stats: ColStats | None = None, out=None,
+            stream=None):
+    """RMSNorm of x [rows, cols] (bf16 or fp32) with fp32 weight [cols]; writes the column
+    statistics of the output into `stats` when given."""
+    assert x.dim() == 2 and x.is_cuda and x.stride(1) == 1 and weight.dtype == torch.float32
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().averis_rmsnorm_stats(x.data_ptr() if rows else None, _dtype_code(x), rows, cols,
+                                      x.stride(0) if rows else cols, weight.data_ptr(), float(eps),
+                                      out.data_ptr() if rows else None, out.stride(0) if rows else cols,
+                                      ctypes.byref(stats.cs) if stats is not None else None, _stream(stream)))
+    return out
+
+
+def swiglu(gate: torch.Tensor, up: torch.Tensor, stats: ColStats | None = None, out=None, stream=None):
+    """silu(gate) * up for gate, up [rows, cols] (same dtype and strides); writes the column
+    statistics of the output into `stats` when given."""
+    assert gate.shape == up.shape and gate.dtype == up.dtype and gate.stride() == up.stride()
+    assert gate.dim() == 2 and gate.is_cuda and gate.stride(1) == 1
+    rows, cols = gate.shape
+    if out is None:
+        out = torch.empty_like(gate)
+    _check(lib().averis_swiglu_stats(gate.data_ptr() if rows else None, up.data_ptr() if rows else None,
+                                     _dtype_code(gate), rows, cols, gate.stride(0) if rows else cols,
+                                     out.data_ptr() if rows else None, out.stride(0) if rows else cols,
+                                     ctypes.byref(stats.cs) if stats is not None else None, _stream(stream)))
+    return out
 
 
 def split_quant_stats(x: torch.Tensor, stats: ColStats, fmt: int, hadamard: bool = False, row: bool = True,

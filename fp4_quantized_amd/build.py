@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libaveris.so")
-SOURCES = ["quant.hip", "gemm.hip", "api.hip"]
+SOURCES = ["quant.hip", "gemm.hip", "producers.hip", "api.hip"]
 HEADERS = ["common.h", "launch.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

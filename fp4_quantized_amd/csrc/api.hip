@@ -277,6 +277,43 @@ int64_t averis_colstats_capacity(int64_t rows, int64_t cols) {
   return ceil_div(rows, kStatsMinPartRows) * cols;
 }
 
+static int32_t producer_common(int op, const void* x, const void* u, int32_t dt, int64_t rows, int64_t cols,
+                               int64_t ldx, const float* w, float eps, void* y, int64_t ldy, averis_colstats* stats,
+                               void* stream) {
+  if (!dtype_ok(dt)) return AVERIS_E_DTYPE;
+  if (rows < 0 || cols <= 0 || cols % kColMult != 0 || ldx < cols || ldy < cols) return AVERIS_E_SHAPE;
+  if (rows > ((int64_t)1 << 31) || cols > ((int64_t)1 << 24)) return AVERIS_E_SHAPE;
+  if (op == 0 && !(eps >= 0.0f)) return AVERIS_E_SHAPE;
+  if (rows > 0 && (!x || !y || (op == 0 && !w) || (op == 1 && !u))) return AVERIS_E_NULL;
+  const int64_t es = elem_size(dt);
+  if ((x && !aligned16(x)) || (u && !aligned16(u)) || (y && !aligned16(y)) || (ldx * es) % 16 != 0 ||
+      (ldy * es) % 16 != 0)
+    return AVERIS_E_ALIGN;
+  if (stats) {
+    if (!stats->sum || (stats->min == nullptr) != (stats->max == nullptr)) return AVERIS_E_NULL;
+    if (stats->capacity < averis_colstats_capacity(rows, cols)) return AVERIS_E_SHAPE;
+  }
+  if (producer_launch(op, dt, x, u, rows, cols, ldx, w, eps, y, ldy, stats ? stats->sum : nullptr,
+                      stats ? stats->min : nullptr, stats ? stats->max : nullptr,
+                      reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return AVERIS_E_HIP;
+  if (stats) {
+    stats->rows = rows; stats->cols = cols; stats->part_rows = producer_part_rows();
+    stats->parts = ceil_div(rows, producer_part_rows());
+  }
+  return AVERIS_OK;
+}
+
+int32_t averis_rmsnorm_stats(const void* x, int32_t dt, int64_t rows, int64_t cols, int64_t ldx, const float* weight,
+                             float eps, void* y, int64_t ldy, averis_colstats* stats, void* stream) {
+  return producer_common(0, x, nullptr, dt, rows, cols, ldx, weight, eps, y, ldy, stats, stream);
+}
+
+int32_t averis_swiglu_stats(const void* gate, const void* up, int32_t dt, int64_t rows, int64_t cols, int64_t ld,
+                            void* y, int64_t ldy, averis_colstats* stats, void* stream) {
+  return producer_common(1, gate, up, dt, rows, cols, ld, nullptr, 0.0f, y, ldy, stats, stream);
+}
+
 int32_t averis_linear_fwd_stats(const averis_qtensor* xr, const averis_qtensor* mu_x, const averis_qtensor* w, void* y,
                                 int32_t ydt, int64_t ldy, averis_colstats* stats, void* ws, size_t ws_bytes,
                                 void* stream) {

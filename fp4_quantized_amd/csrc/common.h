@@ -33,6 +33,13 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
+// Two fp32 values as bf16 (round to nearest even), the first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+  const v2bf16 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // ---------------------------------------------------------------- element loads ------------
 // Inputs are bf16 (bit patterns in uint16) or fp32.  VEC = elements per 16-byte load.
 template <typename T> struct Elem;

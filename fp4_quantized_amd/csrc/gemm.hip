@@ -153,13 +153,6 @@ __device__ inline float mean_value(const MeanVec& mv, int64_t row, int64_t k) {
   return (float)(s * 0.25);
 }
 
-// Two fp32 values to packed bf16 (round to nearest even), low half first.
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
-  const v2bf16 v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
 // Tile order: consecutive logical tiles walk down a group of `gm` tile rows, then move one
 // tile column right.  With the XCD remap each XCD owns a contiguous run of logical tiles, so
 // it works on a compact (group rows x run / group columns) block and re-reads little of A or B

@@ -49,6 +49,14 @@ struct GemmPlan {
   // [part * part_rows, ...), sums, and minima / maxima when min is set; part_rows is written
   struct Stats { float* sum; float* min; float* max; int64_t part_rows; }* stats = nullptr;
 };
+// Producers with column statistics (producers.hip): op 0 RMSNorm of x with weight w, op 1
+// SwiGLU of gate x and up u; y written as dt; statistics per producer_part_rows() rows when
+// st_sum is set.
+int64_t producer_part_rows();
+hipError_t producer_launch(int op, int dt, const void* x, const void* u, int64_t rows, int64_t cols, int64_t ldx,
+                           const float* w, float eps, void* y, int64_t ldy, float* st_sum, float* st_min,
+                           float* st_max, hipStream_t s);
+
 int choose_splits(int fmt, int64_t M, int64_t N, int64_t K);
 size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K, int splits);
 size_t gemm_grouped_ws_bytes(int64_t M, int64_t N, int64_t E);

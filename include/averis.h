@@ -270,6 +270,26 @@ int32_t averis_linear_bwd_dx_stats(const averis_qtensor *dr, const averis_qtenso
                                    const averis_qtensor *w, void *dx, int32_t dxdt, int64_t lddx,
                                    averis_colstats *stats, void *ws, size_t ws_bytes, void *stream);
 
+/* The producers of a transformer block's linear inputs, with the same column statistics: the
+ * normalization writes the input of q/k/v and of gate/up, the activation the input of down.
+ *   averis_rmsnorm_stats: y[r, c] = x[r, c] * rs_r * weight[c], rs_r = 1 / sqrt(s_r / cols + eps),
+ *     s_r = sum_c x[r, c]^2 (RMSNorm, Zhang and Sennrich 2019).  fp32 arithmetic: s_r summed
+ *     per lane over its columns in order, then across the 64 lanes of a wave; each product
+ *     rounded; y rounded to dt.
+ *   averis_swiglu_stats: y = silu(gate) * up, silu(g) = g / (1 + exp(-g)) (Shazeer 2020), fp32,
+ *     each operation rounded, y rounded to dt.
+ * x, gate, up: device [rows, cols] row-major of element type dt (ld elements, ld * size % 16
+ * == 0); y: device [rows, cols] of type dt, leading dimension ldy; weight: device fp32 [cols];
+ * cols % 32 == 0.  stats: NULL (no statistics) or as for averis_linear_fwd_stats (64-row
+ * parts; min / max when both are set).  Errors: AVERIS_E_DTYPE, AVERIS_E_SHAPE (sizes, eps < 0,
+ * capacity), AVERIS_E_NULL, AVERIS_E_ALIGN, AVERIS_E_HIP. */
+int32_t averis_rmsnorm_stats(const void *x, int32_t dt, int64_t rows, int64_t cols, int64_t ldx,
+                             const float *weight, float eps, void *y, int64_t ldy,
+                             averis_colstats *stats, void *stream);
+
+int32_t averis_swiglu_stats(const void *gate, const void *up, int32_t dt, int64_t rows, int64_t cols,
+                            int64_t ld, void *y, int64_t ldy, averis_colstats *stats, void *stream);
+
 /* averis_split_quant of x with SPLIT from the column statistics `stats` that x's producer wrote
  * (stats->rows == rows, stats->cols == cols): the mean is the fp64 sum of the partial sums in
  * part order divided by rows (as fp32, written to `mean`), and x is read once, by the

@@ -38,7 +38,7 @@ def operands(l, m, n, fmt, seed):
     return av.split_quant(x, fmt), av.split_quant(d, fmt), av.split_quant(w, fmt, split=False)
 
 
-def check_partials(st, yh):
+def check_partials(st, yh, depth=12):
     rows, cols = yh.shape
     assert st.cs.rows == rows and st.cs.cols == cols
     pr = st.part_rows
@@ -48,7 +48,7 @@ def check_partials(st, yh):
     for p in range(st.parts):
         blk = y64[p * pr:(p + 1) * pr]
         ref = blk.sum(axis=0)
-        tol = 12 * 2.0 ** -24 * np.abs(blk).sum(axis=0) + 1e-45
+        tol = depth * 2.0 ** -24 * np.abs(blk).sum(axis=0) + 1e-45
         bad = np.abs(got[p] - ref) > tol
         assert not bad.any(), f"part {p}: {bad.sum()} column sums off"
         if st.min is not None:
