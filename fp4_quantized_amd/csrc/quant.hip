@@ -20,6 +20,8 @@
 //               the rotated amax is not available from min / max, so k_quant first runs once
 //               in amax-only mode.
 // A vanilla MXFP4 operand (no split) needs k_quant only.
+#include <algorithm>
+
 #include "launch.h"
 
 namespace av {
@@ -112,6 +114,7 @@ struct ColArgs {
   float* o_sum; float* o_min; float* o_max;
   // k_colstats_given: fp32 partials [g_parts][cols] of the column sums (min, max) of the rows
   const float* g_sum; const float* g_min; const float* g_max; int64_t g_parts;
+  int64_t g_per;  // k_colstats_given: parts per workgroup
 };
 
 __device__ __host__ inline int64_t cs_slabs(int64_t len) {
@@ -322,35 +325,37 @@ __global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
 
 // ------------------------------------------------------------------------------------------
 // k_colstats_given: the mean and the strip maxima from column partials that the producer of X
-// computed (a GEMM epilogue, or k_colstats in PARTS mode): g_parts rows of fp32 sums (and, for
-// MINMAX, minima and maxima) per column.  One workgroup of kGivenWaves waves per 64-column
-// strip; wave q takes the q-th run of consecutive parts (fp64 sums in part order, its loads in
-// flight together), the runs are combined in wave order, then finalized as in k_colstats.
-// Block 0 also zeroes the amax slots.  Dense SPLIT only.
+// computed (a GEMM epilogue, RMSNorm, SwiGLU, or k_colstats in PARTS mode): g_parts rows of
+// fp32 sums (and, for MINMAX, minima and maxima) per column.  Grid (n_strips, groups of g_per
+// parts): workgroup (s, k) sums parts [k g_per, (k + 1) g_per) of strip s's 64 columns
+// in fp64 (wave q takes every fourth batch of eight parts, in part order; the four waves are
+// added in wave order) and stores the sums as slab k of the workspace's partials.  The slabs
+// meet as k_colstats' do: agent-scope stores, an arrival on the strip's counter, and the last
+// workgroup to arrive reduces the slabs in slab order and finalizes the strip (the same
+// coherence argument).  Block (0, 0) also zeroes the amax slots.  Dense SPLIT only.
 // ------------------------------------------------------------------------------------------
-constexpr int kGivenWaves = 16;
+constexpr int kGivenParts = 32;  // producer parts per workgroup (at most the workspace's slabs)
 
 template <bool MINMAX>
-__global__ __launch_bounds__(64 * kGivenWaves) void k_colstats_given(ColArgs a) {
+__global__ __launch_bounds__(kThreads) void k_colstats_given(ColArgs a) {
   static_assert(kCsWaves == 1, "one wave per strip");
-  constexpr int BATCH = 16;
-  __shared__ double f_sum[kGivenWaves][kCsCols];
-  __shared__ float f_min[MINMAX ? kGivenWaves : 1][kCsCols], f_max[MINMAX ? kGivenWaves : 1][kCsCols];
+  __shared__ double f_sum[4][kCsCols];
+  __shared__ float f_min[4][kCsCols], f_max[4][kCsCols];
+  __shared__ int s_last;
   const int t = threadIdx.x, q = t >> 6, lane = t & 63;
-  if (blockIdx.x == 0)
-    for (int i = t; i < a.n_slots; i += 64 * kGivenWaves) a.slots[i] = 0u;
-  const int strip = blockIdx.x;
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = t; i < a.n_slots; i += kThreads) a.slots[i] = 0u;
+  const int strip = blockIdx.x, slab = blockIdx.y, nsl = (int)gridDim.y;
   const int64_t c = (int64_t)strip * kCsCols + lane;
   const bool cin = c < a.cols;
-  const int64_t per = (a.g_parts + kGivenWaves - 1) / kGivenWaves;
-  const int64_t pb = q * per, pe = pb + per < a.g_parts ? pb + per : a.g_parts;
+  const int64_t pb = (int64_t)slab * a.g_per, pe = pb + a.g_per < a.g_parts ? pb + a.g_per : a.g_parts;
   double sacc = 0.0;
   float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
   if (cin)
-    for (int64_t p0 = pb; p0 < pe; p0 += BATCH) {
-      float v[BATCH], l8[MINMAX ? BATCH : 1], h8[MINMAX ? BATCH : 1];
+    for (int64_t p0 = pb + 8 * q; p0 < pe; p0 += 32) {
+      float v[8], l8[MINMAX ? 8 : 1], h8[MINMAX ? 8 : 1];
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const bool ok = p0 + u < pe;
         const int64_t o = (p0 + u) * a.cols + c;
         v[u] = ok ? a.g_sum[o] : 0.0f;
@@ -360,21 +365,43 @@ __global__ __launch_bounds__(64 * kGivenWaves) void k_colstats_given(ColArgs a) 
         }
       }
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
+      for (int u = 0; u < 8; ++u) {
         sacc += (double)v[u];
         if constexpr (MINMAX) { lo = fminf(lo, l8[u]); hi = fmaxf(hi, h8[u]); }
       }
     }
-  f_sum[q][lane] = sacc;
-  if constexpr (MINMAX) { f_min[q][lane] = lo; f_max[q][lane] = hi; }
+  f_sum[q][lane] = sacc; f_min[q][lane] = lo; f_max[q][lane] = hi;
   __syncthreads();
-  if (q != 0) return;
-  double S = 0.0;
-  for (int i = 0; i < kGivenWaves; ++i) {
-    S += f_sum[i][lane];
-    if constexpr (MINMAX) { lo = fminf(lo, f_min[i][lane]); hi = fmaxf(hi, f_max[i][lane]); }
+  uint32_t* counter = a.counters + (int64_t)strip * kCounterStride;
+  if (q == 0 && cin) {
+    const double S = ((f_sum[0][lane] + f_sum[1][lane]) + f_sum[2][lane]) + f_sum[3][lane];
+    const int64_t o = (int64_t)slab * a.cols + c;
+    __hip_atomic_store(a.psum + o, S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (MINMAX) {
+      __hip_atomic_store(a.pmin + o, fminf(fminf(f_min[0][lane], f_min[1][lane]), fminf(f_min[2][lane], f_min[3][lane])),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.pmax + o, fmaxf(fmaxf(f_max[0][lane], f_max[1][lane]), fmaxf(f_max[2][lane], f_max[3][lane])),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
+  __syncthreads();  // the partial stores have completed
+  if (t == 0)
+    s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nsl - 1);
+  __syncthreads();
+  if (!s_last || q != 0) return;
+  double S = 0.0;
+  lo = __builtin_huge_valf(); hi = -__builtin_huge_valf();
+  if (cin)
+    for (int k = 0; k < nsl; ++k) {
+      const int64_t o = (int64_t)k * a.cols + c;
+      S += __hip_atomic_load(a.psum + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (MINMAX) {
+        lo = fminf(lo, __hip_atomic_load(a.pmin + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        hi = fmaxf(hi, __hip_atomic_load(a.pmax + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      }
+    }
   strip_finalize<MINMAX>(a, 0, strip, 0, lane, c, cin, a.rows, S, lo, hi);
+  if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1037,15 +1064,19 @@ template <bool MINMAX>
 static void launch_stats_given(const SplitQuantPlan& p, const SqLayout& L) {
   ColArgs a{};
   a.rows = p.rows; a.cols = p.cols;
-  a.slots = L.slots; a.n_slots = L.n_slots;
+  a.slots = L.slots; a.n_slots = L.n_slots; a.counters = L.counters;
+  a.psum = L.psum; a.pmin = L.pmin; a.pmax = L.pmax;
   a.mean = p.mean; a.ramax_part = L.ramax; a.mamax_part = L.mamax;
   a.n_strips = (int)n_strips(p.cols);
   a.mode = 1;
   a.h16 = p.h16 ? 1 : 0;
   a.E = 1;
   a.g_sum = p.st_sum; a.g_min = p.st_min; a.g_max = p.st_max; a.g_parts = p.st_parts;
-  hipLaunchKernelGGL((k_colstats_given<MINMAX>), dim3((unsigned)n_strips(p.cols)), dim3(64 * kGivenWaves), 0, p.stream,
-                     a);
+  // groups of about kGivenParts parts, at most the workspace's slabs
+  const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(ceil_div(p.st_parts, kGivenParts), L.nslab));
+  a.g_per = std::max<int64_t>(1, ceil_div(p.st_parts, groups));
+  hipLaunchKernelGGL((k_colstats_given<MINMAX>), dim3((unsigned)n_strips(p.cols), (unsigned)groups), dim3(kThreads), 0,
+                     p.stream, a);
 }
 
 template <typename T, bool MINMAX>
