@@ -374,10 +374,12 @@ struct GemmTile {
   // MXFP4 K-step with every fragment of the step read from LDS before the first MFMA: a wave that
   // is alone on its SIMD (the warp-specialized kernel) then waits for LDS once per step instead of
   // once per 64-element substep.
+  // MSO: byte offset of the mean's scale bytes from its codes in smu
+  template <int MSO = kMuCodes>
   __device__ __forceinline__ void compute_mx_preload(const uint8_t* s, const uint8_t* smu, int kstep) {
     static_assert(FMT == AVERIS_MXFP4, "MXFP4 only");
     uint32_t msc = 0;
-    if constexpr (MU) msc = *reinterpret_cast<const uint32_t*>(smu + kMuCodes + kstep * C::SB + mu_soff);
+    if constexpr (MU) msc = *reinterpret_cast<const uint32_t*>(smu + MSO + kstep * C::SB + mu_soff);
     uint32_t sa[TM], sb[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -1119,6 +1121,160 @@ __global__ __launch_bounds__(64 * (4 + L), 1) void k_gemm_ws_dw(GemmArgs g, cons
   }
 }
 
+// Warp-specialized grouped forward / input gradient (MXFP4, 128 x 128 tiles): logical tile lin
+// enumerates, group after group, the ceil(l_e / 128) x tiles_n tiles of every group (expert);
+// every tile has the same K, so a workgroup's K-steps form one stream as in k_gemm_ws.  Each
+// group's first row, first 32-row-padded row and first logical tile sit in an LDS table built
+// once per workgroup, so a tile switch reads no global memory.  MU: the mean row differs per
+// group, so with every K-step the loaders also copy that step's 128 mean code bytes and 8 scale
+// bytes of the tile's group into the stage (both loaders copy the same bytes), and the
+// multiplying waves read them from there.
+constexpr int kWsgMaxGroups = 256;
+
+struct GTile { int e; int64_t m0, n0; };
+
+template <class C>
+__device__ __forceinline__ GTile wsg_tile(const GemmArgs& gin, int lin, const int* s_off, const int* s_p32,
+                                          const int* s_t0, GemmArgs& g) {
+  int lo = 0, hi = gin.E;  // the last group whose first tile is <= lin (it is not empty)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_t0[mid] <= lin) lo = mid; else hi = mid;
+  }
+  GTile t;
+  t.e = uniform32(lo);
+  const int64_t off = uniform32(s_off[t.e]), len = uniform32(s_off[t.e + 1]) - off, p32 = uniform32(s_p32[t.e]);
+  const int tms = (int)ceil_div(len, (int64_t)C::BM);
+  int tm, tn;
+  tile_coords(lin - uniform32(s_t0[t.e]), tms, gin.tiles_n, gin.group_m < tms ? gin.group_m : tms, tm, tn);
+  const int64_t gsa = (gin.K / C::BKE) * C::PIECE;  // tiled scale bytes per 32-row group
+  g = gin;
+  g.M = len;
+  g.a_codes += p32 * gin.lda_b;
+  g.a_scales += (p32 / 32) * gsa;
+  g.b_codes += (int64_t)t.e * gin.N * gin.ldb_b;
+  g.b_scales += ((int64_t)t.e * gin.N / 32) * gsa;
+  g.c = reinterpret_cast<uint8_t*>(gin.c) + off * gin.ldc * (gin.c_bf16 ? 2 : 4);
+  t.m0 = (int64_t)tm * C::BM;
+  t.n0 = (int64_t)tn * C::BN;
+  return t;
+}
+
+template <int FMT, bool MU, int S, int L>
+__global__ __launch_bounds__(64 * (4 + L), 1) void k_gemm_ws_g(GemmArgs g) {
+  constexpr int WM = 2, WN = 2, TM = 2, TN = 2;
+  using T = GemmTile<FMT, WM, WN, TM, TN, 2, 0, MU>;
+  using C = typename T::C;
+  constexpr int MU_OFF = (C::STAGE + 255) / 256 * 256;  // the K-step's mean codes, then at +256 its scales
+  constexpr int SSZ = (MU_OFF + (MU ? 512 : 0) + 1023) / 1024 * 1024;
+  constexpr int SH = C::NW / L;
+  constexpr int LPW = C::LPS * SH + (MU ? 2 : 0);  // loads per loader wave per K-step
+  static_assert(C::NW % L == 0 && LPW * (S - 2) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[S * SSZ];
+  __shared__ float s_bias[MU ? WN * TN * 32 : 1];
+  __shared__ int s_off[kWsgMaxGroups + 1], s_p32[kWsgMaxGroups], s_t0[kWsgMaxGroups + 1];
+
+  int first, stride, end;
+  xcd_tiles((int)blockIdx.x, (int)gridDim.x, g.n_work, first, stride, end);
+  if (first >= end) return;
+  const int nsteps = (int)(g.K / C::BKE);
+  const int ntw = (end - first + stride - 1) / stride;
+  const int total = ntw * nsteps;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+
+  // group table (wave 0, 64-group prefix scans), before any operand load is in flight
+  if (wave == 0) {
+    int bp = 0, bt = 0;
+    for (int e0 = 0; e0 < g.E; e0 += 64) {
+      const int e = e0 + lane;
+      const int64_t o = e < g.E ? g.offsets[e] : 0;
+      const int len = e < g.E ? (int)(g.offsets[e + 1] - o) : 0;
+      const int p = (int)round_up(len, 32), tl = (int)ceil_div(len, (int64_t)C::BM) * g.tiles_n;
+      int sp = p, st = tl;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int xp = __shfl_up(sp, d, 64), xt = __shfl_up(st, d, 64);
+        if (lane >= d) { sp += xp; st += xt; }
+      }
+      if (e < g.E) { s_off[e] = (int)o; s_p32[e] = bp + sp - p; s_t0[e] = bt + st - tl; }
+      bp += __shfl(sp, 63, 64);
+      bt += __shfl(st, 63, 64);
+    }
+    if (lane == 0) { s_off[g.E] = (int)g.offsets[g.E]; s_t0[g.E] = bt; }
+  }
+  __syncthreads();
+
+  if (wave >= C::NW) {
+    // ---- loader wave l ----
+    const int l = wave - C::NW;
+    T lt[SH];
+    int bound = -1;
+    __amdgpu_buffer_rsrc_t rmc = make_rsrc(g.mu_codes, 0), rms = make_rsrc(g.mu_scales, 0);
+    int ms_off = 0x7FFFFFF0;
+    auto issue = [&](int q) __attribute__((always_inline)) {  // global step q into stage q % S
+      const int qq = q < total ? q : total - 1;  // past the end: re-load the last step (unread)
+      const int ti = qq / nsteps, st = qq - ti * nsteps;
+      if (ti != bound) {
+        bound = ti;
+        GemmArgs v;
+        const GTile gt = wsg_tile<C>(g, first + ti * stride, s_off, s_p32, s_t0, v);
+#pragma unroll
+        for (int i = 0; i < SH; ++i) lt[i].bind(v, gt.m0, gt.n0, l + i * L);
+        if constexpr (MU) {
+          rmc = make_rsrc(g.mu_codes + (int64_t)gt.e * (g.K / 2), g.K / 2);
+          rms = make_rsrc(g.mu_scales, (int64_t)round_up(g.E, 32) * (g.K / C::G));
+          ms_off = lane < 2 ? (int)(((int64_t)(gt.e >> 5) * (g.K / C::BKE)) * C::PIECE + (gt.e & 31) * C::SB) + lane * 4
+                            : 0x7FFFFFF0;
+        }
+      }
+      uint8_t* stg = ring + (q % S) * SSZ;
+#pragma unroll
+      for (int i = 0; i < SH; ++i) lt[i].issue(st * C::BKB, st * C::PIECE, stg);
+      if constexpr (MU) {
+        dma4<0>(rmc, stg + MU_OFF, lane < 32 ? lane * 4 : 0x7FFFFFF0, st * C::BKB);
+        dma4<0>(rms, stg + MU_OFF + 256, ms_off, st * C::PIECE);
+      }
+    };
+    for (int q = 0; q < S - 1; ++q) issue(q);
+    for (int q = 0; q < total; ++q) {
+      wait_vm<LPW * (S - 2)>();
+      __builtin_amdgcn_s_barrier();
+      issue(q + S - 1);
+      if (MU && q % nsteps == nsteps - 1) __builtin_amdgcn_s_barrier();  // the epilogue barrier
+    }
+    wait_vm<0>();  // the trailing re-loads land before the workgroup ends
+    return;
+  }
+
+  // ---- multiplying waves ----
+  T t;
+  t.bind(g, 0, 0);  // lane constants (this wave loads nothing)
+  int q = 0;
+  for (int ti = 0; ti < ntw; ++ti) {
+    GemmArgs gu;
+    const GTile gt = wsg_tile<C>(g, first + ti * stride, s_off, s_p32, s_t0, gu);
+    t.clear();
+    for (int st = 0; st < nsteps; ++st, ++q) {
+      __builtin_amdgcn_s_barrier();
+      const uint8_t* stg = ring + (q % S) * SSZ;
+      t.template compute_mx_preload<256>(stg, stg + MU_OFF, 0);
+    }
+    if constexpr (MU) {
+      if ((threadIdx.x & 31) == 0) {
+        float* sb = s_bias + (t.wn * TN + t.wm) * 32 + 4 * ((threadIdx.x >> 5) & 1);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sb[8 * qq + r] = t.acc_mu[4 * qq + r];
+      }
+      lds_barrier();
+    }
+    epilogue_regs<FMT, TM, TN, MU, false>(gu, t.acc, gt.m0 + t.wm * TM * 32, gt.n0 + t.wn * TN * 32, 0, lane,
+                                          s_bias, s_bias, s_bias + t.wn * TN * 32);
+  }
+}
+
 // Split-K reduce: C = (accumulate ? C : 0) + (sum_s P[s] in split order + bias[col]
 // + r1 * u[row] * v[col]), four columns per thread (N % 8 == 0); fp32 or bf16 output; u and v
 // dequantized from the quantized means in place.
@@ -1230,7 +1386,7 @@ static int g_count(int fmt) { return fmt == AVERIS_MXFP4 ? 32 : 16; }
 //   KCFG_LONG96 the long-K kernel on 128 x 96 tiles (4 x 1 waves of 32 x 96), for dense
 //               single-split long-K launches whose 128 x 128 tiles would leave CUs idle in
 //               their last round (the NVFP4 1024 x 3072 weight gradient: 192 tiles -> 256).
-constexpr int KCFG_LONG = 0, KCFG_SHORT = 1, KCFG_WS = 2, KCFG_LONG96 = 3, KCFG_WSW = 4, KCFG_WSDW = 5;
+constexpr int KCFG_LONG = 0, KCFG_SHORT = 1, KCFG_WS = 2, KCFG_LONG96 = 3, KCFG_WSW = 4, KCFG_WSDW = 5, KCFG_WSG = 6;
 constexpr int kWsStages = 4, kWsLoaders = 2;  // warp-specialized kernel: ring depth, loader waves
 constexpr bool kWsLongK = true;               // warp-specialized kernel for long K too
 constexpr bool kWsWide = true;                // 256 x 128 warp-specialized tiles for short K
@@ -1283,6 +1439,12 @@ template <int F>
 static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipStream_t s, void* ws,
                        const int64_t* h_offsets, bool stats = false) {
   if constexpr (F == AVERIS_MXFP4) {
+    if (cfg == KCFG_WSG) {  // grouped forward / input gradient
+      constexpr int S = kWsStages, L = kWsLoaders;
+      if (g.mu_codes) hipLaunchKernelGGL((k_gemm_ws_g<F, true, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+      else hipLaunchKernelGGL((k_gemm_ws_g<F, false, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+      return;
+    }
     if (cfg == KCFG_WSDW) {  // grouped weight gradient
       constexpr int S = kWsStages, L = kWsLoaders;
       const int64_t mpad = round_up(g.M, 128), npad = round_up(g.N, 128);
@@ -1388,18 +1550,23 @@ hipError_t gemm_launch(const GemmPlan& p) {
   g.M = M; g.N = N; g.K = K;
   g.offsets = p.d_offsets; g.E = (int)E; g.grouped = p.grouped;
   // mean term inside the GEMM: MXFP4 while the mean row fits the tile's LDS copy (see below)
-  const bool mu_in = p.mu && fmt == AVERIS_MXFP4 && K <= kMuMaxK;
+  const bool mu_row_fits = p.mu && fmt == AVERIS_MXFP4 && K <= kMuMaxK;
   int cfg = p.grouped == 2 ? KCFG_LONG : pick_cfg(K);  // grouped dW: long, varying K
   // the warp-specialized kernel: MXFP4 dense launches with K > 0 split into equal K chunks (every
   // (tile, split) unit then has the same nonzero number of K-steps), no accumulation and no bias
   // vector
-  const bool ws_ok = fmt == AVERIS_MXFP4 && !p.grouped && !p.accumulate && (!p.mu || mu_in) && K > 0 &&
+  const bool ws_ok = fmt == AVERIS_MXFP4 && !p.grouped && !p.accumulate && (!p.mu || mu_row_fits) && K > 0 &&
                      ceil_div(K, (int64_t)kBKE) % p.splits == 0;
   if (cfg == KCFG_WS && !ws_ok) cfg = KCFG_SHORT;
   // grouped weight gradient, MXFP4: the warp-specialized form with per-group K
   if (p.grouped == 2 && fmt == AVERIS_MXFP4 && !p.accumulate && !p.mu && K > 0 && K < (int64_t(1) << 30) &&
       E <= kDwMaxGroups)
     cfg = KCFG_WSDW;  // (group lengths in the LDS table are int)
+  // grouped forward / input gradient, MXFP4: the warp-specialized form with the group's mean
+  // K-step in every stage (group offsets in the LDS table are int)
+  if (p.grouped == 1 && fmt == AVERIS_MXFP4 && !p.accumulate && K > 0 && E <= kWsgMaxGroups &&
+      p.h_offsets[E] < (int64_t(1) << 31))
+    cfg = KCFG_WSG;
   if (kWsLongK && cfg == KCFG_LONG && ws_ok) cfg = KCFG_WS;
   if (kWsWide && cfg == KCFG_WS && K < 4096 && !p.mu_u &&
       ceil_div(M, (int64_t)256) * ceil_div(N, (int64_t)128) * p.splits >= cu_count())
@@ -1411,6 +1578,8 @@ hipError_t gemm_launch(const GemmPlan& p) {
     const int64_t t128 = ceil_div(M, (int64_t)128) * ceil_div(N, (int64_t)128), t96 = ceil_div(M, (int64_t)128) * (N / 96);
     if (fill(t96) > fill(t128) + 0.05) cfg = KCFG_LONG96;
   }
+  // (the grouped warp-specialized kernel carries each K-step of the mean in its stages: any K)
+  const bool mu_in = mu_row_fits || (p.mu && cfg == KCFG_WSG);
   const TileCfg tc = tile_of(cfg);
   g.tiles_m = (int)ceil_div(M, tc.bm); g.tiles_n = (int)ceil_div(N, tc.bn);
   if (p.grouped == 1)
