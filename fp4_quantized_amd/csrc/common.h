@@ -189,6 +189,9 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int
 }
 // Wait until at most N vector-memory ops of this wave are outstanding and all its LDS ops are
 // done (gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+// Cache policy bits of buffer stores: non-temporal (streamed past the caches).
+constexpr int kNonTemporal = 2;
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");

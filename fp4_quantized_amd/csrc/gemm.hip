@@ -444,10 +444,12 @@ __device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt((15) |
 
 // Epilogue of one wave, straight from the accumulators: acc[i][j][4q + r] holds
 // C[row i*32 + lane%32][col j*32 + 8q + 4h + r], h = lane / 32.
-//   fp32 output (and split-K partials): a lane's 4 consecutive columns are one 16-byte store.
+//   fp32 output (and split-K partials): a lane's 4 consecutive columns are 16 bytes; a transpose
+//   within lane quads makes each store whole 128-byte row segments, written non-temporally.
 //   bf16 output: v_permlane32_swap exchanges quad q+1 of the low half with quad q of the high
 //   half, after which lane (fr, h) holds the 8 consecutive columns j*32 + 16p + 8h of its row
-//   (p = q / 2): one 16-byte store of 8 bf16.
+//   (p = q / 2), 16 bytes of bf16; with two column blocks (TN = 2) a transpose within lane quads
+//   makes each store whole 128-byte row segments, written non-temporally.
 // Per-column terms (bias, v) and per-row terms (u) are loaded once per tile, in one batch,
 // before the first store; u (times r1) and v come from the tile's LDS copy (su: this wave's rows,
 // sv: its columns).
@@ -494,9 +496,48 @@ __device__ __forceinline__ float half_reduce_scatter16(float (&v)[16], int lane,
   return op(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
 
+// 4 x 4 transpose of 16-byte chunks within each quad of lanes: chunk s of lane 4 q + k moves to
+// chunk k of lane 4 q + s.  Two exchange rounds (lane bit 0 with chunk bit 0, then bit 1 with
+// bit 1); in each a lane keeps two chunks and swaps the other two with its partner through DPP
+// quad permutations.
+__device__ __forceinline__ void quad_transpose(v4u (&c)[4], int lane) {
+  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+#pragma unroll
+  for (int m = 0; m < 4; m += 2)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t a = c[m][d], b = c[m + 1][d];
+      asm("" : "+v"(a), "+v"(b));  // keep the lane choice a register select
+      const uint32_t send = b0 ? a : b;
+      const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+      c[m][d] = b0 ? recv : a;
+      c[m + 1][d] = b0 ? b : recv;
+    }
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t a = c[m][d], b = c[m + 2][d];
+      asm("" : "+v"(a), "+v"(b));
+      const uint32_t send = b1 ? a : b;
+      const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0x4E, 0xF, 0xF, false);  // lane ^ 2
+      c[m][d] = b1 ? recv : a;
+      c[m + 2][d] = b1 ? b : recv;
+    }
+}
+
 // STATS: column sums of the stored output over each wave's rows (fp32 partials [part][N],
 // part = row / (32 TM)).
-template <int FMT, int TM, int TN, bool MU, bool ALL = true, bool STATS = false>
+// 16-byte buffer store, non-temporal or with the default policy.
+__device__ __forceinline__ void store16(v4u v, __amdgpu_buffer_rsrc_t r, int off, bool nt) {
+  if (nt) __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kNonTemporal);
+  else __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
+// ST: 2 = whole-line stores, non-temporal for outputs (split-K partials, re-read at once by the
+// reduction, with the default policy); 1 = whole-line stores, default policy; 0 = each lane's
+// 16-byte pieces as they come.
+template <int FMT, int TM, int TN, bool MU, bool ALL = true, bool STATS = false, int ST = 2>
 __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&acc)[TM][TN], int64_t rbase,
                                               int64_t cbase, int split, int lane, const float* su, const float* sv,
                                               const float* sbias) {
@@ -557,6 +598,7 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
     const int64_t row = rbase + i * 32 + fr;
     const bool row_ok = row < g.M;
     const int roff = (i * 32 + fr) * (int)(ldo * esz);
+    v4u ob[4];  // bf16, TN == 2: this row's four 16-byte chunks (j, p) at 2 j + p
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       float x[16];
@@ -592,7 +634,8 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
           const int64_t col = cbase + j * 32 + 16 * p + 8 * h;
           const v4u o = {pack_bf16x2(x[8 * p], x[8 * p + 1]), pack_bf16x2(x[8 * p + 2], x[8 * p + 3]),
                          pack_bf16x2(x[8 * p + 4], x[8 * p + 5]), pack_bf16x2(x[8 * p + 6], x[8 * p + 7])};
-          __builtin_amdgcn_raw_buffer_store_b128(o, ro, col < g.N ? roff + (int)col * 2 : 0x7FFFFFF0, 0, 0);
+          if constexpr (TN == 2 && ST > 0) ob[2 * j + p] = o;  // stored below, after the quad transpose
+          else __builtin_amdgcn_raw_buffer_store_b128(o, ro, col < g.N ? roff + (int)col * 2 : 0x7FFFFFF0, 0, 0);
           if constexpr (STATS) {  // the values as stored
 #pragma unroll
             for (int r = 0; r < 8; ++r)
@@ -600,12 +643,29 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
           }
         }
       } else if (!acc_in) {
+        // fp32 (outputs and split-K partials): lane (fr, h) holds 4 chunks of 4 columns
+        // j*32 + 8q + 4h of row fr; after the quad transpose store s writes row 4 (fr / 4) + s and
+        // the eight lanes of a quad pair cover the block's 32 columns, one whole 128-byte line
+        // (non-temporal, as for bf16)
+        v4u of[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t col = cbase + j * 32 + 8 * q + 4 * h;
-          const v4u o = {__float_as_uint(x[4 * q]), __float_as_uint(x[4 * q + 1]), __float_as_uint(x[4 * q + 2]),
-                         __float_as_uint(x[4 * q + 3])};
-          __builtin_amdgcn_raw_buffer_store_b128(o, ro, col < g.N ? roff + (int)col * 4 : 0x7FFFFFF0, 0, 0);
+        for (int q = 0; q < 4; ++q)
+          of[q] = v4u{__float_as_uint(x[4 * q]), __float_as_uint(x[4 * q + 1]), __float_as_uint(x[4 * q + 2]),
+                      __float_as_uint(x[4 * q + 3])};
+        if constexpr (ST > 0) {
+          quad_transpose(of, lane);
+          const int64_t col = cbase + j * 32 + 8 * (fr & 3) + 4 * h;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const int rs = (i * 32 + (fr & ~3) + s) * (int)(ldo * esz);
+            store16(of[s], ro, col < g.N ? rs + (int)col * 4 : 0x7FFFFFF0, ST == 2 && g.splits == 1);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t col = cbase + j * 32 + 8 * q + 4 * h;
+            store16(of[q], ro, col < g.N ? roff + (int)col * 4 : 0x7FFFFFF0, false);
+          }
         }
       } else {  // accumulate into fp32 C (no STATS)
         if (!row_ok) continue;
@@ -624,6 +684,25 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
         for (int e = 0; e < 16; ++e) {
           const float v = row_ok ? x[e] : 0.0f;
           csum[j][e] = i == 0 ? v : __fadd_rn(csum[j][e], v);
+        }
+      }
+    }
+    if constexpr (TN == 2 && ST > 0) {
+      // bf16 with two column blocks: lane (fr, h) holds 64 bytes of row fr in four chunks; after
+      // the transpose within its lane quad, store s writes row 4 (fr / 4) + s and the eight lanes
+      // of a quad pair (both halves) cover that row's 64 columns, one whole 128-byte line.  The
+      // stores are non-temporal: the output is not re-read here, and whole lines streamed past
+      // the L2 leave the operands that the next tiles re-read resident (partial-line
+      // non-temporal stores are much slower).
+      if (bf) {
+        quad_transpose(ob, lane);
+        const int k = fr & 3;
+        const int64_t col = cbase + 32 * (k >> 1) + 16 * (k & 1) + 8 * h;
+        const int coff = col < g.N ? (int)col * 2 : -1;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int rs = (i * 32 + (fr & ~3) + s) * (int)(ldo * esz);
+          store16(ob[s], ro, coff >= 0 ? rs + coff : 0x7FFFFFF0, ST == 2);
         }
       }
     }
@@ -779,7 +858,9 @@ __global__ __launch_bounds__(64 * WM * WN, (STAGES == 2 && TM * TN <= 4) ? 2 : 1
     }
     if (hr && (int)threadIdx.x < C::BM + C::BN) s_uv[threadIdx.x] = uv;
     if (MU || hr) lds_barrier();
-    epilogue_regs<FMT, TM, TN, MU, true, STATS>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, split, threadIdx.x & 63,
+    // (plain per-lane stores: in these kernels, whose multiplying waves also issue the operand
+    // loads, whole-line non-temporal stores measured 1-2 % slower)
+    epilogue_regs<FMT, TM, TN, MU, true, STATS, 0>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, split, threadIdx.x & 63,
                                    s_uv + t.wm * TM * 32, s_uv + C::BM + t.wn * TN * 32, s_bias + t.wn * TN * 32);
     t.clear();
   }
