@@ -192,6 +192,12 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, int
 // Cache policy bits of buffer stores: non-temporal (streamed past the caches).
 constexpr int kNonTemporal = 2;
 
+// 16-byte non-temporal global load.
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
