@@ -30,7 +30,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libaveris.s
 
 EXPORTS = [
     "averis_abi_version", "averis_status_string", "averis_source_digest",
-    "averis_split_quant_workspace_size", "averis_split_quant", "averis_split_quant_sr",
+    "averis_split_quant_workspace_size", "averis_split_quant", "averis_split_quant_sr", "averis_split_quant_batch",
     "averis_split_quant_noalloc_max_bytes", "averis_split_quant_noalloc",
     "averis_linear_workspace_size", "averis_linear_fwd", "averis_linear_bwd_dx",
     "averis_colstats_capacity", "averis_linear_fwd_stats", "averis_linear_bwd_dx_stats", "averis_split_quant_stats",
@@ -53,6 +53,24 @@ class CQTensor(ctypes.Structure):
         ("fmt", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
     ]
+
+
+class CSplitQuantItem(ctypes.Structure):
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("ldx", ctypes.c_int64),
+        ("mean", ctypes.c_void_p),
+        ("q_row", ctypes.POINTER(CQTensor)),
+        ("q_col", ctypes.POINTER(CQTensor)),
+        ("q_mean", ctypes.POINTER(CQTensor)),
+        ("ws", ctypes.c_void_p),
+        ("ws_bytes", ctypes.c_size_t),
+    ]
+
+
+BATCH_MAX = 8
 
 
 class CColStats(ctypes.Structure):
@@ -102,6 +120,7 @@ def lib():
             "averis_split_quant_workspace_size": (SZ, [I64, I64, I32, U32]),
             "averis_split_quant": (I32, [P, I32, I64, I64, I64, I32, U32, P, Q, Q, Q, P, SZ, P]),
             "averis_split_quant_sr": (I32, [P, I32, I64, I64, I64, I32, U32, ctypes.c_uint64, P, Q, Q, Q, P, SZ, P]),
+            "averis_split_quant_batch": (I32, [I32, ctypes.POINTER(CSplitQuantItem), I32, I32, U32, P]),
             "averis_split_quant_noalloc_max_bytes": (SZ, []),
             "averis_split_quant_noalloc": (I32, [P, I32, I64, I64, I64, I32, U32, P, Q, Q, Q, P]),
             "averis_linear_workspace_size": (SZ, [I64, I64, I64, I32]),
@@ -245,6 +264,35 @@ def split_quant(x: torch.Tensor, fmt: int, split: bool = True, hadamard: bool = 
     if check_finite:
         out = dict(out, status=ws[:4].view(torch.int32))
     return out
+
+
+def split_quant_batch(xs, fmt: int, split: bool = True, hadamard: bool = False, outs=None, wss=None,
+                      row: bool = True, col: bool = True, stream=None):
+    """split_quant of up to BATCH_MAX independent tensors xs (one dtype) in one statistics and one
+    quantizing launch (averis_split_quant_batch).  Returns one split_quant-style dict per tensor;
+    `outs` / `wss`: preallocated outputs and workspaces, one per tensor."""
+    n = len(xs)
+    assert 1 <= n <= BATCH_MAX
+    dev = xs[0].device
+    flags = (SPLIT if split else 0) | (HADAMARD16 if hadamard else 0)
+    if outs is None:
+        outs = [split_quant_outputs(x.shape[0], x.shape[1], fmt, split, hadamard, row, col, dev) for x in xs]
+    if wss is None:
+        wss = [split_quant_workspace(x.shape[0], x.shape[1], fmt, split, hadamard, dev) for x in xs]
+    items = (CSplitQuantItem * n)()
+    keep = []  # the CQTensor structs the items point to
+    for i, (x, o, ws) in enumerate(zip(xs, outs, wss)):
+        assert x.dim() == 2 and x.is_cuda and x.dtype == xs[0].dtype
+        rows, cols = x.shape
+        assert rows == 0 or x.stride(1) == 1, "x must be row-major"
+        qs = [o[k].c() if o[k] is not None else None for k in ("row", "col", "mean_q")]
+        keep.append(qs)
+        ptr = [ctypes.pointer(q) if q is not None else None for q in qs]
+        items[i] = CSplitQuantItem(x.data_ptr() if rows else None, rows, cols, x.stride(0) if rows > 0 else cols,
+                                   o["mean"].data_ptr() if o["mean"] is not None else None, ptr[0], ptr[1], ptr[2],
+                                   ws.data_ptr(), ws.numel())
+    _check(lib().averis_split_quant_batch(n, items, _dtype_code(xs[0]), fmt, flags, _stream(stream)))
+    return outs
 
 
 def split_quant_noalloc(x: torch.Tensor, fmt: int, split: bool = True, hadamard: bool = False, out=None,

@@ -87,11 +87,12 @@ size_t averis_split_quant_workspace_size(int64_t rows, int64_t cols, int32_t fmt
   return split_quant_ws_bytes(rows, cols);
 }
 
-static int32_t split_quant_common(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ldx, int32_t fmt,
-                                  uint32_t flags, float* mean, const averis_qtensor* q_row,
-                                  const averis_qtensor* q_col, const averis_qtensor* q_mean, void* ws,
-                                  size_t ws_bytes, void* stream, bool sr, uint64_t seed,
-                                  const averis_colstats* stats = nullptr) {
+// Validates one split + quantization request and fills its plan (nothing is launched).
+static int32_t split_quant_plan(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ldx, int32_t fmt,
+                                uint32_t flags, float* mean, const averis_qtensor* q_row,
+                                const averis_qtensor* q_col, const averis_qtensor* q_mean, void* ws,
+                                size_t ws_bytes, void* stream, bool sr, uint64_t seed,
+                                const averis_colstats* stats, SplitQuantPlan& p) {
   if (!dtype_ok(xdt)) return AVERIS_E_DTYPE;
   if (!fmt_ok(fmt)) return AVERIS_E_FORMAT;
   if (flags & ~(AVERIS_SPLIT | AVERIS_HADAMARD16 | AVERIS_MEAN_GIVEN | AVERIS_CHECK_FINITE)) return AVERIS_E_FLAGS;
@@ -124,8 +125,8 @@ static int32_t split_quant_common(const void* x, int32_t xdt, int64_t rows, int6
   if (!ws || ws_bytes < split_quant_ws_bytes(rows, cols)) return AVERIS_E_WORKSPACE;
   if (!aligned16(ws)) return AVERIS_E_ALIGN;
 
-  SplitQuantPlan p{x, xdt, rows, cols, ldx, fmt, split, h16, given, mean, q_row, q_col, q_mean, ws,
-                   reinterpret_cast<hipStream_t>(stream)};
+  p = SplitQuantPlan{x, xdt, rows, cols, ldx, fmt, split, h16, given, mean, q_row, q_col, q_mean, ws,
+                     reinterpret_cast<hipStream_t>(stream)};
   p.sr = sr;
   p.seed = seed;
   p.check = (flags & AVERIS_CHECK_FINITE) != 0;
@@ -133,7 +134,41 @@ static int32_t split_quant_common(const void* x, int32_t xdt, int64_t rows, int6
     p.st_sum = stats->sum; p.st_parts = stats->parts;
     if (fmt == AVERIS_NVFP4 && !h16) { p.st_min = stats->min; p.st_max = stats->max; }
   }
+  return AVERIS_OK;
+}
+
+static int32_t split_quant_common(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ldx, int32_t fmt,
+                                  uint32_t flags, float* mean, const averis_qtensor* q_row,
+                                  const averis_qtensor* q_col, const averis_qtensor* q_mean, void* ws,
+                                  size_t ws_bytes, void* stream, bool sr, uint64_t seed,
+                                  const averis_colstats* stats = nullptr) {
+  SplitQuantPlan p{};
+  const int32_t st = split_quant_plan(x, xdt, rows, cols, ldx, fmt, flags, mean, q_row, q_col, q_mean, ws, ws_bytes,
+                                      stream, sr, seed, stats, p);
+  if (st != AVERIS_OK) return st;
   return split_quant_launch(p) == hipSuccess ? AVERIS_OK : AVERIS_E_HIP;
+}
+
+int32_t averis_split_quant_batch(int32_t n, const averis_split_quant_item* items, int32_t xdt, int32_t fmt,
+                                 uint32_t flags, void* stream) {
+  if (n < 1 || n > AVERIS_BATCH_MAX || n > batch_max()) return AVERIS_E_SHAPE;
+  if (!items) return AVERIS_E_NULL;
+  if (flags & AVERIS_CHECK_FINITE) return AVERIS_E_FLAGS;
+  SplitQuantPlan ps[AVERIS_BATCH_MAX];
+  for (int i = 0; i < n; ++i) {
+    const averis_split_quant_item& it = items[i];
+    const int32_t st = split_quant_plan(it.x, xdt, it.rows, it.cols, it.ldx, fmt, flags, it.mean, it.q_row, it.q_col,
+                                        it.q_mean, it.ws, it.ws_bytes, stream, false, 0, nullptr, ps[i]);
+    if (st != AVERIS_OK) return st;
+    // each tensor needs a workspace of its own (counters, partials and amax slots)
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(it.ws), e0 = b0 + split_quant_ws_bytes(it.rows, it.cols);
+    for (int j = 0; j < i; ++j) {
+      const uintptr_t b1 = reinterpret_cast<uintptr_t>(items[j].ws);
+      const uintptr_t e1 = b1 + split_quant_ws_bytes(items[j].rows, items[j].cols);
+      if (b0 < e1 && b1 < e0) return AVERIS_E_WORKSPACE;
+    }
+  }
+  return split_quant_batch_launch(ps, n) == hipSuccess ? AVERIS_OK : AVERIS_E_HIP;
 }
 
 int32_t averis_split_quant(const void* x, int32_t xdt, int64_t rows, int64_t cols, int64_t ldx, int32_t fmt,

@@ -31,6 +31,10 @@ void colparts_launch(const void* c, int cdt, int64_t M, int64_t N, int64_t ldc, 
 size_t split_quant_ws_bytes(int64_t rows, int64_t cols);
 size_t split_quant_grouped_ws_bytes(int64_t rows, int64_t cols, int64_t E);
 hipError_t split_quant_launch(const SplitQuantPlan& p);
+// Batched form: n <= batch_max() dense plans with one input type, format and flags (no
+// stochastic rounding, producer statistics or CHECK_FINITE), each with its own workspace.
+int batch_max();
+hipError_t split_quant_batch_launch(const SplitQuantPlan* ps, int n);
 
 struct GemmPlan {
   const averis_qtensor* a; const averis_qtensor* b;   // C = A B^T, both K-inner

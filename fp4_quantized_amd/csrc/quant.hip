@@ -152,8 +152,9 @@ __device__ __forceinline__ void strip_finalize(const ColArgs& a, int e, int stri
 // PARTS: write the slab's column partials (fp32) to o_sum / o_min / o_max and stop (no
 // counters, no slots, no finalize): the column statistics of an output whose producer could not
 // take them in its epilogue.
+// The workgroup (bx, by) = (column strip, slab) of launch a.
 template <typename T, bool MINMAX, bool PARTS = false>
-__global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
+__device__ __forceinline__ void colstats_body(const ColArgs& a, int bx, int by) {
   constexpr int VEC = Elem<T>::VEC;
   constexpr int LPR = kCsCols / VEC;   // lanes per row
   constexpr int RPB = kThreads / LPR;  // rows per pass of the workgroup
@@ -168,14 +169,14 @@ __global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
   __shared__ int s_last;
 
   const int t = threadIdx.x;
-  if (!PARTS && blockIdx.x == 0 && blockIdx.y == 0)
+  if (!PARTS && bx == 0 && by == 0)
     for (int i = t; i < a.n_slots; i += kThreads) a.slots[i] = 0u;  // maxed by later kernels
 
   // this workgroup's rows [rb, re) and its group's slabs [s0, s0 + nsl)
-  int64_t rb = (int64_t)blockIdx.y * kCsRows, re = a.rows, s0 = 0, glen = a.rows;
+  int64_t rb = (int64_t)by * kCsRows, re = a.rows, s0 = 0, glen = a.rows;
   int e = 0, nsl = (int)cs_slabs(a.rows);
   if (a.offsets) {
-    const GroupPos gp = group_scan(a.offsets, a.E, blockIdx.y, true, [](int64_t len) { return cs_slabs(len); });
+    const GroupPos gp = group_scan(a.offsets, a.E, by, true, [](int64_t len) { return cs_slabs(len); });
     if (gp.e < 0) return;
     e = gp.e;
     rb = gp.off + gp.local * kCsRows;
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
     glen = gp.len;
   }
   if (re > rb + kCsRows) re = rb + kCsRows;
-  const int strip = blockIdx.x;
+  const int strip = bx;
   const int64_t c0 = (int64_t)strip * kCsCols;
   const int lc = t % LPR, rr = t / LPR;
   const int64_t col = c0 + lc * VEC;
@@ -238,13 +239,13 @@ __global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
       if (MINMAX) { lo = fminf(lo, s_min[q][t]); hi = fmaxf(hi, s_max[q][t]); }
     }
     if constexpr (PARTS) {
-      const int64_t o = (int64_t)blockIdx.y * a.cols + c0 + t;
+      const int64_t o = (int64_t)by * a.cols + c0 + t;
       a.o_sum[o] = (float)sacc;
       if (MINMAX) { a.o_min[o] = lo; a.o_max[o] = hi; }
       return;
     }
     // agent-scope atomic stores: complete only at the coherence point all XCDs read from
-    const int64_t o = (int64_t)blockIdx.y * a.cols + c0 + t;
+    const int64_t o = (int64_t)by * a.cols + c0 + t;
     __hip_atomic_store(a.psum + o, sacc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (MINMAX) {
       __hip_atomic_store(a.pmin + o, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -321,6 +322,27 @@ __global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
     strip_finalize<MINMAX>(a, e, strip, cw, lane, c, cin, glen, S, lo, hi);
     if (lane == 0 && cw == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next call
   }
+}
+
+
+template <typename T, bool MINMAX, bool PARTS = false>
+__global__ __launch_bounds__(kThreads) void k_colstats(ColArgs a) {
+  colstats_body<T, MINMAX, PARTS>(a, (int)blockIdx.x, (int)blockIdx.y);
+}
+
+// Batched launches: several independent tensors' statistics passes in one grid.  Workgroup b
+// belongs to the tensor i with start[i] <= b < start[i + 1] and is workgroup b - start[i] of that
+// tensor's own (strip, slab) grid, strips first.
+constexpr int kBatchMax = 8;
+struct ColBatch { ColArgs a[kBatchMax]; int start[kBatchMax + 1]; int n; };
+
+template <typename T, bool MINMAX>
+__global__ __launch_bounds__(kThreads) void k_colstats_batch(ColBatch b) {
+  const int blk = (int)blockIdx.x;
+  int i = 0;
+  while (i + 1 < b.n && blk >= b.start[i + 1]) ++i;
+  const int local = blk - b.start[i], ns = b.a[i].n_strips;
+  colstats_body<T, MINMAX>(b.a[i], local % ns, local / ns);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -821,8 +843,9 @@ __device__ __forceinline__ void tile_cols(const QuantArgs& a, int64_t r0, int64_
   }
 }
 
+// Tile `tile` (row tiles first) of launch ain.
 template <typename T, int FMT, bool H16, bool AMAX_ONLY, bool SR = false>
-__global__ __launch_bounds__(kThreads, 4) void k_quant(QuantArgs ain) {
+__device__ __forceinline__ void quant_body(const QuantArgs& ain, const int tile) {
   constexpr int SZ = (int)sizeof(T);
   constexpr int TC = 32 * Elem<T>::VEC;
   constexpr int EPU = 64 / SZ, EPC = 16 / SZ;  // elements per unit, per chunk
@@ -833,7 +856,6 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant(QuantArgs ain) {
   __shared__ float s_red[2][8];
 
   QuantArgs a = ain;  // this workgroup's view (grouped launches retarget it to one group)
-  const int tile = xcd_remap(blockIdx.x, (int)gridDim.x);
   int tr, tc;
   if (ain.offsets) {
     const int tcs = ain.tiles_c, cov = ain.cover_kpad;
@@ -935,6 +957,24 @@ __global__ __launch_bounds__(kThreads, 4) void k_quant(QuantArgs ain) {
   if (AMAX_ONLY) amax_commit(a, amax_row, amax_col, s_red, kThreads / 64);
 }
 
+template <typename T, int FMT, bool H16, bool AMAX_ONLY, bool SR = false>
+__global__ __launch_bounds__(kThreads, 4) void k_quant(QuantArgs ain) {
+  quant_body<T, FMT, H16, AMAX_ONLY, SR>(ain, xcd_remap(blockIdx.x, (int)gridDim.x));
+}
+
+// Batched quantization: tile b (after the XCD remap) belongs to the tensor i with start[i] <= b <
+// start[i + 1] and is tile b - start[i] of it.
+struct QuantBatch { QuantArgs a[kBatchMax]; int start[kBatchMax + 1]; int n; };
+static_assert(sizeof(QuantBatch) <= 4096 && sizeof(ColBatch) <= 4096, "kernel argument size");
+
+template <typename T, int FMT, bool H16, bool AMAX_ONLY>
+__global__ __launch_bounds__(kThreads, 4) void k_quant_batch(QuantBatch b) {
+  const int blk = xcd_remap(blockIdx.x, (int)gridDim.x);
+  int i = 0;
+  while (i + 1 < b.n && blk >= b.start[i + 1]) ++i;
+  quant_body<T, FMT, H16, AMAX_ONLY>(b.a[i], blk - b.start[i]);
+}
+
 __global__ void k_fill_f32(float* p, int n, float v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -984,8 +1024,10 @@ size_t split_quant_grouped_ws_bytes(int64_t rows, int64_t cols, int64_t E) {
   return sq_bytes(ceil_div(rows, kCsRows) + E + 1, cols, E);
 }
 
-template <typename T, int FMT, bool H16>
-static hipError_t launch_quant_t(const SplitQuantPlan& p, const SqLayout& L) {
+// Arguments of the quantizing pass for plan p (before the output pointers: the rotated-amax pass
+// takes the same ones); ntiles = its workgroups.
+template <typename T>
+static QuantArgs quant_args(const SplitQuantPlan& p, const SqLayout& L, int64_t& ntiles) {
   constexpr int TC = 32 * Elem<T>::VEC;
   const bool grouped = p.E > 0;
   QuantArgs a{};
@@ -1001,7 +1043,6 @@ static hipError_t launch_quant_t(const SplitQuantPlan& p, const SqLayout& L) {
   a.rows_out = p.rows;
   a.mean_row = 0; a.mean_rows = grouped ? (int)p.E : 1;
   a.cover_kpad = p.q_col ? 1 : 0;
-  int64_t ntiles;
   if (grouped) {
     a.offsets = p.d_offsets; a.E = (int)p.E;
     int64_t tr = 0;
@@ -1014,21 +1055,17 @@ static hipError_t launch_quant_t(const SplitQuantPlan& p, const SqLayout& L) {
     a.tiles_r = (int)quant_row_tiles<kQRows>(p.rows, a.cover_kpad);
     ntiles = (int64_t)a.tiles_r * a.tiles_c;
   }
-  if (ntiles == 0) {  // no columns or no groups: still define the tensor scales (0)
-    if (FMT == AVERIS_NVFP4 && !grouped) {
-      float* ts[3] = {p.q_row ? p.q_row->tensor_scale : nullptr, p.q_col ? p.q_col->tensor_scale : nullptr,
-                      p.q_mean ? p.q_mean->tensor_scale : nullptr};
-      for (float* t : ts)
-        if (t) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(64), 0, p.stream, t, 1, 0.0f);
-    }
-    return hipGetLastError();
-  }
-  if (FMT == AVERIS_NVFP4 && H16) {
-    QuantArgs m = a;
-    m.want_row_amax = p.q_row != nullptr;
-    m.want_col_amax = p.q_col != nullptr;
-    hipLaunchKernelGGL((k_quant<T, FMT, H16, true>), dim3((unsigned)ntiles), dim3(kThreads), 0, p.stream, m);
-  }
+  return a;
+}
+
+// The rotated-amax pass's view of a (NVFP4 with H16), and the quantizing pass's outputs.
+static QuantArgs amax_view(const QuantArgs& a, const SplitQuantPlan& p) {
+  QuantArgs m = a;
+  m.want_row_amax = p.q_row != nullptr;
+  m.want_col_amax = p.q_col != nullptr;
+  return m;
+}
+static void set_outputs(QuantArgs& a, const SplitQuantPlan& p) {
   if (p.q_row) { a.row_codes = p.q_row->codes; a.row_scales = p.q_row->scales; a.row_ts = p.q_row->tensor_scale; }
   if (p.q_col) { a.col_codes = p.q_col->codes; a.col_scales = p.q_col->scales; a.col_ts = p.q_col->tensor_scale; }
   if (p.split && p.q_mean) {
@@ -1038,10 +1075,28 @@ static hipError_t launch_quant_t(const SplitQuantPlan& p, const SqLayout& L) {
   if (p.sr) {
     a.sr_k0 = (uint32_t)p.seed;
     a.sr_k1 = (uint32_t)(p.seed >> 32);
-    hipLaunchKernelGGL((k_quant<T, FMT, H16, false, true>), dim3((unsigned)ntiles), dim3(kThreads), 0, p.stream, a);
-  } else {
-    hipLaunchKernelGGL((k_quant<T, FMT, H16, false>), dim3((unsigned)ntiles), dim3(kThreads), 0, p.stream, a);
   }
+}
+
+template <typename T, int FMT, bool H16>
+static hipError_t launch_quant_t(const SplitQuantPlan& p, const SqLayout& L) {
+  const bool grouped = p.E > 0;
+  int64_t ntiles = 0;
+  QuantArgs a = quant_args<T>(p, L, ntiles);
+  if (ntiles == 0) {  // no columns or no groups: still define the tensor scales (0)
+    if (FMT == AVERIS_NVFP4 && !grouped) {
+      float* ts[3] = {p.q_row ? p.q_row->tensor_scale : nullptr, p.q_col ? p.q_col->tensor_scale : nullptr,
+                      p.q_mean ? p.q_mean->tensor_scale : nullptr};
+      for (float* t : ts)
+        if (t) hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(64), 0, p.stream, t, 1, 0.0f);
+    }
+    return hipGetLastError();
+  }
+  if (FMT == AVERIS_NVFP4 && H16)
+    hipLaunchKernelGGL((k_quant<T, FMT, H16, true>), dim3((unsigned)ntiles), dim3(kThreads), 0, p.stream, amax_view(a, p));
+  set_outputs(a, p);
+  if (p.sr) hipLaunchKernelGGL((k_quant<T, FMT, H16, false, true>), dim3((unsigned)ntiles), dim3(kThreads), 0, p.stream, a);
+  else hipLaunchKernelGGL((k_quant<T, FMT, H16, false>), dim3((unsigned)ntiles), dim3(kThreads), 0, p.stream, a);
   return hipGetLastError();
 }
 
@@ -1050,8 +1105,7 @@ static hipError_t launch_quant_f(const SplitQuantPlan& p, const SqLayout& L) {
   return p.xdt == AVERIS_BF16 ? launch_quant_t<uint16_t, FMT, H16>(p, L) : launch_quant_t<float, FMT, H16>(p, L);
 }
 
-template <typename T, bool MINMAX>
-static void launch_stats_t(const SplitQuantPlan& p, const SqLayout& L) {
+static ColArgs col_args(const SplitQuantPlan& p, const SqLayout& L) {
   const bool grouped = p.E > 0;
   ColArgs a{};
   a.x = p.x; a.rows = p.rows; a.cols = p.cols; a.ldx = p.ldx;
@@ -1063,8 +1117,13 @@ static void launch_stats_t(const SplitQuantPlan& p, const SqLayout& L) {
   a.h16 = (p.split && p.h16) ? 1 : 0;
   a.offsets = grouped ? p.d_offsets : nullptr;
   a.E = grouped ? (int)p.E : 1;
+  return a;
+}
+
+template <typename T, bool MINMAX>
+static void launch_stats_t(const SplitQuantPlan& p, const SqLayout& L) {
   const dim3 grid((unsigned)n_strips(p.cols), (unsigned)L.nslab);
-  hipLaunchKernelGGL((k_colstats<T, MINMAX>), grid, dim3(kThreads), 0, p.stream, a);
+  hipLaunchKernelGGL((k_colstats<T, MINMAX>), grid, dim3(kThreads), 0, p.stream, col_args(p, L));
 }
 
 template <bool MINMAX>
@@ -1140,6 +1199,69 @@ hipError_t split_quant_launch(const SplitQuantPlan& p) {
   if (e != hipSuccess) return e;
   if (nv) return p.h16 ? launch_quant_f<AVERIS_NVFP4, true>(p, L) : launch_quant_f<AVERIS_NVFP4, false>(p, L);
   return p.h16 ? launch_quant_f<AVERIS_MXFP4, true>(p, L) : launch_quant_f<AVERIS_MXFP4, false>(p, L);
+}
+
+// ------------------------------------------------------------------------------------------
+// Batched split + quantization of independent dense tensors that share the input type, format
+// and flags: one statistics launch over every tensor's (strip, slab) workgroups, then one
+// quantizing launch over every tensor's tiles (NVFP4 with H16: one rotated-amax launch before
+// it).  Each tensor keeps its own workspace (counters, partials, amax slots), so the kernels do
+// per tensor exactly what the single launches do.
+// ------------------------------------------------------------------------------------------
+int batch_max() { return kBatchMax; }
+
+template <typename T, int FMT, bool H16>
+static void launch_batch_t(const SplitQuantPlan* ps, const SqLayout* L, int n) {
+  const SplitQuantPlan& p0 = ps[0];
+  const bool nv = FMT == AVERIS_NVFP4;
+  if (nv || (p0.split && !p0.mean_given)) {
+    ColBatch b{};
+    int total = 0;
+    for (int i = 0; i < n; ++i) {
+      b.a[i] = col_args(ps[i], L[i]);
+      b.start[i] = total;
+      total += (int)(n_strips(ps[i].cols) * L[i].nslab);
+    }
+    b.start[n] = total;
+    b.n = n;
+    hipLaunchKernelGGL((k_colstats_batch<T, nv>), dim3((unsigned)total), dim3(kThreads), 0, p0.stream, b);
+  }
+  QuantBatch q{};
+  int total = 0;
+  for (int i = 0; i < n; ++i) {
+    int64_t nt = 0;
+    q.a[i] = quant_args<T>(ps[i], L[i], nt);
+    q.start[i] = total;
+    total += (int)nt;
+  }
+  q.start[n] = total;
+  q.n = n;
+  if (FMT == AVERIS_NVFP4 && H16) {
+    QuantBatch m = q;
+    for (int i = 0; i < n; ++i) m.a[i] = amax_view(q.a[i], ps[i]);
+    hipLaunchKernelGGL((k_quant_batch<T, FMT, H16, true>), dim3((unsigned)total), dim3(kThreads), 0, p0.stream, m);
+  }
+  for (int i = 0; i < n; ++i) set_outputs(q.a[i], ps[i]);
+  hipLaunchKernelGGL((k_quant_batch<T, FMT, H16, false>), dim3((unsigned)total), dim3(kThreads), 0, p0.stream, q);
+}
+
+template <int FMT, bool H16>
+static void launch_batch_f(const SplitQuantPlan* ps, const SqLayout* L, int n) {
+  if (ps[0].xdt == AVERIS_BF16) launch_batch_t<uint16_t, FMT, H16>(ps, L, n);
+  else launch_batch_t<float, FMT, H16>(ps, L, n);
+}
+
+hipError_t split_quant_batch_launch(const SplitQuantPlan* ps, int n) {
+  if (n <= 0) return hipSuccess;
+  SqLayout L[kBatchMax];
+  for (int i = 0; i < n; ++i) L[i] = sq_layout(ps[i].ws, cs_slabs(ps[i].rows), ps[i].cols, 1);
+  const bool nv = ps[0].fmt == AVERIS_NVFP4, h16 = ps[0].h16;
+  if (nv) {
+    if (h16) launch_batch_f<AVERIS_NVFP4, true>(ps, L, n); else launch_batch_f<AVERIS_NVFP4, false>(ps, L, n);
+  } else {
+    if (h16) launch_batch_f<AVERIS_MXFP4, true>(ps, L, n); else launch_batch_f<AVERIS_MXFP4, false>(ps, L, n);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace av

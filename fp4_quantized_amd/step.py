@@ -62,25 +62,35 @@ class LayerStep:
     """One layer's quantized training step over several linears whose inputs may be shared:
     every distinct input tensor X is split and quantized once (q, k and v read one X; gate and
     up read one X), every output gradient D and weight W once per linear, then each linear's
-    forward, input-gradient and weight-gradient GEMMs.  linears: [(name, x, d, w)]."""
+    forward, input-gradient and weight-gradient GEMMs.  linears: [(name, x, d, w)].
 
-    def __init__(self, linears, fmt, split=True, hadamard=False, out_dtype=torch.bfloat16):
+    batched: tensors that become ready together are split and quantized in one batched launch
+    pair (averis_split_quant_batch): every weight at the start of the step, and the output
+    gradients of the linears that share an input (q/k/v: attention's backward returns them at
+    once; gate/up: the SwiGLU backward)."""
+
+    def __init__(self, linears, fmt, split=True, hadamard=False, out_dtype=torch.bfloat16, batched=True):
         self.fmt, self.split, self.hadamard = fmt, split, hadamard
-        self.quants = []  # (tensor, split, outputs, workspace) in launch order
+        self.quants = []  # (tensor, split, outputs, workspace)
         qx = {}
         self.lin = []
+        w_idx, x_idx, d_idx = [], {}, {}  # indices into quants: weights; per distinct X its own and its D's
         for name, x, d, w in linears:
             l, m = x.shape
             n = d.shape[1]
             dev = x.device
             if id(x) not in qx:
                 out = av.split_quant_outputs(l, m, fmt, split, hadamard, device=dev)
+                x_idx[id(x)] = len(self.quants)
+                d_idx[id(x)] = []
                 self.quants.append((x, split, out, av.split_quant_workspace(l, m, fmt, split, hadamard, dev)))
                 qx[id(x)] = out
             sx = qx[id(x)]
             sd = av.split_quant_outputs(l, n, fmt, split, hadamard, device=dev)
+            d_idx[id(x)].append(len(self.quants))
             self.quants.append((d, split, sd, av.split_quant_workspace(l, n, fmt, split, hadamard, dev)))
             sw = av.split_quant_outputs(m, n, fmt, False, hadamard, device=dev)
+            w_idx.append(len(self.quants))
             self.quants.append((w, False, sw, av.split_quant_workspace(m, n, fmt, False, hadamard, dev)))
             y = torch.empty((l, n), dtype=out_dtype, device=dev)
             dx = torch.empty((l, m), dtype=out_dtype, device=dev)
@@ -89,6 +99,14 @@ class LayerStep:
                                  ws_fwd=av.linear_workspace(sx["row"], sw["col"]),
                                  ws_dx=av.linear_workspace(sd["row"], sw["row"]),
                                  ws_dw=av.linear_bwd_dw_workspace(sx["col"], sd["col"], l)))
+        # launch groups in order: the weights, then per distinct X its split and its D's
+        chunks = lambda ix: [ix[i:i + av.BATCH_MAX] for i in range(0, len(ix), av.BATCH_MAX)]  # noqa: E731
+        if batched:
+            self.groups = chunks(w_idx)
+            for k, i in x_idx.items():
+                self.groups += [[i]] + chunks(d_idx[k])
+        else:
+            self.groups = [[i] for i in range(len(self.quants))]
 
     @property
     def flops(self):
@@ -106,8 +124,14 @@ class LayerStep:
         return tot
 
     def quantize(self, stream=None):
-        for t, sp, out, ws in self.quants:
-            av.split_quant(t, self.fmt, sp, self.hadamard, stream=stream, out=out, ws=ws)
+        for grp in self.groups:
+            qs = [self.quants[i] for i in grp]
+            if len(qs) == 1:
+                t, sp, out, ws = qs[0]
+                av.split_quant(t, self.fmt, sp, self.hadamard, stream=stream, out=out, ws=ws)
+            else:
+                av.split_quant_batch([q[0] for q in qs], self.fmt, qs[0][1], self.hadamard,
+                                     outs=[q[2] for q in qs], wss=[q[3] for q in qs], stream=stream)
 
     def gemms(self, stream=None):
         for c in self.lin:

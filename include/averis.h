@@ -156,6 +156,40 @@ int32_t averis_split_quant(const void *x, int32_t xdt, int64_t rows, int64_t col
                            const averis_qtensor *q_mean, void *ws, size_t ws_bytes, void *stream);
 
 /* -----------------------------------------------------------------------------------------
+ * averis_split_quant_batch -- averis_split_quant of up to AVERIS_BATCH_MAX independent tensors
+ * in one statistics launch and one quantizing launch (two with NVFP4 + HADAMARD16), for tensors
+ * that become ready together: a layer's weights at the start of a step, the q/k/v output
+ * gradients that attention's backward returns at once, the gate/up gradients of the SwiGLU
+ * backward.  Same method as averis_split_quant ([rainbus] 方法步骤详情), applied to each tensor
+ * on its own: every output is bit-identical to that of averis_split_quant with the item's
+ * arguments.
+ *  n       1 .. AVERIS_BATCH_MAX items.
+ *  items   host array; item i holds the x, rows, cols, ldx, mean, q_row, q_col, q_mean, ws and
+ *          ws_bytes arguments of averis_split_quant (same meaning, layout and ownership).  Each
+ *          item needs a workspace of its own (overlapping workspaces: AVERIS_E_WORKSPACE).
+ *  xdt, fmt, flags  shared by every item; flags as averis_split_quant without
+ *          AVERIS_CHECK_FINITE (AVERIS_E_FLAGS).
+ * Every item is validated before anything is enqueued; the first invalid item's status is
+ * returned and nothing is launched.
+ * ----------------------------------------------------------------------------------------- */
+#define AVERIS_BATCH_MAX 8
+typedef struct averis_split_quant_item {
+  const void *x;
+  int64_t rows;
+  int64_t cols;
+  int64_t ldx;
+  float *mean;
+  const averis_qtensor *q_row;
+  const averis_qtensor *q_col;
+  const averis_qtensor *q_mean;
+  void *ws;
+  size_t ws_bytes;
+} averis_split_quant_item;
+
+int32_t averis_split_quant_batch(int32_t n, const averis_split_quant_item *items, int32_t xdt, int32_t fmt,
+                                 uint32_t flags, void *stream);
+
+/* -----------------------------------------------------------------------------------------
  * averis_split_quant_sr -- averis_split_quant with stochastic rounding of every E2M1 code it
  * writes (residual layouts and quantized mean), for callers that round gradient operands
  * stochastically.  The pages round to nearest and do not use this; it is an option.

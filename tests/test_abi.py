@@ -303,3 +303,31 @@ def test_linear_stats_rejects():
         # the plain checks come first
         assert fn(r(a), r(mu), r(q(384, 256)), FAKE, av.BF16, 384, r(colstats(cols=384)), FAKE, 1 << 30,
                   None) == E_SHAPE
+
+
+def batch_items(n, ws_step=1 << 30, bad=None, fmt=av.NVFP4, flags=av.SPLIT):
+    """n valid items on distinct fake workspaces; item `bad` gets cols = 48 (not a multiple of 32)."""
+    items = (av.CSplitQuantItem * n)()
+    keep = []
+    for i in range(n):
+        rows, cols = 256, (48 if i == bad else 128)
+        qs = [q(rows, cols, fmt), q(cols, rows, fmt), q(1, cols, fmt) if flags & av.SPLIT else None]
+        keep.append(qs)
+        ptr = [ctypes.pointer(t) if t is not None else None for t in qs]
+        items[i] = av.CSplitQuantItem(FAKE, rows, cols, cols, FAKE, ptr[0], ptr[1], ptr[2], FAKE + i * ws_step, 1 << 30)
+    return items, keep
+
+
+@pytest.mark.parametrize("case,status", [
+    ("n0", E_SHAPE), ("n9", E_SHAPE), ("null", E_NULL), ("check_finite", E_FLAGS), ("bad_item", E_SHAPE),
+    ("shared_ws", E_WORKSPACE), ("mean_given_without_split", E_FLAGS),
+])
+def test_split_quant_batch_rejects(case, status):
+    # every case fails validation before anything is enqueued (the pointers are never used)
+    L = av.lib()
+    n = 9 if case == "n9" else 3
+    items, keep = batch_items(n, ws_step=(0 if case == "shared_ws" else 1 << 32), bad=(1 if case == "bad_item" else None))
+    flags = {"check_finite": av.SPLIT | av.CHECK_FINITE, "mean_given_without_split": av.MEAN_GIVEN}.get(case, av.SPLIT)
+    arg_n = 0 if case == "n0" else n
+    arg_items = None if case == "null" else items
+    assert L.averis_split_quant_batch(arg_n, arg_items, av.BF16, av.NVFP4, flags, None) == status

@@ -1,0 +1,111 @@
+"""GPU parity of the batched split + quantization (averis_split_quant_batch).
+
+Each batched tensor is quantized on its own, so every output must be bit-identical to a single
+averis_split_quant call on the same tensor (whose parity with the oracle the single-call tests
+establish); one tensor per batch is also checked against the oracle directly.  Shapes mix row
+counts (with an empty tensor and ragged tails), column counts and, in one batch, the seven
+weights of the Qwen3-0.6B-shaped layer.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp4_quantized_amd.averis as av
+from fp4_quantized_amd import workloads
+from oracle import averis_oracle as O
+from tests.gpu_util import assert_q_equal, device, mean_ok, to_oracle
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(300, 384), (0, 96), (1000, 1056), (64, 32), (2048, 512)]
+LAYER_W = [(1024, 2048), (1024, 1024), (1024, 1024), (2048, 1024), (1024, 3072), (1024, 3072), (3072, 1024)]
+
+
+def same(a, b, what):
+    if a is None or b is None:
+        assert a is None and b is None, what
+        return
+    if isinstance(a, torch.Tensor):
+        assert torch.equal(a, b), what
+        return
+    assert torch.equal(a.codes, b.codes), f"{what} codes"
+    assert torch.equal(a.scales, b.scales), f"{what} scales"
+    if a.tensor_scale is not None:
+        assert torch.equal(a.tensor_scale, b.tensor_scale), f"{what} tensor scale"
+
+
+def check_batch(xs, fmt, split, hadamard, tag):
+    print(f"case {tag} n={len(xs)} fmt={fmt} split={split} h16={hadamard}", flush=True)
+    outs = av.split_quant_batch(xs, fmt, split=split, hadamard=hadamard)
+    singles = [av.split_quant(x, fmt, split=split, hadamard=hadamard) for x in xs]
+    torch.cuda.synchronize()
+    for i, (g, r) in enumerate(zip(outs, singles)):
+        for k in ("mean", "row", "col", "mean_q"):
+            same(g[k], r[k], f"{tag} tensor {i} {k}")
+    # the largest tensor against the oracle as well
+    i = max(range(len(xs)), key=lambda j: xs[j].numel())
+    xh = xs[i].float().cpu().numpy()
+    mu = outs[i]["mean"].cpu().numpy() if split else None
+    if split:
+        assert mean_ok(mu, xh), f"{tag}: mean"
+    o = O.split_quant(xh, fmt, split=split, hadamard=hadamard, mean=mu)
+    assert_q_equal(outs[i]["row"], o["row"], f"{tag} oracle row layout")
+    assert_q_equal(outs[i]["col"], o["col"], f"{tag} oracle column layout")
+
+
+@pytest.mark.parametrize("fmt,fname", [(av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")])
+@pytest.mark.parametrize("split", [True, False])
+@pytest.mark.parametrize("hadamard", [False, True])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_batch_matches_single_calls(fmt, fname, split, hadamard, dt):
+    dev = device()
+    xs = [workloads.to_torch(workloads.up_proj_like(70 + i, r, c, 32).x, dt, dev) for i, (r, c) in enumerate(SHAPES)]
+    check_batch(xs, fmt, split, hadamard, f"mixed-{fname}-{dt}")
+
+
+@pytest.mark.parametrize("fmt,fname", [(av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")])
+def test_batch_of_the_layer_weights(fmt, fname):
+    # the seven weights of the layer in one launch pair (no split), and eight tensors (the most a
+    # batch takes) with the split
+    dev = device()
+    rng = np.random.default_rng(75)
+    ws = [torch.from_numpy((rng.standard_normal(s) * 0.02).astype(np.float32)).to(dev).to(torch.bfloat16) for s in LAYER_W]
+    check_batch(ws, fmt, False, False, f"layer-weights-{fname}")
+    xs = [workloads.to_torch(workloads.up_proj_like(80 + i, 512 + 96 * i, 256, 32).x, "bf16", dev) for i in range(8)]
+    check_batch(xs, fmt, True, False, f"eight-{fname}")
+
+
+def test_batch_reuses_workspaces():
+    # a second batch on the same workspaces (the strip counters are back at zero) gives the same
+    # bytes; two items on one workspace are refused
+    dev = device()
+    print("case batch-reuse", flush=True)
+    xs = [workloads.to_torch(workloads.up_proj_like(90 + i, 700, 512, 32).x, "bf16", dev) for i in range(3)]
+    wss = [av.split_quant_workspace(700, 512, av.MXFP4, True, False, dev) for _ in xs]
+    a = av.split_quant_batch(xs, av.MXFP4, wss=wss)
+    b = av.split_quant_batch(xs, av.MXFP4, wss=wss)
+    torch.cuda.synchronize()
+    for i in range(3):
+        for k in ("mean", "row", "col", "mean_q"):
+            same(a[i][k], b[i][k], f"reuse tensor {i} {k}")
+    with pytest.raises(av.AverisError, match="workspace"):
+        av.split_quant_batch(xs[:2], av.MXFP4, wss=[wss[0], wss[0]])
+
+
+@pytest.mark.parametrize("fmt,fname", [(av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")])
+def test_layer_step_batched_quantization_is_unchanged(fmt, fname):
+    # the layer step's batched launches (weights; q/k/v and gate/up output gradients) write the
+    # same bytes as one launch per tensor
+    from fp4_quantized_amd.step import LayerStep
+    dev = device()
+    print(f"case layer-step-batched-{fname}", flush=True)
+    layers = workloads.layer_device(3, 1000, dev, shared=True)
+    a = LayerStep(layers, fmt, split=True, batched=True)
+    b = LayerStep(layers, fmt, split=True, batched=False)
+    assert max(len(g) for g in a.groups) == 7 and len(a.groups) < len(b.groups)
+    a.quantize()
+    b.quantize()
+    torch.cuda.synchronize()
+    for i, (qa, qb) in enumerate(zip(a.quants, b.quants)):
+        for k in ("mean", "row", "col", "mean_q"):
+            same(qa[2][k], qb[2][k], f"{fname} tensor {i} {k}")
