@@ -293,13 +293,15 @@ struct GemmTile {
   }
 
   // One K-step from stage s; with MU also the mean's K-step `kstep` from smu.
+  // MSO: byte offset of the mean's scale bytes from its codes in smu
+  template <int MSO = kMuCodes>
   __device__ __forceinline__ void compute(const uint8_t* s, const uint8_t* smu, int kstep) {
     constexpr int LSB = C::SB / 2;  // scale bytes per lane half per K-step (4 or 8)
     uint32_t msc[LSB / 4];          // MU: the mean's scale bytes of this lane half's chunks
     if constexpr (MU) {
 #pragma unroll
       for (int w = 0; w < LSB / 4; ++w)
-        msc[w] = *reinterpret_cast<const uint32_t*>(smu + kMuCodes + kstep * C::SB + mu_soff + 4 * w);
+        msc[w] = *reinterpret_cast<const uint32_t*>(smu + MSO + kstep * C::SB + mu_soff + 4 * w);
     }
     uint32_t sa[TM][LSB / 4], sb[TN][LSB / 4];
 #pragma unroll
@@ -1202,7 +1204,8 @@ __global__ __launch_bounds__(64 * (4 + L), 1) void k_gemm_ws_dw(GemmArgs g, cons
   }
 }
 
-// Warp-specialized grouped forward / input gradient (MXFP4, 128 x 128 tiles): logical tile lin
+// Warp-specialized grouped forward / input gradient (MXFP4, 128 x 128 tiles, or 256 x 128 with
+// TMW = 4): logical tile lin
 // enumerates, group after group, the ceil(l_e / 128) x tiles_n tiles of every group (expert);
 // every tile has the same K, so a workgroup's K-steps form one stream as in k_gemm_ws.  Each
 // group's first row, first 32-row-padded row and first logical tile sit in an LDS table built
@@ -1241,9 +1244,9 @@ __device__ __forceinline__ GTile wsg_tile(const GemmArgs& gin, int lin, const in
   return t;
 }
 
-template <int FMT, bool MU, int S, int L>
+template <int FMT, bool MU, int S, int L, int TMW = 2>
 __global__ __launch_bounds__(64 * (4 + L), 1) void k_gemm_ws_g(GemmArgs g) {
-  constexpr int WM = 2, WN = 2, TM = 2, TN = 2;
+  constexpr int WM = 2, WN = 2, TM = TMW, TN = 2;
   using T = GemmTile<FMT, WM, WN, TM, TN, 2, 0, MU>;
   using C = typename T::C;
   constexpr int MU_OFF = (C::STAGE + 255) / 256 * 256;  // the K-step's mean codes, then at +256 its scales
@@ -1339,7 +1342,8 @@ __global__ __launch_bounds__(64 * (4 + L), 1) void k_gemm_ws_g(GemmArgs g) {
     for (int st = 0; st < nsteps; ++st, ++q) {
       __builtin_amdgcn_s_barrier();
       const uint8_t* stg = ring + (q % S) * SSZ;
-      t.template compute_mx_preload<256>(stg, stg + MU_OFF, 0);
+      if constexpr (TM == 2) t.template compute_mx_preload<256>(stg, stg + MU_OFF, 0);
+      else t.template compute<256>(stg, stg + MU_OFF, 0);
     }
     if constexpr (MU) {
       if ((threadIdx.x & 31) == 0) {
@@ -1467,13 +1471,15 @@ static int g_count(int fmt) { return fmt == AVERIS_MXFP4 ? 32 : 16; }
 //   KCFG_LONG96 the long-K kernel on 128 x 96 tiles (4 x 1 waves of 32 x 96), for dense
 //               single-split long-K launches whose 128 x 128 tiles would leave CUs idle in
 //               their last round (the NVFP4 1024 x 3072 weight gradient: 192 tiles -> 256).
-constexpr int KCFG_LONG = 0, KCFG_SHORT = 1, KCFG_WS = 2, KCFG_LONG96 = 3, KCFG_WSW = 4, KCFG_WSDW = 5, KCFG_WSG = 6;
+constexpr int KCFG_LONG = 0, KCFG_SHORT = 1, KCFG_WS = 2, KCFG_LONG96 = 3, KCFG_WSW = 4, KCFG_WSDW = 5, KCFG_WSG = 6,
+              KCFG_WSGW = 7;
 constexpr int kWsStages = 4, kWsLoaders = 2;  // warp-specialized kernel: ring depth, loader waves
 constexpr bool kWsLongK = true;               // warp-specialized kernel for long K too
 constexpr bool kWsWide = true;                // 256 x 128 warp-specialized tiles for short K
+constexpr bool kWsgWide = true;               // 256 x 128 tiles for the grouped forward / input gradient
 struct TileCfg { int bm, bn; };
 static TileCfg tile_of(int cfg) {
-  return cfg == KCFG_LONG96 ? TileCfg{128, 96} : cfg == KCFG_WSW ? TileCfg{256, 128} : TileCfg{128, 128};
+  return cfg == KCFG_LONG96 ? TileCfg{128, 96} : (cfg == KCFG_WSW || cfg == KCFG_WSGW) ? TileCfg{256, 128} : TileCfg{128, 128};
 }
 constexpr int kBKE = 256;
 // Short K: the warp-specialized kernel (MXFP4 dense launches; the rest fall back to the two-stage
@@ -1524,6 +1530,12 @@ static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipSt
       constexpr int S = kWsStages, L = kWsLoaders;
       if (g.mu_codes) hipLaunchKernelGGL((k_gemm_ws_g<F, true, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
       else hipLaunchKernelGGL((k_gemm_ws_g<F, false, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+      return;
+    }
+    if (cfg == KCFG_WSGW) {  // the same on 256 x 128 tiles: a 3-stage ring
+      constexpr int L = kWsLoaders;
+      if (g.mu_codes) hipLaunchKernelGGL((k_gemm_ws_g<F, true, 3, L, 4>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
+      else hipLaunchKernelGGL((k_gemm_ws_g<F, false, 3, L, 4>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
       return;
     }
     if (cfg == KCFG_WSDW) {  // grouped weight gradient
@@ -1660,7 +1672,8 @@ hipError_t gemm_launch(const GemmPlan& p) {
     if (fill(t96) > fill(t128) + 0.05) cfg = KCFG_LONG96;
   }
   // (the grouped warp-specialized kernel carries each K-step of the mean in its stages: any K)
-  const bool mu_in = mu_row_fits || (p.mu && cfg == KCFG_WSG);
+  if (cfg == KCFG_WSG && kWsgWide) cfg = KCFG_WSGW;
+  const bool mu_in = mu_row_fits || (p.mu && (cfg == KCFG_WSG || cfg == KCFG_WSGW));
   const TileCfg tc = tile_of(cfg);
   g.tiles_m = (int)ceil_div(M, tc.bm); g.tiles_n = (int)ceil_div(N, tc.bn);
   if (p.grouped == 1)
