@@ -257,13 +257,16 @@ __device__ __forceinline__ void colstats_body(const ColArgs& a, int bx, int by) 
   // Every value exchanged between workgroups is an agent-scope atomic access: on gfx950 the
   // partial stores are written through to the agent's coherence point (sc1), the counter
   // update is performed there, and the finalizer's partial loads are served from there (sc1).
-  // The barrier waits for this workgroup's partial stores to complete (vmcnt 0) before thread 0
-  // counts the arrival, and the finalizer issues its loads only after its own update returned,
-  // so it reads every other workgroup's completed partials.  The language-level form (release
-  // on the update, acquire in the finalizer) compiles to a full L2 write-back and invalidate per
-  // workgroup and measured 2.1x slower for this pass on the layer shapes, so the ordering is
-  // the hardware's completion order of these coherent accesses.
+  // Each thread waits until its partial stores have completed (vmcnt 0; a workgroup barrier
+  // alone does not wait for global stores, and a store and a later atomic to another address
+  // may complete in either order), then the barrier lets thread 0 count the arrival; the
+  // finalizer issues its loads only after its own update returned, so it reads every other
+  // workgroup's completed partials.  The language-level form (release on the update, acquire in
+  // the finalizer) compiles to a full L2 write-back and invalidate per workgroup and measured
+  // 2.1x slower for this pass on the layer shapes; every exchanged value is written through, so
+  // the completion wait is the part of the release these accesses need.
   if constexpr (PARTS) return;
+  wait_vm<0>();
   __syncthreads();
   uint32_t* counter = a.counters + ((int64_t)e * a.n_strips + strip) * kCounterStride;
   if (t == 0)
@@ -406,7 +409,8 @@ __global__ __launch_bounds__(kThreads) void k_colstats_given(ColArgs a) {
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  __syncthreads();  // the partial stores have completed
+  wait_vm<0>();      // this thread's partial stores have completed (the barrier alone does not wait)
+  __syncthreads();  // ... and every thread's
   if (t == 0)
     s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nsl - 1);
   __syncthreads();
