@@ -5,9 +5,12 @@ Headline step: one training step of the seven linears of a Qwen3-0.6B-shaped tra
 layer at l = 16384 tokens (q 1024->2048, k and v 1024->1024, o 2048->1024, gate and up
 1024->3072, down 3072->1024; bf16 inputs): split + FP4-quantize every distinct input (q, k
 and v share theirs, gate and up share theirs) and every output gradient, quantize every
-weight, then each linear's forward (bf16 Y), input-gradient (bf16 dX) and weight-gradient
-(fp32 dW) GEMM with the mean terms.  Format MXFP4 (gfx950's native scaled-MFMA format);
-NVFP4-style blocks and the vanilla (no split) step are timed beside it.
+weight, and run each linear's forward (bf16 Y), input-gradient (bf16 dX) and weight-gradient
+(fp32 dW) GEMM with the mean terms, in a training step's order: the weights (one batched
+launch), the forward input by input (its split, then the forward GEMMs reading it), the
+backward in reverse (the batched split of the output gradients of the linears sharing an
+input, then their dX and dW).  Format MXFP4 (gfx950's native scaled-MFMA format); NVFP4-style
+blocks and the vanilla (no split) step are timed beside it.
 value = GEMM flops of the step / the step's median cold time.
 
 Timing: each measured call sequence is captured once in a HIP graph.  Cold replays follow a

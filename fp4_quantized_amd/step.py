@@ -54,8 +54,16 @@ class LinearStep:
                          dw=self.dw, stream=stream, ws=self.ws_dw)
 
     def run(self, stream=None):
-        self.quantize(stream)
-        self.gemms(stream)
+        """The step in training order: the weight, then the forward (split X, Y), then the
+        backward (split D, dX, dW)."""
+        sx, sd, sw = self.sx, self.sd, self.sw
+        av.split_quant(self.w, self.fmt, False, self.hadamard, stream=stream, out=sw, ws=self.ws_w)
+        av.split_quant(self.x, self.fmt, self.split, self.hadamard, stream=stream, out=sx, ws=self.ws_x)
+        av.linear_fwd(sx["row"], sx["mean_q"], sw["col"], stream=stream, out=self.y, ws=self.ws_fwd)
+        av.split_quant(self.d, self.fmt, self.split, self.hadamard, stream=stream, out=sd, ws=self.ws_d)
+        av.linear_bwd_dx(sd["row"], sd["mean_q"], sw["row"], stream=stream, out=self.dx, ws=self.ws_dx)
+        av.linear_bwd_dw(sx["col"], sd["col"], sx["mean_q"], sd["mean_q"], self.l, dw=self.dw, stream=stream,
+                         ws=self.ws_dw)
 
 
 class LayerStep:
@@ -67,7 +75,11 @@ class LayerStep:
     batched: tensors that become ready together are split and quantized in one batched launch
     pair (averis_split_quant_batch): every weight at the start of the step, and the output
     gradients of the linears that share an input (q/k/v: attention's backward returns them at
-    once; gate/up: the SwiGLU backward)."""
+    once; gate/up: the SwiGLU backward).
+
+    run() keeps a training step's order: the weights; the forward, input by input (split X, the
+    forward GEMMs of the linears reading it); the backward in reverse (split the output
+    gradients of those linears, their dX and dW GEMMs)."""
 
     def __init__(self, linears, fmt, split=True, hadamard=False, out_dtype=torch.bfloat16, batched=True):
         self.fmt, self.split, self.hadamard = fmt, split, hadamard
@@ -99,14 +111,19 @@ class LayerStep:
                                  ws_fwd=av.linear_workspace(sx["row"], sw["col"]),
                                  ws_dx=av.linear_workspace(sd["row"], sw["row"]),
                                  ws_dw=av.linear_bwd_dw_workspace(sx["col"], sd["col"], l)))
-        # launch groups in order: the weights, then per distinct X its split and its D's
+        # launch groups: the weights, then per distinct X its split, its D's and its linears
         chunks = lambda ix: [ix[i:i + av.BATCH_MAX] for i in range(0, len(ix), av.BATCH_MAX)]  # noqa: E731
-        if batched:
-            self.groups = chunks(w_idx)
-            for k, i in x_idx.items():
-                self.groups += [[i]] + chunks(d_idx[k])
-        else:
-            self.groups = [[i] for i in range(len(self.quants))]
+        one = lambda ix: [[i] for i in ix]  # noqa: E731
+        self.w_groups = chunks(w_idx) if batched else one(w_idx)
+        self.x_plan = []  # (X group, D groups, indices into lin)
+        li = 0
+        for k, i in x_idx.items():
+            nd = len(d_idx[k])
+            self.x_plan.append(([i], chunks(d_idx[k]) if batched else one(d_idx[k]), list(range(li, li + nd))))
+            li += nd
+        self.groups = list(self.w_groups)
+        for xg, dgs, _ in self.x_plan:
+            self.groups += [xg] + dgs
 
     @property
     def flops(self):
@@ -123,28 +140,48 @@ class LayerStep:
             tot += r * c * (in_bytes + 2 * (0.5 + 1.0 / g)) + (c * (4 + 0.5 + 1.0 / g) if sp else 0.0)
         return tot
 
+    def _split(self, grp, stream):
+        qs = [self.quants[i] for i in grp]
+        if len(qs) == 1:
+            t, sp, out, ws = qs[0]
+            av.split_quant(t, self.fmt, sp, self.hadamard, stream=stream, out=out, ws=ws)
+        else:
+            av.split_quant_batch([q[0] for q in qs], self.fmt, qs[0][1], self.hadamard,
+                                 outs=[q[2] for q in qs], wss=[q[3] for q in qs], stream=stream)
+
+    def _fwd(self, c, stream):
+        mx = c["sx"]["mean_q"] if self.split else None
+        av.linear_fwd(c["sx"]["row"], mx, c["sw"]["col"], stream=stream, out=c["y"], ws=c["ws_fwd"])
+
+    def _bwd(self, c, stream):
+        mx = c["sx"]["mean_q"] if self.split else None
+        md = c["sd"]["mean_q"] if self.split else None
+        av.linear_bwd_dx(c["sd"]["row"], md, c["sw"]["row"], stream=stream, out=c["dx"], ws=c["ws_dx"])
+        av.linear_bwd_dw(c["sx"]["col"], c["sd"]["col"], mx, md, c["l"], dw=c["dw"], stream=stream, ws=c["ws_dw"])
+
     def quantize(self, stream=None):
+        """Every split + quantization of the step, alone."""
         for grp in self.groups:
-            qs = [self.quants[i] for i in grp]
-            if len(qs) == 1:
-                t, sp, out, ws = qs[0]
-                av.split_quant(t, self.fmt, sp, self.hadamard, stream=stream, out=out, ws=ws)
-            else:
-                av.split_quant_batch([q[0] for q in qs], self.fmt, qs[0][1], self.hadamard,
-                                     outs=[q[2] for q in qs], wss=[q[3] for q in qs], stream=stream)
+            self._split(grp, stream)
 
     def gemms(self, stream=None):
+        """Every GEMM of the step, alone (on operands quantize() wrote)."""
         for c in self.lin:
-            mx = c["sx"]["mean_q"] if self.split else None
-            md = c["sd"]["mean_q"] if self.split else None
-            av.linear_fwd(c["sx"]["row"], mx, c["sw"]["col"], stream=stream, out=c["y"], ws=c["ws_fwd"])
-            av.linear_bwd_dx(c["sd"]["row"], md, c["sw"]["row"], stream=stream, out=c["dx"], ws=c["ws_dx"])
-            av.linear_bwd_dw(c["sx"]["col"], c["sd"]["col"], mx, md, c["l"], dw=c["dw"], stream=stream,
-                             ws=c["ws_dw"])
+            self._fwd(c, stream)
+            self._bwd(c, stream)
 
     def run(self, stream=None):
-        self.quantize(stream)
-        self.gemms(stream)
+        for grp in self.w_groups:
+            self._split(grp, stream)
+        for xg, _, lins in self.x_plan:
+            self._split(xg, stream)
+            for li in lins:
+                self._fwd(self.lin[li], stream)
+        for _, dgs, lins in reversed(self.x_plan):
+            for grp in dgs:
+                self._split(grp, stream)
+            for li in lins:
+                self._bwd(self.lin[li], stream)
 
 
 class MoEStep:
@@ -170,6 +207,7 @@ class MoEStep:
         wgrp_f = av.Groups(np.arange(E + 1) * f, dev)
         self.quants = []
         self.q = {}
+        self.qi = {}
         for name, t, grp, sp in (("x", x, self.grp, split), ("xd", x_down, self.grp, split),
                                  ("dg", d_gate, self.grp, split), ("du", d_up, self.grp, split),
                                  ("ddn", d_dn, self.grp, split),
@@ -177,6 +215,7 @@ class MoEStep:
                                  ("wd", w_down, wgrp_f, False)):
             out = av.split_quant_grouped_outputs(grp, t.shape[1], fmt, sp, device=dev)
             ws = av.split_quant_grouped_workspace(t.shape[0], t.shape[1], grp.E, fmt, sp, device=dev)
+            self.qi[name] = len(self.quants)
             self.quants.append((t, grp, sp, out, ws))
             self.q[name] = out
         q = self.q
@@ -200,7 +239,27 @@ class MoEStep:
         return 3 * 6 * self.grp.rows * self.h * self.f
 
     def run(self, stream=None):
-        for t, grp, sp, out, ws in self.quants:
+        """The step in training order: the weights; the forward (split X, gate and up; split the
+        down input, down); the backward (split down's output gradient, its dX and dW; split the
+        gate and up gradients, their dX and dW)."""
+        def split(name):
+            t, grp, sp, out, ws = self.quants[self.qi[name]]
             av.split_quant_grouped(t, grp, self.fmt, sp, stream=stream, out=out, ws=ws)
-        for fn, args, kw in self.gemms:
+
+        def gemm(i):
+            fn, args, kw = self.gemms[i]
             fn(*args, stream=stream, **kw)
+
+        for name in ("wg", "wu", "wd", "x"):
+            split(name)
+        gemm(0)  # gate forward
+        gemm(3)  # up forward
+        split("xd")
+        gemm(6)  # down forward
+        split("ddn")
+        gemm(7)  # down dX
+        gemm(8)  # down dW
+        split("dg")
+        split("du")
+        for i in (1, 2, 4, 5):  # gate and up dX, dW
+            gemm(i)

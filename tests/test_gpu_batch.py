@@ -109,3 +109,21 @@ def test_layer_step_batched_quantization_is_unchanged(fmt, fname):
     for i, (qa, qb) in enumerate(zip(a.quants, b.quants)):
         for k in ("mean", "row", "col", "mean_q"):
             same(qa[2][k], qb[2][k], f"{fname} tensor {i} {k}")
+
+
+def test_layer_step_training_order_is_unchanged():
+    # run() interleaves splits and GEMMs in a training step's order; every output equals that of
+    # all splits followed by all GEMMs
+    from fp4_quantized_amd.step import LayerStep
+    dev = device()
+    print("case layer-step-order", flush=True)
+    layers = workloads.layer_device(3, 1000, dev, shared=True)
+    a = LayerStep(layers, av.MXFP4, split=True)
+    b = LayerStep(layers, av.MXFP4, split=True)
+    a.run()
+    b.quantize()
+    b.gemms()
+    torch.cuda.synchronize()
+    for ca, cb in zip(a.lin, b.lin):
+        for k in ("y", "dx", "dw"):
+            assert torch.equal(ca[k], cb[k]), f"{ca['name']} {k}"
