@@ -539,7 +539,8 @@ __device__ __forceinline__ void store16(v4u v, __amdgpu_buffer_rsrc_t r, int off
 // ST: 2 = whole-line stores, non-temporal for outputs (split-K partials, re-read at once by the
 // reduction, with the default policy); 1 = whole-line stores, default policy; 0 = each lane's
 // 16-byte pieces as they come.
-template <int FMT, int TM, int TN, bool MU, bool ALL = true, bool STATS = false, int ST = 2>
+// BIAS = false: the launch never has a bias vector (its registers are not kept).
+template <int FMT, int TM, int TN, bool MU, bool ALL = true, bool STATS = false, int ST = 2, bool BIAS = true>
 __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&acc)[TM][TN], int64_t rbase,
                                               int64_t cbase, int split, int lane, const float* su, const float* sv,
                                               const float* sbias) {
@@ -548,10 +549,12 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
   const bool terms = g.splits == 1;
   // mean term: from the tile's MFMAs (MU; split-K partials carry their share) or a precomputed
   // bias vector (dense launches without MU)
-  const bool hb = MU || (ALL && terms && g.bias), hr = ALL && terms && g.has_r1;
+  const bool hb = MU || (BIAS && ALL && terms && g.bias), hr = ALL && terms && g.has_r1;
   float alpha_mu = 1.0f;
   if (FMT == AVERIS_NVFP4 && MU) alpha_mu = __fmul_rn(g.mu_ts[g.mu_row], g.b_ts[0]);
   // this lane's columns: bf16 -> j*32 + 16p + 8h + (0..7); fp32 -> j*32 + 8q + 4h + (0..3)
+  // VLAZY (256-row tiles): v is read from LDS where it is used instead of held in registers
+  constexpr bool VLAZY = TM >= 4;
   float bias[TN][16], vv[TN][16], uu[TM];
 #pragma unroll
   for (int j = 0; j < TN; ++j)
@@ -570,7 +573,7 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
       } else if (hb && ok) {
         b = *reinterpret_cast<const float4*>(g.bias + col);
       }
-      const float4 r = hr ? *reinterpret_cast<const float4*>(sv + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 r = (hr && !VLAZY) ? *reinterpret_cast<const float4*>(sv + off) : make_float4(0.f, 0.f, 0.f, 0.f);
       bias[j][4 * c4] = b.x; bias[j][4 * c4 + 1] = b.y; bias[j][4 * c4 + 2] = b.z; bias[j][4 * c4 + 3] = b.w;
       vv[j][4 * c4] = r.x; vv[j][4 * c4 + 1] = r.y; vv[j][4 * c4 + 2] = r.z; vv[j][4 * c4 + 3] = r.w;
     }
@@ -628,7 +631,15 @@ __device__ __forceinline__ void epilogue_regs(const GemmArgs& g, const v16f (&ac
       }
       if (hr) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = __fadd_rn(x[e], __fmul_rn(uu[i], vv[j][e]));
+        for (int e = 0; e < 16; ++e) {
+          float ve = vv[j][e];
+          if constexpr (VLAZY) {
+            const int c4 = e >> 2;
+            const int off = bf ? j * 32 + 16 * (c4 >> 1) + 8 * h + 4 * (c4 & 1) : j * 32 + 8 * c4 + 4 * h;
+            ve = sv[off + (e & 3)];
+          }
+          x[e] = __fadd_rn(x[e], __fmul_rn(uu[i], ve));
+        }
       }
       if (bf) {
 #pragma unroll
@@ -996,7 +1007,7 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
     }
     if constexpr (R1) s_uv[threadIdx.x] = uv;
     if constexpr (ebar) lds_barrier();
-    epilogue_regs<FMT, TM, TN, MU, R1, STATS>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, split, threadIdx.x & 63,
+    epilogue_regs<FMT, TM, TN, MU, R1, STATS, (STATS && TM == 4) ? 0 : 2>(g, t.acc, m0 + t.wm * TM * 32, n0 + t.wn * TN * 32, split, threadIdx.x & 63,
                                        s_uv + t.wm * TM * 32, s_uv + C::BM + t.wn * TN * 32,
                                        s_bias + t.wn * TN * 32);
   }
@@ -1028,7 +1039,6 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
 // Steps past the stream's end re-load the last step issued into the stage just freed, which
 // nobody reads.
 constexpr int kDwMaxGroups = 1024;  // groups of the LDS table (more: the three-stage kernel)
-constexpr int kUvStage = 2048;      // R1: the unit's u (first KB, 128 floats used) and v slices
 
 struct DwOrder { uint16_t e[kDwMaxGroups]; };  // groups, most K-steps first
 
@@ -1080,21 +1090,27 @@ __global__ __launch_bounds__(256) void k_rank_one_vectors(GemmArgs g, float* __r
   else if (i < g.M + g.N) v_tab[e * npad + (i - g.M)] = mean_value<FMT>(g.rv, e, i - g.M);
 }
 
-template <int FMT, bool R1, int S, int L>
+// TMW = 4: 256 x 128 tiles (a 3-stage ring; the group tables hold kDwMaxGroupsWide groups so that
+// the ring and the tables fit the LDS).
+constexpr int kDwMaxGroupsWide = 128;
+template <int FMT, bool R1, int S, int L, int TMW = 2>
 __global__ __launch_bounds__(64 * (4 + L), 1) void k_gemm_ws_dw(GemmArgs g, const float* __restrict__ u_tab,
                                                                 const float* __restrict__ v_tab, int64_t mpad,
                                                                 int64_t npad, DwOrder ord) {
-  constexpr int WM = 2, WN = 2, TM = 2, TN = 2;
+  constexpr int WM = 2, WN = 2, TM = TMW, TN = 2;
   using T = GemmTile<FMT, WM, WN, TM, TN, 2, 0, false>;
   using C = typename T::C;
   constexpr int UV_OFF = (C::STAGE + 255) / 256 * 256;
-  constexpr int SSZ = (UV_OFF + (R1 ? kUvStage : 0) + 1023) / 1024 * 1024;
+  constexpr int MAXG = TMW == 2 ? kDwMaxGroups : kDwMaxGroupsWide;
+  constexpr int UV_BYTES = (C::BM + C::BN) * 4;  // R1: u over the tile's rows, then v over its columns
+  constexpr int ALIGN = TM == 2 ? 1024 : 256;     // (256 x 128: three stages and the tables fit)
+  constexpr int SSZ = (UV_OFF + (R1 ? UV_BYTES : 0) + ALIGN - 1) / ALIGN * ALIGN;
   constexpr int SH = C::NW / L;                     // shares per loader wave
   constexpr int LPW = C::LPS * SH + (R1 ? 1 : 0);  // loads per loader wave per K-step
   static_assert(C::NW % L == 0 && LPW * (S - 2) < 64, "vmcnt range");
-  static_assert(!R1 || (L == 2 && C::BM == 128 && C::BN == 128), "one rank-one slice per loader");
+  static_assert(!R1 || (L == 2 && C::BM <= 256 && C::BN == 128), "one rank-one slice per loader");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S * SSZ];
-  __shared__ int s_len[kDwMaxGroups], s_t256[kDwMaxGroups];
+  __shared__ int s_len[MAXG], s_t256[MAXG];
 
   const int G = (int)gridDim.x, lw = xcd_local((int)blockIdx.x, G);
   int ntw = 0;  // this workgroup's units
@@ -1164,8 +1180,12 @@ __global__ __launch_bounds__(64 * (4 + L), 1) void k_gemm_ws_dw(GemmArgs g, cons
       uint8_t* stg = ring + (q % S) * SSZ;
 #pragma unroll
       for (int i = 0; i < SH; ++i) lt[i].issue(kstep * C::BKB, kstep * C::PIECE, stg);
-      // 32 lanes x 16 bytes = the 128 factors; the other lanes read past the range (zeros)
-      if constexpr (R1) dma16<0>(ruv, stg + UV_OFF + l * 1024, lane < 32 ? lane * 16 : 0x7FFFFFF0, 0);
+      // BM / 4 (u) or BN / 4 (v) lanes x 16 bytes = the factors, packed u then v.  Only those
+      // lanes issue the copy: a direct-to-LDS load writes every active lane's bytes (zeros past
+      // the range), and the packed slots have no room for the rest.
+      if constexpr (R1) {
+        if (lane < (l == 0 ? C::BM : C::BN) / 4) dma16<0>(ruv, stg + UV_OFF + (l == 0 ? 0 : C::BM * 4), lane * 16, 0);
+      }
       skip_empty();
     };
     open_unit(0);
@@ -1195,12 +1215,13 @@ __global__ __launch_bounds__(64 * (4 + L), 1) void k_gemm_ws_dw(GemmArgs g, cons
     t.clear();
     for (int st = 0; st < du.ns; ++st, ++q) {
       __builtin_amdgcn_s_barrier();
-      t.compute_mx_preload(ring + (q % S) * SSZ, ring, st);
+      if constexpr (TM == 2) t.compute_mx_preload(ring + (q % S) * SSZ, ring, st);
+      else t.compute(ring + (q % S) * SSZ, ring, st);
     }
     // R1 with K-steps: the factors sit in the stage of the unit's last K-step
     const float* uv = reinterpret_cast<const float*>(ring + ((q + S - 1) % S) * SSZ + UV_OFF);
-    epilogue_regs<FMT, TM, TN, false, R1>(gu, t.acc, du.m0 + t.wm * TM * 32, du.n0 + t.wn * TN * 32, 0, lane,
-                                          uv + t.wm * TM * 32, uv + 256 + t.wn * TN * 32, uv);
+    epilogue_regs<FMT, TM, TN, false, R1, false, 2, false>(gu, t.acc, du.m0 + t.wm * TM * 32, du.n0 + t.wn * TN * 32, 0, lane,
+                                          uv + t.wm * TM * 32, uv + C::BM + t.wn * TN * 32, uv);
   }
 }
 
@@ -1472,14 +1493,17 @@ static int g_count(int fmt) { return fmt == AVERIS_MXFP4 ? 32 : 16; }
 //               single-split long-K launches whose 128 x 128 tiles would leave CUs idle in
 //               their last round (the NVFP4 1024 x 3072 weight gradient: 192 tiles -> 256).
 constexpr int KCFG_LONG = 0, KCFG_SHORT = 1, KCFG_WS = 2, KCFG_LONG96 = 3, KCFG_WSW = 4, KCFG_WSDW = 5, KCFG_WSG = 6,
-              KCFG_WSGW = 7;
+              KCFG_WSGW = 7, KCFG_WSDWW = 8;
 constexpr int kWsStages = 4, kWsLoaders = 2;  // warp-specialized kernel: ring depth, loader waves
 constexpr bool kWsLongK = true;               // warp-specialized kernel for long K too
 constexpr bool kWsWide = true;                // 256 x 128 warp-specialized tiles for short K
 constexpr bool kWsgWide = true;               // 256 x 128 tiles for the grouped forward / input gradient
+constexpr bool kDwWide = true;                // 256 x 128 tiles for the grouped weight gradient
 struct TileCfg { int bm, bn; };
 static TileCfg tile_of(int cfg) {
-  return cfg == KCFG_LONG96 ? TileCfg{128, 96} : (cfg == KCFG_WSW || cfg == KCFG_WSGW) ? TileCfg{256, 128} : TileCfg{128, 128};
+  return cfg == KCFG_LONG96                                            ? TileCfg{128, 96}
+         : (cfg == KCFG_WSW || cfg == KCFG_WSGW || cfg == KCFG_WSDWW) ? TileCfg{256, 128}
+                                                                      : TileCfg{128, 128};
 }
 constexpr int kBKE = 256;
 // Short K: the warp-specialized kernel (MXFP4 dense launches; the rest fall back to the two-stage
@@ -1538,8 +1562,9 @@ static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipSt
       else hipLaunchKernelGGL((k_gemm_ws_g<F, false, 3, L, 4>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
       return;
     }
-    if (cfg == KCFG_WSDW) {  // grouped weight gradient
+    if (cfg == KCFG_WSDW || cfg == KCFG_WSDWW) {  // grouped weight gradient
       constexpr int S = kWsStages, L = kWsLoaders;
+      const bool wide = cfg == KCFG_WSDWW;
       const int64_t mpad = round_up(g.M, 128), npad = round_up(g.N, 128);
       float* u_tab = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + 256);
       float* v_tab = u_tab + g.E * mpad;
@@ -1552,8 +1577,15 @@ static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipSt
       if (g.has_r1) {
         hipLaunchKernelGGL(k_rank_one_vectors<F>, dim3((unsigned)ceil_div(g.M + g.N, 256), (unsigned)g.E), dim3(256), 0,
                            s, g, u_tab, v_tab, mpad, npad);
-        hipLaunchKernelGGL((k_gemm_ws_dw<F, true, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab, mpad,
-                           npad, ord);
+        if (wide)
+          hipLaunchKernelGGL((k_gemm_ws_dw<F, true, 3, L, 4>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab,
+                             mpad, npad, ord);
+        else
+          hipLaunchKernelGGL((k_gemm_ws_dw<F, true, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab, mpad,
+                             npad, ord);
+      } else if (wide) {
+        hipLaunchKernelGGL((k_gemm_ws_dw<F, false, 3, L, 4>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab,
+                           mpad, npad, ord);
       } else {
         hipLaunchKernelGGL((k_gemm_ws_dw<F, false, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab, mpad,
                            npad, ord);
@@ -1654,7 +1686,7 @@ hipError_t gemm_launch(const GemmPlan& p) {
   // grouped weight gradient, MXFP4: the warp-specialized form with per-group K
   if (p.grouped == 2 && fmt == AVERIS_MXFP4 && !p.accumulate && !p.mu && K > 0 && K < (int64_t(1) << 30) &&
       E <= kDwMaxGroups)
-    cfg = KCFG_WSDW;  // (group lengths in the LDS table are int)
+    cfg = kDwWide && E <= kDwMaxGroupsWide ? KCFG_WSDWW : KCFG_WSDW;  // (group lengths in the LDS table are int)
   // grouped forward / input gradient, MXFP4: the warp-specialized form with the group's mean
   // K-step in every stage (group offsets in the LDS table are int)
   if (p.grouped == 1 && fmt == AVERIS_MXFP4 && !p.accumulate && K > 0 && E <= kWsgMaxGroups &&
