@@ -1013,7 +1013,8 @@ __global__ __launch_bounds__(64 * (4 + L), 2) void k_gemm_ws(GemmArgs g) {
   }
 }
 
-// Warp-specialized form of the grouped weight gradient (MXFP4, 128 x 128 tiles): unit lin is
+// Warp-specialized form of the grouped weight gradient (both formats, 128 x 128 tiles; NVFP4 takes
+// the group's two tensor scales in the epilogue): unit lin is
 // tile lin % (tiles_m tiles_n) of group e = lin / (tiles_m tiles_n), whose K is the group's token
 // count padded to 256, so units differ in their number of K-steps (none for an empty group).
 // Waves as in k_gemm_ws; the loaders walk a cursor over the flattened (unit, K-step) sequence and
@@ -1071,6 +1072,7 @@ __device__ __forceinline__ DwUnit dw_unit(const GemmArgs& gin, int rank, const D
   g.b_codes += gin.N * t0 / 2;
   g.b_scales += gin.N * t0 / C::G;
   g.c = reinterpret_cast<float*>(gin.c) + (int64_t)u.e * gin.M * gin.ldc;
+  if (C::G == 16) { g.a_ts = gin.a_ts + u.e; g.b_ts = gin.b_ts + u.e; }  // NVFP4: per-group tensor scales
   g.has_r1 = gin.has_r1 && len > 0;
   u.m0 = (int64_t)tm * C::BM;
   u.n0 = (int64_t)tn * C::BN;
@@ -1215,7 +1217,7 @@ __global__ __launch_bounds__(64 * (4 + L), 1) void k_gemm_ws_dw(GemmArgs g, cons
     t.clear();
     for (int st = 0; st < du.ns; ++st, ++q) {
       __builtin_amdgcn_s_barrier();
-      if constexpr (TM == 2) t.compute_mx_preload(ring + (q % S) * SSZ, ring, st);
+      if constexpr (TM == 2 && FMT == AVERIS_MXFP4) t.compute_mx_preload(ring + (q % S) * SSZ, ring, st);
       else t.compute(ring + (q % S) * SSZ, ring, st);
     }
     // R1 with K-steps: the factors sit in the stage of the unit's last K-step
@@ -1488,7 +1490,8 @@ static int g_count(int fmt) { return fmt == AVERIS_MXFP4 ? 32 : 16; }
 //   KCFG_SHORT  two LDS stages, two workgroups per CU (70 KB LDS, <= 256 VGPRs each): the other
 //               short-K launches (NVFP4, grouped, accumulate, GEMV mean term);
 //   KCFG_LONG   three stages, one workgroup per CU, deeper prefetch, for the other long-K
-//               launches (NVFP4 and grouped weight gradients);
+//               launches (NVFP4, and grouped weight gradients past the warp-specialized
+//               kernel's group table);
 //   KCFG_LONG96 the long-K kernel on 128 x 96 tiles (4 x 1 waves of 32 x 96), for dense
 //               single-split long-K launches whose 128 x 128 tiles would leave CUs idle in
 //               their last round (the NVFP4 1024 x 3072 weight gradient: 192 tiles -> 256).
@@ -1549,6 +1552,41 @@ size_t gemm_grouped_dw_ws_bytes(int64_t M, int64_t N, int64_t E) {
 template <int F>
 static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipStream_t s, void* ws,
                        const int64_t* h_offsets, bool stats = false) {
+  if (cfg == KCFG_WSDW || cfg == KCFG_WSDWW) {  // grouped weight gradient
+    constexpr int S = kWsStages, L = kWsLoaders;
+    const bool wide = cfg == KCFG_WSDWW;
+    const int64_t mpad = round_up(g.M, 128), npad = round_up(g.N, 128);
+    float* u_tab = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + 256);
+    float* v_tab = u_tab + g.E * mpad;
+    // groups ranked by K-steps, most first (stable: ties keep group order)
+    DwOrder ord;
+    std::vector<std::pair<int64_t, int>> ks((size_t)g.E);
+    for (int e = 0; e < g.E; ++e) ks[e] = {-ceil_div(h_offsets[e + 1] - h_offsets[e], (int64_t)kBKE), e};
+    std::stable_sort(ks.begin(), ks.end());
+    for (int e = 0; e < g.E; ++e) ord.e[e] = (uint16_t)ks[e].second;
+    if (g.has_r1)
+      hipLaunchKernelGGL(k_rank_one_vectors<F>, dim3((unsigned)ceil_div(g.M + g.N, 256), (unsigned)g.E), dim3(256), 0,
+                         s, g, u_tab, v_tab, mpad, npad);
+    // 256 x 128 tiles (MXFP4 only: three NVFP4 stages of that size exceed the LDS)
+    if constexpr (F == AVERIS_MXFP4) {
+      if (wide) {
+        if (g.has_r1)
+          hipLaunchKernelGGL((k_gemm_ws_dw<F, true, 3, L, 4>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab,
+                             mpad, npad, ord);
+        else
+          hipLaunchKernelGGL((k_gemm_ws_dw<F, false, 3, L, 4>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab,
+                             mpad, npad, ord);
+        return;
+      }
+    }
+    if (g.has_r1)
+      hipLaunchKernelGGL((k_gemm_ws_dw<F, true, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab, mpad,
+                         npad, ord);
+    else
+      hipLaunchKernelGGL((k_gemm_ws_dw<F, false, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab, mpad,
+                         npad, ord);
+    return;
+  }
   if constexpr (F == AVERIS_MXFP4) {
     if (cfg == KCFG_WSG) {  // grouped forward / input gradient
       constexpr int S = kWsStages, L = kWsLoaders;
@@ -1560,36 +1598,6 @@ static void launch_cfg(int cfg, bool mu, const GemmArgs& g, unsigned grid, hipSt
       constexpr int L = kWsLoaders;
       if (g.mu_codes) hipLaunchKernelGGL((k_gemm_ws_g<F, true, 3, L, 4>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
       else hipLaunchKernelGGL((k_gemm_ws_g<F, false, 3, L, 4>), dim3(grid), dim3(64 * (4 + L)), 0, s, g);
-      return;
-    }
-    if (cfg == KCFG_WSDW || cfg == KCFG_WSDWW) {  // grouped weight gradient
-      constexpr int S = kWsStages, L = kWsLoaders;
-      const bool wide = cfg == KCFG_WSDWW;
-      const int64_t mpad = round_up(g.M, 128), npad = round_up(g.N, 128);
-      float* u_tab = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + 256);
-      float* v_tab = u_tab + g.E * mpad;
-      // groups ranked by K-steps, most first (stable: ties keep group order)
-      DwOrder ord;
-      std::vector<std::pair<int64_t, int>> ks((size_t)g.E);
-      for (int e = 0; e < g.E; ++e) ks[e] = {-ceil_div(h_offsets[e + 1] - h_offsets[e], (int64_t)kBKE), e};
-      std::stable_sort(ks.begin(), ks.end());
-      for (int e = 0; e < g.E; ++e) ord.e[e] = (uint16_t)ks[e].second;
-      if (g.has_r1) {
-        hipLaunchKernelGGL(k_rank_one_vectors<F>, dim3((unsigned)ceil_div(g.M + g.N, 256), (unsigned)g.E), dim3(256), 0,
-                           s, g, u_tab, v_tab, mpad, npad);
-        if (wide)
-          hipLaunchKernelGGL((k_gemm_ws_dw<F, true, 3, L, 4>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab,
-                             mpad, npad, ord);
-        else
-          hipLaunchKernelGGL((k_gemm_ws_dw<F, true, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab, mpad,
-                             npad, ord);
-      } else if (wide) {
-        hipLaunchKernelGGL((k_gemm_ws_dw<F, false, 3, L, 4>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab,
-                           mpad, npad, ord);
-      } else {
-        hipLaunchKernelGGL((k_gemm_ws_dw<F, false, S, L>), dim3(grid), dim3(64 * (4 + L)), 0, s, g, u_tab, v_tab, mpad,
-                           npad, ord);
-      }
       return;
     }
     if (cfg == KCFG_WSW) {  // 256 x 128 tiles: a 3-stage ring of 51 KB stages
@@ -1683,10 +1691,11 @@ hipError_t gemm_launch(const GemmPlan& p) {
   const bool ws_ok = fmt == AVERIS_MXFP4 && !p.grouped && !p.accumulate && (!p.mu || mu_row_fits) && K > 0 &&
                      ceil_div(K, (int64_t)kBKE) % p.splits == 0;
   if (cfg == KCFG_WS && !ws_ok) cfg = KCFG_SHORT;
-  // grouped weight gradient, MXFP4: the warp-specialized form with per-group K
-  if (p.grouped == 2 && fmt == AVERIS_MXFP4 && !p.accumulate && !p.mu && K > 0 && K < (int64_t(1) << 30) &&
+  // grouped weight gradient: the warp-specialized form with per-group K (NVFP4 too: measured 1.5x
+  // faster over the MoE step than the three-stage kernel's per-tile K loop)
+  if (p.grouped == 2 && !p.accumulate && !p.mu && K > 0 && K < (int64_t(1) << 30) &&
       E <= kDwMaxGroups)
-    cfg = kDwWide && E <= kDwMaxGroupsWide ? KCFG_WSDWW : KCFG_WSDW;  // (group lengths in the LDS table are int)
+    cfg = kDwWide && fmt == AVERIS_MXFP4 && E <= kDwMaxGroupsWide ? KCFG_WSDWW : KCFG_WSDW;  // (group lengths in the LDS table are int)
   // grouped forward / input gradient, MXFP4: the warp-specialized form with the group's mean
   // K-step in every stage (group offsets in the LDS table are int)
   if (p.grouped == 1 && fmt == AVERIS_MXFP4 && !p.accumulate && K > 0 && E <= kWsgMaxGroups &&
