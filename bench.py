@@ -9,7 +9,8 @@ weight, and run each linear's forward (bf16 Y), input-gradient (bf16 dX) and wei
 (fp32 dW) GEMM with the mean terms, in a training step's order: the weights (one batched
 launch), the forward input by input (its split, then the forward GEMMs reading it), the
 backward in reverse (the batched split of the output gradients of the linears sharing an
-input, then their dX and dW).  Format MXFP4 (gfx950's native scaled-MFMA format); NVFP4-style
+input, then their dX and dW); the weights and the dW GEMMs on a second stream that forks from the
+timed stream and joins it before the step ends.  Format MXFP4 (gfx950's native scaled-MFMA format); NVFP4-style
 blocks and the vanilla (no split) step are timed beside it.
 value = GEMM flops of the step / the step's median cold time.
 

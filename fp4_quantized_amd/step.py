@@ -79,10 +79,19 @@ class LayerStep:
 
     run() keeps a training step's order: the weights; the forward, input by input (split X, the
     forward GEMMs of the linears reading it); the backward in reverse (split the output
-    gradients of those linears, their dX and dW GEMMs)."""
+    gradients of those linears, their dX and dW GEMMs).
 
-    def __init__(self, linears, fmt, split=True, hadamard=False, out_dtype=torch.bfloat16, batched=True):
+    overlap: nothing on the step's critical path waits for the weight quantization until the
+    first forward GEMM, or for a weight gradient at all (the next layer down needs dX, not dW).
+    With overlap the weights are quantized and every dW GEMM runs on a second stream (default
+    priority) that forks from the caller's stream at the start of run() and joins it at the
+    end; each dW waits only for its output gradient's split.  The two streams' kernels then
+    fill each other's ramp and tail.  Every result is the same as without overlap."""
+
+    def __init__(self, linears, fmt, split=True, hadamard=False, out_dtype=torch.bfloat16, batched=True,
+                 overlap=True):
         self.fmt, self.split, self.hadamard = fmt, split, hadamard
+        self.side = torch.cuda.Stream(device=linears[0][1].device) if overlap else None
         self.quants = []  # (tensor, split, outputs, workspace)
         qx = {}
         self.lin = []
@@ -153,11 +162,18 @@ class LayerStep:
         mx = c["sx"]["mean_q"] if self.split else None
         av.linear_fwd(c["sx"]["row"], mx, c["sw"]["col"], stream=stream, out=c["y"], ws=c["ws_fwd"])
 
-    def _bwd(self, c, stream):
-        mx = c["sx"]["mean_q"] if self.split else None
+    def _dx(self, c, stream):
         md = c["sd"]["mean_q"] if self.split else None
         av.linear_bwd_dx(c["sd"]["row"], md, c["sw"]["row"], stream=stream, out=c["dx"], ws=c["ws_dx"])
+
+    def _dw(self, c, stream):
+        mx = c["sx"]["mean_q"] if self.split else None
+        md = c["sd"]["mean_q"] if self.split else None
         av.linear_bwd_dw(c["sx"]["col"], c["sd"]["col"], mx, md, c["l"], dw=c["dw"], stream=stream, ws=c["ws_dw"])
+
+    def _bwd(self, c, stream):
+        self._dx(c, stream)
+        self._dw(c, stream)
 
     def quantize(self, stream=None):
         """Every split + quantization of the step, alone."""
@@ -171,17 +187,42 @@ class LayerStep:
             self._bwd(c, stream)
 
     def run(self, stream=None):
+        if self.side is None:
+            for grp in self.w_groups:
+                self._split(grp, stream)
+            for xg, _, lins in self.x_plan:
+                self._split(xg, stream)
+                for li in lins:
+                    self._fwd(self.lin[li], stream)
+            for _, dgs, lins in reversed(self.x_plan):
+                for grp in dgs:
+                    self._split(grp, stream)
+                for li in lins:
+                    self._bwd(self.lin[li], stream)
+            return
+        main = stream if stream is not None else torch.cuda.current_stream()
+        side = self.side
+        side.wait_stream(main)  # fork
         for grp in self.w_groups:
-            self._split(grp, stream)
-        for xg, _, lins in self.x_plan:
-            self._split(xg, stream)
+            self._split(grp, side)
+        weights = torch.cuda.Event()
+        weights.record(side)
+        for k, (xg, _, lins) in enumerate(self.x_plan):
+            self._split(xg, main)
+            if k == 0:
+                main.wait_event(weights)
             for li in lins:
-                self._fwd(self.lin[li], stream)
+                self._fwd(self.lin[li], main)
         for _, dgs, lins in reversed(self.x_plan):
             for grp in dgs:
-                self._split(grp, stream)
+                self._split(grp, main)
+            grads = torch.cuda.Event()
+            grads.record(main)
+            side.wait_event(grads)
             for li in lins:
-                self._bwd(self.lin[li], stream)
+                self._dx(self.lin[li], main)
+                self._dw(self.lin[li], side)
+        main.wait_stream(side)  # join
 
 
 class MoEStep:
@@ -194,10 +235,11 @@ class MoEStep:
     [h, f]), w_down [E * f, h]; offsets [E + 1] over the L rows (host array)."""
 
     def __init__(self, x, x_down, d_gate, d_up, d_dn, w_gate, w_up, w_down, offsets, fmt, split=True,
-                 out_dtype=torch.bfloat16):
+                 out_dtype=torch.bfloat16, overlap=True):
         import numpy as np
         dev = x.device
         self.fmt, self.split = fmt, split
+        self.side = torch.cuda.Stream(device=dev) if overlap else None  # as in LayerStep
         E = len(offsets) - 1
         L, h = x.shape
         f = x_down.shape[1]
@@ -241,25 +283,43 @@ class MoEStep:
     def run(self, stream=None):
         """The step in training order: the weights; the forward (split X, gate and up; split the
         down input, down); the backward (split down's output gradient, its dX and dW; split the
-        gate and up gradients, their dX and dW)."""
-        def split(name):
+        gate and up gradients, their dX and dW).  With overlap the weights and the dW GEMMs run on
+        the second stream, as in LayerStep.run."""
+        main = stream if stream is not None else torch.cuda.current_stream()
+        side = self.side if self.side is not None else main
+
+        def split(name, s):
             t, grp, sp, out, ws = self.quants[self.qi[name]]
-            av.split_quant_grouped(t, grp, self.fmt, sp, stream=stream, out=out, ws=ws)
+            av.split_quant_grouped(t, grp, self.fmt, sp, stream=s, out=out, ws=ws)
 
-        def gemm(i):
+        def gemm(i, s):
             fn, args, kw = self.gemms[i]
-            fn(*args, stream=stream, **kw)
+            fn(*args, stream=s, **kw)
 
-        for name in ("wg", "wu", "wd", "x"):
-            split(name)
-        gemm(0)  # gate forward
-        gemm(3)  # up forward
-        split("xd")
-        gemm(6)  # down forward
-        split("ddn")
-        gemm(7)  # down dX
-        gemm(8)  # down dW
-        split("dg")
-        split("du")
-        for i in (1, 2, 4, 5):  # gate and up dX, dW
-            gemm(i)
+        def hand_over(src, dst):  # dst waits for what src has enqueued so far
+            if src is not dst:
+                e = torch.cuda.Event()
+                e.record(src)
+                dst.wait_event(e)
+
+        hand_over(main, side)  # fork
+        for name in ("wg", "wu", "wd"):
+            split(name, side)
+        split("x", main)
+        hand_over(side, main)  # the forward needs the weights
+        gemm(0, main)  # gate forward
+        gemm(3, main)  # up forward
+        split("xd", main)
+        gemm(6, main)  # down forward
+        split("ddn", main)
+        hand_over(main, side)
+        gemm(7, main)  # down dX
+        gemm(8, side)  # down dW
+        split("dg", main)
+        split("du", main)
+        hand_over(main, side)
+        for i in (1, 4):  # gate and up dX
+            gemm(i, main)
+        for i in (2, 5):  # gate and up dW
+            gemm(i, side)
+        hand_over(side, main)  # join

@@ -127,3 +127,37 @@ def test_layer_step_training_order_is_unchanged():
     for ca, cb in zip(a.lin, b.lin):
         for k in ("y", "dx", "dw"):
             assert torch.equal(ca[k], cb[k]), f"{ca['name']} {k}"
+
+
+@pytest.mark.parametrize("fmt,fname", [(av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")])
+def test_layer_step_overlap_matches_one_stream(fmt, fname):
+    # the two-stream step (weights and weight gradients on a second stream), eager and replayed
+    # from a graph three times (outputs cleared between replays), equals the one-stream step
+    from fp4_quantized_amd.step import LayerStep
+    dev = device()
+    print(f"case layer-step-overlap-{fname}", flush=True)
+    layers = workloads.layer_device(3, 1000, dev, shared=True)
+    a = LayerStep(layers, fmt, split=True, overlap=True)
+    b = LayerStep(layers, fmt, split=True, overlap=False)
+    assert a.side is not None and b.side is None
+    b.run()
+    a.run()
+    torch.cuda.synchronize()
+
+    def check(tag):
+        for ca, cb in zip(a.lin, b.lin):
+            for k in ("y", "dx", "dw"):
+                assert torch.equal(ca[k], cb[k]), f"{tag} {ca['name']} {k}"
+
+    check("eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        a.run()
+    for r in range(3):
+        for c in a.lin:
+            for k in ("y", "dx", "dw"):
+                c[k].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check(f"replay {r}")

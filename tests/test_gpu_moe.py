@@ -212,3 +212,35 @@ def test_moe_step_matches_grouped_calls():
     _, _, kw_dx = st.gemms[4]
     _, _, kw_dw = st.gemms[5]
     assert torch.equal(kw_y["out"], y) and torch.equal(kw_dx["out"], dx) and torch.equal(kw_dw["dw"], dw)
+
+
+def test_moe_step_overlap_matches_one_stream():
+    # the two-stream MoE step (weights and weight gradients on a second stream), eager and
+    # replayed from a graph three times (outputs cleared between replays), equals the one-stream
+    # step
+    from fp4_quantized_amd.step import MoEStep
+    dev = device()
+    print("case moe-step-overlap", flush=True)
+    inp = workloads.moe_device(5, tokens=2048, hidden=256, ffn=384, experts=8, device=dev)
+    a = MoEStep(*inp[:8], inp[8], av.MXFP4, overlap=True)
+    b = MoEStep(*inp[:8], inp[8], av.MXFP4, overlap=False)
+    b.run()
+    a.run()
+    torch.cuda.synchronize()
+    outs = lambda st: [kw[k] for _, _, kw in st.gemms for k in ("out", "dw") if k in kw]  # noqa: E731
+
+    def check(tag):
+        for i, (ta, tb) in enumerate(zip(outs(a), outs(b))):
+            assert torch.equal(ta, tb), f"{tag} output {i}"
+
+    check("eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        a.run()
+    for r in range(3):
+        for t in outs(a):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check(f"replay {r}")
