@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50, help="timed replays per measurement (cold and warm each)")
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--one-stream", action="store_true",
+                   help="run the layer and MoE steps on one stream (per-launch attribution in a trace)")
     p.add_argument("--stages", default="all",
                    help="comma list of stages to run: layer,independent,chain,mlp,up_proj,down_proj,moe,prep,roofline")
     return p.parse_args()
@@ -224,7 +226,7 @@ def main():
         for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
             r = {}
             for split in (True, False):
-                st = LayerStep(layers, fmt, split=split)
+                st = LayerStep(layers, fmt, split=split, overlap=not args.one_stream)
                 tag = "averis" if split else "vanilla"
                 r[tag] = r4(timed(st.run))
                 if fmt == av.MXFP4 or split:
@@ -390,7 +392,7 @@ def main():
         for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
             r = {}
             for split in (True, False):
-                st = LayerStep(layers, fmt, split=split)
+                st = LayerStep(layers, fmt, split=split, overlap=not args.one_stream)
                 r["averis" if split else "vanilla"] = r4(timed(st.run, max(5, steps // 2)))
                 flops = st.flops
                 del st
@@ -457,7 +459,7 @@ def main():
         for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
             r = {}
             for split in (True, False):
-                ms = MoEStep(*moe_in[:8], moe_in[8], fmt, split=split)
+                ms = MoEStep(*moe_in[:8], moe_in[8], fmt, split=split, overlap=not args.one_stream)
                 r["averis" if split else "vanilla"] = r4(timed(ms.run, max(5, steps // 2)))
                 flops = ms.flops
                 del ms
@@ -522,7 +524,8 @@ def main():
                                "o 2048->1024, gate/up 1024->3072, down 3072->1024) at l=16384 tokens, fwd+dX+dW "
                                "each, bf16 in, bf16 Y/dX, fp32 dW, MXFP4 with the Averis split; q/k/v and gate/up "
                                "share their split input",
-                   "l": L_LAYER, "format": "mxfp4", "timing": "median of cold (cache-evicted) graph replays"},
+                   "l": L_LAYER, "format": "mxfp4", "timing": "median of cold (cache-evicted) graph replays",
+                   "streams": 1 if args.one_stream else 2},
         "split_quant": {"GBps": mx.get("split_quant_GBps"),
                         "frac_hbm": round(mx["split_quant_GBps"] / PEAK_HBM_GBPS, 4) if mx else None,
                         "frac_measured_copy": round(mx["split_quant_GBps"] / env["copy_GBps"], 4) if mx else None},
