@@ -458,16 +458,20 @@ def main():
         res = {}
         for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
             r = {}
-            for split in (True, False):
-                ms = MoEStep(*moe_in[:8], moe_in[8], fmt, split=split, overlap=not args.one_stream)
-                r["averis" if split else "vanilla"] = r4(timed(ms.run, max(5, steps // 2)))
-                flops = ms.flops
-                del ms
-            r["overhead_pct"] = round(100.0 * (r["averis"]["cold_med"] - r["vanilla"]["cold_med"])
-                                      / r["vanilla"]["cold_med"], 2)
-            r["step_tflops"] = round(flops / (r["averis"]["cold_med"] * 1e-3) / 1e12, 1)
+            # gate and up as one projection (hidden -> 2 ffn, the gated MLP's layout), and as two
+            for fused, sfx in ((True, ""), (False, "_separate")):
+                for split in (True, False):
+                    ms = MoEStep(*moe_in[:8], moe_in[8], fmt, split=split, overlap=not args.one_stream,
+                                 fuse_gate_up=fused)
+                    r[("averis" if split else "vanilla") + sfx] = r4(timed(ms.run, max(5, steps // 2)))
+                    flops = ms.flops
+                    del ms
+                r["overhead_pct" + sfx] = round(100.0 * (r["averis" + sfx]["cold_med"] - r["vanilla" + sfx]["cold_med"])
+                                                / r["vanilla" + sfx]["cold_med"], 2)
+                r["step_tflops" + sfx] = round(flops / (r["averis" + sfx]["cold_med"] * 1e-3) / 1e12, 1)
+                log(f"moe {name}{sfx}: averis {r['averis' + sfx]['cold_med']*1e3:.0f} us, "
+                    f"vanilla {r['vanilla' + sfx]['cold_med']*1e3:.0f} us")
             res[name] = r
-            log(f"moe {name}: averis {r['averis']['cold_med']*1e3:.0f} us, vanilla {r['vanilla']['cold_med']*1e3:.0f} us")
         res["routed_rows"] = int(moe_in[8][-1])
         res["gflop"] = round(flops / 1e9, 1)
         out["moe"] = res

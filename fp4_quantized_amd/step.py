@@ -232,13 +232,23 @@ class MoEStep:
 
     x [L, h] routed token states, x_down [L, f] the down projection's input, d_gate and d_up
     [L, f] the output gradients of gate and up, d_dn [L, h]; w_gate and w_up [E * h, f] (E stacked
-    [h, f]), w_down [E * f, h]; offsets [E + 1] over the L rows (host array)."""
+    [h, f]), w_down [E * f, h]; offsets [E + 1] over the L rows (host array).
+
+    fuse_gate_up: gate and up as one projection hidden -> 2 ffn, the layout of a gated MLP whose
+    two input projections share their input: per expert W = [W_gate | W_up] [h, 2f] and
+    D = [D_gate | D_up] [L, 2f].  One forward GEMM writes [Y_gate | Y_up], one weight-gradient
+    GEMM [dW_gate | dW_up], and one input-gradient GEMM (K = 2f) writes the input gradient of
+    X, D_gate W_gate^T + D_up W_up^T, which the separate projections leave as two terms.  The
+    column means, residuals and blocks of the concatenated tensors are those of the parts (the
+    blocks never straddle the boundary, f % 32 == 0), so with MXFP4 every quantized operand,
+    Y and dW equal the separate projections' bit for bit; NVFP4 has one tensor scale per
+    concatenated tensor (per expert for the weights) instead of one per part."""
 
     def __init__(self, x, x_down, d_gate, d_up, d_dn, w_gate, w_up, w_down, offsets, fmt, split=True,
-                 out_dtype=torch.bfloat16, overlap=True):
+                 out_dtype=torch.bfloat16, overlap=True, fuse_gate_up=False):
         import numpy as np
         dev = x.device
-        self.fmt, self.split = fmt, split
+        self.fmt, self.split, self.fused = fmt, split, fuse_gate_up
         self.side = torch.cuda.Stream(device=dev) if overlap else None  # as in LayerStep
         E = len(offsets) - 1
         L, h = x.shape
@@ -247,14 +257,25 @@ class MoEStep:
         self.grp = av.Groups(offsets, dev)
         wgrp_h = av.Groups(np.arange(E + 1) * h, dev)
         wgrp_f = av.Groups(np.arange(E + 1) * f, dev)
+        if fuse_gate_up:
+            assert f % 32 == 0
+            # (w, x, d, rows of one expert's weight, output columns) per projection
+            projs = [("wgu", "x", "dgu", h, 2 * f), ("wd", "xd", "ddn", f, h)]
+            tensors = (("x", x, self.grp, split), ("xd", x_down, self.grp, split),
+                       ("dgu", torch.cat([d_gate, d_up], dim=1), self.grp, split), ("ddn", d_dn, self.grp, split),
+                       ("wgu", torch.cat([w_gate, w_up], dim=1), wgrp_h, False), ("wd", w_down, wgrp_f, False))
+        else:
+            projs = [("wg", "x", "dg", h, f), ("wu", "x", "du", h, f), ("wd", "xd", "ddn", f, h)]
+            tensors = (("x", x, self.grp, split), ("xd", x_down, self.grp, split),
+                       ("dg", d_gate, self.grp, split), ("du", d_up, self.grp, split),
+                       ("ddn", d_dn, self.grp, split),
+                       ("wg", w_gate, wgrp_h, False), ("wu", w_up, wgrp_h, False),
+                       ("wd", w_down, wgrp_f, False))
+        self.projs = projs
         self.quants = []
         self.q = {}
         self.qi = {}
-        for name, t, grp, sp in (("x", x, self.grp, split), ("xd", x_down, self.grp, split),
-                                 ("dg", d_gate, self.grp, split), ("du", d_up, self.grp, split),
-                                 ("ddn", d_dn, self.grp, split),
-                                 ("wg", w_gate, wgrp_h, False), ("wu", w_up, wgrp_h, False),
-                                 ("wd", w_down, wgrp_f, False)):
+        for name, t, grp, sp in tensors:
             out = av.split_quant_grouped_outputs(grp, t.shape[1], fmt, sp, device=dev)
             ws = av.split_quant_grouped_workspace(t.shape[0], t.shape[1], grp.E, fmt, sp, device=dev)
             self.qi[name] = len(self.quants)
@@ -262,8 +283,8 @@ class MoEStep:
             self.q[name] = out
         q = self.q
         mu = (lambda n: q[n]["mean_q"]) if split else (lambda n: None)
-        self.gemms = []
-        for wq, xin, din, k_in, n_out in (("wg", "x", "dg", h, f), ("wu", "x", "du", h, f), ("wd", "xd", "ddn", f, h)):
+        self.gemms = []  # per projection p: 3 p forward, 3 p + 1 input gradient, 3 p + 2 weight gradient
+        for wq, xin, din, k_in, n_out in projs:
             y = torch.empty((L, n_out), dtype=out_dtype, device=dev)
             dx = torch.empty((L, k_in), dtype=out_dtype, device=dev)
             dw = torch.empty((E, k_in, n_out), dtype=torch.float32, device=dev)
@@ -284,9 +305,12 @@ class MoEStep:
         """The step in training order: the weights; the forward (split X, gate and up; split the
         down input, down); the backward (split down's output gradient, its dX and dW; split the
         gate and up gradients, their dX and dW).  With overlap the weights and the dW GEMMs run on
-        the second stream, as in LayerStep.run."""
+        the second stream, as in LayerStep.run; the gate and up forward wait only for their own
+        weights, the down forward for the down weight."""
         main = stream if stream is not None else torch.cuda.current_stream()
         side = self.side if self.side is not None else main
+        gu = list(range(len(self.projs) - 1))  # the gate / up projections; the last one is down
+        dn = len(self.projs) - 1
 
         def split(name, s):
             t, grp, sp, out, ws = self.quants[self.qi[name]]
@@ -303,23 +327,27 @@ class MoEStep:
                 dst.wait_event(e)
 
         hand_over(main, side)  # fork
-        for name in ("wg", "wu", "wd"):
-            split(name, side)
+        for p in gu:
+            split(self.projs[p][0], side)
+        gate_up_w = torch.cuda.Event()
+        gate_up_w.record(side)
+        split(self.projs[dn][0], side)  # needed from the down forward on
         split("x", main)
-        hand_over(side, main)  # the forward needs the weights
-        gemm(0, main)  # gate forward
-        gemm(3, main)  # up forward
+        main.wait_event(gate_up_w)
+        for p in gu:
+            gemm(3 * p, main)  # gate and up forward
         split("xd", main)
-        gemm(6, main)  # down forward
+        hand_over(side, main)  # the down weight
+        gemm(3 * dn, main)  # down forward
         split("ddn", main)
         hand_over(main, side)
-        gemm(7, main)  # down dX
-        gemm(8, side)  # down dW
-        split("dg", main)
-        split("du", main)
+        gemm(3 * dn + 1, main)  # down dX
+        gemm(3 * dn + 2, side)  # down dW
+        for p in gu:
+            split(self.projs[p][2], main)  # the gate and up output gradients
         hand_over(main, side)
-        for i in (1, 4):  # gate and up dX
-            gemm(i, main)
-        for i in (2, 5):  # gate and up dW
-            gemm(i, side)
+        for p in gu:
+            gemm(3 * p + 1, main)  # gate and up dX
+        for p in gu:
+            gemm(3 * p + 2, side)  # gate and up dW
         hand_over(side, main)  # join

@@ -214,16 +214,17 @@ def test_moe_step_matches_grouped_calls():
     assert torch.equal(kw_y["out"], y) and torch.equal(kw_dx["out"], dx) and torch.equal(kw_dw["dw"], dw)
 
 
-def test_moe_step_overlap_matches_one_stream():
+@pytest.mark.parametrize("fused", [False, True])
+def test_moe_step_overlap_matches_one_stream(fused):
     # the two-stream MoE step (weights and weight gradients on a second stream), eager and
     # replayed from a graph three times (outputs cleared between replays), equals the one-stream
     # step
     from fp4_quantized_amd.step import MoEStep
     dev = device()
-    print("case moe-step-overlap", flush=True)
+    print(f"case moe-step-overlap fused={fused}", flush=True)
     inp = workloads.moe_device(5, tokens=2048, hidden=256, ffn=384, experts=8, device=dev)
-    a = MoEStep(*inp[:8], inp[8], av.MXFP4, overlap=True)
-    b = MoEStep(*inp[:8], inp[8], av.MXFP4, overlap=False)
+    a = MoEStep(*inp[:8], inp[8], av.MXFP4, overlap=True, fuse_gate_up=fused)
+    b = MoEStep(*inp[:8], inp[8], av.MXFP4, overlap=False, fuse_gate_up=fused)
     b.run()
     a.run()
     torch.cuda.synchronize()
@@ -244,3 +245,33 @@ def test_moe_step_overlap_matches_one_stream():
         g.replay()
         torch.cuda.synchronize()
         check(f"replay {r}")
+
+
+def test_moe_step_fused_gate_up_matches_separate():
+    # gate and up as one projection hidden -> 2 ffn: with MXFP4 the means, Y = [Y_gate | Y_up]
+    # and dW = [dW_gate | dW_up] equal the separate projections' bit for bit, and the one
+    # input-gradient GEMM gives D_gate W_gate^T + D_up W_up^T (fp32 outputs here: within the
+    # fp32 summation order of the two terms)
+    from fp4_quantized_amd.step import MoEStep
+    dev = device()
+    print("case moe-step-fused-gate-up", flush=True)
+    inp = workloads.moe_device(6, tokens=1024, hidden=512, ffn=384, experts=8, device=dev)
+    f = 384
+    a = MoEStep(*inp[:8], inp[8], av.MXFP4, out_dtype=torch.float32, overlap=False, fuse_gate_up=True)
+    b = MoEStep(*inp[:8], inp[8], av.MXFP4, out_dtype=torch.float32, overlap=False, fuse_gate_up=False)
+    a.run()
+    b.run()
+    torch.cuda.synchronize()
+    ma, mg, mu = a.q["dgu"]["mean"], b.q["dg"]["mean"], b.q["du"]["mean"]
+    assert torch.equal(ma[:, :f], mg) and torch.equal(ma[:, f:], mu), "output-gradient means"
+    ya, yg, yu = a.gemms[0][2]["out"], b.gemms[0][2]["out"], b.gemms[3][2]["out"]
+    assert torch.equal(ya[:, :f], yg) and torch.equal(ya[:, f:], yu), "forward"
+    wa, wg, wu = a.gemms[2][2]["dw"], b.gemms[2][2]["dw"], b.gemms[5][2]["dw"]
+    assert torch.equal(wa[:, :, :f], wg) and torch.equal(wa[:, :, f:], wu), "weight gradient"
+    for i in (3, 4, 5):  # the down projection is the same in both
+        ka = "out" if "out" in a.gemms[i][2] else "dw"
+        assert torch.equal(a.gemms[i][2][ka], b.gemms[i + 3][2][ka]), f"down gemm {i}"
+    dxa = a.gemms[1][2]["out"].double()
+    dxs = b.gemms[1][2]["out"].double() + b.gemms[4][2]["out"].double()
+    e = float(torch.linalg.norm(dxa - dxs) / torch.linalg.norm(dxs))
+    assert e <= 1e-6, f"input gradient: {e:.3e}"
