@@ -89,7 +89,7 @@ class LayerStep:
     fill each other's ramp and tail.  Every result is the same as without overlap."""
 
     def __init__(self, linears, fmt, split=True, hadamard=False, out_dtype=torch.bfloat16, batched=True,
-                 overlap=True):
+                 overlap=True, fuse_dw=True):
         self.fmt, self.split, self.hadamard = fmt, split, hadamard
         self.side = torch.cuda.Stream(device=linears[0][1].device) if overlap else None
         self.quants = []  # (tensor, split, outputs, workspace)
@@ -133,6 +133,54 @@ class LayerStep:
         self.groups = list(self.w_groups)
         for xg, dgs, _ in self.x_plan:
             self.groups += [xg] + dgs
+        self.dw_fused = {}  # x_plan index -> the fused weight gradient of its linears
+        if fuse_dw:
+            for pi, (_, _, lins) in enumerate(self.x_plan):
+                self._fuse_dw(pi, [self.lin[i] for i in lins])
+
+    def _fuse_dw(self, pi, cs):
+        """Linears that share their input X have weight gradients X_R^T D_i + l mu_X^T mu_D_i that
+        form the column blocks of one GEMM, X_R^T [D_1 .. D_k] + l mu_X^T [mu_D_1 .. mu_D_k]
+        ([rainbus] 方法步骤详情, weight gradient, applied to each D_i): the D_i's K = tokens layouts
+        and quantized means are written as adjacent row blocks of one operand and the dW_i as
+        column blocks of one output, so one launch replaces one per linear (and their split-K
+        reductions).  MXFP4 (no tensor scale per D_i to keep apart), D_i widths that are
+        multiples of 256, and only when the fused GEMM fills the GPU with one round of
+        128 x 128 tiles (q/k/v: 8 x 32 = 256 tiles): every quantized operand is the same as
+        without fusion, dW the same up to fp32 summation order."""
+        if len(cs) < 2 or self.fmt != av.MXFP4 or any(c["n"] % 256 for c in cs):
+            return
+        l, m = cs[0]["l"], cs[0]["m"]
+        N = sum(c["n"] for c in cs)
+        if -(-m // 128) * -(-N // 128) > 256:
+            return
+        dev = cs[0]["dw"].device
+        fmt, h16 = self.fmt, self.hadamard
+        col = av.empty_qtensor(N, l, fmt, h16, dev)
+        mq = av.empty_qtensor(1, N, fmt, h16, dev) if self.split else None
+        piece = 32 * (256 // av.BLOCK[fmt])  # tiled scale bytes of one 32-row group and 256-element K-step
+        dw = torch.empty((m, N), dtype=torch.float32, device=dev)
+        off = 0
+        for c in cs:
+            n, sd = c["n"], c["sd"]  # sd is the dict the D split writes (shared with self.quants)
+            sd["col"] = av.QTensor(col.codes[off:off + n], col.scales[off:off + n], None, n, l, fmt, h16)
+            if self.split:
+                sc = mq.scales.view(-1)[(off // 256) * piece:((off + n) // 256) * piece].view(32, n // av.BLOCK[fmt])
+                sd["mean_q"] = av.QTensor(mq.codes[:, off // 2:(off + n) // 2], sc, None, 1, n, fmt, h16)
+            c["dw"] = dw[:, off:off + n]
+            off += n
+        self.dw_fused[pi] = dict(col=col, mean_q=mq, dw=dw, l=l, sx=cs[0]["sx"],
+                                 ws=av.linear_bwd_dw_workspace(cs[0]["sx"]["col"], col, l))
+
+    def _dws(self, pi, lins, stream):
+        """The weight gradients of the linears reading input pi: one fused launch or one each."""
+        f = self.dw_fused.get(pi)
+        if f is None:
+            for li in lins:
+                self._dw(self.lin[li], stream)
+            return
+        mx = f["sx"]["mean_q"] if self.split else None
+        av.linear_bwd_dw(f["sx"]["col"], f["col"], mx, f["mean_q"], f["l"], dw=f["dw"], stream=stream, ws=f["ws"])
 
     @property
     def flops(self):
@@ -182,9 +230,11 @@ class LayerStep:
 
     def gemms(self, stream=None):
         """Every GEMM of the step, alone (on operands quantize() wrote)."""
-        for c in self.lin:
-            self._fwd(c, stream)
-            self._bwd(c, stream)
+        for pi, (_, _, lins) in enumerate(self.x_plan):
+            for li in lins:
+                self._fwd(self.lin[li], stream)
+                self._dx(self.lin[li], stream)
+            self._dws(pi, lins, stream)
 
     def run(self, stream=None):
         if self.side is None:
@@ -194,11 +244,13 @@ class LayerStep:
                 self._split(xg, stream)
                 for li in lins:
                     self._fwd(self.lin[li], stream)
-            for _, dgs, lins in reversed(self.x_plan):
+            for pi in reversed(range(len(self.x_plan))):
+                _, dgs, lins = self.x_plan[pi]
                 for grp in dgs:
                     self._split(grp, stream)
                 for li in lins:
-                    self._bwd(self.lin[li], stream)
+                    self._dx(self.lin[li], stream)
+                self._dws(pi, lins, stream)
             return
         main = stream if stream is not None else torch.cuda.current_stream()
         side = self.side
@@ -213,7 +265,8 @@ class LayerStep:
                 main.wait_event(weights)
             for li in lins:
                 self._fwd(self.lin[li], main)
-        for _, dgs, lins in reversed(self.x_plan):
+        for pi in reversed(range(len(self.x_plan))):
+            _, dgs, lins = self.x_plan[pi]
             for grp in dgs:
                 self._split(grp, main)
             grads = torch.cuda.Event()
@@ -221,7 +274,7 @@ class LayerStep:
             side.wait_event(grads)
             for li in lins:
                 self._dx(self.lin[li], main)
-                self._dw(self.lin[li], side)
+            self._dws(pi, lins, side)
         main.wait_stream(side)  # join
 
 

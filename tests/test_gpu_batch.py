@@ -161,3 +161,43 @@ def test_layer_step_overlap_matches_one_stream(fmt, fname):
         g.replay()
         torch.cuda.synchronize()
         check(f"replay {r}")
+
+
+@pytest.mark.parametrize("split", [True, False])
+def test_layer_step_fused_qkv_weight_gradient(split):
+    # q, k and v share their input, so their weight gradients are the column blocks of one GEMM
+    # X_R^T [D_q D_k D_v] (+ l mu_X^T [mu_Dq mu_Dk mu_Dv]): every quantized operand equals the
+    # unfused step's (the D column layouts and means are views into one operand), Y and dX are
+    # bit-identical, dW agrees up to fp32 summation order (the unfused launches split K) and
+    # against the oracle
+    from fp4_quantized_amd.step import LayerStep
+    from tests.gpu_util import rel_fro
+    dev = device()
+    print(f"case layer-step-fused-dw split={split}", flush=True)
+    layers = workloads.layer_device(3, 1000, dev, shared=True)
+    a = LayerStep(layers, av.MXFP4, split=split, out_dtype=torch.float32, fuse_dw=True)
+    b = LayerStep(layers, av.MXFP4, split=split, out_dtype=torch.float32, fuse_dw=False)
+    assert list(a.dw_fused) == [0] and not b.dw_fused  # q/k/v fused; gate/up would need two tile rounds
+    a.run()
+    b.run()
+    torch.cuda.synchronize()
+    for i, (qa, qb) in enumerate(zip(a.quants, b.quants)):
+        for k in ("mean", "row", "col", "mean_q"):
+            same(qa[2][k], qb[2][k], f"tensor {i} {k}")
+    for ca, cb in zip(a.lin, b.lin):
+        assert torch.equal(ca["y"], cb["y"]) and torch.equal(ca["dx"], cb["dx"]), ca["name"]
+        e = rel_fro(ca["dw"].cpu().numpy(), cb["dw"].cpu().numpy())
+        assert e <= 1e-6, f"{ca['name']} dW: {e:.3e}"
+    # the fused block of k against the oracle
+    name, x, d, _ = layers[1]
+    c = a.lin[1]
+    assert name == "k" == c["name"]
+    xh, dh = x.float().cpu().numpy(), d.float().cpu().numpy()
+    ox = O.split_quant(xh, av.MXFP4, split=split, mean=c["sx"]["mean"].cpu().numpy() if split else None)
+    od = O.split_quant(dh, av.MXFP4, split=split, mean=c["sd"]["mean"].cpu().numpy() if split else None)
+    assert_q_equal(c["sd"]["col"], od["col"], "k: D column layout (view)")
+    if split:
+        assert_q_equal(c["sd"]["mean_q"], od["mean"], "k: quantized mean of D (view)")
+    ref = O.linear_bwd_dw(ox["col"], od["col"], ox["mean"], od["mean"], x.shape[0])
+    e = rel_fro(c["dw"].cpu().numpy(), ref)
+    assert e <= 1e-5, f"k dW against the oracle: {e:.3e}"
