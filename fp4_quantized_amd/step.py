@@ -89,7 +89,7 @@ class LayerStep:
     fill each other's ramp and tail.  Every result is the same as without overlap."""
 
     def __init__(self, linears, fmt, split=True, hadamard=False, out_dtype=torch.bfloat16, batched=True,
-                 overlap=True, fuse_dw=True):
+                 overlap=True, fuse_dw=True, fuse_fwd=True):
         self.fmt, self.split, self.hadamard = fmt, split, hadamard
         self.side = torch.cuda.Stream(device=linears[0][1].device) if overlap else None
         self.quants = []  # (tensor, split, outputs, workspace)
@@ -134,9 +134,44 @@ class LayerStep:
         for xg, dgs, _ in self.x_plan:
             self.groups += [xg] + dgs
         self.dw_fused = {}  # x_plan index -> the fused weight gradient of its linears
-        if fuse_dw:
-            for pi, (_, _, lins) in enumerate(self.x_plan):
+        self.fwd_fused = {}  # x_plan index -> the fused forward GEMM of its linears
+        for pi, (_, _, lins) in enumerate(self.x_plan):
+            if fuse_dw:
                 self._fuse_dw(pi, [self.lin[i] for i in lins])
+            if fuse_fwd:
+                self._fuse_fwd(pi, [self.lin[i] for i in lins])
+
+    def _fuse_fwd(self, pi, cs):
+        """Linears that share their input X have forward outputs 1 (mu_X W_i) + X_R W_i that are
+        the column blocks of X_R [W_1 .. W_k] plus the mean row ([rainbus] 方法步骤详情, forward):
+        the weights' K = m layouts are written as adjacent row blocks of one operand and the Y_i
+        are column blocks of one output, so one launch replaces one per linear.  MXFP4 (no
+        tensor scale per W_i to keep apart); every Y_i is bit-identical to its own launch's."""
+        if len(cs) < 2 or self.fmt != av.MXFP4 or any(c["n"] % 32 for c in cs):
+            return
+        l, m = cs[0]["l"], cs[0]["m"]
+        N = sum(c["n"] for c in cs)
+        dev = cs[0]["y"].device
+        wcol = av.empty_qtensor(N, m, self.fmt, self.hadamard, dev)
+        y = torch.empty((l, N), dtype=cs[0]["y"].dtype, device=dev)
+        off = 0
+        for c in cs:
+            n, sw = c["n"], c["sw"]  # sw is the dict the weight quantization writes
+            sw["col"] = av.QTensor(wcol.codes[off:off + n], wcol.scales[off:off + n], None, n, m, self.fmt,
+                                   self.hadamard)
+            c["y"] = y[:, off:off + n]
+            off += n
+        self.fwd_fused[pi] = dict(w=wcol, y=y, sx=cs[0]["sx"], ws=av.linear_workspace(cs[0]["sx"]["row"], wcol))
+
+    def _fwds(self, pi, lins, stream):
+        """The forward GEMMs of the linears reading input pi: one fused launch or one each."""
+        f = self.fwd_fused.get(pi)
+        if f is None:
+            for li in lins:
+                self._fwd(self.lin[li], stream)
+            return
+        mx = f["sx"]["mean_q"] if self.split else None
+        av.linear_fwd(f["sx"]["row"], mx, f["w"], stream=stream, out=f["y"], ws=f["ws"])
 
     def _fuse_dw(self, pi, cs):
         """Linears that share their input X have weight gradients X_R^T D_i + l mu_X^T mu_D_i that
@@ -231,8 +266,8 @@ class LayerStep:
     def gemms(self, stream=None):
         """Every GEMM of the step, alone (on operands quantize() wrote)."""
         for pi, (_, _, lins) in enumerate(self.x_plan):
+            self._fwds(pi, lins, stream)
             for li in lins:
-                self._fwd(self.lin[li], stream)
                 self._dx(self.lin[li], stream)
             self._dws(pi, lins, stream)
 
@@ -240,10 +275,9 @@ class LayerStep:
         if self.side is None:
             for grp in self.w_groups:
                 self._split(grp, stream)
-            for xg, _, lins in self.x_plan:
+            for pi, (xg, _, lins) in enumerate(self.x_plan):
                 self._split(xg, stream)
-                for li in lins:
-                    self._fwd(self.lin[li], stream)
+                self._fwds(pi, lins, stream)
             for pi in reversed(range(len(self.x_plan))):
                 _, dgs, lins = self.x_plan[pi]
                 for grp in dgs:
@@ -263,8 +297,7 @@ class LayerStep:
             self._split(xg, main)
             if k == 0:
                 main.wait_event(weights)
-            for li in lins:
-                self._fwd(self.lin[li], main)
+            self._fwds(k, lins, main)
         for pi in reversed(range(len(self.x_plan))):
             _, dgs, lins = self.x_plan[pi]
             for grp in dgs:

@@ -164,20 +164,22 @@ def test_layer_step_overlap_matches_one_stream(fmt, fname):
 
 
 @pytest.mark.parametrize("split", [True, False])
-def test_layer_step_fused_qkv_weight_gradient(split):
+def test_layer_step_fused_shared_input_gemms(split):
     # q, k and v share their input, so their weight gradients are the column blocks of one GEMM
-    # X_R^T [D_q D_k D_v] (+ l mu_X^T [mu_Dq mu_Dk mu_Dv]): every quantized operand equals the
-    # unfused step's (the D column layouts and means are views into one operand), Y and dX are
-    # bit-identical, dW agrees up to fp32 summation order (the unfused launches split K) and
-    # against the oracle
+    # X_R^T [D_q D_k D_v] (+ l mu_X^T [mu_Dq mu_Dk mu_Dv]), and q/k/v and gate/up have one
+    # forward GEMM each, X_R [W_1 .. W_k]^T: every quantized operand equals the unfused step's
+    # (the D column layouts, their means and the weights' K = m layouts are views into one
+    # operand), Y and dX are bit-identical, dW agrees up to fp32 summation order (the unfused
+    # launches split K) and against the oracle
     from fp4_quantized_amd.step import LayerStep
     from tests.gpu_util import rel_fro
     dev = device()
     print(f"case layer-step-fused-dw split={split}", flush=True)
     layers = workloads.layer_device(3, 1000, dev, shared=True)
     a = LayerStep(layers, av.MXFP4, split=split, out_dtype=torch.float32, fuse_dw=True)
-    b = LayerStep(layers, av.MXFP4, split=split, out_dtype=torch.float32, fuse_dw=False)
+    b = LayerStep(layers, av.MXFP4, split=split, out_dtype=torch.float32, fuse_dw=False, fuse_fwd=False)
     assert list(a.dw_fused) == [0] and not b.dw_fused  # q/k/v fused; gate/up would need two tile rounds
+    assert list(a.fwd_fused) == [0, 2] and not b.fwd_fused  # q/k/v and gate/up
     a.run()
     b.run()
     torch.cuda.synchronize()
@@ -189,10 +191,12 @@ def test_layer_step_fused_qkv_weight_gradient(split):
         e = rel_fro(ca["dw"].cpu().numpy(), cb["dw"].cpu().numpy())
         assert e <= 1e-6, f"{ca['name']} dW: {e:.3e}"
     # the fused block of k against the oracle
-    name, x, d, _ = layers[1]
+    name, x, d, w = layers[1]
     c = a.lin[1]
     assert name == "k" == c["name"]
     xh, dh = x.float().cpu().numpy(), d.float().cpu().numpy()
+    assert_q_equal(c["sw"]["col"], O.split_quant(w.float().cpu().numpy(), av.MXFP4, split=False)["col"],
+                   "k: W K = m layout (view)")
     ox = O.split_quant(xh, av.MXFP4, split=split, mean=c["sx"]["mean"].cpu().numpy() if split else None)
     od = O.split_quant(dh, av.MXFP4, split=split, mean=c["sd"]["mean"].cpu().numpy() if split else None)
     assert_q_equal(c["sd"]["col"], od["col"], "k: D column layout (view)")
