@@ -257,10 +257,13 @@ def main():
     # ---------------- roofline: the step's longest kernel ----------------
     roofline = None
     if headline is not None:
-        c = next(c for c in headline.lin if c["name"] == "gate")  # gate / up forward, down dX: same shape
-        l, m, n = c["l"], c["m"], c["n"]
-        t = timed_launch(lambda: av.linear_fwd(c["sx"]["row"], c["sx"]["mean_q"], c["sw"]["col"], out=c["y"],
-                                               ws=c["ws_fwd"]))
+        # the fused gate/up forward GEMM (X_R [W_gate W_up]^T + the mean row, one launch for both)
+        pi = next(i for i, (_, _, lins) in enumerate(headline.x_plan)
+                  if [headline.lin[j]["name"] for j in lins] == ["gate", "up"])
+        f = headline.fwd_fused[pi]
+        c = headline.lin[headline.x_plan[pi][2][0]]
+        l, m, n = c["l"], c["m"], f["w"].outer
+        t = timed_launch(lambda: av.linear_fwd(f["sx"]["row"], f["sx"]["mean_q"], f["w"], out=f["y"], ws=f["ws"]))
         launch_s = t["mean"] * 1e-3
         op = 0.5 + 1.0 / 32
         flops = 2.0 * l * m * n
@@ -269,8 +272,8 @@ def main():
         hbm_bound = t_hbm > t_mfma
         roofline = {
             "bound": "hbm" if hbm_bound else "mfma",
-            "kernel": "k_gemm_ws<MXFP4, mean term> forward GEMM, 16384 x 3072 x 1024, bf16 Y (gate and up "
-                      "forward, down input gradient: the step's longest launches)",
+            "kernel": f"k_gemm_ws<MXFP4, mean term> forward GEMM of gate and up together, {l} x {n} x {m}, bf16 Y "
+                      "(the step's longest launch)",
             "achieved": round(nbytes / launch_s / 1e9, 1) if hbm_bound else round(flops / launch_s / 1e12, 1),
             "peak": PEAK_HBM_GBPS if hbm_bound else PEAK_FP4_TFLOPS,
             "unit": "GB/s" if hbm_bound else "TFLOP/s",
@@ -553,7 +556,7 @@ def gemm_traffic():
     """HBM bytes per launch of the roofline kernel from the committed counter summary, or None
     once the GEMM source has changed since those counters were taken."""
     import re
-    prof = os.path.join(ROOT, "profiles", "k_gemm_ws_mxfp4_mean_16384x3072x1024_traffic.txt")
+    prof = os.path.join(ROOT, "profiles", "k_gemm_ws_mxfp4_mean_16384x6144x1024_traffic.txt")
     try:
         text = open(prof).read()
     except OSError:
