@@ -10,7 +10,9 @@ weight, and run each linear's forward (bf16 Y), input-gradient (bf16 dX) and wei
 launch), the forward input by input (its split, then the forward GEMMs reading it), the
 backward in reverse (the batched split of the output gradients of the linears sharing an
 input, then their dX and dW); the weights and the dW GEMMs on a second stream that forks from the
-timed stream and joins it before the step ends.  Format MXFP4 (gfx950's native scaled-MFMA format); NVFP4-style
+timed stream and joins it before the step ends.  Linears that share an input share GEMMs:
+q/k/v and gate/up one forward GEMM each (the Y_i are its column blocks), q/k/v one
+weight-gradient GEMM (the dW_i are its column blocks); each linear keeps its own dX.  Format MXFP4 (gfx950's native scaled-MFMA format); NVFP4-style
 blocks and the vanilla (no split) step are timed beside it.
 value = GEMM flops of the step / the step's median cold time.
 
@@ -530,7 +532,8 @@ def main():
         "config": {"workload": "Qwen3-0.6B-shaped transformer layer, 7 linears (q 1024->2048, k/v 1024->1024, "
                                "o 2048->1024, gate/up 1024->3072, down 3072->1024) at l=16384 tokens, fwd+dX+dW "
                                "each, bf16 in, bf16 Y/dX, fp32 dW, MXFP4 with the Averis split; q/k/v and gate/up "
-                               "share their split input",
+                               "share their split input and their forward GEMM, q/k/v also their "
+                               "weight-gradient GEMM",
                    "l": L_LAYER, "format": "mxfp4", "timing": "median of cold (cache-evicted) graph replays",
                    "streams": 1 if args.one_stream else 2},
         "split_quant": {"GBps": mx.get("split_quant_GBps"),
