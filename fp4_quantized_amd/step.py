@@ -86,7 +86,12 @@ class LayerStep:
     With overlap the weights are quantized and every dW GEMM runs on a second stream (default
     priority) that forks from the caller's stream at the start of run() and joins it at the
     end; each dW waits only for its output gradient's split.  The two streams' kernels then
-    fill each other's ramp and tail.  Every result is the same as without overlap."""
+    fill each other's ramp and tail.  Every result is the same as without overlap.
+
+    fuse_fwd / fuse_dw (MXFP4): linears that share an input run one forward GEMM (q/k/v,
+    gate/up) and, where it fills the GPU in one round of tiles, one weight-gradient GEMM (q/k/v),
+    whose output column blocks are the linears' Y_i and dW_i (see _fuse_fwd, _fuse_dw); the
+    per-linear "y" and "dw" are then views of those outputs.  Each linear keeps its own dX."""
 
     def __init__(self, linears, fmt, split=True, hadamard=False, out_dtype=torch.bfloat16, batched=True,
                  overlap=True, fuse_dw=True, fuse_fwd=True):
