@@ -14,6 +14,34 @@ import torch
 from . import averis as av
 
 
+def _column_blocks(ts):
+    """The tensor [r, N] whose adjacent column blocks, in order, are the 2-D tensors ts, or None."""
+    t0 = ts[0]
+    r, N = t0.shape[0], sum(t.shape[1] for t in ts)
+    off = 0
+    for t in ts:
+        if (t.dim() != 2 or r == 0 or t.shape[0] != r or t.dtype != t0.dtype or t.device != t0.device
+                or t.untyped_storage().data_ptr() != t0.untyped_storage().data_ptr()
+                or t.stride() != (N, 1) or t.storage_offset() != t0.storage_offset() + off):
+            return None
+        off += t.shape[1]
+    return t0.as_strided((r, N), (N, 1))
+
+
+def _rows(q, off, n):
+    """Rows [off, off + n) of a quantized operand (off a multiple of 32): a view."""
+    return av.QTensor(q.codes[off:off + n], q.scales[off:off + n], None, n, q.k, q.fmt, q.rotated)
+
+
+def _k_block(q, off, n):
+    """Elements [off, off + n) of a one-row quantized operand (off, n multiples of 256): a view
+    (the tiled scales of one 256-element K-step of a 32-row group are contiguous)."""
+    g = av.BLOCK[q.fmt]
+    piece = 32 * (256 // g)
+    sc = q.scales.view(-1)[(off // 256) * piece:((off + n) // 256) * piece].view(32, n // g)
+    return av.QTensor(q.codes[:, off // 2:(off + n) // 2], sc, None, 1, n, q.fmt, q.rotated)
+
+
 class LinearStep:
     def __init__(self, x, d, w, fmt, split=True, hadamard=False, out_dtype=torch.bfloat16):
         l, m = x.shape
@@ -91,60 +119,120 @@ class LayerStep:
     fuse_fwd / fuse_dw (MXFP4): linears that share an input run one forward GEMM (q/k/v,
     gate/up) and, where it fills the GPU in one round of tiles, one weight-gradient GEMM (q/k/v),
     whose output column blocks are the linears' Y_i and dW_i (see _fuse_fwd, _fuse_dw); the
-    per-linear "y" and "dw" are then views of those outputs.  Each linear keeps its own dX."""
+    per-linear "y" and "dw" are then views of those outputs.
+
+    fuse_dx (MXFP4): where the output gradients and the weights of the linears sharing an input
+    are adjacent column blocks of one tensor each (as a fused q/k/v or gate/up projection stores
+    them), those two tensors are split and quantized once each and the linears run one
+    input-gradient GEMM, whose output is the input's gradient, the sum over the linears (see
+    _concat); every such linear's "dx" is that one tensor.  Otherwise each linear has its own
+    dX (the sum is left to the caller)."""
 
     def __init__(self, linears, fmt, split=True, hadamard=False, out_dtype=torch.bfloat16, batched=True,
-                 overlap=True, fuse_dw=True, fuse_fwd=True):
+                 overlap=True, fuse_dw=True, fuse_fwd=True, fuse_dx=True):
         self.fmt, self.split, self.hadamard = fmt, split, hadamard
         self.side = torch.cuda.Stream(device=linears[0][1].device) if overlap else None
         self.quants = []  # (tensor, split, outputs, workspace)
-        qx = {}
         self.lin = []
-        w_idx, x_idx, d_idx = [], {}, {}  # indices into quants: weights; per distinct X its own and its D's
-        for name, x, d, w in linears:
-            l, m = x.shape
-            n = d.shape[1]
-            dev = x.device
-            if id(x) not in qx:
-                out = av.split_quant_outputs(l, m, fmt, split, hadamard, device=dev)
-                x_idx[id(x)] = len(self.quants)
-                d_idx[id(x)] = []
-                self.quants.append((x, split, out, av.split_quant_workspace(l, m, fmt, split, hadamard, dev)))
-                qx[id(x)] = out
-            sx = qx[id(x)]
-            sd = av.split_quant_outputs(l, n, fmt, split, hadamard, device=dev)
-            d_idx[id(x)].append(len(self.quants))
-            self.quants.append((d, split, sd, av.split_quant_workspace(l, n, fmt, split, hadamard, dev)))
-            sw = av.split_quant_outputs(m, n, fmt, False, hadamard, device=dev)
-            w_idx.append(len(self.quants))
-            self.quants.append((w, False, sw, av.split_quant_workspace(m, n, fmt, False, hadamard, dev)))
-            y = torch.empty((l, n), dtype=out_dtype, device=dev)
-            dx = torch.empty((l, m), dtype=out_dtype, device=dev)
-            dw = torch.empty((m, n), dtype=torch.float32, device=dev)
-            self.lin.append(dict(name=name, l=l, m=m, n=n, sx=sx, sd=sd, sw=sw, y=y, dx=dx, dw=dw,
-                                 ws_fwd=av.linear_workspace(sx["row"], sw["col"]),
-                                 ws_dx=av.linear_workspace(sd["row"], sw["row"]),
-                                 ws_dw=av.linear_bwd_dw_workspace(sx["col"], sd["col"], l)))
-        # launch groups: the weights, then per distinct X its split, its D's and its linears
+        self.dw_fused = {}  # x_plan index -> the fused weight gradient of its linears
+        self.fwd_fused = {}  # x_plan index -> the fused forward GEMM of its linears
+        self.dx_fused = {}  # x_plan index -> the one input-gradient GEMM of its linears
+        by_x = {}  # linears grouped by their input (callers list each group's linears together)
+        for item in linears:
+            by_x.setdefault(id(item[1]), []).append(item)
         chunks = lambda ix: [ix[i:i + av.BATCH_MAX] for i in range(0, len(ix), av.BATCH_MAX)]  # noqa: E731
         one = lambda ix: [[i] for i in ix]  # noqa: E731
+        w_idx = []  # indices into quants of the weights
+        self.x_plan = []  # (X group, D groups, indices into lin), one per distinct X
+        for pi, items in enumerate(by_x.values()):
+            x = items[0][1]
+            l, m = x.shape
+            xi, sx = self._add(x, split, l, m)
+            li0 = len(self.lin)
+            parents = None
+            if fuse_dx and len(items) >= 2 and fmt == av.MXFP4 and all(it[2].shape[1] % 256 == 0 for it in items):
+                dp, wp = _column_blocks([it[2] for it in items]), _column_blocks([it[3] for it in items])
+                if dp is not None and wp is not None:
+                    parents = (dp, wp)
+            if parents is not None:
+                d_idx = [self._concat(pi, items, sx, parents, out_dtype, fuse_fwd, fuse_dw, w_idx)]
+            else:
+                d_idx = []
+                for name, _, d, w in items:
+                    n = d.shape[1]
+                    di, sd = self._add(d, split, l, n)
+                    wi, sw = self._add(w, False, m, n)
+                    d_idx.append(di)
+                    w_idx.append(wi)
+                    dev = x.device
+                    self.lin.append(dict(name=name, l=l, m=m, n=n, sx=sx, sd=sd, sw=sw,
+                                         y=torch.empty((l, n), dtype=out_dtype, device=dev),
+                                         dx=torch.empty((l, m), dtype=out_dtype, device=dev),
+                                         dw=torch.empty((m, n), dtype=torch.float32, device=dev),
+                                         ws_fwd=av.linear_workspace(sx["row"], sw["col"]),
+                                         ws_dx=av.linear_workspace(sd["row"], sw["row"]),
+                                         ws_dw=av.linear_bwd_dw_workspace(sx["col"], sd["col"], l)))
+                if fuse_dw:
+                    self._fuse_dw(pi, self.lin[li0:])
+                if fuse_fwd:
+                    self._fuse_fwd(pi, self.lin[li0:])
+            self.x_plan.append(([xi], chunks(d_idx) if batched else one(d_idx), list(range(li0, len(self.lin)))))
+        # launch groups: the weights, then per distinct X its split and its D's
         self.w_groups = chunks(w_idx) if batched else one(w_idx)
-        self.x_plan = []  # (X group, D groups, indices into lin)
-        li = 0
-        for k, i in x_idx.items():
-            nd = len(d_idx[k])
-            self.x_plan.append(([i], chunks(d_idx[k]) if batched else one(d_idx[k]), list(range(li, li + nd))))
-            li += nd
         self.groups = list(self.w_groups)
         for xg, dgs, _ in self.x_plan:
             self.groups += [xg] + dgs
-        self.dw_fused = {}  # x_plan index -> the fused weight gradient of its linears
-        self.fwd_fused = {}  # x_plan index -> the fused forward GEMM of its linears
-        for pi, (_, _, lins) in enumerate(self.x_plan):
-            if fuse_dw:
-                self._fuse_dw(pi, [self.lin[i] for i in lins])
-            if fuse_fwd:
-                self._fuse_fwd(pi, [self.lin[i] for i in lins])
+
+    def _add(self, t, sp, rows, cols):
+        """A split (+ quantization) of t [rows, cols] with its outputs and workspace."""
+        dev = t.device
+        out = av.split_quant_outputs(rows, cols, self.fmt, sp, self.hadamard, device=dev)
+        self.quants.append((t, sp, out, av.split_quant_workspace(rows, cols, self.fmt, sp, self.hadamard, dev)))
+        return len(self.quants) - 1, out
+
+    def _concat(self, pi, items, sx, parents, out_dtype, fuse_fwd, fuse_dw, w_idx):
+        """Linears that share their input X and whose output gradients D_i and weights W_i are
+        adjacent column blocks of one tensor each, D = [D_1 .. D_k] [l, N] and W = [W_1 .. W_k]
+        [m, N] (a fused projection's storage), are one linear of width N for the split: the column
+        means are per column and MXFP4 blocks never straddle a block boundary (widths multiples of
+        256), so D and W are split and quantized once and every D_i, W_i operand that the
+        per-linear GEMMs read (the K = tokens layout of D_i, its quantized mean, the K = m layout
+        of W_i) is a view of D's or W's.  The input gradient of X is the sum over the linears,
+        sum_i 1 (mu_Di W_i^T) + D_R,i W_i^T = 1 (mu_D W^T) + D_R W^T ([rainbus] 方法步骤详情,
+        input gradient, over D and W): one GEMM with K = N, which the per-linear launches would
+        leave to a separate sum.  Forward: one GEMM (as _fuse_fwd); weight gradient: one GEMM
+        where it fills the GPU in one round of 128 x 128 tiles (as _fuse_dw), else one per
+        linear on the views.  Returns the index of D's split."""
+        dp, wp = parents
+        fmt, h16, split = self.fmt, self.hadamard, self.split
+        l, m, N = dp.shape[0], wp.shape[0], dp.shape[1]
+        dev = dp.device
+        di, sdc = self._add(dp, split, l, N)
+        wi, swc = self._add(wp, False, m, N)
+        w_idx.append(wi)
+        y = torch.empty((l, N), dtype=out_dtype, device=dev)
+        dx = torch.empty((l, m), dtype=out_dtype, device=dev)
+        one_dw = fuse_dw and -(-m // 128) * -(-N // 128) <= 256
+        dw = torch.empty((m, N), dtype=torch.float32, device=dev) if one_dw else None
+        off = 0
+        for name, _, d, w in items:
+            n = d.shape[1]
+            sd = dict(mean=sdc["mean"][off:off + n] if split else None, row=None, col=_rows(sdc["col"], off, n),
+                      mean_q=_k_block(sdc["mean_q"], off, n) if split else None)
+            sw = dict(mean=None, row=None, col=_rows(swc["col"], off, n), mean_q=None)
+            self.lin.append(dict(name=name, l=l, m=m, n=n, sx=sx, sd=sd, sw=sw, y=y[:, off:off + n], dx=dx,
+                                 dw=dw[:, off:off + n] if one_dw else torch.empty((m, n), dtype=torch.float32,
+                                                                                   device=dev),
+                                 ws_fwd=av.linear_workspace(sx["row"], sw["col"]),
+                                 ws_dw=av.linear_bwd_dw_workspace(sx["col"], sd["col"], l)))
+            off += n
+        if fuse_fwd:
+            self.fwd_fused[pi] = dict(w=swc["col"], y=y, sx=sx, ws=av.linear_workspace(sx["row"], swc["col"]))
+        self.dx_fused[pi] = dict(d=sdc, w=swc, dx=dx, ws=av.linear_workspace(sdc["row"], swc["row"]))
+        if one_dw:
+            self.dw_fused[pi] = dict(col=sdc["col"], mean_q=sdc["mean_q"], dw=dw, l=l, sx=sx,
+                                     ws=av.linear_bwd_dw_workspace(sx["col"], sdc["col"], l))
+        return di
 
     def _fuse_fwd(self, pi, cs):
         """Linears that share their input X have forward outputs 1 (mu_X W_i) + X_R W_i that are
@@ -162,8 +250,7 @@ class LayerStep:
         off = 0
         for c in cs:
             n, sw = c["n"], c["sw"]  # sw is the dict the weight quantization writes
-            sw["col"] = av.QTensor(wcol.codes[off:off + n], wcol.scales[off:off + n], None, n, m, self.fmt,
-                                   self.hadamard)
+            sw["col"] = _rows(wcol, off, n)
             c["y"] = y[:, off:off + n]
             off += n
         self.fwd_fused[pi] = dict(w=wcol, y=y, sx=cs[0]["sx"], ws=av.linear_workspace(cs[0]["sx"]["row"], wcol))
@@ -198,15 +285,13 @@ class LayerStep:
         fmt, h16 = self.fmt, self.hadamard
         col = av.empty_qtensor(N, l, fmt, h16, dev)
         mq = av.empty_qtensor(1, N, fmt, h16, dev) if self.split else None
-        piece = 32 * (256 // av.BLOCK[fmt])  # tiled scale bytes of one 32-row group and 256-element K-step
         dw = torch.empty((m, N), dtype=torch.float32, device=dev)
         off = 0
         for c in cs:
             n, sd = c["n"], c["sd"]  # sd is the dict the D split writes (shared with self.quants)
-            sd["col"] = av.QTensor(col.codes[off:off + n], col.scales[off:off + n], None, n, l, fmt, h16)
+            sd["col"] = _rows(col, off, n)
             if self.split:
-                sc = mq.scales.view(-1)[(off // 256) * piece:((off + n) // 256) * piece].view(32, n // av.BLOCK[fmt])
-                sd["mean_q"] = av.QTensor(mq.codes[:, off // 2:(off + n) // 2], sc, None, 1, n, fmt, h16)
+                sd["mean_q"] = _k_block(mq, off, n)
             c["dw"] = dw[:, off:off + n]
             off += n
         self.dw_fused[pi] = dict(col=col, mean_q=mq, dw=dw, l=l, sx=cs[0]["sx"],
@@ -254,14 +339,20 @@ class LayerStep:
         md = c["sd"]["mean_q"] if self.split else None
         av.linear_bwd_dx(c["sd"]["row"], md, c["sw"]["row"], stream=stream, out=c["dx"], ws=c["ws_dx"])
 
+    def _dxs(self, pi, lins, stream):
+        """The input gradients of the linears reading input pi: their one summed launch or one each."""
+        f = self.dx_fused.get(pi)
+        if f is None:
+            for li in lins:
+                self._dx(self.lin[li], stream)
+            return
+        md = f["d"]["mean_q"] if self.split else None
+        av.linear_bwd_dx(f["d"]["row"], md, f["w"]["row"], stream=stream, out=f["dx"], ws=f["ws"])
+
     def _dw(self, c, stream):
         mx = c["sx"]["mean_q"] if self.split else None
         md = c["sd"]["mean_q"] if self.split else None
         av.linear_bwd_dw(c["sx"]["col"], c["sd"]["col"], mx, md, c["l"], dw=c["dw"], stream=stream, ws=c["ws_dw"])
-
-    def _bwd(self, c, stream):
-        self._dx(c, stream)
-        self._dw(c, stream)
 
     def quantize(self, stream=None):
         """Every split + quantization of the step, alone."""
@@ -272,8 +363,7 @@ class LayerStep:
         """Every GEMM of the step, alone (on operands quantize() wrote)."""
         for pi, (_, _, lins) in enumerate(self.x_plan):
             self._fwds(pi, lins, stream)
-            for li in lins:
-                self._dx(self.lin[li], stream)
+            self._dxs(pi, lins, stream)
             self._dws(pi, lins, stream)
 
     def run(self, stream=None):
@@ -287,8 +377,7 @@ class LayerStep:
                 _, dgs, lins = self.x_plan[pi]
                 for grp in dgs:
                     self._split(grp, stream)
-                for li in lins:
-                    self._dx(self.lin[li], stream)
+                self._dxs(pi, lins, stream)
                 self._dws(pi, lins, stream)
             return
         main = stream if stream is not None else torch.cuda.current_stream()
@@ -310,8 +399,7 @@ class LayerStep:
             grads = torch.cuda.Event()
             grads.record(main)
             side.wait_event(grads)
-            for li in lins:
-                self._dx(self.lin[li], main)
+            self._dxs(pi, lins, main)
             self._dws(pi, lins, side)
         main.wait_stream(side)  # join
 

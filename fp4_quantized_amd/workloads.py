@@ -159,12 +159,16 @@ def sweep_device(seed=3, l=16384, device="cuda"):
     return out
 
 
-def layer_device(seed=3, l=16384, device="cuda", shared=True):
+def layer_device(seed=3, l=16384, device="cuda", shared=True, cat=False):
     """The seven linears of one Qwen3-0.6B-shaped transformer layer at l tokens, drawn on the
     device with the recipe of `sweep_device`.  shared=True: q, k and v read the same input
     X [l, 1024] and gate and up the same X [l, 1024], as in the layer (the attention and MLP
     inputs after their norms); o and down have inputs of their own.  Every linear has its own
-    output gradient and weight.  Returns [(name, x, d, w)]; shared inputs are one tensor."""
+    output gradient and weight.  cat=True (with shared): the output gradients and the weights
+    of q/k/v, and those of gate/up, are adjacent column blocks of one tensor each (D [l, 4096],
+    W [1024, 4096]; D [l, 6144], W [1024, 6144]), the storage of a fused projection; the values
+    are the same.  Returns [(name, x, d, w)]; shared inputs are one tensor."""
+    import torch
     layers = sweep_device(seed, l, device)
     if not shared:
         return layers
@@ -176,6 +180,17 @@ def layer_device(seed=3, l=16384, device="cuda", shared=True):
         elif name == "up":
             x = x_mlp
         out.append((name, x, d, w))
+    if cat:
+        for names in (("q", "k", "v"), ("gate", "up")):
+            idx = [i for i, c in enumerate(out) if c[0] in names]
+            dp = torch.cat([out[i][2] for i in idx], 1)
+            wp = torch.cat([out[i][3] for i in idx], 1)
+            off = 0
+            for i in idx:
+                name, x, d, _ = out[i]
+                n = d.shape[1]
+                out[i] = (name, x, dp[:, off:off + n], wp[:, off:off + n])
+                off += n
     return out
 
 

@@ -117,7 +117,7 @@ def test_layer_step_training_order_is_unchanged():
     from fp4_quantized_amd.step import LayerStep
     dev = device()
     print("case layer-step-order", flush=True)
-    layers = workloads.layer_device(3, 1000, dev, shared=True)
+    layers = workloads.layer_device(3, 1000, dev, shared=True, cat=True)
     a = LayerStep(layers, av.MXFP4, split=True)
     b = LayerStep(layers, av.MXFP4, split=True)
     a.run()
@@ -136,7 +136,7 @@ def test_layer_step_overlap_matches_one_stream(fmt, fname):
     from fp4_quantized_amd.step import LayerStep
     dev = device()
     print(f"case layer-step-overlap-{fname}", flush=True)
-    layers = workloads.layer_device(3, 1000, dev, shared=True)
+    layers = workloads.layer_device(3, 1000, dev, shared=True, cat=True)
     a = LayerStep(layers, fmt, split=True, overlap=True)
     b = LayerStep(layers, fmt, split=True, overlap=False)
     assert a.side is not None and b.side is None
@@ -163,33 +163,55 @@ def test_layer_step_overlap_matches_one_stream(fmt, fname):
         check(f"replay {r}")
 
 
+@pytest.mark.parametrize("cat", [False, True])
 @pytest.mark.parametrize("split", [True, False])
-def test_layer_step_fused_shared_input_gemms(split):
+def test_layer_step_fused_shared_input_gemms(split, cat):
     # q, k and v share their input, so their weight gradients are the column blocks of one GEMM
     # X_R^T [D_q D_k D_v] (+ l mu_X^T [mu_Dq mu_Dk mu_Dv]), and q/k/v and gate/up have one
     # forward GEMM each, X_R [W_1 .. W_k]^T: every quantized operand equals the unfused step's
     # (the D column layouts, their means and the weights' K = m layouts are views into one
-    # operand), Y and dX are bit-identical, dW agrees up to fp32 summation order (the unfused
-    # launches split K) and against the oracle
+    # operand), Y is bit-identical, dW agrees up to fp32 summation order (the unfused launches
+    # split K) and against the oracle.  cat: the D_i and W_i of q/k/v and of gate/up are column
+    # blocks of one tensor each, which are then split once, and each group runs one input
+    # gradient GEMM, [D_1 .. D_k] [W_1 .. W_k]^T + 1 mu_D W^T: the sum of the unfused dX_i up to
+    # fp32 summation order, and the oracle's dX of the concatenated operands
     from fp4_quantized_amd.step import LayerStep
     from tests.gpu_util import rel_fro
     dev = device()
-    print(f"case layer-step-fused-dw split={split}", flush=True)
-    layers = workloads.layer_device(3, 1000, dev, shared=True)
-    a = LayerStep(layers, av.MXFP4, split=split, out_dtype=torch.float32, fuse_dw=True)
-    b = LayerStep(layers, av.MXFP4, split=split, out_dtype=torch.float32, fuse_dw=False, fuse_fwd=False)
+    print(f"case layer-step-fused split={split} cat={cat}", flush=True)
+    layers = workloads.layer_device(3, 1000, dev, shared=True, cat=cat)
+    a = LayerStep(layers, av.MXFP4, split=split, out_dtype=torch.float32)
+    b = LayerStep(layers, av.MXFP4, split=split, out_dtype=torch.float32, fuse_dw=False, fuse_fwd=False,
+                  fuse_dx=False)
     assert list(a.dw_fused) == [0] and not b.dw_fused  # q/k/v fused; gate/up would need two tile rounds
     assert list(a.fwd_fused) == [0, 2] and not b.fwd_fused  # q/k/v and gate/up
+    assert list(a.dx_fused) == ([0, 2] if cat else []) and not b.dx_fused
+    # 4 inputs, then 7 output gradients and 7 weights, or with cat 2 + 2 of each
+    assert len(a.quants) == (4 + 2 * 4 if cat else 18) and len(b.quants) == 18
     a.run()
     b.run()
     torch.cuda.synchronize()
-    for i, (qa, qb) in enumerate(zip(a.quants, b.quants)):
-        for k in ("mean", "row", "col", "mean_q"):
-            same(qa[2][k], qb[2][k], f"tensor {i} {k}")
+    grouped = ("q", "k", "v", "gate", "up") if cat else ()
     for ca, cb in zip(a.lin, b.lin):
-        assert torch.equal(ca["y"], cb["y"]) and torch.equal(ca["dx"], cb["dx"]), ca["name"]
+        for k in ("mean", "row", "col", "mean_q"):
+            same(ca["sx"][k], cb["sx"][k], f"{ca['name']} X {k}")
+        for k in ("mean", "col", "mean_q") + (() if ca["name"] in grouped else ("row",)):
+            same(ca["sd"][k], cb["sd"][k], f"{ca['name']} D {k}")
+        same(ca["sw"]["col"], cb["sw"]["col"], f"{ca['name']} W col")
+        if ca["name"] not in grouped:
+            same(ca["sw"]["row"], cb["sw"]["row"], f"{ca['name']} W row")
+        assert torch.equal(ca["y"], cb["y"]), ca["name"]
         e = rel_fro(ca["dw"].cpu().numpy(), cb["dw"].cpu().numpy())
         assert e <= 1e-6, f"{ca['name']} dW: {e:.3e}"
+    for pi, (_, _, lins) in enumerate(a.x_plan):
+        got = a.lin[lins[0]]["dx"]
+        if pi not in a.dx_fused:
+            for li in lins:
+                assert torch.equal(a.lin[li]["dx"], b.lin[li]["dx"]), a.lin[li]["name"]
+            continue
+        assert all(a.lin[li]["dx"] is got for li in lins)
+        e = rel_fro(got.cpu().numpy(), sum(b.lin[li]["dx"].double() for li in lins).cpu().numpy())
+        assert e <= 1e-6, f"group {pi} dX against the sum of the unfused dX_i: {e:.3e}"
     # the fused block of k against the oracle
     name, x, d, w = layers[1]
     c = a.lin[1]
@@ -205,3 +227,17 @@ def test_layer_step_fused_shared_input_gemms(split):
     ref = O.linear_bwd_dw(ox["col"], od["col"], ox["mean"], od["mean"], x.shape[0])
     e = rel_fro(c["dw"].cpu().numpy(), ref)
     assert e <= 1e-5, f"k dW against the oracle: {e:.3e}"
+    if cat:
+        # gate/up's one input gradient against the oracle on the concatenated D and W
+        f = a.dx_fused[2]
+        dp = torch.cat([cc[2] for cc in layers if cc[0] in ("gate", "up")], 1).float().cpu().numpy()
+        wp = torch.cat([cc[3] for cc in layers if cc[0] in ("gate", "up")], 1).float().cpu().numpy()
+        if split:
+            assert mean_ok(f["d"]["mean"].cpu().numpy(), dp), "gate/up: mean of D"
+        odp = O.split_quant(dp, av.MXFP4, split=split, mean=f["d"]["mean"].cpu().numpy() if split else None)
+        owp = O.split_quant(wp, av.MXFP4, split=False)
+        assert_q_equal(f["d"]["row"], odp["row"], "gate/up: D row layout")
+        assert_q_equal(f["w"]["row"], owp["row"], "gate/up: W row layout")
+        ref = O.linear_bwd_dx(odp["row"], odp["mean"] if split else None, owp["row"])
+        e = rel_fro(f["dx"].cpu().numpy(), ref)
+        assert e <= 1e-5, f"gate/up dX against the oracle: {e:.3e}"
