@@ -292,7 +292,7 @@ def main():
         roofline = {
             "bound": "hbm" if hbm_bound else "mfma",
             "kernel": f"k_gemm_ws<MXFP4, mean term> forward GEMM of gate and up together, {l} x {n} x {m}, bf16 Y "
-                      "(the step's longest launch)",
+                      "(the step's longest launch when its launches run one at a time)",
             "achieved": round(nbytes / launch_s / 1e9, 1) if hbm_bound else round(flops / launch_s / 1e12, 1),
             "peak": PEAK_HBM_GBPS if hbm_bound else PEAK_FP4_TFLOPS,
             "unit": "GB/s" if hbm_bound else "TFLOP/s",
