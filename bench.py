@@ -217,14 +217,12 @@ def main():
     headline = None
     if "roofline" in stages and "layer" not in stages:
         # the roofline launch alone: its operands, without timing the step
-        headline = LayerStep(workloads.layer_device(3, L_LAYER, dev, shared=True, cat=True), av.MXFP4, split=True)
+        headline = LayerStep(workloads.layer_device(3, L_LAYER, dev, shared=True), av.MXFP4, split=True)
         headline.quantize()
         torch.cuda.synchronize()
     if "layer" in stages:
         t0 = time.time()
-        # q/k/v and gate/up stored as fused projections (their output gradients and weights
-        # column blocks of one tensor each): one split of each and one summed dX GEMM per group
-        layers = workloads.layer_device(3, L_LAYER, dev, shared=True, cat=True)
+        layers = workloads.layer_device(3, L_LAYER, dev, shared=True)
         log(f"layer inputs ready in {time.time() - t0:.1f}s")
         res = {}
         for fmt, name in ((av.MXFP4, "mxfp4"), (av.NVFP4, "nvfp4")):
@@ -256,9 +254,10 @@ def main():
             res[name] = r
         res["gflop"] = round(flops / 1e9, 1)
         del layers
-        # the same linears stored one tensor per linear: a split per output gradient and weight,
-        # a dX per linear (their sum left to the caller)
-        layers = workloads.layer_device(3, L_LAYER, dev, shared=True, cat=False)
+        # q/k/v and gate/up stored as fused projections (their output gradients and weights
+        # column blocks of one tensor each): one split of each group's D and W and one dX GEMM
+        # per group, the sum of its linears' dX_i (the same flops)
+        layers = workloads.layer_device(3, L_LAYER, dev, shared=True, cat=True)
         r = {}
         for split in (True, False):
             st = LayerStep(layers, av.MXFP4, split=split, overlap=not args.one_stream)
@@ -267,8 +266,8 @@ def main():
         r["overhead_pct"] = round(100.0 * (r["averis"]["cold_med"] - r["vanilla"]["cold_med"])
                                   / r["vanilla"]["cold_med"], 2)
         r["step_tflops"] = round(flops / (r["averis"]["cold_med"] * 1e-3) / 1e12, 1)
-        res["mxfp4_per_linear_storage"] = r
-        log(f"layer mxfp4 per-linear storage: averis {r['averis']['cold_med']*1e3:.1f} us, "
+        res["mxfp4_fused_projections"] = r
+        log(f"layer mxfp4 fused projections: averis {r['averis']['cold_med']*1e3:.1f} us, "
             f"vanilla {r['vanilla']['cold_med']*1e3:.1f} us")
         out["layer"] = res
         del layers
@@ -550,9 +549,7 @@ def main():
                                "o 2048->1024, gate/up 1024->3072, down 3072->1024) at l=16384 tokens, fwd+dX+dW "
                                "each, bf16 in, bf16 Y/dX, fp32 dW, MXFP4 with the Averis split; q/k/v and gate/up "
                                "share their split input and their forward GEMM, q/k/v also their "
-                               "weight-gradient GEMM; q/k/v and gate/up stored as fused projections, "
-                               "so each group's output gradient and weight are split once and its dX "
-                               "is one GEMM (the sum over the group)",
+                               "weight-gradient GEMM",
                    "l": L_LAYER, "format": "mxfp4", "timing": "median of cold (cache-evicted) graph replays",
                    "streams": 1 if args.one_stream else 2},
         "split_quant": {"GBps": mx.get("split_quant_GBps"),
