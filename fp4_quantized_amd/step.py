@@ -204,7 +204,7 @@ class LayerStep:
         where it fills the GPU in one round of 128 x 128 tiles (as _fuse_dw), else one per
         linear on the views.  Returns the index of D's split."""
         dp, wp = parents
-        fmt, h16, split = self.fmt, self.hadamard, self.split
+        split = self.split
         l, m, N = dp.shape[0], wp.shape[0], dp.shape[1]
         dev = dp.device
         di, sdc = self._add(dp, split, l, N)
