@@ -11,8 +11,10 @@ bench uses) and its inputs are copied to the oracle.  Per linear:
 Workloads: the seven Qwen3-0.6B-shaped sweep linears at l = 16384 (q 1024->2048, k and v
 1024->1024, o 2048->1024, gate and up 1024->3072, down 3072->1024) on the bench's own device
 draws, and the down_proj layer (l = 16384, 3072 -> 1024, SwiGLU-like input) with and without the
-16x16 Hadamard.  At these sizes a short-K GEMM workgroup loops over up to six tiles and the
-long-K weight gradients run over 64 K-steps.
+16x16 Hadamard; and the layer step with q/k/v and gate/up stored as fused projections (one
+split of each group's output gradient and weight, one summed input gradient per group).  At
+these sizes a short-K GEMM workgroup loops over up to six tiles and the long-K weight gradients
+run over 64 K-steps.
 """
 import functools
 
@@ -24,7 +26,7 @@ import fp4_quantized_amd.averis as av
 from fp4_quantized_amd import workloads
 from fp4_quantized_amd.step import LinearStep
 from oracle import averis_oracle as O
-from tests.gpu_util import device, mean_ok, rel_fro, to_oracle
+from tests.gpu_util import assert_q_equal, device, mean_ok, rel_fro, to_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -141,3 +143,44 @@ def test_down_proj_sampled(fmt, fname, hadamard):
     x, d, w = (workloads.to_torch(a, "bf16", dev) for a in (lin.x, lin.d, lin.w))
     check_linear_sampled(f"down_proj-{fname}{'-h16' if hadamard else ''}", x, d, w, fmt, hadamard,
                          np.random.default_rng(12))
+
+
+def test_layer_fused_projections_sampled():
+    # The layer step as the bench times it with q/k/v and gate/up stored as fused projections
+    # (MXFP4, two streams, l = 16384): per group, the mean of the concatenated output gradient
+    # D = [D_1 .. D_k] in full, sampled rows of D's row layout and the whole weight W = [W_1 .. W_k]
+    # in its K = N layout bit-exact, and sampled rows of the group's forward output and of its one
+    # input gradient 1 (mu_D W^T) + D_R W^T against the oracle's exact products
+    from fp4_quantized_amd.step import LayerStep
+    dev = device()
+    rng = np.random.default_rng(13)
+    print("case layer-fused-projections l=16384 mxfp4", flush=True)
+    layers = workloads.layer_device(3, 16384, dev, shared=True, cat=True)
+    st = LayerStep(layers, av.MXFP4, split=True)
+    assert sorted(st.dx_fused) == [0, 2]
+    st.run()
+    torch.cuda.synchronize()
+    fmt = av.MXFP4
+    for pi, names in ((0, ("q", "k", "v")), (2, ("gate", "up"))):
+        what = "/".join(names)
+        grp = [c for c in layers if c[0] in names]
+        f, fw = st.dx_fused[pi], st.fwd_fused[pi]
+        x = grp[0][1]
+        l = x.shape[0]
+        dh = torch.cat([c[2] for c in grp], 1).float().cpu().numpy()
+        wh = torch.cat([c[3] for c in grp], 1).float().cpu().numpy()
+        mud = f["d"]["mean"].cpu().numpy()
+        assert mean_ok(mud, dh), f"{what}: mean of D"
+        rows = np.unique(np.concatenate([[0, 127, 128, l - 1], rng.choice(l, 44, replace=False)]))
+        q_dr = to_oracle(f["d"]["row"])
+        check_rows_quantized(q_dr, O.residual(dh, mud), fmt, False, rows, f"{what}: D row layout")
+        del dh
+        ow = O.split_quant(wh, fmt, split=False)
+        assert_q_equal(f["w"]["row"], ow["row"], f"{what}: W row layout")
+        assert_q_equal(fw["w"], ow["col"], f"{what}: W column layout")
+        q_wr, q_wc = to_oracle(f["w"]["row"]), to_oracle(fw["w"])
+        dx_ref = O.linear_bwd_dx(sub(q_dr, rows), to_oracle(f["d"]["mean_q"]), q_wr)
+        check_bf16(f["dx"].float().cpu().numpy()[rows], dx_ref, f"{what}: summed dX")
+        sx = fw["sx"]
+        y_ref = O.linear_fwd(sub(to_oracle(sx["row"]), rows), to_oracle(sx["mean_q"]), q_wc)
+        check_bf16(fw["y"].float().cpu().numpy()[rows], y_ref, f"{what}: Y")
